@@ -1,0 +1,140 @@
+// C-ABI front end of the gated delta-rule library: argument validation and
+// dispatch to the kernel launchers.  Declarations and contracts: include/kda.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "common.h"
+#include "launch.h"
+
+namespace kda {
+namespace {
+
+__global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, long n) {
+  for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<long>(gridDim.x) * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+float resolve_scale(float s, int dk) {
+  if (!(s > 0.f) || !isfinite(s)) return 1.0f / sqrtf(static_cast<float>(dk));
+  return s;
+}
+
+int check_common(const void* q, const void* k, const void* v, const void* beta, const void* decay,
+                 int decay_kind, int B, int T, int H, int DK, int DV, int dtype) {
+  // with no tokens there is nothing to read: empty tensors may carry NULL
+  if (T != 0 && (!q || !k || !v || !beta)) return KDA_ERR_NULL;
+  if (decay_kind != KDA_DECAY_NONE && decay_kind != KDA_DECAY_HEAD && decay_kind != KDA_DECAY_CHANNEL)
+    return KDA_ERR_UNSUPPORTED;
+  if (T != 0 && decay_kind != KDA_DECAY_NONE && !decay) return KDA_ERR_NULL;
+  if (B < 1 || H < 1 || T < 0 || DK < 1 || DV < 1) return KDA_ERR_SHAPE;
+  const long long tokens = static_cast<long long>(B) * T * H;
+  const long long widest = static_cast<long long>(DK > DV ? DK : DV);
+  if (tokens * widest >= (1LL << 31)) return KDA_ERR_SHAPE;
+  if (static_cast<long long>(B) * H * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
+  if (!dim_ok(DK) || !dim_ok(DV)) return KDA_ERR_UNSUPPORTED;
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+FwdArgs make_args(const void* q, const void* k, const void* v, const void* beta, const void* decay,
+                  int decay_kind, const float* init, float* o, float* state, int B, int T, int H,
+                  int DK, int DV, int dtype, float scale, int l2, int chunk) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.beta = beta;
+  a.decay = decay_kind == KDA_DECAY_NONE ? nullptr : decay;
+  a.decay_kind = decay_kind;
+  a.init = init; a.o = o; a.state = state;
+  a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.dtype = dtype;
+  a.scale = resolve_scale(scale, DK);
+  a.l2norm = l2 ? 1 : 0;
+  a.chunk = chunk;
+  return a;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s) {
+  if (n == 0 || src == dst) return hipSuccess;
+  long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  state_copy_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace kda
+
+extern "C" {
+
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                    const void* decay, int decay_kind, const float* initial_state,
+                    float* o, float* final_state,
+                    int B, int T, int H, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int chunk_size, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  if (st != KDA_OK) return st;
+  if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
+  if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  if (kda::chunked_lds_bytes(DK, DV, chunk_size, dtype) == 0) return KDA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    return kda::to_status(kda::launch_state_copy(initial_state, final_state,
+                                                 static_cast<long>(B) * H * DK * DV, s));
+  }
+  const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
+                                        final_state, B, T, H, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, chunk_size);
+  return kda::to_status(kda::launch_chunked(a, s));
+}
+
+int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
+                      const void* decay, int decay_kind, const float* initial_state,
+                      float* o, float* final_state,
+                      int B, int T, int H, int DK, int DV, int dtype,
+                      float softmax_scale, int use_qk_l2norm, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  if (st != KDA_OK) return st;
+  if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    return kda::to_status(kda::launch_state_copy(initial_state, final_state,
+                                                 static_cast<long>(B) * H * DK * DV, s));
+  }
+  const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
+                                        final_state, B, T, H, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, 0);
+  return kda::to_status(kda::launch_recurrent(a, s));
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                    const void* decay, int decay_kind, float* state, float* o,
+                    int B, int H, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, 1, H, DK, DV, dtype);
+  if (st != KDA_OK) return st;
+  if (!state || !o) return KDA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, state, o, state, B, 1, H,
+                                        DK, DV, dtype, softmax_scale, use_qk_l2norm, 0);
+  return kda::to_status(kda::launch_decode(a, s));
+}
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head size, chunk size, dtype or decay kind";
+    case KDA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+int kda_abi_version(void) { return 100; }
+
+}  // extern "C"

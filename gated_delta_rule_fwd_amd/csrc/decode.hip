@@ -1,0 +1,145 @@
+// Single-token decode: one step of the gated delta rule for every (batch, head),
+// the fp32 state streamed from HBM and written back in place.
+//
+// Closed form of one step (TileOPs "Linear Attention Operators",
+// DeltaNetRecurrentFwdOp, with the ejkernel recurrence's gate on the state):
+//   r     = S^T k_hat                  (read of the undecayed state)
+//   delta = beta (v - r)
+//   o     = S^T (exp(g) * q_hat) + (q_hat . k_hat) delta
+//   S'    = diag(exp(g)) S + k_hat delta^T
+// so the whole step needs one read and one write of S.  The kernel is bound
+// by HBM bandwidth: 2 * DK * DV * 4 bytes of state traffic per (batch, head)
+// against about 6 * DK * DV flops.
+#include "common.h"
+#include "launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DK, int DV, typename In>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
+    float* __restrict__ state, float* __restrict__ o, float scale, int l2norm) {
+  constexpr int NC4 = DV / 4;             // float4 column groups per state row
+  constexpr int NRG = kThreads / NC4;     // row groups
+  constexpr int RPT = DK / NRG;           // rows per thread
+  static_assert(RPT >= 1 && DK % NRG == 0, "shape");
+  constexpr int NW = kThreads / 64;
+
+  __shared__ float s_q[DK], s_k[DK], s_gate[DK], s_v[DV];
+  __shared__ float s_red[3][NW];
+  __shared__ f32x4 s_part[2][NW][NC4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long bh = blockIdx.x;
+  const int cg = tid % NC4, rg = tid / NC4;
+  float* S = state + bh * DK * DV;
+
+  // Issue the state loads first: they are the bulk of the traffic.
+  f32x4 st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + NRG * i;
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + c * DV) + cg);
+  }
+
+  // Token vectors; norms and q.k by block reduction.
+  float pq = 0.f, pk = 0.f, pqk = 0.f;
+  for (int c = tid; c < DK; c += kThreads) {
+    const float qc = act<In>::load1(q + bh * DK + c);
+    const float kc = act<In>::load1(k + bh * DK + c);
+    s_q[c] = qc;
+    s_k[c] = kc;
+    float gc = 1.f;
+    if (decay_kind == DECAY_CHANNEL) gc = __expf(act<In>::load1(decay + bh * DK + c));
+    s_gate[c] = gc;
+    pq += qc * qc; pk += kc * kc; pqk += qc * kc;
+  }
+  for (int n = tid; n < DV; n += kThreads) s_v[n] = act<In>::load1(v + bh * DV + n);
+  pq = group_sum<64>(pq); pk = group_sum<64>(pk); pqk = group_sum<64>(pqk);
+  if (lane == 0) { s_red[0][wave] = pq; s_red[1][wave] = pk; s_red[2][wave] = pqk; }
+  __syncthreads();
+  float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { sq += s_red[0][w]; sk += s_red[1][w]; sqk += s_red[2][w]; }
+  const float iq = (l2norm ? inv_norm(sq) : 1.f) * scale;   // q_hat = q * iq
+  const float ik = l2norm ? inv_norm(sk) : 1.f;             // k_hat = k * ik
+  const float qk = sqk * iq * ik;                           // q_hat . k_hat
+  const float b = act<In>::load1(beta + bh);
+  float ghead = 1.f;
+  if (decay_kind == DECAY_HEAD) ghead = __expf(act<In>::load1(decay + bh));
+
+  // Partial reads r = S^T k_hat and y = S^T (gate * q_hat) over this thread's rows.
+  f32x4 r = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + NRG * i;
+    const float kc = s_k[c] * ik;
+    const float qc = s_q[c] * iq * s_gate[c] * ghead;
+    r += st[i] * kc;
+    y += st[i] * qc;
+  }
+  // Reduce over the row groups that share a wave, then across waves.
+#pragma unroll
+  for (int off = NC4; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] += __shfl_xor(r[e], off, 64);
+      y[e] += __shfl_xor(y[e], off, 64);
+    }
+  }
+  if (lane < NC4) { s_part[0][wave][cg] = r; s_part[1][wave][cg] = y; }
+  __syncthreads();
+  r = s_part[0][0][cg];
+  y = s_part[1][0][cg];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { r += s_part[0][w][cg]; y += s_part[1][w][cg]; }
+
+  f32x4 delta;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) delta[e] = b * (s_v[4 * cg + e] - r[e]);
+  if (rg == 0) {
+    const f32x4 out = y + qk * delta;
+    *reinterpret_cast<f32x4*>(o + bh * DV + 4 * cg) = out;
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + NRG * i;
+    const float gc = s_gate[c] * ghead;
+    const float kc = s_k[c] * ik;
+    const f32x4 ns = st[i] * gc + kc * delta;
+    __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV) + cg);
+  }
+}
+
+template <typename In>
+hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
+  const dim3 grid(a.B * a.H), block(kThreads);
+  const In* q = static_cast<const In*>(a.q);
+  const In* k = static_cast<const In*>(a.k);
+  const In* v = static_cast<const In*>(a.v);
+  const In* be = static_cast<const In*>(a.beta);
+  const In* de = static_cast<const In*>(a.decay);
+#define KDA_DECODE_CASE(dk, dv)                                                              \
+  if (a.DK == dk && a.DV == dv) {                                                            \
+    decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.state, \
+                                                      a.o, a.scale, a.l2norm);              \
+    return hipGetLastError();                                                                \
+  }
+  KDA_DECODE_CASE(32, 32) KDA_DECODE_CASE(32, 64) KDA_DECODE_CASE(32, 128)
+  KDA_DECODE_CASE(64, 32) KDA_DECODE_CASE(64, 64) KDA_DECODE_CASE(64, 128)
+  KDA_DECODE_CASE(128, 32) KDA_DECODE_CASE(128, 64) KDA_DECODE_CASE(128, 128)
+#undef KDA_DECODE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdArgs& a, hipStream_t s) {
+  return a.dtype == 0 ? dispatch<float>(a, s) : dispatch<bf16_t>(a, s);
+}
+
+}  // namespace kda

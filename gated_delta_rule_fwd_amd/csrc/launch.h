@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI front end and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* decay;
+  int decay_kind;
+  const float* init;   // NULL = zeros (decode: unused)
+  float* o;
+  float* state;        // final state (decode: state updated in place)
+  int B, T, H, DK, DV;
+  int dtype;           // 0 f32, 1 bf16
+  float scale;         // already resolved (> 0)
+  int l2norm;
+  int chunk;
+};
+
+// Each launcher assumes the front end has validated the arguments.
+hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
+hipError_t launch_recurrent(const FwdArgs& a, hipStream_t s);
+hipError_t launch_chunked(const FwdArgs& a, hipStream_t s);
+hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
+// Largest LDS footprint (bytes) the chunked kernel needs for this shape, 0 if unsupported.
+size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype);
+
+}  // namespace kda

@@ -1,0 +1,195 @@
+"""Python binding of libkda.so: argument marshalling only.
+
+Every function here checks tensor placement, dtype and shape, allocates the
+outputs with torch (device memory is all torch is used for), and calls the
+C entry point of the same name on torch's current stream.  All arithmetic
+runs in the library's HIP kernels; there is no fallback.  Calls are
+asynchronous like any torch op on that stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+DECAY_NONE, DECAY_HEAD, DECAY_CHANNEL = 0, 1, 2
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_HIP"}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = lib().kda_status_string(status).decode()
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (built by ``gated_delta_rule_fwd_amd.build``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m gated_delta_rule_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
+                                      i, i, i, i, i, i, f, i, i, vp]
+        L.kda_fwd_chunked.restype = i
+        L.kda_fwd_recurrent.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
+                                        i, i, i, i, i, i, f, i, vp]
+        L.kda_fwd_recurrent.restype = i
+        L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, i, vp, vp,
+                                      i, i, i, i, i, f, i, vp]
+        L.kda_decode_step.restype = i
+        L.kda_status_string.argtypes = [i]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_abi_version.argtypes = []
+        L.kda_abi_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_act(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_state(name, t, shape, device):
+    if t is None:
+        return
+    if t.device != device or t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
+def _scale(softmax_scale):
+    return 0.0 if softmax_scale is None else float(softmax_scale)
+
+
+def _decay_kind(decay, lead, dk):
+    if decay is None:
+        return DECAY_NONE
+    if tuple(decay.shape) == tuple(lead):
+        return DECAY_HEAD
+    if tuple(decay.shape) == tuple(lead) + (dk,):
+        return DECAY_CHANNEL
+    raise ValueError(f"decay has shape {tuple(decay.shape)}; expected {tuple(lead)} or "
+                     f"{tuple(lead) + (dk,)}")
+
+
+def _prep_fwd(q, k, v, beta, decay, initial_state):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, DK]")
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _check_act("q", q, (B, T, H, DK), dt, dev)
+    _check_act("k", k, (B, T, H, DK), dt, dev)
+    _check_act("v", v, (B, T, H, DV), dt, dev)
+    _check_act("beta", beta, (B, T, H), dt, dev)
+    kind = _decay_kind(decay, (B, T, H), DK)
+    if decay is not None:
+        _check_act("decay", decay, tuple(decay.shape), dt, dev)
+    _check_state("initial_state", initial_state, (B, H, DK, DV), dev)
+    return B, T, H, DK, DV, dev, kind
+
+
+def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
+                use_qk_l2norm=True, chunk_size=64, out=None, final_state=None):
+    """Chunked forward.  Returns (o [B,T,H,DV] fp32, final_state [B,H,DK,DV] fp32)."""
+    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
+    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, T, H, DV), dev)
+    fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
+                                                                 dtype=torch.float32)
+    _check_state("final_state", fs, (B, H, DK, DV), dev)
+    st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
+                               _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
+                               _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
+                               int(chunk_size), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_fwd_chunked", st)
+    return o, fs
+
+
+def fwd_recurrent(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
+                  use_qk_l2norm=True, out=None, final_state=None):
+    """Recurrent (sequential) forward.  Same returns as fwd_chunked."""
+    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
+    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, T, H, DV), dev)
+    fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
+                                                                 dtype=torch.float32)
+    _check_state("final_state", fs, (B, H, DK, DV), dev)
+    st = lib().kda_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
+                                 _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
+                                 _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
+                                 _stream(dev))
+    if st != 0:
+        raise KdaError("kda_fwd_recurrent", st)
+    return o, fs
+
+
+def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=True, out=None):
+    """One decode step for every (batch, head); ``state`` [B,H,DK,DV] fp32 is
+    updated in place.  Returns o [B,H,DV] fp32."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, DK]")
+    B, H, DK = q.shape
+    DV = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _check_act("q", q, (B, H, DK), dt, dev)
+    _check_act("k", k, (B, H, DK), dt, dev)
+    _check_act("v", v, (B, H, DV), dt, dev)
+    _check_act("beta", beta, (B, H), dt, dev)
+    kind = _decay_kind(decay, (B, H), DK)
+    if decay is not None:
+        _check_act("decay", decay, tuple(decay.shape), dt, dev)
+    if state is None:
+        raise ValueError("state is required")
+    _check_state("state", state, (B, H, DK, DV), dev)
+    o = out if out is not None else torch.empty((B, H, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, H, DV), dev)
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
+                               _ptr(state), _ptr(o), B, H, DK, DV, _dtype_code(q),
+                               _scale(softmax_scale), int(bool(use_qk_l2norm)), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_decode_step", st)
+    return o

@@ -1,0 +1,135 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) gated delta-rule forward library.
+ *
+ * The operation (ejkernel "kernel_delta_attention._interface", section "Kernel
+ * Delta Attention", the core recurrence and its parameter list): per
+ * (batch, head) a [DK, DV] fp32 state S (rows = key channels) evolves as
+ *
+ *     S_t = diag(exp(decay_t)) S_{t-1} + k_t (beta_t (v_t - S_{t-1}^T k_t))^T
+ *     o_t = S_t^T q_t
+ *
+ * where q_t and k_t are first divided by their L2 norm (if use_qk_l2norm) and
+ * q_t is multiplied by softmax_scale.  The delta term reads the previous state
+ * before it is decayed, as the recurrence is printed.  decay is log-space and
+ * is either absent, one value per (token, head) (the scalar gate of TileOPs
+ * GDNFwdOp), or one value per (token, head, key channel) (the per-key-channel
+ * gate of TileOPs KDAFwdOp, which scales the state rows).  beta is used as
+ * given (TileOPs DeltaNetFwdOp: already transformed).
+ *
+ * Conventions common to every entry point:
+ *
+ *  - Every tensor pointer is a DEVICE pointer, owned by the caller, dense and
+ *    row-major in the shape stated.  The library never allocates, frees or
+ *    keeps device memory, and keeps no state between calls: calls are
+ *    thread-safe and need no init.
+ *  - Activations (q, k, v, beta, decay) share one dtype, KDA_F32 or KDA_BF16.
+ *    Outputs o are fp32; states are fp32 (TileOPs DeltaNetFwdOp: the
+ *    recurrent state is FP32 and belongs to the caller).
+ *  - softmax_scale <= 0 or NaN means the default DK^-0.5 (ejkernel kda:
+ *    "If None, uses head_dim^-0.5"; TileOPs GLA ops: non-positive means the
+ *    default).  use_qk_l2norm != 0 normalises q and k by max(||x||_2, 1e-12).
+ *  - decay must be <= 0 (ejkernel kda parameter list: "should be <= 0"); the
+ *    kernels rely on it to keep decay factors <= 1 and do not check it.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.  The return value reports
+ *    argument validation (nothing is launched when it fails) and launch
+ *    errors; a device-side fault surfaces at the caller's next
+ *    synchronisation.
+ *  - Supported sizes: DK, DV in {32, 64, 128}; B, H >= 1; T >= 0 with
+ *    B*T*H*max(DK,DV) < 2^31.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
+  KDA_ERR_UNSUPPORTED = 3, /* DK/DV/chunk/dtype/decay kind not implemented   */
+  KDA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_DECAY_NONE = 0,    /* decay ignored (may be NULL): no decay             */
+  KDA_DECAY_HEAD = 1,    /* decay [.., H]: one log-space value per token-head */
+  KDA_DECAY_CHANNEL = 2  /* decay [.., H, DK]: one per token-head-key channel */
+} kda_decay_kind;
+
+/*
+ * Chunked forward: "parallel within chunks, sequential across chunks"
+ * (ejkernel kda, section "Algorithm Modes", Chunked), in the WY form of the
+ * TileOPs DeltaNet pipeline (prepare_wy_repr, then the forward).
+ *
+ *   q, k           [B, T, H, DK]  activation dtype
+ *   v              [B, T, H, DV]  activation dtype
+ *   beta           [B, T, H]      activation dtype
+ *   decay          NULL | [B, T, H] | [B, T, H, DK] per decay_kind
+ *   initial_state  NULL (zeros) | [B, H, DK, DV] fp32
+ *   o              [B, T, H, DV] fp32, written
+ *   final_state    [B, H, DK, DV] fp32, written; may alias initial_state
+ *   chunk_size     16, 32 or 64 (ejkernel default 64); the result does not
+ *                  depend on it beyond rounding.  T need not be a multiple.
+ *
+ * T == 0 copies initial_state (or zeros) to final_state; then q, k, v, beta,
+ * decay and o are not read and may be NULL.
+ * Errors: KDA_ERR_NULL if final_state is NULL, or (T > 0) q/k/v/beta/o is
+ * NULL or decay is NULL with decay_kind != NONE; KDA_ERR_SHAPE for negative or overflowing sizes;
+ * KDA_ERR_UNSUPPORTED for other DK/DV/chunk/dtype/decay_kind values, and for
+ * KDA_F32 with DK = 128 and chunk_size = 64 (its tiles exceed the LDS of one
+ * compute unit; use chunk_size <= 32 or the recurrent entry point).
+ */
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                    const void* decay, int decay_kind, const float* initial_state,
+                    float* o, float* final_state,
+                    int B, int T, int H, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int chunk_size,
+                    void* stream);
+
+/*
+ * Recurrent forward: the pure sequential scan (ejkernel kda, section
+ * "Algorithm Modes", Recurrent).  Same arguments and errors as
+ * kda_fwd_chunked without chunk_size.  Computes in fp32 throughout.
+ */
+int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
+                      const void* decay, int decay_kind, const float* initial_state,
+                      float* o, float* final_state,
+                      int B, int T, int H, int DK, int DV, int dtype,
+                      float softmax_scale, int use_qk_l2norm, void* stream);
+
+/*
+ * Single-step decode (ejkernel kda, "Single-step: optimized path when
+ * seq_len=1 with initial_state"; the closed form of TileOPs
+ * DeltaNetRecurrentFwdOp extended with the gate): one token for every
+ * (batch, head), the state updated IN PLACE.
+ *
+ *   q, k   [B, H, DK]; v [B, H, DV]; beta [B, H] (activation dtype)
+ *   decay  NULL | [B, H] | [B, H, DK] per decay_kind
+ *   state  [B, H, DK, DV] fp32, read then overwritten with the new state
+ *   o      [B, H, DV] fp32, written (must not overlap state)
+ *
+ * Errors as kda_fwd_chunked (state must be non-NULL).
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                    const void* decay, int decay_kind, float* state, float* o,
+                    int B, int H, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kda_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,86 @@
+"""CPU tests of the C ABI: the library loads, exports what include/kda.h
+declares, and rejects bad arguments on the host without launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_fwd_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(kda_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(K.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return K.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for fn in ("kda_fwd_chunked", "kda_fwd_recurrent", "kda_decode_step", "kda_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_status_strings_and_version(L):
+    assert L.kda_abi_version() == 100
+    assert L.kda_status_string(0) == b"ok"
+    for code in (1, 2, 3, 5):
+        assert len(L.kda_status_string(code)) > 3
+    assert L.kda_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def chunked(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
+             B=1, T=8, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64)
+    a.update(kw)
+    return L.kda_fwd_chunked(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
+                             a["o"], a["fs"], a["B"], a["T"], a["H"], a["DK"], a["DV"], a["dtype"],
+                             a["scale"], a["l2"], a["chunk"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(fs=None), 1), (dict(beta=None), 1),
+    (dict(kind=1, decay=None), 1), (dict(kind=2, decay=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(B=1 << 20, T=1 << 12, H=8), 2),
+    (dict(DK=48), 3), (dict(DV=256), 3), (dict(dtype=7), 3), (dict(kind=5), 3),
+    (dict(chunk=128), 3), (dict(chunk=8), 3), (dict(dtype=0, DK=128, DV=128, chunk=64), 3),
+])
+def test_chunked_rejects_bad_arguments(L, kw, code):
+    assert chunked(L, **kw) == code
+
+
+def test_recurrent_and_decode_reject_bad_arguments(L):
+    assert L.kda_fwd_recurrent(None, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
+                               1, 4, 1, 64, 64, 1, 0.0, 1, None) == 1
+    assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
+                               1, 4, 1, 96, 64, 1, 0.0, 1, None) == 3
+    assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE,
+                             1, 1, 64, 64, 1, 0.0, 1, None) == 1
+    assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
+                             0, 1, 64, 64, 1, 0.0, 1, None) == 2
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        K.fwd_chunked(x, x, x, torch.zeros(1, 4, 1))

@@ -1,0 +1,252 @@
+#!/usr/bin/env python
+"""Benchmark of the gated delta-rule forward on one MI355X.
+
+One step = one kda_fwd_chunked call (prep, WY, state walk and output, fused in
+one kernel launch) over one batch of synthetic inputs already resident in HBM.
+The default workload is the scalar-gated DK = DV = 128 case
+(B8 T4096 H16, chunk 64, initial state); the printed JSON line also carries the
+per-channel-gated DK = DV = 128 case and the single-token decode as extra
+measurements, the roofline of the chunked kernel (HIP-event kernel time,
+algorithmic bytes) and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunked fwd tokens/s + MFMA util (DK=DV=128); decode state GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_F16 = 2.5e15         # MI355X dense fp16/bf16 MFMA, flop/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["chunked_impl.h", "chunked_layout.h", "common.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def act_bytes(w) -> int:
+    return 4 if w.dtype == "f32" else 2
+
+
+def chunked_bytes(w) -> int:
+    """Algorithmic HBM bytes of one chunked call: every input read once, o and
+    the final state written once."""
+    a = act_bytes(w)
+    tok = w.B * w.T * w.H
+    per_tok = (2 * w.DK + w.DV + 1) * a + w.DV * 4
+    if w.decay_kind == 1:
+        per_tok += a
+    elif w.decay_kind == 2:
+        per_tok += w.DK * a
+    state = w.B * w.H * w.DK * w.DV * 4
+    return tok * per_tok + state * (2 if w.init_state else 1)
+
+
+def chunked_flops(w) -> float:
+    """Algorithmic flops of the chunked WY form, dense C x C tiles: per
+    token-head 3 C DK + 2 C DV + 3 DK DV + C^2 / 6 multiply-adds."""
+    C = w.chunk
+    macs = 3 * C * w.DK + 2 * C * w.DV + 3 * w.DK * w.DV + C * C / 6
+    return 2.0 * macs * w.B * w.T * w.H
+
+
+def decode_bytes(w) -> int:
+    a = act_bytes(w)
+    bh = w.B * w.H
+    per = 2 * w.DK * w.DV * 4 + (2 * w.DK + w.DV + 1) * a + w.DV * 4
+    if w.decay_kind == 1:
+        per += a
+    elif w.decay_kind == 2:
+        per += w.DK * a
+    return bh * per
+
+
+def to_dev(inp, dev):
+    return {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+
+
+def time_chunked(w, steps, warmup, dev):
+    import torch
+    from gated_delta_rule_fwd_amd import fwd_chunked
+    from gated_delta_rule_fwd_amd.inputs import make_inputs
+    d = to_dev(make_inputs(w), dev)
+    o = torch.empty((w.B, w.T, w.H, w.DV), device=dev, dtype=torch.float32)
+    fs = torch.empty((w.B, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
+    for _ in range(warmup):
+        fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs)
+    torch.cuda.synchronize()
+    # Events on torch's current stream, which is the stream the library launches on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs)
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in evs]
+    return wall / steps * 1e3, sum(kern_ms) / len(kern_ms), min(kern_ms)
+
+
+def time_decode(w, steps, warmup, dev):
+    import torch
+    from gated_delta_rule_fwd_amd import decode_step
+    from gated_delta_rule_fwd_amd.inputs import make_inputs
+    inp = make_inputs(w)
+    d = to_dev(inp, dev)
+    # two state buffers used alternately so consecutive calls stream different memory
+    states = [d["initial_state"], d["initial_state"].clone()]
+    o = torch.empty((w.B, w.H, w.DV), device=dev, dtype=torch.float32)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["decay"])
+    for i in range(warmup):
+        decode_step(*args, states[i % 2], out=o)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (s, e) in enumerate(evs):
+        s.record()
+        decode_step(*args, states[i % 2], out=o)
+        e.record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in evs]
+    return sum(ms) / len(ms)
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, as it is, on the first two sequences (all heads, full
+    length) of the workload; scaled to tokens/s of the same head count."""
+    import numpy as np
+    from gated_delta_rule_fwd_amd.inputs import make_inputs
+    from oracle import kda_scan
+    inp = make_inputs(w)
+    nb = min(2, w.B)
+    sl = slice(0, nb)
+    t0 = time.perf_counter()
+    kda_scan(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["beta"][sl],
+             None if inp["decay"] is None else inp["decay"][sl],
+             None if inp["initial_state"] is None else inp["initial_state"][sl])
+    dt = time.perf_counter() - t0
+    return {"value": nb * w.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{w.name}: {nb} of {w.B} sequences x {w.H} heads x {w.T} tokens, "
+                      f"NumPy fp64 sequential scan on one host thread "
+                      f"(numpy {np.__version__})"}
+
+
+def stored_traffic(name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(name)
+    if not ent or ent.get("kernel_hash") != kernel_hash():
+        return None   # counters were taken on another version of the kernel
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gdn_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); each (batch, head) is independent, so a "
+              f"multi-GPU run would be this single-GPU kernel on each GPU's share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_fwd_amd.inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    if w.decode:
+        print("--workload must be a chunked workload", file=sys.stderr)
+        sys.exit(2)
+
+    ms_step, kern_ms, kern_min = time_chunked(w, args.steps, args.warmup, dev)
+    tokens = w.B * w.T
+    byts = chunked_bytes(w)
+    flops = chunked_flops(w)
+    achieved = byts / (kern_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
+            "kernel": "chunked_kernel", "kernel_ms_mean": round(kern_ms, 4),
+            "kernel_ms_min": round(kern_min, 4), "algorithmic_bytes": byts,
+            "mfma_frac_dense_count": round(flops / (kern_ms * 1e-3) / MFMA_PEAK_F16, 4)}
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "DK": w.DK, "DV": w.DV,
+                   "chunk": w.chunk, "decay": w.decay, "initial_state": w.init_state,
+                   "activations": w.dtype, "mfma": "f16 x f16 -> f32", "state": "f32",
+                   "output": "f32"},
+        "roofline": roof,
+    }
+    if not args.no_extra:
+        extra = {}
+        w4 = WORKLOADS["kda_d128"]
+        if w4.name != w.name:
+            m4, k4, _ = time_chunked(w4, max(3, args.steps // 2), args.warmup, dev)
+            extra[w4.name] = {"tokens_per_s": round(w4.B * w4.T / (m4 * 1e-3), 1),
+                              "kernel_ms_mean": round(k4, 4),
+                              "hbm_frac": round(chunked_bytes(w4) / (k4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac_dense_count": round(chunked_flops(w4) / (k4 * 1e-3) / MFMA_PEAK_F16, 4)}
+        w5 = WORKLOADS["decode_d128"]
+        d_ms = time_decode(w5, max(5, args.steps), args.warmup, dev)
+        gbs = decode_bytes(w5) / (d_ms * 1e-3) / 1e9
+        extra[w5.name] = {"kernel_ms_mean": round(d_ms, 4), "GB_per_s": round(gbs, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_call": decode_bytes(w5)}
+        line["extra"] = extra
+        torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,54 +7,57 @@
 namespace kda {
 
 // OpBytes: 2 (fp16 MFMA operands, bf16 activations) or 4 (fp32 operands).
-// CM: largest chunk the instantiation handles (32 or 64).
-// DVS: value columns owned by one workgroup.
-template <int DK, int DVS, int CM, int OpBytes>
+// C: chunk size (16, 32 or 64).  DVS: value columns owned by one workgroup.
+template <int DK, int DVS, int C, int OpBytes>
 struct ChunkLayout {
-  static constexpr int PAD = 16 / OpBytes;        // 16-byte row padding
-  static constexpr int LDK = DK + PAD;            // row stride of [CM][DK] operand tiles
-  static constexpr int LC = CM + PAD;             // row stride of [*][CM] operand tiles
-  static constexpr int LF = CM + 4;               // row stride of fp32 [CM][CM] tiles
-  static constexpr int NB = CM / 16;
+  static constexpr int NB = C / 16;                 // 16-token blocks per chunk
+  static constexpr int NCOL = C < 32 ? 32 : C;      // token columns read by 32-wide k steps
+  static constexpr int PAD = 16 / OpBytes;          // 16-byte row padding
+  static constexpr int LDK = DK + PAD;              // row stride of [C][DK] operand tiles
+  static constexpr int LC = NCOL + PAD;             // row stride of [*][tokens] operand tiles
+  static constexpr int LF = C + 4;                  // row stride of fp32 [C][C] tiles
+  static constexpr int KinvBytes = OpBytes == 2 ? 2 : 4;
 
-  static constexpr size_t kRowTile = size_t(CM) * LDK * OpBytes;   // [CM][DK]
-  static constexpr size_t kColTile = size_t(DK) * LC * OpBytes;    // [DK][CM]
-  static constexpr size_t kVT = size_t(DVS) * LC * OpBytes;         // [DVS][CM]
-  static constexpr size_t kCC = size_t(CM) * LC * OpBytes;          // [CM][CM] operand
-  static constexpr size_t kF32CC = size_t(CM) * LF * 4;             // [CM][CM] fp32
-  static constexpr size_t kKinv = size_t(CM) * LDK * (OpBytes == 2 ? 2 : 4);
+  static constexpr size_t kRowTile = size_t(C) * LDK * OpBytes;     // [C][DK]
+  static constexpr size_t kColTile = size_t(DK) * LC * OpBytes;     // [DK][tokens]
+  static constexpr size_t kVT = size_t(DVS) * LC * OpBytes;          // [DVS][tokens]
+  static constexpr size_t kCC = size_t(C) * LC * OpBytes;            // [C][tokens] operand
+  static constexpr size_t kF32CC = size_t(C) * LF * 4;               // [C][C] fp32
+  static constexpr size_t kGst = size_t(C) * DK * OpBytes;           // staged per-channel gate
 
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t al(size_t a) { return (a + 255) & ~size_t(255); }
 
-  // Regions, in order.  Live ranges within one chunk step:
-  //   Q   q tile (raw, or decayed in per-channel mode)         load .. output
-  //   KT  k^T (raw, or k*exp(Gx) transposed)                    load .. state update / W
-  //   VT  v^T of this workgroup's value columns                 load .. U
-  //   P   masked decayed q k^T                                  Gram .. output
-  //   RA  k tile (load .. Gram)  |  fp32 inverse T (inverse)
-  //   RB  fp32 A (Gram .. inverse)  |  -W (W .. state step)
-  //   RC  per-channel Gram factors (load .. Gram)  |  T-derived operands Tw, Tu (inverse .. state step)
-  //   KF  per-channel: staged gate (load) | (k*F)^T (load .. state update)
+  // Regions and what they hold within one chunk step:
+  //   Q    q (normalised, scaled; per-channel: times its decay)      load .. output
+  //   K    k (normalised; per-channel: times its decay)             load .. state step
+  //   KT   k transposed (per-channel: k times decay to chunk end)    load .. state update
+  //   VT   v transposed, this workgroup's value columns              load .. state step
+  //   P    masked decayed q k^T                                      Gram .. output
+  //   AM   fp32 A (Gram .. inverse); per-channel: staged gate first (load)
+  //   RA   per-channel Gram factors Kb, Kinv (load .. Gram)  |  fp32 T and T diag(beta) (inverse ..)
   static constexpr size_t oQ = 0;
-  static constexpr size_t oKT = al(oQ + kRowTile);
+  static constexpr size_t oK = al(oQ + kRowTile);
+  static constexpr size_t oKT = al(oK + kRowTile);
   static constexpr size_t oVT = al(oKT + kColTile);
   static constexpr size_t oP = al(oVT + kVT);
-  static constexpr size_t oRA = al(oP + kCC);
-  static constexpr size_t oRB = al(oRA + mx(kRowTile, kF32CC));
-  static constexpr size_t oRC = al(oRB + mx(kF32CC, kRowTile));
-  static constexpr size_t szRC(bool ch) { return mx(ch ? kRowTile + kKinv : 0, 2 * kCC); }
-  static constexpr size_t oKF(bool ch) { return al(oRC + szRC(ch)); }
-  static constexpr size_t szKF(bool ch) { return ch ? mx(kColTile, size_t(CM) * DK * OpBytes) : 0; }
-  // fp32 vectors
-  static constexpr int kVecRows = 8;              // sq sk bt Gi Ge eG eGx eF  (each CM)
-  // D[i][j] is needed for i - j >= 2 only
+  static constexpr size_t oAM = al(oP + kCC);
+  static constexpr size_t oRA = al(oAM + mx(kF32CC, kGst));
+  static constexpr size_t oTu = al(oRA + kF32CC);                     // T diag(beta), fp16/fp32
+  static constexpr size_t oKinv = al(oRA + kRowTile);                 // after Kb
+  static constexpr size_t szRA(bool ch) {
+    return mx(ch ? (oKinv - oRA) + size_t(C) * LDK * KinvBytes : 0, (oTu - oRA) + kCC);
+  }
+  // D[i][j] (decay of the blocks strictly between j and i) is needed for i - j >= 2
   static constexpr int ND = NB >= 3 ? (NB - 2) * (NB - 1) / 2 : 1;
   static constexpr int dslot(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
-  static constexpr int kChanVecs = 3 * NB + ND + 1;   // tau[NB] Cb[NB] rsq[NB] D[ND] decC
-  static constexpr size_t oVec(bool ch) { return al(oKF(ch) + szKF(ch)); }
+  // fp32 vectors: bt Gi Ge eG eGx eF (each C), misc[16]; per-channel:
+  // tau[NB] Cb[NB] rsq[NB] D[ND] decC  (each DK)
+  static constexpr int kVecRows = 6;
+  static constexpr int kChanVecs = 3 * NB + ND + 1;
+  static constexpr size_t oVec(bool ch) { return al(oRA + szRA(ch)); }
   static constexpr size_t szVec(bool ch) {
-    return size_t(kVecRows) * CM * 4 + 64 + (ch ? size_t(kChanVecs) * DK * 4 : 0);
+    return size_t(kVecRows) * C * 4 + 64 + (ch ? size_t(kChanVecs) * DK * 4 : 0);
   }
   static constexpr size_t bytes(bool ch) { return al(oVec(ch) + szVec(ch)); }
 };

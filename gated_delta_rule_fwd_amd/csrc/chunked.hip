@@ -48,8 +48,11 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const int nheads = a.B * a.H;
   cp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
   const int nwg = nheads * cp.nsl;
-  return a.dtype == 0 ? chunked::launch_f32(a.DK, pl.dvs, a.chunk, cp, nwg, chan, s)
-                      : chunked::launch_bf16(a.DK, pl.dvs, a.chunk, cp, nwg, chan, s);
+  using LaunchFn = hipError_t (*)(int, int, int, const ChunkParams&, int, hipStream_t);
+  static const LaunchFn table[2][3] = {
+      {chunked::launch_f32_d0, chunked::launch_f32_d1, chunked::launch_f32_d2},
+      {chunked::launch_bf16_d0, chunked::launch_bf16_d1, chunked::launch_bf16_d2}};
+  return table[a.dtype == 0 ? 0 : 1][a.decay_kind](a.DK, pl.dvs, a.chunk, cp, nwg, s);
 }
 
 }  // namespace kda

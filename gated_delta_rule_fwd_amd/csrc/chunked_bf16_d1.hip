@@ -1,0 +1,13 @@
+// Instantiations of the fused chunked kernel: bf16 activations, decay kind 1
+// (0 none, 1 per head, 2 per key channel).
+#include "chunked_impl.h"
+
+namespace kda {
+namespace chunked {
+
+hipError_t launch_bf16_d1(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s) {
+  return launch_any<bf16_t, 1>(DK, DVS, C, cp, nwg, s);
+}
+
+}  // namespace chunked
+}  // namespace kda

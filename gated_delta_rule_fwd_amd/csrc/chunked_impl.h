@@ -156,7 +156,7 @@ __host__ __device__ constexpr int pair_j(int n) { int i = 0; while (n > i) { n -
 
 // ------------------------------------------------------------------ kernel --
 
-template <int DK, int DVS, int C, typename In>
+template <int DK, int DVS, int C, typename In, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
@@ -182,9 +182,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int T = p.T, H = p.H, DV = p.DV;
-  const int decay_kind = p.decay_kind;
-  const bool chan = decay_kind == DECAY_CHANNEL;
-  const bool headdecay = decay_kind == DECAY_HEAD;
+  // one kernel per decay kind keeps the chunk loop small enough for the
+  // instruction cache
+  constexpr bool chan = DECAY == DECAY_CHANNEL;
+  constexpr bool headdecay = DECAY == DECAY_HEAD;
 
   // Workgroup -> (head, slice).  With xcd_map the slices of one head get ids
   // that are equal mod 8, i.e. run on the same XCD and share its L2.
@@ -246,7 +247,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
   // ---- prefetch registers (one chunk ahead) ----
   uint4 rq[NP], rk[NP], rg[NP], rv[NPv];
-  float rbeta = 0.f, rgh = 0.f;
+  // kept as raw activation values: converting right after the load would make
+  // the compiler wait for every outstanding load, the prefetch included
+  In rbeta{}, rgh{};
 
   auto issue_loads = [&](int t0) {
     const int Lc = min(C, T - t0);
@@ -270,11 +273,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
         rv[pp] = *reinterpret_cast<const uint4*>(gv + off);
       }
     }
-    rbeta = 0.f; rgh = 0.f;
+    rbeta = In{}; rgh = In{};
     if (tid < C && tid < Lc) {
       const long off = (tok0 + t0 + tid) * H + h;
-      rbeta = act<In>::load1(gb + off);
-      if (headdecay) rgh = act<In>::load1(gg + off);
+      rbeta = gb[off];
+      if (headdecay) rgh = gg[off];
     }
   };
   auto unpack = [&](const uint4& raw, float (&x)[V]) {
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
     }
     if (wave == 0) {
       // beta and the scalar gate: lane r holds token r of the chunk (C <= 64).
-      float G = (lane < C) ? rgh : 0.f;
+      float G = (lane < C) ? act<In>::cvt(rgh) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(G, off, 64);
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
       if (lane == 0) Gx = 0.f;
       const float Glast = __shfl(G, 63, 64);
       if (lane < C) {
-        s_bt[lane] = rbeta;
+        s_bt[lane] = act<In>::cvt(rbeta);
         s_Gi[lane] = G;
         s_Ge[lane] = Gx;
         s_eG[lane] = __expf(G);
@@ -465,9 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
     }
 
     // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-#pragma unroll
-    for (int job = 0; job < 2 * NPAIR; ++job) {
-      if (job % kWaves != wave) continue;
+    for (int job = wave; job < 2 * NPAIR; job += kWaves) {
       const bool isP = job >= NPAIR;
       const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
       const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
@@ -689,16 +690,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
 // ---------------------------------------------------------------- launcher --
 
-template <int DK, int DVS, int C, typename In>
-hipError_t launch_one(const ChunkParams& cp, int nwg, bool chan, hipStream_t s) {
+template <int DK, int DVS, int C, typename In, int DECAY>
+hipError_t launch_one(const ChunkParams& cp, int nwg, hipStream_t s) {
   using OpT = typename OpOf<In>::T;
   using L = ChunkLayout<DK, DVS, C, sizeof(OpT)>;
-  const size_t lds = L::bytes(chan);
-  if (lds > kMaxLds) return hipErrorInvalidConfiguration;
-  if constexpr (L::bytes(false) > kMaxLds) {
+  constexpr bool chan = DECAY == DECAY_CHANNEL;
+  if constexpr (L::bytes(chan) > kMaxLds) {
     return hipErrorInvalidConfiguration;   // never instantiated as a kernel
   } else {
-    auto fn = chunked_kernel<DK, DVS, C, In>;
+    auto fn = chunked_kernel<DK, DVS, C, In, DECAY>;
     static bool attr_set = false;   // benign race: the attribute call is idempotent
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -707,7 +707,7 @@ hipError_t launch_one(const ChunkParams& cp, int nwg, bool chan, hipStream_t s) 
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    fn<<<dim3(nwg), dim3(kThreads), lds, s>>>(cp);
+    fn<<<dim3(nwg), dim3(kThreads), L::bytes(chan), s>>>(cp);
     return hipGetLastError();
   }
 }
@@ -725,11 +725,10 @@ size_t lds_bytes(int DK, int DVS, int C, bool chan) {
   return 0;
 }
 
-template <typename In>
-hipError_t launch_any(int DK, int DVS, int C, const ChunkParams& cp, int nwg, bool chan,
-                      hipStream_t s) {
+template <typename In, int DECAY>
+hipError_t launch_any(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s) {
 #define KDA_C(dk, dvs, c) \
-  if (DK == dk && DVS == dvs && C == c) return launch_one<dk, dvs, c, In>(cp, nwg, chan, s);
+  if (DK == dk && DVS == dvs && C == c) return launch_one<dk, dvs, c, In, DECAY>(cp, nwg, s);
 #define KDA_C2(dk, c) KDA_C(dk, 16, c) KDA_C(dk, 32, c) KDA_C(dk, 64, c)
 #define KDA_C3(c) KDA_C2(32, c) KDA_C2(64, c) KDA_C2(128, c)
   KDA_C3(16) KDA_C3(32) KDA_C3(64)
@@ -739,9 +738,16 @@ hipError_t launch_any(int DK, int DVS, int C, const ChunkParams& cp, int nwg, bo
   return hipErrorInvalidValue;
 }
 
-// Defined in chunked_bf16.hip / chunked_f32.hip.
-hipError_t launch_bf16(int DK, int DVS, int C, const ChunkParams& cp, int nwg, bool chan, hipStream_t s);
-hipError_t launch_f32(int DK, int DVS, int C, const ChunkParams& cp, int nwg, bool chan, hipStream_t s);
+// One instantiation unit per (activation dtype, decay kind): chunked_<dtype>_d<kind>.hip.
+#define KDA_DECLARE_LAUNCH(name) \
+  hipError_t name(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s);
+KDA_DECLARE_LAUNCH(launch_bf16_d0)
+KDA_DECLARE_LAUNCH(launch_bf16_d1)
+KDA_DECLARE_LAUNCH(launch_bf16_d2)
+KDA_DECLARE_LAUNCH(launch_f32_d0)
+KDA_DECLARE_LAUNCH(launch_f32_d1)
+KDA_DECLARE_LAUNCH(launch_f32_d2)
+#undef KDA_DECLARE_LAUNCH
 
 }  // namespace chunked
 }  // namespace kda

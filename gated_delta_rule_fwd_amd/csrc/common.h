@@ -34,6 +34,7 @@ template <typename In> struct act;
 template <> struct act<float> {
   static constexpr int kVec = 4;  // elements per 16-byte load
   __device__ static float load1(const float* p) { return *p; }
+  __device__ static float cvt(float x) { return x; }
   __device__ static void load_vec(const float* p, float (&out)[4]) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(p);
     out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
@@ -42,6 +43,7 @@ template <> struct act<float> {
 template <> struct act<bf16_t> {
   static constexpr int kVec = 8;
   __device__ static float load1(const bf16_t* p) { return bf16_to_f32(p->bits); }
+  __device__ static float cvt(bf16_t x) { return bf16_to_f32(x.bits); }
   __device__ static void load_vec(const bf16_t* p, float (&out)[8]) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

@@ -156,6 +156,38 @@ __host__ __device__ constexpr int pair_j(int n) { int i = 0; while (n > i) { n -
 
 // ------------------------------------------------------------------ kernel --
 
+// Transposed 4 x fp16 read (gfx950 ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane j supplies the address of an 8-byte row piece E_j; lane
+// i = 4a + e receives (E_a[e], E_{a+4}[e], E_{a+8}[e], E_{a+12}[e]).
+__device__ __forceinline__ f16x4 ld_tr16(const _Float16* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+// A operand of a product contracting over tokens, read from a row-major
+// [tokens][channels] tile: lane (g, l16) gets channel c0 + l16 at tokens
+// k0 + 4g + j and k0 + 16 + 4g + j (the "perm" k map).  Without `hi` the
+// tile ends at k0 + 16 and the second half is zero.
+__device__ __forceinline__ f16x8 ld_tokens(const _Float16* tile, int ld, int k0, int c0,
+                                           int g, int l16, bool hi) {
+  const _Float16* p = tile + (k0 + 4 * g + (l16 >> 2)) * ld + c0 + 4 * (l16 & 3);
+  const f16x4 lo = ld_tr16(p);
+  const f16x4 up = hi ? ld_tr16(p + 16 * ld) : f16x4{0, 0, 0, 0};
+  return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ Mma<float>::frag ld_tokens(const float* tile, int ld, int k0, int c0,
+                                                      int g, int l16, bool hi) {
+  Mma<float>::frag f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.lo[j] = tile[(k0 + 4 * g + j) * ld + c0 + l16];
+    f.hi[j] = hi ? tile[(k0 + 16 + 4 * g + j) * ld + c0 + l16] : 0.f;
+  }
+  return f;
+}
+
 template <int DK, int DVS, int C, typename In, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   using OpT = typename OpOf<In>::T;
@@ -174,18 +206,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
   constexpr int NPAIR = NB * (NB + 1) / 2;
   constexpr int NOWN = DVS / 16;             // waves that own state columns
+  constexpr int NH = (NB + 1) / 2;           // 32-wide k steps over the chunk's tokens
   static_assert(LPR <= 64 && (64 % LPR) == 0, "q/k rows must pack into waves");
   static_assert(LPRv >= 1 && (64 % LPRv) == 0, "v rows must pack into waves");
   static_assert(DVS % 16 == 0 && NOWN <= kWaves, "slice width");
+  // one kernel per decay kind keeps the chunk loop small enough for the
+  // instruction cache
+  constexpr bool chan = DECAY == DECAY_CHANNEL;
+  constexpr bool headdecay = DECAY == DECAY_HEAD;
 
   extern __shared__ __align__(256) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int T = p.T, H = p.H, DV = p.DV;
-  // one kernel per decay kind keeps the chunk loop small enough for the
-  // instruction cache
-  constexpr bool chan = DECAY == DECAY_CHANNEL;
-  constexpr bool headdecay = DECAY == DECAY_HEAD;
 
   // Workgroup -> (head, slice).  With xcd_map the slices of one head get ids
   // that are equal mod 8, i.e. run on the same XCD and share its L2.
@@ -206,8 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
   OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
   OpT* sK = reinterpret_cast<OpT*>(smem + L::oK);
-  OpT* sKT = reinterpret_cast<OpT*>(smem + L::oKT);
-  OpT* sVT = reinterpret_cast<OpT*>(smem + L::oVT);
+  OpT* sV = reinterpret_cast<OpT*>(smem + L::oV);
   OpT* sP = reinterpret_cast<OpT*>(smem + L::oP);
   float* sAm = reinterpret_cast<float*>(smem + L::oAM);
   OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
@@ -215,6 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   OpT* sTu = reinterpret_cast<OpT*>(smem + L::oTu);
   OpT* sKb = reinterpret_cast<OpT*>(smem + L::oRA);
   KinvT* sKinv = reinterpret_cast<KinvT*>(smem + L::oKinv);
+  OpT* sKF = reinterpret_cast<OpT*>(smem + L::oKF(true));
   float* sv = reinterpret_cast<float*>(smem + L::oVec(chan));
   float* s_bt = sv;
   float* s_Gi = sv + C;
@@ -232,10 +265,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
   // Zero all of LDS once: padding columns and never-written blocks read as zero.
   {
-    constexpr int kMaxVec = static_cast<int>(L::bytes(true) / 16);
-    const int nvec = static_cast<int>(L::bytes(chan) / 16);
+    constexpr int nvec = static_cast<int>(L::bytes(chan) / 16);
     uint4* z = reinterpret_cast<uint4*>(smem);
-    for (int i = tid; i < nvec && i < kMaxVec; i += kThreads) z[i] = uint4{0, 0, 0, 0};
+    for (int i = tid; i < nvec; i += kThreads) z[i] = uint4{0, 0, 0, 0};
   }
 
   const In* gq = static_cast<const In*>(p.q);
@@ -283,6 +315,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   auto unpack = [&](const uint4& raw, float (&x)[V]) {
     act<In>::load_vec(reinterpret_cast<const In*>(&raw), x);
   };
+  auto store_row = [&](OpT* dst, const float (&x)[V]) {
+    if constexpr (sizeof(OpT) == 2) {
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+      *reinterpret_cast<f16x8*>(dst) = hv;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+    }
+  };
 
   // ---- the state slice: owner wave w keeps value columns n0 + 16w .. +15 ----
   const bool owner = wave < NOWN;
@@ -306,34 +348,31 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
     const int t0 = ch * C;
     const int Lc = min(C, T - t0);
 
-    // ============ phase 1: normalise and stage the chunk, gates ============
+    // ============ phase 1: stage the chunk: normalised rows, gates ============
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int r = pp * RPP + tid / LPR, seg = tid % LPR;
       float qv[V], kv[V];
       unpack(rq[pp], qv);
       unpack(rk[pp], kv);
-      float sq = 0.f, sk = 0.f;
+      float fq = p.scale, fk = 1.f;
+      if (p.l2norm) {
+        // row norms: the LPR lanes of a row are consecutive, reduce with DPP moves
+        float sq = 0.f, sk = 0.f;
 #pragma unroll
-      for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-      sq = group_sum<LPR>(sq);
-      sk = group_sum<LPR>(sk);
-      const float qn = (p.l2norm ? inv_norm(sq) : 1.f) * p.scale;
-      const float kn = p.l2norm ? inv_norm(sk) : 1.f;
+        for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
+        fq *= inv_norm(dpp_group_sum<LPR>(sq));
+        fk = inv_norm(dpp_group_sum<LPR>(sk));
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) { qv[e] *= fq; kv[e] *= fk; }
       if (r < C) {
-        OpT* qrow = sQ + r * L::LDK + seg * V;
-        OpT* krow = sK + r * L::LDK + seg * V;
-#pragma unroll
-        for (int e = 0; e < V; ++e) { qrow[e] = (OpT)(qv[e] * qn); krow[e] = (OpT)(kv[e] * kn); }
-        if (!chan) {
-#pragma unroll
-          for (int e = 0; e < V; ++e) sKT[(seg * V + e) * L::LC + r] = (OpT)(kv[e] * kn);
-        } else {
+        store_row(sQ + r * L::LDK + seg * V, qv);
+        store_row(sK + r * L::LDK + seg * V, kv);
+        if (chan) {
           float gvv[V];
           unpack(rg[pp], gvv);
-          OpT* grow = sGst + r * DK + seg * V;
-#pragma unroll
-          for (int e = 0; e < V; ++e) grow[e] = (OpT)gvv[e];
+          store_row(sGst + r * DK + seg * V, gvv);
         }
       }
     }
@@ -343,8 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
       if (r < C) {
         float vv[V];
         unpack(rv[pp], vv);
-#pragma unroll
-        for (int e = 0; e < V; ++e) sVT[(seg * V + e) * L::LC + r] = (OpT)vv[e];
+        store_row(sV + r * L::LDV + seg * V, vv);
       }
     }
     if (wave == 0) {
@@ -376,8 +414,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
     lds_barrier();
 
     if (chan) {
-      // (1b) per (16-token block, key channel): exp(g) products referenced to
-      // the block start (prefix) and end (suffix); all of them are <= 1.
+      // (1b) per (16-token block, key channel): normalised q, k times exp(g)
+      // products referenced to the block start (prefix) and end (suffix);
+      // all of them are <= 1.
       constexpr int NT = (NB * DK + kThreads - 1) / kThreads;
       uint32_t kin16[NT][8];   // bf16 copy of the inverse-prefix operand, two per register
 #pragma unroll
@@ -427,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
       }
       lds_barrier();
       const bool steep = *s_flag != 0;
-      // (1c) chunk-level factors and the transposed operand of the state update
+      // (1c) chunk-level factors and k decayed to the chunk end
 #pragma unroll
       for (int it = 0; it < NT; ++it) {
         const int task = tid + it * kThreads;
@@ -453,15 +492,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
           float dd = 1.f;
 #pragma unroll
           for (int j = NB - 1; j >= 0; --j) {    // D[i][j] = prod_{j < m < i} tau_m
-            if (j < i - 1) {
-              s_D[L::dslot(i, j) * DK + c] = dd;
-            }
+            if (j < i - 1) s_D[L::dslot(i, j) * DK + c] = dd;
             if (j < i) dd *= s_tau[j * DK + c];
           }
-          OpT* kft = sKT + c * L::LC + 16 * i;   // k * exp(G_last - G), transposed
 #pragma unroll
-          for (int t = 0; t < 16; ++t)
-            kft[t] = (OpT)(static_cast<float>(sKb[(16 * i + t) * L::LDK + c]) * ca);
+          for (int t = 0; t < 16; ++t) {
+            const int r = 16 * i + t;
+            sKF[r * L::LDK + c] = (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
+          }
         }
       }
       lds_barrier();
@@ -475,8 +513,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
       f32x4 acc = {0, 0, 0, 0};
       if (!chan) {
         const OpT* brow = sK + (16 * j + l16) * L::LDK;
+        typename M::frag fa[NKP], fb[NKP];
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(arow, 32 * m, g), M::ld_cont(brow, 32 * m, g));
+        for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) M::mma(acc, fa[m], fb[m]);
       } else if (i == j) {
         if constexpr (sizeof(OpT) == 2) {
           const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
@@ -525,20 +566,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
     // ============ phase 3: T = (I + A)^-1, stored as T (fp32) and T diag(beta) ============
     if (wave == 0) {
-      // diagonal 16x16 blocks: lane -> (block, column), forward substitution
+      // diagonal 16x16 blocks, lane -> (block, column): right-looking
+      // substitution, so each step leaves only independent updates behind
       const int i = g, jc = l16;
       if (i < NB) {
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float* arow = sAm + (16 * i + r) * L::LF + 16 * i;
-          float a0 = (r == jc) ? 1.f : 0.f, a1 = 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+        const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
 #pragma unroll
-          for (int s = 0; s < r; ++s) {
-            if (s & 1) a1 -= arow[s] * x[s];
-            else a0 -= arow[s] * x[s];
-          }
-          x[r] = a0 + a1;
+        for (int s = 0; s < 15; ++s) {
+#pragma unroll
+          for (int r = s + 1; r < 16; ++r) x[r] -= ablk[r * L::LF + s] * x[s];
         }
         const float bj = s_bt[16 * i + jc];
 #pragma unroll
@@ -547,19 +586,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
           sTu[(16 * i + r) * L::LC + 16 * i + jc] = (OpT)(x[r] * bj);
         }
       }
-    } else {
-      // zero T diag(beta) above the block diagonal (and past the chunk for C = 16)
+    } else if (chan) {
+      // T diag(beta) shares its LDS with the Gram factors: zero it above the
+      // block diagonal (and past the chunk for C = 16)
       for (int idx = tid - 64; idx < C * L::NCOL; idx += kThreads - 64) {
         const int r = idx / L::NCOL, s = idx % L::NCOL;
         if ((s >> 4) > (r >> 4)) sTu[r * L::LC + s] = (OpT)0.f;
       }
-      if (chan) {
+      {
         // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)
-        for (int idx = tid - 64; idx < C * DK; idx += kThreads - 64) {
-          const int r = idx / DK, c = idx % DK;
-          const float cb = s_Cb[(r >> 4) * DK + c];
-          sK[r * L::LDK + c] = (OpT)(static_cast<float>(sK[r * L::LDK + c]) * cb);
-          sQ[r * L::LDK + c] = (OpT)(static_cast<float>(sQ[r * L::LDK + c]) * cb);
+        constexpr int VE = sizeof(OpT) == 2 ? 8 : 4;
+        for (int idx = tid - 64; idx < C * DK / VE; idx += kThreads - 64) {
+          const int r = idx / (DK / VE), c = (idx % (DK / VE)) * VE;
+          const float* cb = s_Cb + (r >> 4) * DK + c;
+          OpT* kp = sK + r * L::LDK + c;
+          OpT* qp = sQ + r * L::LDK + c;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            kp[e] = (OpT)(static_cast<float>(kp[e]) * cb[e]);
+            qp[e] = (OpT)(static_cast<float>(qp[e]) * cb[e]);
+          }
         }
       }
     }
@@ -598,26 +644,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
       typename M::frag Sf[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
-      // X = V - (K * exp(Gx)) S0, one 16-token tile at a time
+      // X = V - diag(sk exp(Gx)) K S0, one 16-token tile at a time
       f32x4 Xl[NB];
-      const OpT* vrow = sVT + (16 * wave + l16) * L::LC;
+      const OpT* vcol = sV + 16 * wave + l16;
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         f32x4 acc = {0, 0, 0, 0};
         const OpT* krow = sK + (16 * rt + l16) * L::LDK;
+        typename M::frag fk[NKP];
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_perm(krow, 32 * m, g), Sf[m]);
+        for (int m = 0; m < NKP; ++m) fk[m] = M::ld_perm(krow, 32 * m, g);
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) M::mma(acc, fk[m], Sf[m]);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int r = 16 * rt + 4 * g + jj;
-          const float ks = headdecay ? acc[jj] * s_eGx[r] : acc[jj];
-          Xl[rt][jj] = static_cast<float>(vrow[r]) - ks;
+          float ks = acc[jj];
+          if (headdecay) ks *= s_eGx[r];
+          Xl[rt][jj] = static_cast<float>(vcol[r * L::LDV]) - ks;
         }
       }
       // D = T diag(beta) X
-      typename M::frag Xf[(NB + 1) / 2];
+      typename M::frag Xf[NH];
 #pragma unroll
-      for (int m = 0; m < (NB + 1) / 2; ++m)
+      for (int m = 0; m < NH; ++m)
         Xf[m] = M::from_acc(Xl[2 * m], 2 * m + 1 < NB ? Xl[2 * m + 1] : f32x4{0, 0, 0, 0});
       f32x4 Dl[NB];
 #pragma unroll
@@ -627,17 +677,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 #pragma unroll
         for (int m = 0; m <= rt / 2; ++m) M::mma(Dl[rt], M::ld_perm(urow, 32 * m, g), Xf[m]);
       }
-      typename M::frag Df[(NB + 1) / 2];
+      typename M::frag Df[NH];
 #pragma unroll
-      for (int m = 0; m < (NB + 1) / 2; ++m)
+      for (int m = 0; m < NH; ++m)
         Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
-      // O^T = S0^T (Q * exp(G))^T + D^T P^T, one 16-token tile at a time
+      // O^T = S0^T (diag(sq exp(G)) Q)^T + D^T P^T, one 16-token tile at a time
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const OpT* qrow = sQ + (16 * rt + l16) * L::LDK;
+        typename M::frag fq[NKP];
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) fq[m] = M::ld_perm(qrow, 32 * m, g);
         f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, Sf[m], M::ld_perm(qrow, 32 * m, g));
+        for (int m = 0; m < NKP; ++m) M::mma(acc, Sf[m], fq[m]);
         const int r = 16 * rt + l16;
         if (headdecay) acc *= s_eG[r];
         const OpT* prow = sP + r * L::LC;
@@ -648,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
           *reinterpret_cast<f32x4*>(op) = acc;
         }
       }
-      // S <- exp(G_last) S0 + KY D', KY = (K * exp(G_last - G))^T
+      // S <- exp(G_last) S0 + KY D', KY = (diag(sk exp(G_last - G)) K)^T
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
         if (chan) {
@@ -665,14 +718,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
           for (int jj = 0; jj < 4; ++jj) Dl[st][jj] *= s_eF[16 * st + 4 * g + jj];
         }
 #pragma unroll
-        for (int m = 0; m < (NB + 1) / 2; ++m)
+        for (int m = 0; m < NH; ++m)
           Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
       }
+      const OpT* KY = chan ? sKF : sK;
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
-        const OpT* arow = sKT + (16 * t + l16) * L::LC;
 #pragma unroll
-        for (int m = 0; m < (NB + 1) / 2; ++m) M::mma(S[t], M::ld_perm(arow, 32 * m, g), Df[m]);
+        for (int m = 0; m < NH; ++m)
+          M::mma(S[t], ld_tokens(KY, L::LDK, 32 * m, 16 * t, g, l16, 2 * m + 1 < NB), Df[m]);
       }
     }
     lds_barrier();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -60,6 +62,31 @@ template <int width>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
   for (int off = width / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Sum over aligned groups of W consecutive lanes with DPP lane moves (no LDS
+// traffic), the result in every lane of the group.  W = 4, 8, 16, 32 or 64.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+  auto mov = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  using xor1 = std::integral_constant<int, 0xB1>;   // quad_perm [1,0,3,2]
+  using xor2 = std::integral_constant<int, 0x4E>;   // quad_perm [2,3,0,1]
+  using hmir = std::integral_constant<int, 0x141>;  // row_half_mirror (within 8)
+  using ror4 = std::integral_constant<int, 0x124>;  // row_ror:4 (within 16)
+  using ror8 = std::integral_constant<int, 0x128>;  // row_ror:8 (within 16)
+  if constexpr (W == 8) x += mov(x, hmir{});
+  if constexpr (W >= 16) {
+    x += mov(x, ror8{});
+    x += mov(x, ror4{});
+  }
+  x += mov(x, xor2{});
+  x += mov(x, xor1{});
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
 

@@ -80,7 +80,7 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
   if (st != KDA_OK) return st;
   if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
-  if (kda::chunked_lds_bytes(DK, DV, chunk_size, dtype) == 0) return KDA_ERR_UNSUPPORTED;
+  if (kda::chunked_lds_bytes(DK, DV, chunk_size, dtype, decay_kind) == 0) return KDA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,

@@ -1,14 +1,20 @@
-// Host planning of the fused chunked forward: value-slice width, grid, and
-// dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
+// Host planning of the chunked forward: value-slice width, grids, the
+// workspace that carries the per-chunk records from the prep kernel to the
+// state kernel, and dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "chunked_impl.h"
 
 namespace kda {
 namespace {
 
-using chunked::ChunkParams;
+using chunked::PrepParams;
+using chunked::StateParams;
 
-// Pick the value-slice width: enough workgroups to cover the 256 CUs, no
-// wider than 64 columns, and an LDS plan that fits one CU.
+// Pick the value-slice width of the state kernel: enough workgroups to cover
+// the 256 CUs, no wider than 64 columns, and LDS plans that fit one CU.
 struct Plan { int dvs; size_t lds; };
 
 Plan plan_for(int B, int H, int DK, int DV, int C, int dtype, bool chan) {
@@ -23,36 +29,79 @@ Plan plan_for(int B, int H, int DK, int DV, int C, int dtype, bool chan) {
   return Plan{0, 0};
 }
 
+// Workspace: one device buffer per (device, stream), grown on demand and kept
+// until the process ends.  Work on one stream runs in order, so a stream's
+// buffer is never used by two calls at once; calls on different streams use
+// different buffers.
+hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& ent = cache[{dev, s}];
+  if (ent.second < bytes) {
+    if (ent.first) {
+      // the old buffer may still be read by this stream's earlier work
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return e;
+      e = hipFree(ent.first);
+      ent = {nullptr, 0};
+      if (e != hipSuccess) return e;
+    }
+    const size_t want = bytes + bytes / 4;   // headroom for nearby sizes
+    e = hipMalloc(&ent.first, want);
+    if (e != hipSuccess) {
+      ent = {nullptr, 0};
+      return e;
+    }
+    ent.second = want;
+  }
+  *out = ent.first;
+  return hipSuccess;
+}
+
 }  // namespace
 
-size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype) {
-  // the largest plan over decay kinds at the smallest grid (B = H = 1)
-  const Plan a = plan_for(1, 1, DK, DV, chunk, dtype, true);
-  const Plan b = plan_for(1, 1, DK, DV, chunk, dtype, false);
-  if (a.dvs == 0 || b.dvs == 0) return 0;
-  return a.lds > b.lds ? a.lds : b.lds;
+size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind) {
+  // the plan at the smallest grid (B = H = 1) is the widest slice
+  const Plan a = plan_for(1, 1, DK, DV, chunk, dtype, decay_kind == DECAY_CHANNEL);
+  return a.dvs == 0 ? 0 : a.lds;
 }
 
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const bool chan = a.decay_kind == DECAY_CHANNEL;
   const Plan pl = plan_for(a.B, a.H, a.DK, a.DV, a.chunk, a.dtype, chan);
   if (pl.dvs == 0) return hipErrorInvalidConfiguration;
-  ChunkParams cp;
-  cp.q = a.q; cp.k = a.k; cp.v = a.v; cp.beta = a.beta; cp.decay = a.decay;
-  cp.init = a.init; cp.o = a.o; cp.state = a.state;
-  cp.T = a.T; cp.H = a.H; cp.DV = a.DV;
-  cp.nsl = a.DV / pl.dvs;
-  cp.decay_kind = a.decay_kind;
-  cp.l2norm = a.l2norm;
-  cp.scale = a.scale;
+  const int nchunks = (a.T + a.chunk - 1) / a.chunk;
   const int nheads = a.B * a.H;
-  cp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
-  const int nwg = nheads * cp.nsl;
-  using LaunchFn = hipError_t (*)(int, int, int, const ChunkParams&, int, hipStream_t);
+  const size_t rec = a.dtype == 0 ? chunked::record_bytes<4>(a.DK, a.chunk, chan)
+                                  : chunked::record_bytes<2>(a.DK, a.chunk, chan);
+  if (rec == 0) return hipErrorInvalidConfiguration;
+  void* ws = nullptr;
+  hipError_t e = workspace(s, rec * nchunks * static_cast<size_t>(nheads), &ws);
+  if (e != hipSuccess) return e;
+
+  PrepParams pp;
+  pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
+  pp.ws = static_cast<unsigned char*>(ws);
+  pp.T = a.T; pp.H = a.H; pp.nchunks = nchunks; pp.l2norm = a.l2norm; pp.scale = a.scale;
+
+  StateParams sp;
+  sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
+  sp.init = a.init; sp.o = a.o; sp.state = a.state;
+  sp.T = a.T; sp.H = a.H; sp.DV = a.DV; sp.nchunks = nchunks;
+  sp.nsl = a.DV / pl.dvs;
+  sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
+
+  using LaunchFn = hipError_t (*)(int, int, int, const PrepParams&, int, const StateParams&, int,
+                                  hipStream_t);
   static const LaunchFn table[2][3] = {
       {chunked::launch_f32_d0, chunked::launch_f32_d1, chunked::launch_f32_d2},
       {chunked::launch_bf16_d0, chunked::launch_bf16_d1, chunked::launch_bf16_d2}};
-  return table[a.dtype == 0 ? 0 : 1][a.decay_kind](a.DK, pl.dvs, a.chunk, cp, nwg, s);
+  return table[a.dtype == 0 ? 0 : 1][a.decay_kind](a.DK, pl.dvs, a.chunk, pp, nheads * nchunks,
+                                                   sp, nheads * sp.nsl, s);
 }
 
 }  // namespace kda

@@ -1,12 +1,13 @@
-// Instantiations of the fused chunked kernel: f32 activations, decay kind 2
+// Instantiations of the chunked kernels: f32 activations, decay kind 2
 // (0 none, 1 per head, 2 per key channel).
 #include "chunked_impl.h"
 
 namespace kda {
 namespace chunked {
 
-hipError_t launch_f32_d2(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s) {
-  return launch_any<float, 2>(DK, DVS, C, cp, nwg, s);
+hipError_t launch_f32_d2(int DK, int DVS, int C, const PrepParams& pp, int nwg_prep,
+                          const StateParams& sp, int nwg_state, hipStream_t s) {
+  return launch_any<float, 2>(DK, DVS, C, pp, nwg_prep, sp, nwg_state, s);
 }
 
 }  // namespace chunked

@@ -1,4 +1,4 @@
-// Fused chunked forward of the gated delta rule on gfx950 (kernel template).
+// Chunked forward of the gated delta rule on gfx950 (kernel templates).
 //
 // The recurrence (ejkernel kda, core recurrence) is computed "parallel within
 // chunks, sequential across chunks" (ejkernel kda, Algorithm Modes) in the WY
@@ -16,13 +16,18 @@
 // (D is the WY form U - W S0 with U = T diag(beta) V and W = T diag(beta)
 // (K * exp(Gx)), associated so that W is never formed.)
 //
-// One workgroup owns one (batch, head, slice of DVS value columns) and walks
-// all chunks of its sequence.  The columns of S are independent, so each of
-// its DVS/16 "owner" waves keeps 16 columns of S in MFMA accumulators for the
-// whole sequence; the chunk-shared work (normalisation, gates, A, P, T) is
-// spread over all 4 waves and recomputed by every slice of a head.  Only
-// q, k, v, beta, decay (read once) and o, the final state (written once)
-// touch HBM.
+// Two kernels on the caller's stream:
+//
+//  * prep_kernel, one workgroup per (sequence, head, chunk), all chunks in
+//    parallel: normalisation, gate cumsums, A and P on MFMA, the inverse, and
+//    the decayed operands.  It writes one record per chunk to a workspace:
+//    Q, K (and for per-channel decay K * exp(G_last - G)), T diag(beta), P and
+//    the per-token / per-channel decay factors.
+//  * state_kernel, one workgroup per (sequence, head, slice of DVS value
+//    columns), walks the chunks in order.  Its DVS/16 "owner" waves keep 16
+//    columns of S each in MFMA accumulators for the whole sequence; per chunk
+//    the workgroup stages the record into LDS (prefetched into registers one
+//    chunk ahead) and the owner waves form D, the output rows and the new state.
 //
 // MFMA: v_mfma_f32_16x16x32_f16 for bf16 activations (q, k normalised and v
 // rounded once to fp16; derived operands rounded once to fp16) and
@@ -143,18 +148,22 @@ __device__ __forceinline__ void mma_diag_bf16(f32x4& acc, const f16x8& a_f16,
 template <typename In> struct OpOf { using T = _Float16; using KinvT = uint16_t; };
 template <> struct OpOf<float> { using T = float; using KinvT = float; };
 
-struct ChunkParams {
-  const void* q; const void* k; const void* v; const void* beta; const void* decay;
-  const float* init; float* o; float* state;
-  int T, H, DV, nsl, xcd_map, decay_kind, l2norm;
+struct PrepParams {
+  const void* q; const void* k; const void* beta; const void* decay;
+  unsigned char* ws;     // records, [B*H][nchunks]
+  int T, H, nchunks, l2norm;
   float scale;
+};
+
+struct StateParams {
+  const void* v; const unsigned char* ws;
+  const float* init; float* o; float* state;
+  int T, H, DV, nchunks, nsl, xcd_map;
 };
 
 // Lower-triangular block pair (i, j), j <= i, of pair index n.
 __host__ __device__ constexpr int pair_i(int n) { int i = 0; while (n > i) { n -= i + 1; ++i; } return i; }
 __host__ __device__ constexpr int pair_j(int n) { int i = 0; while (n > i) { n -= i + 1; ++i; } return n; }
-
-// ------------------------------------------------------------------ kernel --
 
 // Transposed 4 x fp16 read (gfx950 ds_read_b64_tr_b16).  Within each group of
 // 16 lanes, lane j supplies the address of an 8-byte row piece E_j; lane
@@ -188,32 +197,423 @@ __device__ __forceinline__ Mma<float>::frag ld_tokens(const float* tile, int ld,
   return f;
 }
 
-template <int DK, int DVS, int C, typename In, int DECAY>
-__global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
+// 16 bytes of operands (8 fp16 or 4 fp32) from fp32 values.
+template <typename OpT, int N>
+__device__ __forceinline__ void store16(OpT* dst, const float (&x)[N]) {
+  if constexpr (sizeof(OpT) == 2) {
+    static_assert(N == 8, "8 fp16 per 16 bytes");
+    f16x8 hv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+    *reinterpret_cast<f16x8*>(dst) = hv;
+  } else {
+    static_assert(N == 4, "4 fp32 per 16 bytes");
+    *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+  }
+}
+
+// ------------------------------------------------------------- prep kernel --
+
+template <int DK, int C, typename In, int DECAY>
+__global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
-  using L = ChunkLayout<DK, DVS, C, sizeof(OpT)>;
+  constexpr bool chan = DECAY == DECAY_CHANNEL;
+  constexpr bool headdecay = DECAY == DECAY_HEAD;
+  using L = PrepLayout<DK, C, sizeof(OpT)>;
+  using R = RecLayout<DK, C, sizeof(OpT), chan>;
   constexpr int NB = L::NB;
   constexpr int V = act<In>::kVec;           // activation elements per 16-byte load
+  static_assert(V * sizeof(OpT) == 16, "one 16-byte load makes one 16-byte operand store");
   constexpr int LPR = DK / V;                // lanes per q/k row
   constexpr int RPP = kThreads / LPR;        // q/k rows per load pass
   constexpr int NP = (C + RPP - 1) / RPP;    // q/k load passes
-  constexpr int LPRv = DVS / V;
+  constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
+  constexpr int NPAIR = NB * (NB + 1) / 2;
+  static_assert(LPR <= 64 && (64 % LPR) == 0, "q/k rows must pack into waves");
+
+  extern __shared__ __align__(256) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int T = p.T, H = p.H;
+  const int ch = blockIdx.x % p.nchunks, head = blockIdx.x / p.nchunks;
+  const int b = head / H, h = head % H;
+  const int t0 = ch * C;
+  const int Lc = min(C, T - t0);
+  const long tok0 = static_cast<long>(b) * T + t0;   // first token of the chunk
+  unsigned char* rec = p.ws + (static_cast<size_t>(head) * p.nchunks + ch) * R::bytes;
+  OpT* rQ = reinterpret_cast<OpT*>(rec + R::oQ);
+  OpT* rK = reinterpret_cast<OpT*>(rec + R::oK);
+  OpT* rF = reinterpret_cast<OpT*>(rec + R::oF);
+  float* rvec = reinterpret_cast<float*>(rec + R::oVec);
+
+  OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
+  OpT* sK = reinterpret_cast<OpT*>(smem + L::oK);
+  OpT* sP = reinterpret_cast<OpT*>(smem + L::oP);
+  float* sAm = reinterpret_cast<float*>(smem + L::oAM);
+  OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
+  float* sTm = reinterpret_cast<float*>(smem + L::oRA(chan));
+  OpT* sKb = reinterpret_cast<OpT*>(smem + L::oRA(chan));
+  KinvT* sKinv = reinterpret_cast<KinvT*>(smem + L::oKinv(chan));
+  float* sv = reinterpret_cast<float*>(smem + L::oVec(chan));
+  float* s_bt = sv;
+  float* s_Gi = sv + C;
+  float* s_Ge = sv + 2 * C;
+  float* s_misc = sv + 3 * C;                  // [1] = steep-gate flag
+  int* s_flag = reinterpret_cast<int*>(s_misc + 1);
+  float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
+  float* s_Cb = s_tau + NB * DK;               // [NB][DK] decay of all earlier blocks
+  float* s_rsq = s_Cb + NB * DK;               // [NB][DK] 1/sqrt(block factor)
+  float* s_D = s_rsq + NB * DK;                // [ND][DK] decay strictly between blocks
+
+  const In* gq = static_cast<const In*>(p.q);
+  const In* gk = static_cast<const In*>(p.k);
+  const In* gb = static_cast<const In*>(p.beta);
+  const In* gg = static_cast<const In*>(p.decay);
+
+  // ============ phase 1: normalised q, k rows; gates ============
+  {
+    uint4 rq[NP], rk[NP], rg[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int r = pp * RPP + tid / LPR, seg = tid % LPR;
+      rq[pp] = rk[pp] = rg[pp] = uint4{0, 0, 0, 0};
+      if (r < Lc) {
+        const long off = ((tok0 + r) * H + h) * DK + seg * V;
+        rq[pp] = *reinterpret_cast<const uint4*>(gq + off);
+        rk[pp] = *reinterpret_cast<const uint4*>(gk + off);
+        if (chan) rg[pp] = *reinterpret_cast<const uint4*>(gg + off);
+      }
+    }
+    float bt = 0.f, G = 0.f;
+    if (wave == 0 && lane < Lc) {
+      const long off = (tok0 + lane) * H + h;
+      bt = act<In>::load1(gb + off);
+      if (headdecay) G = act<In>::load1(gg + off);
+    }
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int r = pp * RPP + tid / LPR, seg = tid % LPR;
+      float qv[V], kv[V];
+      act<In>::load_vec(reinterpret_cast<const In*>(&rq[pp]), qv);
+      act<In>::load_vec(reinterpret_cast<const In*>(&rk[pp]), kv);
+      float fq = p.scale, fk = 1.f;
+      if (p.l2norm) {
+        // row norms: the LPR lanes of a row are consecutive, reduce with DPP moves
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
+        fq *= inv_norm(dpp_group_sum<LPR>(sq));
+        fk = inv_norm(dpp_group_sum<LPR>(sk));
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) { qv[e] *= fq; kv[e] *= fk; }
+      if (r < C) {
+        store16<OpT>(sQ + r * L::LDK + seg * V, qv);
+        store16<OpT>(sK + r * L::LDK + seg * V, kv);
+        if (!chan) {   // final record operands already
+          store16<OpT>(rQ + r * DK + seg * V, qv);
+          store16<OpT>(rK + r * DK + seg * V, kv);
+        } else {
+          float gv[V];
+          act<In>::load_vec(reinterpret_cast<const In*>(&rg[pp]), gv);
+          store16<OpT>(sGst + r * DK + seg * V, gv);
+        }
+      }
+    }
+    if (wave == 0) {
+      // the scalar gate: lane r holds token r of the chunk (C <= 64)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(G, off, 64);
+        if (lane >= off) G += y;
+      }
+      float Gx = __shfl_up(G, 1, 64);
+      if (lane == 0) Gx = 0.f;
+      const float Glast = __shfl(G, 63, 64);
+      if (lane < C) {
+        s_bt[lane] = bt;
+        s_Gi[lane] = G;
+        s_Ge[lane] = Gx;
+        if (headdecay) {
+          rvec[R::vEG + lane] = __expf(G);
+          rvec[R::vEGx + lane] = __expf(Gx);
+          rvec[R::vEF + lane] = __expf(Glast - G);
+        }
+      }
+      if (lane == 0) {
+        if (headdecay) rvec[R::vMisc] = __expf(Glast);
+        *s_flag = 0;
+      }
+    }
+  }
+  lds_barrier();
+
+  if constexpr (chan) {
+    // (1b) per (16-token block, key channel): normalised q, k times exp(g)
+    // products referenced to the block start (prefix) and end (suffix);
+    // all of them are <= 1.
+    constexpr int NT = (NB * DK + kThreads - 1) / kThreads;
+    uint32_t kin16[NT][8];   // bf16 copy of the inverse-prefix operand, two per register
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int task = tid + it * kThreads;
+      if (task < NB * DK) {
+        const int i = task / DK, c = task % DK;
+        float a[16], kx[16], kin[16];
+        float pre = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = 16 * i + t;
+          a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
+          kx[t] = static_cast<float>(sK[r * L::LDK + c]);
+          const float qx = static_cast<float>(sQ[r * L::LDK + c]);
+          sK[r * L::LDK + c] = (OpT)(kx[t] * pre);          // Ka: exclusive prefix
+          pre *= a[t];
+          kin[t] = kx[t] / pre;                             // k / inclusive prefix
+          sQ[r * L::LDK + c] = (OpT)(qx * pre);             // Qa: inclusive prefix
+        }
+        float suf = 1.f;
+#pragma unroll
+        for (int t = 15; t >= 0; --t) {
+          sKb[(16 * i + t) * L::LDK + c] = (OpT)(kx[t] * suf);  // Kb: decay to block end
+          suf *= a[t];
+        }
+        s_tau[i * DK + c] = pre;   // whole-block factor
+        if constexpr (sizeof(OpT) == 2) {
+          // diagonal blocks pair a factor <= 1 with its inverse; balanced by
+          // sqrt(block factor) both stay within exp(+-8) for a block factor
+          // >= exp(-16), which fp16 holds
+          const float rs = sqrtf(pre);
+          s_rsq[i * DK + c] = 1.f / rs;
+#pragma unroll
+          for (int t = 0; t < 16; ++t)
+            *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            kin16[it][t] = static_cast<uint32_t>(f32_to_bf16(kin[2 * t])) |
+                           (static_cast<uint32_t>(f32_to_bf16(kin[2 * t + 1])) << 16);
+          if (pre < kSafeBlockDecay) *s_flag = 1;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = kin[t];
+        }
+      }
+    }
+    lds_barrier();
+    const bool steep = *s_flag != 0;
+    // (1c) chunk-level factors; k decayed to the chunk end goes to the record
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int task = tid + it * kThreads;
+      if (task < NB * DK) {
+        const int i = task / DK, c = task % DK;
+        const float tau = s_tau[i * DK + c];
+        if constexpr (sizeof(OpT) == 2) {
+          if (steep) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+              sKinv[(16 * i + t) * L::LDK + c] = static_cast<uint16_t>(kin16[it][t >> 1] >> (16 * (t & 1)));
+          }
+        }
+        float cb = 1.f, ca = 1.f;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float tj = s_tau[j * DK + c];
+          if (j < i) cb *= tj;
+          if (j > i) ca *= tj;
+        }
+        s_Cb[i * DK + c] = cb;
+        if (i == 0) rvec[R::vDecC + c] = ca * tau;
+        float dd = 1.f;
+#pragma unroll
+        for (int j = NB - 1; j >= 0; --j) {    // D[i][j] = prod_{j < m < i} tau_m
+          if (j < i - 1) s_D[L::dslot(i, j) * DK + c] = dd;
+          if (j < i) dd *= s_tau[j * DK + c];
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = 16 * i + t;
+          rF[r * DK + c] = (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
+  for (int job = wave; job < 2 * NPAIR; job += kWaves) {
+    const bool isP = job >= NPAIR;
+    const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
+    const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+    f32x4 acc = {0, 0, 0, 0};
+    if (!chan) {
+      const OpT* brow = sK + (16 * j + l16) * L::LDK;
+      typename M::frag fa[NKP], fb[NKP];
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) M::mma(acc, fa[m], fb[m]);
+    } else if (i == j) {
+      if constexpr (sizeof(OpT) == 2) {
+        const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
+        if (*s_flag == 0) {
+          const OpT* krh = reinterpret_cast<const OpT*>(krow);
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) {
+            auto fa = M::ld_cont(arow, 32 * m, g);
+            M::scale_cont(fa, s_rsq + i * DK, 32 * m, g);
+            M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) mma_diag_bf16(acc, M::ld_cont(arow, 32 * m, g), krow, 32 * m, g);
+        }
+      } else {
+        const OpT* krow = sKinv + (16 * j + l16) * L::LDK;
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(arow, 32 * m, g), M::ld_cont(krow, 32 * m, g));
+      }
+    } else {
+      const OpT* brow = sKb + (16 * j + l16) * L::LDK;
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) {
+        auto fa = M::ld_cont(arow, 32 * m, g);
+        if (i - j >= 2) M::scale_cont(fa, s_D + L::dslot(i, j) * DK, 32 * m, g);
+        M::mma(acc, fa, M::ld_cont(brow, 32 * m, g));
+      }
+    }
+    const int s = 16 * j + l16;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * i + 4 * g + jj;
+      if (!isP) {
+        float val = acc[jj] * s_bt[r];
+        if (headdecay) val *= __expf(s_Ge[r] - s_Gi[s]);
+        sAm[r * L::LF + s] = (i > j || s < r) ? val : 0.f;
+      } else {
+        float val = acc[jj];
+        if (headdecay) val *= __expf(s_Gi[r] - s_Gi[s]);
+        sP[r * L::LC + s] = (OpT)((i > j || s <= r) ? val : 0.f);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ============ phase 3: T = (I + A)^-1 (fp32) ============
+  if (wave == 0) {
+    // diagonal 16x16 blocks, lane -> (block, column): right-looking
+    // substitution, so each step leaves only independent updates behind
+    const int i = g, jc = l16;
+    if (i < NB) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+      const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
+#pragma unroll
+      for (int s = 0; s < 15; ++s) {
+#pragma unroll
+        for (int r = s + 1; r < 16; ++r) x[r] -= ablk[r * L::LF + s] * x[s];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];
+    }
+  } else {
+    // meanwhile the other waves write the finished record tiles
+    constexpr int VE = 16 / sizeof(OpT);
+    constexpr int RowV = C / VE;             // 16-byte pieces per P row
+    for (int idx = tid - 64; idx < C * RowV; idx += kThreads - 64) {
+      const int r = idx / RowV, s0 = (idx % RowV) * VE;
+      uint4 val = *reinterpret_cast<const uint4*>(sP + r * L::LC + s0);
+      if ((s0 >> 4) > (r >> 4)) val = uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4*>(rec + R::oP + (static_cast<size_t>(r) * C + s0) * sizeof(OpT)) = val;
+    }
+    if (chan) {
+      // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)
+      constexpr int RowK = DK / VE;
+      for (int idx = tid - 64; idx < C * RowK; idx += kThreads - 64) {
+        const int r = idx / RowK, c = (idx % RowK) * VE;
+        const float* cb = s_Cb + (r >> 4) * DK + c;
+        float kx[VE], qx[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          kx[e] = static_cast<float>(sK[r * L::LDK + c + e]) * cb[e];
+          qx[e] = static_cast<float>(sQ[r * L::LDK + c + e]) * cb[e];
+        }
+        store16<OpT>(rK + r * DK + c, kx);
+        store16<OpT>(rQ + r * DK + c, qx);
+      }
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int d = 1; d < NB; ++d) {
+    // blocks on diagonal d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, on waves 1..
+    const int j = wave - 1, i = j + d;
+    if (wave >= 1 && i < NB) {
+      f32x4 X = {0, 0, 0, 0};
+      for (int kb = j; kb < i; ++kb) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sAm + (16 * i + l16) * L::LF + 16 * kb + 4 * g);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float bv = sTm[(16 * kb + 4 * g + jj) * L::LF + 16 * j + l16];
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], bv, X, 0, 0, 0);
+        }
+      }
+      const f32x4 t4 = *reinterpret_cast<const f32x4*>(sTm + (16 * i + l16) * L::LF + 16 * i + 4 * g);
+      f32x4 Y = {0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[jj], X[jj], Y, 0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sTm[(16 * i + 4 * g + jj) * L::LF + 16 * j + l16] = -Y[jj];
+    }
+    lds_barrier();
+  }
+
+  // ============ record: T diag(beta), zero above the block diagonal ============
+  {
+    constexpr int VE = 16 / sizeof(OpT);
+    constexpr int RowV = C / VE;
+    for (int idx = tid; idx < C * RowV; idx += kThreads) {
+      const int r = idx / RowV, s0 = (idx % RowV) * VE;
+      float x[VE];
+      const bool upper = (s0 >> 4) > (r >> 4);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) x[e] = upper ? 0.f : sTm[r * L::LF + s0 + e] * s_bt[s0 + e];
+      store16<OpT>(reinterpret_cast<OpT*>(rec + R::oTu) + r * C + s0, x);
+    }
+  }
+}
+
+// ------------------------------------------------------------ state kernel --
+
+template <int DK, int DVS, int C, typename In, int DECAY>
+__global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
+  using OpT = typename OpOf<In>::T;
+  using M = Mma<OpT>;
+  constexpr bool chan = DECAY == DECAY_CHANNEL;
+  constexpr bool headdecay = DECAY == DECAY_HEAD;
+  using L = StateLayout<DK, DVS, C, sizeof(OpT), chan>;
+  using R = RecLayout<DK, C, sizeof(OpT), chan>;
+  constexpr int NB = L::NB;
+  constexpr int V = act<In>::kVec;
+  constexpr int VE = 16 / sizeof(OpT);       // operands per 16 bytes
+  constexpr int LPRv = DVS / V;              // lanes per value row
   constexpr int RPPv = kThreads / LPRv;
   constexpr int NPv = (C + RPPv - 1) / RPPv;
   constexpr int NKT = DK / 16;               // 16-row tiles of the state
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
-  constexpr int NPAIR = NB * (NB + 1) / 2;
   constexpr int NOWN = DVS / 16;             // waves that own state columns
   constexpr int NH = (NB + 1) / 2;           // 32-wide k steps over the chunk's tokens
-  static_assert(LPR <= 64 && (64 % LPR) == 0, "q/k rows must pack into waves");
+  // record pieces (16 bytes each) and their share per thread
+  constexpr int nT16 = static_cast<int>(R::kTile / 16), PT = (nT16 + kThreads - 1) / kThreads;
+  constexpr int nC16 = static_cast<int>(R::kCC / 16), PC = (nC16 + kThreads - 1) / kThreads;
+  constexpr int nE16 = R::kVecFloats * 4 / 16, PE = (nE16 + kThreads - 1) / kThreads;
+  constexpr int rowT16 = DK / VE, rowC16 = C / VE;
+  static_assert(R::kVecFloats % 4 == 0, "vector block in 16-byte pieces");
   static_assert(LPRv >= 1 && (64 % LPRv) == 0, "v rows must pack into waves");
   static_assert(DVS % 16 == 0 && NOWN <= kWaves, "slice width");
-  // one kernel per decay kind keeps the chunk loop small enough for the
-  // instruction cache
-  constexpr bool chan = DECAY == DECAY_CHANNEL;
-  constexpr bool headdecay = DECAY == DECAY_HEAD;
 
   extern __shared__ __align__(256) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -236,93 +636,105 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
   }
   const int b = head / H, h = head % H;
   const int n0 = slice * DVS;   // first value column of this slice
+  const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::bytes;
 
-  OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
-  OpT* sK = reinterpret_cast<OpT*>(smem + L::oK);
-  OpT* sV = reinterpret_cast<OpT*>(smem + L::oV);
-  OpT* sP = reinterpret_cast<OpT*>(smem + L::oP);
-  float* sAm = reinterpret_cast<float*>(smem + L::oAM);
-  OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
-  float* sTm = reinterpret_cast<float*>(smem + L::oRA);
-  OpT* sTu = reinterpret_cast<OpT*>(smem + L::oTu);
-  OpT* sKb = reinterpret_cast<OpT*>(smem + L::oRA);
-  KinvT* sKinv = reinterpret_cast<KinvT*>(smem + L::oKinv);
-  OpT* sKF = reinterpret_cast<OpT*>(smem + L::oKF(true));
-  float* sv = reinterpret_cast<float*>(smem + L::oVec(chan));
-  float* s_bt = sv;
-  float* s_Gi = sv + C;
-  float* s_Ge = sv + 2 * C;
-  float* s_eG = sv + 3 * C;
-  float* s_eGx = sv + 4 * C;
-  float* s_eF = sv + 5 * C;
-  float* s_misc = sv + 6 * C;                  // [0] = exp(G_last), [1] = steep-gate flag
-  int* s_flag = reinterpret_cast<int*>(s_misc + 1);
-  float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
-  float* s_Cb = s_tau + NB * DK;               // [NB][DK] decay of all earlier blocks
-  float* s_rsq = s_Cb + NB * DK;               // [NB][DK] 1/sqrt(block factor)
-  float* s_D = s_rsq + NB * DK;                // [ND][DK] decay strictly between blocks
-  float* s_decC = s_D + L::ND * DK;            // [DK] decay of the whole chunk
+  const OpT* sQ = reinterpret_cast<const OpT*>(smem + L::oQ);
+  const OpT* sK = reinterpret_cast<const OpT*>(smem + L::oK);
+  const OpT* sKF = reinterpret_cast<const OpT*>(smem + L::oF);
+  const OpT* sTu = reinterpret_cast<const OpT*>(smem + L::oTu);
+  const OpT* sP = reinterpret_cast<const OpT*>(smem + L::oP);
+  const OpT* sV = reinterpret_cast<const OpT*>(smem + L::oV);
+  const float* svec = reinterpret_cast<const float*>(smem + L::oVec);
+  const float* s_eG = svec + R::vEG;
+  const float* s_eGx = svec + R::vEGx;
+  const float* s_eF = svec + R::vEF;
+  const float* s_misc = svec + R::vMisc;
+  const float* s_decC = svec + R::vDecC;
 
-  // Zero all of LDS once: padding columns and never-written blocks read as zero.
+  // Zero all of LDS once: the token columns past a 16-token chunk read as zero.
   {
-    constexpr int nvec = static_cast<int>(L::bytes(chan) / 16);
+    constexpr int nvec = static_cast<int>(L::bytes / 16);
     uint4* z = reinterpret_cast<uint4*>(smem);
     for (int i = tid; i < nvec; i += kThreads) z[i] = uint4{0, 0, 0, 0};
   }
 
-  const In* gq = static_cast<const In*>(p.q);
-  const In* gk = static_cast<const In*>(p.k);
   const In* gv = static_cast<const In*>(p.v);
-  const In* gb = static_cast<const In*>(p.beta);
-  const In* gg = static_cast<const In*>(p.decay);
-  const long tok0 = static_cast<long>(b) * T;   // token index base of this sequence
+  const long seq0 = static_cast<long>(b) * T;
 
   // ---- prefetch registers (one chunk ahead) ----
-  uint4 rq[NP], rk[NP], rg[NP], rv[NPv];
-  // kept as raw activation values: converting right after the load would make
-  // the compiler wait for every outstanding load, the prefetch included
-  In rbeta{}, rgh{};
-
-  auto issue_loads = [&](int t0) {
-    const int Lc = min(C, T - t0);
+  u32x4 rT[R::kTiles][PT], rC[2][PC], rE[PE], rv[NPv];
+  auto issue_loads = [&](int c) {
+    const u32x4* rec = reinterpret_cast<const u32x4*>(rec0 + static_cast<size_t>(c) * R::bytes);
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int r = pp * RPP + tid / LPR, seg = tid % LPR;
-      rq[pp] = rk[pp] = rg[pp] = uint4{0, 0, 0, 0};
-      if (r < Lc) {
-        const long off = ((tok0 + t0 + r) * H + h) * DK + seg * V;
-        rq[pp] = *reinterpret_cast<const uint4*>(gq + off);
-        rk[pp] = *reinterpret_cast<const uint4*>(gk + off);
-        if (chan) rg[pp] = *reinterpret_cast<const uint4*>(gg + off);
+    for (int t = 0; t < R::kTiles; ++t) {
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int u = tid + i * kThreads;
+        if (nT16 % kThreads == 0 || u < nT16) rT[t][i] = rec[(R::oQ + t * R::kTile) / 16 + u];
       }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < PC; ++i) {
+        const int u = tid + i * kThreads;
+        if (nC16 % kThreads == 0 || u < nC16) rC[t][i] = rec[(R::oTu + t * R::kCC) / 16 + u];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < nE16) rE[i] = rec[R::oVec / 16 + u];
+    }
+    const int t0 = c * C, Lc = min(C, T - t0);
+#pragma unroll
+    for (int pp = 0; pp < NPv; ++pp) {
+      const int r = pp * RPPv + tid / LPRv, seg = tid % LPRv;
+      rv[pp] = u32x4{0, 0, 0, 0};
+      if (r < Lc) {
+        const long off = ((seq0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + seg * V;
+        rv[pp] = *reinterpret_cast<const u32x4*>(gv + off);
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int t = 0; t < R::kTiles; ++t) {
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int u = tid + i * kThreads;
+        if (nT16 % kThreads == 0 || u < nT16) {
+          const int r = u / rowT16, c16 = u % rowT16;
+          const size_t base = t == 0 ? L::oQ : t == 1 ? L::oK : L::oF;
+          *reinterpret_cast<u32x4*>(smem + base + (static_cast<size_t>(r) * L::LDK) * sizeof(OpT) + c16 * 16) = rT[t][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < PC; ++i) {
+        const int u = tid + i * kThreads;
+        if (nC16 % kThreads == 0 || u < nC16) {
+          const int r = u / rowC16, c16 = u % rowC16;
+          const size_t base = t == 0 ? L::oTu : L::oP;
+          *reinterpret_cast<u32x4*>(smem + base + (static_cast<size_t>(r) * L::LC) * sizeof(OpT) + c16 * 16) = rC[t][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < nE16) reinterpret_cast<u32x4*>(smem + L::oVec)[u] = rE[i];
     }
 #pragma unroll
     for (int pp = 0; pp < NPv; ++pp) {
       const int r = pp * RPPv + tid / LPRv, seg = tid % LPRv;
-      rv[pp] = uint4{0, 0, 0, 0};
-      if (r < Lc) {
-        const long off = ((tok0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + seg * V;
-        rv[pp] = *reinterpret_cast<const uint4*>(gv + off);
+      if (r < C) {
+        float vv[V];
+        act<In>::load_vec(reinterpret_cast<const In*>(&rv[pp]), vv);
+        store16<OpT>(reinterpret_cast<OpT*>(smem + L::oV) + r * L::LDV + seg * V, vv);
       }
-    }
-    rbeta = In{}; rgh = In{};
-    if (tid < C && tid < Lc) {
-      const long off = (tok0 + t0 + tid) * H + h;
-      rbeta = gb[off];
-      if (headdecay) rgh = gg[off];
-    }
-  };
-  auto unpack = [&](const uint4& raw, float (&x)[V]) {
-    act<In>::load_vec(reinterpret_cast<const In*>(&raw), x);
-  };
-  auto store_row = [&](OpT* dst, const float (&x)[V]) {
-    if constexpr (sizeof(OpT) == 2) {
-      f16x8 hv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
-      *reinterpret_cast<f16x8*>(dst) = hv;
-    } else {
-      *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
     }
   };
 
@@ -340,311 +752,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
     }
   }
 
-  const int nchunks = (T + C - 1) / C;
+  const int nchunks = p.nchunks;
   if (nchunks > 0) issue_loads(0);
-  lds_barrier();   // LDS zero-fill visible
 
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int t0 = ch * C;
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * C;
     const int Lc = min(C, T - t0);
-
-    // ============ phase 1: stage the chunk: normalised rows, gates ============
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int r = pp * RPP + tid / LPR, seg = tid % LPR;
-      float qv[V], kv[V];
-      unpack(rq[pp], qv);
-      unpack(rk[pp], kv);
-      float fq = p.scale, fk = 1.f;
-      if (p.l2norm) {
-        // row norms: the LPR lanes of a row are consecutive, reduce with DPP moves
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-        fq *= inv_norm(dpp_group_sum<LPR>(sq));
-        fk = inv_norm(dpp_group_sum<LPR>(sk));
-      }
-#pragma unroll
-      for (int e = 0; e < V; ++e) { qv[e] *= fq; kv[e] *= fk; }
-      if (r < C) {
-        store_row(sQ + r * L::LDK + seg * V, qv);
-        store_row(sK + r * L::LDK + seg * V, kv);
-        if (chan) {
-          float gvv[V];
-          unpack(rg[pp], gvv);
-          store_row(sGst + r * DK + seg * V, gvv);
-        }
-      }
-    }
-#pragma unroll
-    for (int pp = 0; pp < NPv; ++pp) {
-      const int r = pp * RPPv + tid / LPRv, seg = tid % LPRv;
-      if (r < C) {
-        float vv[V];
-        unpack(rv[pp], vv);
-        store_row(sV + r * L::LDV + seg * V, vv);
-      }
-    }
-    if (wave == 0) {
-      // beta and the scalar gate: lane r holds token r of the chunk (C <= 64).
-      float G = (lane < C) ? act<In>::cvt(rgh) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off, 64);
-        if (lane >= off) G += y;
-      }
-      float Gx = __shfl_up(G, 1, 64);
-      if (lane == 0) Gx = 0.f;
-      const float Glast = __shfl(G, 63, 64);
-      if (lane < C) {
-        s_bt[lane] = act<In>::cvt(rbeta);
-        s_Gi[lane] = G;
-        s_Ge[lane] = Gx;
-        s_eG[lane] = __expf(G);
-        s_eGx[lane] = __expf(Gx);
-        s_eF[lane] = __expf(Glast - G);
-      }
-      if (lane == 0) {
-        s_misc[0] = __expf(Glast);
-        *s_flag = 0;
-      }
-    }
-    // registers are free: fetch the next chunk while this one is computed
-    if (ch + 1 < nchunks) issue_loads(t0 + C);
+    lds_barrier();            // the previous chunk's reads are done (first: zero fill)
+    stage();
     lds_barrier();
+    if (c + 1 < nchunks) issue_loads(c + 1);   // lands while this chunk is computed
 
-    if (chan) {
-      // (1b) per (16-token block, key channel): normalised q, k times exp(g)
-      // products referenced to the block start (prefix) and end (suffix);
-      // all of them are <= 1.
-      constexpr int NT = (NB * DK + kThreads - 1) / kThreads;
-      uint32_t kin16[NT][8];   // bf16 copy of the inverse-prefix operand, two per register
-#pragma unroll
-      for (int it = 0; it < NT; ++it) {
-        const int task = tid + it * kThreads;
-        if (task < NB * DK) {
-          const int i = task / DK, c = task % DK;
-          float a[16], kx[16], kin[16];
-          float pre = 1.f;
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int r = 16 * i + t;
-            a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
-            kx[t] = static_cast<float>(sK[r * L::LDK + c]);
-            const float qx = static_cast<float>(sQ[r * L::LDK + c]);
-            sK[r * L::LDK + c] = (OpT)(kx[t] * pre);          // Ka: exclusive prefix
-            pre *= a[t];
-            kin[t] = kx[t] / pre;                             // k / inclusive prefix
-            sQ[r * L::LDK + c] = (OpT)(qx * pre);             // Qa: inclusive prefix
-          }
-          float suf = 1.f;
-#pragma unroll
-          for (int t = 15; t >= 0; --t) {
-            sKb[(16 * i + t) * L::LDK + c] = (OpT)(kx[t] * suf);  // Kb: decay to block end
-            suf *= a[t];
-          }
-          s_tau[i * DK + c] = pre;   // whole-block factor
-          if constexpr (sizeof(OpT) == 2) {
-            // diagonal blocks pair a factor <= 1 with its inverse; balanced by
-            // sqrt(block factor) both stay within exp(+-8) for a block factor
-            // >= exp(-16), which fp16 holds
-            const float rs = sqrtf(pre);
-            s_rsq[i * DK + c] = 1.f / rs;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-              *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-              kin16[it][t] = static_cast<uint32_t>(f32_to_bf16(kin[2 * t])) |
-                             (static_cast<uint32_t>(f32_to_bf16(kin[2 * t + 1])) << 16);
-            if (pre < kSafeBlockDecay) *s_flag = 1;
-          } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = kin[t];
-          }
-        }
-      }
-      lds_barrier();
-      const bool steep = *s_flag != 0;
-      // (1c) chunk-level factors and k decayed to the chunk end
-#pragma unroll
-      for (int it = 0; it < NT; ++it) {
-        const int task = tid + it * kThreads;
-        if (task < NB * DK) {
-          const int i = task / DK, c = task % DK;
-          const float tau = s_tau[i * DK + c];
-          if constexpr (sizeof(OpT) == 2) {
-            if (steep) {
-#pragma unroll
-              for (int t = 0; t < 16; ++t)
-                sKinv[(16 * i + t) * L::LDK + c] = static_cast<uint16_t>(kin16[it][t >> 1] >> (16 * (t & 1)));
-            }
-          }
-          float cb = 1.f, ca = 1.f;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const float tj = s_tau[j * DK + c];
-            if (j < i) cb *= tj;
-            if (j > i) ca *= tj;
-          }
-          s_Cb[i * DK + c] = cb;
-          if (i == 0) s_decC[c] = ca * tau;
-          float dd = 1.f;
-#pragma unroll
-          for (int j = NB - 1; j >= 0; --j) {    // D[i][j] = prod_{j < m < i} tau_m
-            if (j < i - 1) s_D[L::dslot(i, j) * DK + c] = dd;
-            if (j < i) dd *= s_tau[j * DK + c];
-          }
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int r = 16 * i + t;
-            sKF[r * L::LDK + c] = (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
-          }
-        }
-      }
-      lds_barrier();
-    }
-
-    // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-    for (int job = wave; job < 2 * NPAIR; job += kWaves) {
-      const bool isP = job >= NPAIR;
-      const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
-      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
-      f32x4 acc = {0, 0, 0, 0};
-      if (!chan) {
-        const OpT* brow = sK + (16 * j + l16) * L::LDK;
-        typename M::frag fa[NKP], fb[NKP];
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, fa[m], fb[m]);
-      } else if (i == j) {
-        if constexpr (sizeof(OpT) == 2) {
-          const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
-          if (*s_flag == 0) {
-            const OpT* krh = reinterpret_cast<const OpT*>(krow);
-#pragma unroll
-            for (int m = 0; m < NKP; ++m) {
-              auto fa = M::ld_cont(arow, 32 * m, g);
-              M::scale_cont(fa, s_rsq + i * DK, 32 * m, g);
-              M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
-            }
-          } else {
-#pragma unroll
-            for (int m = 0; m < NKP; ++m) mma_diag_bf16(acc, M::ld_cont(arow, 32 * m, g), krow, 32 * m, g);
-          }
-        } else {
-          const OpT* krow = sKinv + (16 * j + l16) * L::LDK;
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(arow, 32 * m, g), M::ld_cont(krow, 32 * m, g));
-        }
-      } else {
-        const OpT* brow = sKb + (16 * j + l16) * L::LDK;
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          auto fa = M::ld_cont(arow, 32 * m, g);
-          if (i - j >= 2) M::scale_cont(fa, s_D + L::dslot(i, j) * DK, 32 * m, g);
-          M::mma(acc, fa, M::ld_cont(brow, 32 * m, g));
-        }
-      }
-      const int s = 16 * j + l16;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * i + 4 * g + jj;
-        if (!isP) {
-          float val = acc[jj] * s_bt[r];
-          if (headdecay) val *= __expf(s_Ge[r] - s_Gi[s]);
-          sAm[r * L::LF + s] = (i > j || s < r) ? val : 0.f;
-        } else {
-          float val = acc[jj];
-          if (headdecay) val *= __expf(s_Gi[r] - s_Gi[s]);
-          sP[r * L::LC + s] = (OpT)((i > j || s <= r) ? val : 0.f);
-        }
-      }
-    }
-    lds_barrier();
-
-    // ============ phase 3: T = (I + A)^-1, stored as T (fp32) and T diag(beta) ============
-    if (wave == 0) {
-      // diagonal 16x16 blocks, lane -> (block, column): right-looking
-      // substitution, so each step leaves only independent updates behind
-      const int i = g, jc = l16;
-      if (i < NB) {
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
-        const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
-#pragma unroll
-        for (int s = 0; s < 15; ++s) {
-#pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] -= ablk[r * L::LF + s] * x[s];
-        }
-        const float bj = s_bt[16 * i + jc];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];
-          sTu[(16 * i + r) * L::LC + 16 * i + jc] = (OpT)(x[r] * bj);
-        }
-      }
-    } else if (chan) {
-      // T diag(beta) shares its LDS with the Gram factors: zero it above the
-      // block diagonal (and past the chunk for C = 16)
-      for (int idx = tid - 64; idx < C * L::NCOL; idx += kThreads - 64) {
-        const int r = idx / L::NCOL, s = idx % L::NCOL;
-        if ((s >> 4) > (r >> 4)) sTu[r * L::LC + s] = (OpT)0.f;
-      }
-      {
-        // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)
-        constexpr int VE = sizeof(OpT) == 2 ? 8 : 4;
-        for (int idx = tid - 64; idx < C * DK / VE; idx += kThreads - 64) {
-          const int r = idx / (DK / VE), c = (idx % (DK / VE)) * VE;
-          const float* cb = s_Cb + (r >> 4) * DK + c;
-          OpT* kp = sK + r * L::LDK + c;
-          OpT* qp = sQ + r * L::LDK + c;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) {
-            kp[e] = (OpT)(static_cast<float>(kp[e]) * cb[e]);
-            qp[e] = (OpT)(static_cast<float>(qp[e]) * cb[e]);
-          }
-        }
-      }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int d = 1; d < NB; ++d) {
-      // blocks on diagonal d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, on waves 1..
-      const int j = wave - 1, i = j + d;
-      if (wave >= 1 && i < NB) {
-        f32x4 X = {0, 0, 0, 0};
-        for (int kb = j; kb < i; ++kb) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4*>(sAm + (16 * i + l16) * L::LF + 16 * kb + 4 * g);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float bv = sTm[(16 * kb + 4 * g + jj) * L::LF + 16 * j + l16];
-            X = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], bv, X, 0, 0, 0);
-          }
-        }
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(sTm + (16 * i + l16) * L::LF + 16 * i + 4 * g);
-        f32x4 Y = {0, 0, 0, 0};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[jj], X[jj], Y, 0, 0, 0);
-        const float bj = s_bt[16 * j + l16];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * i + 4 * g + jj;
-          sTm[r * L::LF + 16 * j + l16] = -Y[jj];
-          sTu[r * L::LC + 16 * j + l16] = (OpT)(-Y[jj] * bj);
-        }
-      }
-      lds_barrier();
-    }
-
-    // ============ phase 4: state step and output (owner waves) ============
     if (owner) {
       typename M::frag Sf[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
-      // X = V - diag(sk exp(Gx)) K S0, one 16-token tile at a time
+      // X = V - (K * exp(Gx)) S0, one 16-token tile at a time
       f32x4 Xl[NB];
       const OpT* vcol = sV + 16 * wave + l16;
 #pragma unroll
@@ -681,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 #pragma unroll
       for (int m = 0; m < NH; ++m)
         Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
-      // O^T = S0^T (diag(sq exp(G)) Q)^T + D^T P^T, one 16-token tile at a time
+      // O^T = S0^T (Q * exp(G))^T + D^T P^T, one 16-token tile at a time
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         const OpT* qrow = sQ + (16 * rt + l16) * L::LDK;
@@ -697,11 +820,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 #pragma unroll
         for (int m = 0; m <= rt / 2; ++m) M::mma(acc, Df[m], M::ld_perm(prow, 32 * m, g));
         if (r < Lc) {
-          float* op = p.o + ((tok0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + 16 * wave + 4 * g;
+          float* op = p.o + ((seq0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + 16 * wave + 4 * g;
           *reinterpret_cast<f32x4*>(op) = acc;
         }
       }
-      // S <- exp(G_last) S0 + KY D', KY = (diag(sk exp(G_last - G)) K)^T
+      // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
         if (chan) {
@@ -712,6 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
         }
       }
       if (headdecay) {
+        // the per-token factor goes on D's rows
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
 #pragma unroll
@@ -729,7 +853,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
           M::mma(S[t], ld_tokens(KY, L::LDK, 32 * m, 16 * t, g, l16, 2 * m + 1 < NB), Df[m]);
       }
     }
-    lds_barrier();
   }
 
   if (owner) {
@@ -744,57 +867,90 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_kernel(ChunkParams p) {
 
 // ---------------------------------------------------------------- launcher --
 
+inline hipError_t set_max_lds(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
+}
+
 template <int DK, int DVS, int C, typename In, int DECAY>
-hipError_t launch_one(const ChunkParams& cp, int nwg, hipStream_t s) {
+hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp, int nwg_state,
+                      hipStream_t s) {
   using OpT = typename OpOf<In>::T;
-  using L = ChunkLayout<DK, DVS, C, sizeof(OpT)>;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
-  if constexpr (L::bytes(chan) > kMaxLds) {
-    return hipErrorInvalidConfiguration;   // never instantiated as a kernel
+  using LP = PrepLayout<DK, C, sizeof(OpT)>;
+  using LS = StateLayout<DK, DVS, C, sizeof(OpT), chan>;
+  if constexpr (LP::bytes(chan) > kMaxLds || LS::bytes > kMaxLds) {
+    return hipErrorInvalidConfiguration;   // never instantiated as kernels
   } else {
-    auto fn = chunked_kernel<DK, DVS, C, In, DECAY>;
-    static bool attr_set = false;   // benign race: the attribute call is idempotent
+    auto fp = prep_kernel<DK, C, In, DECAY>;
+    auto fs = state_kernel<DK, DVS, C, In, DECAY>;
+    static bool attr_set = false;   // per instantiation; benign race: the calls are idempotent
+    hipError_t e = hipSuccess;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(kMaxLds));
+      e = set_max_lds(reinterpret_cast<const void*>(fp));
+      if (e != hipSuccess) return e;
+      e = set_max_lds(reinterpret_cast<const void*>(fs));
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    fn<<<dim3(nwg), dim3(kThreads), L::bytes(chan), s>>>(cp);
+    fp<<<dim3(nwg_prep), dim3(kThreads), LP::bytes(chan), s>>>(pp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    fs<<<dim3(nwg_state), dim3(kThreads), LS::bytes, s>>>(sp);
     return hipGetLastError();
   }
 }
 
+// Shape tables shared by the host planning and the dispatch.
+#define KDA_FOR_SHAPES(X)                                                                \
+  X(32, 16, 16) X(32, 32, 16) X(32, 64, 16) X(64, 16, 16) X(64, 32, 16) X(64, 64, 16)    \
+  X(128, 16, 16) X(128, 32, 16) X(128, 64, 16)                                           \
+  X(32, 16, 32) X(32, 32, 32) X(32, 64, 32) X(64, 16, 32) X(64, 32, 32) X(64, 64, 32)    \
+  X(128, 16, 32) X(128, 32, 32) X(128, 64, 32)                                           \
+  X(32, 16, 64) X(32, 32, 64) X(32, 64, 64) X(64, 16, 64) X(64, 32, 64) X(64, 64, 64)    \
+  X(128, 16, 64) X(128, 32, 64) X(128, 64, 64)
+
+// LDS bytes of the larger of the two kernels, 0 for an unknown shape.
 template <int OpBytes>
 size_t lds_bytes(int DK, int DVS, int C, bool chan) {
-#define KDA_L(dk, dvs, c) \
-  if (DK == dk && DVS == dvs && C == c) return ChunkLayout<dk, dvs, c, OpBytes>::bytes(chan);
-#define KDA_L2(dk, c) KDA_L(dk, 16, c) KDA_L(dk, 32, c) KDA_L(dk, 64, c)
-#define KDA_L3(c) KDA_L2(32, c) KDA_L2(64, c) KDA_L2(128, c)
-  KDA_L3(16) KDA_L3(32) KDA_L3(64)
-#undef KDA_L3
-#undef KDA_L2
+#define KDA_L(dk, dvs, c)                                                                  \
+  if (DK == dk && DVS == dvs && C == c) {                                                  \
+    const size_t a = PrepLayout<dk, c, OpBytes>::bytes(chan);                              \
+    const size_t b = chan ? StateLayout<dk, dvs, c, OpBytes, true>::bytes                  \
+                          : StateLayout<dk, dvs, c, OpBytes, false>::bytes;                \
+    return a > b ? a : b;                                                                  \
+  }
+  KDA_FOR_SHAPES(KDA_L)
 #undef KDA_L
   return 0;
 }
 
+// Workspace bytes of one chunk's record.
+template <int OpBytes>
+size_t record_bytes(int DK, int C, bool chan) {
+#define KDA_R(dk, c)                                                                       \
+  if (DK == dk && C == c)                                                                  \
+    return chan ? RecLayout<dk, c, OpBytes, true>::bytes : RecLayout<dk, c, OpBytes, false>::bytes;
+  KDA_R(32, 16) KDA_R(64, 16) KDA_R(128, 16) KDA_R(32, 32) KDA_R(64, 32) KDA_R(128, 32)
+  KDA_R(32, 64) KDA_R(64, 64) KDA_R(128, 64)
+#undef KDA_R
+  return 0;
+}
+
 template <typename In, int DECAY>
-hipError_t launch_any(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s) {
-#define KDA_C(dk, dvs, c) \
-  if (DK == dk && DVS == dvs && C == c) return launch_one<dk, dvs, c, In, DECAY>(cp, nwg, s);
-#define KDA_C2(dk, c) KDA_C(dk, 16, c) KDA_C(dk, 32, c) KDA_C(dk, 64, c)
-#define KDA_C3(c) KDA_C2(32, c) KDA_C2(64, c) KDA_C2(128, c)
-  KDA_C3(16) KDA_C3(32) KDA_C3(64)
-#undef KDA_C3
-#undef KDA_C2
+hipError_t launch_any(int DK, int DVS, int C, const PrepParams& pp, int nwg_prep,
+                      const StateParams& sp, int nwg_state, hipStream_t s) {
+#define KDA_C(dk, dvs, c)                                                                  \
+  if (DK == dk && DVS == dvs && C == c)                                                    \
+    return launch_two<dk, dvs, c, In, DECAY>(pp, nwg_prep, sp, nwg_state, s);
+  KDA_FOR_SHAPES(KDA_C)
 #undef KDA_C
   return hipErrorInvalidValue;
 }
 
 // One instantiation unit per (activation dtype, decay kind): chunked_<dtype>_d<kind>.hip.
-#define KDA_DECLARE_LAUNCH(name) \
-  hipError_t name(int DK, int DVS, int C, const ChunkParams& cp, int nwg, hipStream_t s);
+#define KDA_DECLARE_LAUNCH(name)                                                           \
+  hipError_t name(int DK, int DVS, int C, const PrepParams& pp, int nwg_prep,              \
+                  const StateParams& sp, int nwg_state, hipStream_t s);
 KDA_DECLARE_LAUNCH(launch_bf16_d0)
 KDA_DECLARE_LAUNCH(launch_bf16_d1)
 KDA_DECLARE_LAUNCH(launch_bf16_d2)

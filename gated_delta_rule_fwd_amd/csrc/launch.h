@@ -27,7 +27,7 @@ hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
-// Largest LDS footprint (bytes) the chunked kernel needs for this shape, 0 if unsupported.
-size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype);
+// LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.
+size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind);
 
 }  // namespace kda

@@ -78,13 +78,22 @@ typedef enum {
  *   chunk_size     16, 32 or 64 (ejkernel default 64); the result does not
  *                  depend on it beyond rounding.  T need not be a multiple.
  *
+ * Two kernels run on `stream`: a chunk-parallel one that prepares every
+ * chunk (normalisation, gate sums, the WY inverse, decayed operands) and a
+ * sequential one that carries the state through the chunks and writes o.
+ * The prepared chunks pass through a device workspace that the library
+ * allocates on first use and keeps, one per (device, stream), growing it when
+ * a larger problem arrives (about 50 KB per chunk and head for DK = 128 fp16
+ * operands; the first call of a larger size synchronises `stream`).
+ *
  * T == 0 copies initial_state (or zeros) to final_state; then q, k, v, beta,
  * decay and o are not read and may be NULL.
  * Errors: KDA_ERR_NULL if final_state is NULL, or (T > 0) q/k/v/beta/o is
  * NULL or decay is NULL with decay_kind != NONE; KDA_ERR_SHAPE for negative or overflowing sizes;
  * KDA_ERR_UNSUPPORTED for other DK/DV/chunk/dtype/decay_kind values, and for
- * KDA_F32 with DK = 128 and chunk_size = 64 (its tiles exceed the LDS of one
- * compute unit; use chunk_size <= 32 or the recurrent entry point).
+ * KDA_F32 with DK = 128, chunk_size = 64 and KDA_DECAY_CHANNEL (its tiles
+ * exceed the LDS of one compute unit; use chunk_size <= 32 or the recurrent
+ * entry point); KDA_ERR_HIP if a launch or the workspace allocation fails.
  */
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, const float* initial_state,

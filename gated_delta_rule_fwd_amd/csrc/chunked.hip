@@ -21,8 +21,8 @@ Plan plan_for(int B, int H, int DK, int DV, int C, int dtype, bool chan) {
   int dvs = DV < 64 ? DV : 64;
   while (dvs > 16 && static_cast<long>(B) * H * (DV / dvs) < 256) dvs /= 2;
   while (dvs >= 16) {
-    const size_t l = dtype == 0 ? chunked::lds_bytes<4>(DK, dvs, C, chan)
-                                : chunked::lds_bytes<2>(DK, dvs, C, chan);
+    const size_t l = dtype == 0 ? chunked::lds_bytes<4, 4>(DK, dvs, C, chan)
+                                : chunked::lds_bytes<2, 2>(DK, dvs, C, chan);
     if (l != 0 && l <= kMaxLds) return Plan{dvs, l};
     dvs /= 2;
   }

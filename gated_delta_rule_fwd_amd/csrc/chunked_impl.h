@@ -212,10 +212,31 @@ __device__ __forceinline__ void store16(OpT* dst, const float (&x)[N]) {
   }
 }
 
+// N consecutive elements e0.. of row r of a record tile (N, e0 multiples of 4),
+// placed in perm_pos order, 4 elements per store.
+template <typename OpT, int PPR, int N>
+__device__ __forceinline__ void put_perm(unsigned char* tile, int r, int e0, const float (&x)[N]) {
+#pragma unroll
+  for (int a = 0; a < N / 4; ++a) {
+    unsigned char* dst = tile + swz_off<PPR>(r, perm_pos(e0 + 4 * a) * static_cast<int>(sizeof(OpT)));
+    if constexpr (sizeof(OpT) == 2) {
+      *reinterpret_cast<f16x4*>(dst) = f16x4{(_Float16)x[4 * a], (_Float16)x[4 * a + 1],
+                                             (_Float16)x[4 * a + 2], (_Float16)x[4 * a + 3]};
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{x[4 * a], x[4 * a + 1], x[4 * a + 2], x[4 * a + 3]};
+    }
+  }
+}
+
 // ------------------------------------------------------------- prep kernel --
 
+// Eight waves per workgroup: the chunk's work is short, so more waves hide
+// the LDS and HBM latencies of its dependent phases.
+constexpr int kPrepThreads = 512;
+constexpr int kPrepWaves = kPrepThreads / 64;
+
 template <int DK, int C, typename In, int DECAY>
-__global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   constexpr int V = act<In>::kVec;           // activation elements per 16-byte load
   static_assert(V * sizeof(OpT) == 16, "one 16-byte load makes one 16-byte operand store");
   constexpr int LPR = DK / V;                // lanes per q/k row
-  constexpr int RPP = kThreads / LPR;        // q/k rows per load pass
+  constexpr int RPP = kPrepThreads / LPR;        // q/k rows per load pass
   constexpr int NP = (C + RPP - 1) / RPP;    // q/k load passes
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
   constexpr int NPAIR = NB * (NB + 1) / 2;
@@ -243,9 +264,6 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   const int Lc = min(C, T - t0);
   const long tok0 = static_cast<long>(b) * T + t0;   // first token of the chunk
   unsigned char* rec = p.ws + (static_cast<size_t>(head) * p.nchunks + ch) * R::bytes;
-  OpT* rQ = reinterpret_cast<OpT*>(rec + R::oQ);
-  OpT* rK = reinterpret_cast<OpT*>(rec + R::oK);
-  OpT* rF = reinterpret_cast<OpT*>(rec + R::oF);
   float* rvec = reinterpret_cast<float*>(rec + R::oVec);
 
   OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
@@ -313,8 +331,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
         store16<OpT>(sQ + r * L::LDK + seg * V, qv);
         store16<OpT>(sK + r * L::LDK + seg * V, kv);
         if (!chan) {   // final record operands already
-          store16<OpT>(rQ + r * DK + seg * V, qv);
-          store16<OpT>(rK + r * DK + seg * V, kv);
+          put_perm<OpT, R::PPRK>(rec + R::oQ, r, seg * V, qv);
+          put_perm<OpT, R::PPRK>(rec + R::oK, r, seg * V, kv);
         } else {
           float gv[V];
           act<In>::load_vec(reinterpret_cast<const In*>(&rg[pp]), gv);
@@ -354,11 +372,11 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
     // (1b) per (16-token block, key channel): normalised q, k times exp(g)
     // products referenced to the block start (prefix) and end (suffix);
     // all of them are <= 1.
-    constexpr int NT = (NB * DK + kThreads - 1) / kThreads;
+    constexpr int NT = (NB * DK + kPrepThreads - 1) / kPrepThreads;
     uint32_t kin16[NT][8];   // bf16 copy of the inverse-prefix operand, two per register
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
-      const int task = tid + it * kThreads;
+      const int task = tid + it * kPrepThreads;
       if (task < NB * DK) {
         const int i = task / DK, c = task % DK;
         float a[16], kx[16], kin[16];
@@ -406,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
     // (1c) chunk-level factors; k decayed to the chunk end goes to the record
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
-      const int task = tid + it * kThreads;
+      const int task = tid + it * kPrepThreads;
       if (task < NB * DK) {
         const int i = task / DK, c = task % DK;
         const float tau = s_tau[i * DK + c];
@@ -435,7 +453,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const int r = 16 * i + t;
-          rF[r * DK + c] = (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
+          *reinterpret_cast<OpT*>(rec + R::oF + swz_off<R::PPRK>(r, perm_pos(c) * static_cast<int>(sizeof(OpT)))) =
+              (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
         }
       }
     }
@@ -443,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   }
 
   // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-  for (int job = wave; job < 2 * NPAIR; job += kWaves) {
+  for (int job = wave; job < 2 * NPAIR; job += kPrepWaves) {
     const bool isP = job >= NPAIR;
     const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
     const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
@@ -522,17 +541,19 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   } else {
     // meanwhile the other waves write the finished record tiles
     constexpr int VE = 16 / sizeof(OpT);
-    constexpr int RowV = C / VE;             // 16-byte pieces per P row
-    for (int idx = tid - 64; idx < C * RowV; idx += kThreads - 64) {
+    constexpr int RowV = R::NCOL / VE;       // 16-byte pieces per P row
+    for (int idx = tid - 64; idx < C * RowV; idx += kPrepThreads - 64) {
       const int r = idx / RowV, s0 = (idx % RowV) * VE;
-      uint4 val = *reinterpret_cast<const uint4*>(sP + r * L::LC + s0);
-      if ((s0 >> 4) > (r >> 4)) val = uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4*>(rec + R::oP + (static_cast<size_t>(r) * C + s0) * sizeof(OpT)) = val;
+      const bool upper = (s0 >> 4) > (r >> 4);
+      float x[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) x[e] = upper ? 0.f : static_cast<float>(sP[r * L::LC + s0 + e]);
+      put_perm<OpT, R::PPRC>(rec + R::oP, r, s0, x);
     }
     if (chan) {
       // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)
       constexpr int RowK = DK / VE;
-      for (int idx = tid - 64; idx < C * RowK; idx += kThreads - 64) {
+      for (int idx = tid - 64; idx < C * RowK; idx += kPrepThreads - 64) {
         const int r = idx / RowK, c = (idx % RowK) * VE;
         const float* cb = s_Cb + (r >> 4) * DK + c;
         float kx[VE], qx[VE];
@@ -541,8 +562,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
           kx[e] = static_cast<float>(sK[r * L::LDK + c + e]) * cb[e];
           qx[e] = static_cast<float>(sQ[r * L::LDK + c + e]) * cb[e];
         }
-        store16<OpT>(rK + r * DK + c, kx);
-        store16<OpT>(rQ + r * DK + c, qx);
+        put_perm<OpT, R::PPRK>(rec + R::oK, r, c, kx);
+        put_perm<OpT, R::PPRK>(rec + R::oQ, r, c, qx);
       }
     }
   }
@@ -574,19 +595,115 @@ __global__ __launch_bounds__(kThreads, 2) void prep_kernel(PrepParams p) {
   // ============ record: T diag(beta), zero above the block diagonal ============
   {
     constexpr int VE = 16 / sizeof(OpT);
-    constexpr int RowV = C / VE;
-    for (int idx = tid; idx < C * RowV; idx += kThreads) {
+    constexpr int RowV = R::NCOL / VE;
+    for (int idx = tid; idx < C * RowV; idx += kPrepThreads) {
       const int r = idx / RowV, s0 = (idx % RowV) * VE;
       float x[VE];
       const bool upper = (s0 >> 4) > (r >> 4);
 #pragma unroll
       for (int e = 0; e < VE; ++e) x[e] = upper ? 0.f : sTm[r * L::LF + s0 + e] * s_bt[s0 + e];
-      store16<OpT>(reinterpret_cast<OpT*>(rec + R::oTu) + r * C + s0, x);
+      put_perm<OpT, R::PPRC>(rec + R::oTu, r, s0, x);
     }
   }
 }
 
 // ------------------------------------------------------------ state kernel --
+
+// Asynchronous 16-byte copy global -> LDS (gfx950 global_load_lds_dwordx4):
+// lane i of the wave writes lds_base + 16 i; lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+// Wait until this wave's global loads (the LDS copies included) have landed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// MFMA fragments from a chunk record in LDS (tiles with rows of 16-byte
+// pieces, elements in perm_pos order, swizzled).  The swizzle repeats every
+// 16 rows, so every fragment address is one of a few per-lane offsets,
+// computed once, plus a compile-time displacement (row block, k step, tile,
+// buffer).
+//   kq(tile, rt, m)    Q/K/F rows 16 rt + l16, k = 32 m + {4g..4g+3, 16+4g..}
+//   cc(tile, rt, m)    the same for the [C][NCOL] tiles Tu and P
+//   tok(tile, m, t, hi) the transposed operand: channel 16 t + l16 at tokens
+//                      32 m + 4g + j and (hi) 32 m + 16 + 4g + j
+template <int DK, int C, typename OpT> struct RecFrags;
+template <int DK, int C> struct RecFrags<DK, C, _Float16> {
+  using R = RecLayout<DK, C, 2, false>;
+  static constexpr int RowK = R::PPRK * 16, RowC = R::PPRC * 16;
+  int kqo[DK / 32], cco[R::NCOL / 32], toko[DK / 32];
+  __device__ void init(int g, int l16) {
+#pragma unroll
+    for (int m = 0; m < DK / 32; ++m) kqo[m] = swz_off<R::PPRK>(l16, 2 * (32 * m + 8 * g));
+#pragma unroll
+    for (int m = 0; m < R::NCOL / 32; ++m) cco[m] = swz_off<R::PPRC>(l16, 2 * (32 * m + 8 * g));
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+      toko[a] = swz_off<R::PPRK>(4 * g + (l16 >> 2), 2 * perm_pos(32 * a + 4 * (l16 & 3)));
+  }
+  __device__ f16x8 kq(const unsigned char* tile, int rt, int m) const {
+    return *reinterpret_cast<const f16x8*>(tile + kqo[m] + 16 * rt * RowK);
+  }
+  __device__ f16x8 cc(const unsigned char* tile, int rt, int m) const {
+    return *reinterpret_cast<const f16x8*>(tile + cco[m] + 16 * rt * RowC);
+  }
+  __device__ f16x8 tok(const unsigned char* tile, int m, int t, bool hi) const {
+    const unsigned char* at = tile + toko[t >> 1] + 32 * m * RowK + 8 * (t & 1);
+    const f16x4 lo = ld_tr16(reinterpret_cast<const _Float16*>(at));
+    const f16x4 up = hi ? ld_tr16(reinterpret_cast<const _Float16*>(at + 16 * RowK)) : f16x4{0, 0, 0, 0};
+    return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+template <int DK, int C> struct RecFrags<DK, C, float> {
+  using R = RecLayout<DK, C, 4, false>;
+  using frag = Mma<float>::frag;
+  int g, l16;
+  __device__ void init(int g_, int l16_) { g = g_; l16 = l16_; }
+  template <int PPR>
+  __device__ frag perm(const unsigned char* tile, int r, int m) const {
+    frag f;
+    f.lo = *reinterpret_cast<const f32x4*>(tile + swz_off<PPR>(r, 4 * (32 * m + 8 * g)));
+    f.hi = *reinterpret_cast<const f32x4*>(tile + swz_off<PPR>(r, 4 * (32 * m + 8 * g + 4)));
+    return f;
+  }
+  __device__ frag kq(const unsigned char* tile, int rt, int m) const { return perm<R::PPRK>(tile, 16 * rt + l16, m); }
+  __device__ frag cc(const unsigned char* tile, int rt, int m) const { return perm<R::PPRC>(tile, 16 * rt + l16, m); }
+  __device__ frag tok(const unsigned char* tile, int m, int t, bool hi) const {
+    frag f;
+    const int b = 4 * perm_pos(16 * t + l16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.lo[j] = *reinterpret_cast<const float*>(tile + swz_off<R::PPRK>(32 * m + 4 * g + j, b));
+      f.hi[j] = hi ? *reinterpret_cast<const float*>(tile + swz_off<R::PPRK>(32 * m + 16 + 4 * g + j, b)) : 0.f;
+    }
+    return f;
+  }
+};
+
+// Raw buffer resource (V#) over `bytes` bytes at `base`, dword data.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int32_t>(a & 0xffffffffu), static_cast<int32_t>((a >> 32) & 0xffffu), bytes,
+               0x00020000};
+}
+// Asynchronous 16-byte copy global -> LDS (buffer_load_dwordx4 ... lds):
+// lane i of the wave writes lds_base + 16 i (lds_base wave-uniform, in M0),
+// reading the buffer at voff (per lane) + soff (uniform).  Written as
+// assembly so that the compiler does not wait for the copy before unrelated
+// LDS reads; the caller waits (wait_vm) and synchronises before the copied
+// data is read.
+__device__ __forceinline__ void dma16_buf(i32x4 rs, void* lds_base, int voff, int soff) {
+  // the LDS byte address: the pointer in the local address space
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(lds_base)));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+      : "memory", "m0");
+}
 
 template <int DK, int DVS, int C, typename In, int DECAY>
 __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
@@ -594,29 +711,26 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   using M = Mma<OpT>;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
   constexpr bool headdecay = DECAY == DECAY_HEAD;
-  using L = StateLayout<DK, DVS, C, sizeof(OpT), chan>;
+  constexpr int AB = sizeof(In);               // activation bytes
+  using L = StateLayout<DK, DVS, C, sizeof(OpT), AB, chan>;
   using R = RecLayout<DK, C, sizeof(OpT), chan>;
-  constexpr int NB = L::NB;
-  constexpr int V = act<In>::kVec;
-  constexpr int VE = 16 / sizeof(OpT);       // operands per 16 bytes
-  constexpr int LPRv = DVS / V;              // lanes per value row
-  constexpr int RPPv = kThreads / LPRv;
-  constexpr int NPv = (C + RPPv - 1) / RPPv;
+  constexpr int NB = C / 16;
   constexpr int NKT = DK / 16;               // 16-row tiles of the state
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
   constexpr int NOWN = DVS / 16;             // waves that own state columns
   constexpr int NH = (NB + 1) / 2;           // 32-wide k steps over the chunk's tokens
-  // record pieces (16 bytes each) and their share per thread
-  constexpr int nT16 = static_cast<int>(R::kTile / 16), PT = (nT16 + kThreads - 1) / kThreads;
-  constexpr int nC16 = static_cast<int>(R::kCC / 16), PC = (nC16 + kThreads - 1) / kThreads;
-  constexpr int nE16 = R::kVecFloats * 4 / 16, PE = (nE16 + kThreads - 1) / kThreads;
-  constexpr int rowT16 = DK / VE, rowC16 = C / VE;
-  static_assert(R::kVecFloats % 4 == 0, "vector block in 16-byte pieces");
-  static_assert(LPRv >= 1 && (64 % LPRv) == 0, "v rows must pack into waves");
+  // 16-byte copies per chunk: the record, then the value rows; each wave
+  // issues its share in kSlots instruction slots
+  constexpr int nRec = static_cast<int>(R::bytes / 16), nRecI = (nRec + 63) / 64;
+  constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
+  constexpr int kSlotsR = (nRecI + kWaves - 1) / kWaves, kSlotsV = (nValI + kWaves - 1) / kWaves;
+  constexpr int kSlots = kSlotsR + kSlotsV;
   static_assert(DVS % 16 == 0 && NOWN <= kWaves, "slice width");
+  static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
 
   extern __shared__ __align__(256) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int T = p.T, H = p.H, DV = p.DV;
 
@@ -637,104 +751,63 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   const int b = head / H, h = head % H;
   const int n0 = slice * DVS;   // first value column of this slice
   const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::bytes;
-
-  const OpT* sQ = reinterpret_cast<const OpT*>(smem + L::oQ);
-  const OpT* sK = reinterpret_cast<const OpT*>(smem + L::oK);
-  const OpT* sKF = reinterpret_cast<const OpT*>(smem + L::oF);
-  const OpT* sTu = reinterpret_cast<const OpT*>(smem + L::oTu);
-  const OpT* sP = reinterpret_cast<const OpT*>(smem + L::oP);
-  const OpT* sV = reinterpret_cast<const OpT*>(smem + L::oV);
-  const float* svec = reinterpret_cast<const float*>(smem + L::oVec);
-  const float* s_eG = svec + R::vEG;
-  const float* s_eGx = svec + R::vEGx;
-  const float* s_eF = svec + R::vEF;
-  const float* s_misc = svec + R::vMisc;
-  const float* s_decC = svec + R::vDecC;
-
-  // Zero all of LDS once: the token columns past a 16-token chunk read as zero.
-  {
-    constexpr int nvec = static_cast<int>(L::bytes / 16);
-    uint4* z = reinterpret_cast<uint4*>(smem);
-    for (int i = tid; i < nvec; i += kThreads) z[i] = uint4{0, 0, 0, 0};
-  }
-
   const In* gv = static_cast<const In*>(p.v);
   const long seq0 = static_cast<long>(b) * T;
+  const int nchunks = p.nchunks;
+  const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
+  const int rowO = H * DV * 4;               // ... and of o
 
-  // ---- prefetch registers (one chunk ahead) ----
-  u32x4 rT[R::kTiles][PT], rC[2][PC], rE[PE], rv[NPv];
-  auto issue_loads = [&](int c) {
-    const u32x4* rec = reinterpret_cast<const u32x4*>(rec0 + static_cast<size_t>(c) * R::bytes);
+  RecFrags<DK, C, OpT> fr;
+  fr.init(g, l16);
+  // value rows 4g + jj (+16 rt) at this lane's column: bf16 rows are read
+  // transposed (one read per 16-row block), fp32 rows one element at a time
+  constexpr int RowV = L::PPRV * 16;
+  const int vtr = swzv_off<L::PPRV>(4 * g + (l16 >> 2), (16 * wave + 4 * (l16 & 3)) * AB);
+  int vo[4];
 #pragma unroll
-    for (int t = 0; t < R::kTiles; ++t) {
+  for (int jj = 0; jj < 4; ++jj) vo[jj] = swzv_off<L::PPRV>(4 * g + jj, (16 * wave + l16) * AB);
+
+  // Per-lane copy offsets, the same for every chunk: value piece of slot s is
+  // row vr[s], at byte voff[s] from the chunk's first value element.
+  int vr[kSlotsV], voff[kSlotsV];
 #pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int u = tid + i * kThreads;
-        if (nT16 % kThreads == 0 || u < nT16) rT[t][i] = rec[(R::oQ + t * R::kTile) / 16 + u];
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < PC; ++i) {
-        const int u = tid + i * kThreads;
-        if (nC16 % kThreads == 0 || u < nC16) rC[t][i] = rec[(R::oTu + t * R::kCC) / 16 + u];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      const int u = tid + i * kThreads;
-      if (u < nE16) rE[i] = rec[R::oVec / 16 + u];
-    }
+  for (int sv = 0; sv < kSlotsV; ++sv) {
+    const int piece = (sv * kWaves + wave) * 64 + lane;
+    const int r = piece / L::PPRV, q = piece % L::PPRV;
+    vr[sv] = piece < nVal ? r : C;           // C: no copy
+    voff[sv] = r * rowV + (q ^ swzv<L::PPRV>(r)) * 16;
+  }
+
+  // Copy slots [s0, s1) of chunk c's record and value rows into LDS buffer
+  // `buf` (asynchronous; slot s of a wave is one 1 KiB copy instruction).
+  auto issue = [&](int c, int buf, int s0, int s1) {
+    unsigned char* dst = smem + buf * L::kBuf;
+    const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::bytes, static_cast<int>(R::bytes));
     const int t0 = c * C, Lc = min(C, T - t0);
+    const i32x4 rv =
+        rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
 #pragma unroll
-    for (int pp = 0; pp < NPv; ++pp) {
-      const int r = pp * RPPv + tid / LPRv, seg = tid % LPRv;
-      rv[pp] = u32x4{0, 0, 0, 0};
-      if (r < Lc) {
-        const long off = ((seq0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + seg * V;
-        rv[pp] = *reinterpret_cast<const u32x4*>(gv + off);
+    for (int sl = 0; sl < kSlots; ++sl) {
+      if (sl < s0 || sl >= s1) continue;
+      if (sl < kSlotsR) {
+        const int j = sl * kWaves + wave;
+        if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
+          dma16_buf(rr, dst + j * 1024, lane * 16, j * 1024);
+      } else {
+        const int sv = sl - kSlotsR, j = sv * kWaves + wave;
+        if (j < nValI && vr[sv] < Lc) dma16_buf(rv, dst + L::oV + j * 1024, voff[sv], 0);
       }
     }
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int t = 0; t < R::kTiles; ++t) {
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int u = tid + i * kThreads;
-        if (nT16 % kThreads == 0 || u < nT16) {
-          const int r = u / rowT16, c16 = u % rowT16;
-          const size_t base = t == 0 ? L::oQ : t == 1 ? L::oK : L::oF;
-          *reinterpret_cast<u32x4*>(smem + base + (static_cast<size_t>(r) * L::LDK) * sizeof(OpT) + c16 * 16) = rT[t][i];
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < PC; ++i) {
-        const int u = tid + i * kThreads;
-        if (nC16 % kThreads == 0 || u < nC16) {
-          const int r = u / rowC16, c16 = u % rowC16;
-          const size_t base = t == 0 ? L::oTu : L::oP;
-          *reinterpret_cast<u32x4*>(smem + base + (static_cast<size_t>(r) * L::LC) * sizeof(OpT) + c16 * 16) = rC[t][i];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      const int u = tid + i * kThreads;
-      if (u < nE16) reinterpret_cast<u32x4*>(smem + L::oVec)[u] = rE[i];
-    }
-#pragma unroll
-    for (int pp = 0; pp < NPv; ++pp) {
-      const int r = pp * RPPv + tid / LPRv, seg = tid % LPRv;
-      if (r < C) {
-        float vv[V];
-        act<In>::load_vec(reinterpret_cast<const In*>(&rv[pp]), vv);
-        store16<OpT>(reinterpret_cast<OpT*>(smem + L::oV) + r * L::LDV + seg * V, vv);
-      }
+  // After the copy of chunk c into `buf` has landed: value rows past the
+  // sequence end read as zero.
+  auto finish = [&](int c, int buf) {
+    wait_vm();
+    const int Lc = min(C, T - c * C);
+    if (Lc < C) {
+      unsigned char* dst = smem + buf * L::kBuf + L::oV;
+      for (int piece = tid; piece < nVal; piece += kThreads)
+        if (piece / L::PPRV >= Lc) *reinterpret_cast<u32x4*>(dst + piece * 16) = u32x4{0, 0, 0, 0};
     }
   };
 
@@ -752,39 +825,88 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
     }
   }
 
-  const int nchunks = p.nchunks;
-  if (nchunks > 0) issue_loads(0);
+  if (nchunks > 0) {
+    issue(0, 0, 0, kSlots);
+    finish(0, 0);
+  }
+  lds_barrier();
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * C;
-    const int Lc = min(C, T - t0);
-    lds_barrier();            // the previous chunk's reads are done (first: zero fill)
-    stage();
-    lds_barrier();
-    if (c + 1 < nchunks) issue_loads(c + 1);   // lands while this chunk is computed
+  // Output rows of a chunk: stored at the start of the next one, when the
+  // wave's memory queue holds no copies.
+  f32x4 Oprev[NB];
+  const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
+  auto store_out = [&](int c) {
+    const int t0 = c * C, Lc = min(C, T - t0);
+    unsigned char* ob = reinterpret_cast<unsigned char*>(p.o + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const int r = 16 * rt + l16;
+      if (r < Lc) *reinterpret_cast<f32x4*>(ob + r * rowO + obyte) = Oprev[rt];
+    }
+  };
+
+  // One chunk step on LDS buffer CUR (a compile-time constant, so every LDS
+  // address below is a per-lane base plus an immediate).
+  auto step = [&](auto cur_tag, int c) {
+    constexpr int cur = decltype(cur_tag)::value;
+    // the next chunk's copies go out in three parts between the products
+    const bool pre = L::NBUF == 2 && c + 1 < nchunks;
+    constexpr int kS1 = kSlots / 3, kS2 = 2 * kSlots / 3;
 
     if (owner) {
+      const unsigned char* bq = smem + cur * L::kBuf;
+      const unsigned char* sQ = bq + R::oQ;
+      const unsigned char* sK = bq + R::oK;
+      const unsigned char* sKF = bq + R::oF;
+      const unsigned char* sTu = bq + R::oTu;
+      const unsigned char* sP = bq + R::oP;
+      const unsigned char* sV = bq + L::oV;
+      const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
+
+      if (c > 0) store_out(c - 1);
+      if (pre) issue(c + 1, cur ^ 1, 0, kS1);
       typename M::frag Sf[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
-      // X = V - (K * exp(Gx)) S0, one 16-token tile at a time
-      f32x4 Xl[NB];
-      const OpT* vcol = sV + 16 * wave + l16;
+      // K S0 and S0^T Q^T: both read only S0, so their products interleave
+      f32x4 Xl[NB], Ol[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        f32x4 acc = {0, 0, 0, 0};
-        const OpT* krow = sK + (16 * rt + l16) * L::LDK;
-        typename M::frag fk[NKP];
+        typename M::frag fk[NKP], fq[NKP];
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) fk[m] = M::ld_perm(krow, 32 * m, g);
+        for (int m = 0; m < NKP; ++m) {
+          fk[m] = fr.kq(sK, rt, m);
+          fq[m] = fr.kq(sQ, rt, m);
+        }
+        Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, fk[m], Sf[m]);
+        for (int m = 0; m < NKP; ++m) {
+          M::mma(Xl[rt], fk[m], Sf[m]);
+          M::mma(Ol[rt], Sf[m], fq[m]);
+        }
+      }
+      if (pre) issue(c + 1, cur ^ 1, kS1, kS2);
+      // X = V - (K * exp(Gx)) S0
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        float vv[4];
+        if constexpr (AB == 2) {
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          const s4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4*)(sV + vtr + 16 * rt * RowV));
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) vv[jj] = bf16_to_f32(static_cast<uint16_t>(tv[jj]));
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            vv[jj] = act<In>::load1(reinterpret_cast<const In*>(sV + vo[jj] + 16 * rt * RowV));
+        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int r = 16 * rt + 4 * g + jj;
-          float ks = acc[jj];
-          if (headdecay) ks *= s_eGx[r];
-          Xl[rt][jj] = static_cast<float>(vcol[r * L::LDV]) - ks;
+          float ks = Xl[rt][jj];
+          if (headdecay) ks *= svec[R::vEGx + r];
+          Xl[rt][jj] = vv[jj] - ks;
         }
       }
       // D = T diag(beta) X
@@ -796,42 +918,29 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
         Dl[rt] = f32x4{0, 0, 0, 0};
-        const OpT* urow = sTu + (16 * rt + l16) * L::LC;
 #pragma unroll
-        for (int m = 0; m <= rt / 2; ++m) M::mma(Dl[rt], M::ld_perm(urow, 32 * m, g), Xf[m]);
+        for (int m = 0; m <= rt / 2; ++m) M::mma(Dl[rt], fr.cc(sTu, rt, m), Xf[m]);
       }
       typename M::frag Df[NH];
 #pragma unroll
       for (int m = 0; m < NH; ++m)
         Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
-      // O^T = S0^T (Q * exp(G))^T + D^T P^T, one 16-token tile at a time
+      // O^T = S0^T (Q * exp(G))^T + D^T P^T
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        const OpT* qrow = sQ + (16 * rt + l16) * L::LDK;
-        typename M::frag fq[NKP];
+        if (headdecay) Ol[rt] *= svec[R::vEG + 16 * rt + l16];
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) fq[m] = M::ld_perm(qrow, 32 * m, g);
-        f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, Sf[m], fq[m]);
-        const int r = 16 * rt + l16;
-        if (headdecay) acc *= s_eG[r];
-        const OpT* prow = sP + r * L::LC;
-#pragma unroll
-        for (int m = 0; m <= rt / 2; ++m) M::mma(acc, Df[m], M::ld_perm(prow, 32 * m, g));
-        if (r < Lc) {
-          float* op = p.o + ((seq0 + t0 + r) * H + h) * static_cast<long>(DV) + n0 + 16 * wave + 4 * g;
-          *reinterpret_cast<f32x4*>(op) = acc;
-        }
+        for (int m = 0; m <= rt / 2; ++m) M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
       }
+      if (pre) issue(c + 1, cur ^ 1, kS2, kSlots);
       // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
         if (chan) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) S[t][jj] *= s_decC[16 * t + 4 * g + jj];
+          for (int jj = 0; jj < 4; ++jj) S[t][jj] *= svec[R::vDecC + 16 * t + 4 * g + jj];
         } else if (headdecay) {
-          S[t] *= s_misc[0];
+          S[t] *= svec[R::vMisc];
         }
       }
       if (headdecay) {
@@ -839,22 +948,40 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) Dl[st][jj] *= s_eF[16 * st + 4 * g + jj];
+          for (int jj = 0; jj < 4; ++jj) Dl[st][jj] *= svec[R::vEF + 16 * st + 4 * g + jj];
         }
 #pragma unroll
         for (int m = 0; m < NH; ++m)
           Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
       }
-      const OpT* KY = chan ? sKF : sK;
+      const unsigned char* KY = chan ? sKF : sK;
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
 #pragma unroll
         for (int m = 0; m < NH; ++m)
-          M::mma(S[t], ld_tokens(KY, L::LDK, 32 * m, 16 * t, g, l16, 2 * m + 1 < NB), Df[m]);
+          M::mma(S[t], fr.tok(KY, m, t, 2 * m + 1 < NB), Df[m]);
       }
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
+    } else if (pre) {
+      issue(c + 1, cur ^ 1, 0, kSlots);
     }
+    if (c + 1 < nchunks) {
+      if (L::NBUF == 1) {
+        lds_barrier();              // every wave is done with the only buffer
+        issue(c + 1, 0, 0, kSlots);
+      }
+      finish(c + 1, L::NBUF == 2 ? (cur ^ 1) : 0);
+      lds_barrier();                // the next chunk is visible to all waves
+    }
+  };
+
+  for (int c = 0; c < nchunks; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < nchunks) step(std::integral_constant<int, L::NBUF == 2 ? 1 : 0>{}, c + 1);
   }
 
+  if (owner && nchunks > 0) store_out(nchunks - 1);
   if (owner) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
@@ -877,7 +1004,7 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
   using OpT = typename OpOf<In>::T;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
   using LP = PrepLayout<DK, C, sizeof(OpT)>;
-  using LS = StateLayout<DK, DVS, C, sizeof(OpT), chan>;
+  using LS = StateLayout<DK, DVS, C, sizeof(OpT), sizeof(In), chan>;
   if constexpr (LP::bytes(chan) > kMaxLds || LS::bytes > kMaxLds) {
     return hipErrorInvalidConfiguration;   // never instantiated as kernels
   } else {
@@ -892,7 +1019,7 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    fp<<<dim3(nwg_prep), dim3(kThreads), LP::bytes(chan), s>>>(pp);
+    fp<<<dim3(nwg_prep), dim3(kPrepThreads), LP::bytes(chan), s>>>(pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     fs<<<dim3(nwg_state), dim3(kThreads), LS::bytes, s>>>(sp);
@@ -910,13 +1037,13 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
   X(128, 16, 64) X(128, 32, 64) X(128, 64, 64)
 
 // LDS bytes of the larger of the two kernels, 0 for an unknown shape.
-template <int OpBytes>
+template <int OpBytes, int ActBytes>
 size_t lds_bytes(int DK, int DVS, int C, bool chan) {
 #define KDA_L(dk, dvs, c)                                                                  \
   if (DK == dk && DVS == dvs && C == c) {                                                  \
     const size_t a = PrepLayout<dk, c, OpBytes>::bytes(chan);                              \
-    const size_t b = chan ? StateLayout<dk, dvs, c, OpBytes, true>::bytes                  \
-                          : StateLayout<dk, dvs, c, OpBytes, false>::bytes;                \
+    const size_t b = chan ? StateLayout<dk, dvs, c, OpBytes, ActBytes, true>::bytes        \
+                          : StateLayout<dk, dvs, c, OpBytes, ActBytes, false>::bytes;      \
     return a > b ? a : b;                                                                  \
   }
   KDA_FOR_SHAPES(KDA_L)

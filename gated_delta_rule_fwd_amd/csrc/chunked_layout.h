@@ -8,6 +8,7 @@
 //                 chunks in order, reads the records, keeps the state
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 
 namespace kda {
@@ -19,19 +20,64 @@ constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t al(size_t a) { return (a + 255) & ~size_t(255); }
 }  // namespace chunked_layout
 
-// Per-chunk record in the workspace (global memory), all tiles row-major with
-// one row per token of the chunk.  OpBytes: 2 (fp16 operands) or 4 (fp32).
+// XOR swizzle of the 16-byte pieces of a row of PPR pieces: the piece p of
+// row r is stored at position p ^ swz<PPR>(r).  The LDS serves 128 bytes per
+// step (32 banks): 8 lanes of a 16-byte read, 16 lanes of an 8-byte read.
+// With the rows copied unpadded into LDS this swizzle makes (a) 16-byte reads
+// of one piece column by 16 consecutive rows conflict-free and (b) the
+// transposed 8-byte token reads (4 consecutive rows, 4 consecutive 8-byte
+// pieces of a half) two-way, the least a fixed half allows.
+template <int PPR>
+__host__ __device__ constexpr int swz(int r) {
+  return PPR >= 32 ? (r & 15)
+       : PPR == 16 ? (((r & 1) << 2) | ((r >> 1) & 3) | (r & 8))
+       : PPR == 8  ? (((r & 1) << 2) | ((r >> 1) & 3))
+       : PPR == 4  ? ((r >> 1) & 3)
+       : PPR == 2  ? ((r >> 2) & 1)
+                   : 0;
+}
+// Byte offset of byte `b` of row r in a swizzled tile with PPR pieces per row.
+template <int PPR>
+__host__ __device__ constexpr int swz_off(int r, int b) {
+  return r * PPR * 16 + (((b >> 4) ^ swz<PPR>(r)) << 4) + (b & 15);
+}
+// Value rows (activations, read only transposed: 4 consecutive rows x 16
+// columns per 16 lanes): conflict-free with this swizzle.
+template <int PPR>
+__host__ __device__ constexpr int swzv(int r) {
+  return PPR >= 8 ? 2 * (r & 3) : PPR == 4 ? 2 * ((r >> 1) & 1) : 0;
+}
+template <int PPR>
+__host__ __device__ constexpr int swzv_off(int r, int b) {
+  return r * PPR * 16 + (((b >> 4) ^ swzv<PPR>(r)) << 4) + (b & 15);
+}
+// Stored position of element e of a record row: within each 32-element group
+// the 4-element subgroups are kept in the order 0 4 1 5 2 6 3 7, so the
+// operand of an MFMA lane (elements 4g..4g+3 and 16+4g..16+4g+3 of a group)
+// is 8 consecutive stored elements.
+__host__ __device__ constexpr int perm_pos(int e) {
+  return (e & ~31) + 4 * (2 * ((e >> 2) & 3) + ((e >> 4) & 1)) + (e & 3);
+}
+
+// Per-chunk record in the workspace (global memory).  Each tile has one row
+// per token of the chunk, elements in perm_pos order, rows unpadded and
+// swizzled (swz above), so that the state kernel copies the record into LDS
+// as it is.  OpBytes: 2 (fp16 operands) or 4 (fp32).
 //   Q    q normalised and scaled; per-channel decay: times exp(G)
 //   K    k normalised; per-channel decay: times exp(Gx)
 //   F    per-channel decay only: k normalised times exp(G_last - G)
-//   Tu   T diag(beta), T = (I + A)^-1, zero above the block diagonal  [C][C]
-//   P    masked decayed q k^T, zero above the block diagonal          [C][C]
+//   Tu   T diag(beta), T = (I + A)^-1, zero above the block diagonal  [C][NCOL]
+//   P    masked decayed q k^T, zero above the block diagonal          [C][NCOL]
+//        (NCOL = max(C, 32): the columns a 32-wide k step reads)
 //   vec  fp32: exp(G), exp(Gx), exp(G_last - G) (each C), misc[16] with
 //        misc[0] = exp(G_last); per-channel: exp(G_last) per key channel [DK]
 template <int DK, int C, int OpBytes, bool Chan>
 struct RecLayout {
+  static constexpr int PPRK = DK * OpBytes / 16;   // pieces per Q/K/F row
+  static constexpr int NCOL = C < 32 ? 32 : C;
+  static constexpr int PPRC = NCOL * OpBytes / 16; // pieces per Tu/P row
   static constexpr size_t kTile = size_t(C) * DK * OpBytes;
-  static constexpr size_t kCC = size_t(C) * C * OpBytes;
+  static constexpr size_t kCC = size_t(C) * NCOL * OpBytes;
   static constexpr int kTiles = Chan ? 3 : 2;       // Q, K (, F)
   static constexpr size_t oQ = 0;
   static constexpr size_t oK = oQ + kTile;
@@ -89,26 +135,17 @@ struct PrepLayout {
   static constexpr size_t bytes(bool ch) { return chunked_layout::al(oVec(ch) + szVec(ch)); }
 };
 
-// LDS of the state kernel: one chunk's record (padded rows) and its values.
-template <int DK, int DVS, int C, int OpBytes, bool Chan>
+// LDS of the state kernel: NBUF buffers, each one chunk's record image
+// followed by its value rows ([C][DVS] activations, rows swizzled).  With two
+// buffers the next chunk is copied in while the current one is computed.
+template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
-  static constexpr int NB = C / 16;
-  static constexpr int NCOL = C < 32 ? 32 : C;
-  static constexpr int PAD = 16 / OpBytes;
-  static constexpr int LDK = DK + PAD;
-  static constexpr int LDV = DVS + PAD;
-  static constexpr int LC = NCOL + PAD;
-  static constexpr size_t kRowTile = size_t(C) * LDK * OpBytes;
-  static constexpr size_t kCC = size_t(C) * LC * OpBytes;
-  static constexpr size_t oQ = 0;
-  static constexpr size_t oK = chunked_layout::al(oQ + kRowTile);
-  static constexpr size_t oF = chunked_layout::al(oK + kRowTile);
-  static constexpr size_t oTu = chunked_layout::al(oF + (Chan ? kRowTile : 0));
-  static constexpr size_t oP = chunked_layout::al(oTu + kCC);
-  static constexpr size_t oV = chunked_layout::al(oP + kCC);
-  static constexpr size_t oVec = chunked_layout::al(oV + size_t(C) * LDV * OpBytes);
-  static constexpr int kVecFloats = RecLayout<DK, C, OpBytes, Chan>::kVecFloats;
-  static constexpr size_t bytes = chunked_layout::al(oVec + size_t(kVecFloats) * 4);
+  using R = RecLayout<DK, C, OpBytes, Chan>;
+  static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
+  static constexpr size_t oV = R::bytes;
+  static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
+  static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
+  static constexpr size_t bytes = NBUF * kBuf;
 };
 
 }  // namespace kda

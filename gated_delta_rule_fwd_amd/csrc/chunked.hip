@@ -1,6 +1,8 @@
 // Host planning of the chunked forward: value-slice width, grids, the
 // workspace that carries the per-chunk records from the prep kernel to the
 // state kernel, and dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
+#include <stdlib.h>
+
 #include <map>
 #include <mutex>
 #include <utility>
@@ -70,6 +72,20 @@ size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind) {
   return a.dvs == 0 ? 0 : a.lds;
 }
 
+// Chunks per launch pair.  Long inputs are processed in segments of chunks
+// (the state kernel of one segment hands its final state to the next) so that
+// the workspace holds the records of one segment only: at most 1 GiB by
+// default, KDA_CHUNKED_SEGMENT_MB (MiB) overrides it.
+int segment_chunks(int nchunks, int nheads, size_t rec) {
+  const char* env = getenv("KDA_CHUNKED_SEGMENT_MB");
+  const long mb = env ? atol(env) : 0;
+  const long budget = (mb > 0 ? mb : 1024L) << 20;
+  long seg = budget / static_cast<long>(rec * nheads);
+  if (seg < 1) seg = 1;
+  if (seg > nchunks) seg = nchunks;
+  return static_cast<int>(seg);
+}
+
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const bool chan = a.decay_kind == DECAY_CHANNEL;
   const Plan pl = plan_for(a.B, a.H, a.DK, a.DV, a.chunk, a.dtype, chan);
@@ -79,19 +95,20 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const size_t rec = a.dtype == 0 ? chunked::record_bytes<4>(a.DK, a.chunk, chan)
                                   : chunked::record_bytes<2>(a.DK, a.chunk, chan);
   if (rec == 0) return hipErrorInvalidConfiguration;
+  const int seg = segment_chunks(nchunks, nheads, rec);
   void* ws = nullptr;
-  hipError_t e = workspace(s, rec * nchunks * static_cast<size_t>(nheads), &ws);
+  hipError_t e = workspace(s, rec * seg * static_cast<size_t>(nheads), &ws);
   if (e != hipSuccess) return e;
 
   PrepParams pp;
   pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
   pp.ws = static_cast<unsigned char*>(ws);
-  pp.T = a.T; pp.H = a.H; pp.nchunks = nchunks; pp.l2norm = a.l2norm; pp.scale = a.scale;
+  pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
 
   StateParams sp;
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
-  sp.init = a.init; sp.o = a.o; sp.state = a.state;
-  sp.T = a.T; sp.H = a.H; sp.DV = a.DV; sp.nchunks = nchunks;
+  sp.o = a.o; sp.state = a.state;
+  sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
   sp.nsl = a.DV / pl.dvs;
   sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
 
@@ -100,8 +117,17 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   static const LaunchFn table[2][3] = {
       {chunked::launch_f32_d0, chunked::launch_f32_d1, chunked::launch_f32_d2},
       {chunked::launch_bf16_d0, chunked::launch_bf16_d1, chunked::launch_bf16_d2}};
-  return table[a.dtype == 0 ? 0 : 1][a.decay_kind](a.DK, pl.dvs, a.chunk, pp, nheads * nchunks,
-                                                   sp, nheads * sp.nsl, s);
+  const LaunchFn fn = table[a.dtype == 0 ? 0 : 1][a.decay_kind];
+  for (int c0 = 0; c0 < nchunks; c0 += seg) {
+    const int n = nchunks - c0 < seg ? nchunks - c0 : seg;
+    pp.c0 = c0; pp.nchunks = n;
+    sp.c0 = c0; sp.nchunks = n;
+    // the state entering a later segment is the one the previous segment left
+    sp.init = c0 == 0 ? a.init : a.state;
+    e = fn(a.DK, pl.dvs, a.chunk, pp, nheads * n, sp, nheads * sp.nsl, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -152,6 +152,7 @@ struct PrepParams {
   const void* q; const void* k; const void* beta; const void* decay;
   unsigned char* ws;     // records, [B*H][nchunks]
   int T, H, nchunks, l2norm;
+  int c0;                // first chunk of this launch (records are indexed from it)
   float scale;
 };
 
@@ -159,6 +160,7 @@ struct StateParams {
   const void* v; const unsigned char* ws;
   const float* init; float* o; float* state;
   int T, H, DV, nchunks, nsl, xcd_map;
+  int c0;                // first chunk of this launch; `init` holds the state entering it
 };
 
 // Lower-triangular block pair (i, j), j <= i, of pair index n.
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void 
   const int T = p.T, H = p.H;
   const int ch = blockIdx.x % p.nchunks, head = blockIdx.x / p.nchunks;
   const int b = head / H, h = head % H;
-  const int t0 = ch * C;
+  const int t0 = (p.c0 + ch) * C;
   const int Lc = min(C, T - t0);
   const long tok0 = static_cast<long>(b) * T + t0;   // first token of the chunk
   unsigned char* rec = p.ws + (static_cast<size_t>(head) * p.nchunks + ch) * R::bytes;
@@ -752,7 +754,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   const int n0 = slice * DVS;   // first value column of this slice
   const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::bytes;
   const In* gv = static_cast<const In*>(p.v);
-  const long seq0 = static_cast<long>(b) * T;
+  const long seq0 = static_cast<long>(b) * T + static_cast<long>(p.c0) * C;   // first token of this launch
+  const int Trem = T - p.c0 * C;             // tokens from there to the sequence end
   const int nchunks = p.nchunks;
   const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
   const int rowO = H * DV * 4;               // ... and of o
@@ -783,7 +786,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   auto issue = [&](int c, int buf, int s0, int s1) {
     unsigned char* dst = smem + buf * L::kBuf;
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::bytes, static_cast<int>(R::bytes));
-    const int t0 = c * C, Lc = min(C, T - t0);
+    const int t0 = c * C, Lc = min(C, Trem - t0);
     const i32x4 rv =
         rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
 #pragma unroll
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   // sequence end read as zero.
   auto finish = [&](int c, int buf) {
     wait_vm();
-    const int Lc = min(C, T - c * C);
+    const int Lc = min(C, Trem - c * C);
     if (Lc < C) {
       unsigned char* dst = smem + buf * L::kBuf + L::oV;
       for (int piece = tid; piece < nVal; piece += kThreads)
@@ -836,7 +839,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   f32x4 Oprev[NB];
   const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
   auto store_out = [&](int c) {
-    const int t0 = c * C, Lc = min(C, T - t0);
+    const int t0 = c * C, Lc = min(C, Trem - t0);
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {

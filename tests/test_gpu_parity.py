@@ -272,3 +272,26 @@ def test_nan_stays_in_its_head():
             assert fin != bool(bad[b, h]), (b, h)
     # chunks before the NaN's chunk are untouched by it
     assert torch.isfinite(o[1, :64, 2]).all()
+
+
+def test_segmented_chunk_walk_matches_single_pass(monkeypatch):
+    """A small workspace budget splits the sequence into segments of chunks
+    (each state pass hands its final state to the next); the result must be
+    bitwise the single-pass result and within tolerance of the oracle."""
+    for name, kw in (("gdn_d128", dict(B=2, T=333, H=4)),
+                     ("kda_d128", dict(B=1, T=300, H=4, init_state=True))):
+        w = small(name, **kw)
+        announce(f"segmented {w}")
+        inp = make_inputs(w)
+        d = to_dev(inp)
+        args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
+        monkeypatch.delenv("KDA_CHUNKED_SEGMENT_MB", raising=False)
+        o1, S1 = fwd_chunked(*args, chunk_size=w.chunk)
+        monkeypatch.setenv("KDA_CHUNKED_SEGMENT_MB", "1")   # ~1 MiB of records: several segments
+        o2, S2 = fwd_chunked(*args, chunk_size=w.chunk)
+        monkeypatch.delenv("KDA_CHUNKED_SEGMENT_MB")
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), "segmented walk differs from one pass"
+        o_ref, S_ref = kda_scan(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                                inp["initial_state"])
+        check("segmented", o2, S2, o_ref, S_ref, TOL[w.dtype])

@@ -1,8 +1,9 @@
 #!/usr/bin/env python
 """Benchmark of the gated delta-rule forward on one MI355X.
 
-One step = one kda_fwd_chunked call (prep, WY, state walk and output, fused in
-one kernel launch) over one batch of synthetic inputs already resident in HBM.
+One step = one kda_fwd_chunked call (two launches: the chunk-parallel prep/WY
+kernel, then the sequential state-and-output kernel) over one batch of
+synthetic inputs already resident in HBM.
 The default workload is the scalar-gated DK = DV = 128 case
 (B8 T4096 H16, chunk 64, initial state); the printed JSON line also carries the
 per-channel-gated DK = DV = 128 case and the single-token decode as extra
@@ -10,6 +11,8 @@ measurements, the roofline of the chunked kernel (HIP-event kernel time,
 algorithmic bytes) and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --write-traffic FETCH_DIR WRITE_DIR   (profiles/traffic.json
+        from two rocprofv3 --pmc runs of this script with --calibrate-copy)
 """
 
 from __future__ import annotations
@@ -158,8 +161,67 @@ def stored_traffic(name):
         return None
     ent = t.get(name)
     if not ent or ent.get("kernel_hash") != kernel_hash():
-        return None   # counters were taken on another version of the kernel
-    return ent.get("bytes_per_launch")
+        return None   # counters were taken on another version of the kernels
+    return ent.get("bytes_per_call")
+
+
+# kernel-name fragments of one call of each workload, as rocprofv3 prints them
+TRAFFIC_KERNELS = {
+    "gdn_d128": ["prep_kernel<128, 64, kda::bf16_t, 1>", "state_kernel<128, 64, 64, kda::bf16_t, 1>"],
+    "kda_d128": ["prep_kernel<128, 64, kda::bf16_t, 2>", "state_kernel<128, 32, 64, kda::bf16_t, 2>"],
+    "decode_d128": ["decode_kernel<128, 128, kda::bf16_t>"],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30   # the --calibrate-copy copies: 1 GiB read and 1 GiB written
+
+
+def write_traffic(fetch_dir, write_dir):
+    """profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs
+    (KiB per dispatch): each counter is scaled by what it read for a plain
+    1 GiB device copy, then averaged over dispatches of each kernel and summed
+    over the kernels of one call."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
+        return vals
+
+    out = {"_comment": "HBM bytes per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                       "(KiB per dispatch), each scaled by the ratio of a plain 1 GiB device "
+                       "copy's true bytes to what the same counter read for it, summed over the "
+                       "kernels of one call; kernel_hash names the chunked kernel sources",
+           "kernel_hash": kernel_hash()}
+    scale = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        v = per_kernel(d, counter)
+        copies = [x for k, xs in v.items() if COPY_KERNEL in k for x in xs if x > COPY_BYTES / 2]
+        if not copies:
+            raise SystemExit(f"no 1 GiB calibration copy found under {d}")
+        scale[counter] = COPY_BYTES / (sum(copies) / len(copies))
+        out[counter.lower() + "_scale"] = round(scale[counter], 4)
+        for name, frags in TRAFFIC_KERNELS.items():
+            ent = out.setdefault(name, {"kernels": frags})
+            total = 0.0
+            for fr in frags:
+                xs = [x for k, xs in v.items() if fr in k for x in xs]
+                if not xs:
+                    raise SystemExit(f"{counter}: no dispatch of {fr} under {d}")
+                total += sum(xs) / len(xs) * scale[counter]
+            ent[counter.lower() + "_bytes"] = int(total)
+    for name in TRAFFIC_KERNELS:
+        ent = out[name]
+        ent["bytes_per_call"] = ent["fetch_size_bytes"] + ent["write_size_bytes"]
+        ent["kernel_hash"] = None if name.startswith("decode") else out["kernel_hash"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -172,7 +234,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); each (batch, head) is independent, so a "
@@ -198,7 +265,7 @@ def main():
     achieved = byts / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
-            "kernel": "chunked_kernel", "kernel_ms_mean": round(kern_ms, 4),
+            "kernel": "prep_kernel + state_kernel (one chunked call)", "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_min": round(kern_min, 4), "algorithmic_bytes": byts,
             "mfma_frac_dense_count": round(flops / (kern_ms * 1e-3) / MFMA_PEAK_F16, 4)}
     line = {

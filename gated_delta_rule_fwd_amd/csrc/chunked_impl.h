@@ -238,7 +238,9 @@ constexpr int kPrepThreads = 512;
 constexpr int kPrepWaves = kPrepThreads / 64;
 
 template <int DK, int C, typename In, int DECAY>
-__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void prep_kernel(PrepParams p) {
+// (second bound: waves per SIMD; without per-channel decay three 8-wave
+// workgroups share a CU)
+__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
@@ -270,7 +272,6 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void 
 
   OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
   OpT* sK = reinterpret_cast<OpT*>(smem + L::oK);
-  OpT* sP = reinterpret_cast<OpT*>(smem + L::oP);
   float* sAm = reinterpret_cast<float*>(smem + L::oAM);
   OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
   float* sTm = reinterpret_cast<float*>(smem + L::oRA(chan));
@@ -516,7 +517,9 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void 
       } else {
         float val = acc[jj];
         if (headdecay) val *= __expf(s_Gi[r] - s_Gi[s]);
-        sP[r * L::LC + s] = (OpT)((i > j || s <= r) ? val : 0.f);
+        // straight to the record (the state kernel is its only reader)
+        *reinterpret_cast<OpT*>(rec + R::oP + swz_off<R::PPRC>(r, perm_pos(s) * static_cast<int>(sizeof(OpT)))) =
+            (OpT)((i > j || s <= r) ? val : 0.f);
       }
     }
   }
@@ -542,15 +545,17 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 1 : 2) void 
     }
   } else {
     // meanwhile the other waves write the finished record tiles
+    // P above the block diagonal (never produced by the Gram) is zero
     constexpr int VE = 16 / sizeof(OpT);
     constexpr int RowV = R::NCOL / VE;       // 16-byte pieces per P row
     for (int idx = tid - 64; idx < C * RowV; idx += kPrepThreads - 64) {
       const int r = idx / RowV, s0 = (idx % RowV) * VE;
-      const bool upper = (s0 >> 4) > (r >> 4);
-      float x[VE];
+      if ((s0 >> 4) > (r >> 4)) {
+        float x[VE];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) x[e] = upper ? 0.f : static_cast<float>(sP[r * L::LC + s0 + e]);
-      put_perm<OpT, R::PPRC>(rec + R::oP, r, s0, x);
+        for (int e = 0; e < VE; ++e) x[e] = 0.f;
+        put_perm<OpT, R::PPRC>(rec + R::oP, r, s0, x);
+      }
     }
     if (chan) {
       // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)

@@ -109,18 +109,23 @@ struct PrepLayout {
   // Regions and what they hold:
   //   Q    q normalised (per-channel: and decayed)                load .. Gram
   //   K    k normalised (per-channel: and decayed)                load .. Gram
-  //   P    masked decayed q k^T                                    Gram .. record
   //   AM   fp32 A (Gram .. inverse); per-channel: staged gate first (load)
-  //   RA   per-channel Gram factors Kb, Kinv (load .. Gram)  |  fp32 T (inverse .. record)
+  //   RA   per-channel: Gram factors Kb, Kinv (load .. Gram), then fp32 T;
+  //        otherwise fp32 T over the Q and K tiles, dead after the Gram
+  // (P goes from the MFMA accumulators straight to the record.)
   static constexpr size_t oQ = 0;
   static constexpr size_t oK = chunked_layout::al(oQ + kRowTile);
-  static constexpr size_t oP = chunked_layout::al(oK + kRowTile);
-  static constexpr size_t oAM = chunked_layout::al(oP + kCC);
+  static constexpr size_t oAM = chunked_layout::al(oK + kRowTile);
   static constexpr size_t szAM(bool ch) { return ch ? chunked_layout::mx(kF32CC, kGst) : kF32CC; }
-  static constexpr size_t oRA(bool ch) { return chunked_layout::al(oAM + szAM(ch)); }
+  static constexpr bool kTinQK = kF32CC <= oAM - oQ;   // T fits over Q and K
+  static constexpr size_t oRA(bool ch) {
+    return (!ch && kTinQK) ? oQ : chunked_layout::al(oAM + szAM(ch));
+  }
   static constexpr size_t oKinv(bool ch) { return chunked_layout::al(oRA(ch) + kRowTile); }  // after Kb
   static constexpr size_t szRA(bool ch) {
-    return chunked_layout::mx(ch ? (oKinv(ch) - oRA(ch)) + size_t(C) * LDK * KinvBytes : 0, kF32CC);
+    return (!ch && kTinQK) ? 0
+                           : chunked_layout::mx(ch ? (oKinv(ch) - oRA(ch)) + size_t(C) * LDK * KinvBytes : 0,
+                                                kF32CC);
   }
   // D[i][j] (decay of the blocks strictly between j and i) is needed for i - j >= 2
   static constexpr int ND = NB >= 3 ? (NB - 2) * (NB - 1) / 2 : 1;
@@ -128,7 +133,9 @@ struct PrepLayout {
   // fp32 vectors: bt Gi Ge (each C), misc[16]; per-channel: tau[NB] Cb[NB] rsq[NB] D[ND] (each DK)
   static constexpr int kVecRows = 3;
   static constexpr int kChanVecs = 3 * NB + ND;
-  static constexpr size_t oVec(bool ch) { return chunked_layout::al(oRA(ch) + szRA(ch)); }
+  static constexpr size_t oVec(bool ch) {
+    return (!ch && kTinQK) ? chunked_layout::al(oAM + szAM(ch)) : chunked_layout::al(oRA(ch) + szRA(ch));
+  }
   static constexpr size_t szVec(bool ch) {
     return size_t(kVecRows) * C * 4 + 64 + (ch ? size_t(kChanVecs) * DK * 4 : 0);
   }

@@ -35,10 +35,11 @@
 //
 // Per-key-channel decay uses products of per-token factors exp(g) <= 1
 // referenced to 16-token block boundaries, so no factor exceeds 1 except the
-// inverse-prefix operand of the diagonal blocks: balanced by sqrt of the block
-// factor it stays within exp(+-8) (fp16) when a block decays by at most
-// exp(-16); a chunk with a steeper block uses a bf16 copy instead (fp32
-// range: the decay over 16 tokens must stay above about -87 in every channel).
+// inverse-prefix operand: balanced by sqrt of the block factor it stays
+// within exp(+-8) (fp16) when a block decays by at most exp(-16).  A chunk
+// with a steeper block keeps all its Gram operands as bf16 (fp32 range: the
+// decay over 16 tokens must stay above about -87 in every channel), and the
+// diagonal of P (no decay) is computed directly from the normalised rows.
 //
 // Accumulator layout of a 16x16 MFMA result: lane l holds rows 4*(l/16)+j,
 // j = 0..3, of column l%16.  The k index of an MFMA is a sum, so A and B may
@@ -57,7 +58,7 @@ namespace chunked {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr float kSafeBlockDecay = 1.1253517e-07f;   // exp(-16)
+constexpr float kSteepBlockLogDecay = -16.f;   // a 16-token block decaying faster is "steep"
 
 // Barrier over LDS only: outstanding global loads (the next chunk's prefetch)
 // stay in flight across it.
@@ -127,17 +128,29 @@ template <> struct Mma<float> {
   }
 };
 
-// bf16 x bf16 product for the diagonal-block Gram of a steep per-channel
-// chunk.  Whole-vector bit casts: building a __bf16 vector element by element
-// from 16-bit patterns is not reliably compiled.
-__device__ __forceinline__ void mma_diag_bf16(f32x4& acc, const f16x8& a_f16,
-                                              const uint16_t* kinv_row, int k0, int g) {
-  const uint4 braw = *reinterpret_cast<const uint4*>(kinv_row + k0 + 8 * g);
+// bf16 x bf16 products for the Gram blocks of a steep per-channel chunk,
+// whose operands are stored as bf16 bit patterns (fp32 range).  Whole-vector
+// bit casts: building a __bf16 vector element by element from 16-bit patterns
+// is not reliably compiled.
+__device__ __forceinline__ void mma_bf16_raw(f32x4& acc, const uint16_t* a_row, const uint16_t* b_row,
+                                             int k0, int g) {
+  const uint4 araw = *reinterpret_cast<const uint4*>(a_row + k0 + 8 * g);
+  const uint4 braw = *reinterpret_cast<const uint4*>(b_row + k0 + 8 * g);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
+                                               __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
+}
+// The same with the A operand scaled per k (v[k0 + 8g + e]) in fp32 and
+// rounded once more to bf16.
+__device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* a_row, const float* v,
+                                                    const uint16_t* b_row, int k0, int g) {
+  const uint4 a0 = *reinterpret_cast<const uint4*>(a_row + k0 + 8 * g);
+  const uint4 braw = *reinterpret_cast<const uint4*>(b_row + k0 + 8 * g);
+  const uint32_t w[4] = {a0.x, a0.y, a0.z, a0.w};
   uint32_t aw[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = f32_to_bf16(static_cast<float>(a_f16[2 * e]));
-    const uint32_t hi = f32_to_bf16(static_cast<float>(a_f16[2 * e + 1]));
+    const uint32_t lo = f32_to_bf16(__uint_as_float(w[e] << 16) * v[k0 + 8 * g + 2 * e]);
+    const uint32_t hi = f32_to_bf16(__uint_as_float(w[e] & 0xffff0000u) * v[k0 + 8 * g + 2 * e + 1]);
     aw[e] = lo | (hi << 16);
   }
   const uint4 araw = uint4{aw[0], aw[1], aw[2], aw[3]};
@@ -238,9 +251,9 @@ constexpr int kPrepThreads = 512;
 constexpr int kPrepWaves = kPrepThreads / 64;
 
 template <int DK, int C, typename In, int DECAY>
-// (second bound: waves per SIMD; without per-channel decay three 8-wave
-// workgroups share a CU)
-__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void prep_kernel(PrepParams p) {
+// (second bound: waves per SIMD; two 8-wave workgroups share a CU with
+// per-channel decay, three without)
+__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
@@ -275,13 +288,13 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
   float* sAm = reinterpret_cast<float*>(smem + L::oAM);
   OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
   float* sTm = reinterpret_cast<float*>(smem + L::oRA(chan));
-  OpT* sKb = reinterpret_cast<OpT*>(smem + L::oRA(chan));
   KinvT* sKinv = reinterpret_cast<KinvT*>(smem + L::oKinv(chan));
   float* sv = reinterpret_cast<float*>(smem + L::oVec(chan));
   float* s_bt = sv;
   float* s_Gi = sv + C;
   float* s_Ge = sv + 2 * C;
-  float* s_misc = sv + 3 * C;                  // [1] = steep-gate flag
+  float* s_qk = sv + 3 * C;                    // per-channel decay: q_hat . k_hat per token
+  float* s_misc = sv + 4 * C;                  // [1] = steep-gate flag
   int* s_flag = reinterpret_cast<int*>(s_misc + 1);
   float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
   float* s_Cb = s_tau + NB * DK;               // [NB][DK] decay of all earlier blocks
@@ -330,6 +343,15 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
       }
 #pragma unroll
       for (int e = 0; e < V; ++e) { qv[e] *= fq; kv[e] *= fk; }
+      if constexpr (chan) {
+        // the diagonal of P takes no decay: kept exact rather than through
+        // the decay-referenced operands
+        float qk = 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) qk += qv[e] * kv[e];
+        qk = dpp_group_sum<LPR>(qk);
+        if (r < C && seg == 0) s_qk[r] = qk;
+      }
       if (r < C) {
         store16<OpT>(sQ + r * L::LDK + seg * V, qv);
         store16<OpT>(sK + r * L::LDK + seg * V, kv);
@@ -372,11 +394,27 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
   lds_barrier();
 
   if constexpr (chan) {
+    if constexpr (sizeof(OpT) == 2) {
+      // (1a) a chunk with a block that decays by more than exp(-16) in some
+      // channel is "steep": its Gram operands are kept as bf16 (fp32 range),
+      // since the prefix factors can then underflow fp16
+      for (int task = tid; task < NB * DK; task += kPrepThreads) {
+        const int i = task / DK, c = task % DK;
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sum += static_cast<float>(sGst[(16 * i + t) * DK + c]);
+        if (sum < kSteepBlockLogDecay) *s_flag = 1;
+      }
+      lds_barrier();
+    }
+    const bool steep = *s_flag != 0;
     // (1b) per (16-token block, key channel): normalised q, k times exp(g)
     // products referenced to the block start (prefix) and end (suffix);
-    // all of them are <= 1.
+    // all of them are <= 1.  The decay-to-block-end operand of the
+    // off-diagonal Gram blocks is the inverse-prefix one times the block
+    // factor, folded into their A-operand scale (D below).
     constexpr int NT = (NB * DK + kPrepThreads - 1) / kPrepThreads;
-    uint32_t kin16[NT][8];   // bf16 copy of the inverse-prefix operand, two per register
+    float kbr[NT][16];       // k decayed to the block end (for the record's F)
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
       const int task = tid + it * kPrepThreads;
@@ -384,38 +422,46 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
         const int i = task / DK, c = task % DK;
         float a[16], kx[16], kin[16];
         float pre = 1.f;
+        // Ka (k times the exclusive prefix) and Qa (q times the inclusive
+        // one) replace k and q in place: fp16, or bf16 bit patterns when steep
+        auto put = [&](OpT* tile, int r, float x) {
+          if (sizeof(OpT) == 2 && steep)
+            reinterpret_cast<uint16_t*>(tile)[r * L::LDK + c] = f32_to_bf16(x);
+          else
+            tile[r * L::LDK + c] = (OpT)x;
+        };
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const int r = 16 * i + t;
           a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
           kx[t] = static_cast<float>(sK[r * L::LDK + c]);
           const float qx = static_cast<float>(sQ[r * L::LDK + c]);
-          sK[r * L::LDK + c] = (OpT)(kx[t] * pre);          // Ka: exclusive prefix
+          put(sK, r, kx[t] * pre);
           pre *= a[t];
           kin[t] = kx[t] / pre;                             // k / inclusive prefix
-          sQ[r * L::LDK + c] = (OpT)(qx * pre);             // Qa: inclusive prefix
+          put(sQ, r, qx * pre);
         }
         float suf = 1.f;
 #pragma unroll
         for (int t = 15; t >= 0; --t) {
-          sKb[(16 * i + t) * L::LDK + c] = (OpT)(kx[t] * suf);  // Kb: decay to block end
+          kbr[it][t] = kx[t] * suf;                         // decay to the block end
           suf *= a[t];
         }
         s_tau[i * DK + c] = pre;   // whole-block factor
         if constexpr (sizeof(OpT) == 2) {
-          // diagonal blocks pair a factor <= 1 with its inverse; balanced by
-          // sqrt(block factor) both stay within exp(+-8) for a block factor
-          // >= exp(-16), which fp16 holds
-          const float rs = sqrtf(pre);
-          s_rsq[i * DK + c] = 1.f / rs;
+          if (!steep) {
+            // diagonal blocks pair a factor <= 1 with its inverse; balanced by
+            // sqrt(block factor) both stay within exp(+-8) for a block factor
+            // >= exp(-16), which fp16 holds
+            const float rs = sqrtf(pre);
+            s_rsq[i * DK + c] = 1.f / rs;
 #pragma unroll
-          for (int t = 0; t < 16; ++t)
-            *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
+            for (int t = 0; t < 16; ++t)
+              *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
+          } else {
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            kin16[it][t] = static_cast<uint32_t>(f32_to_bf16(kin[2 * t])) |
-                           (static_cast<uint32_t>(f32_to_bf16(kin[2 * t + 1])) << 16);
-          if (pre < kSafeBlockDecay) *s_flag = 1;
+            for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = f32_to_bf16(kin[t]);
+          }
         } else {
 #pragma unroll
           for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = kin[t];
@@ -423,7 +469,6 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
       }
     }
     lds_barrier();
-    const bool steep = *s_flag != 0;
     // (1c) chunk-level factors; k decayed to the chunk end goes to the record
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
@@ -431,13 +476,6 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
       if (task < NB * DK) {
         const int i = task / DK, c = task % DK;
         const float tau = s_tau[i * DK + c];
-        if constexpr (sizeof(OpT) == 2) {
-          if (steep) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-              sKinv[(16 * i + t) * L::LDK + c] = static_cast<uint16_t>(kin16[it][t >> 1] >> (16 * (t & 1)));
-          }
-        }
         float cb = 1.f, ca = 1.f;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -447,17 +485,24 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
         }
         s_Cb[i * DK + c] = cb;
         if (i == 0) rvec[R::vDecC + c] = ca * tau;
+        // D[i][j] = prod_{j < m < i} tau_m * f(tau_j): the stored inverse-prefix
+        // operand of block j times f(tau_j) is k decayed to the end of block j
+        // (f = sqrt for the balanced fp16 operand, identity otherwise)
+        const bool bal = sizeof(OpT) == 2 && !steep;
         float dd = 1.f;
 #pragma unroll
-        for (int j = NB - 1; j >= 0; --j) {    // D[i][j] = prod_{j < m < i} tau_m
-          if (j < i - 1) s_D[L::dslot(i, j) * DK + c] = dd;
-          if (j < i) dd *= s_tau[j * DK + c];
+        for (int j = NB - 1; j >= 0; --j) {
+          if (j < i) {
+            const float tj = s_tau[j * DK + c];
+            s_D[L::dslot(i, j) * DK + c] = dd * (bal ? sqrtf(tj) : tj);
+            dd *= tj;
+          }
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const int r = 16 * i + t;
           *reinterpret_cast<OpT*>(rec + R::oF + swz_off<R::PPRK>(r, perm_pos(c) * static_cast<int>(sizeof(OpT)))) =
-              (OpT)(static_cast<float>(sKb[r * L::LDK + c]) * ca);
+              (OpT)(kbr[it][t] * ca);
         }
       }
     }
@@ -489,8 +534,9 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
             M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
           }
         } else {
+          const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
 #pragma unroll
-          for (int m = 0; m < NKP; ++m) mma_diag_bf16(acc, M::ld_cont(arow, 32 * m, g), krow, 32 * m, g);
+          for (int m = 0; m < NKP; ++m) mma_bf16_raw(acc, arh, krow, 32 * m, g);
         }
       } else {
         const OpT* krow = sKinv + (16 * j + l16) * L::LDK;
@@ -498,12 +544,29 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
         for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(arow, 32 * m, g), M::ld_cont(krow, 32 * m, g));
       }
     } else {
-      const OpT* brow = sKb + (16 * j + l16) * L::LDK;
+      const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
+      const float* dv = s_D + L::dslot(i, j) * DK;
+      if constexpr (sizeof(OpT) == 2) {
+        if (*s_flag == 0) {
+          const OpT* krh = reinterpret_cast<const OpT*>(krow);
 #pragma unroll
-      for (int m = 0; m < NKP; ++m) {
-        auto fa = M::ld_cont(arow, 32 * m, g);
-        if (i - j >= 2) M::scale_cont(fa, s_D + L::dslot(i, j) * DK, 32 * m, g);
-        M::mma(acc, fa, M::ld_cont(brow, 32 * m, g));
+          for (int m = 0; m < NKP; ++m) {
+            auto fa = M::ld_cont(arow, 32 * m, g);
+            M::scale_cont(fa, dv, 32 * m, g);
+            M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
+          }
+        } else {
+          const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) mma_bf16_raw_scaled(acc, arh, dv, krow, 32 * m, g);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) {
+          auto fa = M::ld_cont(arow, 32 * m, g);
+          M::scale_cont(fa, dv, 32 * m, g);
+          M::mma(acc, fa, M::ld_cont(krow, 32 * m, g));
+        }
       }
     }
     const int s = 16 * j + l16;
@@ -517,6 +580,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
       } else {
         float val = acc[jj];
         if (headdecay) val *= __expf(s_Gi[r] - s_Gi[s]);
+        if (chan && s == r) val = s_qk[r];
         // straight to the record (the state kernel is its only reader)
         *reinterpret_cast<OpT*>(rec + R::oP + swz_off<R::PPRC>(r, perm_pos(s) * static_cast<int>(sizeof(OpT)))) =
             (OpT)((i > j || s <= r) ? val : 0.f);
@@ -563,11 +627,17 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 2 : 6) void 
       for (int idx = tid - 64; idx < C * RowK; idx += kPrepThreads - 64) {
         const int r = idx / RowK, c = (idx % RowK) * VE;
         const float* cb = s_Cb + (r >> 4) * DK + c;
+        const bool steep = sizeof(OpT) == 2 && *s_flag != 0;   // tiles hold bf16 patterns
+        auto get = [&](const OpT* tile, int e) {
+          if (sizeof(OpT) == 2 && steep)
+            return bf16_to_f32(reinterpret_cast<const uint16_t*>(tile)[r * L::LDK + c + e]);
+          return static_cast<float>(tile[r * L::LDK + c + e]);
+        };
         float kx[VE], qx[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
-          kx[e] = static_cast<float>(sK[r * L::LDK + c + e]) * cb[e];
-          qx[e] = static_cast<float>(sQ[r * L::LDK + c + e]) * cb[e];
+          kx[e] = get(sK, e) * cb[e];
+          qx[e] = get(sQ, e) * cb[e];
         }
         put_perm<OpT, R::PPRK>(rec + R::oK, r, c, kx);
         put_perm<OpT, R::PPRK>(rec + R::oQ, r, c, qx);
@@ -703,13 +773,20 @@ __device__ __forceinline__ void dma16_buf(i32x4 rs, void* lds_base, int voff, in
   // the LDS byte address: the pointer in the local address space
   const uint32_t m0 = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(lds_base)));
+  // every scalar operand is wave-uniform; make that explicit so each lands in
+  // an SGPR, and leave M0 as it was found
+  const i32x4 r = i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                        __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+  int saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
-      : "memory", "m0");
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
 }
 
 template <int DK, int DVS, int C, typename In, int DECAY>

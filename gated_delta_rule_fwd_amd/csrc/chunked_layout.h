@@ -110,8 +110,9 @@ struct PrepLayout {
   //   Q    q normalised (per-channel: and decayed)                load .. Gram
   //   K    k normalised (per-channel: and decayed)                load .. Gram
   //   AM   fp32 A (Gram .. inverse); per-channel: staged gate first (load)
-  //   RA   per-channel: Gram factors Kb, Kinv (load .. Gram), then fp32 T;
-  //        otherwise fp32 T over the Q and K tiles, dead after the Gram
+  //   RA   per-channel: the inverse-prefix Gram factor Kinv (load .. Gram),
+  //        then fp32 T; otherwise fp32 T over the Q and K tiles, dead after
+  //        the Gram
   // (P goes from the MFMA accumulators straight to the record.)
   static constexpr size_t oQ = 0;
   static constexpr size_t oK = chunked_layout::al(oQ + kRowTile);
@@ -121,17 +122,17 @@ struct PrepLayout {
   static constexpr size_t oRA(bool ch) {
     return (!ch && kTinQK) ? oQ : chunked_layout::al(oAM + szAM(ch));
   }
-  static constexpr size_t oKinv(bool ch) { return chunked_layout::al(oRA(ch) + kRowTile); }  // after Kb
+  static constexpr size_t oKinv(bool ch) { return oRA(ch); }
   static constexpr size_t szRA(bool ch) {
-    return (!ch && kTinQK) ? 0
-                           : chunked_layout::mx(ch ? (oKinv(ch) - oRA(ch)) + size_t(C) * LDK * KinvBytes : 0,
-                                                kF32CC);
+    return (!ch && kTinQK) ? 0 : chunked_layout::mx(ch ? size_t(C) * LDK * KinvBytes : 0, kF32CC);
   }
-  // D[i][j] (decay of the blocks strictly between j and i) is needed for i - j >= 2
-  static constexpr int ND = NB >= 3 ? (NB - 2) * (NB - 1) / 2 : 1;
-  static constexpr int dslot(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
-  // fp32 vectors: bt Gi Ge (each C), misc[16]; per-channel: tau[NB] Cb[NB] rsq[NB] D[ND] (each DK)
-  static constexpr int kVecRows = 3;
+  // D[i][j], j < i: the A-operand factor of the off-diagonal Gram block (i, j)
+  // (decay of the blocks strictly between j and i, times the factor that turns
+  // block j's inverse-prefix operand into its decay-to-block-end one)
+  static constexpr int ND = NB >= 2 ? NB * (NB - 1) / 2 : 1;
+  static constexpr int dslot(int i, int j) { return i * (i - 1) / 2 + j; }
+  // fp32 vectors: bt Gi Ge qk (each C), misc[16]; per-channel: tau[NB] Cb[NB] rsq[NB] D[ND] (each DK)
+  static constexpr int kVecRows = 4;
   static constexpr int kChanVecs = 3 * NB + ND;
   static constexpr size_t oVec(bool ch) {
     return (!ch && kTinQK) ? chunked_layout::al(oAM + szAM(ch)) : chunked_layout::al(oRA(ch) + szRA(ch));

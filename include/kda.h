@@ -90,10 +90,8 @@ typedef enum {
  * decay and o are not read and may be NULL.
  * Errors: KDA_ERR_NULL if final_state is NULL, or (T > 0) q/k/v/beta/o is
  * NULL or decay is NULL with decay_kind != NONE; KDA_ERR_SHAPE for negative or overflowing sizes;
- * KDA_ERR_UNSUPPORTED for other DK/DV/chunk/dtype/decay_kind values, and for
- * KDA_F32 with DK = 128, chunk_size = 64 and KDA_DECAY_CHANNEL (its tiles
- * exceed the LDS of one compute unit; use chunk_size <= 32 or the recurrent
- * entry point); KDA_ERR_HIP if a launch or the workspace allocation fails.
+ * KDA_ERR_UNSUPPORTED for other DK/DV/chunk/dtype/decay_kind values;
+ * KDA_ERR_HIP if a launch or the workspace allocation fails.
  */
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, const float* initial_state,

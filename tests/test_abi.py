@@ -63,7 +63,6 @@ def chunked(L, **kw):
     (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(B=1 << 20, T=1 << 12, H=8), 2),
     (dict(DK=48), 3), (dict(DV=256), 3), (dict(dtype=7), 3), (dict(kind=5), 3),
     (dict(chunk=128), 3), (dict(chunk=8), 3),
-    (dict(dtype=0, DK=128, DV=128, chunk=64, kind=2, decay=FAKE), 3),
 ])
 def test_chunked_rejects_bad_arguments(L, kw, code):
     assert chunked(L, **kw) == code

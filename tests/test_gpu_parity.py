@@ -70,6 +70,14 @@ CHUNK_CASES = [
     ("gdn_d128", dict(B=1, T=100, H=2, DK=64, DV=128)),
     ("kda_d128", dict(B=1, T=90, H=2, DK=128, DV=32)),
     ("deltanet_d64", dict(B=1, T=64, H=2, DK=32, DV=64, chunk=32)),
+    # per-channel decay steep enough for the wide-range operand fallback
+    ("kda_d128", dict(B=1, T=200, H=2, decay="channel_steep", init_state=True)),
+    ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_steep")),
+    ("fp32_small", dict(T=70, chunk=32, decay="channel_steep", init_state=True)),
+    # fp32 at DK = 128: the state kernel's single-buffer LDS plan
+    ("fp32_small", dict(B=1, T=150, H=2, DK=128, DV=128, chunk=64, init_state=True)),
+    ("fp32_small", dict(B=1, T=100, H=2, DK=128, DV=64, chunk=64, decay="channel_softplus")),
+    ("fp32_small", dict(B=1, T=90, H=3, DK=128, DV=128, chunk=32, decay="none")),
 ]
 
 

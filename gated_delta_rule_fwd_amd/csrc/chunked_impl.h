@@ -789,8 +789,14 @@ __device__ __forceinline__ void dma16_buf(i32x4 rs, void* lds_base, int voff, in
       : "memory");
 }
 
+// State-kernel workgroup: DVS/16 owner waves that compute, and as many
+// helper waves that copy the next chunk into LDS, so the owners never wait to
+// issue a copy.
+template <int DVS> constexpr int state_waves() { return 2 * (DVS / 16); }
+
 template <int DK, int DVS, int C, typename In, int DECAY>
-__global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
+__global__ __launch_bounds__(64 * state_waves<DVS>(), state_waves<DVS>() > 4 ? 2 : 1)
+void state_kernel(StateParams p) {
   using OpT = typename OpOf<In>::T;
   using M = Mma<OpT>;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
@@ -807,9 +813,10 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   // issues its share in kSlots instruction slots
   constexpr int nRec = static_cast<int>(R::bytes / 16), nRecI = (nRec + 63) / 64;
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
-  constexpr int kSlotsR = (nRecI + kWaves - 1) / kWaves, kSlotsV = (nValI + kWaves - 1) / kWaves;
-  constexpr int kSlots = kSlotsR + kSlotsV;
-  static_assert(DVS % 16 == 0 && NOWN <= kWaves, "slice width");
+  constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
+  constexpr int kStThreads = 64 * state_waves<DVS>();
+  constexpr int kSlotsR = (nRecI + NHELP - 1) / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
 
   extern __shared__ __align__(256) unsigned char smem[];
@@ -852,36 +859,36 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) vo[jj] = swzv_off<L::PPRV>(4 * g + jj, (16 * wave + l16) * AB);
 
-  // Per-lane copy offsets, the same for every chunk: value piece of slot s is
-  // row vr[s], at byte voff[s] from the chunk's first value element.
+  // Per-lane copy offsets of a helper wave, the same for every chunk: value
+  // piece of slot s is row vr[s], at byte voff[s] from the chunk's first
+  // value element.
+  const int hw = wave - NOWN;                // helper index (helper waves)
   int vr[kSlotsV], voff[kSlotsV];
 #pragma unroll
   for (int sv = 0; sv < kSlotsV; ++sv) {
-    const int piece = (sv * kWaves + wave) * 64 + lane;
+    const int piece = (sv * NHELP + hw) * 64 + lane;
     const int r = piece / L::PPRV, q = piece % L::PPRV;
     vr[sv] = piece < nVal ? r : C;           // C: no copy
     voff[sv] = r * rowV + (q ^ swzv<L::PPRV>(r)) * 16;
   }
 
-  // Copy slots [s0, s1) of chunk c's record and value rows into LDS buffer
-  // `buf` (asynchronous; slot s of a wave is one 1 KiB copy instruction).
-  auto issue = [&](int c, int buf, int s0, int s1) {
+  // Copy chunk c's record and value rows into LDS buffer `buf` (helper
+  // waves, asynchronous; slot s of a helper is one 1 KiB copy instruction).
+  auto issue = [&](int c, int buf) {
     unsigned char* dst = smem + buf * L::kBuf;
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::bytes, static_cast<int>(R::bytes));
     const int t0 = c * C, Lc = min(C, Trem - t0);
     const i32x4 rv =
         rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
+    for (int sl = 0; sl < kSlotsR; ++sl) {
+      const int j = sl * NHELP + hw;
+      if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
+        dma16_buf(rr, dst + j * 1024, lane * 16, j * 1024);
+    }
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      if (sl < s0 || sl >= s1) continue;
-      if (sl < kSlotsR) {
-        const int j = sl * kWaves + wave;
-        if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
-          dma16_buf(rr, dst + j * 1024, lane * 16, j * 1024);
-      } else {
-        const int sv = sl - kSlotsR, j = sv * kWaves + wave;
-        if (j < nValI && vr[sv] < Lc) dma16_buf(rv, dst + L::oV + j * 1024, voff[sv], 0);
-      }
+    for (int sv = 0; sv < kSlotsV; ++sv) {
+      const int j = sv * NHELP + hw;
+      if (j < nValI && vr[sv] < Lc) dma16_buf(rv, dst + L::oV + j * 1024, voff[sv], 0);
     }
   };
   // After the copy of chunk c into `buf` has landed: value rows past the
@@ -891,7 +898,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
     const int Lc = min(C, Trem - c * C);
     if (Lc < C) {
       unsigned char* dst = smem + buf * L::kBuf + L::oV;
-      for (int piece = tid; piece < nVal; piece += kThreads)
+      for (int piece = tid; piece < nVal; piece += kStThreads)
         if (piece / L::PPRV >= Lc) *reinterpret_cast<u32x4*>(dst + piece * 16) = u32x4{0, 0, 0, 0};
     }
   };
@@ -911,13 +918,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   }
 
   if (nchunks > 0) {
-    issue(0, 0, 0, kSlots);
+    if (!owner) issue(0, 0);
     finish(0, 0);
   }
   lds_barrier();
 
-  // Output rows of a chunk: stored at the start of the next one, when the
-  // wave's memory queue holds no copies.
+  // Output rows of a chunk: stored at the start of the next one.
   f32x4 Oprev[NB];
   const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
   auto store_out = [&](int c) {
@@ -934,9 +940,8 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
   // address below is a per-lane base plus an immediate).
   auto step = [&](auto cur_tag, int c) {
     constexpr int cur = decltype(cur_tag)::value;
-    // the next chunk's copies go out in three parts between the products
+    // the helpers copy the next chunk into the other buffer meanwhile
     const bool pre = L::NBUF == 2 && c + 1 < nchunks;
-    constexpr int kS1 = kSlots / 3, kS2 = 2 * kSlots / 3;
 
     if (owner) {
       const unsigned char* bq = smem + cur * L::kBuf;
@@ -949,7 +954,6 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
       const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
 
       if (c > 0) store_out(c - 1);
-      if (pre) issue(c + 1, cur ^ 1, 0, kS1);
       typename M::frag Sf[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
@@ -970,7 +974,6 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
           M::mma(Ol[rt], Sf[m], fq[m]);
         }
       }
-      if (pre) issue(c + 1, cur ^ 1, kS1, kS2);
       // X = V - (K * exp(Gx)) S0
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
@@ -1017,7 +1020,6 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
 #pragma unroll
         for (int m = 0; m <= rt / 2; ++m) M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
       }
-      if (pre) issue(c + 1, cur ^ 1, kS2, kSlots);
       // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
@@ -1049,12 +1051,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_kernel(StateParams p) {
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
     } else if (pre) {
-      issue(c + 1, cur ^ 1, 0, kSlots);
+      issue(c + 1, cur ^ 1);
     }
     if (c + 1 < nchunks) {
       if (L::NBUF == 1) {
         lds_barrier();              // every wave is done with the only buffer
-        issue(c + 1, 0, 0, kSlots);
+        if (!owner) issue(c + 1, 0);
       }
       finish(c + 1, L::NBUF == 2 ? (cur ^ 1) : 0);
       lds_barrier();                // the next chunk is visible to all waves
@@ -1107,7 +1109,7 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
     fp<<<dim3(nwg_prep), dim3(kPrepThreads), LP::bytes(chan), s>>>(pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    fs<<<dim3(nwg_state), dim3(kThreads), LS::bytes, s>>>(sp);
+    fs<<<dim3(nwg_state), dim3(64 * state_waves<DVS>()), LS::bytes, s>>>(sp);
     return hipGetLastError();
   }
 }

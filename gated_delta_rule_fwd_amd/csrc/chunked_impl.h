@@ -139,6 +139,23 @@ __device__ __forceinline__ void mma_bf16_raw(f32x4& acc, const uint16_t* a_row, 
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
                                                __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
 }
+// bf16 operand of 8 elements from two accumulator tiles (rows 4g..4g+3 of
+// each), rounded to nearest even; and the bf16 product.
+__device__ __forceinline__ bf16x8 bf_from_acc(const f32x4& a, const f32x4& b) {
+  return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+}
+// The rounding remainder of bf_from_acc(a, b) == hi, itself rounded to bf16:
+// hi + lo carries about 16 significant bits.
+__device__ __forceinline__ bf16x8 bf_lo(const f32x4& a, const f32x4& b, const bf16x8& hi) {
+  return bf16x8{(__bf16)(a[0] - (float)hi[0]), (__bf16)(a[1] - (float)hi[1]),
+                (__bf16)(a[2] - (float)hi[2]), (__bf16)(a[3] - (float)hi[3]),
+                (__bf16)(b[0] - (float)hi[4]), (__bf16)(b[1] - (float)hi[5]),
+                (__bf16)(b[2] - (float)hi[6]), (__bf16)(b[3] - (float)hi[7])};
+}
+__device__ __forceinline__ void mma_bf(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
 // The same with the A operand scaled per k (v[k0 + 8g + e]) in fp32 and
 // rounded once more to bf16.
 __device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* a_row, const float* v,
@@ -170,6 +187,7 @@ struct PrepParams {
 };
 
 struct StateParams {
+  const void* k;                  // raw k rows (records without a K tile)
   const void* v; const unsigned char* ws;
   const float* init; float* o; float* state;
   int T, H, DV, nchunks, nsl, xcd_map;
@@ -243,6 +261,17 @@ __device__ __forceinline__ void put_perm(unsigned char* tile, int r, int e0, con
   }
 }
 
+// Eight consecutive elements e0.. of row r of a record tile kept in natural
+// element order (one 16-byte store).
+template <typename OpT, int PPR>
+__device__ __forceinline__ void put_nat(unsigned char* tile, int r, int e0, const float (&x)[8]) {
+  static_assert(sizeof(OpT) == 2, "fp16 tiles");
+  f16x8 hv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+  *reinterpret_cast<f16x8*>(tile + swz_off<PPR>(r, 2 * e0)) = hv;
+}
+
 // ------------------------------------------------------------- prep kernel --
 
 // Eight waves per workgroup: the chunk's work is short, so more waves hide
@@ -280,7 +309,9 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
   const int t0 = (p.c0 + ch) * C;
   const int Lc = min(C, T - t0);
   const long tok0 = static_cast<long>(b) * T + t0;   // first token of the chunk
-  unsigned char* rec = p.ws + (static_cast<size_t>(head) * p.nchunks + ch) * R::bytes;
+  // the chunk's record image; the workspace holds its bytes from R::gOff on
+  unsigned char* rec = reinterpret_cast<unsigned char*>(
+      reinterpret_cast<uintptr_t>(p.ws) + (static_cast<size_t>(head) * p.nchunks + ch) * R::gBytes - R::gOff);
   float* rvec = reinterpret_cast<float*>(rec + R::oVec);
 
   OpT* sQ = reinterpret_cast<OpT*>(smem + L::oQ);
@@ -293,7 +324,8 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
   float* s_bt = sv;
   float* s_Gi = sv + C;
   float* s_Ge = sv + 2 * C;
-  float* s_qk = sv + 3 * C;                    // per-channel decay: q_hat . k_hat per token
+  float* s_qk = sv + 3 * C;                    // per-channel decay: q_hat . k_hat per token;
+  float* s_fk = s_qk;                          // raw K: the row factor of k
   float* s_misc = sv + 4 * C;                  // [1] = steep-gate flag
   int* s_flag = reinterpret_cast<int*>(s_misc + 1);
   float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
@@ -355,7 +387,13 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
       if (r < C) {
         store16<OpT>(sQ + r * L::LDK + seg * V, qv);
         store16<OpT>(sK + r * L::LDK + seg * V, kv);
-        if (!chan) {   // final record operands already
+        if constexpr (R::kRawK) {
+          // the state kernel takes k as it is; its row factor goes into the
+          // record's per-token vectors below (zero past the sequence end,
+          // where the state kernel's rows are copies)
+          put_nat<OpT, R::PPRK>(rec + R::oQ, r, seg * V, qv);
+          if (seg == 0) s_fk[r] = r < Lc ? fk : 0.f;
+        } else if (!chan) {   // final record operands already
           put_perm<OpT, R::PPRK>(rec + R::oQ, r, seg * V, qv);
           put_perm<OpT, R::PPRK>(rec + R::oK, r, seg * V, kv);
         } else {
@@ -379,7 +417,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
         s_bt[lane] = bt;
         s_Gi[lane] = G;
         s_Ge[lane] = Gx;
-        if (headdecay) {
+        if (headdecay && !R::kRawK) {
           rvec[R::vEG + lane] = __expf(G);
           rvec[R::vEGx + lane] = __expf(Gx);
           rvec[R::vEF + lane] = __expf(Glast - G);
@@ -392,6 +430,17 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
     }
   }
   lds_barrier();
+
+  if constexpr (R::kRawK) {
+    // per-token record vectors, k's row factor folded into the two that
+    // multiply its products
+    if (wave == 0 && lane < C) {
+      const float Gi = s_Gi[lane], Gl = s_Gi[C - 1];
+      rvec[R::vEG + lane] = __expf(Gi);
+      rvec[R::vEGx + lane] = __expf(s_Ge[lane]) * s_fk[lane];
+      rvec[R::vEF + lane] = __expf(Gl - Gi) * s_fk[lane];
+    }
+  }
 
   if constexpr (chan) {
     if constexpr (sizeof(OpT) == 2) {
@@ -693,6 +742,13 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 }
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // MFMA fragments from a chunk record in LDS (tiles with rows of 16-byte
 // pieces, elements in perm_pos order, swizzled).  The swizzle repeats every
@@ -809,15 +865,19 @@ void state_kernel(StateParams p) {
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
   constexpr int NOWN = DVS / 16;             // waves that own state columns
   constexpr int NH = (NB + 1) / 2;           // 32-wide k steps over the chunk's tokens
-  // 16-byte copies per chunk: the record, then the value rows; each wave
-  // issues its share in kSlots instruction slots
-  constexpr int nRec = static_cast<int>(R::bytes / 16), nRecI = (nRec + 63) / 64;
+  // 16-byte copies per chunk, each helper wave issuing its share: (raw K)
+  // the k rows, the record, the value rows
+  constexpr bool rawk = R::kRawK;
+  constexpr int nRec = static_cast<int>(R::gBytes / 16), nRecI = (nRec + 63) / 64;
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
+  constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
   constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
   constexpr int kStThreads = 64 * state_waves<DVS>();
   constexpr int kSlotsR = (nRecI + NHELP - 1) / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  constexpr int kSlotsQ = rawk ? (nQKI + NHELP - 1) / NHELP : 0;
   static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
+  static_assert(nQK % 64 == 0, "k copies fill whole instructions");
 
   extern __shared__ __align__(256) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -841,12 +901,14 @@ void state_kernel(StateParams p) {
   }
   const int b = head / H, h = head % H;
   const int n0 = slice * DVS;   // first value column of this slice
-  const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::bytes;
+  const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::gBytes;
   const In* gv = static_cast<const In*>(p.v);
+  const In* gk = static_cast<const In*>(p.k);
   const long seq0 = static_cast<long>(b) * T + static_cast<long>(p.c0) * C;   // first token of this launch
   const int Trem = T - p.c0 * C;             // tokens from there to the sequence end
   const int nchunks = p.nchunks;
   const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
+  const int rowK = H * DK * AB;              // ... of k
   const int rowO = H * DV * 4;               // ... and of o
 
   RecFrags<DK, C, OpT> fr;
@@ -859,53 +921,84 @@ void state_kernel(StateParams p) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) vo[jj] = swzv_off<L::PPRV>(4 * g + jj, (16 * wave + l16) * AB);
 
-  // Per-lane copy offsets of a helper wave, the same for every chunk: value
-  // piece of slot s is row vr[s], at byte voff[s] from the chunk's first
-  // value element.
+  // ---- the state slice: owner wave w keeps value columns n0 + 16w .. +15 ----
+  const bool owner = wave < NOWN;
   const int hw = wave - NOWN;                // helper index (helper waves)
+  // Per-lane copy offsets of a helper wave, the same for every chunk: value
+  // piece of slot s is row vr[s] (-1: past the value rows, no copy), at byte
+  // voff[s] from the chunk's first value element; k piece of slot s is row
+  // kr[s], at byte kvo[s] from the chunk's first k element, landing at the
+  // swizzled position of the K tile.
   int vr[kSlotsV], voff[kSlotsV];
 #pragma unroll
   for (int sv = 0; sv < kSlotsV; ++sv) {
     const int piece = (sv * NHELP + hw) * 64 + lane;
     const int r = piece / L::PPRV, q = piece % L::PPRV;
-    vr[sv] = piece < nVal ? r : C;           // C: no copy
+    vr[sv] = piece < nVal ? r : -1;
     voff[sv] = r * rowV + (q ^ swzv<L::PPRV>(r)) * 16;
   }
+  int kr[kSlotsQ > 0 ? kSlotsQ : 1], kvo[kSlotsQ > 0 ? kSlotsQ : 1];
+#pragma unroll
+  for (int sq = 0; sq < kSlotsQ; ++sq) {
+    const int w = (sq * NHELP + hw) * 64 + lane;   // piece of the K tile
+    const int r = w / R::PPRK, pos = w % R::PPRK;
+    kr[sq] = r;
+    kvo[sq] = r * rowK + (pos ^ swz<R::PPRK>(r)) * 16;
+  }
 
-  // Copy chunk c's record and value rows into LDS buffer `buf` (helper
-  // waves, asynchronous; slot s of a helper is one 1 KiB copy instruction).
+  // Copy chunk c into LDS buffer `buf` (helper waves, asynchronous; slot s of
+  // a helper is one 1 KiB copy instruction).  Rows past the sequence end copy
+  // the chunk's row 0 instead (finite data; their products only meet zero
+  // rows of T and P, and value rows are cleared once the copies land).
   auto issue = [&](int c, int buf) {
     unsigned char* dst = smem + buf * L::kBuf;
-    const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::bytes, static_cast<int>(R::bytes));
+    const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
     const int t0 = c * C, Lc = min(C, Trem - t0);
+    if constexpr (rawk) {
+      const i32x4 rk = rsrc(gk + ((seq0 + t0) * H + h) * static_cast<long>(DK), (Lc - 1) * rowK + DK * AB);
+#pragma unroll
+      for (int sq = 0; sq < kSlotsQ; ++sq) {
+        const int j = sq * NHELP + hw;
+        if (j < nQKI) dma16_buf(rk, dst + R::oK + j * 1024, kr[sq] < Lc ? kvo[sq] : 0, 0);
+      }
+    }
     const i32x4 rv =
         rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
       if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
-        dma16_buf(rr, dst + j * 1024, lane * 16, j * 1024);
+        dma16_buf(rr, dst + R::gOff + j * 1024, lane * 16, j * 1024);
     }
 #pragma unroll
     for (int sv = 0; sv < kSlotsV; ++sv) {
       const int j = sv * NHELP + hw;
-      if (j < nValI && vr[sv] < Lc) dma16_buf(rv, dst + L::oV + j * 1024, voff[sv], 0);
+      if (j < nValI && vr[sv] >= 0) dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
     }
   };
   // After the copy of chunk c into `buf` has landed: value rows past the
-  // sequence end read as zero.
+  // sequence end read as zero (each helper clears the pieces it copied).
   auto finish = [&](int c, int buf) {
     wait_vm();
     const int Lc = min(C, Trem - c * C);
-    if (Lc < C) {
+    if (!owner && Lc < C) {
       unsigned char* dst = smem + buf * L::kBuf + L::oV;
-      for (int piece = tid; piece < nVal; piece += kStThreads)
-        if (piece / L::PPRV >= Lc) *reinterpret_cast<u32x4*>(dst + piece * 16) = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int sv = 0; sv < kSlotsV; ++sv) {
+        const int j = sv * NHELP + hw;
+        if (j < nValI && vr[sv] >= Lc) *reinterpret_cast<u32x4*>(dst + j * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+      }
     }
   };
 
-  // ---- the state slice: owner wave w keeps value columns n0 + 16w .. +15 ----
-  const bool owner = wave < NOWN;
   const int ncol = n0 + 16 * wave + l16;   // this lane's value column (owner waves)
+  // Row j of lane group g of tile t holds key channel srow(t, j).  With the
+  // record's perm_pos order the tiles are plain 16-row bands; with raw K
+  // (natural order Q and K rows) tiles 2m and 2m+1 interleave the channels of
+  // the 32-channel block m in fours, so that a lane's 8 operand elements are
+  // 8 consecutive channels in both layouts.
+  auto srow = [&](int t, int j) {
+    return rawk ? 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j : 16 * t + 4 * g + j;
+  };
   f32x4 S[NKT];
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
@@ -913,7 +1006,7 @@ void state_kernel(StateParams p) {
     if (owner && p.init) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        S[t][j] = p.init[((static_cast<long>(b) * H + h) * DK + 16 * t + 4 * g + j) * DV + ncol];
+        S[t][j] = p.init[((static_cast<long>(b) * H + h) * DK + srow(t, j)) * DV + ncol];
     }
   }
 
@@ -954,23 +1047,34 @@ void state_kernel(StateParams p) {
       const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
 
       if (c > 0) store_out(c - 1);
+      // Raw K: the products with k run in bf16 (its rows as given, S0 and D
+      // rounded to bf16, D in two parts); k's row factor is in the
+      // per-token vectors.
       typename M::frag Sf[NKP];
+      [[maybe_unused]] bf16x8 Sb[NKP];
 #pragma unroll
-      for (int m = 0; m < NKP; ++m) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
+      for (int m = 0; m < NKP; ++m) {
+        Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
+        if constexpr (rawk) Sb[m] = bf_from_acc(S[2 * m], S[2 * m + 1]);
+      }
       // K S0 and S0^T Q^T: both read only S0, so their products interleave
       f32x4 Xl[NB], Ol[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        typename M::frag fk[NKP], fq[NKP];
+        typename M::frag fq[NKP];
+        [[maybe_unused]] typename M::frag fk[NKP];
+        [[maybe_unused]] bf16x8 fkb[NKP];
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
-          fk[m] = fr.kq(sK, rt, m);
+          if constexpr (rawk) fkb[m] = __builtin_bit_cast(bf16x8, fr.kq(sK, rt, m));
+          else fk[m] = fr.kq(sK, rt, m);
           fq[m] = fr.kq(sQ, rt, m);
         }
         Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
-          M::mma(Xl[rt], fk[m], Sf[m]);
+          if constexpr (rawk) mma_bf(Xl[rt], fkb[m], Sb[m]);
+          else M::mma(Xl[rt], fk[m], Sf[m]);
           M::mma(Ol[rt], Sf[m], fq[m]);
         }
       }
@@ -993,7 +1097,7 @@ void state_kernel(StateParams p) {
         for (int jj = 0; jj < 4; ++jj) {
           const int r = 16 * rt + 4 * g + jj;
           float ks = Xl[rt][jj];
-          if (headdecay) ks *= svec[R::vEGx + r];
+          if (headdecay || rawk) ks *= svec[R::vEGx + r];
           Xl[rt][jj] = vv[jj] - ks;
         }
       }
@@ -1030,23 +1134,46 @@ void state_kernel(StateParams p) {
           S[t] *= svec[R::vMisc];
         }
       }
-      if (headdecay) {
+      if (headdecay || rawk) {
         // the per-token factor goes on D's rows
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) Dl[st][jj] *= svec[R::vEF + 16 * st + 4 * g + jj];
         }
-#pragma unroll
-        for (int m = 0; m < NH; ++m)
-          Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
       }
-      const unsigned char* KY = chan ? sKF : sK;
+      if constexpr (rawk) {
+        // D in two bf16 parts (hi + lo), k as it is
+        bf16x8 Db[NH];
+        bf16x8 Dlo[NH];
 #pragma unroll
-      for (int t = 0; t < NKT; ++t) {
+        for (int m = 0; m < NH; ++m) {
+          const f32x4 d1 = 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0};
+          Db[m] = bf_from_acc(Dl[2 * m], d1);
+          Dlo[m] = bf_lo(Dl[2 * m], d1, Db[m]);
+        }
 #pragma unroll
-        for (int m = 0; m < NH; ++m)
-          M::mma(S[t], fr.tok(KY, m, t, 2 * m + 1 < NB), Df[m]);
+        for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+          for (int m = 0; m < NH; ++m) {
+            const bf16x8 kt = __builtin_bit_cast(bf16x8, fr.tok(sK, m, t, 2 * m + 1 < NB));
+            mma_bf(S[t], kt, Db[m]);
+            mma_bf(S[t], kt, Dlo[m]);
+          }
+        }
+      } else {
+        if (headdecay) {
+#pragma unroll
+          for (int m = 0; m < NH; ++m)
+            Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
+        }
+        const unsigned char* KY = chan ? sKF : sK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+          for (int m = 0; m < NH; ++m)
+            M::mma(S[t], fr.tok(KY, m, t, 2 * m + 1 < NB), Df[m]);
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
@@ -1074,7 +1201,7 @@ void state_kernel(StateParams p) {
     for (int t = 0; t < NKT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        p.state[((static_cast<long>(b) * H + h) * DK + 16 * t + 4 * g + j) * DV + ncol] = S[t][j];
+        p.state[((static_cast<long>(b) * H + h) * DK + srow(t, j)) * DV + ncol] = S[t][j];
     }
   }
 }
@@ -1143,7 +1270,7 @@ template <int OpBytes>
 size_t record_bytes(int DK, int C, bool chan) {
 #define KDA_R(dk, c)                                                                       \
   if (DK == dk && C == c)                                                                  \
-    return chan ? RecLayout<dk, c, OpBytes, true>::bytes : RecLayout<dk, c, OpBytes, false>::bytes;
+    return chan ? RecLayout<dk, c, OpBytes, true>::gBytes : RecLayout<dk, c, OpBytes, false>::gBytes;
   KDA_R(32, 16) KDA_R(64, 16) KDA_R(128, 16) KDA_R(32, 32) KDA_R(64, 32) KDA_R(128, 32)
   KDA_R(32, 64) KDA_R(64, 64) KDA_R(128, 64)
 #undef KDA_R

@@ -59,10 +59,10 @@ __host__ __device__ constexpr int perm_pos(int e) {
   return (e & ~31) + 4 * (2 * ((e >> 2) & 3) + ((e >> 4) & 1)) + (e & 3);
 }
 
-// Per-chunk record in the workspace (global memory).  Each tile has one row
-// per token of the chunk, elements in perm_pos order, rows unpadded and
-// swizzled (swz above), so that the state kernel copies the record into LDS
-// as it is.  OpBytes: 2 (fp16 operands) or 4 (fp32).
+// Per-chunk record: the image of one chunk in the state kernel's LDS.  Each
+// tile has one row per token of the chunk, rows unpadded and swizzled (swz
+// above), elements in perm_pos order (raw K below: natural order).  OpBytes:
+// 2 (fp16 operands) or 4 (fp32).
 //   Q    q normalised and scaled; per-channel decay: times exp(G)
 //   K    k normalised; per-channel decay: times exp(Gx)
 //   F    per-channel decay only: k normalised times exp(G_last - G)
@@ -70,24 +70,34 @@ __host__ __device__ constexpr int perm_pos(int e) {
 //   P    masked decayed q k^T, zero above the block diagonal          [C][NCOL]
 //        (NCOL = max(C, 32): the columns a 32-wide k step reads)
 //   vec  fp32: exp(G), exp(Gx), exp(G_last - G) (each C), misc[16] with
-//        misc[0] = exp(G_last); per-channel: exp(G_last) per key channel [DK]
+//        misc[0] = exp(G_last); per-channel: exp(G_last) per key channel [DK];
+//        with raw K the last two also carry k's row factor fk
+// The workspace holds bytes [gOff, bytes) of the image per chunk.  Raw K
+// (bf16 activations without per-channel decay, where K is k times a per-row
+// factor): the K tile heads the image and is not stored; the state kernel
+// copies k's bf16 rows as they are and multiplies with them in bf16, the row
+// factor going onto the products' rows.  Q is then kept in natural element
+// order too (fp16), like the K rows.
 template <int DK, int C, int OpBytes, bool Chan>
 struct RecLayout {
+  static constexpr bool kRawK = !Chan && OpBytes == 2;
   static constexpr int PPRK = DK * OpBytes / 16;   // pieces per Q/K/F row
   static constexpr int NCOL = C < 32 ? 32 : C;
   static constexpr int PPRC = NCOL * OpBytes / 16; // pieces per Tu/P row
   static constexpr size_t kTile = size_t(C) * DK * OpBytes;
   static constexpr size_t kCC = size_t(C) * NCOL * OpBytes;
   static constexpr int kTiles = Chan ? 3 : 2;       // Q, K (, F)
-  static constexpr size_t oQ = 0;
-  static constexpr size_t oK = oQ + kTile;
-  static constexpr size_t oF = oK + kTile;
-  static constexpr size_t oTu = oQ + kTiles * kTile;
+  static constexpr size_t oK = kRawK ? 0 : kTile;
+  static constexpr size_t oQ = kRawK ? kTile : 0;
+  static constexpr size_t oF = 2 * kTile;
+  static constexpr size_t oTu = kTiles * kTile;
   static constexpr size_t oP = oTu + kCC;
   static constexpr size_t oVec = oP + kCC;
   static constexpr int vEG = 0, vEGx = C, vEF = 2 * C, vMisc = 3 * C, vDecC = 3 * C + 16;
   static constexpr int kVecFloats = 3 * C + 16 + (Chan ? DK : 0);
   static constexpr size_t bytes = chunked_layout::al(oVec + size_t(kVecFloats) * 4);
+  static constexpr size_t gOff = kRawK ? kTile : 0;
+  static constexpr size_t gBytes = bytes - gOff;
 };
 
 // LDS of the prep kernel.

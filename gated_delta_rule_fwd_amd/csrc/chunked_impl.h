@@ -742,6 +742,8 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 }
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Wait until at most N of this wave's vector memory operations are
 // outstanding (they complete in issue order).
 template <int N>
@@ -1010,6 +1012,30 @@ void state_kernel(StateParams p) {
     }
   }
 
+  // Helper-formed output (see StateLayout): the S0 operand exchange slots,
+  // the owners' flags, and the D fragments' places in the value rows.
+  constexpr bool hout = L::kHelperOut;
+  const int pw = owner ? wave : hw;          // the owner/helper pair of this wave
+  int* flags = reinterpret_cast<int*>(smem + L::oFlags);
+  auto xs_at = [&](int m) { return smem + L::oXS + ((pw * NKP + m) * 64 + lane) * 16; };
+  int dfo[NH];                               // D fragment m: this lane's 16 bytes
+#pragma unroll
+  for (int m = 0; m < NH; ++m) {
+    const int q = m * 64 + lane, r = q >> 1;
+    dfo[m] = static_cast<int>(L::oV) + r * (L::PPRV * 16) + (((2 * pw + (q & 1)) ^ swzv<L::PPRV>(r)) << 4);
+  }
+  auto put_xs = [&]() {                      // owner: S's fp16 operand fragments
+#pragma unroll
+    for (int m = 0; m < NKP; ++m)
+      *reinterpret_cast<typename M::frag*>(xs_at(m)) = M::from_acc(S[2 * m], S[2 * m + 1]);
+  };
+  if constexpr (hout) {
+    if (owner) {
+      put_xs();
+      if (lane == 0) flags[pw] = 0;
+    }
+  }
+
   if (nchunks > 0) {
     if (!owner) issue(0, 0);
     finish(0, 0);
@@ -1018,7 +1044,7 @@ void state_kernel(StateParams p) {
 
   // Output rows of a chunk: stored at the start of the next one.
   f32x4 Oprev[NB];
-  const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
+  const int obyte = 16 * pw * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
   auto store_out = [&](int c) {
     const int t0 = c * C, Lc = min(C, Trem - t0);
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0);
@@ -1027,6 +1053,37 @@ void state_kernel(StateParams p) {
       const int r = 16 * rt + l16;
       if (r < Lc) *reinterpret_cast<f32x4*>(ob + r * rowO + obyte) = Oprev[rt];
     }
+  };
+  // Helper: finish chunk c's output from buffer bq (its S0^T Q^T part is in
+  // Oprev): scale by exp(G), add D^T P^T, store.  The operands are read
+  // first, so that the buffer can be copied over before the products run.
+  constexpr int NPF = NB * (NB + 2) / 4;     // P fragments: sum over rt of rt/2 + 1
+  struct OutOps {
+    typename M::frag Df[NH], Pf[NPF > 0 ? NPF : 1];
+    float eg[NB];
+  };
+  auto helper_out_load = [&](const unsigned char* bq, OutOps& x) {
+    const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
+#pragma unroll
+    for (int m = 0; m < NH; ++m) x.Df[m] = *reinterpret_cast<const typename M::frag*>(bq + dfo[m]);
+    int n = 0;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      x.eg[rt] = headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f;
+#pragma unroll
+      for (int m = 0; m <= rt / 2; ++m) x.Pf[n++] = fr.cc(bq + R::oP, rt, m);
+    }
+    wait_lgkm();   // the buffer may be copied over from here on
+  };
+  auto helper_out_finish = [&](const OutOps& x, int c) {
+    int n = 0;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      if (headdecay) Oprev[rt] *= x.eg[rt];
+#pragma unroll
+      for (int m = 0; m <= rt / 2; ++m) M::mma(Oprev[rt], x.Df[m], x.Pf[n++]);
+    }
+    store_out(c);
   };
 
   // One chunk step on LDS buffer CUR (a compile-time constant, so every LDS
@@ -1046,7 +1103,7 @@ void state_kernel(StateParams p) {
       const unsigned char* sV = bq + L::oV;
       const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
 
-      if (c > 0) store_out(c - 1);
+      if (!hout && c > 0) store_out(c - 1);
       // Raw K: the products with k run in bf16 (its rows as given, S0 and D
       // rounded to bf16, D in two parts); k's row factor is in the
       // per-token vectors.
@@ -1054,28 +1111,29 @@ void state_kernel(StateParams p) {
       [[maybe_unused]] bf16x8 Sb[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) {
-        Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
+        if (!(hout && rawk)) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
         if constexpr (rawk) Sb[m] = bf_from_acc(S[2 * m], S[2 * m + 1]);
       }
-      // K S0 and S0^T Q^T: both read only S0, so their products interleave
+      // K S0 and (unless the helper forms it) S0^T Q^T: both read only S0, so
+      // their products interleave
       f32x4 Xl[NB], Ol[NB];
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) {
-        typename M::frag fq[NKP];
+        [[maybe_unused]] typename M::frag fq[NKP];
         [[maybe_unused]] typename M::frag fk[NKP];
         [[maybe_unused]] bf16x8 fkb[NKP];
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
           if constexpr (rawk) fkb[m] = __builtin_bit_cast(bf16x8, fr.kq(sK, rt, m));
           else fk[m] = fr.kq(sK, rt, m);
-          fq[m] = fr.kq(sQ, rt, m);
+          if (!hout) fq[m] = fr.kq(sQ, rt, m);
         }
         Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
           if constexpr (rawk) mma_bf(Xl[rt], fkb[m], Sb[m]);
           else M::mma(Xl[rt], fk[m], Sf[m]);
-          M::mma(Ol[rt], Sf[m], fq[m]);
+          if (!hout) M::mma(Ol[rt], Sf[m], fq[m]);
         }
       }
       // X = V - (K * exp(Gx)) S0
@@ -1117,12 +1175,19 @@ void state_kernel(StateParams p) {
 #pragma unroll
       for (int m = 0; m < NH; ++m)
         Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
-      // O^T = S0^T (Q * exp(G))^T + D^T P^T
+      if constexpr (hout) {
+        // D's fragments to this wave's own columns of the value rows
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        if (headdecay) Ol[rt] *= svec[R::vEG + 16 * rt + l16];
+        for (int m = 0; m < NH; ++m)
+          *reinterpret_cast<typename M::frag*>(const_cast<unsigned char*>(bq) + dfo[m]) = Df[m];
+      } else {
+        // O^T = S0^T (Q * exp(G))^T + D^T P^T
 #pragma unroll
-        for (int m = 0; m <= rt / 2; ++m) M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
+        for (int rt = 0; rt < NB; ++rt) {
+          if (headdecay) Ol[rt] *= svec[R::vEG + 16 * rt + l16];
+#pragma unroll
+          for (int m = 0; m <= rt / 2; ++m) M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
+        }
       }
       // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
@@ -1175,10 +1240,39 @@ void state_kernel(StateParams p) {
             M::mma(S[t], fr.tok(KY, m, t, 2 * m + 1 < NB), Df[m]);
         }
       }
+      if constexpr (hout) {
+        if (c + 1 < nchunks) {
+          // S for the helper's next output, once it has read this chunk's
+          while (__hip_atomic_load(&flags[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
+            __builtin_amdgcn_s_sleep(1);
+          put_xs();
+        }
+      } else {
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
-    } else if (pre) {
-      issue(c + 1, cur ^ 1);
+        for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
+      }
+    } else {
+      // helper: the previous chunk's output (its buffer is copied over next)
+      [[maybe_unused]] OutOps ops;
+      if constexpr (hout) {
+        if (c > 0) helper_out_load(smem + (cur ^ 1) * L::kBuf, ops);
+      }
+      if (pre) issue(c + 1, cur ^ 1);
+      if constexpr (hout) {
+        if (c > 0) helper_out_finish(ops, c - 1);
+        // S0^T Q^T of this chunk, S0 from the owner
+        const unsigned char* sQ = smem + cur * L::kBuf + R::oQ;
+        typename M::frag Sx[NKP];
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) Sx[m] = *reinterpret_cast<const typename M::frag*>(xs_at(m));
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          Oprev[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) M::mma(Oprev[rt], Sx[m], fr.kq(sQ, rt, m));
+        }
+        if (lane == 0) __hip_atomic_store(&flags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
     if (c + 1 < nchunks) {
       if (L::NBUF == 1) {
@@ -1195,7 +1289,16 @@ void state_kernel(StateParams p) {
     if (c + 1 < nchunks) step(std::integral_constant<int, L::NBUF == 2 ? 1 : 0>{}, c + 1);
   }
 
-  if (owner && nchunks > 0) store_out(nchunks - 1);
+  if constexpr (hout) {
+    lds_barrier();                  // the last chunk's D fragments
+    if (!owner && nchunks > 0) {
+      OutOps ops;
+      helper_out_load(smem + ((nchunks - 1) & 1) * L::kBuf, ops);
+      helper_out_finish(ops, nchunks - 1);
+    }
+  } else {
+    if (owner && nchunks > 0) store_out(nchunks - 1);
+  }
   if (owner) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {

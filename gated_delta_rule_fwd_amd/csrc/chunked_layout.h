@@ -156,6 +156,15 @@ struct PrepLayout {
 // LDS of the state kernel: NBUF buffers, each one chunk's record image
 // followed by its value rows ([C][DVS] activations, rows swizzled).  With two
 // buffers the next chunk is copied in while the current one is computed.
+//
+// With fp16 operands, bf16 activations, no per-channel decay, two buffers and
+// C >= 32 the helper waves also form the output (kHelperOut; with per-channel
+// decay the kernel is bound by its copies, which the extra exchange would
+// only slow): each owner wave passes its S0 operand fragments to its
+// helper through the XS region (one 1 KiB fragment per 32 key channels, then
+// one int flag per owner: the last chunk whose S0 its helper has read), and
+// its D fragments through its own columns of the chunk's value rows, which
+// no other wave reads.
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
@@ -163,7 +172,13 @@ struct StateLayout {
   static constexpr size_t oV = R::bytes;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
   static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
-  static constexpr size_t bytes = NBUF * kBuf;
+  static constexpr size_t kXS = size_t(DVS / 16) * (DK / 32) * 1024;
+  static constexpr size_t kFlags = 256;
+  static constexpr bool kHelperOut =
+      !Chan && OpBytes == 2 && ActBytes == 2 && C >= 32 && NBUF == 2 && 2 * kBuf + kXS + kFlags <= kMaxLds;
+  static constexpr size_t oXS = NBUF * kBuf;
+  static constexpr size_t oFlags = oXS + kXS;
+  static constexpr size_t bytes = kHelperOut ? oFlags + kFlags : NBUF * kBuf;
 };
 
 }  // namespace kda

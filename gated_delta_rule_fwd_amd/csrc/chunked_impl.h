@@ -157,7 +157,9 @@ __device__ __forceinline__ void mma_bf(f32x4& acc, const bf16x8& a, const bf16x8
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 // The same with the A operand scaled per k (v[k0 + 8g + e]) in fp32 and
-// rounded once more to bf16.
+// rounded once more to bf16; kT: the product with the operands' roles
+// swapped (the transposed tile).
+template <bool kT = false>
 __device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* a_row, const float* v,
                                                     const uint16_t* b_row, int k0, int g) {
   const uint4 a0 = *reinterpret_cast<const uint4*>(a_row + k0 + 8 * g);
@@ -171,8 +173,12 @@ __device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* 
     aw[e] = lo | (hi << 16);
   }
   const uint4 araw = uint4{aw[0], aw[1], aw[2], aw[3]};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
-                                               __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
+  if constexpr (kT)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, braw),
+                                                 __builtin_bit_cast(bf16x8, araw), acc, 0, 0, 0);
+  else
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
+                                                 __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
 }
 
 template <typename In> struct OpOf { using T = _Float16; using KinvT = uint16_t; };
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
 #pragma unroll
       for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
 #pragma unroll
-      for (int m = 0; m < NKP; ++m) M::mma(acc, fa[m], fb[m]);
+      for (int m = 0; m < NKP; ++m) M::mma(acc, fb[m], fa[m]);
     } else if (i == j) {
       if constexpr (sizeof(OpT) == 2) {
         const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
@@ -580,17 +586,17 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
           for (int m = 0; m < NKP; ++m) {
             auto fa = M::ld_cont(arow, 32 * m, g);
             M::scale_cont(fa, s_rsq + i * DK, 32 * m, g);
-            M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
+            M::mma(acc, M::ld_cont(krh, 32 * m, g), fa);
           }
         } else {
           const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
 #pragma unroll
-          for (int m = 0; m < NKP; ++m) mma_bf16_raw(acc, arh, krow, 32 * m, g);
+          for (int m = 0; m < NKP; ++m) mma_bf16_raw(acc, krow, arh, 32 * m, g);
         }
       } else {
         const OpT* krow = sKinv + (16 * j + l16) * L::LDK;
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(arow, 32 * m, g), M::ld_cont(krow, 32 * m, g));
+        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(krow, 32 * m, g), M::ld_cont(arow, 32 * m, g));
       }
     } else {
       const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
@@ -602,37 +608,53 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
           for (int m = 0; m < NKP; ++m) {
             auto fa = M::ld_cont(arow, 32 * m, g);
             M::scale_cont(fa, dv, 32 * m, g);
-            M::mma(acc, fa, M::ld_cont(krh, 32 * m, g));
+            M::mma(acc, M::ld_cont(krh, 32 * m, g), fa);
           }
         } else {
           const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
 #pragma unroll
-          for (int m = 0; m < NKP; ++m) mma_bf16_raw_scaled(acc, arh, dv, krow, 32 * m, g);
+          for (int m = 0; m < NKP; ++m) mma_bf16_raw_scaled<true>(acc, arh, dv, krow, 32 * m, g);
         }
       } else {
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
           auto fa = M::ld_cont(arow, 32 * m, g);
           M::scale_cont(fa, dv, 32 * m, g);
-          M::mma(acc, fa, M::ld_cont(krow, 32 * m, g));
+          M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
         }
       }
     }
-    const int s = 16 * j + l16;
+    // The tile comes out transposed (row block j's rows times block i's): a
+    // lane holds row r = 16 i + l16 at the four consecutive columns s0 ..
+    // s0 + 3, written with one store.
+    const int r = 16 * i + l16, s0 = 16 * j + 4 * g;
+    const f32x4 gs = *reinterpret_cast<const f32x4*>(s_Gi + s0);
+    if (!isP) {
+      const float bt = s_bt[r], ge = s_Ge[r];
+      f32x4 v;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = 16 * i + 4 * g + jj;
-      if (!isP) {
-        float val = acc[jj] * s_bt[r];
-        if (headdecay) val *= __expf(s_Ge[r] - s_Gi[s]);
-        sAm[r * L::LF + s] = (i > j || s < r) ? val : 0.f;
-      } else {
+      for (int jj = 0; jj < 4; ++jj) {
+        float val = acc[jj] * bt;
+        if (headdecay) val *= __expf(ge - gs[jj]);
+        v[jj] = (i > j || s0 + jj < r) ? val : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(sAm + r * L::LF + s0) = v;
+    } else {
+      const float gi = s_Gi[r];
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
         float val = acc[jj];
-        if (headdecay) val *= __expf(s_Gi[r] - s_Gi[s]);
-        if (chan && s == r) val = s_qk[r];
-        // straight to the record (the state kernel is its only reader)
-        *reinterpret_cast<OpT*>(rec + R::oP + swz_off<R::PPRC>(r, perm_pos(s) * static_cast<int>(sizeof(OpT)))) =
-            (OpT)((i > j || s <= r) ? val : 0.f);
+        if (headdecay) val *= __expf(gi - gs[jj]);
+        if (chan && s0 + jj == r) val = s_qk[r];
+        v[jj] = (i > j || s0 + jj <= r) ? val : 0.f;
+      }
+      // straight to the record (the state kernel is its only reader)
+      unsigned char* dst = rec + R::oP + swz_off<R::PPRC>(r, perm_pos(s0) * static_cast<int>(sizeof(OpT)));
+      if constexpr (sizeof(OpT) == 2) {
+        *reinterpret_cast<f16x4*>(dst) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
       }
     }
   }

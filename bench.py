@@ -83,6 +83,22 @@ def to_dev(inp, dev):
     return {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
 
 
+WARM_SECONDS = 0.5
+
+
+def warm_up(call, warmup):
+    """The untimed warm-up: at least `warmup` calls, and more until the GPU
+    has been busy for WARM_SECONDS (its clocks ramp up over the first few
+    hundred milliseconds of work; without this a short run times the ramp)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
+        for _ in range(8):
+            call()
+        n += 8
+        torch.cuda.synchronize()
+
+
 def time_chunked(w, steps, warmup, dev):
     import torch
     from gated_delta_rule_fwd_amd import fwd_chunked
@@ -91,9 +107,7 @@ def time_chunked(w, steps, warmup, dev):
     o = torch.empty((w.B, w.T, w.H, w.DV), device=dev, dtype=torch.float32)
     fs = torch.empty((w.B, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
     args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
-    for _ in range(warmup):
-        fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs)
-    torch.cuda.synchronize()
+    warm_up(lambda: fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs), warmup)
     # Events on torch's current stream, which is the stream the library launches on.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
@@ -118,9 +132,8 @@ def time_decode(w, steps, warmup, dev):
     states = [d["initial_state"], d["initial_state"].clone()]
     o = torch.empty((w.B, w.H, w.DV), device=dev, dtype=torch.float32)
     args = (d["q"], d["k"], d["v"], d["beta"], d["decay"])
-    for i in range(warmup):
-        decode_step(*args, states[i % 2], out=o)
-    torch.cuda.synchronize()
+    it = iter(range(1 << 30))
+    warm_up(lambda: decode_step(*args, states[next(it) % 2], out=o), warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i, (s, e) in enumerate(evs):
@@ -132,25 +145,32 @@ def time_decode(w, steps, warmup, dev):
     return sum(ms) / len(ms)
 
 
+CPU_SECONDS = 10.0
+
+
 def cpu_baseline(w):
-    """The fp64 oracle, as it is, on the first two sequences (all heads, full
-    length) of the workload; scaled to tokens/s of the same head count."""
+    """The fp64 oracle, as it is, on whole sequences (all heads, full length)
+    of the workload, one after another until CPU_SECONDS have passed or all
+    are done; scaled to tokens/s of the same head count."""
     import numpy as np
     from gated_delta_rule_fwd_amd.inputs import make_inputs
     from oracle import kda_scan
     inp = make_inputs(w)
-    nb = min(2, w.B)
-    sl = slice(0, nb)
-    t0 = time.perf_counter()
-    kda_scan(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["beta"][sl],
-             None if inp["decay"] is None else inp["decay"][sl],
-             None if inp["initial_state"] is None else inp["initial_state"][sl])
+    nb, t0, c0 = 0, time.perf_counter(), time.process_time()
+    while nb < w.B and (nb == 0 or time.perf_counter() - t0 < CPU_SECONDS):
+        sl = slice(nb, nb + 1)
+        kda_scan(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["beta"][sl],
+                 None if inp["decay"] is None else inp["decay"][sl],
+                 None if inp["initial_state"] is None else inp["initial_state"][sl])
+        nb += 1
     dt = time.perf_counter() - t0
-    return {"value": nb * w.T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    # threads actually used: the process's CPU time over the wall time
+    cores = max(1, round((time.process_time() - c0) / dt))
+    return {"value": nb * w.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{w.name}: {nb} of {w.B} sequences x {w.H} heads x {w.T} tokens, "
-                      f"NumPy fp64 sequential scan on one host thread "
-                      f"(numpy {np.__version__})"}
+                      f"NumPy fp64 sequential scan (numpy {np.__version__}); "
+                      f"cores = process CPU time / wall time"}
 
 
 def stored_traffic(name):
@@ -227,7 +247,7 @@ def write_traffic(fetch_dir, write_dir):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gdn_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,11 +299,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16+bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "DK": w.DK, "DV": w.DV,
                    "chunk": w.chunk, "decay": w.decay, "initial_state": w.init_state,
-                   "activations": w.dtype, "mfma": "f16 x f16 -> f32", "state": "f32",
+                   "activations": w.dtype, "mfma": "f16 x f16 and bf16 x bf16 -> f32", "state": "f32",
                    "output": "f32"},
         "roofline": roof,
     }

@@ -9,7 +9,9 @@
 //   S'    = diag(exp(g)) S + k_hat delta^T
 // so the whole step needs one read and one write of S.  The kernel is bound
 // by HBM bandwidth: 2 * DK * DV * 4 bytes of state traffic per (batch, head)
-// against about 6 * DK * DV flops.
+// against about 6 * DK * DV flops.  Every value column is independent given
+// the token vectors, so a workgroup takes CS of the DV columns of one
+// (batch, head): more, smaller workgroups keep more of the state in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -18,25 +20,31 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Columns per workgroup.
+template <int DV> constexpr int decode_cols() { return DV > 64 ? 64 : DV; }
+
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     float* __restrict__ state, float* __restrict__ o, float scale, int l2norm) {
-  constexpr int NC4 = DV / 4;             // float4 column groups per state row
+  constexpr int CS = decode_cols<DV>();
+  constexpr int NSPLIT = DV / CS;
+  constexpr int NC4 = CS / 4;             // float4 column groups per state row
   constexpr int NRG = kThreads / NC4;     // row groups
   constexpr int RPT = DK / NRG;           // rows per thread
-  static_assert(RPT >= 1 && DK % NRG == 0, "shape");
+  static_assert(RPT >= 1 && DK % NRG == 0 && DV % CS == 0, "shape");
   constexpr int NW = kThreads / 64;
 
-  __shared__ float s_q[DK], s_k[DK], s_gate[DK], s_v[DV];
+  __shared__ float s_q[DK], s_k[DK], s_gate[DK], s_v[CS];
   __shared__ float s_red[3][NW];
   __shared__ f32x4 s_part[2][NW][NC4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long bh = blockIdx.x;
+  const long bh = blockIdx.x / NSPLIT;
+  const int n0 = (blockIdx.x % NSPLIT) * CS;   // first value column of this workgroup
   const int cg = tid % NC4, rg = tid / NC4;
-  float* S = state + bh * DK * DV;
+  float* S = state + bh * DK * DV + n0;
 
   // Issue the state loads first: they are the bulk of the traffic.
   f32x4 st[RPT];
@@ -58,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     s_gate[c] = gc;
     pq += qc * qc; pk += kc * kc; pqk += qc * kc;
   }
-  for (int n = tid; n < DV; n += kThreads) s_v[n] = act<In>::load1(v + bh * DV + n);
+  for (int n = tid; n < CS; n += kThreads) s_v[n] = act<In>::load1(v + bh * DV + n0 + n);
   pq = group_sum<64>(pq); pk = group_sum<64>(pk); pqk = group_sum<64>(pqk);
   if (lane == 0) { s_red[0][wave] = pq; s_red[1][wave] = pk; s_red[2][wave] = pqk; }
   __syncthreads();
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   for (int e = 0; e < 4; ++e) delta[e] = b * (s_v[4 * cg + e] - r[e]);
   if (rg == 0) {
     const f32x4 out = y + qk * delta;
-    *reinterpret_cast<f32x4*>(o + bh * DV + 4 * cg) = out;
+    *reinterpret_cast<f32x4*>(o + bh * DV + n0 + 4 * cg) = out;
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
 template <typename In>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H), block(kThreads);
+  const dim3 block(kThreads);
   const In* q = static_cast<const In*>(a.q);
   const In* k = static_cast<const In*>(a.k);
   const In* v = static_cast<const In*>(a.v);
@@ -125,6 +133,7 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   const In* de = static_cast<const In*>(a.decay);
 #define KDA_DECODE_CASE(dk, dv)                                                              \
   if (a.DK == dk && a.DV == dv) {                                                            \
+    const dim3 grid(a.B * a.H * (dv / decode_cols<dv>()));                                   \
     decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.state, \
                                                       a.o, a.scale, a.l2norm);              \
     return hipGetLastError();                                                                \

@@ -974,29 +974,37 @@ void state_kernel(StateParams p) {
   // a helper is one 1 KiB copy instruction).  Rows past the sequence end copy
   // the chunk's row 0 instead (finite data; their products only meet zero
   // rows of T and P, and value rows are cleared once the copies land).
-  auto issue = [&](int c, int buf) {
+  // part 1: k rows and the record before P (the tiles a finished chunk's
+  // output no longer reads); part 2: the rest; 0: all of it.
+  constexpr int jP = static_cast<int>((R::oP - R::gOff) / 1024);
+  auto issue = [&](int c, int buf, int part = 0) {
     unsigned char* dst = smem + buf * L::kBuf;
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
     const int t0 = c * C, Lc = min(C, Trem - t0);
-    if constexpr (rawk) {
-      const i32x4 rk = rsrc(gk + ((seq0 + t0) * H + h) * static_cast<long>(DK), (Lc - 1) * rowK + DK * AB);
+    if (part != 2) {
+      if constexpr (rawk) {
+        const i32x4 rk = rsrc(gk + ((seq0 + t0) * H + h) * static_cast<long>(DK), (Lc - 1) * rowK + DK * AB);
 #pragma unroll
-      for (int sq = 0; sq < kSlotsQ; ++sq) {
-        const int j = sq * NHELP + hw;
-        if (j < nQKI) dma16_buf(rk, dst + R::oK + j * 1024, kr[sq] < Lc ? kvo[sq] : 0, 0);
+        for (int sq = 0; sq < kSlotsQ; ++sq) {
+          const int j = sq * NHELP + hw;
+          if (j < nQKI) dma16_buf(rk, dst + R::oK + j * 1024, kr[sq] < Lc ? kvo[sq] : 0, 0);
+        }
       }
     }
-    const i32x4 rv =
-        rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
+      if (part == 1 ? j >= jP : part == 2 ? j < jP : false) continue;
       if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
         dma16_buf(rr, dst + R::gOff + j * 1024, lane * 16, j * 1024);
     }
+    if (part != 1) {
+      const i32x4 rv =
+          rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
 #pragma unroll
-    for (int sv = 0; sv < kSlotsV; ++sv) {
-      const int j = sv * NHELP + hw;
-      if (j < nValI && vr[sv] >= 0) dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
+      for (int sv = 0; sv < kSlotsV; ++sv) {
+        const int j = sv * NHELP + hw;
+        if (j < nValI && vr[sv] >= 0) dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
+      }
     }
   };
   // After the copy of chunk c into `buf` has landed: value rows past the
@@ -1277,9 +1285,13 @@ void state_kernel(StateParams p) {
       // helper: the previous chunk's output (its buffer is copied over next)
       [[maybe_unused]] OutOps ops;
       if constexpr (hout) {
+        // the tiles the previous output does not read go out first
+        if (pre) issue(c + 1, cur ^ 1, 1);
         if (c > 0) helper_out_load(smem + (cur ^ 1) * L::kBuf, ops);
+        if (pre) issue(c + 1, cur ^ 1, 2);
+      } else {
+        if (pre) issue(c + 1, cur ^ 1);
       }
-      if (pre) issue(c + 1, cur ^ 1);
       if constexpr (hout) {
         if (c > 0) helper_out_finish(ops, c - 1);
         // S0^T Q^T of this chunk, S0 from the owner

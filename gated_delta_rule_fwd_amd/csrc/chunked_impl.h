@@ -757,22 +757,10 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
 
 // ------------------------------------------------------------ state kernel --
 
-// Asynchronous 16-byte copy global -> LDS (gfx950 global_load_lds_dwordx4):
-// lane i of the wave writes lds_base + 16 i; lds_base must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
-}
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// Wait until at most N of this wave's vector memory operations are
-// outstanding (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 
 // MFMA fragments from a chunk record in LDS (tiles with rows of 16-byte
 // pieces, elements in perm_pos order, swizzled).  The swizzle repeats every
@@ -843,16 +831,17 @@ __device__ __forceinline__ i32x4 rsrc(const void* base, int bytes) {
   return i32x4{static_cast<int32_t>(a & 0xffffffffu), static_cast<int32_t>((a >> 32) & 0xffffu), bytes,
                0x00020000};
 }
+// The LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
 // Asynchronous 16-byte copy global -> LDS (buffer_load_dwordx4 ... lds):
-// lane i of the wave writes lds_base + 16 i (lds_base wave-uniform, in M0),
+// lane i of the wave writes LDS byte address m0 + 16 i (m0 wave-uniform),
 // reading the buffer at voff (per lane) + soff (uniform).  Written as
 // assembly so that the compiler does not wait for the copy before unrelated
-// LDS reads; the caller waits (wait_vm) and synchronises before the copied
-// data is read.
-__device__ __forceinline__ void dma16_buf(i32x4 rs, void* lds_base, int voff, int soff) {
-  // the LDS byte address: the pointer in the local address space
-  const uint32_t m0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(lds_base)));
+// LDS reads; the caller waits (wait_vm) and synchronises before
+// the copied data is read.
+__device__ __forceinline__ void dma16_buf(i32x4 rs, uint32_t m0, int voff, int soff) {
   // every scalar operand is wave-uniform; make that explicit so each lands in
   // an SGPR, and leave M0 as it was found
   const i32x4 r = i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
@@ -974,14 +963,12 @@ void state_kernel(StateParams p) {
   // a helper is one 1 KiB copy instruction).  Rows past the sequence end copy
   // the chunk's row 0 instead (finite data; their products only meet zero
   // rows of T and P, and value rows are cleared once the copies land).
-  // part 1: k rows and the record before P (the tiles a finished chunk's
-  // output no longer reads); part 2: the rest; 0: all of it.
-  constexpr int jP = static_cast<int>((R::oP - R::gOff) / 1024);
-  auto issue = [&](int c, int buf, int part = 0) {
-    unsigned char* dst = smem + buf * L::kBuf;
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int c, unsigned char* dstp) {
+    const uint32_t dst = lds0 + static_cast<uint32_t>(dstp - smem);
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
     const int t0 = c * C, Lc = min(C, Trem - t0);
-    if (part != 2) {
+    {
       if constexpr (rawk) {
         const i32x4 rk = rsrc(gk + ((seq0 + t0) * H + h) * static_cast<long>(DK), (Lc - 1) * rowK + DK * AB);
 #pragma unroll
@@ -993,11 +980,10 @@ void state_kernel(StateParams p) {
     }
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
-      if (part == 1 ? j >= jP : part == 2 ? j < jP : false) continue;
       if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
         dma16_buf(rr, dst + R::gOff + j * 1024, lane * 16, j * 1024);
     }
-    if (part != 1) {
+    {
       const i32x4 rv =
           rsrc(gv + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0, (Lc - 1) * rowV + DVS * AB);
 #pragma unroll
@@ -1009,17 +995,20 @@ void state_kernel(StateParams p) {
   };
   // After the copy of chunk c into `buf` has landed: value rows past the
   // sequence end read as zero (each helper clears the pieces it copied).
-  auto finish = [&](int c, int buf) {
-    wait_vm();
+  auto zero_tail = [&](int c, unsigned char* buf) {
     const int Lc = min(C, Trem - c * C);
     if (!owner && Lc < C) {
-      unsigned char* dst = smem + buf * L::kBuf + L::oV;
+      unsigned char* dst = buf + L::oV;
 #pragma unroll
       for (int sv = 0; sv < kSlotsV; ++sv) {
         const int j = sv * NHELP + hw;
         if (j < nValI && vr[sv] >= Lc) *reinterpret_cast<u32x4*>(dst + j * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
       }
     }
+  };
+  auto finish = [&](int c, unsigned char* buf) {
+    wait_vm();
+    zero_tail(c, buf);
   };
 
   const int ncol = n0 + 16 * wave + l16;   // this lane's value column (owner waves)
@@ -1046,7 +1035,8 @@ void state_kernel(StateParams p) {
   // the owners' flags, and the D fragments' places in the value rows.
   constexpr bool hout = L::kHelperOut;
   const int pw = owner ? wave : hw;          // the owner/helper pair of this wave
-  int* flags = reinterpret_cast<int*>(smem + L::oFlags);
+  int* flags = reinterpret_cast<int*>(smem + L::oFlags);   // S0 read by the helper: chunk + 1
+  int* dflags = flags + 8;                                  // D written by the owner: chunk + 1
   auto xs_at = [&](int m) { return smem + L::oXS + ((pw * NKP + m) * 64 + lane) * 16; };
   int dfo[NH];                               // D fragment m: this lane's 16 bytes
 #pragma unroll
@@ -1062,13 +1052,13 @@ void state_kernel(StateParams p) {
   if constexpr (hout) {
     if (owner) {
       put_xs();
-      if (lane == 0) flags[pw] = 0;
+      if (lane == 0) flags[pw] = dflags[pw] = 0;
     }
   }
 
   if (nchunks > 0) {
-    if (!owner) issue(0, 0);
-    finish(0, 0);
+    if (!owner) issue(0, smem);
+    finish(0, smem);
   }
   lds_barrier();
 
@@ -1084,9 +1074,8 @@ void state_kernel(StateParams p) {
       if (r < Lc) *reinterpret_cast<f32x4*>(ob + r * rowO + obyte) = Oprev[rt];
     }
   };
-  // Helper: finish chunk c's output from buffer bq (its S0^T Q^T part is in
-  // Oprev): scale by exp(G), add D^T P^T, store.  The operands are read
-  // first, so that the buffer can be copied over before the products run.
+  // Helper: finish chunk c's output from its buffer bq (its S0^T Q^T part is
+  // in Oprev): scale by exp(G), add D^T P^T, store.
   constexpr int NPF = NB * (NB + 2) / 4;     // P fragments: sum over rt of rt/2 + 1
   struct OutOps {
     typename M::frag Df[NH], Pf[NPF > 0 ? NPF : 1];
@@ -1117,13 +1106,16 @@ void state_kernel(StateParams p) {
   };
 
   // One chunk step on LDS buffer CUR (a compile-time constant, so every LDS
-  // address below is a per-lane base plus an immediate).
-  auto step = [&](auto cur_tag, int c) {
+  // address below is a per-lane base plus an immediate), for an owner or a
+  // helper wave (a compile-time choice: the two kinds of wave run separate
+  // loops, so neither holds the other's registers).
+  auto step = [&](auto cur_tag, auto own_tag, int c) {
     constexpr int cur = decltype(cur_tag)::value;
+    constexpr bool own = decltype(own_tag)::value;
     // the helpers copy the next chunk into the other buffer meanwhile
     const bool pre = L::NBUF == 2 && c + 1 < nchunks;
 
-    if (owner) {
+    if constexpr (own) {
       const unsigned char* bq = smem + cur * L::kBuf;
       const unsigned char* sQ = bq + R::oQ;
       const unsigned char* sK = bq + R::oK;
@@ -1210,6 +1202,7 @@ void state_kernel(StateParams p) {
 #pragma unroll
         for (int m = 0; m < NH; ++m)
           *reinterpret_cast<typename M::frag*>(const_cast<unsigned char*>(bq) + dfo[m]) = Df[m];
+        if (lane == 0) __hip_atomic_store(&dflags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       } else {
         // O^T = S0^T (Q * exp(G))^T + D^T P^T
 #pragma unroll
@@ -1282,18 +1275,10 @@ void state_kernel(StateParams p) {
         for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
       }
     } else {
-      // helper: the previous chunk's output (its buffer is copied over next)
-      [[maybe_unused]] OutOps ops;
+      // helper: the next chunk's copies, then (helper-formed output) this
+      // chunk's output
+      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf);
       if constexpr (hout) {
-        // the tiles the previous output does not read go out first
-        if (pre) issue(c + 1, cur ^ 1, 1);
-        if (c > 0) helper_out_load(smem + (cur ^ 1) * L::kBuf, ops);
-        if (pre) issue(c + 1, cur ^ 1, 2);
-      } else {
-        if (pre) issue(c + 1, cur ^ 1);
-      }
-      if constexpr (hout) {
-        if (c > 0) helper_out_finish(ops, c - 1);
         // S0^T Q^T of this chunk, S0 from the owner
         const unsigned char* sQ = smem + cur * L::kBuf + R::oQ;
         typename M::frag Sx[NKP];
@@ -1306,31 +1291,39 @@ void state_kernel(StateParams p) {
           for (int m = 0; m < NKP; ++m) M::mma(Oprev[rt], Sx[m], fr.kq(sQ, rt, m));
         }
         if (lane == 0) __hip_atomic_store(&flags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the rest once the owner's D is in place
+        while (__hip_atomic_load(&dflags[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
+          __builtin_amdgcn_s_sleep(1);
+        OutOps ops;
+        helper_out_load(smem + cur * L::kBuf, ops);
+        helper_out_finish(ops, c);
       }
     }
     if (c + 1 < nchunks) {
       if (L::NBUF == 1) {
         lds_barrier();              // every wave is done with the only buffer
-        if (!owner) issue(c + 1, 0);
+        if constexpr (!own) issue(c + 1, smem);
       }
-      finish(c + 1, L::NBUF == 2 ? (cur ^ 1) : 0);
+      finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
       lds_barrier();                // the next chunk is visible to all waves
     }
   };
 
-  for (int c = 0; c < nchunks; c += 2) {
-    step(std::integral_constant<int, 0>{}, c);
-    if (c + 1 < nchunks) step(std::integral_constant<int, L::NBUF == 2 ? 1 : 0>{}, c + 1);
-  }
-
-  if constexpr (hout) {
-    lds_barrier();                  // the last chunk's D fragments
-    if (!owner && nchunks > 0) {
-      OutOps ops;
-      helper_out_load(smem + ((nchunks - 1) & 1) * L::kBuf, ops);
-      helper_out_finish(ops, nchunks - 1);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, L::NBUF == 2 ? 1 : 0>;
+  if (owner) {
+    for (int c = 0; c < nchunks; c += 2) {
+      step(C0{}, std::true_type{}, c);
+      if (c + 1 < nchunks) step(C1{}, std::true_type{}, c + 1);
     }
   } else {
+    for (int c = 0; c < nchunks; c += 2) {
+      step(C0{}, std::false_type{}, c);
+      if (c + 1 < nchunks) step(C1{}, std::false_type{}, c + 1);
+    }
+  }
+
+  if constexpr (!hout) {
     if (owner && nchunks > 0) store_out(nchunks - 1);
   }
   if (owner) {

@@ -77,7 +77,7 @@ __host__ __device__ constexpr int perm_pos(int e) {
 // factor): the K tile heads the image and is not stored; the state kernel
 // copies k's bf16 rows as they are and multiplies with them in bf16, the row
 // factor going onto the products' rows.  Q is then kept in natural element
-// order too (fp16), like the K rows.
+// order too (fp16), like the K rows, and comes last, after the vectors.
 template <int DK, int C, int OpBytes, bool Chan>
 struct RecLayout {
   static constexpr bool kRawK = !Chan && OpBytes == 2;
@@ -88,14 +88,15 @@ struct RecLayout {
   static constexpr size_t kCC = size_t(C) * NCOL * OpBytes;
   static constexpr int kTiles = Chan ? 3 : 2;       // Q, K (, F)
   static constexpr size_t oK = kRawK ? 0 : kTile;
-  static constexpr size_t oQ = kRawK ? kTile : 0;
   static constexpr size_t oF = 2 * kTile;
-  static constexpr size_t oTu = kTiles * kTile;
+  static constexpr size_t oTu = kRawK ? kTile : kTiles * kTile;
   static constexpr size_t oP = oTu + kCC;
   static constexpr size_t oVec = oP + kCC;
   static constexpr int vEG = 0, vEGx = C, vEF = 2 * C, vMisc = 3 * C, vDecC = 3 * C + 16;
   static constexpr int kVecFloats = 3 * C + 16 + (Chan ? DK : 0);
-  static constexpr size_t bytes = chunked_layout::al(oVec + size_t(kVecFloats) * 4);
+  static constexpr size_t oQ = kRawK ? chunked_layout::al(oVec + size_t(kVecFloats) * 4) : 0;
+  static constexpr size_t bytes =
+      kRawK ? oQ + kTile : chunked_layout::al(oVec + size_t(kVecFloats) * 4);
   static constexpr size_t gOff = kRawK ? kTile : 0;
   static constexpr size_t gBytes = bytes - gOff;
 };
@@ -161,10 +162,10 @@ struct PrepLayout {
 // C >= 32 the helper waves also form the output (kHelperOut; with per-channel
 // decay the kernel is bound by its copies, which the extra exchange would
 // only slow): each owner wave passes its S0 operand fragments to its
-// helper through the XS region (one 1 KiB fragment per 32 key channels, then
-// one int flag per owner: the last chunk whose S0 its helper has read), and
+// helper through the XS region (one 1 KiB fragment per 32 key channels), and
 // its D fragments through its own columns of the chunk's value rows, which
-// no other wave reads.
+// no other wave reads.  Flags (ints after XS): per owner, the chunk (+1)
+// whose S0 its helper has read, and the chunk (+1) whose D it has written.
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;

@@ -172,6 +172,13 @@ def test_chunked_full_size_sampled_heads(name):
     o_s = torch.stack([o[b, :, h] for b, h in heads])
     S_s = torch.stack([S[b, h] for b, h in heads])
     check("chunked sampled", o_s, S_s, o_ref, S_ref, TOL[w.dtype])
+    # every (b, h) at full size, run to run: the waves of a workgroup hand
+    # each other operands through LDS, and any missing wait shows up here
+    for _ in range(3):
+        o2, S2 = fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"],
+                             chunk_size=w.chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o) and torch.equal(S2, S), "full-size run-to-run difference"
 
 
 def test_decode_full_size_sampled_heads():

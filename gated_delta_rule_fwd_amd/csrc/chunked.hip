@@ -106,7 +106,8 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
 
   StateParams sp;
-  sp.k = a.k;
+  sp.q = a.q; sp.k = a.k;
+  sp.l2norm = a.l2norm; sp.scale = a.scale;
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
   sp.o = a.o; sp.state = a.state;
   sp.T = a.T; sp.H = a.H; sp.DV = a.DV;

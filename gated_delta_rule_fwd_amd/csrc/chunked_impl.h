@@ -53,6 +53,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <utility>
+
 namespace kda {
 namespace chunked {
 
@@ -156,6 +158,15 @@ __device__ __forceinline__ bf16x8 bf_lo(const f32x4& a, const f32x4& b, const bf
 __device__ __forceinline__ void mma_bf(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+// acc + the sum of squares of the 8 elements of x (fp32, in pairs)
+__device__ __forceinline__ float sumsq_bf(const bf16x8& x, float acc) {
+  const bf16x2 a = __builtin_shufflevector(x, x, 0, 1), b = __builtin_shufflevector(x, x, 2, 3);
+  const bf16x2 c = __builtin_shufflevector(x, x, 4, 5), d = __builtin_shufflevector(x, x, 6, 7);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(a, a, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(c, c, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(d, d, acc, false);
+}
 // The same with the A operand scaled per k (v[k0 + 8g + e]) in fp32 and
 // rounded once more to bf16; kT: the product with the operands' roles
 // swapped (the transposed tile).
@@ -193,16 +204,31 @@ struct PrepParams {
 };
 
 struct StateParams {
-  const void* k;                  // raw k rows (records without a K tile)
+  const void* q; const void* k;   // raw q, k rows (records without Q, K tiles)
   const void* v; const unsigned char* ws;
   const float* init; float* o; float* state;
   int T, H, DV, nchunks, nsl, xcd_map;
   int c0;                // first chunk of this launch; `init` holds the state entering it
+  int l2norm; float scale;   // q's row factor (raw rows)
 };
 
 // Lower-triangular block pair (i, j), j <= i, of pair index n.
 __host__ __device__ constexpr int pair_i(int n) { int i = 0; while (n > i) { n -= i + 1; ++i; } return i; }
 __host__ __device__ constexpr int pair_j(int n) { int i = 0; while (n > i) { n -= i + 1; ++i; } return n; }
+// f(std::integral_constant<int, i>) for i = 0 .. N-1: a loop whose index is
+// a compile-time constant in the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// P operand fragment n of the state kernel's helper waves: row block
+// pf_ib(n) and 32-token k step pf_m(n), running over ib, then m <= ib / 2.
+__host__ __device__ constexpr int pf_ib(int n) { int i = 0; while (n > i / 2) { n -= i / 2 + 1; ++i; } return i; }
+__host__ __device__ constexpr int pf_m(int n) { int i = 0; while (n > i / 2) { n -= i / 2 + 1; ++i; } return n; }
 
 // Transposed 4 x fp16 read (gfx950 ds_read_b64_tr_b16).  Within each group of
 // 16 lanes, lane j supplies the address of an 8-byte row piece E_j; lane
@@ -265,17 +291,6 @@ __device__ __forceinline__ void put_perm(unsigned char* tile, int r, int e0, con
       *reinterpret_cast<f32x4*>(dst) = f32x4{x[4 * a], x[4 * a + 1], x[4 * a + 2], x[4 * a + 3]};
     }
   }
-}
-
-// Eight consecutive elements e0.. of row r of a record tile kept in natural
-// element order (one 16-byte store).
-template <typename OpT, int PPR>
-__device__ __forceinline__ void put_nat(unsigned char* tile, int r, int e0, const float (&x)[8]) {
-  static_assert(sizeof(OpT) == 2, "fp16 tiles");
-  f16x8 hv;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
-  *reinterpret_cast<f16x8*>(tile + swz_off<PPR>(r, 2 * e0)) = hv;
 }
 
 // ------------------------------------------------------------- prep kernel --
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
       rq[pp] = rk[pp] = rg[pp] = uint4{0, 0, 0, 0};
       if (r < Lc) {
         const long off = ((tok0 + r) * H + h) * DK + seg * V;
-        rq[pp] = *reinterpret_cast<const uint4*>(gq + off);
+        if constexpr (!R::kRawK) rq[pp] = *reinterpret_cast<const uint4*>(gq + off);
         rk[pp] = *reinterpret_cast<const uint4*>(gk + off);
         if (chan) rg[pp] = *reinterpret_cast<const uint4*>(gg + off);
       }
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-        fq *= inv_norm(dpp_group_sum<LPR>(sq));
+        if constexpr (!R::kRawK) fq *= inv_norm(dpp_group_sum<LPR>(sq));
         fk = inv_norm(dpp_group_sum<LPR>(sk));
       }
 #pragma unroll
@@ -391,13 +406,12 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
         if (r < C && seg == 0) s_qk[r] = qk;
       }
       if (r < C) {
-        store16<OpT>(sQ + r * L::LDK + seg * V, qv);
+        if constexpr (!R::kRawK) store16<OpT>(sQ + r * L::LDK + seg * V, qv);
         store16<OpT>(sK + r * L::LDK + seg * V, kv);
         if constexpr (R::kRawK) {
-          // the state kernel takes k as it is; its row factor goes into the
-          // record's per-token vectors below (zero past the sequence end,
-          // where the state kernel's rows are copies)
-          put_nat<OpT, R::PPRK>(rec + R::oQ, r, seg * V, qv);
+          // the state kernel takes q and k as they are; k's row factor goes
+          // into the record's per-token vectors below (zero past the
+          // sequence end, where the state kernel's rows are copies)
           if (seg == 0) s_fk[r] = r < Lc ? fk : 0.f;
         } else if (!chan) {   // final record operands already
           put_perm<OpT, R::PPRK>(rec + R::oQ, r, seg * V, qv);
@@ -445,6 +459,8 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
       rvec[R::vEG + lane] = __expf(Gi);
       rvec[R::vEGx + lane] = __expf(s_Ge[lane]) * s_fk[lane];
       rvec[R::vEF + lane] = __expf(Gl - Gi) * s_fk[lane];
+      rvec[R::vG + lane] = Gi;
+      rvec[R::vFK + lane] = s_fk[lane];
     }
   }
 
@@ -565,7 +581,8 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
   }
 
   // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-  for (int job = wave; job < 2 * NPAIR; job += kPrepWaves) {
+  // (raw rows: A only; the state kernel forms P)
+  for (int job = wave; job < (R::kRawK ? NPAIR : 2 * NPAIR); job += kPrepWaves) {
     const bool isP = job >= NPAIR;
     const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
     const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
@@ -683,7 +700,7 @@ __global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void 
     // P above the block diagonal (never produced by the Gram) is zero
     constexpr int VE = 16 / sizeof(OpT);
     constexpr int RowV = R::NCOL / VE;       // 16-byte pieces per P row
-    for (int idx = tid - 64; idx < C * RowV; idx += kPrepThreads - 64) {
+    for (int idx = tid - 64; !R::kRawK && idx < C * RowV; idx += kPrepThreads - 64) {
       const int r = idx / RowV, s0 = (idx % RowV) * VE;
       if ((s0 >> 4) > (r >> 4)) {
         float x[VE];
@@ -878,15 +895,17 @@ void state_kernel(StateParams p) {
   constexpr int NKP = DK / 32;               // 32-wide k steps over the key dim
   constexpr int NOWN = DVS / 16;             // waves that own state columns
   constexpr int NH = (NB + 1) / 2;           // 32-wide k steps over the chunk's tokens
-  // 16-byte copies per chunk, each helper wave issuing its share: (raw K)
-  // the k rows, the record, the value rows
+  // 16-byte copies per chunk, each helper wave issuing its share: (raw rows)
+  // the q and k rows, the record, the value rows
   constexpr bool rawk = R::kRawK;
-  constexpr int nRec = static_cast<int>(R::gBytes / 16), nRecI = (nRec + 63) / 64;
+  constexpr int nRecI = static_cast<int>(L::kRecLds / 1024);   // whole slots (image padded)
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
   constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
   constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
+  constexpr int NPF = L::kNPF;                // P operand fragments (helper-formed output)
   constexpr int kStThreads = 64 * state_waves<DVS>();
-  constexpr int kSlotsR = (nRecI + NHELP - 1) / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  constexpr int kSlotsR = nRecI / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  static_assert(nRecI % NHELP == 0, "record slots shared evenly");
   constexpr int kSlotsQ = rawk ? (nQKI + NHELP - 1) / NHELP : 0;
   static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
@@ -916,6 +935,7 @@ void state_kernel(StateParams p) {
   const int n0 = slice * DVS;   // first value column of this slice
   const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::gBytes;
   const In* gv = static_cast<const In*>(p.v);
+  const In* gq = static_cast<const In*>(p.q);
   const In* gk = static_cast<const In*>(p.k);
   const long seq0 = static_cast<long>(b) * T + static_cast<long>(p.c0) * C;   // first token of this launch
   const int Trem = T - p.c0 * C;             // tokens from there to the sequence end
@@ -939,9 +959,9 @@ void state_kernel(StateParams p) {
   const int hw = wave - NOWN;                // helper index (helper waves)
   // Per-lane copy offsets of a helper wave, the same for every chunk: value
   // piece of slot s is row vr[s] (-1: past the value rows, no copy), at byte
-  // voff[s] from the chunk's first value element; k piece of slot s is row
-  // kr[s], at byte kvo[s] from the chunk's first k element, landing at the
-  // swizzled position of the K tile.
+  // voff[s] from the chunk's first value element; q and k piece of slot s is
+  // row kr[s], at byte kvo[s] from the chunk's first q or k element, landing
+  // at the swizzled position of the Q or K tile.
   int vr[kSlotsV], voff[kSlotsV];
 #pragma unroll
   for (int sv = 0; sv < kSlotsV; ++sv) {
@@ -964,24 +984,37 @@ void state_kernel(StateParams p) {
   // the chunk's row 0 instead (finite data; their products only meet zero
   // rows of T and P, and value rows are cleared once the copies land).
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int c, unsigned char* dstp) {
+  // part 1: (raw rows) the q and k rows; part 2: the record and the value
+  // rows.  The helper-formed output issues the two parts at different points
+  // of a step, so that the copies queue behind each other while it computes.
+  auto issue = [&](int c, unsigned char* dstp, auto part_tag) {
+    constexpr int part = decltype(part_tag)::value;   // 0: both, 1, 2
     const uint32_t dst = lds0 + static_cast<uint32_t>(dstp - smem);
-    const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
     const int t0 = c * C, Lc = min(C, Trem - t0);
-    {
+    if constexpr (part != 2) {
       if constexpr (rawk) {
-        const i32x4 rk = rsrc(gk + ((seq0 + t0) * H + h) * static_cast<long>(DK), (Lc - 1) * rowK + DK * AB);
+        const long e0 = ((seq0 + t0) * H + h) * static_cast<long>(DK);
+        const int nb = (Lc - 1) * rowK + DK * AB;
+        const i32x4 rk = rsrc(gk + e0, nb), rq = rsrc(gq + e0, nb);
 #pragma unroll
         for (int sq = 0; sq < kSlotsQ; ++sq) {
           const int j = sq * NHELP + hw;
-          if (j < nQKI) dma16_buf(rk, dst + R::oK + j * 1024, kr[sq] < Lc ? kvo[sq] : 0, 0);
+          if (nQKI % NHELP == 0 || j < nQKI) {
+            const int off = kr[sq] < Lc ? kvo[sq] : 0;
+            dma16_buf(rk, dst + R::oK + j * 1024, off, 0);
+            dma16_buf(rq, dst + R::oQ + j * 1024, off, 0);
+          }
         }
       }
     }
+    if constexpr (part == 1) return;
+    const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
+    // (the record's LDS image is padded to whole slots of every helper;
+    // pieces past the record read as zero through the buffer's range check)
+#pragma unroll
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
-      if (j < nRecI && (nRec % 64 == 0 || j * 64 + lane < nRec))
-        dma16_buf(rr, dst + R::gOff + j * 1024, lane * 16, j * 1024);
+      dma16_buf(rr, dst + R::gOff + j * 1024, j * 1024 + lane * 16, 0);
     }
     {
       const i32x4 rv =
@@ -989,7 +1022,8 @@ void state_kernel(StateParams p) {
 #pragma unroll
       for (int sv = 0; sv < kSlotsV; ++sv) {
         const int j = sv * NHELP + hw;
-        if (j < nValI && vr[sv] >= 0) dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
+        if ((nVal % (64 * NHELP) == 0 || (j < nValI && vr[sv] >= 0)))
+          dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
       }
     }
   };
@@ -1002,7 +1036,8 @@ void state_kernel(StateParams p) {
 #pragma unroll
       for (int sv = 0; sv < kSlotsV; ++sv) {
         const int j = sv * NHELP + hw;
-        if (j < nValI && vr[sv] >= Lc) *reinterpret_cast<u32x4*>(dst + j * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+        if ((nVal % (64 * NHELP) == 0 || (j < nValI && vr[sv] >= 0)) && vr[sv] >= Lc)
+          *reinterpret_cast<u32x4*>(dst + j * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -1034,30 +1069,38 @@ void state_kernel(StateParams p) {
   // Helper-formed output (see StateLayout): the S0 operand exchange slots,
   // the owners' flags, and the D fragments' places in the value rows.
   constexpr bool hout = L::kHelperOut;
+  static_assert(hout == rawk, "raw rows go with the helper-formed output");
   const int pw = owner ? wave : hw;          // the owner/helper pair of this wave
   int* flags = reinterpret_cast<int*>(smem + L::oFlags);   // S0 read by the helper: chunk + 1
   int* dflags = flags + 8;                                  // D written by the owner: chunk + 1
-  auto xs_at = [&](int m) { return smem + L::oXS + ((pw * NKP + m) * 64 + lane) * 16; };
+  int* pflags = flags + 16;                                 // P fragments written by the helper: chunk + 1
+  // fragment m, part 0 (bf16 high) or 1 (the remainder), of this pair
+  auto xs_at = [&](int m, int part) {
+    return smem + L::oXS + (((pw * NKP + m) * 2 + part) * 64 + lane) * 16;
+  };
   int dfo[NH];                               // D fragment m: this lane's 16 bytes
 #pragma unroll
   for (int m = 0; m < NH; ++m) {
     const int q = m * 64 + lane, r = q >> 1;
     dfo[m] = static_cast<int>(L::oV) + r * (L::PPRV * 16) + (((2 * pw + (q & 1)) ^ swzv<L::PPRV>(r)) << 4);
   }
-  auto put_xs = [&]() {                      // owner: S's fp16 operand fragments
+  auto put_xs = [&]() {                      // owner: S's operand fragments
 #pragma unroll
-    for (int m = 0; m < NKP; ++m)
-      *reinterpret_cast<typename M::frag*>(xs_at(m)) = M::from_acc(S[2 * m], S[2 * m + 1]);
+    for (int m = 0; m < NKP; ++m) {
+      const bf16x8 hi = bf_from_acc(S[2 * m], S[2 * m + 1]);
+      *reinterpret_cast<bf16x8*>(xs_at(m, 0)) = hi;
+      *reinterpret_cast<bf16x8*>(xs_at(m, 1)) = bf_lo(S[2 * m], S[2 * m + 1], hi);
+    }
   };
   if constexpr (hout) {
     if (owner) {
       put_xs();
-      if (lane == 0) flags[pw] = dflags[pw] = 0;
+      if (lane == 0) flags[pw] = dflags[pw] = pflags[pw] = 0;
     }
   }
 
   if (nchunks > 0) {
-    if (!owner) issue(0, smem);
+    if (!owner) issue(0, smem, std::integral_constant<int, 0>{});
     finish(0, smem);
   }
   lds_barrier();
@@ -1074,37 +1117,6 @@ void state_kernel(StateParams p) {
       if (r < Lc) *reinterpret_cast<f32x4*>(ob + r * rowO + obyte) = Oprev[rt];
     }
   };
-  // Helper: finish chunk c's output from its buffer bq (its S0^T Q^T part is
-  // in Oprev): scale by exp(G), add D^T P^T, store.
-  constexpr int NPF = NB * (NB + 2) / 4;     // P fragments: sum over rt of rt/2 + 1
-  struct OutOps {
-    typename M::frag Df[NH], Pf[NPF > 0 ? NPF : 1];
-    float eg[NB];
-  };
-  auto helper_out_load = [&](const unsigned char* bq, OutOps& x) {
-    const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
-#pragma unroll
-    for (int m = 0; m < NH; ++m) x.Df[m] = *reinterpret_cast<const typename M::frag*>(bq + dfo[m]);
-    int n = 0;
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      x.eg[rt] = headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f;
-#pragma unroll
-      for (int m = 0; m <= rt / 2; ++m) x.Pf[n++] = fr.cc(bq + R::oP, rt, m);
-    }
-    wait_lgkm();   // the buffer may be copied over from here on
-  };
-  auto helper_out_finish = [&](const OutOps& x, int c) {
-    int n = 0;
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      if (headdecay) Oprev[rt] *= x.eg[rt];
-#pragma unroll
-      for (int m = 0; m <= rt / 2; ++m) M::mma(Oprev[rt], x.Df[m], x.Pf[n++]);
-    }
-    store_out(c);
-  };
-
   // One chunk step on LDS buffer CUR (a compile-time constant, so every LDS
   // address below is a per-lane base plus an immediate), for an owner or a
   // helper wave (a compile-time choice: the two kinds of wave run separate
@@ -1133,7 +1145,7 @@ void state_kernel(StateParams p) {
       [[maybe_unused]] bf16x8 Sb[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) {
-        if (!(hout && rawk)) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
+        if (!hout) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
         if constexpr (rawk) Sb[m] = bf_from_acc(S[2 * m], S[2 * m + 1]);
       }
       // K S0 and (unless the helper forms it) S0^T Q^T: both read only S0, so
@@ -1277,32 +1289,106 @@ void state_kernel(StateParams p) {
     } else {
       // helper: the next chunk's copies, then (helper-formed output) this
       // chunk's output
-      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf);
+      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, hout ? 1 : 0>{});
       if constexpr (hout) {
-        // S0^T Q^T of this chunk, S0 from the owner
-        const unsigned char* sQ = smem + cur * L::kBuf + R::oQ;
-        typename M::frag Sx[NKP];
+        const unsigned char* bq = smem + cur * L::kBuf;
+        const unsigned char* sQ = bq + R::oQ;
+        const unsigned char* sK = bq + R::oK;
+        const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
+        // S0 from the owner, in two bf16 parts; once read the owner may put
+        // the next one
+        bf16x8 Sh[NKP], Sl[NKP];
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) Sx[m] = *reinterpret_cast<const typename M::frag*>(xs_at(m));
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          Oprev[rt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) M::mma(Oprev[rt], Sx[m], fr.kq(sQ, rt, m));
+        for (int m = 0; m < NKP; ++m) {
+          Sh[m] = *reinterpret_cast<const bf16x8*>(xs_at(m, 0));
+          Sl[m] = *reinterpret_cast<const bf16x8*>(xs_at(m, 1));
         }
         if (lane == 0) __hip_atomic_store(&flags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        // the rest once the owner's D is in place
+        // q rows as given, and q's row factor from the same fragments (a
+        // lane's 8 channels per k step; the 4 lane groups of a row hold its
+        // other channels)
+        bf16x8 Qf[NB][NKP];
+        float fq[NB];
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          fq[rt] = 0.f;
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) {
+            Qf[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, rt, m));
+            fq[rt] = sumsq_bf(Qf[rt][m], fq[rt]);
+          }
+          fq[rt] = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(fq[rt]))) : 1.f);
+        }
+        // S0^T q^T, the row blocks' products interleaved
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Oprev[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) {
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Oprev[rt], Sh[m], Qf[rt][m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Oprev[rt], Sl[m], Qf[rt][m]);
+        }
+        if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, 2>{});
+        // This helper's share of P's operand fragments: fragment n covers
+        // row block pf_ib(n) and the 32-token k step pf_m(n), i.e. the
+        // column blocks 2 pf_m(n) and 2 pf_m(n) + 1:
+        //   P_ij = fq_i fk_j exp(G_i - G_j) q_i . k_j for j <= i, else 0
+        // (the raw products come transposed: tokens j by tokens i)
+        static_for<NPF>([&](auto n_) {
+          constexpr int n = decltype(n_)::value, ib = pf_ib(n), m2 = pf_m(n);
+          if (n * NHELP / NPF != hw) return;
+          const int i = 16 * ib + l16;
+          const float gi = headdecay ? svec[R::vG + i] : 0.f;
+          f32x4 blk[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int jb = 2 * m2 + h2;
+            blk[h2] = f32x4{0, 0, 0, 0};
+            if (jb > ib) continue;
+#pragma unroll
+            for (int m = 0; m < NKP; ++m)
+              mma_bf(blk[h2], __builtin_bit_cast(bf16x8, fr.kq(sK, jb, m)), Qf[ib][m]);
+            const f32x4 fk = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * jb + 4 * g);
+            f32x4 gj = f32x4{0, 0, 0, 0};
+            if (headdecay) gj = *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * jb + 4 * g);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              float x = blk[h2][jj] * fq[ib] * fk[jj];
+              if (headdecay) x *= __expf(gi - gj[jj]);
+              blk[h2][jj] = (jb < ib || 4 * g + jj <= l16) ? x : 0.f;
+            }
+          }
+          *reinterpret_cast<typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16) = M::from_acc(blk[0], blk[1]);
+        });
+        if (lane == 0) __hip_atomic_store(&pflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Oprev[rt] *= fq[rt] * (headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f);
+        // O^T += D^T P^T once the owner's D and every helper's share of P
+        // are in place; store
         while (__hip_atomic_load(&dflags[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
           __builtin_amdgcn_s_sleep(1);
-        OutOps ops;
-        helper_out_load(smem + cur * L::kBuf, ops);
-        helper_out_finish(ops, c);
+#pragma unroll
+        for (int h2 = 0; h2 < NHELP; ++h2) {
+          while (__hip_atomic_load(&pflags[h2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
+            __builtin_amdgcn_s_sleep(1);
+        }
+        typename M::frag Df[NH];
+#pragma unroll
+        for (int m = 0; m < NH; ++m) Df[m] = *reinterpret_cast<const typename M::frag*>(bq + dfo[m]);
+#pragma unroll
+        for (int ib = 0, n = 0; ib < NB; ++ib) {
+#pragma unroll
+          for (int m = 0; m <= ib / 2; ++m, ++n)
+            M::mma(Oprev[ib], Df[m], *reinterpret_cast<const typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16));
+        }
+        store_out(c);
       }
     }
     if (c + 1 < nchunks) {
       if (L::NBUF == 1) {
         lds_barrier();              // every wave is done with the only buffer
-        if constexpr (!own) issue(c + 1, smem);
+        if constexpr (!own) issue(c + 1, smem, std::integral_constant<int, 0>{});
       }
       finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
       lds_barrier();                // the next chunk is visible to all waves

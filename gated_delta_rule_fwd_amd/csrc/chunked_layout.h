@@ -61,8 +61,8 @@ __host__ __device__ constexpr int perm_pos(int e) {
 
 // Per-chunk record: the image of one chunk in the state kernel's LDS.  Each
 // tile has one row per token of the chunk, rows unpadded and swizzled (swz
-// above), elements in perm_pos order (raw K below: natural order).  OpBytes:
-// 2 (fp16 operands) or 4 (fp32).
+// above), elements in perm_pos order (raw rows below: natural order).
+// OpBytes: 2 (fp16 operands) or 4 (fp32).
 //   Q    q normalised and scaled; per-channel decay: times exp(G)
 //   K    k normalised; per-channel decay: times exp(Gx)
 //   F    per-channel decay only: k normalised times exp(G_last - G)
@@ -71,33 +71,34 @@ __host__ __device__ constexpr int perm_pos(int e) {
 //        (NCOL = max(C, 32): the columns a 32-wide k step reads)
 //   vec  fp32: exp(G), exp(Gx), exp(G_last - G) (each C), misc[16] with
 //        misc[0] = exp(G_last); per-channel: exp(G_last) per key channel [DK];
-//        with raw K the last two also carry k's row factor fk
-// The workspace holds bytes [gOff, bytes) of the image per chunk.  Raw K
-// (bf16 activations without per-channel decay, where K is k times a per-row
-// factor): the K tile heads the image and is not stored; the state kernel
-// copies k's bf16 rows as they are and multiplies with them in bf16, the row
-// factor going onto the products' rows.  Q is then kept in natural element
-// order too (fp16), like the K rows, and comes last, after the vectors.
+//        raw rows: G and k's row factor fk (each C), and fk also folded
+//        into exp(Gx) and exp(G_last - G)
+// The workspace holds bytes [gOff, bytes) of the image per chunk.  Raw rows
+// (bf16 activations, no per-channel decay, C >= 32): the image starts with q
+// and k as they are (bf16, natural element order), which the state kernel
+// copies from the inputs itself, and P is not stored: the state kernel forms
+// it from those rows, the row factors and G.  The record is then Tu and the
+// vectors only.
 template <int DK, int C, int OpBytes, bool Chan>
 struct RecLayout {
-  static constexpr bool kRawK = !Chan && OpBytes == 2;
+  static constexpr bool kRawK = !Chan && OpBytes == 2 && C >= 32;
   static constexpr int PPRK = DK * OpBytes / 16;   // pieces per Q/K/F row
   static constexpr int NCOL = C < 32 ? 32 : C;
   static constexpr int PPRC = NCOL * OpBytes / 16; // pieces per Tu/P row
   static constexpr size_t kTile = size_t(C) * DK * OpBytes;
   static constexpr size_t kCC = size_t(C) * NCOL * OpBytes;
   static constexpr int kTiles = Chan ? 3 : 2;       // Q, K (, F)
+  static constexpr size_t oQ = kRawK ? kTile : 0;
   static constexpr size_t oK = kRawK ? 0 : kTile;
   static constexpr size_t oF = 2 * kTile;
-  static constexpr size_t oTu = kRawK ? kTile : kTiles * kTile;
-  static constexpr size_t oP = oTu + kCC;
-  static constexpr size_t oVec = oP + kCC;
+  static constexpr size_t oTu = kTiles * kTile;
+  static constexpr size_t oP = oTu + kCC;           // not with raw rows
+  static constexpr size_t oVec = kRawK ? oTu + kCC : oP + kCC;
   static constexpr int vEG = 0, vEGx = C, vEF = 2 * C, vMisc = 3 * C, vDecC = 3 * C + 16;
-  static constexpr int kVecFloats = 3 * C + 16 + (Chan ? DK : 0);
-  static constexpr size_t oQ = kRawK ? chunked_layout::al(oVec + size_t(kVecFloats) * 4) : 0;
-  static constexpr size_t bytes =
-      kRawK ? oQ + kTile : chunked_layout::al(oVec + size_t(kVecFloats) * 4);
-  static constexpr size_t gOff = kRawK ? kTile : 0;
+  static constexpr int vG = 3 * C + 16, vFK = 4 * C + 16;   // raw rows
+  static constexpr int kVecFloats = 3 * C + 16 + (Chan ? DK : 0) + (kRawK ? 2 * C : 0);
+  static constexpr size_t bytes = chunked_layout::al(oVec + size_t(kVecFloats) * 4);
+  static constexpr size_t gOff = kRawK ? 2 * kTile : 0;
   static constexpr size_t gBytes = bytes - gOff;
 };
 
@@ -158,28 +159,39 @@ struct PrepLayout {
 // followed by its value rows ([C][DVS] activations, rows swizzled).  With two
 // buffers the next chunk is copied in while the current one is computed.
 //
-// With fp16 operands, bf16 activations, no per-channel decay, two buffers and
-// C >= 32 the helper waves also form the output (kHelperOut; with per-channel
-// decay the kernel is bound by its copies, which the extra exchange would
-// only slow): each owner wave passes its S0 operand fragments to its
-// helper through the XS region (one 1 KiB fragment per 32 key channels), and
-// its D fragments through its own columns of the chunk's value rows, which
-// no other wave reads.  Flags (ints after XS): per owner, the chunk (+1)
-// whose S0 its helper has read, and the chunk (+1) whose D it has written.
+// With raw rows (see RecLayout) the helper waves also form the output
+// (kHelperOut): each owner wave passes its S0 to its helper through the XS
+// region (per 32 key channels two 1 KiB fragments: S0 in two bf16 parts),
+// and its D fragments through its own columns of the chunk's value rows,
+// which no other wave reads.  The helpers share the work of P: each forms
+// some of its fp16 operand fragments (PF, one 1 KiB fragment per 16-token
+// row block and 32-token k step) for all of them.  Flags (ints after XS):
+// per owner, the chunk (+1) whose S0 its helper has read and the chunk (+1)
+// whose D it has written; per helper, the chunk (+1) whose P fragments it
+// has written.
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
   static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
-  static constexpr size_t oV = R::bytes;
+  // the record's bytes in the image, padded to whole 1 KiB copies for each of
+  // the DVS / 16 waves that issue them
+  static constexpr size_t kRecSlot = size_t(1024) * (DVS / 16);
+  static constexpr size_t kRecLds = (R::gBytes + kRecSlot - 1) / kRecSlot * kRecSlot;
+  static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
   static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
-  static constexpr size_t kXS = size_t(DVS / 16) * (DK / 32) * 1024;
+  static constexpr size_t kXS = size_t(DVS / 16) * (DK / 32) * 2048;
   static constexpr size_t kFlags = 256;
-  static constexpr bool kHelperOut =
-      !Chan && OpBytes == 2 && ActBytes == 2 && C >= 32 && NBUF == 2 && 2 * kBuf + kXS + kFlags <= kMaxLds;
+  static constexpr int NBT = C / 16;
+  static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
+  static constexpr size_t kPF = size_t(kNPF) * 1024;
+  static constexpr bool kHelperOut = R::kRawK && NBUF == 2 && 2 * kBuf + kXS + kFlags + kPF <= kMaxLds;
   static constexpr size_t oXS = NBUF * kBuf;
   static constexpr size_t oFlags = oXS + kXS;
-  static constexpr size_t bytes = kHelperOut ? oFlags + kFlags : NBUF * kBuf;
+  static constexpr size_t oPF = oFlags + kFlags;
+  // raw rows without the helper-formed output: no plan (more than the LDS)
+  static constexpr size_t bytes =
+      (R::kRawK && !kHelperOut) ? kMaxLds + 1 : kHelperOut ? oPF + kPF : NBUF * kBuf;
 };
 
 }  // namespace kda

@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -91,9 +92,20 @@ __device__ __forceinline__ float dpp_group_sum(float x) {
   return x;
 }
 
+// x + x of lane ^ 16, and x + x of lane ^ 32 (gfx950 lane-swap moves)
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) {
-  // 1 / max(||x||_2, 1e-12)
-  return 1.0f / fmaxf(sqrtf(sumsq), 1e-12f);
+  // 1 / max(||x||_2, 1e-12): the hardware reciprocal square root (about
+  // 1 ulp), capped where the norm is below 1e-12 (a NaN sum gives the cap)
+  return fminf(__builtin_amdgcn_rsqf(sumsq), 1e12f);
 }
 
 }  // namespace kda

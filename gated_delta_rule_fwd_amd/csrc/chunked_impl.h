@@ -225,10 +225,13 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
-// P operand fragment n of the state kernel's helper waves: row block
-// pf_ib(n) and 32-token k step pf_m(n), running over ib, then m <= ib / 2.
-__host__ __device__ constexpr int pf_ib(int n) { int i = 0; while (n > i / 2) { n -= i / 2 + 1; ++i; } return i; }
-__host__ __device__ constexpr int pf_m(int n) { int i = 0; while (n > i / 2) { n -= i / 2 + 1; ++i; } return n; }
+// P operand fragments of the state kernel: fragment pf_n(ib, m) holds row
+// block ib at the 32-token k step m (m <= ib / 2), fragments running over ib,
+// then m.  P's 16 x 16 blocks (ib, jb <= ib) in the order the helper waves
+// share them: ib from the last row block down, then jb up.
+__host__ __device__ constexpr int pf_n(int ib, int m) { return ib / 2 * (ib / 2 + 1) + (ib & 1) * (ib / 2 + 1) + m; }
+__host__ __device__ constexpr int blk_ib(int b, int nb) { int i = nb - 1; while (b > i) { b -= i + 1; --i; } return i; }
+__host__ __device__ constexpr int blk_jb(int b, int nb) { int i = nb - 1; while (b > i) { b -= i + 1; --i; } return b; }
 
 // Transposed 4 x fp16 read (gfx950 ds_read_b64_tr_b16).  Within each group of
 // 16 lanes, lane j supplies the address of an 8-byte row piece E_j; lane
@@ -902,7 +905,8 @@ void state_kernel(StateParams p) {
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
   constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
   constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
-  constexpr int NPF = L::kNPF;                // P operand fragments (helper-formed output)
+  constexpr int NPF = L::kNPF;                // P operand fragments (raw rows: formed by the helpers)
+  constexpr int NBLK = NB * (NB + 1) / 2;     // P's lower-triangular 16 x 16 blocks
   constexpr int kStThreads = 64 * state_waves<DVS>();
   constexpr int kSlotsR = nRecI / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
   static_assert(nRecI % NHELP == 0, "record slots shared evenly");
@@ -984,11 +988,10 @@ void state_kernel(StateParams p) {
   // the chunk's row 0 instead (finite data; their products only meet zero
   // rows of T and P, and value rows are cleared once the copies land).
   const uint32_t lds0 = lds_addr(smem);
-  // part 1: (raw rows) the q and k rows; part 2: the record and the value
-  // rows.  The helper-formed output issues the two parts at different points
-  // of a step, so that the copies queue behind each other while it computes.
+  // part 1: (raw rows) the q and k rows, part 2: the record and the value
+  // rows, 0: both
   auto issue = [&](int c, unsigned char* dstp, auto part_tag) {
-    constexpr int part = decltype(part_tag)::value;   // 0: both, 1, 2
+    constexpr int part = decltype(part_tag)::value;
     const uint32_t dst = lds0 + static_cast<uint32_t>(dstp - smem);
     const int t0 = c * C, Lc = min(C, Trem - t0);
     if constexpr (part != 2) {
@@ -1066,36 +1069,20 @@ void state_kernel(StateParams p) {
     }
   }
 
-  // Helper-formed output (see StateLayout): the S0 operand exchange slots,
-  // the owners' flags, and the D fragments' places in the value rows.
-  constexpr bool hout = L::kHelperOut;
-  static_assert(hout == rawk, "raw rows go with the helper-formed output");
-  const int pw = owner ? wave : hw;          // the owner/helper pair of this wave
-  int* flags = reinterpret_cast<int*>(smem + L::oFlags);   // S0 read by the helper: chunk + 1
-  int* dflags = flags + 8;                                  // D written by the owner: chunk + 1
-  int* pflags = flags + 16;                                 // P fragments written by the helper: chunk + 1
-  // fragment m, part 0 (bf16 high) or 1 (the remainder), of this pair
-  auto xs_at = [&](int m, int part) {
-    return smem + L::oXS + (((pw * NKP + m) * 2 + part) * 64 + lane) * 16;
-  };
-  int dfo[NH];                               // D fragment m: this lane's 16 bytes
+  // Raw rows (see StateLayout): the helpers form P's operand fragments and
+  // q's row factors, and flag each chunk's.
+  constexpr bool hp = L::kHelperP;
+  static_assert(hp == rawk, "raw rows go with the helper-formed P");
+  int* pflags = reinterpret_cast<int*>(smem + L::oFlags);   // helper h's P of chunk c written: c + 1
+  float* sfq = reinterpret_cast<float*>(smem + L::oFQ);     // q's row factor per token of the chunk
+  if constexpr (hp) {
+    if (!owner && lane == 0) pflags[hw] = 0;
+    // the fragments' halves above the diagonal (column block ib + 1 of an
+    // even row block ib) stay zero
+    if (hw == 0) {
 #pragma unroll
-  for (int m = 0; m < NH; ++m) {
-    const int q = m * 64 + lane, r = q >> 1;
-    dfo[m] = static_cast<int>(L::oV) + r * (L::PPRV * 16) + (((2 * pw + (q & 1)) ^ swzv<L::PPRV>(r)) << 4);
-  }
-  auto put_xs = [&]() {                      // owner: S's operand fragments
-#pragma unroll
-    for (int m = 0; m < NKP; ++m) {
-      const bf16x8 hi = bf_from_acc(S[2 * m], S[2 * m + 1]);
-      *reinterpret_cast<bf16x8*>(xs_at(m, 0)) = hi;
-      *reinterpret_cast<bf16x8*>(xs_at(m, 1)) = bf_lo(S[2 * m], S[2 * m + 1], hi);
-    }
-  };
-  if constexpr (hout) {
-    if (owner) {
-      put_xs();
-      if (lane == 0) flags[pw] = dflags[pw] = pflags[pw] = 0;
+      for (int ib = 0; ib < NB; ib += 2)
+        *reinterpret_cast<f16x4*>(smem + L::oPF + pf_n(ib, ib / 2) * 1024 + lane * 16 + 8) = f16x4{0, 0, 0, 0};
     }
   }
 
@@ -1105,9 +1092,10 @@ void state_kernel(StateParams p) {
   }
   lds_barrier();
 
-  // Output rows of a chunk: stored at the start of the next one.
+  // Output rows of a chunk (without raw rows stored at the start of the next
+  // one, so that the stores wait for nothing)
   f32x4 Oprev[NB];
-  const int obyte = 16 * pw * 4 + 4 * g * 4;   // this lane's column bytes within a row of o
+  const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o (owners)
   auto store_out = [&](int c) {
     const int t0 = c * C, Lc = min(C, Trem - t0);
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o + ((seq0 + t0) * H + h) * static_cast<long>(DV) + n0);
@@ -1137,37 +1125,61 @@ void state_kernel(StateParams p) {
       const unsigned char* sV = bq + L::oV;
       const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
 
-      if (!hout && c > 0) store_out(c - 1);
-      // Raw K: the products with k run in bf16 (its rows as given, S0 and D
-      // rounded to bf16, D in two parts); k's row factor is in the
-      // per-token vectors.
-      typename M::frag Sf[NKP];
+      if (!rawk && c > 0) store_out(c - 1);
+      // Raw rows: the products with q and k run in bf16 (their rows as given,
+      // S0 and D in two bf16 parts, or S0 in one for K S0); the row factors
+      // are in the per-token vectors and FQ.
+      [[maybe_unused]] typename M::frag Sf[NKP];
       [[maybe_unused]] bf16x8 Sb[NKP];
 #pragma unroll
       for (int m = 0; m < NKP; ++m) {
-        if (!hout) Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
         if constexpr (rawk) Sb[m] = bf_from_acc(S[2 * m], S[2 * m + 1]);
+        else Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
       }
-      // K S0 and (unless the helper forms it) S0^T Q^T: both read only S0, so
-      // their products interleave
+      // K S0 and S0^T Q^T: both read only S0, so their products interleave
       f32x4 Xl[NB], Ol[NB];
+      if constexpr (rawk) {
+        // every operand first, then the products with each accumulator's
+        // successive steps NB products apart (S0 in two bf16 parts for the
+        // output, the low part into Ol2)
+        bf16x8 fqb[NB][NKP], fkb[NB][NKP];
+        f32x4 Ol2[NB];
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        [[maybe_unused]] typename M::frag fq[NKP];
-        [[maybe_unused]] typename M::frag fk[NKP];
-        [[maybe_unused]] bf16x8 fkb[NKP];
+        for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          if constexpr (rawk) fkb[m] = __builtin_bit_cast(bf16x8, fr.kq(sK, rt, m));
-          else fk[m] = fr.kq(sK, rt, m);
-          if (!hout) fq[m] = fr.kq(sQ, rt, m);
+          for (int m = 0; m < NKP; ++m) {
+            fkb[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sK, rt, m));
+            fqb[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, rt, m));
+          }
+          Xl[rt] = Ol[rt] = Ol2[rt] = f32x4{0, 0, 0, 0};
         }
-        Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
-          if constexpr (rawk) mma_bf(Xl[rt], fkb[m], Sb[m]);
-          else M::mma(Xl[rt], fk[m], Sf[m]);
-          if (!hout) M::mma(Ol[rt], Sf[m], fq[m]);
+          const bf16x8 sl = bf_lo(S[2 * m], S[2 * m + 1], Sb[m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Xl[rt], fkb[rt][m], Sb[m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol[rt], Sb[m], fqb[rt][m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol2[rt], sl, fqb[rt][m]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Ol[rt] += Ol2[rt];
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) {
+          typename M::frag fqf[NKP], fkf[NKP];
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) {
+            fkf[m] = fr.kq(sK, rt, m);
+            fqf[m] = fr.kq(sQ, rt, m);
+          }
+          Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int m = 0; m < NKP; ++m) {
+            M::mma(Xl[rt], fkf[m], Sf[m]);
+            M::mma(Ol[rt], Sf[m], fqf[m]);
+          }
         }
       }
       // X = V - (K * exp(Gx)) S0
@@ -1209,21 +1221,32 @@ void state_kernel(StateParams p) {
 #pragma unroll
       for (int m = 0; m < NH; ++m)
         Df[m] = M::from_acc(Dl[2 * m], 2 * m + 1 < NB ? Dl[2 * m + 1] : f32x4{0, 0, 0, 0});
-      if constexpr (hout) {
-        // D's fragments to this wave's own columns of the value rows
+      // O^T = S0^T (Q * exp(G))^T + D^T P^T; raw rows: q's row factor on
+      // the first term, P from the helpers (after the state step, which
+      // does not need it)
+      auto form_out = [&]() {
+        if constexpr (rawk) {
 #pragma unroll
-        for (int m = 0; m < NH; ++m)
-          *reinterpret_cast<typename M::frag*>(const_cast<unsigned char*>(bq) + dfo[m]) = Df[m];
-        if (lane == 0) __hip_atomic_store(&dflags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
-        // O^T = S0^T (Q * exp(G))^T + D^T P^T
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          if (headdecay) Ol[rt] *= svec[R::vEG + 16 * rt + l16];
-#pragma unroll
-          for (int m = 0; m <= rt / 2; ++m) M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
+          for (int h2 = 0; h2 < NHELP; ++h2) {
+            while (__hip_atomic_load(&pflags[h2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
+              __builtin_amdgcn_s_sleep(1);
+          }
         }
-      }
+#pragma unroll
+        for (int rt = 0, n = 0; rt < NB; ++rt) {
+          float f = headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f;
+          if constexpr (rawk) f *= sfq[16 * rt + l16];
+          if (headdecay || rawk) Ol[rt] *= f;
+#pragma unroll
+          for (int m = 0; m <= rt / 2; ++m, ++n) {
+            if constexpr (rawk)
+              M::mma(Ol[rt], Df[m], *reinterpret_cast<const typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16));
+            else
+              M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
+          }
+        }
+      };
+      if constexpr (!rawk) form_out();
       // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
@@ -1275,114 +1298,69 @@ void state_kernel(StateParams p) {
             M::mma(S[t], fr.tok(KY, m, t, 2 * m + 1 < NB), Df[m]);
         }
       }
-      if constexpr (hout) {
-        if (c + 1 < nchunks) {
-          // S for the helper's next output, once it has read this chunk's
-          while (__hip_atomic_load(&flags[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
-            __builtin_amdgcn_s_sleep(1);
-          put_xs();
-        }
-      } else {
+      if constexpr (rawk) form_out();
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
-      }
+      for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
+      if constexpr (rawk) store_out(c);
     } else {
-      // helper: the next chunk's copies, then (helper-formed output) this
-      // chunk's output
-      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, hout ? 1 : 0>{});
-      if constexpr (hout) {
+      // helper: the next chunk's copies; with raw rows its share of this
+      // chunk's P between the q, k rows and the rest
+      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, hp ? 1 : 0>{});
+      if constexpr (hp) {
         const unsigned char* bq = smem + cur * L::kBuf;
         const unsigned char* sQ = bq + R::oQ;
         const unsigned char* sK = bq + R::oK;
         const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
-        // S0 from the owner, in two bf16 parts; once read the owner may put
-        // the next one
-        bf16x8 Sh[NKP], Sl[NKP];
+        // Block (ib, jb) of P: P_ij = fq_i fk_j exp(G_i - G_j) q_i . k_j for
+        // j <= i, else 0 (the raw products come transposed: tokens j by
+        // tokens i), the fp16 half jb & 1 of operand fragment pf_n(ib, jb / 2).
+        // q's row factor comes from the q fragments (a lane's 8 channels per
+        // k step; the 4 lane groups of a row hold its other channels); the
+        // helper with block (ib, 0) also puts it in FQ.  The blocks of a helper
+        // are fixed at compile time (one code path per helper).
+        auto share = [&](auto hh_) {
+          constexpr int hh = decltype(hh_)::value;
+          bf16x8 Qf[NKP];
+          float fq = 0.f, gi = 0.f;
+          static_for<NBLK>([&](auto b_) {
+            constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
+            if constexpr (b * NHELP / NBLK == hh) {
+              constexpr bool newrow = b == 0 || (b - 1) * NHELP / NBLK != hh || blk_ib(b - 1, NB) != ib;
+              const int i = 16 * ib + l16;
+              if constexpr (newrow) {
+                float ss = 0.f;
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          Sh[m] = *reinterpret_cast<const bf16x8*>(xs_at(m, 0));
-          Sl[m] = *reinterpret_cast<const bf16x8*>(xs_at(m, 1));
-        }
-        if (lane == 0) __hip_atomic_store(&flags[pw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        // q rows as given, and q's row factor from the same fragments (a
-        // lane's 8 channels per k step; the 4 lane groups of a row hold its
-        // other channels)
-        bf16x8 Qf[NB][NKP];
-        float fq[NB];
+                for (int m = 0; m < NKP; ++m) {
+                  Qf[m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, ib, m));
+                  ss = sumsq_bf(Qf[m], ss);
+                }
+                fq = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(ss))) : 1.f);
+                gi = headdecay ? svec[R::vG + i] : 0.f;
+              }
+              if (jb == 0 && g == 0) sfq[i] = fq;
+              f32x4 acc = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
-          fq[rt] = 0.f;
+              for (int m = 0; m < NKP; ++m)
+                mma_bf(acc, __builtin_bit_cast(bf16x8, fr.kq(sK, jb, m)), Qf[m]);
+              const f32x4 fk = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * jb + 4 * g);
+              f32x4 gj = f32x4{0, 0, 0, 0};
+              if (headdecay) gj = *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * jb + 4 * g);
+              f16x4 hv;
 #pragma unroll
-          for (int m = 0; m < NKP; ++m) {
-            Qf[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, rt, m));
-            fq[rt] = sumsq_bf(Qf[rt][m], fq[rt]);
-          }
-          fq[rt] = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(fq[rt]))) : 1.f);
-        }
-        // S0^T q^T, the row blocks' products interleaved
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Oprev[rt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) mma_bf(Oprev[rt], Sh[m], Qf[rt][m]);
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) mma_bf(Oprev[rt], Sl[m], Qf[rt][m]);
-        }
-        if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, 2>{});
-        // This helper's share of P's operand fragments: fragment n covers
-        // row block pf_ib(n) and the 32-token k step pf_m(n), i.e. the
-        // column blocks 2 pf_m(n) and 2 pf_m(n) + 1:
-        //   P_ij = fq_i fk_j exp(G_i - G_j) q_i . k_j for j <= i, else 0
-        // (the raw products come transposed: tokens j by tokens i)
-        static_for<NPF>([&](auto n_) {
-          constexpr int n = decltype(n_)::value, ib = pf_ib(n), m2 = pf_m(n);
-          if (n * NHELP / NPF != hw) return;
-          const int i = 16 * ib + l16;
-          const float gi = headdecay ? svec[R::vG + i] : 0.f;
-          f32x4 blk[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int jb = 2 * m2 + h2;
-            blk[h2] = f32x4{0, 0, 0, 0};
-            if (jb > ib) continue;
-#pragma unroll
-            for (int m = 0; m < NKP; ++m)
-              mma_bf(blk[h2], __builtin_bit_cast(bf16x8, fr.kq(sK, jb, m)), Qf[ib][m]);
-            const f32x4 fk = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * jb + 4 * g);
-            f32x4 gj = f32x4{0, 0, 0, 0};
-            if (headdecay) gj = *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * jb + 4 * g);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float x = blk[h2][jj] * fq[ib] * fk[jj];
-              if (headdecay) x *= __expf(gi - gj[jj]);
-              blk[h2][jj] = (jb < ib || 4 * g + jj <= l16) ? x : 0.f;
+              for (int jj = 0; jj < 4; ++jj) {
+                float x = acc[jj] * fq * fk[jj];
+                if (headdecay) x *= __expf(gi - gj[jj]);
+                hv[jj] = static_cast<_Float16>((jb < ib || 4 * g + jj <= l16) ? x : 0.f);
+              }
+              *reinterpret_cast<f16x4*>(smem + L::oPF + pf_n(ib, jb / 2) * 1024 + lane * 16 + (jb & 1) * 8) = hv;
             }
-          }
-          *reinterpret_cast<typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16) = M::from_acc(blk[0], blk[1]);
+          });
+        };
+        static_for<NHELP>([&](auto hh_) {
+          if (hw == decltype(hh_)::value) share(hh_);
         });
         if (lane == 0) __hip_atomic_store(&pflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Oprev[rt] *= fq[rt] * (headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f);
-        // O^T += D^T P^T once the owner's D and every helper's share of P
-        // are in place; store
-        while (__hip_atomic_load(&dflags[pw], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int h2 = 0; h2 < NHELP; ++h2) {
-          while (__hip_atomic_load(&pflags[h2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
-            __builtin_amdgcn_s_sleep(1);
-        }
-        typename M::frag Df[NH];
-#pragma unroll
-        for (int m = 0; m < NH; ++m) Df[m] = *reinterpret_cast<const typename M::frag*>(bq + dfo[m]);
-#pragma unroll
-        for (int ib = 0, n = 0; ib < NB; ++ib) {
-#pragma unroll
-          for (int m = 0; m <= ib / 2; ++m, ++n)
-            M::mma(Oprev[ib], Df[m], *reinterpret_cast<const typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16));
-        }
-        store_out(c);
+        if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, 2>{});
       }
     }
     if (c + 1 < nchunks) {
@@ -1409,7 +1387,7 @@ void state_kernel(StateParams p) {
     }
   }
 
-  if constexpr (!hout) {
+  if constexpr (!rawk) {
     if (owner && nchunks > 0) store_out(nchunks - 1);
   }
   if (owner) {

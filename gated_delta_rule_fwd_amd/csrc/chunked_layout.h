@@ -159,16 +159,11 @@ struct PrepLayout {
 // followed by its value rows ([C][DVS] activations, rows swizzled).  With two
 // buffers the next chunk is copied in while the current one is computed.
 //
-// With raw rows (see RecLayout) the helper waves also form the output
-// (kHelperOut): each owner wave passes its S0 to its helper through the XS
-// region (per 32 key channels two 1 KiB fragments: S0 in two bf16 parts),
-// and its D fragments through its own columns of the chunk's value rows,
-// which no other wave reads.  The helpers share the work of P: each forms
-// some of its fp16 operand fragments (PF, one 1 KiB fragment per 16-token
-// row block and 32-token k step) for all of them.  Flags (ints after XS):
-// per owner, the chunk (+1) whose S0 its helper has read and the chunk (+1)
-// whose D it has written; per helper, the chunk (+1) whose P fragments it
-// has written.
+// With raw rows (see RecLayout) the helper waves also form P for the
+// owners: each forms some of its 16 x 16 blocks, into the fp16 operand
+// fragments (PF, one 1 KiB fragment per 16-token row block and 32-token k
+// step), and the row factors of q (FQ, one float per token), then sets its
+// flag (ints after FQ) to the chunk + 1.
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
@@ -180,18 +175,15 @@ struct StateLayout {
   static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
   static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
-  static constexpr size_t kXS = size_t(DVS / 16) * (DK / 32) * 2048;
-  static constexpr size_t kFlags = 256;
   static constexpr int NBT = C / 16;
   static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
-  static constexpr size_t kPF = size_t(kNPF) * 1024;
-  static constexpr bool kHelperOut = R::kRawK && NBUF == 2 && 2 * kBuf + kXS + kFlags + kPF <= kMaxLds;
-  static constexpr size_t oXS = NBUF * kBuf;
-  static constexpr size_t oFlags = oXS + kXS;
-  static constexpr size_t oPF = oFlags + kFlags;
-  // raw rows without the helper-formed output: no plan (more than the LDS)
-  static constexpr size_t bytes =
-      (R::kRawK && !kHelperOut) ? kMaxLds + 1 : kHelperOut ? oPF + kPF : NBUF * kBuf;
+  static constexpr bool kHelperP = R::kRawK && NBUF == 2;
+  static constexpr size_t oPF = NBUF * kBuf;
+  static constexpr size_t oFQ = oPF + size_t(kNPF) * 1024;
+  static constexpr size_t oFlags = oFQ + chunked_layout::al(size_t(C) * 4);
+  static constexpr size_t kFlags = 256;
+  // raw rows need the helper-formed P: otherwise no plan (more than the LDS)
+  static constexpr size_t bytes = kHelperP ? oFlags + kFlags : R::kRawK ? kMaxLds + 1 : NBUF * kBuf;
 };
 
 }  // namespace kda

@@ -303,17 +303,23 @@ __device__ __forceinline__ void put_perm(unsigned char* tile, int r, int e0, con
 constexpr int kPrepThreads = 512;
 constexpr int kPrepWaves = kPrepThreads / 64;
 
+// Waves per SIMD of the prep kernel: two 8-wave workgroups share a CU with
+// per-channel decay, four with raw rows (the smaller LDS plan), else three.
 template <int DK, int C, typename In, int DECAY>
-// (second bound: waves per SIMD; two 8-wave workgroups share a CU with
-// per-channel decay, three without)
-__global__ __launch_bounds__(kPrepThreads, DECAY == DECAY_CHANNEL ? 4 : 6) void prep_kernel(PrepParams p) {
+constexpr int prep_waves() {
+  return DECAY == DECAY_CHANNEL ? 4
+       : RecLayout<DK, C, sizeof(typename OpOf<In>::T), false>::kRawK ? 8 : 6;
+}
+
+template <int DK, int C, typename In, int DECAY>
+__global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
   constexpr bool headdecay = DECAY == DECAY_HEAD;
-  using L = PrepLayout<DK, C, sizeof(OpT)>;
   using R = RecLayout<DK, C, sizeof(OpT), chan>;
+  using L = PrepLayout<DK, C, sizeof(OpT), R::kRawK>;
   constexpr int NB = L::NB;
   constexpr int V = act<In>::kVec;           // activation elements per 16-byte load
   static_assert(V * sizeof(OpT) == 16, "one 16-byte load makes one 16-byte operand store");
@@ -1411,7 +1417,7 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
                       hipStream_t s) {
   using OpT = typename OpOf<In>::T;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
-  using LP = PrepLayout<DK, C, sizeof(OpT)>;
+  using LP = PrepLayout<DK, C, sizeof(OpT), RecLayout<DK, C, sizeof(OpT), chan>::kRawK>;
   using LS = StateLayout<DK, DVS, C, sizeof(OpT), sizeof(In), chan>;
   if constexpr (LP::bytes(chan) > kMaxLds || LS::bytes > kMaxLds) {
     return hipErrorInvalidConfiguration;   // never instantiated as kernels
@@ -1449,7 +1455,8 @@ template <int OpBytes, int ActBytes>
 size_t lds_bytes(int DK, int DVS, int C, bool chan) {
 #define KDA_L(dk, dvs, c)                                                                  \
   if (DK == dk && DVS == dvs && C == c) {                                                  \
-    const size_t a = PrepLayout<dk, c, OpBytes>::bytes(chan);                              \
+    const size_t a = chan ? PrepLayout<dk, c, OpBytes, false>::bytes(true)                 \
+                          : PrepLayout<dk, c, OpBytes, RecLayout<dk, c, OpBytes, false>::kRawK>::bytes(false); \
     const size_t b = chan ? StateLayout<dk, dvs, c, OpBytes, ActBytes, true>::bytes        \
                           : StateLayout<dk, dvs, c, OpBytes, ActBytes, false>::bytes;      \
     return a > b ? a : b;                                                                  \

@@ -102,8 +102,8 @@ struct RecLayout {
   static constexpr size_t gBytes = bytes - gOff;
 };
 
-// LDS of the prep kernel.
-template <int DK, int C, int OpBytes>
+// LDS of the prep kernel; Raw: raw rows in the record (no q tile here).
+template <int DK, int C, int OpBytes, bool Raw>
 struct PrepLayout {
   static constexpr int NB = C / 16;                 // 16-token blocks per chunk
   static constexpr int NCOL = C < 32 ? 32 : C;      // token columns read by 32-wide k steps
@@ -120,14 +120,15 @@ struct PrepLayout {
 
   // Regions and what they hold:
   //   Q    q normalised (per-channel: and decayed)                load .. Gram
+  //        (none with raw rows)
   //   K    k normalised (per-channel: and decayed)                load .. Gram
   //   AM   fp32 A (Gram .. inverse); per-channel: staged gate first (load)
   //   RA   per-channel: the inverse-prefix Gram factor Kinv (load .. Gram),
-  //        then fp32 T; otherwise fp32 T over the Q and K tiles, dead after
-  //        the Gram
+  //        then fp32 T; otherwise, where it fits, fp32 T over the Q and K
+  //        tiles, dead after the Gram
   // (P goes from the MFMA accumulators straight to the record.)
   static constexpr size_t oQ = 0;
-  static constexpr size_t oK = chunked_layout::al(oQ + kRowTile);
+  static constexpr size_t oK = Raw ? 0 : chunked_layout::al(oQ + kRowTile);
   static constexpr size_t oAM = chunked_layout::al(oK + kRowTile);
   static constexpr size_t szAM(bool ch) { return ch ? chunked_layout::mx(kF32CC, kGst) : kF32CC; }
   static constexpr bool kTinQK = kF32CC <= oAM - oQ;   // T fits over Q and K

@@ -1094,7 +1094,7 @@ void state_kernel(StateParams p) {
 
   if (nchunks > 0) {
     if (!owner) issue(0, smem, std::integral_constant<int, 0>{});
-    finish(0, smem);
+    if (!owner) finish(0, smem);
   }
   lds_barrier();
 
@@ -1326,36 +1326,60 @@ void state_kernel(StateParams p) {
         // are fixed at compile time (one code path per helper).
         auto share = [&](auto hh_) {
           constexpr int hh = decltype(hh_)::value;
-          bf16x8 Qf[NKP];
-          float fq = 0.f, gi = 0.f;
+          auto mine = [](int b) { return b * NHELP / NBLK == hh; };
+          // every operand first (loads are not moved past the fragment
+          // stores below), then the products, then the stores
+          bf16x8 qf[NB][NKP], kf[NB][NKP];
+          float fq[NB], gi[NB];
+          f32x4 fk[NB], gj[NB], acc[NBLK];
+          static_for<NB>([&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
+            constexpr bool col = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_jb(b, NB) == r) return true; return false; }();
+            if constexpr (row) {
+#pragma unroll
+              for (int m = 0; m < NKP; ++m) qf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, r, m));
+              gi[r] = headdecay ? svec[R::vG + 16 * r + l16] : 0.f;
+            }
+            if constexpr (col) {
+#pragma unroll
+              for (int m = 0; m < NKP; ++m) kf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sK, r, m));
+              fk[r] = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * r + 4 * g);
+              gj[r] = headdecay ? *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * r + 4 * g) : f32x4{0, 0, 0, 0};
+            }
+          });
           static_for<NBLK>([&](auto b_) {
             constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
-            if constexpr (b * NHELP / NBLK == hh) {
-              constexpr bool newrow = b == 0 || (b - 1) * NHELP / NBLK != hh || blk_ib(b - 1, NB) != ib;
-              const int i = 16 * ib + l16;
-              if constexpr (newrow) {
-                float ss = 0.f;
+            if constexpr (mine(b)) {
+              acc[b] = f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int m = 0; m < NKP; ++m) {
-                  Qf[m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, ib, m));
-                  ss = sumsq_bf(Qf[m], ss);
-                }
-                fq = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(ss))) : 1.f);
-                gi = headdecay ? svec[R::vG + i] : 0.f;
+              for (int m = 0; m < NKP; ++m) mma_bf(acc[b], kf[jb][m], qf[ib][m]);
+            }
+          });
+          static_for<NB>([&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
+            if constexpr (row) {
+              float s0 = 0.f, s1 = 0.f;   // two chains of dependent dot products
+#pragma unroll
+              for (int m = 0; m < NKP; m += 2) {
+                s0 = sumsq_bf(qf[r][m], s0);
+                if (m + 1 < NKP) s1 = sumsq_bf(qf[r][m + 1], s1);
               }
-              if (jb == 0 && g == 0) sfq[i] = fq;
-              f32x4 acc = f32x4{0, 0, 0, 0};
-#pragma unroll
-              for (int m = 0; m < NKP; ++m)
-                mma_bf(acc, __builtin_bit_cast(bf16x8, fr.kq(sK, jb, m)), Qf[m]);
-              const f32x4 fk = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * jb + 4 * g);
-              f32x4 gj = f32x4{0, 0, 0, 0};
-              if (headdecay) gj = *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * jb + 4 * g);
+              fq[r] = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(s0 + s1))) : 1.f);
+              // the helper with the row's first block publishes its factor
+              constexpr bool pub = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r && blk_jb(b, NB) == 0) return true; return false; }();
+              if (pub && g == 0) sfq[16 * r + l16] = fq[r];
+            }
+          });
+          static_for<NBLK>([&](auto b_) {
+            constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
+            if constexpr (mine(b)) {
               f16x4 hv;
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
-                float x = acc[jj] * fq * fk[jj];
-                if (headdecay) x *= __expf(gi - gj[jj]);
+                float x = acc[b][jj] * fq[ib] * fk[jb][jj];
+                if (headdecay) x *= __expf(gi[ib] - gj[jb][jj]);
                 hv[jj] = static_cast<_Float16>((jb < ib || 4 * g + jj <= l16) ? x : 0.f);
               }
               *reinterpret_cast<f16x4*>(smem + L::oPF + pf_n(ib, jb / 2) * 1024 + lane * 16 + (jb & 1) * 8) = hv;
@@ -1374,7 +1398,9 @@ void state_kernel(StateParams p) {
         lds_barrier();              // every wave is done with the only buffer
         if constexpr (!own) issue(c + 1, smem, std::integral_constant<int, 0>{});
       }
-      finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
+      // (only the helpers wait: the owners' own memory operations are the
+      // output stores, which nothing here reads)
+      if constexpr (!own) finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
       lds_barrier();                // the next chunk is visible to all waves
     }
   };

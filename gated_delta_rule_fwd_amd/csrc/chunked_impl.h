@@ -785,6 +785,12 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// ... all but the latest N of them (vmcnt N: bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 // Wait until this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -907,16 +913,20 @@ void state_kernel(StateParams p) {
   // 16-byte copies per chunk, each helper wave issuing its share: (raw rows)
   // the q and k rows, the record, the value rows
   constexpr bool rawk = R::kRawK;
-  constexpr int nRecI = static_cast<int>(L::kRecLds / 1024);   // whole slots (image padded)
+  constexpr int nRecI = static_cast<int>(L::kRecLds / 1024);   // whole 1 KiB copies (image padded)
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
   constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
   constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
   constexpr int NPF = L::kNPF;                // P operand fragments (raw rows: formed by the helpers)
   constexpr int NBLK = NB * (NB + 1) / 2;     // P's lower-triangular 16 x 16 blocks
   constexpr int kStThreads = 64 * state_waves<DVS>();
-  constexpr int kSlotsR = nRecI / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
-  static_assert(nRecI % NHELP == 0, "record slots shared evenly");
+  constexpr int kSlotsR = (nRecI + NHELP - 1) / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  // Copy instructions of one chunk per helper (for the waits on all but the
+  // latest chunk's copies with three buffers): exact where every slot but
+  // the record's last is taken, else the wait covers every copy.
+  constexpr bool kCountExact = (!rawk || nQKI % NHELP == 0) && nVal % (64 * NHELP) == 0;
   constexpr int kSlotsQ = rawk ? (nQKI + NHELP - 1) / NHELP : 0;
+  constexpr int kCopiesLo = (rawk ? 2 * kSlotsQ : 0) + nRecI / NHELP + kSlotsV;
   static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
   static_assert(nQK % 64 == 0, "k copies fill whole instructions");
@@ -1018,12 +1028,12 @@ void state_kernel(StateParams p) {
     }
     if constexpr (part == 1) return;
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
-    // (the record's LDS image is padded to whole slots of every helper;
-    // pieces past the record read as zero through the buffer's range check)
+    // (the record's LDS image is padded to whole 1 KiB copies; pieces past
+    // the record read as zero through the buffer's range check)
 #pragma unroll
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
-      dma16_buf(rr, dst + R::gOff + j * 1024, j * 1024 + lane * 16, 0);
+      if (nRecI % NHELP == 0 || j < nRecI) dma16_buf(rr, dst + R::gOff + j * 1024, j * 1024 + lane * 16, 0);
     }
     {
       const i32x4 rv =
@@ -1050,8 +1060,16 @@ void state_kernel(StateParams p) {
       }
     }
   };
-  auto finish = [&](int c, unsigned char* buf) {
-    wait_vm();
+  // Helpers, once chunk c's copies into buf have landed: its value rows past
+  // the sequence end.  `newer`: the copies of the chunk after it were issued
+  // since, and may stay in flight.
+  auto finish = [&](int c, unsigned char* buf, bool newer) {
+    if (kCountExact && newer) {
+      if (nRecI % NHELP != 0 && hw < nRecI % NHELP) wait_vm_n<kCopiesLo + 1>();
+      else wait_vm_n<kCopiesLo>();
+    } else {
+      wait_vm();
+    }
     zero_tail(c, buf);
   };
 
@@ -1092,9 +1110,11 @@ void state_kernel(StateParams p) {
     }
   }
 
-  if (nchunks > 0) {
-    if (!owner) issue(0, smem, std::integral_constant<int, 0>{});
-    if (!owner) finish(0, smem);
+  if (nchunks > 0 && !owner) {
+    issue(0, smem, std::integral_constant<int, 0>{});
+    const bool two = L::NBUF == 3 && nchunks > 1;
+    if (two) issue(1, smem + L::kBuf, std::integral_constant<int, 0>{});
+    finish(0, smem, two);
   }
   lds_barrier();
 
@@ -1119,7 +1139,10 @@ void state_kernel(StateParams p) {
     constexpr int cur = decltype(cur_tag)::value;
     constexpr bool own = decltype(own_tag)::value;
     // the helpers copy the next chunk into the other buffer meanwhile
-    const bool pre = L::NBUF == 2 && c + 1 < nchunks;
+    // the helpers copy chunk c + NBUF - 1 into the buffer chunk c - 1 used
+    constexpr int ahead = L::NBUF - 1;
+    const bool pre = L::NBUF >= 2 && c + ahead < nchunks;
+    unsigned char* const nbuf = smem + ((cur + ahead) % (ahead > 0 ? L::NBUF : 1)) * L::kBuf;
 
     if constexpr (own) {
       const unsigned char* bq = smem + cur * L::kBuf;
@@ -1311,7 +1334,8 @@ void state_kernel(StateParams p) {
     } else {
       // helper: the next chunk's copies; with raw rows its share of this
       // chunk's P between the q, k rows and the rest
-      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, hp ? 1 : 0>{});
+      // (three buffers: the copies after P, which then comes first)
+      if (pre && L::NBUF == 2) issue(c + ahead, nbuf, std::integral_constant<int, hp ? 1 : 0>{});
       if constexpr (hp) {
         const unsigned char* bq = smem + cur * L::kBuf;
         const unsigned char* sQ = bq + R::oQ;
@@ -1390,7 +1414,10 @@ void state_kernel(StateParams p) {
           if (hw == decltype(hh_)::value) share(hh_);
         });
         if (lane == 0) __hip_atomic_store(&pflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, 2>{});
+        if (pre) {
+          if constexpr (L::NBUF == 2) issue(c + ahead, nbuf, std::integral_constant<int, 2>{});
+          else issue(c + ahead, nbuf, std::integral_constant<int, 0>{});
+        }
       }
     }
     if (c + 1 < nchunks) {
@@ -1400,24 +1427,27 @@ void state_kernel(StateParams p) {
       }
       // (only the helpers wait: the owners' own memory operations are the
       // output stores, which nothing here reads)
-      if constexpr (!own) finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
+      if constexpr (!own) finish(c + 1, smem + ((cur + 1) % L::NBUF) * L::kBuf, L::NBUF == 3 && pre);
       lds_barrier();                // the next chunk is visible to all waves
     }
   };
 
   using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, L::NBUF == 2 ? 1 : 0>;
-  if (owner) {
-    for (int c = 0; c < nchunks; c += 2) {
-      step(C0{}, std::true_type{}, c);
-      if (c + 1 < nchunks) step(C1{}, std::true_type{}, c + 1);
+  using C1 = std::integral_constant<int, L::NBUF >= 2 ? 1 : 0>;
+  using C2 = std::integral_constant<int, L::NBUF == 3 ? 2 : 0>;
+  auto run = [&](auto own_tag) {
+    for (int c = 0; c < nchunks; c += L::NBUF) {
+      step(C0{}, own_tag, c);
+      if constexpr (L::NBUF >= 2) {
+        if (c + 1 < nchunks) step(C1{}, own_tag, c + 1);
+      }
+      if constexpr (L::NBUF == 3) {
+        if (c + 2 < nchunks) step(C2{}, own_tag, c + 2);
+      }
     }
-  } else {
-    for (int c = 0; c < nchunks; c += 2) {
-      step(C0{}, std::false_type{}, c);
-      if (c + 1 < nchunks) step(C1{}, std::false_type{}, c + 1);
-    }
-  }
+  };
+  if (owner) run(std::true_type{});
+  else run(std::false_type{});
 
   if constexpr (!rawk) {
     if (owner && nchunks > 0) store_out(nchunks - 1);

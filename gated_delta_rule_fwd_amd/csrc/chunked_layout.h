@@ -158,7 +158,9 @@ struct PrepLayout {
 
 // LDS of the state kernel: NBUF buffers, each one chunk's record image
 // followed by its value rows ([C][DVS] activations, rows swizzled).  With two
-// buffers the next chunk is copied in while the current one is computed.
+// buffers the next chunk is copied in while the current one is computed;
+// with three (raw rows, where they fit) the one after it, so that a copy has
+// a whole chunk step more to land.
 //
 // With raw rows (see RecLayout) the helper waves also form P for the
 // owners: each forms some of its 16 x 16 blocks, into the fp16 operand
@@ -169,20 +171,20 @@ template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
   static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
-  // the record's bytes in the image, padded to whole 1 KiB copies for each of
-  // the DVS / 16 waves that issue them
-  static constexpr size_t kRecSlot = size_t(1024) * (DVS / 16);
-  static constexpr size_t kRecLds = (R::gBytes + kRecSlot - 1) / kRecSlot * kRecSlot;
+  // the record's bytes in the image, padded to whole 1 KiB copies
+  static constexpr size_t kRecLds = (R::gBytes + 1023) / 1024 * 1024;
   static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
-  static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
   static constexpr int NBT = C / 16;
   static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
-  static constexpr bool kHelperP = R::kRawK && NBUF == 2;
+  static constexpr size_t kFlags = 256;
+  // beyond the buffers (raw rows): PF, FQ, flags
+  static constexpr size_t kExtra = R::kRawK ? size_t(kNPF) * 1024 + chunked_layout::al(size_t(C) * 4) + kFlags : 0;
+  static constexpr int NBUF = (R::kRawK && 3 * kBuf + kExtra <= kMaxLds) ? 3 : 2 * kBuf <= kMaxLds ? 2 : 1;
+  static constexpr bool kHelperP = R::kRawK && NBUF >= 2;
   static constexpr size_t oPF = NBUF * kBuf;
   static constexpr size_t oFQ = oPF + size_t(kNPF) * 1024;
   static constexpr size_t oFlags = oFQ + chunked_layout::al(size_t(C) * 4);
-  static constexpr size_t kFlags = 256;
   // raw rows need the helper-formed P: otherwise no plan (more than the LDS)
   static constexpr size_t bytes = kHelperP ? oFlags + kFlags : R::kRawK ? kMaxLds + 1 : NBUF * kBuf;
 };

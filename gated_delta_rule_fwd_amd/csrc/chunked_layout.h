@@ -163,28 +163,43 @@ struct PrepLayout {
 // a whole chunk step more to land.
 //
 // With raw rows (see RecLayout) the helper waves also form P for the
-// owners: each forms some of its 16 x 16 blocks, into the fp16 operand
-// fragments (PF, one 1 KiB fragment per 16-token row block and 32-token k
-// step), and the row factors of q (FQ, one float per token), then sets its
-// flag (ints after FQ) to the chunk + 1.
+// owners, one chunk ahead: during the step of chunk c they form chunk c+1's
+// P (three buffers hold chunks c, c+1 and c+2).  Each forms some of its
+// 16 x 16 blocks into the fp16 operand fragments (PF, per 16-token row block
+// ib and 32-token k step m <= ib/2 a 1 KiB fragment, 512 bytes where the
+// upper half is above the diagonal and not stored) and the row factors of q
+// (FQ, one float per token); both are kept for two chunks.  Flags (ints
+// after FQ): per helper, the chunk (+1) whose P share it has written, and
+// the chunk (+1) whose copies of its own have landed.
+__host__ __device__ constexpr bool pf_half(int ib, int m) { return (ib & 1) == 0 && m == ib / 2; }
+// byte offset of fragment (ib, m) within PF
+__host__ __device__ constexpr int pf_off(int ib, int m) {
+  int off = 0;
+  for (int i = 0; i <= ib; ++i)
+    for (int k = 0; k <= i / 2; ++k) {
+      if (i == ib && k == m) return off;
+      off += pf_half(i, k) ? 512 : 1024;
+    }
+  return off;
+}
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
   static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
-  // the record's bytes in the image, padded to whole 1 KiB copies
-  static constexpr size_t kRecLds = (R::gBytes + 1023) / 1024 * 1024;
-  static constexpr size_t oV = R::gOff + kRecLds;
+  static constexpr size_t oV = R::gOff + R::gBytes;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
   static constexpr int NBT = C / 16;
   static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
-  static constexpr size_t kFlags = 256;
-  // beyond the buffers (raw rows): PF, FQ, flags
-  static constexpr size_t kExtra = R::kRawK ? size_t(kNPF) * 1024 + chunked_layout::al(size_t(C) * 4) + kFlags : 0;
+  static constexpr size_t kPF = chunked_layout::al(size_t(pf_off(NBT, 0)));   // one chunk's fragments
+  static constexpr size_t kFQ = chunked_layout::al(size_t(C) * 4);
+  static constexpr size_t kFlags = 64;
+  // beyond the buffers (raw rows): PF and FQ for two chunks, flags
+  static constexpr size_t kExtra = R::kRawK ? 2 * kPF + 2 * kFQ + kFlags : 0;
   static constexpr int NBUF = (R::kRawK && 3 * kBuf + kExtra <= kMaxLds) ? 3 : 2 * kBuf <= kMaxLds ? 2 : 1;
-  static constexpr bool kHelperP = R::kRawK && NBUF >= 2;
+  static constexpr bool kHelperP = R::kRawK && NBUF == 3;
   static constexpr size_t oPF = NBUF * kBuf;
-  static constexpr size_t oFQ = oPF + size_t(kNPF) * 1024;
-  static constexpr size_t oFlags = oFQ + chunked_layout::al(size_t(C) * 4);
+  static constexpr size_t oFQ = oPF + 2 * kPF;
+  static constexpr size_t oFlags = oFQ + 2 * kFQ;
   // raw rows need the helper-formed P: otherwise no plan (more than the LDS)
   static constexpr size_t bytes = kHelperP ? oFlags + kFlags : R::kRawK ? kMaxLds + 1 : NBUF * kBuf;
 };

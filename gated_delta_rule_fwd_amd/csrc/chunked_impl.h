@@ -225,8 +225,11 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
-// P's 16 x 16 blocks (ib, jb <= ib) in the order the state kernel's helper
-// waves share them: ib from the last row block down, then jb up.
+// P operand fragments of the state kernel: fragment pf_n(ib, m) holds row
+// block ib at the 32-token k step m (m <= ib / 2), fragments running over ib,
+// then m.  P's 16 x 16 blocks (ib, jb <= ib) in the order the helper waves
+// share them: ib from the last row block down, then jb up.
+__host__ __device__ constexpr int pf_n(int ib, int m) { return ib / 2 * (ib / 2 + 1) + (ib & 1) * (ib / 2 + 1) + m; }
 __host__ __device__ constexpr int blk_ib(int b, int nb) { int i = nb - 1; while (b > i) { b -= i + 1; --i; } return i; }
 __host__ __device__ constexpr int blk_jb(int b, int nb) { int i = nb - 1; while (b > i) { b -= i + 1; --i; } return b; }
 
@@ -782,12 +785,6 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// ... all but the latest N of them (vmcnt N: bits 3:0 and 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vm_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 // Wait until this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -910,20 +907,16 @@ void state_kernel(StateParams p) {
   // 16-byte copies per chunk, each helper wave issuing its share: (raw rows)
   // the q and k rows, the record, the value rows
   constexpr bool rawk = R::kRawK;
-  constexpr int nRec = static_cast<int>(R::gBytes / 16), nRecI = (nRec + 63) / 64;
+  constexpr int nRecI = static_cast<int>(L::kRecLds / 1024);   // whole slots (image padded)
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
   constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
   constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
   constexpr int NPF = L::kNPF;                // P operand fragments (raw rows: formed by the helpers)
   constexpr int NBLK = NB * (NB + 1) / 2;     // P's lower-triangular 16 x 16 blocks
   constexpr int kStThreads = 64 * state_waves<DVS>();
-  constexpr int kSlotsR = (nRecI + NHELP - 1) / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
-  // Copy instructions of one chunk per helper (for the waits on all but the
-  // latest chunk's copies with three buffers): exact where every slot but
-  // the record's last is taken, else the wait covers every copy.
-  constexpr bool kCountExact = (!rawk || nQKI % NHELP == 0) && nVal % (64 * NHELP) == 0;
+  constexpr int kSlotsR = nRecI / NHELP, kSlotsV = (nValI + NHELP - 1) / NHELP;
+  static_assert(nRecI % NHELP == 0, "record slots shared evenly");
   constexpr int kSlotsQ = rawk ? (nQKI + NHELP - 1) / NHELP : 0;
-  constexpr int kCopiesLo = (rawk ? 2 * kSlotsQ : 0) + nRecI / NHELP + kSlotsV;
   static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
   static_assert(nQK % 64 == 0, "k copies fill whole instructions");
@@ -1025,14 +1018,12 @@ void state_kernel(StateParams p) {
     }
     if constexpr (part == 1) return;
     const i32x4 rr = rsrc(rec0 + static_cast<size_t>(c) * R::gBytes, static_cast<int>(R::gBytes));
+    // (the record's LDS image is padded to whole slots of every helper;
+    // pieces past the record read as zero through the buffer's range check)
 #pragma unroll
     for (int sl = 0; sl < kSlotsR; ++sl) {
       const int j = sl * NHELP + hw;
-      if (nRecI % NHELP == 0 || j < nRecI) {
-        // (the last copy may hold fewer than 64 pieces)
-        if (nRec % 64 == 0 || j < nRecI - 1 || lane < nRec % 64)
-          dma16_buf(rr, dst + R::gOff + j * 1024, j * 1024 + lane * 16, 0);
-      }
+      dma16_buf(rr, dst + R::gOff + j * 1024, j * 1024 + lane * 16, 0);
     }
     {
       const i32x4 rv =
@@ -1059,16 +1050,8 @@ void state_kernel(StateParams p) {
       }
     }
   };
-  // Helpers, once chunk c's copies into buf have landed: its value rows past
-  // the sequence end.  `newer`: the copies of the chunk after it were issued
-  // since, and may stay in flight.
-  auto finish = [&](int c, unsigned char* buf, bool newer) {
-    if (kCountExact && newer) {
-      if (nRecI % NHELP != 0 && hw < nRecI % NHELP) wait_vm_n<kCopiesLo + 1>();
-      else wait_vm_n<kCopiesLo>();
-    } else {
-      wait_vm();
-    }
+  auto finish = [&](int c, unsigned char* buf) {
+    wait_vm();
     zero_tail(c, buf);
   };
 
@@ -1093,119 +1076,30 @@ void state_kernel(StateParams p) {
   }
 
   // Raw rows (see StateLayout): the helpers form P's operand fragments and
-  // q's row factors a chunk ahead, and flag each chunk's.
+  // q's row factors, and flag each chunk's.
   constexpr bool hp = L::kHelperP;
   static_assert(hp == rawk, "raw rows go with the helper-formed P");
   int* pflags = reinterpret_cast<int*>(smem + L::oFlags);   // helper h's P of chunk c written: c + 1
-  int* lflags = pflags + 8;                                 // helper h's copies of chunk c landed: c + 1
-  auto pf_at = [&](int c) { return smem + L::oPF + (c & 1) * L::kPF; };
-  auto fq_at = [&](int c) { return reinterpret_cast<float*>(smem + L::oFQ + (c & 1) * L::kFQ); };
-
-  // Helper hh's share of chunk c's P, from the chunk's buffer bqp.  Block
-  // (ib, jb) of P: P_ij = fq_i fk_j exp(G_i - G_j) q_i . k_j for j <= i, else
-  // 0 (the raw products come transposed: tokens j by tokens i), the fp16
-  // half jb & 1 of operand fragment (ib, jb / 2).  q's row factor comes from
-  // the q fragments (a lane's 8 channels per k step; the 4 lane groups of a
-  // row hold its other channels); the helper with block (ib, 0) also puts it
-  // in FQ.  A helper's blocks are fixed at compile time (one code path per
-  // helper).
-  auto share = [&](auto hh_, const unsigned char* bqp, int c) __attribute__((always_inline)) {
-    constexpr int hh = decltype(hh_)::value;
-    const unsigned char* sQ = bqp + R::oQ;
-    const unsigned char* sK = bqp + R::oK;
-    const float* svec = reinterpret_cast<const float*>(bqp + R::oVec);
-    unsigned char* pf = pf_at(c);
-    float* sfq = fq_at(c);
-    auto mine = [](int b) { return b * NHELP / NBLK == hh; };
-    // every operand first (loads are not moved past the fragment stores
-    // below), then the products, then the stores
-    bf16x8 qf[NB][NKP], kf[NB][NKP];
-    float fq[NB], gi[NB];
-    f32x4 fk[NB], gj[NB], acc[NBLK];
-    static_for<NB>([&](auto r_) {
-      constexpr int r = decltype(r_)::value;
-      constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
-      constexpr bool col = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_jb(b, NB) == r) return true; return false; }();
-      if constexpr (row) {
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) qf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, r, m));
-        gi[r] = headdecay ? svec[R::vG + 16 * r + l16] : 0.f;
-      }
-      if constexpr (col) {
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) kf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sK, r, m));
-        fk[r] = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * r + 4 * g);
-        gj[r] = headdecay ? *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * r + 4 * g) : f32x4{0, 0, 0, 0};
-      }
-    });
-    static_for<NBLK>([&](auto b_) {
-      constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
-      if constexpr (mine(b)) {
-        acc[b] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) mma_bf(acc[b], kf[jb][m], qf[ib][m]);
-      }
-    });
-    static_for<NB>([&](auto r_) {
-      constexpr int r = decltype(r_)::value;
-      constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
-      if constexpr (row) {
-        float s0 = 0.f, s1 = 0.f;   // two chains of dependent dot products
-#pragma unroll
-        for (int m = 0; m < NKP; m += 2) {
-          s0 = sumsq_bf(qf[r][m], s0);
-          if (m + 1 < NKP) s1 = sumsq_bf(qf[r][m + 1], s1);
-        }
-        fq[r] = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(s0 + s1))) : 1.f);
-        constexpr bool pub = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r && blk_jb(b, NB) == 0) return true; return false; }();
-        if (pub && g == 0) sfq[16 * r + l16] = fq[r];
-      }
-    });
-    static_for<NBLK>([&](auto b_) {
-      constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
-      if constexpr (mine(b)) {
-        f16x4 hv;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float x = acc[b][jj] * fq[ib] * fk[jb][jj];
-          if (headdecay) x *= __expf(gi[ib] - gj[jb][jj]);
-          hv[jj] = static_cast<_Float16>((jb < ib || 4 * g + jj <= l16) ? x : 0.f);
-        }
-        constexpr bool half = pf_half(ib, jb / 2);
-        *reinterpret_cast<f16x4*>(pf + pf_off(ib, jb / 2) + lane * (half ? 8 : 16) + (jb & 1) * 8) = hv;
-      }
-    });
-  };
-  // Helpers, once their own copies of chunk c have landed: flag that, wait
-  // for every helper's, form their share of chunk c's P from buffer bqp, flag.
-  auto p_ahead = [&](int c, const unsigned char* bqp) __attribute__((always_inline)) {
-    if (lane == 0) __hip_atomic_store(&lflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-    for (int h2 = 0; h2 < NHELP; ++h2) {
-      while (__hip_atomic_load(&lflags[h2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 1)
-        __builtin_amdgcn_s_sleep(1);
-    }
-    static_for<NHELP>([&](auto hh_) {
-      if (hw == decltype(hh_)::value) share(hh_, bqp, c);
-    });
-    if (lane == 0) __hip_atomic_store(&pflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  };
+  float* sfq = reinterpret_cast<float*>(smem + L::oFQ);     // q's row factor per token of the chunk
   if constexpr (hp) {
-    if (!owner && lane == 0) pflags[hw] = lflags[hw] = 0;
-    lds_barrier();
+    if (!owner && lane == 0) pflags[hw] = 0;
+    // the fragments' halves above the diagonal (column block ib + 1 of an
+    // even row block ib) stay zero
+    if (hw == 0) {
+#pragma unroll
+      for (int ib = 0; ib < NB; ib += 2)
+        *reinterpret_cast<f16x4*>(smem + L::oPF + pf_n(ib, ib / 2) * 1024 + lane * 16 + 8) = f16x4{0, 0, 0, 0};
+    }
   }
 
-  if (nchunks > 0 && !owner) {
-    issue(0, smem, std::integral_constant<int, 0>{});
-    const bool two = L::NBUF == 3 && nchunks > 1;
-    if (two) issue(1, smem + L::kBuf, std::integral_constant<int, 0>{});
-    finish(0, smem, two);
-    if constexpr (hp) p_ahead(0, smem);
+  if (nchunks > 0) {
+    if (!owner) issue(0, smem, std::integral_constant<int, 0>{});
+    if (!owner) finish(0, smem);
   }
   lds_barrier();
 
-  // Output rows of a chunk: stored during the next step, so that the stores
-  // wait for nothing
+  // Output rows of a chunk (without raw rows stored at the start of the next
+  // one, so that the stores wait for nothing)
   f32x4 Oprev[NB];
   const int obyte = 16 * wave * 4 + 4 * g * 4;   // this lane's column bytes within a row of o (owners)
   auto store_out = [&](int c) {
@@ -1225,10 +1119,7 @@ void state_kernel(StateParams p) {
     constexpr int cur = decltype(cur_tag)::value;
     constexpr bool own = decltype(own_tag)::value;
     // the helpers copy the next chunk into the other buffer meanwhile
-    // the helpers copy chunk c + NBUF - 1 into the buffer chunk c - 1 used
-    constexpr int ahead = L::NBUF - 1;
-    const bool pre = L::NBUF >= 2 && c + ahead < nchunks;
-    unsigned char* const nbuf = smem + ((cur + ahead) % (ahead > 0 ? L::NBUF : 1)) * L::kBuf;
+    const bool pre = L::NBUF == 2 && c + 1 < nchunks;
 
     if constexpr (own) {
       const unsigned char* bq = smem + cur * L::kBuf;
@@ -1251,15 +1142,14 @@ void state_kernel(StateParams p) {
         if constexpr (rawk) Sb[m] = bf_from_acc(S[2 * m], S[2 * m + 1]);
         else Sf[m] = M::from_acc(S[2 * m], S[2 * m + 1]);
       }
-      // K S0 and S0^T Q^T: both read only S0.  Raw rows: K S0 first, S0^T Q^T
-      // (S0 in two bf16 parts) once D's products are issued, so that the
-      // chain K S0 -> X -> D does not queue behind it on the MFMA pipe; the
-      // previous chunk's output rows are stored once K S0 is issued (their
-      // products are done by then).
+      // K S0 and S0^T Q^T: both read only S0, so their products interleave
       f32x4 Xl[NB], Ol[NB];
-      [[maybe_unused]] bf16x8 fqb[NB][NKP];
       if constexpr (rawk) {
-        bf16x8 fkb[NB][NKP];
+        // every operand first, then the products with each accumulator's
+        // successive steps NB products apart (S0 in two bf16 parts for the
+        // output, the low part into Ol2)
+        bf16x8 fqb[NB][NKP], fkb[NB][NKP];
+        f32x4 Ol2[NB];
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
 #pragma unroll
@@ -1267,14 +1157,20 @@ void state_kernel(StateParams p) {
             fkb[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sK, rt, m));
             fqb[rt][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, rt, m));
           }
-          Xl[rt] = Ol[rt] = f32x4{0, 0, 0, 0};
+          Xl[rt] = Ol[rt] = Ol2[rt] = f32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
+          const bf16x8 sl = bf_lo(S[2 * m], S[2 * m + 1], Sb[m]);
 #pragma unroll
           for (int rt = 0; rt < NB; ++rt) mma_bf(Xl[rt], fkb[rt][m], Sb[m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol[rt], Sb[m], fqb[rt][m]);
+#pragma unroll
+          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol2[rt], sl, fqb[rt][m]);
         }
-        if (c > 0) store_out(c - 1);
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) Ol[rt] += Ol2[rt];
       } else {
 #pragma unroll
         for (int rt = 0; rt < NB; ++rt) {
@@ -1342,46 +1238,21 @@ void state_kernel(StateParams p) {
               __builtin_amdgcn_s_sleep(1);
           }
         }
-        [[maybe_unused]] const unsigned char* pf = pf_at(c);
-        [[maybe_unused]] const float* sfq = fq_at(c);
 #pragma unroll
-        for (int rt = 0; rt < NB; ++rt) {
+        for (int rt = 0, n = 0; rt < NB; ++rt) {
           float f = headdecay ? svec[R::vEG + 16 * rt + l16] : 1.f;
           if constexpr (rawk) f *= sfq[16 * rt + l16];
           if (headdecay || rawk) Ol[rt] *= f;
 #pragma unroll
-          for (int m = 0; m <= rt / 2; ++m) {
-            if constexpr (rawk) {
-              typename M::frag pv;
-              if (pf_half(rt, m)) {
-                const f16x4 lo = *reinterpret_cast<const f16x4*>(pf + pf_off(rt, m) + lane * 8);
-                pv = __builtin_shufflevector(lo, f16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-              } else {
-                pv = *reinterpret_cast<const typename M::frag*>(pf + pf_off(rt, m) + lane * 16);
-              }
-              M::mma(Ol[rt], Df[m], pv);
-            } else {
+          for (int m = 0; m <= rt / 2; ++m, ++n) {
+            if constexpr (rawk)
+              M::mma(Ol[rt], Df[m], *reinterpret_cast<const typename M::frag*>(smem + L::oPF + n * 1024 + lane * 16));
+            else
               M::mma(Ol[rt], Df[m], fr.cc(sP, rt, m));
-            }
           }
         }
       };
       if constexpr (!rawk) form_out();
-      if constexpr (rawk) {
-        f32x4 Ol2[NB];
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Ol2[rt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          const bf16x8 sl = bf_lo(S[2 * m], S[2 * m + 1], Sb[m]);
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol[rt], Sb[m], fqb[rt][m]);
-#pragma unroll
-          for (int rt = 0; rt < NB; ++rt) mma_bf(Ol2[rt], sl, fqb[rt][m]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NB; ++rt) Ol[rt] += Ol2[rt];
-      }
       // S <- exp(G_last) S0 + KY^T D, KY = K * exp(G_last - G)
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
@@ -1436,17 +1307,90 @@ void state_kernel(StateParams p) {
       if constexpr (rawk) form_out();
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt) Oprev[rt] = Ol[rt];
+      if constexpr (rawk) store_out(c);
     } else {
-      // helper: the copies of the chunk NBUF - 1 ahead; with raw rows (three
-      // buffers) then, once the next chunk's own copies have landed, its
-      // share of the next chunk's P
-      if (pre) issue(c + ahead, nbuf, std::integral_constant<int, 0>{});
+      // helper: the next chunk's copies; with raw rows its share of this
+      // chunk's P between the q, k rows and the rest
+      if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, hp ? 1 : 0>{});
       if constexpr (hp) {
-        if (c + 1 < nchunks) {
-          unsigned char* b1 = smem + ((cur + 1) % L::NBUF) * L::kBuf;
-          finish(c + 1, b1, pre);
-          p_ahead(c + 1, b1);
-        }
+        const unsigned char* bq = smem + cur * L::kBuf;
+        const unsigned char* sQ = bq + R::oQ;
+        const unsigned char* sK = bq + R::oK;
+        const float* svec = reinterpret_cast<const float*>(bq + R::oVec);
+        // Block (ib, jb) of P: P_ij = fq_i fk_j exp(G_i - G_j) q_i . k_j for
+        // j <= i, else 0 (the raw products come transposed: tokens j by
+        // tokens i), the fp16 half jb & 1 of operand fragment pf_n(ib, jb / 2).
+        // q's row factor comes from the q fragments (a lane's 8 channels per
+        // k step; the 4 lane groups of a row hold its other channels); the
+        // helper with block (ib, 0) also puts it in FQ.  The blocks of a helper
+        // are fixed at compile time (one code path per helper).
+        auto share = [&](auto hh_) {
+          constexpr int hh = decltype(hh_)::value;
+          auto mine = [](int b) { return b * NHELP / NBLK == hh; };
+          // every operand first (loads are not moved past the fragment
+          // stores below), then the products, then the stores
+          bf16x8 qf[NB][NKP], kf[NB][NKP];
+          float fq[NB], gi[NB];
+          f32x4 fk[NB], gj[NB], acc[NBLK];
+          static_for<NB>([&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
+            constexpr bool col = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_jb(b, NB) == r) return true; return false; }();
+            if constexpr (row) {
+#pragma unroll
+              for (int m = 0; m < NKP; ++m) qf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sQ, r, m));
+              gi[r] = headdecay ? svec[R::vG + 16 * r + l16] : 0.f;
+            }
+            if constexpr (col) {
+#pragma unroll
+              for (int m = 0; m < NKP; ++m) kf[r][m] = __builtin_bit_cast(bf16x8, fr.kq(sK, r, m));
+              fk[r] = *reinterpret_cast<const f32x4*>(svec + R::vFK + 16 * r + 4 * g);
+              gj[r] = headdecay ? *reinterpret_cast<const f32x4*>(svec + R::vG + 16 * r + 4 * g) : f32x4{0, 0, 0, 0};
+            }
+          });
+          static_for<NBLK>([&](auto b_) {
+            constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
+            if constexpr (mine(b)) {
+              acc[b] = f32x4{0, 0, 0, 0};
+#pragma unroll
+              for (int m = 0; m < NKP; ++m) mma_bf(acc[b], kf[jb][m], qf[ib][m]);
+            }
+          });
+          static_for<NB>([&](auto r_) {
+            constexpr int r = decltype(r_)::value;
+            constexpr bool row = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r) return true; return false; }();
+            if constexpr (row) {
+              float s0 = 0.f, s1 = 0.f;   // two chains of dependent dot products
+#pragma unroll
+              for (int m = 0; m < NKP; m += 2) {
+                s0 = sumsq_bf(qf[r][m], s0);
+                if (m + 1 < NKP) s1 = sumsq_bf(qf[r][m + 1], s1);
+              }
+              fq[r] = p.scale * (p.l2norm ? inv_norm(xor32_sum(xor16_sum(s0 + s1))) : 1.f);
+              // the helper with the row's first block publishes its factor
+              constexpr bool pub = [] { for (int b = 0; b < NBLK; ++b) if (b * NHELP / NBLK == hh && blk_ib(b, NB) == r && blk_jb(b, NB) == 0) return true; return false; }();
+              if (pub && g == 0) sfq[16 * r + l16] = fq[r];
+            }
+          });
+          static_for<NBLK>([&](auto b_) {
+            constexpr int b = decltype(b_)::value, ib = blk_ib(b, NB), jb = blk_jb(b, NB);
+            if constexpr (mine(b)) {
+              f16x4 hv;
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                float x = acc[b][jj] * fq[ib] * fk[jb][jj];
+                if (headdecay) x *= __expf(gi[ib] - gj[jb][jj]);
+                hv[jj] = static_cast<_Float16>((jb < ib || 4 * g + jj <= l16) ? x : 0.f);
+              }
+              *reinterpret_cast<f16x4*>(smem + L::oPF + pf_n(ib, jb / 2) * 1024 + lane * 16 + (jb & 1) * 8) = hv;
+            }
+          });
+        };
+        static_for<NHELP>([&](auto hh_) {
+          if (hw == decltype(hh_)::value) share(hh_);
+        });
+        if (lane == 0) __hip_atomic_store(&pflags[hw], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (pre) issue(c + 1, smem + (cur ^ 1) * L::kBuf, std::integral_constant<int, 2>{});
       }
     }
     if (c + 1 < nchunks) {
@@ -1454,32 +1398,30 @@ void state_kernel(StateParams p) {
         lds_barrier();              // every wave is done with the only buffer
         if constexpr (!own) issue(c + 1, smem, std::integral_constant<int, 0>{});
       }
-      // (only the helpers wait, and with raw rows they have already: the
-      // owners' own memory operations are the output stores, which nothing
-      // here reads)
-      if constexpr (!own && !hp) finish(c + 1, smem + ((cur + 1) % L::NBUF) * L::kBuf, L::NBUF == 3 && pre);
+      // (only the helpers wait: the owners' own memory operations are the
+      // output stores, which nothing here reads)
+      if constexpr (!own) finish(c + 1, L::NBUF == 2 ? smem + (cur ^ 1) * L::kBuf : smem);
       lds_barrier();                // the next chunk is visible to all waves
     }
   };
 
   using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, L::NBUF >= 2 ? 1 : 0>;
-  using C2 = std::integral_constant<int, L::NBUF == 3 ? 2 : 0>;
-  auto run = [&](auto own_tag) {
-    for (int c = 0; c < nchunks; c += L::NBUF) {
-      step(C0{}, own_tag, c);
-      if constexpr (L::NBUF >= 2) {
-        if (c + 1 < nchunks) step(C1{}, own_tag, c + 1);
-      }
-      if constexpr (L::NBUF == 3) {
-        if (c + 2 < nchunks) step(C2{}, own_tag, c + 2);
-      }
+  using C1 = std::integral_constant<int, L::NBUF == 2 ? 1 : 0>;
+  if (owner) {
+    for (int c = 0; c < nchunks; c += 2) {
+      step(C0{}, std::true_type{}, c);
+      if (c + 1 < nchunks) step(C1{}, std::true_type{}, c + 1);
     }
-  };
-  if (owner) run(std::true_type{});
-  else run(std::false_type{});
+  } else {
+    for (int c = 0; c < nchunks; c += 2) {
+      step(C0{}, std::false_type{}, c);
+      if (c + 1 < nchunks) step(C1{}, std::false_type{}, c + 1);
+    }
+  }
 
-  if (owner && nchunks > 0) store_out(nchunks - 1);
+  if constexpr (!rawk) {
+    if (owner && nchunks > 0) store_out(nchunks - 1);
+  }
   if (owner) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {

@@ -158,48 +158,31 @@ struct PrepLayout {
 
 // LDS of the state kernel: NBUF buffers, each one chunk's record image
 // followed by its value rows ([C][DVS] activations, rows swizzled).  With two
-// buffers the next chunk is copied in while the current one is computed;
-// with three (raw rows, where they fit) the one after it, so that a copy has
-// a whole chunk step more to land.
+// buffers the next chunk is copied in while the current one is computed.
 //
 // With raw rows (see RecLayout) the helper waves also form P for the
-// owners, one chunk ahead: during the step of chunk c they form chunk c+1's
-// P (three buffers hold chunks c, c+1 and c+2).  Each forms some of its
-// 16 x 16 blocks into the fp16 operand fragments (PF, per 16-token row block
-// ib and 32-token k step m <= ib/2 a 1 KiB fragment, 512 bytes where the
-// upper half is above the diagonal and not stored) and the row factors of q
-// (FQ, one float per token); both are kept for two chunks.  Flags (ints
-// after FQ): per helper, the chunk (+1) whose P share it has written, and
-// the chunk (+1) whose copies of its own have landed.
-__host__ __device__ constexpr bool pf_half(int ib, int m) { return (ib & 1) == 0 && m == ib / 2; }
-// byte offset of fragment (ib, m) within PF
-__host__ __device__ constexpr int pf_off(int ib, int m) {
-  int off = 0;
-  for (int i = 0; i <= ib; ++i)
-    for (int k = 0; k <= i / 2; ++k) {
-      if (i == ib && k == m) return off;
-      off += pf_half(i, k) ? 512 : 1024;
-    }
-  return off;
-}
+// owners: each forms some of its 16 x 16 blocks, into the fp16 operand
+// fragments (PF, one 1 KiB fragment per 16-token row block and 32-token k
+// step), and the row factors of q (FQ, one float per token), then sets its
+// flag (ints after FQ) to the chunk + 1.
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
   static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
-  static constexpr size_t oV = R::gOff + R::gBytes;
+  // the record's bytes in the image, padded to whole 1 KiB copies for each of
+  // the DVS / 16 waves that issue them
+  static constexpr size_t kRecSlot = size_t(1024) * (DVS / 16);
+  static constexpr size_t kRecLds = (R::gBytes + kRecSlot - 1) / kRecSlot * kRecSlot;
+  static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
+  static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
   static constexpr int NBT = C / 16;
   static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
-  static constexpr size_t kPF = chunked_layout::al(size_t(pf_off(NBT, 0)));   // one chunk's fragments
-  static constexpr size_t kFQ = chunked_layout::al(size_t(C) * 4);
-  static constexpr size_t kFlags = 64;
-  // beyond the buffers (raw rows): PF and FQ for two chunks, flags
-  static constexpr size_t kExtra = R::kRawK ? 2 * kPF + 2 * kFQ + kFlags : 0;
-  static constexpr int NBUF = (R::kRawK && 3 * kBuf + kExtra <= kMaxLds) ? 3 : 2 * kBuf <= kMaxLds ? 2 : 1;
-  static constexpr bool kHelperP = R::kRawK && NBUF == 3;
+  static constexpr bool kHelperP = R::kRawK && NBUF == 2;
   static constexpr size_t oPF = NBUF * kBuf;
-  static constexpr size_t oFQ = oPF + 2 * kPF;
-  static constexpr size_t oFlags = oFQ + 2 * kFQ;
+  static constexpr size_t oFQ = oPF + size_t(kNPF) * 1024;
+  static constexpr size_t oFlags = oFQ + chunked_layout::al(size_t(C) * 4);
+  static constexpr size_t kFlags = 256;
   // raw rows need the helper-formed P: otherwise no plan (more than the LDS)
   static constexpr size_t bytes = kHelperP ? oFlags + kFlags : R::kRawK ? kMaxLds + 1 : NBUF * kBuf;
 };

@@ -70,6 +70,12 @@ CHUNK_CASES = [
     ("gdn_d128", dict(B=1, T=100, H=2, DK=64, DV=128)),
     ("kda_d128", dict(B=1, T=90, H=2, DK=128, DV=32)),
     ("deltanet_d64", dict(B=1, T=64, H=2, DK=32, DV=64, chunk=32)),
+    # enough heads for the wider value slices (64 and 32 columns: four and
+    # two helper waves sharing P), ragged tails
+    ("gdn_d128", dict(B=2, T=100, H=64)),
+    ("gdn_d128", dict(B=1, T=70, H=64, init_state=True)),
+    ("gdn_d128", dict(B=1, T=90, H=64, chunk=32)),
+    ("deltanet_d64", dict(B=4, T=70, H=64)),
     # per-channel decay steep enough for the wide-range operand fallback
     ("kda_d128", dict(B=1, T=200, H=2, decay="channel_steep", init_state=True)),
     ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_steep")),

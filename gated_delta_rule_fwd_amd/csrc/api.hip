@@ -92,6 +92,32 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
   return kda::to_status(kda::launch_chunked(a, s));
 }
 
+int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* beta,
+                           const void* decay, int decay_kind, const float* initial_state,
+                           float* o, float* final_state, const int* cu_seqlens,
+                           const int* cu_seqlens_host, int N,
+                           int T, int H, int DK, int DV, int dtype,
+                           float softmax_scale, int use_qk_l2norm, int chunk_size, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, 1, T, H, DK, DV, dtype);
+  if (st != KDA_OK) return st;
+  if (!final_state || !cu_seqlens || !cu_seqlens_host || (T != 0 && !o)) return KDA_ERR_NULL;
+  if (N < 1 || static_cast<long long>(N) * H * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T) return KDA_ERR_SHAPE;
+  for (int n = 0; n < N; ++n)
+    if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_SHAPE;
+  if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  if (kda::chunked_lds_bytes(DK, DV, chunk_size, dtype, decay_kind) == 0) return KDA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    return kda::to_status(kda::launch_state_copy(initial_state, final_state,
+                                                 static_cast<long>(N) * H * DK * DV, s));
+  }
+  const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
+                                        final_state, 1, T, H, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, chunk_size);
+  return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, s));
+}
+
 int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
                       const void* decay, int decay_kind, const float* initial_state,
                       float* o, float* final_state,
@@ -135,6 +161,6 @@ const char* kda_status_string(int status) {
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 100; }
+int kda_abi_version(void) { return 101; }
 
 }  // extern "C"

@@ -101,11 +101,13 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   PrepParams pp;
+  pp.cu = nullptr; pp.cb = nullptr; pp.nseq = a.B;
   pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
   pp.ws = static_cast<unsigned char*>(ws);
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
 
   StateParams sp;
+  sp.cu = nullptr; sp.cb = nullptr;
   sp.q = a.q; sp.k = a.k;
   sp.l2norm = a.l2norm; sp.scale = a.scale;
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
@@ -130,6 +132,80 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+namespace {
+
+// cb[0] = 0, cb[n + 1] = cb[n] + ceil((cu[n + 1] - cu[n]) / C): one wave,
+// an inclusive lane scan per 64 sequences.
+__global__ void chunk_offsets_kernel(const int* __restrict__ cu, int* __restrict__ cb, int nseq, int C) {
+  const int lane = threadIdx.x;
+  int carry = 0;
+  if (lane == 0) cb[0] = 0;
+  for (int base = 0; base < nseq; base += 64) {
+    const int n = base + lane;
+    int x = n < nseq ? (cu[n + 1] - cu[n] + C - 1) / C : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (n < nseq) cb[n + 1] = carry + x;
+    carry += __shfl(x, 63, 64);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int* cu_host, int nseq,
+                                 hipStream_t s) {
+  const bool chan = a.decay_kind == DECAY_CHANNEL;
+  const Plan pl = plan_for(nseq, a.H, a.DK, a.DV, a.chunk, a.dtype, chan);
+  if (pl.dvs == 0) return hipErrorInvalidConfiguration;
+  long total = 0;   // chunks of all sequences
+  for (int n = 0; n < nseq; ++n) total += (cu_host[n + 1] - cu_host[n] + a.chunk - 1) / a.chunk;
+  const size_t rec = a.dtype == 0 ? chunked::record_bytes<4>(a.DK, a.chunk, chan)
+                                  : chunked::record_bytes<2>(a.DK, a.chunk, chan);
+  if (rec == 0) return hipErrorInvalidConfiguration;
+  const size_t recs = rec * static_cast<size_t>(total) * a.H;
+  void* ws = nullptr;
+  hipError_t e = workspace(s, recs + (static_cast<size_t>(nseq) + 1) * sizeof(int), &ws);
+  if (e != hipSuccess) return e;
+  int* cb = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + recs);
+  chunk_offsets_kernel<<<dim3(1), dim3(64), 0, s>>>(cu_dev, cb, nseq, a.chunk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (total == 0) {
+    // every sequence is empty: the final states are the initial ones
+    return launch_state_copy(a.init, a.state, static_cast<long>(nseq) * a.H * a.DK * a.DV, s);
+  }
+
+  PrepParams pp;
+  pp.cu = cu_dev; pp.cb = cb; pp.nseq = nseq;
+  pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
+  pp.ws = static_cast<unsigned char*>(ws);
+  pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
+  pp.c0 = 0; pp.nchunks = static_cast<int>(total);
+
+  StateParams sp;
+  sp.cu = cu_dev; sp.cb = cb;
+  sp.q = a.q; sp.k = a.k;
+  sp.l2norm = a.l2norm; sp.scale = a.scale;
+  sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
+  sp.o = a.o; sp.state = a.state; sp.init = a.init;
+  sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
+  sp.nsl = a.DV / pl.dvs;
+  const int nheads = nseq * a.H;
+  sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
+  sp.c0 = 0; sp.nchunks = static_cast<int>(total);
+
+  using LaunchFn = hipError_t (*)(int, int, int, const PrepParams&, int, const StateParams&, int,
+                                  hipStream_t);
+  static const LaunchFn table[2][3] = {
+      {chunked::launch_f32_d0, chunked::launch_f32_d1, chunked::launch_f32_d2},
+      {chunked::launch_bf16_d0, chunked::launch_bf16_d1, chunked::launch_bf16_d2}};
+  const LaunchFn fn = table[a.dtype == 0 ? 0 : 1][a.decay_kind];
+  return fn(a.DK, pl.dvs, a.chunk, pp, a.H * static_cast<int>(total), sp, nheads * sp.nsl, s);
 }
 
 }  // namespace kda

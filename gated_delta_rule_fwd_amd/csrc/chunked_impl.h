@@ -195,12 +195,17 @@ __device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* 
 template <typename In> struct OpOf { using T = _Float16; using KinvT = uint16_t; };
 template <> struct OpOf<float> { using T = float; using KinvT = float; };
 
+// Packed variable-length input (B = 1, N sequences back to back in T): cu
+// holds the N + 1 token offsets of the sequences, cb the N + 1 offsets of
+// their chunks (chunks never cross a sequence end); nchunks is then the total
+// chunk count.  NULL cu: N = B sequences of T tokens each.
 struct PrepParams {
   const void* q; const void* k; const void* beta; const void* decay;
-  unsigned char* ws;     // records, [B*H][nchunks]
+  unsigned char* ws;     // records, [B*H][nchunks] ([H][chunks] packed)
   int T, H, nchunks, l2norm;
   int c0;                // first chunk of this launch (records are indexed from it)
   float scale;
+  const int* cu; const int* cb; int nseq;   // packed input
 };
 
 struct StateParams {
@@ -210,7 +215,20 @@ struct StateParams {
   int T, H, DV, nchunks, nsl, xcd_map;
   int c0;                // first chunk of this launch; `init` holds the state entering it
   int l2norm; float scale;   // q's row factor (raw rows)
+  const int* cu; const int* cb;   // packed input (see PrepParams); state and o by sequence
 };
+
+// The sequence of packed chunk g: the last n with cb[n] <= g (cb
+// nondecreasing, cb[0] = 0 <= g < cb[nseq]).
+__device__ __forceinline__ int seq_of_chunk(const int* cb, int nseq, int g) {
+  int lo = 0, hi = nseq;   // cb[lo] <= g < cb[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cb[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 // Lower-triangular block pair (i, j), j <= i, of pair index n.
 __host__ __device__ constexpr int pair_i(int n) { int i = 0; while (n > i) { n -= i + 1; ++i; } return i; }
@@ -336,9 +354,18 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   const int T = p.T, H = p.H;
   const int ch = blockIdx.x % p.nchunks, head = blockIdx.x / p.nchunks;
   const int b = head / H, h = head % H;
-  const int t0 = (p.c0 + ch) * C;
-  const int Lc = min(C, T - t0);
-  const long tok0 = static_cast<long>(b) * T + t0;   // first token of the chunk
+  int Lc;                 // tokens in the chunk
+  long tok0;              // first token of the chunk
+  if (p.cu) {
+    const int n = seq_of_chunk(p.cb, p.nseq, ch);
+    const int t0 = p.cu[n] + (ch - p.cb[n]) * C;
+    Lc = min(C, p.cu[n + 1] - t0);
+    tok0 = t0;
+  } else {
+    const int t0 = (p.c0 + ch) * C;
+    Lc = min(C, T - t0);
+    tok0 = static_cast<long>(b) * T + t0;
+  }
   // the chunk's record image; the workspace holds its bytes from R::gOff on
   unsigned char* rec = reinterpret_cast<unsigned char*>(
       reinterpret_cast<uintptr_t>(p.ws) + (static_cast<size_t>(head) * p.nchunks + ch) * R::gBytes - R::gOff);
@@ -941,15 +968,26 @@ void state_kernel(StateParams p) {
       slice = id % p.nsl;
     }
   }
-  const int b = head / H, h = head % H;
+  const int b = head / H, h = head % H;   // (packed input: b is the sequence)
   const int n0 = slice * DVS;   // first value column of this slice
-  const unsigned char* rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::gBytes;
   const In* gv = static_cast<const In*>(p.v);
   const In* gq = static_cast<const In*>(p.q);
   const In* gk = static_cast<const In*>(p.k);
-  const long seq0 = static_cast<long>(b) * T + static_cast<long>(p.c0) * C;   // first token of this launch
-  const int Trem = T - p.c0 * C;             // tokens from there to the sequence end
-  const int nchunks = p.nchunks;
+  const unsigned char* rec0;                 // the first chunk's record
+  long seq0;                                 // first token of this launch
+  int Trem;                                  // tokens from there to the sequence end
+  int nchunks;
+  if (p.cu) {
+    rec0 = p.ws + (static_cast<size_t>(h) * p.nchunks + p.cb[b]) * R::gBytes;
+    seq0 = p.cu[b];
+    Trem = p.cu[b + 1] - p.cu[b];
+    nchunks = p.cb[b + 1] - p.cb[b];
+  } else {
+    rec0 = p.ws + static_cast<size_t>(head) * p.nchunks * R::gBytes;
+    seq0 = static_cast<long>(b) * T + static_cast<long>(p.c0) * C;
+    Trem = T - p.c0 * C;
+    nchunks = p.nchunks;
+  }
   const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
   const int rowK = H * DK * AB;              // ... of k
   const int rowO = H * DV * 4;               // ... and of o

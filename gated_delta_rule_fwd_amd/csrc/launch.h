@@ -26,6 +26,10 @@ struct FwdArgs {
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t s);
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s);
+// Packed variable-length input: a.B is unused; nseq sequences at the token
+// offsets cu (device) / cu_host (host, the same N + 1 values).
+hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int* cu_host, int nseq,
+                                 hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
 // LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.
 size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind);

@@ -43,6 +43,9 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
                                       i, i, i, i, i, i, f, i, i, vp]
         L.kda_fwd_chunked.restype = i
+        L.kda_fwd_chunked_varlen.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i,
+                                             i, i, i, i, i, f, i, i, vp]
+        L.kda_fwd_chunked_varlen.restype = i
         L.kda_fwd_recurrent.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
                                         i, i, i, i, i, i, f, i, vp]
         L.kda_fwd_recurrent.restype = i
@@ -144,6 +147,37 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
                                int(chunk_size), _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked", st)
+    return o, fs
+
+
+def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None,
+                       softmax_scale=None, use_qk_l2norm=True, chunk_size=64, out=None,
+                       final_state=None):
+    """Chunked forward over N packed sequences (tokens [1, T, ...], sequence n
+    is tokens cu_seqlens[n] .. cu_seqlens[n + 1]).  cu_seqlens: int32, N + 1
+    offsets, on the CPU or the GPU (the other copy is made here).  Returns
+    (o [1,T,H,DV] fp32, final_state [N,H,DK,DV] fp32)."""
+    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, None)
+    if B != 1:
+        raise ValueError("packed sequences need B == 1")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
+    cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+    _check_state("initial_state", initial_state, (N, H, DK, DV), dev)
+    o = out if out is not None else torch.empty((1, T, H, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (1, T, H, DV), dev)
+    fs = final_state if final_state is not None else torch.empty((N, H, DK, DV), device=dev,
+                                                                 dtype=torch.float32)
+    _check_state("final_state", fs, (N, H, DK, DV), dev)
+    st = lib().kda_fwd_chunked_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
+                                      _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(cu_dev),
+                                      _ptr(cu_host), N, T, H, DK, DV, _dtype_code(q),
+                                      _scale(softmax_scale), int(bool(use_qk_l2norm)),
+                                      int(chunk_size), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_fwd_chunked_varlen", st)
     return o, fs
 
 

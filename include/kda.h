@@ -101,6 +101,37 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
                     void* stream);
 
 /*
+ * Chunked forward over packed variable-length sequences (TileOPs
+ * DeltaNetFwdOp / GDNFwdOp / KDAFwdOp: passing cu_seqlens selects the packed
+ * varlen mode, the token tensors have B == 1 and N is the number of packed
+ * sequences).  Same computation as kda_fwd_chunked for each sequence on its
+ * own; chunks never cross a sequence end.
+ *
+ *   q, k           [1, T, H, DK]  the N sequences back to back
+ *   v              [1, T, H, DV]
+ *   beta           [1, T, H]
+ *   decay          NULL | [1, T, H] | [1, T, H, DK] per decay_kind
+ *   cu_seqlens     DEVICE int32 [N + 1]: sequence n is tokens
+ *                  [cu_seqlens[n], cu_seqlens[n + 1])
+ *   cu_seqlens_host HOST int32 [N + 1], the same values (sizes the launch)
+ *   initial_state  NULL (zeros) | [N, H, DK, DV] fp32
+ *   o              [1, T, H, DV] fp32, written
+ *   final_state    [N, H, DK, DV] fp32, written; may alias initial_state
+ *
+ * An empty sequence passes its initial state through.  The workspace holds
+ * the records of all chunks of all sequences at once (no segmentation).
+ * Errors as kda_fwd_chunked, plus: KDA_ERR_NULL if cu_seqlens or
+ * cu_seqlens_host is NULL; KDA_ERR_SHAPE if N < 1, cu_seqlens_host[0] != 0,
+ * cu_seqlens_host[N] != T or the offsets decrease.
+ */
+int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* beta,
+                           const void* decay, int decay_kind, const float* initial_state,
+                           float* o, float* final_state, const int* cu_seqlens,
+                           const int* cu_seqlens_host, int N,
+                           int T, int H, int DK, int DV, int dtype,
+                           float softmax_scale, int use_qk_l2norm, int chunk_size,
+                           void* stream);
+/*
  * Recurrent forward: the pure sequential scan (ejkernel kda, section
  * "Algorithm Modes", Recurrent).  Same arguments and errors as
  * kda_fwd_chunked without chunk_size.  Computes in fp32 throughout.

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 100
+    assert L.kda_abi_version() == 101
     assert L.kda_status_string(0) == b"ok"
     for code in (1, 2, 3, 5):
         assert len(L.kda_status_string(code)) > 3
@@ -77,6 +77,32 @@ def test_recurrent_and_decode_reject_bad_arguments(L):
                              1, 1, 64, 64, 1, 0.0, 1, None) == 1
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
                              0, 1, 64, 64, 1, 0.0, 1, None) == 2
+
+
+def varlen(L, cu, N, T=8, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
+             cud=FAKE, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64)
+    a.update(kw)
+    cuh = None if cu is None else (ctypes.c_int * len(cu))(*cu)
+    return L.kda_fwd_chunked_varlen(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"],
+                                    a["init"], a["o"], a["fs"], a["cud"], cuh, N, T, a["H"],
+                                    a["DK"], a["DV"], a["dtype"], a["scale"], a["l2"], a["chunk"],
+                                    None)
+
+
+@pytest.mark.parametrize("cu,N,T,kw,code", [
+    (None, 2, 8, {}, 1),                       # no host offsets
+    ([0, 4, 8], 2, 8, dict(cud=None), 1),      # no device offsets
+    ([0, 4, 8], 2, 8, dict(fs=None), 1),
+    ([0, 8], 0, 8, {}, 2),                     # N < 1
+    ([1, 4, 8], 2, 8, {}, 2),                  # does not start at 0
+    ([0, 4, 7], 2, 8, {}, 2),                  # does not end at T
+    ([0, 6, 4, 8], 3, 8, {}, 2),               # decreasing
+    ([0, 4, 8], 2, 8, dict(chunk=128), 3),
+    ([0, 4, 8], 2, 8, dict(DK=48), 3),
+])
+def test_varlen_rejects_bad_arguments(L, cu, N, T, kw, code):
+    assert varlen(L, cu, N, T, **kw) == code
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_fwd_amd import decode_step, fwd_chunked, fwd_recurrent
+from gated_delta_rule_fwd_amd import decode_step, fwd_chunked, fwd_chunked_varlen, fwd_recurrent
 from gated_delta_rule_fwd_amd.inputs import WORKLOADS, make_inputs
 from oracle import kda_decode, kda_scan, kda_scan_heads
 
@@ -199,6 +199,58 @@ def test_decode_full_size_sampled_heads():
     o_ref, S_ref = kda_decode(inp["q"][bs], inp["k"][bs], inp["v"][bs], inp["beta"][bs],
                               inp["decay"][bs], inp["initial_state"][bs])
     check("decode sampled", o[bs], state[bs], o_ref, S_ref, TOL[w.dtype])
+
+
+# ------------------------------------------------- packed variable length --
+
+VARLEN_CASES = [
+    # lengths of the packed sequences (empty, shorter than a chunk, exact
+    # chunks, ragged), then the workload's reductions
+    ("gdn_d128", [0, 1, 63, 64, 65, 130, 17, 200], dict(H=4)),
+    ("gdn_d128", [300, 0, 520, 77], dict(H=32)),          # 32-column value slices
+    ("kda_d128", [100, 0, 64, 33], dict(H=2)),
+    ("deltanet_d64", [5, 300, 64], dict(H=4, chunk=32)),
+    ("fp32_small", [10, 70, 0, 33], dict(H=2, DK=64, DV=64, chunk=16)),
+]
+
+
+@pytest.mark.parametrize("name,lens,kw", VARLEN_CASES, ids=lambda x: str(x))
+def test_varlen_matches_oracle_per_sequence(name, lens, kw):
+    T = sum(lens)
+    w = small(name, B=1, T=T, **kw)
+    announce(f"varlen {lens} {w}")
+    inp = make_inputs(w)
+    g = torch.Generator().manual_seed(77)
+    N = len(lens)
+    s0 = 0.1 * torch.randn((N, w.H, w.DK, w.DV), generator=g, dtype=torch.float64).float()
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    d = to_dev(inp)
+    o, S = fwd_chunked_varlen(d["q"], d["k"], d["v"], d["beta"], cu, decay=d["decay"],
+                              initial_state=s0.to(dev()), chunk_size=w.chunk)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((1, T, w.H, w.DV))
+    S_ref = np.zeros((N, w.H, w.DK, w.DV))
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: None if x is None else x[:, a:b]
+        o_n, S_n = kda_scan(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]),
+                            sl(inp["decay"]), s0[n:n + 1])
+        o_ref[:, a:b] = o_n
+        S_ref[n] = S_n[0]
+    check("varlen", o, S, o_ref, S_ref, TOL[w.dtype])
+
+
+def test_varlen_equal_lengths_match_batched_bitwise():
+    w = small("gdn_d128", B=3, T=150, H=4, init_state=True)
+    announce(f"varlen vs batched {w}")
+    d = to_dev(make_inputs(w))
+    o, S = fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
+    pack = lambda x: x.reshape((1, w.B * w.T) + tuple(x.shape[2:])).contiguous()
+    cu = torch.arange(0, w.B * w.T + 1, w.T, dtype=torch.int32)
+    ov, Sv = fwd_chunked_varlen(pack(d["q"]), pack(d["k"]), pack(d["v"]), pack(d["beta"]), cu,
+                                decay=pack(d["decay"]), initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(ov.reshape(o.shape), o) and torch.equal(Sv, S)
 
 
 # ------------------------------------------------------------- properties --

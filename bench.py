@@ -122,6 +122,52 @@ def time_chunked(w, steps, warmup, dev):
     return wall / steps * 1e3, sum(kern_ms) / len(kern_ms), min(kern_ms)
 
 
+VARLEN_SEQS = 16
+
+
+def varlen_lengths(total, n, seed=2024):
+    """n sequence lengths summing to total, from a seeded gamma(2) mix (a
+    spread of short and long prompts, none empty)."""
+    import numpy as np
+    x = np.random.default_rng(seed).gamma(2.0, size=n)
+    lens = np.maximum(1, np.floor(x / x.sum() * total)).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    return [int(v) for v in lens]
+
+
+def time_chunked_varlen(w, steps, warmup, dev):
+    """The workload's B*T tokens per head packed as VARLEN_SEQS sequences of
+    mixed lengths (one launch pair over all of them), a state per sequence."""
+    import torch
+    from gated_delta_rule_fwd_amd import fwd_chunked_varlen
+    from gated_delta_rule_fwd_amd.inputs import make_inputs
+    d = to_dev(make_inputs(w), dev)
+    tot = w.B * w.T
+    pack = lambda x: None if x is None else x.reshape((1, tot) + tuple(x.shape[2:])).contiguous()
+    q, k, v, be, de = (pack(d[n]) for n in ("q", "k", "v", "beta", "decay"))
+    lens = varlen_lengths(tot, VARLEN_SEQS)
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0).tolist()), dtype=torch.int32)
+    g = torch.Generator().manual_seed(7)
+    s0 = (0.1 * torch.randn((VARLEN_SEQS, w.H, w.DK, w.DV), generator=g)).to(dev)
+    o = torch.empty((1, tot, w.H, w.DV), device=dev, dtype=torch.float32)
+    fs = torch.empty((VARLEN_SEQS, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
+    cu_dev = cu.to(dev)
+    call = lambda: fwd_chunked_varlen(q, k, v, be, cu_dev, decay=de, initial_state=s0,
+                                      chunk_size=w.chunk, out=o, final_state=fs)
+    warm_up(call, warmup)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for s, e in evs:
+        s.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    kern_ms = [s.elapsed_time(e) for s, e in evs]
+    state = VARLEN_SEQS * w.H * w.DK * w.DV * 4
+    byts = chunked_bytes(w) - w.B * w.H * w.DK * w.DV * 4 * (2 if w.init_state else 1) + 2 * state
+    return sum(kern_ms) / len(kern_ms), byts, lens
+
+
 def time_decode(w, steps, warmup, dev):
     import torch
     from gated_delta_rule_fwd_amd import decode_step
@@ -316,6 +362,12 @@ def main():
                               "kernel_ms_mean": round(k4, 4),
                               "hbm_frac": round(chunked_bytes(w4) / (k4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "mfma_frac_dense_count": round(chunked_flops(w4) / (k4 * 1e-3) / MFMA_PEAK_F16, 4)}
+        # the same tokens as packed sequences of mixed lengths
+        vk, vb, lens = time_chunked_varlen(w, max(3, args.steps // 2), args.warmup, dev)
+        extra[w.name + "_varlen"] = {
+            "sequences": VARLEN_SEQS, "tokens": w.B * w.T, "min_len": min(lens), "max_len": max(lens),
+            "tokens_per_s": round(w.B * w.T / (vk * 1e-3), 1), "kernel_ms_mean": round(vk, 4),
+            "hbm_frac": round(vb / (vk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         w5 = WORKLOADS["decode_d128"]
         d_ms = time_decode(w5, max(5, args.steps), args.warmup, dev)
         gbs = decode_bytes(w5) / (d_ms * 1e-3) / 1e9

@@ -6,9 +6,12 @@ binding never import it, and it imports nothing from them.
 
 * ``scan.kda_scan`` -- the oracle: the sequential recurrence, token by token.
 * ``scan.kda_decode`` -- the single-step mode (the scan with T = 1).
+* ``transforms.kda_decay`` / ``transforms.beta_transform`` -- the optional
+  raw-gate and raw-beta input transforms, in fp64.
 * ``chunked_ref.kda_chunked_ref`` -- the chunked WY form, kept only to pin the
   chunk algebra against the scan on the CPU; it is not used as a reference for
   the GPU path.
 """
 from .scan import kda_scan, kda_decode, kda_scan_heads, resolve_scale, l2_normalize  # noqa: F401
 from .chunked_ref import kda_chunked_ref  # noqa: F401
+from .transforms import beta_transform, kda_decay, softplus  # noqa: F401

@@ -40,10 +40,32 @@ int check_common(const void* q, const void* k, const void* v, const void* beta, 
   return KDA_OK;
 }
 
+int check_transforms(int decay_kind, int T, const float* A_log, float lower_bound, int tf) {
+  if (tf & ~(KDA_TF_GATE | KDA_TF_LOWER_BOUND | KDA_TF_BETA_SIGMOID | KDA_TF_NEG_EIGVAL))
+    return KDA_ERR_VALUE;
+  if ((tf & KDA_TF_GATE) && decay_kind == KDA_DECAY_NONE) return KDA_ERR_VALUE;
+  if ((tf & KDA_TF_LOWER_BOUND) && (!(tf & KDA_TF_GATE) || !(lower_bound <= 0.f)))
+    return KDA_ERR_VALUE;
+  if ((tf & KDA_TF_NEG_EIGVAL) && !(tf & KDA_TF_BETA_SIGMOID)) return KDA_ERR_VALUE;
+  if (T != 0 && (tf & KDA_TF_GATE) && !A_log) return KDA_ERR_NULL;
+  return KDA_OK;
+}
+
+Transforms make_tf(const float* A_log, const float* dt_bias, float lower_bound, int tf) {
+  Transforms t;
+  const bool gate = (tf & KDA_TF_GATE) != 0;
+  t.A_log = gate ? A_log : nullptr;
+  t.dt_bias = gate ? dt_bias : nullptr;
+  t.lower = (tf & KDA_TF_LOWER_BOUND) ? lower_bound : -INFINITY;
+  t.beta_mode = !(tf & KDA_TF_BETA_SIGMOID) ? 0 : (tf & KDA_TF_NEG_EIGVAL) ? 2 : 1;
+  return t;
+}
+
 FwdArgs make_args(const void* q, const void* k, const void* v, const void* beta, const void* decay,
                   int decay_kind, const float* init, float* o, float* state, int B, int T, int H,
-                  int DK, int DV, int dtype, float scale, int l2, int chunk) {
+                  int DK, int DV, int dtype, float scale, int l2, int chunk, const Transforms& tf) {
   FwdArgs a;
+  a.tf = tf;
   a.q = q; a.k = k; a.v = v; a.beta = beta;
   a.decay = decay_kind == KDA_DECAY_NONE ? nullptr : decay;
   a.decay_kind = decay_kind;
@@ -75,8 +97,11 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
                     const void* decay, int decay_kind, const float* initial_state,
                     float* o, float* final_state,
                     int B, int T, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm, int chunk_size, void* stream) {
+                    float softmax_scale, int use_qk_l2norm, int chunk_size,
+                    const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+                    void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
@@ -88,7 +113,8 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
                                         final_state, B, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, chunk_size);
+                                        use_qk_l2norm, chunk_size,
+                                        kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_chunked(a, s));
 }
 
@@ -97,8 +123,11 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            float* o, float* final_state, const int* cu_seqlens,
                            const int* cu_seqlens_host, int N,
                            int T, int H, int DK, int DV, int dtype,
-                           float softmax_scale, int use_qk_l2norm, int chunk_size, void* stream) {
+                           float softmax_scale, int use_qk_l2norm, int chunk_size,
+                    const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+                    void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, 1, T, H, DK, DV, dtype);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || !cu_seqlens || !cu_seqlens_host || (T != 0 && !o)) return KDA_ERR_NULL;
   if (N < 1 || static_cast<long long>(N) * H * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
@@ -114,7 +143,8 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
                                         final_state, 1, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, chunk_size);
+                                        use_qk_l2norm, chunk_size,
+                                        kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, s));
 }
 
@@ -122,8 +152,11 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* b
                       const void* decay, int decay_kind, const float* initial_state,
                       float* o, float* final_state,
                       int B, int T, int H, int DK, int DV, int dtype,
-                      float softmax_scale, int use_qk_l2norm, void* stream) {
+                      float softmax_scale, int use_qk_l2norm,
+                    const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+                    void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -133,20 +166,25 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* b
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
                                         final_state, B, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, 0);
+                                        use_qk_l2norm, 0,
+                                        kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_recurrent(a, s));
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, float* state, float* o,
                     int B, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm, void* stream) {
+                    float softmax_scale, int use_qk_l2norm,
+                    const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+                    void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, 1, H, DK, DV, dtype);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, 1, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!state || !o) return KDA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, state, o, state, B, 1, H,
-                                        DK, DV, dtype, softmax_scale, use_qk_l2norm, 0);
+                                        DK, DV, dtype, softmax_scale, use_qk_l2norm, 0,
+                                        kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_decode(a, s));
 }
 
@@ -156,11 +194,12 @@ const char* kda_status_string(int status) {
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
     case KDA_ERR_UNSUPPORTED: return "unsupported head size, chunk size, dtype or decay kind";
+    case KDA_ERR_VALUE: return "invalid transform flags or lower bound";
     case KDA_ERR_HIP: return "HIP runtime error at launch";
   }
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 101; }
+int kda_abi_version(void) { return 102; }
 
 }  // extern "C"

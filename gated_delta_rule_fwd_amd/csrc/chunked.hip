@@ -105,6 +105,7 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
   pp.ws = static_cast<unsigned char*>(ws);
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
+  pp.tf = a.tf;
 
   StateParams sp;
   sp.cu = nullptr; sp.cb = nullptr;
@@ -185,6 +186,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
   pp.q = a.q; pp.k = a.k; pp.beta = a.beta; pp.decay = a.decay;
   pp.ws = static_cast<unsigned char*>(ws);
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
+  pp.tf = a.tf;
   pp.c0 = 0; pp.nchunks = static_cast<int>(total);
 
   StateParams sp;

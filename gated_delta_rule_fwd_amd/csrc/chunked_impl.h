@@ -206,6 +206,7 @@ struct PrepParams {
   int c0;                // first chunk of this launch (records are indexed from it)
   float scale;
   const int* cu; const int* cb; int nseq;   // packed input
+  Transforms tf;         // raw gate / raw beta (applied where decay and beta are read)
 };
 
 struct StateParams {
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   int* s_flag = reinterpret_cast<int*>(s_misc + 1);
   float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
   float* s_Cb = s_tau + NB * DK;               // [NB][DK] decay of all earlier blocks
-  float* s_rsq = s_Cb + NB * DK;               // [NB][DK] 1/sqrt(block factor)
+  float* s_rsq = s_Cb + NB * DK;               // [NB][DK] rs: exp(block log decay / 2)
   float* s_D = s_rsq + NB * DK;                // [ND][DK] decay strictly between blocks
 
   const In* gq = static_cast<const In*>(p.q);
@@ -409,11 +410,17 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         if (chan) rg[pp] = *reinterpret_cast<const uint4*>(gg + off);
       }
     }
+    // raw gate: -exp(A_log) of the head; tokens past the sequence end keep a
+    // zero decay (the chunk-end sums run over all C rows)
+    const float negA = p.tf.A_log ? -__expf(p.tf.A_log[h]) : 0.f;
     float bt = 0.f, G = 0.f;
     if (wave == 0 && lane < Lc) {
       const long off = (tok0 + lane) * H + h;
-      bt = act<In>::load1(gb + off);
-      if (headdecay) G = act<In>::load1(gg + off);
+      bt = beta_transform(act<In>::load1(gb + off), p.tf.beta_mode);
+      if (headdecay) {
+        G = act<In>::load1(gg + off);
+        if (p.tf.A_log) G = gate_decay(G, negA, p.tf.dt_bias ? p.tf.dt_bias[h] : 0.f, p.tf.lower);
+      }
     }
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
@@ -455,6 +462,12 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         } else {
           float gv[V];
           act<In>::load_vec(reinterpret_cast<const In*>(&rg[pp]), gv);
+          if (p.tf.A_log && r < Lc) {
+            const float* bias = p.tf.dt_bias;
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+              gv[e] = gate_decay(gv[e], negA, bias ? bias[h * DK + seg * V + e] : 0.f, p.tf.lower);
+          }
           store16<OpT>(sGst + r * DK + seg * V, gv);
         }
       }
@@ -520,6 +533,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     // all of them are <= 1.  The decay-to-block-end operand of the
     // off-diagonal Gram blocks is the inverse-prefix one times the block
     // factor, folded into their A-operand scale (D below).
+    // fp16 operands (not steep) are balanced: the prefix products are stored
+    // divided by rs = exp(block log decay / 2) and the inverse-prefix ones
+    // multiplied by it, so both lie within exp(+-8) of the normalised rows
+    // and neither underflows fp16 late in a strongly decaying block.
     constexpr int NT = (NB * DK + kPrepThreads - 1) / kPrepThreads;
     float kbr[NT][16];       // k decayed to the block end (for the record's F)
 #pragma unroll
@@ -529,6 +546,15 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         const int i = task / DK, c = task % DK;
         float a[16], kx[16], kin[16];
         float pre = 1.f;
+        const bool bal = sizeof(OpT) == 2 && !steep;
+        float rs = 1.f;
+        if (bal) {
+          float tot = 0.f;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) tot += static_cast<float>(sGst[(16 * i + t) * DK + c]);
+          rs = __expf(0.5f * tot);
+        }
+        const float irs = 1.f / rs;
         // Ka (k times the exclusive prefix) and Qa (q times the inclusive
         // one) replace k and q in place: fp16, or bf16 bit patterns when steep
         auto put = [&](OpT* tile, int r, float x) {
@@ -543,10 +569,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
           kx[t] = static_cast<float>(sK[r * L::LDK + c]);
           const float qx = static_cast<float>(sQ[r * L::LDK + c]);
-          put(sK, r, kx[t] * pre);
+          put(sK, r, kx[t] * pre * irs);
           pre *= a[t];
           kin[t] = kx[t] / pre;                             // k / inclusive prefix
-          put(sQ, r, qx * pre);
+          put(sQ, r, qx * pre * irs);
         }
         float suf = 1.f;
 #pragma unroll
@@ -558,10 +584,9 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         if constexpr (sizeof(OpT) == 2) {
           if (!steep) {
             // diagonal blocks pair a factor <= 1 with its inverse; balanced by
-            // sqrt(block factor) both stay within exp(+-8) for a block factor
-            // >= exp(-16), which fp16 holds
-            const float rs = sqrtf(pre);
-            s_rsq[i * DK + c] = 1.f / rs;
+            // rs both stay within exp(+-8) for a block factor >= exp(-16),
+            // which fp16 holds
+            s_rsq[i * DK + c] = rs;
 #pragma unroll
             for (int t = 0; t < 16; ++t)
               *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
@@ -590,18 +615,21 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           if (j < i) cb *= tj;
           if (j > i) ca *= tj;
         }
-        s_Cb[i * DK + c] = cb;
-        if (i == 0) rvec[R::vDecC + c] = ca * tau;
-        // D[i][j] = prod_{j < m < i} tau_m * f(tau_j): the stored inverse-prefix
-        // operand of block j times f(tau_j) is k decayed to the end of block j
-        // (f = sqrt for the balanced fp16 operand, identity otherwise)
+        // balanced fp16 operands: block i's prefix products carry 1 / rs_i,
+        // block j's inverse-prefix ones rs_j (restored below)
         const bool bal = sizeof(OpT) == 2 && !steep;
+        const float rsi = bal ? s_rsq[i * DK + c] : 1.f;
+        s_Cb[i * DK + c] = cb * rsi;
+        if (i == 0) rvec[R::vDecC + c] = ca * tau;
+        // D[i][j] = rs_i prod_{j < m < i} tau_m * tau_j / rs_j: the stored
+        // inverse-prefix operand of block j times tau_j / rs_j is k decayed to
+        // the end of block j
         float dd = 1.f;
 #pragma unroll
         for (int j = NB - 1; j >= 0; --j) {
           if (j < i) {
             const float tj = s_tau[j * DK + c];
-            s_D[L::dslot(i, j) * DK + c] = dd * (bal ? sqrtf(tj) : tj);
+            s_D[L::dslot(i, j) * DK + c] = rsi * dd * (bal ? tj / s_rsq[j * DK + c] : tj);
             dd *= tj;
           }
         }
@@ -636,11 +664,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         if (*s_flag == 0) {
           const OpT* krh = reinterpret_cast<const OpT*>(krow);
 #pragma unroll
-          for (int m = 0; m < NKP; ++m) {
-            auto fa = M::ld_cont(arow, 32 * m, g);
-            M::scale_cont(fa, s_rsq + i * DK, 32 * m, g);
-            M::mma(acc, M::ld_cont(krh, 32 * m, g), fa);
-          }
+          for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(krh, 32 * m, g), M::ld_cont(arow, 32 * m, g));
         } else {
           const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
 #pragma unroll

@@ -102,6 +102,33 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Optional input transforms (TileOPs "Linear Attention Operators", GDNFwdOp
+// and KDAFwdOp parameter lists).  With a raw gate the log-space decay is
+// -exp(A_log) * softplus(gate + dt_bias) (ejkernel kda_decay, the Mamba-style
+// discretisation), floored at `lower`; with raw beta the update strength is
+// sigmoid(beta), or twice it when negative eigenvalues are allowed.
+struct Transforms {
+  const float* A_log;     // [H]; non-NULL: the decay input holds the raw gate
+  const float* dt_bias;   // [H] (per-head gate) or [H, DK] (per-channel); NULL = 0
+  float lower;            // log-space floor of the decay (-inf: none)
+  int beta_mode;          // 0 beta as given, 1 sigmoid, 2 twice the sigmoid
+};
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|): no overflow, and an
+// absolute error of a few fp32 ulps of 1 (what the decay sums need).
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));
+}
+// negA = -exp(A_log[h]) of the head
+__device__ __forceinline__ float gate_decay(float gate, float negA, float bias, float lower) {
+  return fmaxf(negA * softplus_f(gate + bias), lower);
+}
+__device__ __forceinline__ float beta_transform(float b, int mode) {
+  if (mode == 0) return b;
+  const float s = 1.f / (1.f + __expf(-b));
+  return mode == 2 ? 2.f * s : s;
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) {
   // 1 / max(||x||_2, 1e-12): the hardware reciprocal square root (about
   // 1 ulp), capped where the norm is below 1e-12 (a NaN sum gives the cap)

@@ -27,7 +27,8 @@ template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
-    float* __restrict__ state, float* __restrict__ o, float scale, int l2norm) {
+    float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
+    Transforms tf) {
   constexpr int CS = decode_cols<DV>();
   constexpr int NSPLIT = DV / CS;
   constexpr int NC4 = CS / 4;             // float4 column groups per state row
@@ -45,6 +46,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int n0 = (blockIdx.x % NSPLIT) * CS;   // first value column of this workgroup
   const int cg = tid % NC4, rg = tid / NC4;
   float* S = state + bh * DK * DV + n0;
+  const int h = static_cast<int>(bh % H);
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
 
   // Issue the state loads first: they are the bulk of the traffic.
   f32x4 st[RPT];
@@ -62,7 +65,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     s_q[c] = qc;
     s_k[c] = kc;
     float gc = 1.f;
-    if (decay_kind == DECAY_CHANNEL) gc = __expf(act<In>::load1(decay + bh * DK + c));
+    if (decay_kind == DECAY_CHANNEL) {
+      float g = act<In>::load1(decay + bh * DK + c);
+      if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h * DK + c] : 0.f, tf.lower);
+      gc = __expf(g);
+    }
     s_gate[c] = gc;
     pq += qc * qc; pk += kc * kc; pqk += qc * kc;
   }
@@ -76,9 +83,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const float iq = (l2norm ? inv_norm(sq) : 1.f) * scale;   // q_hat = q * iq
   const float ik = l2norm ? inv_norm(sk) : 1.f;             // k_hat = k * ik
   const float qk = sqk * iq * ik;                           // q_hat . k_hat
-  const float b = act<In>::load1(beta + bh);
+  const float b = beta_transform(act<In>::load1(beta + bh), tf.beta_mode);
   float ghead = 1.f;
-  if (decay_kind == DECAY_HEAD) ghead = __expf(act<In>::load1(decay + bh));
+  if (decay_kind == DECAY_HEAD) {
+    float g = act<In>::load1(decay + bh);
+    if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h] : 0.f, tf.lower);
+    ghead = __expf(g);
+  }
 
   // Partial reads r = S^T k_hat and y = S^T (gate * q_hat) over this thread's rows.
   f32x4 r = {0, 0, 0, 0}, y = {0, 0, 0, 0};
@@ -135,7 +146,7 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   if (a.DK == dk && a.DV == dv) {                                                            \
     const dim3 grid(a.B * a.H * (dv / decode_cols<dv>()));                                   \
     decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.state, \
-                                                      a.o, a.scale, a.l2norm);              \
+                                                      a.o, a.scale, a.l2norm, a.H, a.tf);  \
     return hipGetLastError();                                                                \
   }
   KDA_DECODE_CASE(32, 32) KDA_DECODE_CASE(32, 64) KDA_DECODE_CASE(32, 128)

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.h"
+
 namespace kda {
 
 struct FwdArgs {
@@ -20,6 +22,7 @@ struct FwdArgs {
   float scale;         // already resolved (> 0)
   int l2norm;
   int chunk;
+  Transforms tf;       // raw gate / raw beta handling (all off: inputs as given)
 };
 
 // Each launcher assumes the front end has validated the arguments.

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     const float* __restrict__ init, float* __restrict__ o, float* __restrict__ state_out,
-    int T, int H, float scale, int l2norm) {
+    int T, int H, float scale, int l2norm, Transforms tf) {
   constexpr int CPW = DV / 4;           // value columns per wave
   constexpr int NCG = CPW / 4;          // float4 column groups per wave
   constexpr int NRG = 64 / NCG;         // row groups per wave
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
   const int col = wave * CPW + 4 * cg;          // first of this lane's 4 columns
   const int row0 = rg * RPL;                    // this lane's state rows row0 .. row0+RPL-1
   const long bh = static_cast<long>(b) * H + h;
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
 
   f32x4 S[RPL];
 #pragma unroll
@@ -79,8 +80,15 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
       }
       if (decay_kind == DECAY_CHANNEL) {
         float gv[V];
-        if (live) act<In>::load_vec(decay + base, gv);
-        else {
+        if (live) {
+          act<In>::load_vec(decay + base, gv);
+          if (tf.A_log) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+              gv[e] = gate_decay(gv[e], negA, tf.dt_bias ? tf.dt_bias[h * DK + seg * V + e] : 0.f,
+                                 tf.lower);
+          }
+        } else {
 #pragma unroll
           for (int e = 0; e < V; ++e) gv[e] = 0.f;
         }
@@ -96,8 +104,13 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     if (tid < kTB) {
       const bool live = tid < nt;
       const long tok = (static_cast<long>(b) * T + t0 + tid) * H + h;
-      s_b[tid] = live ? act<In>::load1(beta + tok) : 0.f;
-      s_gh[tid] = (decay_kind == DECAY_HEAD && live) ? __expf(act<In>::load1(decay + tok)) : 1.f;
+      s_b[tid] = live ? beta_transform(act<In>::load1(beta + tok), tf.beta_mode) : 0.f;
+      float gh = 0.f;
+      if (decay_kind == DECAY_HEAD && live) {
+        gh = act<In>::load1(decay + tok);
+        if (tf.A_log) gh = gate_decay(gh, negA, tf.dt_bias ? tf.dt_bias[h] : 0.f, tf.lower);
+      }
+      s_gh[tid] = __expf(gh);
     }
     __syncthreads();
 
@@ -152,7 +165,7 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   if (a.DK == dk && a.DV == dv) {                                                         \
     recurrent_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,    \
                                                         a.init, a.o, a.state, a.T, a.H,   \
-                                                        a.scale, a.l2norm);               \
+                                                        a.scale, a.l2norm, a.tf);         \
     return hipGetLastError();                                                             \
   }
   KDA_REC_CASE(32, 32) KDA_REC_CASE(32, 64) KDA_REC_CASE(32, 128)

@@ -21,6 +21,11 @@ Workloads (the value distributions of the five standard cases):
 
 q, k, v are N(0,1) and are passed raw with ``use_qk_l2norm`` on; beta is
 sigmoid(N(0,1)).
+
+``make_transform_inputs`` draws the raw inputs of the in-kernel transforms
+instead: a raw gate N(0,1) in the decay's shape, A_log 0.3 N(0,1) per head
+(near zero), dt_bias U(-2, 0) per head (or per head and key channel) and beta
+logits N(0,1).
 """
 
 from __future__ import annotations
@@ -43,7 +48,8 @@ class Workload:
     DK: int
     DV: int
     chunk: int            # 0 for decode
-    decay: str            # "none" | "head_small" | "head_logsig" | "channel_softplus" | "channel_steep"
+    decay: str            # "none" | "head_small" | "head_logsig" | "channel_softplus"
+                          # | "channel_strong" | "channel_steep"
     init_state: bool
     decode: bool = False
     seed: int = 1000
@@ -51,6 +57,7 @@ class Workload:
     @property
     def decay_kind(self) -> int:
         return {"none": DECAY_NONE, "channel_softplus": DECAY_CHANNEL,
+                "channel_strong": DECAY_CHANNEL,
                 "channel_steep": DECAY_CHANNEL}.get(self.decay, DECAY_HEAD)
 
     def scaled(self, **kw) -> "Workload":
@@ -105,6 +112,10 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         decay = act(-_softplus(-(2.0 + normal(lead))))
     elif w.decay == "channel_softplus":
         decay = act(-_softplus(-3.0 + normal(lead + (w.DK,))))
+    elif w.decay == "channel_strong":
+        # a 16-token block decays by exp(-6) to exp(-14) in most channels:
+        # strong, but short of the steep threshold exp(-16)
+        decay = act(-_softplus(-1.0 + normal(lead + (w.DK,))))
     elif w.decay == "channel_steep":
         # strong per-channel decay: a 16-token block decays by about exp(-20)
         # (steeper than exp(-16) in most channels), still far from fp32 underflow
@@ -115,3 +126,28 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     if w.init_state:
         init = torch.from_numpy(0.1 * normal((w.B, w.H, w.DK, w.DV)))
     return dict(q=q, k=k, v=v, beta=beta, decay=decay, initial_state=init)
+
+
+def make_transform_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Inputs for the raw-gate / raw-beta transforms of workload ``w``.
+
+    Everything ``make_inputs(w, seed)`` returns, and from a second stream gate (None, [lead] or [lead, DK] as w's decay kind, in
+    the activation dtype), beta_logits [lead] (activation dtype), A_log [H]
+    and dt_bias [H] or [H, DK] (fp32).
+    """
+    base = make_inputs(w, seed)
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    dt = torch_dtype(w.dtype)
+    lead = (w.B, w.H) if w.decode else (w.B, w.T, w.H)
+
+    def act(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dt)
+
+    kind = w.decay_kind
+    gshape = lead + ((w.DK,) if kind == DECAY_CHANNEL else ())
+    bshape = (w.H, w.DK) if kind == DECAY_CHANNEL else (w.H,)
+    gate = act(rng.standard_normal(gshape, dtype=np.float32)) if kind != DECAY_NONE else None
+    beta_logits = act(rng.standard_normal(lead, dtype=np.float32))
+    A_log = torch.from_numpy(0.3 * rng.standard_normal((w.H,), dtype=np.float32))
+    dt_bias = torch.from_numpy(rng.uniform(-2.0, 0.0, bshape).astype(np.float32))
+    return dict(base, gate=gate, beta_logits=beta_logits, A_log=A_log, dt_bias=dt_bias)

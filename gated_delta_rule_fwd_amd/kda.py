@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 DECAY_NONE, DECAY_HEAD, DECAY_CHANNEL = 0, 1, 2
-STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_HIP"}
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+          4: "KDA_ERR_VALUE", 5: "KDA_ERR_HIP"}
+TF_GATE, TF_LOWER_BOUND, TF_BETA_SIGMOID, TF_NEG_EIGVAL = 1, 2, 4, 8
 
 _lib = None
 
@@ -41,16 +43,16 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
-                                      i, i, i, i, i, i, f, i, i, vp]
+                                      i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_fwd_chunked.restype = i
         L.kda_fwd_chunked_varlen.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i,
-                                             i, i, i, i, i, f, i, i, vp]
+                                             i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_fwd_chunked_varlen.restype = i
         L.kda_fwd_recurrent.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
-                                        i, i, i, i, i, i, f, i, vp]
+                                        i, i, i, i, i, i, f, i, vp, vp, f, i, vp]
         L.kda_fwd_recurrent.restype = i
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, i, vp, vp,
-                                      i, i, i, i, i, f, i, vp]
+                                      i, i, i, i, i, f, i, vp, vp, f, i, vp]
         L.kda_decode_step.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
@@ -113,6 +115,29 @@ def _decay_kind(decay, lead, dk):
                      f"{tuple(lead) + (dk,)}")
 
 
+def _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                use_beta_sigmoid_in_kernel, allow_neg_eigval):
+    """(A_log, dt_bias, lower_bound, flags) for the C entry points.  The
+    flag combinations are checked by the library (KDA_ERR_VALUE)."""
+    flags = 0
+    if use_gate_in_kernel:
+        flags |= TF_GATE
+        _check_state("A_log", A_log, (H,), dev)
+        if A_log is None:
+            raise ValueError("use_gate_in_kernel needs A_log [H]")
+        _check_state("dt_bias", dt_bias, (H, DK) if kind == DECAY_CHANNEL else (H,), dev)
+    else:
+        A_log = dt_bias = None
+    if lower_bound is not None:
+        flags |= TF_LOWER_BOUND
+    if use_beta_sigmoid_in_kernel:
+        flags |= TF_BETA_SIGMOID
+    if allow_neg_eigval:
+        flags |= TF_NEG_EIGVAL
+    lb = 0.0 if lower_bound is None else float(lower_bound)
+    return _ptr(A_log), _ptr(dt_bias), lb, flags
+
+
 def _prep_fwd(q, k, v, beta, decay, initial_state):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, DK]")
@@ -133,9 +158,20 @@ def _prep_fwd(q, k, v, beta, decay, initial_state):
 
 
 def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
-                use_qk_l2norm=True, chunk_size=64, out=None, final_state=None):
-    """Chunked forward.  Returns (o [B,T,H,DV] fp32, final_state [B,H,DK,DV] fp32)."""
+                use_qk_l2norm=True, chunk_size=64, out=None, final_state=None,
+                use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+    """Chunked forward.  Returns (o [B,T,H,DV] fp32, final_state [B,H,DK,DV] fp32).
+
+    Input transforms (all entry points): with ``use_gate_in_kernel`` the
+    decay tensor holds the raw gate and the kernels use
+    -exp(A_log) * softplus(gate + dt_bias), floored at ``lower_bound`` if
+    given (A_log [H] fp32; dt_bias [H], or [H, DK] for a per-channel gate,
+    fp32 or None); ``use_beta_sigmoid_in_kernel`` reads beta as logits
+    (sigmoid, or 2 * sigmoid with ``allow_neg_eigval``)."""
     B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
+    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
     o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
     _check_state("out", o, (B, T, H, DV), dev)
     fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
@@ -144,7 +180,7 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
     st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
                                _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                               int(chunk_size), _stream(dev))
+                               int(chunk_size), *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked", st)
     return o, fs
@@ -152,12 +188,16 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
 
 def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None,
                        softmax_scale=None, use_qk_l2norm=True, chunk_size=64, out=None,
-                       final_state=None):
+                       final_state=None, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """Chunked forward over N packed sequences (tokens [1, T, ...], sequence n
     is tokens cu_seqlens[n] .. cu_seqlens[n + 1]).  cu_seqlens: int32, N + 1
     offsets, on the CPU or the GPU (the other copy is made here).  Returns
-    (o [1,T,H,DV] fp32, final_state [N,H,DK,DV] fp32)."""
+    (o [1,T,H,DV] fp32, final_state [N,H,DK,DV] fp32).  Transforms as
+    fwd_chunked."""
     B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, None)
+    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
     if B != 1:
         raise ValueError("packed sequences need B == 1")
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
@@ -175,16 +215,19 @@ def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None
                                       _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(cu_dev),
                                       _ptr(cu_host), N, T, H, DK, DV, _dtype_code(q),
                                       _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                                      int(chunk_size), _stream(dev))
+                                      int(chunk_size), *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked_varlen", st)
     return o, fs
 
 
 def fwd_recurrent(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
-                  use_qk_l2norm=True, out=None, final_state=None):
-    """Recurrent (sequential) forward.  Same returns as fwd_chunked."""
+                  use_qk_l2norm=True, out=None, final_state=None, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+    """Recurrent (sequential) forward.  Same returns and transforms as fwd_chunked."""
     B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
+    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
     o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
     _check_state("out", o, (B, T, H, DV), dev)
     fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
@@ -193,15 +236,17 @@ def fwd_recurrent(q, k, v, beta, decay=None, initial_state=None, softmax_scale=N
     st = lib().kda_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                  _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
                                  _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                                 _stream(dev))
+                                 *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_recurrent", st)
     return o, fs
 
 
-def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=True, out=None):
+def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=True, out=None,
+                use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """One decode step for every (batch, head); ``state`` [B,H,DK,DV] fp32 is
-    updated in place.  Returns o [B,H,DV] fp32."""
+    updated in place.  Returns o [B,H,DV] fp32.  Transforms as fwd_chunked."""
     if q.dim() != 3:
         raise ValueError("q must be [B, H, DK]")
     B, H, DK = q.shape
@@ -221,9 +266,12 @@ def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=T
     _check_state("state", state, (B, H, DK, DV), dev)
     o = out if out is not None else torch.empty((B, H, DV), device=dev, dtype=torch.float32)
     _check_state("out", o, (B, H, DV), dev)
+    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
     st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                _ptr(state), _ptr(o), B, H, DK, DV, _dtype_code(q),
-                               _scale(softmax_scale), int(bool(use_qk_l2norm)), _stream(dev))
+                               _scale(softmax_scale), int(bool(use_qk_l2norm)), *tf,
+                               _stream(dev))
     if st != 0:
         raise KdaError("kda_decode_step", st)
     return o

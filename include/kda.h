@@ -14,7 +14,8 @@
  * is either absent, one value per (token, head) (the scalar gate of TileOPs
  * GDNFwdOp), or one value per (token, head, key channel) (the per-key-channel
  * gate of TileOPs KDAFwdOp, which scales the state rows).  beta is used as
- * given (TileOPs DeltaNetFwdOp: already transformed).
+ * given (TileOPs DeltaNetFwdOp: already transformed) unless the transform
+ * flags below ask for the raw-gate / raw-beta inputs of GDNFwdOp and KDAFwdOp.
  *
  * Conventions common to every entry point:
  *
@@ -26,9 +27,9 @@
  *    Outputs o are fp32; states are fp32 (TileOPs DeltaNetFwdOp: the
  *    recurrent state is FP32 and belongs to the caller).
  *  - softmax_scale <= 0 or NaN means the default DK^-0.5 (ejkernel kda:
- *    "If None, uses head_dim^-0.5"; TileOPs GLA ops: non-positive means the
- *    default).  use_qk_l2norm != 0 normalises q and k by max(||x||_2, 1e-12).
- *  - decay must be <= 0 (ejkernel kda parameter list: "should be <= 0"); the
+ *    no scale given means the inverse square root of the head size; TileOPs
+ *    GLA ops: non-positive means the default).  use_qk_l2norm != 0 normalises q and k by max(||x||_2, 1e-12).
+ *  - decay must be <= 0 (ejkernel kda parameter list: the decay is non-positive); the
  *    kernels rely on it to keep decay factors <= 1 and do not check it.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.  The return value reports
@@ -37,6 +38,26 @@
  *    synchronisation.
  *  - Supported sizes: DK, DV in {32, 64, 128}; B, H >= 1; T >= 0 with
  *    B*T*H*max(DK,DV) < 2^31.
+ *  - Input transforms, the trailing (A_log, dt_bias, lower_bound, transforms)
+ *    of every entry point (TileOPs "Linear Attention Operators", GDNFwdOp and
+ *    KDAFwdOp: use_gate_in_kernel, lower_bound, use_beta_sigmoid_in_kernel,
+ *    allow_neg_eigval; the gate formula is ejkernel's kda_decay).
+ *    `transforms` is a bit set of kda_transform; 0 takes decay and beta as
+ *    given, and then A_log, dt_bias and lower_bound are not read.
+ *      KDA_TF_GATE: decay holds the raw gate; the kernels use
+ *        decay = -exp(A_log[h]) * softplus(gate + dt_bias)
+ *        with A_log DEVICE fp32 [H] (required) and dt_bias DEVICE fp32 [H]
+ *        for KDA_DECAY_HEAD or [H, DK] for KDA_DECAY_CHANNEL (NULL = 0).
+ *        The result is <= 0 by construction.
+ *      KDA_TF_LOWER_BOUND (with KDA_TF_GATE): decay = max(decay, lower_bound),
+ *        a floor of the forget gate in log space; lower_bound must be <= 0.
+ *      KDA_TF_BETA_SIGMOID: beta holds logits; beta = sigmoid(beta).
+ *      KDA_TF_NEG_EIGVAL (with KDA_TF_BETA_SIGMOID): beta = 2 sigmoid(beta).
+ *    The transforms are computed in fp32 inside the kernels that read decay
+ *    and beta; no transformed copy is written.  KDA_ERR_VALUE for unknown
+ *    bits, a flag without the one it needs, KDA_TF_GATE with
+ *    KDA_DECAY_NONE, or lower_bound > 0 or NaN; KDA_ERR_NULL for
+ *    KDA_TF_GATE with A_log NULL (T > 0).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -52,10 +73,18 @@ typedef enum {
   KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
   KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
   KDA_ERR_UNSUPPORTED = 3, /* DK/DV/chunk/dtype/decay kind not implemented   */
+  KDA_ERR_VALUE = 4,       /* invalid transform flags or lower bound         */
   KDA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_TF_GATE = 1,          /* decay is the raw gate (needs A_log)          */
+  KDA_TF_LOWER_BOUND = 2,   /* floor the computed decay at lower_bound      */
+  KDA_TF_BETA_SIGMOID = 4,  /* beta is a logit: sigmoid(beta)               */
+  KDA_TF_NEG_EIGVAL = 8     /* with BETA_SIGMOID: 2 sigmoid(beta)           */
+} kda_transform;
 
 typedef enum {
   KDA_DECAY_NONE = 0,    /* decay ignored (may be NULL): no decay             */
@@ -86,6 +115,11 @@ typedef enum {
  * a larger problem arrives (about 50 KB per chunk and head for DK = 128 fp16
  * operands; the first call of a larger size synchronises `stream`).
  *
+ * With KDA_DECAY_CHANNEL the decay of every 16-token block (aligned to the
+ * chunk start) must stay above about -87 in every channel: the prepared
+ * operands hold products of exp(decay) over a block in fp32 range.  With the
+ * raw gate, KDA_TF_LOWER_BOUND at -5 or above guarantees it.
+ *
  * T == 0 copies initial_state (or zeros) to final_state; then q, k, v, beta,
  * decay and o are not read and may be NULL.
  * Errors: KDA_ERR_NULL if final_state is NULL, or (T > 0) q/k/v/beta/o is
@@ -98,7 +132,8 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
                     float* o, float* final_state,
                     int B, int T, int H, int DK, int DV, int dtype,
                     float softmax_scale, int use_qk_l2norm, int chunk_size,
-                    void* stream);
+                    const float* A_log, const float* dt_bias, float lower_bound,
+                    int transforms, void* stream);
 
 /*
  * Chunked forward over packed variable-length sequences (TileOPs
@@ -130,7 +165,8 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            const int* cu_seqlens_host, int N,
                            int T, int H, int DK, int DV, int dtype,
                            float softmax_scale, int use_qk_l2norm, int chunk_size,
-                           void* stream);
+                           const float* A_log, const float* dt_bias, float lower_bound,
+                           int transforms, void* stream);
 /*
  * Recurrent forward: the pure sequential scan (ejkernel kda, section
  * "Algorithm Modes", Recurrent).  Same arguments and errors as
@@ -140,11 +176,13 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* b
                       const void* decay, int decay_kind, const float* initial_state,
                       float* o, float* final_state,
                       int B, int T, int H, int DK, int DV, int dtype,
-                      float softmax_scale, int use_qk_l2norm, void* stream);
+                      float softmax_scale, int use_qk_l2norm,
+                      const float* A_log, const float* dt_bias, float lower_bound,
+                      int transforms, void* stream);
 
 /*
- * Single-step decode (ejkernel kda, "Single-step: optimized path when
- * seq_len=1 with initial_state"; the closed form of TileOPs
+ * Single-step decode (ejkernel kda, the single-step mode for one
+ * token with an initial state; the closed form of TileOPs
  * DeltaNetRecurrentFwdOp extended with the gate): one token for every
  * (batch, head), the state updated IN PLACE.
  *
@@ -158,7 +196,9 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* b
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, float* state, float* o,
                     int B, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm, void* stream);
+                    float softmax_scale, int use_qk_l2norm,
+                    const float* A_log, const float* dt_bias, float lower_bound,
+                    int transforms, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(int status);

@@ -38,9 +38,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 101
+    assert L.kda_abi_version() == 102
     assert L.kda_status_string(0) == b"ok"
-    for code in (1, 2, 3, 5):
+    for code in (1, 2, 3, 4, 5):
         assert len(L.kda_status_string(code)) > 3
     assert L.kda_status_string(99) == b"unknown status"
 
@@ -50,11 +50,13 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 def chunked(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
-             B=1, T=8, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64)
+             B=1, T=8, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64,
+             A=None, dt=None, lb=0.0, tf=0)
     a.update(kw)
     return L.kda_fwd_chunked(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
                              a["o"], a["fs"], a["B"], a["T"], a["H"], a["DK"], a["DV"], a["dtype"],
-                             a["scale"], a["l2"], a["chunk"], None)
+                             a["scale"], a["l2"], a["chunk"], a["A"], a["dt"], a["lb"], a["tf"],
+                             None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -63,6 +65,14 @@ def chunked(L, **kw):
     (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(B=1 << 20, T=1 << 12, H=8), 2),
     (dict(DK=48), 3), (dict(DV=256), 3), (dict(dtype=7), 3), (dict(kind=5), 3),
     (dict(chunk=128), 3), (dict(chunk=8), 3),
+    # input transforms: KDA_TF_GATE 1, LOWER_BOUND 2, BETA_SIGMOID 4, NEG_EIGVAL 8
+    (dict(tf=16), 4),                                            # unknown bit
+    (dict(tf=1, A=FAKE), 4),                                     # raw gate, no decay tensor
+    (dict(tf=2, kind=1, decay=FAKE), 4),                         # floor without the raw gate
+    (dict(tf=3, kind=1, decay=FAKE, A=FAKE, lb=0.5), 4),         # floor above zero
+    (dict(tf=3, kind=2, decay=FAKE, A=FAKE, lb=float("nan")), 4),
+    (dict(tf=8), 4),                                             # 2 sigmoid without sigmoid
+    (dict(tf=1, kind=1, decay=FAKE), 1),                         # raw gate without A_log
 ])
 def test_chunked_rejects_bad_arguments(L, kw, code):
     assert chunked(L, **kw) == code
@@ -70,24 +80,29 @@ def test_chunked_rejects_bad_arguments(L, kw, code):
 
 def test_recurrent_and_decode_reject_bad_arguments(L):
     assert L.kda_fwd_recurrent(None, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
-                               1, 4, 1, 64, 64, 1, 0.0, 1, None) == 1
+                               1, 4, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 1
     assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
-                               1, 4, 1, 96, 64, 1, 0.0, 1, None) == 3
+                               1, 4, 1, 96, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 3
+    assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
+                               1, 4, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 8, None) == 4
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE,
-                             1, 1, 64, 64, 1, 0.0, 1, None) == 1
+                             1, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 1
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
-                             0, 1, 64, 64, 1, 0.0, 1, None) == 2
+                             0, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 2
+    assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
+                             1, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 1, None) == 1
 
 
 def varlen(L, cu, N, T=8, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
-             cud=FAKE, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64)
+             cud=FAKE, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64,
+             A=None, dt=None, lb=0.0, tf=0)
     a.update(kw)
     cuh = None if cu is None else (ctypes.c_int * len(cu))(*cu)
     return L.kda_fwd_chunked_varlen(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"],
                                     a["init"], a["o"], a["fs"], a["cud"], cuh, N, T, a["H"],
                                     a["DK"], a["DV"], a["dtype"], a["scale"], a["l2"], a["chunk"],
-                                    None)
+                                    a["A"], a["dt"], a["lb"], a["tf"], None)
 
 
 @pytest.mark.parametrize("cu,N,T,kw,code", [
@@ -100,6 +115,7 @@ def varlen(L, cu, N, T=8, **kw):
     ([0, 6, 4, 8], 3, 8, {}, 2),               # decreasing
     ([0, 4, 8], 2, 8, dict(chunk=128), 3),
     ([0, 4, 8], 2, 8, dict(DK=48), 3),
+    ([0, 4, 8], 2, 8, dict(tf=12 | 16), 4),
 ])
 def test_varlen_rejects_bad_arguments(L, cu, N, T, kw, code):
     assert varlen(L, cu, N, T, **kw) == code

@@ -99,22 +99,32 @@ def warm_up(call, warmup):
         torch.cuda.synchronize()
 
 
-def time_chunked(w, steps, warmup, dev):
+def time_chunked(w, steps, warmup, dev, raw=False):
+    """raw: the raw gate and raw beta of make_transform_inputs, transformed in
+    the kernels (gate floor -5, beta sigmoid)."""
     import torch
     from gated_delta_rule_fwd_amd import fwd_chunked
-    from gated_delta_rule_fwd_amd.inputs import make_inputs
-    d = to_dev(make_inputs(w), dev)
+    from gated_delta_rule_fwd_amd.inputs import make_inputs, make_transform_inputs
     o = torch.empty((w.B, w.T, w.H, w.DV), device=dev, dtype=torch.float32)
     fs = torch.empty((w.B, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
-    args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
-    warm_up(lambda: fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs), warmup)
+    if raw:
+        d = to_dev(make_transform_inputs(w), dev)
+        args = (d["q"], d["k"], d["v"], d["beta_logits"], d["gate"], d["initial_state"])
+        tkw = dict(use_gate_in_kernel=True, A_log=d["A_log"], dt_bias=d["dt_bias"],
+                   lower_bound=-5.0, use_beta_sigmoid_in_kernel=True)
+    else:
+        d = to_dev(make_inputs(w), dev)
+        args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
+        tkw = {}
+    call = lambda: fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs, **tkw)
+    warm_up(call, warmup)
     # Events on torch's current stream, which is the stream the library launches on.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
     for s, e in evs:
         s.record()
-        fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs)
+        call()
         e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -362,6 +372,11 @@ def main():
                               "kernel_ms_mean": round(k4, 4),
                               "hbm_frac": round(chunked_bytes(w4) / (k4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "mfma_frac_dense_count": round(chunked_flops(w4) / (k4 * 1e-3) / MFMA_PEAK_F16, 4)}
+            # the same shape from the raw gate and raw beta, transformed in the prep kernel
+            _, k4r, _ = time_chunked(w4, max(3, args.steps // 2), args.warmup, dev, raw=True)
+            extra[w4.name + "_raw_gate"] = {
+                "tokens_per_s": round(w4.B * w4.T / (k4r * 1e-3), 1), "kernel_ms_mean": round(k4r, 4),
+                "transforms": "gate -exp(A_log) softplus(gate + dt_bias) floored at -5, beta sigmoid"}
         # the same tokens as packed sequences of mixed lengths
         vk, vb, lens = time_chunked_varlen(w, max(3, args.steps // 2), args.warmup, dev)
         extra[w.name + "_varlen"] = {

@@ -106,16 +106,33 @@ def recurrence_step(S, q_hat, k_hat, v, beta, gate):
     return o, S_new
 
 
+def expand_qk_heads(x, hv):
+    """q or k [B, T, H, DK] -> [B, T, HV, DK] for HV recurrent heads, a
+    multiple of H (TileOPs "Linear Attention Operators", GDNFwdOp and
+    KDAFwdOp: q and k have H heads, v and the state HV).  The page does not
+    say which q/k head a value head reads; the grouped reading is taken:
+    value head hv reads q/k head hv // (HV // H), so consecutive value heads
+    share one."""
+    h = x.shape[2]
+    if hv == h:
+        return x
+    if hv % h:
+        raise ValueError(f"{hv} value heads is not a multiple of {h} q/k heads")
+    return np.repeat(x, hv // h, axis=2)
+
+
 def kda_scan(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
              use_qk_l2norm=True):
     """Sequential fp64 scan of the recurrence over all tokens.
 
-    q, k [B, T, H, DK]; v [B, T, H, DV]; beta [B, T, H];
-    decay None | [B, T, H] | [B, T, H, DK] (log space);
-    initial_state None (zeros) | [B, H, DK, DV].
-    Returns (o [B, T, H, DV], final_state [B, H, DK, DV]) in float64.
+    q, k [B, T, H, DK]; v [B, T, HV, DV] (HV a multiple of H, see
+    expand_qk_heads; HV = H is the plain case); beta [B, T, HV];
+    decay None | [B, T, HV] | [B, T, HV, DK] (log space);
+    initial_state None (zeros) | [B, HV, DK, DV].
+    Returns (o [B, T, HV, DV], final_state [B, HV, DK, DV]) in float64.
     """
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    q, k = expand_qk_heads(q, v.shape[2]), expand_qk_heads(k, v.shape[2])
     decay = _f64(decay)
     B, T, H, DK = q.shape
     DV = v.shape[-1]

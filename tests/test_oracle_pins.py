@@ -127,3 +127,23 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutant):
         if not err < TOL:
             failures.append(pin.__name__)
     assert failures, f"no pin caught {mutant.__name__}"
+
+
+def test_value_heads_share_their_groups_qk_head():
+    # grouped value heads (HV = 2H): value heads 2j and 2j + 1 read q/k head j,
+    # so with the same v, beta, decay and state they give the same output,
+    # while heads of different groups (2j, 2j + 2) do not
+    rng = np.random.default_rng(11)
+    B, T, H, DK, DV = 1, 9, 2, 8, 4
+    q, k = rng.normal(size=(B, T, H, DK)), rng.normal(size=(B, T, H, DK))
+    v1 = rng.normal(size=(B, T, 1, DV))
+    v = np.repeat(v1, 2 * H, axis=2)
+    beta = np.full((B, T, 2 * H), 0.7)
+    decay = np.repeat(-rng.uniform(0.01, 0.3, size=(B, T, 1)), 2 * H, axis=2)
+    o, S = kda_scan(q, k, v, beta, decay)
+    assert np.max(np.abs(o[:, :, 0] - o[:, :, 1])) == 0.0
+    assert np.max(np.abs(o[:, :, 2] - o[:, :, 3])) == 0.0
+    assert np.max(np.abs(o[:, :, 0] - o[:, :, 2])) > 1e-3
+    # and HV = H is the plain scan, head by head
+    o1, _ = kda_scan(q[:, :, 1:2], k[:, :, 1:2], v[:, :, 2:3], beta[:, :, 2:3], decay[:, :, 2:3])
+    assert np.max(np.abs(o1[:, :, 0] - o[:, :, 2])) < 1e-14

@@ -23,18 +23,22 @@ float resolve_scale(float s, int dk) {
   return s;
 }
 
+// H: query/key heads, HV: recurrent (value) heads, a multiple of H
 int check_common(const void* q, const void* k, const void* v, const void* beta, const void* decay,
-                 int decay_kind, int B, int T, int H, int DK, int DV, int dtype) {
+                 int decay_kind, int B, int T, int H, int HV, int DK, int DV, int dtype,
+                 int state_v_first) {
   // with no tokens there is nothing to read: empty tensors may carry NULL
   if (T != 0 && (!q || !k || !v || !beta)) return KDA_ERR_NULL;
   if (decay_kind != KDA_DECAY_NONE && decay_kind != KDA_DECAY_HEAD && decay_kind != KDA_DECAY_CHANNEL)
     return KDA_ERR_UNSUPPORTED;
   if (T != 0 && decay_kind != KDA_DECAY_NONE && !decay) return KDA_ERR_NULL;
-  if (B < 1 || H < 1 || T < 0 || DK < 1 || DV < 1) return KDA_ERR_SHAPE;
-  const long long tokens = static_cast<long long>(B) * T * H;
+  if (B < 1 || H < 1 || HV < 1 || T < 0 || DK < 1 || DV < 1) return KDA_ERR_SHAPE;
+  if (HV % H != 0) return KDA_ERR_SHAPE;
+  if (state_v_first != 0 && state_v_first != 1) return KDA_ERR_VALUE;
+  const long long tokens = static_cast<long long>(B) * T * HV;
   const long long widest = static_cast<long long>(DK > DV ? DK : DV);
   if (tokens * widest >= (1LL << 31)) return KDA_ERR_SHAPE;
-  if (static_cast<long long>(B) * H * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
+  if (static_cast<long long>(B) * HV * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
   if (!dim_ok(DK) || !dim_ok(DV)) return KDA_ERR_UNSUPPORTED;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
@@ -63,14 +67,17 @@ Transforms make_tf(const float* A_log, const float* dt_bias, float lower_bound, 
 
 FwdArgs make_args(const void* q, const void* k, const void* v, const void* beta, const void* decay,
                   int decay_kind, const float* init, float* o, float* state, int B, int T, int H,
-                  int DK, int DV, int dtype, float scale, int l2, int chunk, const Transforms& tf) {
+                  int HV, int DK, int DV, int dtype, float scale, int l2, int vfirst, int chunk,
+                  const Transforms& tf) {
   FwdArgs a;
   a.tf = tf;
+  a.Hk = H;
+  a.vfirst = vfirst;
   a.q = q; a.k = k; a.v = v; a.beta = beta;
   a.decay = decay_kind == KDA_DECAY_NONE ? nullptr : decay;
   a.decay_kind = decay_kind;
   a.init = init; a.o = o; a.state = state;
-  a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.dtype = dtype;
+  a.B = B; a.T = T; a.H = HV; a.DK = DK; a.DV = DV; a.dtype = dtype;
   a.scale = resolve_scale(scale, DK);
   a.l2norm = l2 ? 1 : 0;
   a.chunk = chunk;
@@ -96,11 +103,12 @@ extern "C" {
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, const float* initial_state,
                     float* o, float* final_state,
-                    int B, int T, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm, int chunk_size,
+                    int B, int T, int H, int HV, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int state_v_first, int chunk_size,
                     const float* A_log, const float* dt_bias, float lower_bound, int transforms,
                     void* stream) {
-  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype,
+                             state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
@@ -109,11 +117,11 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,
-                                                 static_cast<long>(B) * H * DK * DV, s));
+                                                 static_cast<long>(B) * HV * DK * DV, s));
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
-                                        final_state, B, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, chunk_size,
+                                        final_state, B, T, H, HV, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, state_v_first, chunk_size,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_chunked(a, s));
 }
@@ -122,15 +130,17 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            const void* decay, int decay_kind, const float* initial_state,
                            float* o, float* final_state, const int* cu_seqlens,
                            const int* cu_seqlens_host, int N,
-                           int T, int H, int DK, int DV, int dtype,
-                           float softmax_scale, int use_qk_l2norm, int chunk_size,
+                           int T, int H, int HV, int DK, int DV, int dtype,
+                           float softmax_scale, int use_qk_l2norm, int state_v_first,
+                           int chunk_size,
                     const float* A_log, const float* dt_bias, float lower_bound, int transforms,
                     void* stream) {
-  int st = kda::check_common(q, k, v, beta, decay, decay_kind, 1, T, H, DK, DV, dtype);
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, 1, T, H, HV, DK, DV, dtype,
+                             state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || !cu_seqlens || !cu_seqlens_host || (T != 0 && !o)) return KDA_ERR_NULL;
-  if (N < 1 || static_cast<long long>(N) * H * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
+  if (N < 1 || static_cast<long long>(N) * HV * DK * DV >= (1LL << 31)) return KDA_ERR_SHAPE;
   if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T) return KDA_ERR_SHAPE;
   for (int n = 0; n < N; ++n)
     if (cu_seqlens_host[n + 1] < cu_seqlens_host[n]) return KDA_ERR_SHAPE;
@@ -139,11 +149,11 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,
-                                                 static_cast<long>(N) * H * DK * DV, s));
+                                                 static_cast<long>(N) * HV * DK * DV, s));
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
-                                        final_state, 1, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, chunk_size,
+                                        final_state, 1, T, H, HV, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, state_v_first, chunk_size,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, s));
 }
@@ -151,39 +161,42 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
 int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
                       const void* decay, int decay_kind, const float* initial_state,
                       float* o, float* final_state,
-                      int B, int T, int H, int DK, int DV, int dtype,
-                      float softmax_scale, int use_qk_l2norm,
+                      int B, int T, int H, int HV, int DK, int DV, int dtype,
+                      float softmax_scale, int use_qk_l2norm, int state_v_first,
                     const float* A_log, const float* dt_bias, float lower_bound, int transforms,
                     void* stream) {
-  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, DK, DV, dtype);
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype,
+                             state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,
-                                                 static_cast<long>(B) * H * DK * DV, s));
+                                                 static_cast<long>(B) * HV * DK * DV, s));
   }
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
-                                        final_state, B, T, H, DK, DV, dtype, softmax_scale,
-                                        use_qk_l2norm, 0,
+                                        final_state, B, T, H, HV, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, state_v_first, 0,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_recurrent(a, s));
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, float* state, float* o,
-                    int B, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm,
+                    int B, int H, int HV, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int state_v_first,
                     const float* A_log, const float* dt_bias, float lower_bound, int transforms,
                     void* stream) {
-  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, 1, H, DK, DV, dtype);
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, 1, H, HV, DK, DV, dtype,
+                             state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, 1, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (!state || !o) return KDA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, state, o, state, B, 1, H,
-                                        DK, DV, dtype, softmax_scale, use_qk_l2norm, 0,
+                                        HV, DK, DV, dtype, softmax_scale, use_qk_l2norm,
+                                        state_v_first, 0,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
   return kda::to_status(kda::launch_decode(a, s));
 }
@@ -194,12 +207,12 @@ const char* kda_status_string(int status) {
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
     case KDA_ERR_UNSUPPORTED: return "unsupported head size, chunk size, dtype or decay kind";
-    case KDA_ERR_VALUE: return "invalid transform flags or lower bound";
+    case KDA_ERR_VALUE: return "invalid transform flags, lower bound or state layout";
     case KDA_ERR_HIP: return "HIP runtime error at launch";
   }
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 102; }
+int kda_abi_version(void) { return 103; }
 
 }  // extern "C"

@@ -106,6 +106,7 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   pp.ws = static_cast<unsigned char*>(ws);
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
   pp.tf = a.tf;
+  pp.Hk = a.Hk;
 
   StateParams sp;
   sp.cu = nullptr; sp.cb = nullptr;
@@ -114,6 +115,7 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
   sp.o = a.o; sp.state = a.state;
   sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
+  sp.Hk = a.Hk; sp.vfirst = a.vfirst;
   sp.nsl = a.DV / pl.dvs;
   sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
 
@@ -187,6 +189,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
   pp.ws = static_cast<unsigned char*>(ws);
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
   pp.tf = a.tf;
+  pp.Hk = a.Hk;
   pp.c0 = 0; pp.nchunks = static_cast<int>(total);
 
   StateParams sp;
@@ -196,6 +199,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
   sp.o = a.o; sp.state = a.state; sp.init = a.init;
   sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
+  sp.Hk = a.Hk; sp.vfirst = a.vfirst;
   sp.nsl = a.DV / pl.dvs;
   const int nheads = nseq * a.H;
   sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;

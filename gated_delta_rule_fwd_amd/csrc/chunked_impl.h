@@ -207,6 +207,7 @@ struct PrepParams {
   float scale;
   const int* cu; const int* cb; int nseq;   // packed input
   Transforms tf;         // raw gate / raw beta (applied where decay and beta are read)
+  int Hk;                // q/k heads: value head h reads q, k head h / (H / Hk)
 };
 
 struct StateParams {
@@ -217,6 +218,8 @@ struct StateParams {
   int c0;                // first chunk of this launch; `init` holds the state entering it
   int l2norm; float scale;   // q's row factor (raw rows)
   const int* cu; const int* cb;   // packed input (see PrepParams); state and o by sequence
+  int Hk;                // q/k heads (see PrepParams)
+  int vfirst;            // init and state value-major [.., H, DV, DK]
 };
 
 // The sequence of packed chunk g: the last n with cb[n] <= g (cb
@@ -355,6 +358,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   const int T = p.T, H = p.H;
   const int ch = blockIdx.x % p.nchunks, head = blockIdx.x / p.nchunks;
   const int b = head / H, h = head % H;
+  const int hk = h / (H / p.Hk);   // the q/k head of value head h
   int Lc;                 // tokens in the chunk
   long tok0;              // first token of the chunk
   if (p.cu) {
@@ -404,9 +408,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       const int r = pp * RPP + tid / LPR, seg = tid % LPR;
       rq[pp] = rk[pp] = rg[pp] = uint4{0, 0, 0, 0};
       if (r < Lc) {
-        const long off = ((tok0 + r) * H + h) * DK + seg * V;
-        if constexpr (!R::kRawK) rq[pp] = *reinterpret_cast<const uint4*>(gq + off);
-        rk[pp] = *reinterpret_cast<const uint4*>(gk + off);
+        const long off = ((tok0 + r) * H + h) * DK + seg * V;            // per value head
+        const long offk = ((tok0 + r) * p.Hk + hk) * DK + seg * V;       // per q/k head
+        if constexpr (!R::kRawK) rq[pp] = *reinterpret_cast<const uint4*>(gq + offk);
+        rk[pp] = *reinterpret_cast<const uint4*>(gk + offk);
         if (chan) rg[pp] = *reinterpret_cast<const uint4*>(gg + off);
       }
     }
@@ -1013,7 +1018,8 @@ void state_kernel(StateParams p) {
     nchunks = p.nchunks;
   }
   const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
-  const int rowK = H * DK * AB;              // ... of k
+  const int rowK = p.Hk * DK * AB;           // ... of q and k (q/k heads)
+  const int hk = h / (H / p.Hk);             // the q/k head of value head h
   const int rowO = H * DV * 4;               // ... and of o
 
   RecFrags<DK, C, OpT> fr;
@@ -1064,7 +1070,7 @@ void state_kernel(StateParams p) {
     const int t0 = c * C, Lc = min(C, Trem - t0);
     if constexpr (part != 2) {
       if constexpr (rawk) {
-        const long e0 = ((seq0 + t0) * H + h) * static_cast<long>(DK);
+        const long e0 = ((seq0 + t0) * p.Hk + hk) * static_cast<long>(DK);
         const int nb = (Lc - 1) * rowK + DK * AB;
         const i32x4 rk = rsrc(gk + e0, nb), rq = rsrc(gq + e0, nb);
 #pragma unroll
@@ -1126,6 +1132,11 @@ void state_kernel(StateParams p) {
   auto srow = [&](int t, int j) {
     return rawk ? 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j : 16 * t + 4 * g + j;
   };
+  // element (key row, this lane's column) of the initial / final state
+  const long sbase = (static_cast<long>(b) * H + h) * DK * DV;
+  auto sidx = [&](int row) {
+    return sbase + (p.vfirst ? static_cast<long>(ncol) * DK + row : static_cast<long>(row) * DV + ncol);
+  };
   f32x4 S[NKT];
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
@@ -1133,7 +1144,7 @@ void state_kernel(StateParams p) {
     if (owner && p.init) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        S[t][j] = p.init[((static_cast<long>(b) * H + h) * DK + srow(t, j)) * DV + ncol];
+        S[t][j] = p.init[sidx(srow(t, j))];
     }
   }
 
@@ -1489,7 +1500,7 @@ void state_kernel(StateParams p) {
     for (int t = 0; t < NKT; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        p.state[((static_cast<long>(b) * H + h) * DK + srow(t, j)) * DV + ncol] = S[t][j];
+        p.state[sidx(srow(t, j))] = S[t][j];
     }
   }
 }

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
-    Transforms tf) {
+    Transforms tf, int Hk) {
   constexpr int CS = decode_cols<DV>();
   constexpr int NSPLIT = DV / CS;
   constexpr int NC4 = CS / 4;             // float4 column groups per state row
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int cg = tid % NC4, rg = tid / NC4;
   float* S = state + bh * DK * DV + n0;
   const int h = static_cast<int>(bh % H);
+  const long bhk = (bh / H) * Hk + h / (H / Hk);   // q/k row of value head h
   const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
 
   // Issue the state loads first: they are the bulk of the traffic.
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   // Token vectors; norms and q.k by block reduction.
   float pq = 0.f, pk = 0.f, pqk = 0.f;
   for (int c = tid; c < DK; c += kThreads) {
-    const float qc = act<In>::load1(q + bh * DK + c);
-    const float kc = act<In>::load1(k + bh * DK + c);
+    const float qc = act<In>::load1(q + bhk * DK + c);
+    const float kc = act<In>::load1(k + bhk * DK + c);
     s_q[c] = qc;
     s_k[c] = kc;
     float gc = 1.f;
@@ -134,6 +135,97 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
 }
 
+// Value-major state [.., DV, DK] (each value column's DK key rows
+// contiguous): a workgroup takes CS value columns of one (batch, head); DK / 4
+// consecutive lanes hold one column as float4s, so loads and stores stay
+// contiguous, and the two column reductions run over those lanes with DPP.
+template <int DK, int DV, typename In>
+__global__ __launch_bounds__(kThreads) void decode_vm_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
+    float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
+    Transforms tf, int Hk) {
+  constexpr int CS = decode_cols<DV>();
+  constexpr int NSPLIT = DV / CS;
+  constexpr int LPC = DK / 4;             // lanes per value column
+  constexpr int CPP = kThreads / LPC;     // columns per pass
+  constexpr int CPT = CS / CPP;           // columns per thread
+  static_assert(CPT >= 1 && CS % CPP == 0 && 64 % LPC == 0, "shape");
+  constexpr int NW = kThreads / 64;
+
+  __shared__ float s_q[DK], s_k[DK], s_gate[DK], s_v[CS];
+  __shared__ float s_red[3][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long bh = blockIdx.x / NSPLIT;
+  const int n0 = (blockIdx.x % NSPLIT) * CS;
+  const int cq = tid % LPC, cr = tid / LPC;   // key rows 4 cq .. 4 cq + 3 of columns cr + CPP i
+  float* S = state + bh * DK * DV + static_cast<long>(n0) * DK;
+  const int h = static_cast<int>(bh % H);
+  const long bhk = (bh / H) * Hk + h / (H / Hk);
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;
+
+  f32x4 st[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (cr + CPP * i) * DK) + cq);
+
+  float pq = 0.f, pk = 0.f, pqk = 0.f;
+  for (int c = tid; c < DK; c += kThreads) {
+    const float qc = act<In>::load1(q + bhk * DK + c);
+    const float kc = act<In>::load1(k + bhk * DK + c);
+    s_q[c] = qc;
+    s_k[c] = kc;
+    float gc = 1.f;
+    if (decay_kind == DECAY_CHANNEL) {
+      float g = act<In>::load1(decay + bh * DK + c);
+      if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h * DK + c] : 0.f, tf.lower);
+      gc = __expf(g);
+    }
+    s_gate[c] = gc;
+    pq += qc * qc; pk += kc * kc; pqk += qc * kc;
+  }
+  for (int n = tid; n < CS; n += kThreads) s_v[n] = act<In>::load1(v + bh * DV + n0 + n);
+  pq = group_sum<64>(pq); pk = group_sum<64>(pk); pqk = group_sum<64>(pqk);
+  if (lane == 0) { s_red[0][wave] = pq; s_red[1][wave] = pk; s_red[2][wave] = pqk; }
+  __syncthreads();
+  float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { sq += s_red[0][w]; sk += s_red[1][w]; sqk += s_red[2][w]; }
+  const float iq = (l2norm ? inv_norm(sq) : 1.f) * scale;
+  const float ik = l2norm ? inv_norm(sk) : 1.f;
+  const float qk = sqk * iq * ik;
+  const float b = beta_transform(act<In>::load1(beta + bh), tf.beta_mode);
+  float ghead = 1.f;
+  if (decay_kind == DECAY_HEAD) {
+    float g = act<In>::load1(decay + bh);
+    if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h] : 0.f, tf.lower);
+    ghead = __expf(g);
+  }
+
+  // this thread's four key rows
+  f32x4 kc, qg, gc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = 4 * cq + e;
+    kc[e] = s_k[c] * ik;
+    gc[e] = s_gate[c] * ghead;
+    qg[e] = s_q[c] * iq * gc[e];
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int n = cr + CPP * i;
+    float r = st[i][0] * kc[0] + st[i][1] * kc[1] + st[i][2] * kc[2] + st[i][3] * kc[3];
+    float y = st[i][0] * qg[0] + st[i][1] * qg[1] + st[i][2] * qg[2] + st[i][3] * qg[3];
+    r = dpp_group_sum<LPC>(r);
+    y = dpp_group_sum<LPC>(y);
+    const float delta = b * (s_v[n] - r);
+    if (cq == 0) o[bh * DV + n0 + n] = y + qk * delta;
+    const f32x4 ns = st[i] * gc + kc * delta;
+    __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + n * DK) + cq);
+  }
+}
+
 template <typename In>
 hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   const dim3 block(kThreads);
@@ -145,8 +237,14 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
 #define KDA_DECODE_CASE(dk, dv)                                                              \
   if (a.DK == dk && a.DV == dv) {                                                            \
     const dim3 grid(a.B * a.H * (dv / decode_cols<dv>()));                                   \
-    decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.state, \
-                                                      a.o, a.scale, a.l2norm, a.H, a.tf);  \
+    if (a.vfirst)                                                                            \
+      decode_vm_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,     \
+                                                          a.state, a.o, a.scale, a.l2norm,   \
+                                                          a.H, a.tf, a.Hk);                  \
+    else                                                                                     \
+      decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,        \
+                                                       a.state, a.o, a.scale, a.l2norm, a.H, \
+                                                       a.tf, a.Hk);                          \
     return hipGetLastError();                                                                \
   }
   KDA_DECODE_CASE(32, 32) KDA_DECODE_CASE(32, 64) KDA_DECODE_CASE(32, 128)

@@ -17,7 +17,9 @@ struct FwdArgs {
   const float* init;   // NULL = zeros (decode: unused)
   float* o;
   float* state;        // final state (decode: state updated in place)
-  int B, T, H, DK, DV;
+  int B, T, H, DK, DV;   // H: recurrent (value) heads
+  int Hk;              // query/key heads; H is a multiple (value head h reads q, k head h / (H / Hk))
+  int vfirst;          // states are value-major [.., H, DV, DK] (else key-major [.., H, DK, DV])
   int dtype;           // 0 f32, 1 bf16
   float scale;         // already resolved (> 0)
   int l2norm;

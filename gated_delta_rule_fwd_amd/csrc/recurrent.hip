@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     const float* __restrict__ init, float* __restrict__ o, float* __restrict__ state_out,
-    int T, int H, float scale, int l2norm, Transforms tf) {
+    int T, int H, float scale, int l2norm, Transforms tf, int Hk, int vfirst) {
   constexpr int CPW = DV / 4;           // value columns per wave
   constexpr int NCG = CPW / 4;          // float4 column groups per wave
   constexpr int NRG = 64 / NCG;         // row groups per wave
@@ -42,12 +42,19 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
   const int col = wave * CPW + 4 * cg;          // first of this lane's 4 columns
   const int row0 = rg * RPL;                    // this lane's state rows row0 .. row0+RPL-1
   const long bh = static_cast<long>(b) * H + h;
+  const int hk = h / (H / Hk);                  // q/k head of value head h
+  // state element (key row c, value column n): key-major or value-major
+  auto sidx = [&](int c, int n) {
+    return bh * DK * DV + (vfirst ? static_cast<long>(n) * DK + c : static_cast<long>(c) * DV + n);
+  };
   const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
 
   f32x4 S[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
-    if (init) S[i] = *reinterpret_cast<const f32x4*>(init + (bh * DK + row0 + i) * DV + col);
+    if (init && !vfirst) S[i] = *reinterpret_cast<const f32x4*>(init + sidx(row0 + i, col));
+    else if (init) S[i] = f32x4{init[sidx(row0 + i, col)], init[sidx(row0 + i, col + 1)],
+                                init[sidx(row0 + i, col + 2)], init[sidx(row0 + i, col + 3)]};
     else S[i] = f32x4{0, 0, 0, 0};
   }
 
@@ -60,9 +67,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
       float sq = 0.f, sk = 0.f, sqk = 0.f;
       const bool live = tt < nt;
       const long base = ((static_cast<long>(b) * T + t0 + tt) * H + h) * DK + seg * V;
+      const long kbase = ((static_cast<long>(b) * T + t0 + tt) * Hk + hk) * DK + seg * V;
       if (live) {
-        act<In>::load_vec(q + base, qv);
-        act<In>::load_vec(k + base, kv);
+        act<In>::load_vec(q + kbase, qv);
+        act<In>::load_vec(k + kbase, kv);
       } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) { qv[e] = 0.f; kv[e] = 0.f; }
@@ -149,8 +157,14 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(
   }
 
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
-    *reinterpret_cast<f32x4*>(state_out + (bh * DK + row0 + i) * DV + col) = S[i];
+  for (int i = 0; i < RPL; ++i) {
+    if (!vfirst) {
+      *reinterpret_cast<f32x4*>(state_out + sidx(row0 + i, col)) = S[i];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) state_out[sidx(row0 + i, col + e)] = S[i][e];
+    }
+  }
 }
 
 template <typename In>
@@ -165,7 +179,8 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   if (a.DK == dk && a.DV == dv) {                                                         \
     recurrent_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,    \
                                                         a.init, a.o, a.state, a.T, a.H,   \
-                                                        a.scale, a.l2norm, a.tf);         \
+                                                        a.scale, a.l2norm, a.tf, a.Hk,    \
+                                                        a.vfirst);                        \
     return hipGetLastError();                                                             \
   }
   KDA_REC_CASE(32, 32) KDA_REC_CASE(32, 64) KDA_REC_CASE(32, 128)

@@ -53,6 +53,11 @@ class Workload:
     init_state: bool
     decode: bool = False
     seed: int = 1000
+    HV: int = 0           # value (recurrent) heads, a multiple of H; 0 means H
+
+    @property
+    def hv(self) -> int:
+        return self.HV or self.H
 
     @property
     def decay_kind(self) -> int:
@@ -86,12 +91,14 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     """Draw one batch of inputs for workload ``w``.
 
     Returns a dict of CPU tensors: q, k [B,T,H,DK] (decode: [B,H,DK]),
-    v [B,T,H,DV], beta [B,T,H], decay (None, [B,T,H] or [B,T,H,DK]) in the
-    activation dtype, and initial_state [B,H,DK,DV] fp32 or None.
+    v [B,T,HV,DV], beta [B,T,HV], decay (None, [B,T,HV] or [B,T,HV,DK]) in the
+    activation dtype, and initial_state [B,HV,DK,DV] fp32 or None (HV = H
+    unless the workload sets more value heads).
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     dt = torch_dtype(w.dtype)
-    lead = (w.B, w.H) if w.decode else (w.B, w.T, w.H)
+    qk_lead = (w.B, w.H) if w.decode else (w.B, w.T, w.H)
+    lead = (w.B, w.hv) if w.decode else (w.B, w.T, w.hv)
 
     def normal(shape):
         return rng.standard_normal(shape, dtype=np.float32)
@@ -99,8 +106,8 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     def act(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dt)
 
-    q = act(normal(lead + (w.DK,)))
-    k = act(normal(lead + (w.DK,)))
+    q = act(normal(qk_lead + (w.DK,)))
+    k = act(normal(qk_lead + (w.DK,)))
     v = act(normal(lead + (w.DV,)))
     beta = act(1.0 / (1.0 + np.exp(-normal(lead))))
     if w.decay == "none":
@@ -124,7 +131,7 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         raise ValueError(w.decay)
     init = None
     if w.init_state:
-        init = torch.from_numpy(0.1 * normal((w.B, w.H, w.DK, w.DV)))
+        init = torch.from_numpy(0.1 * normal((w.B, w.hv, w.DK, w.DV)))
     return dict(q=q, k=k, v=v, beta=beta, decay=decay, initial_state=init)
 
 
@@ -138,16 +145,16 @@ def make_transform_inputs(w: Workload, seed: int | None = None) -> dict:
     base = make_inputs(w, seed)
     rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
     dt = torch_dtype(w.dtype)
-    lead = (w.B, w.H) if w.decode else (w.B, w.T, w.H)
+    lead = (w.B, w.hv) if w.decode else (w.B, w.T, w.hv)
 
     def act(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dt)
 
     kind = w.decay_kind
     gshape = lead + ((w.DK,) if kind == DECAY_CHANNEL else ())
-    bshape = (w.H, w.DK) if kind == DECAY_CHANNEL else (w.H,)
+    bshape = (w.hv, w.DK) if kind == DECAY_CHANNEL else (w.hv,)
     gate = act(rng.standard_normal(gshape, dtype=np.float32)) if kind != DECAY_NONE else None
     beta_logits = act(rng.standard_normal(lead, dtype=np.float32))
-    A_log = torch.from_numpy(0.3 * rng.standard_normal((w.H,), dtype=np.float32))
+    A_log = torch.from_numpy(0.3 * rng.standard_normal((w.hv,), dtype=np.float32))
     dt_bias = torch.from_numpy(rng.uniform(-2.0, 0.0, bshape).astype(np.float32))
     return dict(base, gate=gate, beta_logits=beta_logits, A_log=A_log, dt_bias=dt_bias)

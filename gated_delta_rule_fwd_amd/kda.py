@@ -43,16 +43,16 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
-                                      i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
+                                      i, i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp]
         L.kda_fwd_chunked.restype = i
         L.kda_fwd_chunked_varlen.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i,
-                                             i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
+                                             i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp]
         L.kda_fwd_chunked_varlen.restype = i
         L.kda_fwd_recurrent.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
-                                        i, i, i, i, i, i, f, i, vp, vp, f, i, vp]
+                                        i, i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_fwd_recurrent.restype = i
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, i, vp, vp,
-                                      i, i, i, i, i, f, i, vp, vp, f, i, vp]
+                                      i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_decode_step.restype = i
         L.kda_status_string.argtypes = [i]
         L.kda_status_string.restype = ctypes.c_char_p
@@ -138,49 +138,59 @@ def _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_boun
     return _ptr(A_log), _ptr(dt_bias), lb, flags
 
 
-def _prep_fwd(q, k, v, beta, decay, initial_state):
-    if q.dim() != 4:
-        raise ValueError("q must be [B, T, H, DK]")
+def _state_shape(N, HV, DK, DV, state_v_first):
+    return (N, HV, DV, DK) if state_v_first else (N, HV, DK, DV)
+
+
+def _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first=False):
+    """q, k [B,T,H,DK]; v [B,T,HV,DV] with HV a multiple of H (value head hv
+    reads q/k head hv // (HV // H)); beta, decay and o per value head."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, T, H, DK] and v [B, T, HV, DV]")
     B, T, H, DK = q.shape
-    DV = v.shape[-1]
+    HV, DV = v.shape[2], v.shape[3]
     dev, dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
     _check_act("q", q, (B, T, H, DK), dt, dev)
     _check_act("k", k, (B, T, H, DK), dt, dev)
-    _check_act("v", v, (B, T, H, DV), dt, dev)
-    _check_act("beta", beta, (B, T, H), dt, dev)
-    kind = _decay_kind(decay, (B, T, H), DK)
+    _check_act("v", v, (B, T, HV, DV), dt, dev)
+    _check_act("beta", beta, (B, T, HV), dt, dev)
+    kind = _decay_kind(decay, (B, T, HV), DK)
     if decay is not None:
         _check_act("decay", decay, tuple(decay.shape), dt, dev)
-    _check_state("initial_state", initial_state, (B, H, DK, DV), dev)
-    return B, T, H, DK, DV, dev, kind
+    _check_state("initial_state", initial_state, _state_shape(B, HV, DK, DV, state_v_first), dev)
+    return B, T, H, HV, DK, DV, dev, kind
 
 
 def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
                 use_qk_l2norm=True, chunk_size=64, out=None, final_state=None,
-                use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
                 lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
-    """Chunked forward.  Returns (o [B,T,H,DV] fp32, final_state [B,H,DK,DV] fp32).
+    """Chunked forward.  q, k [B,T,H,DK]; v [B,T,HV,DV] (HV a multiple of H);
+    beta [B,T,HV]; decay None, [B,T,HV] or [B,T,HV,DK].  Returns (o [B,T,HV,DV]
+    fp32, final_state fp32), states [B,HV,DK,DV], or [B,HV,DV,DK] with
+    ``state_v_first``.
 
     Input transforms (all entry points): with ``use_gate_in_kernel`` the
     decay tensor holds the raw gate and the kernels use
     -exp(A_log) * softplus(gate + dt_bias), floored at ``lower_bound`` if
-    given (A_log [H] fp32; dt_bias [H], or [H, DK] for a per-channel gate,
+    given (A_log [HV] fp32; dt_bias [HV], or [HV, DK] for a per-channel gate,
     fp32 or None); ``use_beta_sigmoid_in_kernel`` reads beta as logits
     (sigmoid, or 2 * sigmoid with ``allow_neg_eigval``)."""
-    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
-    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
-    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
-    _check_state("out", o, (B, T, H, DV), dev)
-    fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
+    sshape = _state_shape(B, HV, DK, DV, state_v_first)
+    o = out if out is not None else torch.empty((B, T, HV, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, T, HV, DV), dev)
+    fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
                                                                  dtype=torch.float32)
-    _check_state("final_state", fs, (B, H, DK, DV), dev)
+    _check_state("final_state", fs, sshape, dev)
     st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
-                               _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
+                               _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, HV, DK, DV,
                                _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                               int(chunk_size), *tf, _stream(dev))
+                               int(bool(state_v_first)), int(chunk_size), *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked", st)
     return o, fs
@@ -188,15 +198,15 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
 
 def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None,
                        softmax_scale=None, use_qk_l2norm=True, chunk_size=64, out=None,
-                       final_state=None, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                       final_state=None, state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
                 lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """Chunked forward over N packed sequences (tokens [1, T, ...], sequence n
     is tokens cu_seqlens[n] .. cu_seqlens[n + 1]).  cu_seqlens: int32, N + 1
     offsets, on the CPU or the GPU (the other copy is made here).  Returns
-    (o [1,T,H,DV] fp32, final_state [N,H,DK,DV] fp32).  Transforms as
-    fwd_chunked."""
-    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, None)
-    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+    (o [1,T,HV,DV] fp32, final_state [N,HV,DK,DV] fp32).  Heads, state layout
+    and transforms as fwd_chunked."""
+    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, None)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
     if B != 1:
         raise ValueError("packed sequences need B == 1")
@@ -205,73 +215,80 @@ def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None
     N = cu_seqlens.numel() - 1
     cu_host = cu_seqlens.to("cpu", torch.int32).contiguous()
     cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
-    _check_state("initial_state", initial_state, (N, H, DK, DV), dev)
-    o = out if out is not None else torch.empty((1, T, H, DV), device=dev, dtype=torch.float32)
-    _check_state("out", o, (1, T, H, DV), dev)
-    fs = final_state if final_state is not None else torch.empty((N, H, DK, DV), device=dev,
+    sshape = _state_shape(N, HV, DK, DV, state_v_first)
+    _check_state("initial_state", initial_state, sshape, dev)
+    o = out if out is not None else torch.empty((1, T, HV, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (1, T, HV, DV), dev)
+    fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
                                                                  dtype=torch.float32)
-    _check_state("final_state", fs, (N, H, DK, DV), dev)
+    _check_state("final_state", fs, sshape, dev)
     st = lib().kda_fwd_chunked_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                       _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(cu_dev),
-                                      _ptr(cu_host), N, T, H, DK, DV, _dtype_code(q),
+                                      _ptr(cu_host), N, T, H, HV, DK, DV, _dtype_code(q),
                                       _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                                      int(chunk_size), *tf, _stream(dev))
+                                      int(bool(state_v_first)), int(chunk_size), *tf,
+                                      _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked_varlen", st)
     return o, fs
 
 
 def fwd_recurrent(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
-                  use_qk_l2norm=True, out=None, final_state=None, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                  use_qk_l2norm=True, out=None, final_state=None, state_v_first=False,
+                  use_gate_in_kernel=False, A_log=None, dt_bias=None,
                 lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
-    """Recurrent (sequential) forward.  Same returns and transforms as fwd_chunked."""
-    B, T, H, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
-    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+    """Recurrent (sequential) forward.  Same arguments and returns as fwd_chunked."""
+    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
-    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
-    _check_state("out", o, (B, T, H, DV), dev)
-    fs = final_state if final_state is not None else torch.empty((B, H, DK, DV), device=dev,
+    sshape = _state_shape(B, HV, DK, DV, state_v_first)
+    o = out if out is not None else torch.empty((B, T, HV, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, T, HV, DV), dev)
+    fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
                                                                  dtype=torch.float32)
-    _check_state("final_state", fs, (B, H, DK, DV), dev)
+    _check_state("final_state", fs, sshape, dev)
     st = lib().kda_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
-                                 _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, DK, DV,
+                                 _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, HV, DK, DV,
                                  _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                                 *tf, _stream(dev))
+                                 int(bool(state_v_first)), *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_recurrent", st)
     return o, fs
 
 
 def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=True, out=None,
-                use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
                 lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
-    """One decode step for every (batch, head); ``state`` [B,H,DK,DV] fp32 is
-    updated in place.  Returns o [B,H,DV] fp32.  Transforms as fwd_chunked."""
-    if q.dim() != 3:
-        raise ValueError("q must be [B, H, DK]")
+    """One decode step for every (batch, value head): q, k [B,H,DK]; v [B,HV,DV];
+    beta [B,HV]; decay None, [B,HV] or [B,HV,DK]; ``state`` [B,HV,DK,DV] fp32
+    ([B,HV,DV,DK] with ``state_v_first``) is updated in place.  Returns
+    o [B,HV,DV] fp32.  Transforms as fwd_chunked."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [B, H, DK] and v [B, HV, DV]")
     B, H, DK = q.shape
-    DV = v.shape[-1]
+    HV, DV = v.shape[1], v.shape[2]
     dev, dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
     _check_act("q", q, (B, H, DK), dt, dev)
     _check_act("k", k, (B, H, DK), dt, dev)
-    _check_act("v", v, (B, H, DV), dt, dev)
-    _check_act("beta", beta, (B, H), dt, dev)
-    kind = _decay_kind(decay, (B, H), DK)
+    _check_act("v", v, (B, HV, DV), dt, dev)
+    _check_act("beta", beta, (B, HV), dt, dev)
+    kind = _decay_kind(decay, (B, HV), DK)
     if decay is not None:
         _check_act("decay", decay, tuple(decay.shape), dt, dev)
     if state is None:
         raise ValueError("state is required")
-    _check_state("state", state, (B, H, DK, DV), dev)
-    o = out if out is not None else torch.empty((B, H, DV), device=dev, dtype=torch.float32)
-    _check_state("out", o, (B, H, DV), dev)
-    tf = _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+    sshape = _state_shape(B, HV, DK, DV, state_v_first)
+    _check_state("state", state, sshape, dev)
+    o = out if out is not None else torch.empty((B, HV, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, HV, DV), dev)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
     st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
-                               _ptr(state), _ptr(o), B, H, DK, DV, _dtype_code(q),
-                               _scale(softmax_scale), int(bool(use_qk_l2norm)), *tf,
-                               _stream(dev))
+                               _ptr(state), _ptr(o), B, H, HV, DK, DV, _dtype_code(q),
+                               _scale(softmax_scale), int(bool(use_qk_l2norm)),
+                               int(bool(state_v_first)), *tf, _stream(dev))
     if st != 0:
         raise KdaError("kda_decode_step", st)
     return o

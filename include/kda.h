@@ -36,8 +36,16 @@
  *    argument validation (nothing is launched when it fails) and launch
  *    errors; a device-side fault surfaces at the caller's next
  *    synchronisation.
- *  - Supported sizes: DK, DV in {32, 64, 128}; B, H >= 1; T >= 0 with
- *    B*T*H*max(DK,DV) < 2^31.
+ *  - Heads (TileOPs GDNFwdOp / KDAFwdOp): q and k have H heads; v, beta,
+ *    decay, o and the states have HV recurrent heads, a multiple of H, and
+ *    value head hv reads q/k head hv / (HV / H) (consecutive value heads
+ *    share a q/k head).  HV == H is the plain case.
+ *  - State layout: key-major [.., HV, DK, DV] (state_v_first = 0) or
+ *    value-major [.., HV, DV, DK] (state_v_first = 1, TileOPs state_v_first);
+ *    initial and final states use the same layout.  Other values:
+ *    KDA_ERR_VALUE.
+ *  - Supported sizes: DK, DV in {32, 64, 128}; B, H, HV >= 1 with HV % H
+ *    == 0; T >= 0 with B*T*HV*max(DK,DV) < 2^31.
  *  - Input transforms, the trailing (A_log, dt_bias, lower_bound, transforms)
  *    of every entry point (TileOPs "Linear Attention Operators", GDNFwdOp and
  *    KDAFwdOp: use_gate_in_kernel, lower_bound, use_beta_sigmoid_in_kernel,
@@ -46,8 +54,8 @@
  *    given, and then A_log, dt_bias and lower_bound are not read.
  *      KDA_TF_GATE: decay holds the raw gate; the kernels use
  *        decay = -exp(A_log[h]) * softplus(gate + dt_bias)
- *        with A_log DEVICE fp32 [H] (required) and dt_bias DEVICE fp32 [H]
- *        for KDA_DECAY_HEAD or [H, DK] for KDA_DECAY_CHANNEL (NULL = 0).
+ *        with A_log DEVICE fp32 [HV] (required) and dt_bias DEVICE fp32 [HV]
+ *        for KDA_DECAY_HEAD or [HV, DK] for KDA_DECAY_CHANNEL (NULL = 0).
  *        The result is <= 0 by construction.
  *      KDA_TF_LOWER_BOUND (with KDA_TF_GATE): decay = max(decay, lower_bound),
  *        a floor of the forget gate in log space; lower_bound must be <= 0.
@@ -73,7 +81,7 @@ typedef enum {
   KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
   KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
   KDA_ERR_UNSUPPORTED = 3, /* DK/DV/chunk/dtype/decay kind not implemented   */
-  KDA_ERR_VALUE = 4,       /* invalid transform flags or lower bound         */
+  KDA_ERR_VALUE = 4,       /* invalid transform flags, floor or state layout */
   KDA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
 } kda_status;
 
@@ -88,8 +96,8 @@ typedef enum {
 
 typedef enum {
   KDA_DECAY_NONE = 0,    /* decay ignored (may be NULL): no decay             */
-  KDA_DECAY_HEAD = 1,    /* decay [.., H]: one log-space value per token-head */
-  KDA_DECAY_CHANNEL = 2  /* decay [.., H, DK]: one per token-head-key channel */
+  KDA_DECAY_HEAD = 1,    /* decay [.., HV]: one log-space value per token-head */
+  KDA_DECAY_CHANNEL = 2  /* decay [.., HV, DK]: one per token-head-key channel */
 } kda_decay_kind;
 
 /*
@@ -98,12 +106,13 @@ typedef enum {
  * TileOPs DeltaNet pipeline (prepare_wy_repr, then the forward).
  *
  *   q, k           [B, T, H, DK]  activation dtype
- *   v              [B, T, H, DV]  activation dtype
- *   beta           [B, T, H]      activation dtype
- *   decay          NULL | [B, T, H] | [B, T, H, DK] per decay_kind
- *   initial_state  NULL (zeros) | [B, H, DK, DV] fp32
- *   o              [B, T, H, DV] fp32, written
- *   final_state    [B, H, DK, DV] fp32, written; may alias initial_state
+ *   v              [B, T, HV, DV] activation dtype
+ *   beta           [B, T, HV]     activation dtype
+ *   decay          NULL | [B, T, HV] | [B, T, HV, DK] per decay_kind
+ *   initial_state  NULL (zeros) | [B, HV, DK, DV] fp32 ([B, HV, DV, DK]
+ *                  value-major)
+ *   o              [B, T, HV, DV] fp32, written
+ *   final_state    like initial_state, written; may alias initial_state
  *   chunk_size     16, 32 or 64 (ejkernel default 64); the result does not
  *                  depend on it beyond rounding.  T need not be a multiple.
  *
@@ -130,8 +139,8 @@ typedef enum {
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, const float* initial_state,
                     float* o, float* final_state,
-                    int B, int T, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm, int chunk_size,
+                    int B, int T, int H, int HV, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int state_v_first, int chunk_size,
                     const float* A_log, const float* dt_bias, float lower_bound,
                     int transforms, void* stream);
 
@@ -143,15 +152,16 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
  * own; chunks never cross a sequence end.
  *
  *   q, k           [1, T, H, DK]  the N sequences back to back
- *   v              [1, T, H, DV]
- *   beta           [1, T, H]
- *   decay          NULL | [1, T, H] | [1, T, H, DK] per decay_kind
+ *   v              [1, T, HV, DV]
+ *   beta           [1, T, HV]
+ *   decay          NULL | [1, T, HV] | [1, T, HV, DK] per decay_kind
  *   cu_seqlens     DEVICE int32 [N + 1]: sequence n is tokens
  *                  [cu_seqlens[n], cu_seqlens[n + 1])
  *   cu_seqlens_host HOST int32 [N + 1], the same values (sizes the launch)
- *   initial_state  NULL (zeros) | [N, H, DK, DV] fp32
- *   o              [1, T, H, DV] fp32, written
- *   final_state    [N, H, DK, DV] fp32, written; may alias initial_state
+ *   initial_state  NULL (zeros) | [N, HV, DK, DV] fp32 ([N, HV, DV, DK]
+ *                  value-major)
+ *   o              [1, T, HV, DV] fp32, written
+ *   final_state    like initial_state, written; may alias initial_state
  *
  * An empty sequence passes its initial state through.  The workspace holds
  * the records of all chunks of all sequences at once (no segmentation).
@@ -163,8 +173,9 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            const void* decay, int decay_kind, const float* initial_state,
                            float* o, float* final_state, const int* cu_seqlens,
                            const int* cu_seqlens_host, int N,
-                           int T, int H, int DK, int DV, int dtype,
-                           float softmax_scale, int use_qk_l2norm, int chunk_size,
+                           int T, int H, int HV, int DK, int DV, int dtype,
+                           float softmax_scale, int use_qk_l2norm, int state_v_first,
+                           int chunk_size,
                            const float* A_log, const float* dt_bias, float lower_bound,
                            int transforms, void* stream);
 /*
@@ -175,8 +186,8 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
 int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
                       const void* decay, int decay_kind, const float* initial_state,
                       float* o, float* final_state,
-                      int B, int T, int H, int DK, int DV, int dtype,
-                      float softmax_scale, int use_qk_l2norm,
+                      int B, int T, int H, int HV, int DK, int DV, int dtype,
+                      float softmax_scale, int use_qk_l2norm, int state_v_first,
                       const float* A_log, const float* dt_bias, float lower_bound,
                       int transforms, void* stream);
 
@@ -186,17 +197,18 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* b
  * DeltaNetRecurrentFwdOp extended with the gate): one token for every
  * (batch, head), the state updated IN PLACE.
  *
- *   q, k   [B, H, DK]; v [B, H, DV]; beta [B, H] (activation dtype)
- *   decay  NULL | [B, H] | [B, H, DK] per decay_kind
- *   state  [B, H, DK, DV] fp32, read then overwritten with the new state
- *   o      [B, H, DV] fp32, written (must not overlap state)
+ *   q, k   [B, H, DK]; v [B, HV, DV]; beta [B, HV] (activation dtype)
+ *   decay  NULL | [B, HV] | [B, HV, DK] per decay_kind
+ *   state  [B, HV, DK, DV] fp32 ([B, HV, DV, DK] value-major), read then
+ *          overwritten with the new state
+ *   o      [B, HV, DV] fp32, written (must not overlap state)
  *
  * Errors as kda_fwd_chunked (state must be non-NULL).
  */
 int kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, float* state, float* o,
-                    int B, int H, int DK, int DV, int dtype,
-                    float softmax_scale, int use_qk_l2norm,
+                    int B, int H, int HV, int DK, int DV, int dtype,
+                    float softmax_scale, int use_qk_l2norm, int state_v_first,
                     const float* A_log, const float* dt_bias, float lower_bound,
                     int transforms, void* stream);
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 102
+    assert L.kda_abi_version() == 103
     assert L.kda_status_string(0) == b"ok"
     for code in (1, 2, 3, 4, 5):
         assert len(L.kda_status_string(code)) > 3
@@ -50,13 +50,14 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 def chunked(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
-             B=1, T=8, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64,
+             B=1, T=8, H=1, HV=None, DK=64, DV=64, dtype=1, scale=0.0, l2=1, vf=0, chunk=64,
              A=None, dt=None, lb=0.0, tf=0)
     a.update(kw)
+    hv = a["H"] if a["HV"] is None else a["HV"]
     return L.kda_fwd_chunked(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
-                             a["o"], a["fs"], a["B"], a["T"], a["H"], a["DK"], a["DV"], a["dtype"],
-                             a["scale"], a["l2"], a["chunk"], a["A"], a["dt"], a["lb"], a["tf"],
-                             None)
+                             a["o"], a["fs"], a["B"], a["T"], a["H"], hv, a["DK"], a["DV"],
+                             a["dtype"], a["scale"], a["l2"], a["vf"], a["chunk"], a["A"], a["dt"],
+                             a["lb"], a["tf"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -73,6 +74,9 @@ def chunked(L, **kw):
     (dict(tf=3, kind=2, decay=FAKE, A=FAKE, lb=float("nan")), 4),
     (dict(tf=8), 4),                                             # 2 sigmoid without sigmoid
     (dict(tf=1, kind=1, decay=FAKE), 1),                         # raw gate without A_log
+    # value heads: a multiple of the q/k heads; state layout flag 0 or 1
+    (dict(H=2, HV=3), 2), (dict(H=2, HV=0), 2), (dict(H=4, HV=2), 2),
+    (dict(vf=2), 4), (dict(vf=-1), 4),
 ])
 def test_chunked_rejects_bad_arguments(L, kw, code):
     assert chunked(L, **kw) == code
@@ -80,29 +84,33 @@ def test_chunked_rejects_bad_arguments(L, kw, code):
 
 def test_recurrent_and_decode_reject_bad_arguments(L):
     assert L.kda_fwd_recurrent(None, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
-                               1, 4, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 1
+                               1, 4, 1, 1, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 0, None) == 1
     assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
-                               1, 4, 1, 96, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 3
+                               1, 4, 1, 1, 96, 64, 1, 0.0, 1, 0, None, None, 0.0, 0, None) == 3
     assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
-                               1, 4, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 8, None) == 4
+                               1, 4, 1, 1, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 8, None) == 4
+    assert L.kda_fwd_recurrent(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE,
+                               1, 4, 2, 3, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 0, None) == 2
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE,
-                             1, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 1
+                             1, 1, 1, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 0, None) == 1
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
-                             0, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 0, None) == 2
+                             0, 1, 1, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 0, None) == 2
     assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE,
-                             1, 1, 64, 64, 1, 0.0, 1, None, None, 0.0, 1, None) == 1
+                             1, 1, 1, 64, 64, 1, 0.0, 1, 0, None, None, 0.0, 1, None) == 1
+    assert L.kda_decode_step(FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE,
+                             1, 1, 1, 64, 64, 1, 0.0, 1, 3, None, None, 0.0, 0, None) == 4
 
 
 def varlen(L, cu, N, T=8, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
-             cud=FAKE, H=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, chunk=64,
+             cud=FAKE, H=1, HV=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, vf=0, chunk=64,
              A=None, dt=None, lb=0.0, tf=0)
     a.update(kw)
     cuh = None if cu is None else (ctypes.c_int * len(cu))(*cu)
     return L.kda_fwd_chunked_varlen(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"],
                                     a["init"], a["o"], a["fs"], a["cud"], cuh, N, T, a["H"],
-                                    a["DK"], a["DV"], a["dtype"], a["scale"], a["l2"], a["chunk"],
-                                    a["A"], a["dt"], a["lb"], a["tf"], None)
+                                    a["HV"], a["DK"], a["DV"], a["dtype"], a["scale"], a["l2"],
+                                    a["vf"], a["chunk"], a["A"], a["dt"], a["lb"], a["tf"], None)
 
 
 @pytest.mark.parametrize("cu,N,T,kw,code", [

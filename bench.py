@@ -105,8 +105,8 @@ def time_chunked(w, steps, warmup, dev, raw=False):
     import torch
     from gated_delta_rule_fwd_amd import fwd_chunked
     from gated_delta_rule_fwd_amd.inputs import make_inputs, make_transform_inputs
-    o = torch.empty((w.B, w.T, w.H, w.DV), device=dev, dtype=torch.float32)
-    fs = torch.empty((w.B, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
+    o = torch.empty((w.B, w.T, w.hv, w.DV), device=dev, dtype=torch.float32)
+    fs = torch.empty((w.B, w.hv, w.DK, w.DV), device=dev, dtype=torch.float32)
     if raw:
         d = to_dev(make_transform_inputs(w), dev)
         args = (d["q"], d["k"], d["v"], d["beta_logits"], d["gate"], d["initial_state"])
@@ -178,23 +178,28 @@ def time_chunked_varlen(w, steps, warmup, dev):
     return sum(kern_ms) / len(kern_ms), byts, lens
 
 
-def time_decode(w, steps, warmup, dev):
+def time_decode(w, steps, warmup, dev, state_v_first=False):
+    """state_v_first: value-major states [B, H, DV, DK] (the same bytes)."""
     import torch
     from gated_delta_rule_fwd_amd import decode_step
     from gated_delta_rule_fwd_amd.inputs import make_inputs
     inp = make_inputs(w)
     d = to_dev(inp, dev)
     # two state buffers used alternately so consecutive calls stream different memory
-    states = [d["initial_state"], d["initial_state"].clone()]
+    s0 = d["initial_state"]
+    if state_v_first:
+        s0 = s0.transpose(-1, -2).contiguous()
+    states = [s0, s0.clone()]
     o = torch.empty((w.B, w.H, w.DV), device=dev, dtype=torch.float32)
     args = (d["q"], d["k"], d["v"], d["beta"], d["decay"])
     it = iter(range(1 << 30))
-    warm_up(lambda: decode_step(*args, states[next(it) % 2], out=o), warmup)
+    kw = dict(out=o, state_v_first=state_v_first)
+    warm_up(lambda: decode_step(*args, states[next(it) % 2], **kw), warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i, (s, e) in enumerate(evs):
         s.record()
-        decode_step(*args, states[i % 2], out=o)
+        decode_step(*args, states[i % 2], **kw)
         e.record()
     torch.cuda.synchronize()
     ms = [s.elapsed_time(e) for s, e in evs]
@@ -377,6 +382,11 @@ def main():
             extra[w4.name + "_raw_gate"] = {
                 "tokens_per_s": round(w4.B * w4.T / (k4r * 1e-3), 1), "kernel_ms_mean": round(k4r, 4),
                 "transforms": "gate -exp(A_log) softplus(gate + dt_bias) floored at -5, beta sigmoid"}
+        # the same shape with grouped value heads: 4 q/k heads, 16 value heads
+        wg = w.scaled(H=4, HV=w.H)
+        _, kg, _ = time_chunked(wg, max(3, args.steps // 2), args.warmup, dev)
+        extra[w.name + "_gva4"] = {"H": wg.H, "HV": wg.hv, "tokens_per_s": round(wg.B * wg.T / (kg * 1e-3), 1),
+                                   "kernel_ms_mean": round(kg, 4)}
         # the same tokens as packed sequences of mixed lengths
         vk, vb, lens = time_chunked_varlen(w, max(3, args.steps // 2), args.warmup, dev)
         extra[w.name + "_varlen"] = {
@@ -389,6 +399,11 @@ def main():
         extra[w5.name] = {"kernel_ms_mean": round(d_ms, 4), "GB_per_s": round(gbs, 1),
                           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_call": decode_bytes(w5)}
+        d_vm = time_decode(w5, max(5, args.steps), args.warmup, dev, state_v_first=True)
+        gbs_vm = decode_bytes(w5) / (d_vm * 1e-3) / 1e9
+        extra[w5.name + "_value_major"] = {"kernel_ms_mean": round(d_vm, 4),
+                                           "GB_per_s": round(gbs_vm, 1),
+                                           "hbm_frac": round(gbs_vm / HBM_PEAK_GBS, 4)}
         line["extra"] = extra
         torch.cuda.empty_cache()
     if args.calibrate_copy:

@@ -33,7 +33,7 @@ int check_common(const void* q, const void* k, const void* v, const void* beta, 
     return KDA_ERR_UNSUPPORTED;
   if (T != 0 && decay_kind != KDA_DECAY_NONE && !decay) return KDA_ERR_NULL;
   if (B < 1 || H < 1 || HV < 1 || T < 0 || DK < 1 || DV < 1) return KDA_ERR_SHAPE;
-  if (HV % H != 0) return KDA_ERR_SHAPE;
+  if (HV % H != 0 || HV > 65535) return KDA_ERR_SHAPE;
   if (state_v_first != 0 && state_v_first != 1) return KDA_ERR_VALUE;
   const long long tokens = static_cast<long long>(B) * T * HV;
   const long long widest = static_cast<long long>(DK > DV ? DK : DV);

@@ -107,6 +107,7 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
   pp.tf = a.tf;
   pp.Hk = a.Hk;
+  pp.hk_magic = ((1ULL << 32) + a.H / a.Hk - 1) / (a.H / a.Hk);
 
   StateParams sp;
   sp.cu = nullptr; sp.cb = nullptr;
@@ -115,7 +116,7 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
   sp.o = a.o; sp.state = a.state;
   sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
-  sp.Hk = a.Hk; sp.vfirst = a.vfirst;
+  sp.Hk = a.Hk; sp.vfirst = a.vfirst; sp.hk_magic = pp.hk_magic;
   sp.nsl = a.DV / pl.dvs;
   sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;
 
@@ -190,6 +191,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
   pp.T = a.T; pp.H = a.H; pp.l2norm = a.l2norm; pp.scale = a.scale;
   pp.tf = a.tf;
   pp.Hk = a.Hk;
+  pp.hk_magic = ((1ULL << 32) + a.H / a.Hk - 1) / (a.H / a.Hk);
   pp.c0 = 0; pp.nchunks = static_cast<int>(total);
 
   StateParams sp;
@@ -199,7 +201,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
   sp.v = a.v; sp.ws = static_cast<const unsigned char*>(ws);
   sp.o = a.o; sp.state = a.state; sp.init = a.init;
   sp.T = a.T; sp.H = a.H; sp.DV = a.DV;
-  sp.Hk = a.Hk; sp.vfirst = a.vfirst;
+  sp.Hk = a.Hk; sp.vfirst = a.vfirst; sp.hk_magic = pp.hk_magic;
   sp.nsl = a.DV / pl.dvs;
   const int nheads = nseq * a.H;
   sp.xcd_map = (nheads % 8 == 0) ? 1 : 0;

@@ -208,7 +208,14 @@ struct PrepParams {
   const int* cu; const int* cb; int nseq;   // packed input
   Transforms tf;         // raw gate / raw beta (applied where decay and beta are read)
   int Hk;                // q/k heads: value head h reads q, k head h / (H / Hk)
+  unsigned long long hk_magic;   // ceil(2^32 / (H / Hk)): that head is (h * hk_magic) >> 32
 };
+
+// q/k head of value head h, (h * ceil(2^32 / g)) >> 32 = h / g exactly for
+// h, g < 2^16 (the error term h * e / 2^32, e < g, stays below 1 / g)
+__device__ __forceinline__ int qk_head(int h, unsigned long long magic) {
+  return static_cast<int>((static_cast<unsigned long long>(h) * magic) >> 32);
+}
 
 struct StateParams {
   const void* q; const void* k;   // raw q, k rows (records without Q, K tiles)
@@ -219,6 +226,7 @@ struct StateParams {
   int l2norm; float scale;   // q's row factor (raw rows)
   const int* cu; const int* cb;   // packed input (see PrepParams); state and o by sequence
   int Hk;                // q/k heads (see PrepParams)
+  unsigned long long hk_magic;
   int vfirst;            // init and state value-major [.., H, DV, DK]
 };
 
@@ -333,7 +341,9 @@ constexpr int prep_waves() {
        : RecLayout<DK, C, sizeof(typename OpOf<In>::T), false>::kRawK ? 8 : 6;
 }
 
-template <int DK, int C, typename In, int DECAY>
+// TF: the raw-gate / raw-beta transforms may be on (a separate instantiation,
+// so the plain inputs pay nothing for them)
+template <int DK, int C, typename In, int DECAY, bool TF>
 __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
   using KinvT = typename OpOf<In>::KinvT;
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   const int T = p.T, H = p.H;
   const int ch = blockIdx.x % p.nchunks, head = blockIdx.x / p.nchunks;
   const int b = head / H, h = head % H;
-  const int hk = h / (H / p.Hk);   // the q/k head of value head h
+  const int hk = qk_head(h, p.hk_magic);   // the q/k head of value head h
   int Lc;                 // tokens in the chunk
   long tok0;              // first token of the chunk
   if (p.cu) {
@@ -417,14 +427,16 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     }
     // raw gate: -exp(A_log) of the head; tokens past the sequence end keep a
     // zero decay (the chunk-end sums run over all C rows)
-    const float negA = p.tf.A_log ? -__expf(p.tf.A_log[h]) : 0.f;
+    const float negA = (TF && p.tf.A_log) ? -__expf(p.tf.A_log[h]) : 0.f;
     float bt = 0.f, G = 0.f;
     if (wave == 0 && lane < Lc) {
       const long off = (tok0 + lane) * H + h;
-      bt = beta_transform(act<In>::load1(gb + off), p.tf.beta_mode);
-      if (headdecay) {
-        G = act<In>::load1(gg + off);
-        if (p.tf.A_log) G = gate_decay(G, negA, p.tf.dt_bias ? p.tf.dt_bias[h] : 0.f, p.tf.lower);
+      bt = act<In>::load1(gb + off);
+      if (headdecay) G = act<In>::load1(gg + off);
+      if constexpr (TF) {
+        bt = beta_transform(bt, p.tf.beta_mode);
+        if (headdecay && p.tf.A_log)
+          G = gate_decay(G, negA, p.tf.dt_bias ? p.tf.dt_bias[h] : 0.f, p.tf.lower);
       }
     }
 #pragma unroll
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         } else {
           float gv[V];
           act<In>::load_vec(reinterpret_cast<const In*>(&rg[pp]), gv);
-          if (p.tf.A_log && r < Lc) {
+          if (TF && p.tf.A_log && r < Lc) {
             const float* bias = p.tf.dt_bias;
 #pragma unroll
             for (int e = 0; e < V; ++e)
@@ -1019,7 +1031,7 @@ void state_kernel(StateParams p) {
   }
   const int rowV = H * DV * AB;              // bytes between consecutive tokens of v
   const int rowK = p.Hk * DK * AB;           // ... of q and k (q/k heads)
-  const int hk = h / (H / p.Hk);             // the q/k head of value head h
+  const int hk = qk_head(h, p.hk_magic);     // the q/k head of value head h
   const int rowO = H * DV * 4;               // ... and of o
 
   RecFrags<DK, C, OpT> fr;
@@ -1521,12 +1533,16 @@ hipError_t launch_two(const PrepParams& pp, int nwg_prep, const StateParams& sp,
   if constexpr (LP::bytes(chan) > kMaxLds || LS::bytes > kMaxLds) {
     return hipErrorInvalidConfiguration;   // never instantiated as kernels
   } else {
-    auto fp = prep_kernel<DK, C, In, DECAY>;
+    auto fp0 = prep_kernel<DK, C, In, DECAY, false>;
+    auto fp1 = prep_kernel<DK, C, In, DECAY, true>;
     auto fs = state_kernel<DK, DVS, C, In, DECAY>;
+    const auto fp = (pp.tf.A_log || pp.tf.beta_mode) ? fp1 : fp0;
     static bool attr_set = false;   // per instantiation; benign race: the calls are idempotent
     hipError_t e = hipSuccess;
     if (!attr_set) {
-      e = set_max_lds(reinterpret_cast<const void*>(fp));
+      e = set_max_lds(reinterpret_cast<const void*>(fp0));
+      if (e != hipSuccess) return e;
+      e = set_max_lds(reinterpret_cast<const void*>(fp1));
       if (e != hipSuccess) return e;
       e = set_max_lds(reinterpret_cast<const void*>(fs));
       if (e != hipSuccess) return e;

@@ -44,8 +44,8 @@
  *    value-major [.., HV, DV, DK] (state_v_first = 1, TileOPs state_v_first);
  *    initial and final states use the same layout.  Other values:
  *    KDA_ERR_VALUE.
- *  - Supported sizes: DK, DV in {32, 64, 128}; B, H, HV >= 1 with HV % H
- *    == 0; T >= 0 with B*T*HV*max(DK,DV) < 2^31.
+ *  - Supported sizes: DK, DV in {32, 64, 128}; B, H >= 1; 1 <= HV <= 65535
+ *    with HV % H == 0; T >= 0 with B*T*HV*max(DK,DV) < 2^31.
  *  - Input transforms, the trailing (A_log, dt_bias, lower_bound, transforms)
  *    of every entry point (TileOPs "Linear Attention Operators", GDNFwdOp and
  *    KDAFwdOp: use_gate_in_kernel, lower_bound, use_beta_sigmoid_in_kernel,

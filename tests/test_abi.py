@@ -75,7 +75,7 @@ def chunked(L, **kw):
     (dict(tf=8), 4),                                             # 2 sigmoid without sigmoid
     (dict(tf=1, kind=1, decay=FAKE), 1),                         # raw gate without A_log
     # value heads: a multiple of the q/k heads; state layout flag 0 or 1
-    (dict(H=2, HV=3), 2), (dict(H=2, HV=0), 2), (dict(H=4, HV=2), 2),
+    (dict(H=2, HV=3), 2), (dict(H=2, HV=0), 2), (dict(H=4, HV=2), 2), (dict(HV=65536), 2),
     (dict(vf=2), 4), (dict(vf=-1), 4),
 ])
 def test_chunked_rejects_bad_arguments(L, kw, code):

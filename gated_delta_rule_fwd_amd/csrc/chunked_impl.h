@@ -541,6 +541,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 #pragma unroll
         for (int t = 0; t < 16; ++t) sum += static_cast<float>(sGst[(16 * i + t) * DK + c]);
         if (sum < kSteepBlockLogDecay) *s_flag = 1;
+        s_rsq[i * DK + c] = __expf(0.5f * sum);   // rs of the balanced operands (1b)
       }
       lds_barrier();
     }
@@ -564,13 +565,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         float a[16], kx[16], kin[16];
         float pre = 1.f;
         const bool bal = sizeof(OpT) == 2 && !steep;
-        float rs = 1.f;
-        if (bal) {
-          float tot = 0.f;
-#pragma unroll
-          for (int t = 0; t < 16; ++t) tot += static_cast<float>(sGst[(16 * i + t) * DK + c]);
-          rs = __expf(0.5f * tot);
-        }
+        const float rs = bal ? s_rsq[i * DK + c] : 1.f;
         const float irs = 1.f / rs;
         // Ka (k times the exclusive prefix) and Qa (q times the inclusive
         // one) replace k and q in place: fp16, or bf16 bit patterns when steep
@@ -603,7 +598,6 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
             // diagonal blocks pair a factor <= 1 with its inverse; balanced by
             // rs both stay within exp(+-8) for a block factor >= exp(-16),
             // which fp16 holds
-            s_rsq[i * DK + c] = rs;
 #pragma unroll
             for (int t = 0; t < 16; ++t)
               *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);

@@ -248,9 +248,17 @@ def stored_traffic(name):
 
 # kernel-name fragments of one call of each workload, as rocprofv3 prints them
 TRAFFIC_KERNELS = {
-    "gdn_d128": ["prep_kernel<128, 64, kda::bf16_t, 1>", "state_kernel<128, 64, 64, kda::bf16_t, 1>"],
-    "kda_d128": ["prep_kernel<128, 64, kda::bf16_t, 2>", "state_kernel<128, 32, 64, kda::bf16_t, 2>"],
+    "gdn_d128": ["prep_kernel<128, 64, kda::bf16_t, 1, false>", "state_kernel<128, 64, 64, kda::bf16_t, 1>"],
+    "kda_d128": ["prep_kernel<128, 64, kda::bf16_t, 2, false>", "state_kernel<128, 32, 64, kda::bf16_t, 2>"],
     "decode_d128": ["decode_kernel<128, 128, kda::bf16_t>"],
+}
+# Later workloads of the same run reuse some of these kernels (the grouped-head
+# and packed gdn calls, the raw-gate kda call): a workload's dispatches are
+# those before the first dispatch of the kernel named here.
+TRAFFIC_WINDOW_END = {
+    "gdn_d128": "prep_kernel<128, 64, kda::bf16_t, 2,",
+    "kda_d128": "prep_kernel<128, 64, kda::bf16_t, 2, true>",
+    "decode_d128": None,
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30   # the --calibrate-copy copies: 1 GiB read and 1 GiB written
@@ -265,13 +273,15 @@ def write_traffic(fetch_dir, write_dir):
     import glob
 
     def per_kernel(d, counter):
-        vals = {}
+        """[(dispatch id, kernel name, bytes)] in dispatch order"""
+        rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
                     if r["Counter_Name"] == counter:
-                        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024)
-        return vals
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                     float(r["Counter_Value"]) * 1024))
+        return sorted(rows)
 
     out = {"_comment": "HBM bytes per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                        "(KiB per dispatch), each scaled by the ratio of a plain 1 GiB device "
@@ -281,16 +291,18 @@ def write_traffic(fetch_dir, write_dir):
     scale = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         v = per_kernel(d, counter)
-        copies = [x for k, xs in v.items() if COPY_KERNEL in k for x in xs if x > COPY_BYTES / 2]
+        copies = [x for _, k, x in v if COPY_KERNEL in k and x > COPY_BYTES / 2]
         if not copies:
             raise SystemExit(f"no 1 GiB calibration copy found under {d}")
         scale[counter] = COPY_BYTES / (sum(copies) / len(copies))
         out[counter.lower() + "_scale"] = round(scale[counter], 4)
         for name, frags in TRAFFIC_KERNELS.items():
             ent = out.setdefault(name, {"kernels": frags})
+            end = TRAFFIC_WINDOW_END[name]
+            last = min([i for i, k, _ in v if end and end in k], default=None)
             total = 0.0
             for fr in frags:
-                xs = [x for k, xs in v.items() if fr in k for x in xs]
+                xs = [x for i, k, x in v if fr in k and (last is None or i < last)]
                 if not xs:
                     raise SystemExit(f"{counter}: no dispatch of {fr} under {d}")
                 total += sum(xs) / len(xs) * scale[counter]

@@ -129,6 +129,18 @@ __device__ __forceinline__ float beta_transform(float b, int mode) {
   return mode == 2 ? 2.f * s : s;
 }
 
+// Sum over the lanes that share lane % W (W = 8 or 16): within each 16-lane
+// row with DPP rotations, then across rows with the lane-swap moves.
+template <int W>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  auto ror = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  if constexpr (W == 8) x += ror(x, std::integral_constant<int, 0x128>{});   // row_ror:8
+  return xor32_sum(xor16_sum(x));
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) {
   // 1 / max(||x||_2, 1e-12): the hardware reciprocal square root (about
   // 1 ulp), capped where the norm is below 1e-12 (a NaN sum gives the cap)

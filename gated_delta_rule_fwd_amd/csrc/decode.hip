@@ -10,8 +10,9 @@
 // so the whole step needs one read and one write of S.  The kernel is bound
 // by HBM bandwidth: 2 * DK * DV * 4 bytes of state traffic per (batch, head)
 // against about 6 * DK * DV flops.  Every value column is independent given
-// the token vectors, so a workgroup takes CS of the DV columns of one
-// (batch, head): more, smaller workgroups keep more of the state in flight.
+// the token vectors, so a wave takes CS of the DV columns of one (batch, head)
+// with all their key rows in registers (32 KB of state in flight per wave at
+// DK = 128), and both column reductions stay inside the wave.
 #include "common.h"
 #include "launch.h"
 
@@ -23,67 +24,67 @@ constexpr int kThreads = 256;
 // Columns per workgroup.
 template <int DV> constexpr int decode_cols() { return DV > 64 ? 64 : DV; }
 
+// Key-major state [.., DK, DV]: one wave takes CS value columns of one
+// (batch, head) and all DK key rows.  A lane holds a float4 of columns in
+// rows rg + NRG i, so each row group reads whole CS-column row pieces; the
+// two reductions over rows run inside the wave (DPP and lane-swap moves), with
+// no LDS round trip and no barrier.  The token vectors go through the wave's
+// own LDS slice.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
-    Transforms tf, int Hk) {
+    Transforms tf, int Hk, int nunits) {
   constexpr int CS = decode_cols<DV>();
   constexpr int NSPLIT = DV / CS;
-  constexpr int NC4 = CS / 4;             // float4 column groups per state row
-  constexpr int NRG = kThreads / NC4;     // row groups
-  constexpr int RPT = DK / NRG;           // rows per thread
-  static_assert(RPT >= 1 && DK % NRG == 0 && DV % CS == 0, "shape");
+  constexpr int NC4 = CS / 4;             // float4 column groups: lanes per row
+  constexpr int NRG = 64 / NC4;           // row groups in the wave
+  constexpr int RPT = DK / NRG;           // rows per lane
+  static_assert(RPT >= 1 && DK % NRG == 0 && DV % CS == 0 && (NC4 == 8 || NC4 == 16), "shape");
   constexpr int NW = kThreads / 64;
 
-  __shared__ float s_q[DK], s_k[DK], s_gate[DK], s_v[CS];
-  __shared__ float s_red[3][NW];
-  __shared__ f32x4 s_part[2][NW][NC4];
+  __shared__ float s_q[NW][DK], s_k[NW][DK], s_gate[NW][DK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long bh = blockIdx.x / NSPLIT;
-  const int n0 = (blockIdx.x % NSPLIT) * CS;   // first value column of this workgroup
-  const int cg = tid % NC4, rg = tid / NC4;
+  const int unit = blockIdx.x * NW + wave;   // (batch, head, column block)
+  if (unit >= nunits) return;                 // whole waves only: no barrier below
+  const long bh = unit / NSPLIT;
+  const int n0 = (unit % NSPLIT) * CS;
+  const int cg = lane % NC4, rg = lane / NC4;
   float* S = state + bh * DK * DV + n0;
   const int h = static_cast<int>(bh % H);
-  const long bhk = (bh / H) * Hk + h / (H / Hk);   // q/k row of value head h
-  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
+  const long bhk = (bh / H) * Hk + h / (H / Hk);
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;
 
-  // Issue the state loads first: they are the bulk of the traffic.
   f32x4 st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int c = rg + NRG * i;
-    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + c * DV) + cg);
-  }
+  for (int i = 0; i < RPT; ++i)
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (rg + NRG * i) * DV) + cg);
 
-  // Token vectors; norms and q.k by block reduction.
+  float* sq_ = s_q[wave];
+  float* sk_ = s_k[wave];
+  float* sg_ = s_gate[wave];
   float pq = 0.f, pk = 0.f, pqk = 0.f;
-  for (int c = tid; c < DK; c += kThreads) {
+#pragma unroll
+  for (int c = lane; c < DK; c += 64) {
     const float qc = act<In>::load1(q + bhk * DK + c);
     const float kc = act<In>::load1(k + bhk * DK + c);
-    s_q[c] = qc;
-    s_k[c] = kc;
+    sq_[c] = qc;
+    sk_[c] = kc;
     float gc = 1.f;
     if (decay_kind == DECAY_CHANNEL) {
       float g = act<In>::load1(decay + bh * DK + c);
       if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h * DK + c] : 0.f, tf.lower);
       gc = __expf(g);
     }
-    s_gate[c] = gc;
+    sg_[c] = gc;
     pq += qc * qc; pk += kc * kc; pqk += qc * kc;
   }
-  for (int n = tid; n < CS; n += kThreads) s_v[n] = act<In>::load1(v + bh * DV + n0 + n);
   pq = group_sum<64>(pq); pk = group_sum<64>(pk); pqk = group_sum<64>(pqk);
-  if (lane == 0) { s_red[0][wave] = pq; s_red[1][wave] = pk; s_red[2][wave] = pqk; }
-  __syncthreads();
-  float sq = 0.f, sk = 0.f, sqk = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) { sq += s_red[0][w]; sk += s_red[1][w]; sqk += s_red[2][w]; }
-  const float iq = (l2norm ? inv_norm(sq) : 1.f) * scale;   // q_hat = q * iq
-  const float ik = l2norm ? inv_norm(sk) : 1.f;             // k_hat = k * ik
-  const float qk = sqk * iq * ik;                           // q_hat . k_hat
+  const float iq = (l2norm ? inv_norm(pq) : 1.f) * scale;
+  const float ik = l2norm ? inv_norm(pk) : 1.f;
+  const float qk = pqk * iq * ik;
   const float b = beta_transform(act<In>::load1(beta + bh), tf.beta_mode);
   float ghead = 1.f;
   if (decay_kind == DECAY_HEAD) {
@@ -91,45 +92,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h] : 0.f, tf.lower);
     ghead = __expf(g);
   }
+  // the wave's own LDS writes land before its lanes read each other's
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
 
-  // Partial reads r = S^T k_hat and y = S^T (gate * q_hat) over this thread's rows.
   f32x4 r = {0, 0, 0, 0}, y = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int c = rg + NRG * i;
-    const float kc = s_k[c] * ik;
-    const float qc = s_q[c] * iq * s_gate[c] * ghead;
+    const float kc = sk_[c] * ik;
+    const float qc = sq_[c] * iq * sg_[c] * ghead;
     r += st[i] * kc;
     y += st[i] * qc;
   }
-  // Reduce over the row groups that share a wave, then across waves.
+  // sum over the NRG row groups: lanes with equal lane % NC4
 #pragma unroll
-  for (int off = NC4; off < 64; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      r[e] += __shfl_xor(r[e], off, 64);
-      y[e] += __shfl_xor(y[e], off, 64);
-    }
+  for (int e = 0; e < 4; ++e) {
+    r[e] = rowgroup_sum<NC4>(r[e]);
+    y[e] = rowgroup_sum<NC4>(y[e]);
   }
-  if (lane < NC4) { s_part[0][wave][cg] = r; s_part[1][wave][cg] = y; }
-  __syncthreads();
-  r = s_part[0][0][cg];
-  y = s_part[1][0][cg];
+  float vc[4];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) { r += s_part[0][w][cg]; y += s_part[1][w][cg]; }
-
+  for (int e = 0; e < 4; ++e) vc[e] = act<In>::load1(v + bh * DV + n0 + 4 * cg + e);
   f32x4 delta;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) delta[e] = b * (s_v[4 * cg + e] - r[e]);
-  if (rg == 0) {
-    const f32x4 out = y + qk * delta;
-    *reinterpret_cast<f32x4*>(o + bh * DV + n0 + 4 * cg) = out;
-  }
+  for (int e = 0; e < 4; ++e) delta[e] = b * (vc[e] - r[e]);
+  if (rg == 0) *reinterpret_cast<f32x4*>(o + bh * DV + n0 + 4 * cg) = y + qk * delta;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int c = rg + NRG * i;
-    const float gc = s_gate[c] * ghead;
-    const float kc = s_k[c] * ik;
+    const float gc = sg_[c] * ghead;
+    const float kc = sk_[c] * ik;
     const f32x4 ns = st[i] * gc + kc * delta;
     __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV) + cg);
   }
@@ -237,14 +230,15 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
 #define KDA_DECODE_CASE(dk, dv)                                                              \
   if (a.DK == dk && a.DV == dv) {                                                            \
     const dim3 grid(a.B * a.H * (dv / decode_cols<dv>()));                                   \
+    const int units = a.B * a.H * (dv / decode_cols<dv>());                                  \
     if (a.vfirst)                                                                            \
       decode_vm_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,     \
                                                           a.state, a.o, a.scale, a.l2norm,   \
                                                           a.H, a.tf, a.Hk);                  \
     else                                                                                     \
-      decode_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,        \
-                                                       a.state, a.o, a.scale, a.l2norm, a.H, \
-                                                       a.tf, a.Hk);                          \
+      decode_kernel<dk, dv, In><<<dim3((units + 3) / 4), block, 0, s>>>(                     \
+          q, k, v, be, de, a.decay_kind, a.state, a.o, a.scale, a.l2norm, a.H, a.tf, a.Hk,   \
+          units);                                                                            \
     return hipGetLastError();                                                                \
   }
   KDA_DECODE_CASE(32, 32) KDA_DECODE_CASE(32, 64) KDA_DECODE_CASE(32, 128)

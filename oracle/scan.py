@@ -160,15 +160,19 @@ def kda_decode(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=Tr
 
 def kda_scan_heads(q, k, v, beta, decay, initial_state, heads, softmax_scale=None,
                    use_qk_l2norm=True):
-    """The scan restricted to a list of (b, h) pairs: each head's recurrence
-    is independent of every other head, so a sample of heads can be checked
-    at full sequence length.  Returns (o [n, T, DV], S [n, DK, DV])."""
+    """The scan restricted to a list of (b, h) pairs, h a value head: each
+    head's recurrence is independent of every other head, so a sample of
+    heads can be checked at full sequence length.  With HV value heads over H
+    q/k heads, value head h reads q/k head h // (HV // H) (expand_qk_heads).
+    Returns (o [n, T, DV], S [n, DK, DV])."""
     outs, states = [], []
+    group = v.shape[2] // q.shape[2]
     for (b, h) in heads:
         sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        qsl = (slice(b, b + 1), slice(None), slice(h // group, h // group + 1))
         dec = None if decay is None else decay[sl]
         init = None if initial_state is None else initial_state[b:b + 1, h:h + 1]
-        o, S = kda_scan(q[sl], k[sl], v[sl], beta[sl], dec, init, softmax_scale,
+        o, S = kda_scan(q[qsl], k[qsl], v[sl], beta[sl], dec, init, softmax_scale,
                         use_qk_l2norm)
         outs.append(o[0, :, 0])
         states.append(S[0, 0])

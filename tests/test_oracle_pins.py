@@ -147,3 +147,19 @@ def test_value_heads_share_their_groups_qk_head():
     # and HV = H is the plain scan, head by head
     o1, _ = kda_scan(q[:, :, 1:2], k[:, :, 1:2], v[:, :, 2:3], beta[:, :, 2:3], decay[:, :, 2:3])
     assert np.max(np.abs(o1[:, :, 0] - o[:, :, 2])) < 1e-14
+
+
+def test_head_sample_with_grouped_value_heads():
+    # the sampled-head scan reads the q/k head of each value head
+    rng = np.random.default_rng(12)
+    B, T, H, HV, DK, DV = 2, 7, 2, 6, 8, 4
+    q, k = rng.normal(size=(B, T, H, DK)), rng.normal(size=(B, T, H, DK))
+    v = rng.normal(size=(B, T, HV, DV))
+    beta = rng.uniform(0.1, 0.9, size=(B, T, HV))
+    decay = -rng.uniform(0.01, 0.3, size=(B, T, HV))
+    o, S = kda_scan(q, k, v, beta, decay)
+    heads = [(0, 0), (1, 4), (0, 2), (1, 5)]
+    o_s, S_s = kda_scan_heads(q, k, v, beta, decay, None, heads)
+    for i, (b, h) in enumerate(heads):
+        assert np.max(np.abs(o_s[i] - o[b, :, h])) < 1e-14
+        assert np.max(np.abs(S_s[i] - S[b, h])) < 1e-14

@@ -413,6 +413,14 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   // ============ phase 1: normalised q, k rows; gates ============
   {
     uint4 rq[NP], rk[NP], rg[NP];
+    // raw per-channel gate: this thread's V channels of dt_bias (a thread
+    // keeps its channel segment tid % LPR in every pass), loaded once
+    float gbias[chan && TF ? V : 1];
+    if constexpr (chan && TF) {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        gbias[e] = (p.tf.A_log && p.tf.dt_bias) ? p.tf.dt_bias[h * DK + (tid % LPR) * V + e] : 0.f;
+    }
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int r = pp * RPP + tid / LPR, seg = tid % LPR;
@@ -479,11 +487,11 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         } else {
           float gv[V];
           act<In>::load_vec(reinterpret_cast<const In*>(&rg[pp]), gv);
-          if (TF && p.tf.A_log && r < Lc) {
-            const float* bias = p.tf.dt_bias;
+          if constexpr (TF) {
+            if (p.tf.A_log && r < Lc) {
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-              gv[e] = gate_decay(gv[e], negA, bias ? bias[h * DK + seg * V + e] : 0.f, p.tf.lower);
+              for (int e = 0; e < V; ++e) gv[e] = gate_decay(gv[e], negA, gbias[e], p.tf.lower);
+            }
           }
           store16<OpT>(sGst + r * DK + seg * V, gv);
         }

@@ -23,6 +23,11 @@ constexpr int kThreads = 256;
 
 // Columns per workgroup.
 template <int DV> constexpr int decode_cols() { return DV > 64 ? 64 : DV; }
+// Columns per workgroup of the value-major kernel: at least one pass of
+// DK / 4-lane columns, at most 32.
+template <int DK, int DV> constexpr int decode_vm_cols() {
+  return DV < 32 ? DV : (32 > 1024 / DK ? 32 : 1024 / DK);
+}
 
 // Key-major state [.., DK, DV]: one wave takes CS value columns of one
 // (batch, head) and all DK key rows.  A lane holds a float4 of columns in
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void decode_vm_kernel(
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
     Transforms tf, int Hk) {
-  constexpr int CS = decode_cols<DV>();
+  constexpr int CS = decode_vm_cols<DK, DV>();
   constexpr int NSPLIT = DV / CS;
   constexpr int LPC = DK / 4;             // lanes per value column
   constexpr int CPP = kThreads / LPC;     // columns per pass
@@ -229,7 +234,7 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
   const In* de = static_cast<const In*>(a.decay);
 #define KDA_DECODE_CASE(dk, dv)                                                              \
   if (a.DK == dk && a.DV == dv) {                                                            \
-    const dim3 grid(a.B * a.H * (dv / decode_cols<dv>()));                                   \
+    const dim3 grid(a.B * a.H * (dv / decode_vm_cols<dk, dv>()));                            \
     const int units = a.B * a.H * (dv / decode_cols<dv>());                                  \
     if (a.vfirst)                                                                            \
       decode_vm_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,     \

@@ -280,6 +280,59 @@ def pin_one_hot_keys_gla(scan):
     return max(worst, np.abs(Sm - S[0, 0]).max())
 
 
+def pin_nonpositive_scale_means_default(scan):
+    """A scale that is zero, negative or NaN means the default DK**-0.5
+    (TileOPs "Linear Attention Operators", GLA ops: a non-positive scale
+    selects the default; ejkernel kda parameter list: no scale given means
+    the inverse square root of the head size).  Compared with the scan at an
+    explicit DK**-0.5, and with queries pre-multiplied by it at scale 1."""
+    rng = _rng(24)
+    DK = 16
+    q, k, v, beta, g, S0 = _inputs(rng, 1, 7, 2, DK, 3, "head")
+    o_ref, S_ref = scan(q, k, v, beta, g, S0, softmax_scale=0.25)
+    # the same through a pre-scaled query: the norm removes the factor, so
+    # the query is normalised first and given to the scan without the norm
+    qn, kn = _unit(q), _unit(k)
+    o_pre, _ = scan(qn * 0.25, kn, v, beta, g, S0, softmax_scale=1.0, use_qk_l2norm=False)
+    worst = np.abs(o_pre - o_ref).max()
+    for s in (0.0, -1.0, -0.0, float("nan"), None):
+        o, S = scan(q, k, v, beta, g, S0, softmax_scale=s)
+        worst = max(worst, np.abs(o - o_ref).max(), np.abs(S - S_ref).max())
+    return worst
+
+
+def _torch_normalize(x):
+    """torch.nn.functional.normalize(x, p=2, dim=-1), the routine the
+    kda-neuron-kernels README names for the caller's L2 norm (its default
+    eps is 1e-12), run on the CPU in float64."""
+    import torch
+    return torch.nn.functional.normalize(torch.from_numpy(x), p=2.0, dim=-1).numpy()
+
+
+def pin_l2_floor_matches_library_normalize(scan):
+    """The in-kernel L2 norm is the library routine F.normalize: rows of
+    ordinary norm, of tiny norm (1e-9, still normalised to unit length), of
+    norm below the 1e-12 floor (divided by the floor, not normalised) and
+    all-zero rows (left zero) give the same result as q, k normalised by
+    that routine and passed with the norm off.  A zero key writes nothing
+    and a zero query reads nothing."""
+    rng = _rng(25)
+    q, k, v, beta, g, S0 = _inputs(rng, 1, 8, 2, 6, 3, "channel")
+    q[0, 1, 0] *= 1e-9 / np.linalg.norm(q[0, 1, 0])
+    k[0, 2, 1] *= 1e-9 / np.linalg.norm(k[0, 2, 1])
+    q[0, 3, 1] *= 3e-13 / np.linalg.norm(q[0, 3, 1])
+    k[0, 4, 0] *= 5e-13 / np.linalg.norm(k[0, 4, 0])
+    q[0, 5, 0] = 0.0
+    k[0, 6, 1] = 0.0
+    o1, S1 = scan(q, k, v, beta, g, S0, softmax_scale=0.5, use_qk_l2norm=True)
+    o2, S2 = scan(_torch_normalize(q), _torch_normalize(k), v, beta, g, S0, softmax_scale=0.5,
+                  use_qk_l2norm=False)
+    worst = max(np.abs(o1 - o2).max(), np.abs(S1 - S2).max())
+    # the zero query reads nothing at its token
+    worst = max(worst, np.abs(o1[0, 5, 0]).max())
+    return worst
+
+
 PINS = [
     pin_single_step_closed_form,
     pin_beta_zero_readout,
@@ -293,4 +346,6 @@ PINS = [
     pin_l2norm_idempotent,
     pin_gate_plumbing,
     pin_one_hot_keys_gla,
+    pin_nonpositive_scale_means_default,
+    pin_l2_floor_matches_library_normalize,
 ]

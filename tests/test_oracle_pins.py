@@ -163,3 +163,48 @@ def test_head_sample_with_grouped_value_heads():
     for i, (b, h) in enumerate(heads):
         assert np.max(np.abs(o_s[i] - o[b, :, h])) < 1e-14
         assert np.max(np.abs(S_s[i] - S[b, h])) < 1e-14
+
+
+# ---- planted mistakes in the query scale and the L2 norm ----
+
+def _scale_taken_literally(softmax_scale, dk):
+    return dk ** -0.5 if softmax_scale is None else float(softmax_scale)
+
+
+def _scale_nan_only_default(softmax_scale, dk):
+    # non-positive values taken literally, only NaN and None mean the default
+    if softmax_scale is None or softmax_scale != softmax_scale:
+        return dk ** -0.5
+    return float(softmax_scale)
+
+
+def _l2_eps_added(x, eps=1e-12):
+    return x / (np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + eps)
+
+
+def _l2_no_floor(x, eps=1e-12):
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def _l2_floor_too_large(x, eps=1e-12):
+    return x / np.maximum(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)), 1e-6)
+
+
+PREP_MUTANTS = [("resolve_scale", _scale_taken_literally), ("resolve_scale", _scale_nan_only_default),
+                ("l2_normalize", _l2_eps_added), ("l2_normalize", _l2_no_floor),
+                ("l2_normalize", _l2_floor_too_large)]
+
+
+@pytest.mark.parametrize("attr,mutant", PREP_MUTANTS, ids=lambda m: getattr(m, "__name__", m))
+def test_pins_catch_planted_prep_mistakes(monkeypatch, attr, mutant):
+    monkeypatch.setattr(scan_mod, attr, mutant)
+    failures = []
+    for pin in pins.PINS:
+        try:
+            err = pin(kda_scan)
+        except Exception:
+            err = np.inf
+        if not err < TOL:
+            failures.append(pin.__name__)
+    assert failures, f"no pin caught {mutant.__name__}"

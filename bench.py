@@ -116,7 +116,12 @@ def time_chunked(w, steps, warmup, dev, raw=False):
         d = to_dev(make_inputs(w), dev)
         args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
         tkw = {}
-    call = lambda: fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs, **tkw)
+    # the caller-owned workspace, allocated once outside the timed calls
+    from gated_delta_rule_fwd_amd import chunked_workspace_bytes
+    ws = torch.empty(chunked_workspace_bytes(w.B, w.T, w.H, w.hv, w.DK, w.DV, args[0].dtype,
+                                             w.decay_kind, w.chunk), dtype=torch.uint8, device=dev)
+    call = lambda: fwd_chunked(*args, chunk_size=w.chunk, out=o, final_state=fs, workspace=ws,
+                               **tkw)
     warm_up(call, warmup)
     # Events on torch's current stream, which is the stream the library launches on.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -162,8 +167,11 @@ def time_chunked_varlen(w, steps, warmup, dev):
     o = torch.empty((1, tot, w.H, w.DV), device=dev, dtype=torch.float32)
     fs = torch.empty((VARLEN_SEQS, w.H, w.DK, w.DV), device=dev, dtype=torch.float32)
     cu_dev = cu.to(dev)
+    from gated_delta_rule_fwd_amd.kda import chunked_varlen_workspace_bytes
+    nws = chunked_varlen_workspace_bytes(cu, w.H, w.hv, w.DK, w.DV, q.dtype, w.decay_kind, w.chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     call = lambda: fwd_chunked_varlen(q, k, v, be, cu_dev, decay=de, initial_state=s0,
-                                      chunk_size=w.chunk, out=o, final_state=fs)
+                                      chunk_size=w.chunk, out=o, final_state=fs, workspace=ws)
     warm_up(call, warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]

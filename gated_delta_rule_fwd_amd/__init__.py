@@ -5,6 +5,7 @@ exports ``kda_fwd_chunked``, ``kda_fwd_chunked_varlen``, ``kda_fwd_recurrent`` a
 ``kda_decode_step``
 (declared in ``include/kda.h``); this package binds them for torch tensors.
 """
-from .kda import (KdaError, decode_step, fwd_chunked, fwd_chunked_varlen, fwd_recurrent,  # noqa: F401
+from .kda import (KdaError, chunked_workspace_bytes, decode_step, fwd_chunked,  # noqa: F401
+                  fwd_chunked_varlen, fwd_recurrent,
                   lib,
                   DECAY_CHANNEL, DECAY_HEAD, DECAY_NONE, KDA_BF16, KDA_F32, LIB_PATH)

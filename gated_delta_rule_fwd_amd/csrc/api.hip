@@ -86,6 +86,21 @@ FwdArgs make_args(const void* q, const void* k, const void* v, const void* beta,
 
 int to_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
+// Bytes of the chunked records for `chunks` chunk indices of `heads` value
+// heads, 0 for an unsupported shape.
+size_t records_bytes(long chunks, long heads, int DK, int DV, int dtype, int decay_kind, int chunk) {
+  if (!chunk_ok(chunk) || chunked_lds_bytes(DK, DV, chunk, dtype, decay_kind) == 0) return 0;
+  return chunked_record_bytes(DK, chunk, dtype, decay_kind) * static_cast<size_t>(chunks) *
+         static_cast<size_t>(heads);
+}
+
+bool ws_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Chunk offsets after the varlen records, 16-byte aligned.
+size_t varlen_offsets_at(size_t recs) { return (recs + 15) & ~static_cast<size_t>(15); }
+
 }  // namespace
 
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s) {
@@ -106,7 +121,7 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
                     int B, int T, int H, int HV, int DK, int DV, int dtype,
                     float softmax_scale, int use_qk_l2norm, int state_v_first, int chunk_size,
                     const float* A_log, const float* dt_bias, float lower_bound, int transforms,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype,
                              state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
@@ -119,11 +134,15 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,
                                                  static_cast<long>(B) * HV * DK * DV, s));
   }
+  // the least workspace: one chunk index of every head
+  const size_t least = kda::records_bytes(1, static_cast<long>(B) * HV, DK, DV, dtype, decay_kind,
+                                          chunk_size);
+  if (!workspace || !kda::ws_aligned(workspace) || workspace_bytes < least) return KDA_ERR_WORKSPACE;
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
                                         final_state, B, T, H, HV, DK, DV, dtype, softmax_scale,
                                         use_qk_l2norm, state_v_first, chunk_size,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
-  return kda::to_status(kda::launch_chunked(a, s));
+  return kda::to_status(kda::launch_chunked(a, workspace, workspace_bytes, s));
 }
 
 int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* beta,
@@ -133,8 +152,9 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            int T, int H, int HV, int DK, int DV, int dtype,
                            float softmax_scale, int use_qk_l2norm, int state_v_first,
                            int chunk_size,
-                    const float* A_log, const float* dt_bias, float lower_bound, int transforms,
-                    void* stream) {
+                           const float* A_log, const float* dt_bias, float lower_bound,
+                           int transforms, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   int st = kda::check_common(q, k, v, beta, decay, decay_kind, 1, T, H, HV, DK, DV, dtype,
                              state_v_first);
   if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
@@ -151,11 +171,43 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
     return kda::to_status(kda::launch_state_copy(initial_state, final_state,
                                                  static_cast<long>(N) * HV * DK * DV, s));
   }
+  if (!workspace || !kda::ws_aligned(workspace) ||
+      workspace_bytes < kda_fwd_chunked_varlen_workspace_bytes(cu_seqlens_host, N, H, HV, DK, DV,
+                                                               dtype, decay_kind, chunk_size))
+    return KDA_ERR_WORKSPACE;
   const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
                                         final_state, 1, T, H, HV, DK, DV, dtype, softmax_scale,
                                         use_qk_l2norm, state_v_first, chunk_size,
                                         kda::make_tf(A_log, dt_bias, lower_bound, transforms));
-  return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, s));
+  return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, workspace, s));
+}
+
+size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int HV, int DK, int DV, int dtype,
+                                       int decay_kind, int chunk_size) {
+  if (B < 1 || T < 1 || H < 1 || HV < 1 || HV % H != 0) return 0;
+  if (!kda::dim_ok(DK) || !kda::dim_ok(DV) || (dtype != KDA_F32 && dtype != KDA_BF16)) return 0;
+  if (decay_kind < KDA_DECAY_NONE || decay_kind > KDA_DECAY_CHANNEL || !kda::chunk_ok(chunk_size)) return 0;
+  const long chunks = (static_cast<long>(T) + chunk_size - 1) / chunk_size;
+  return kda::records_bytes(chunks, static_cast<long>(B) * HV, DK, DV, dtype, decay_kind, chunk_size);
+}
+
+size_t kda_fwd_chunked_varlen_workspace_bytes(const int* cu_seqlens_host, int N, int H, int HV,
+                                              int DK, int DV, int dtype, int decay_kind,
+                                              int chunk_size) {
+  if (!cu_seqlens_host || N < 1 || H < 1 || HV < 1 || HV % H != 0) return 0;
+  if (!kda::dim_ok(DK) || !kda::dim_ok(DV) || (dtype != KDA_F32 && dtype != KDA_BF16)) return 0;
+  if (decay_kind < KDA_DECAY_NONE || decay_kind > KDA_DECAY_CHANNEL || !kda::chunk_ok(chunk_size)) return 0;
+  if (cu_seqlens_host[0] != 0) return 0;
+  long chunks = 0;
+  for (int n = 0; n < N; ++n) {
+    const long len = static_cast<long>(cu_seqlens_host[n + 1]) - cu_seqlens_host[n];
+    if (len < 0) return 0;
+    chunks += (len + chunk_size - 1) / chunk_size;
+  }
+  if (chunks == 0) return 0;
+  const size_t recs = kda::records_bytes(chunks, HV, DK, DV, dtype, decay_kind, chunk_size);
+  if (recs == 0) return 0;
+  return kda::varlen_offsets_at(recs) + (static_cast<size_t>(N) + 1) * sizeof(int);
 }
 
 int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
@@ -209,10 +261,11 @@ const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported head size, chunk size, dtype or decay kind";
     case KDA_ERR_VALUE: return "invalid transform flags, lower bound or state layout";
     case KDA_ERR_HIP: return "HIP runtime error at launch";
+    case KDA_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned or too small";
   }
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 103; }
+int kda_abi_version(void) { return 200; }
 
 }  // extern "C"

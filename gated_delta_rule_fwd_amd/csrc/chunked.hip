@@ -1,12 +1,7 @@
 // Host planning of the chunked forward: value-slice width, grids, the
-// workspace that carries the per-chunk records from the prep kernel to the
-// state kernel, and dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
-#include <stdlib.h>
-
-#include <map>
-#include <mutex>
-#include <utility>
-
+// segments of chunks that the caller's workspace holds the records of (the
+// prep kernel writes one record per chunk, the state kernel reads it), and
+// dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
 #include "chunked_impl.h"
 
 namespace kda {
@@ -31,39 +26,6 @@ Plan plan_for(int B, int H, int DK, int DV, int C, int dtype, bool chan) {
   return Plan{0, 0};
 }
 
-// Workspace: one device buffer per (device, stream), grown on demand and kept
-// until the process ends.  Work on one stream runs in order, so a stream's
-// buffer is never used by two calls at once; calls on different streams use
-// different buffers.
-hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> cache;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  auto& ent = cache[{dev, s}];
-  if (ent.second < bytes) {
-    if (ent.first) {
-      // the old buffer may still be read by this stream's earlier work
-      e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return e;
-      e = hipFree(ent.first);
-      ent = {nullptr, 0};
-      if (e != hipSuccess) return e;
-    }
-    const size_t want = bytes + bytes / 4;   // headroom for nearby sizes
-    e = hipMalloc(&ent.first, want);
-    if (e != hipSuccess) {
-      ent = {nullptr, 0};
-      return e;
-    }
-    ent.second = want;
-  }
-  *out = ent.first;
-  return hipSuccess;
-}
-
 }  // namespace
 
 size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind) {
@@ -72,21 +34,24 @@ size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind) {
   return a.dvs == 0 ? 0 : a.lds;
 }
 
-// Chunks per launch pair.  Long inputs are processed in segments of chunks
-// (the state kernel of one segment hands its final state to the next) so that
-// the workspace holds the records of one segment only: at most 1 GiB by
-// default, KDA_CHUNKED_SEGMENT_MB (MiB) overrides it.
-int segment_chunks(int nchunks, int nheads, size_t rec) {
-  const char* env = getenv("KDA_CHUNKED_SEGMENT_MB");
-  const long mb = env ? atol(env) : 0;
-  const long budget = (mb > 0 ? mb : 1024L) << 20;
-  long seg = budget / static_cast<long>(rec * nheads);
+size_t chunked_record_bytes(int DK, int chunk, int dtype, int decay_kind) {
+  const bool chan = decay_kind == DECAY_CHANNEL;
+  return dtype == 0 ? chunked::record_bytes<4>(DK, chunk, chan) : chunked::record_bytes<2>(DK, chunk, chan);
+}
+
+// Chunks per launch pair: as many as the workspace holds the records of
+// (every head of a chunk index takes one record), at least 1, at most all.
+// Long inputs with a small workspace are processed in segments of chunks; the
+// state kernel of one segment hands its final state to the next.
+int segment_chunks(int nchunks, int nheads, size_t rec, size_t ws_bytes) {
+  const size_t per = rec * static_cast<size_t>(nheads);
+  size_t seg = per ? ws_bytes / per : 0;
   if (seg < 1) seg = 1;
-  if (seg > nchunks) seg = nchunks;
+  if (seg > static_cast<size_t>(nchunks)) seg = nchunks;
   return static_cast<int>(seg);
 }
 
-hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_chunked(const FwdArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   const bool chan = a.decay_kind == DECAY_CHANNEL;
   const Plan pl = plan_for(a.B, a.H, a.DK, a.DV, a.chunk, a.dtype, chan);
   if (pl.dvs == 0) return hipErrorInvalidConfiguration;
@@ -95,10 +60,8 @@ hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const size_t rec = a.dtype == 0 ? chunked::record_bytes<4>(a.DK, a.chunk, chan)
                                   : chunked::record_bytes<2>(a.DK, a.chunk, chan);
   if (rec == 0) return hipErrorInvalidConfiguration;
-  const int seg = segment_chunks(nchunks, nheads, rec);
-  void* ws = nullptr;
-  hipError_t e = workspace(s, rec * seg * static_cast<size_t>(nheads), &ws);
-  if (e != hipSuccess) return e;
+  const int seg = segment_chunks(nchunks, nheads, rec, ws_bytes);
+  hipError_t e = hipSuccess;
 
   PrepParams pp;
   pp.cu = nullptr; pp.cb = nullptr; pp.nseq = a.B;
@@ -162,7 +125,7 @@ __global__ void chunk_offsets_kernel(const int* __restrict__ cu, int* __restrict
 }  // namespace
 
 hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int* cu_host, int nseq,
-                                 hipStream_t s) {
+                                 void* ws, hipStream_t s) {
   const bool chan = a.decay_kind == DECAY_CHANNEL;
   const Plan pl = plan_for(nseq, a.H, a.DK, a.DV, a.chunk, a.dtype, chan);
   if (pl.dvs == 0) return hipErrorInvalidConfiguration;
@@ -172,9 +135,7 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
                                   : chunked::record_bytes<2>(a.DK, a.chunk, chan);
   if (rec == 0) return hipErrorInvalidConfiguration;
   const size_t recs = rec * static_cast<size_t>(total) * a.H;
-  void* ws = nullptr;
-  hipError_t e = workspace(s, recs + (static_cast<size_t>(nseq) + 1) * sizeof(int), &ws);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   int* cb = reinterpret_cast<int*>(static_cast<unsigned char*>(ws) + recs);
   chunk_offsets_kernel<<<dim3(1), dim3(64), 0, s>>>(cu_dev, cb, nseq, a.chunk);
   e = hipGetLastError();

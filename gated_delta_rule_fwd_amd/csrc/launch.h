@@ -30,13 +30,18 @@ struct FwdArgs {
 // Each launcher assumes the front end has validated the arguments.
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t s);
-hipError_t launch_chunked(const FwdArgs& a, hipStream_t s);
+// ws: the caller's workspace of ws_bytes (at least one chunk index's
+// records, 16-byte aligned); fewer bytes than all records: segments of chunks.
+hipError_t launch_chunked(const FwdArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 // Packed variable-length input: a.B is unused; nseq sequences at the token
-// offsets cu (device) / cu_host (host, the same N + 1 values).
+// offsets cu (device) / cu_host (host, the same N + 1 values); ws holds the
+// records of every chunk, then the nseq + 1 chunk offsets.
 hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int* cu_host, int nseq,
-                                 hipStream_t s);
+                                 void* ws, hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
 // LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.
 size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind);
+// Workspace bytes of one chunk's record (one head), 0 if unsupported.
+size_t chunked_record_bytes(int DK, int chunk, int dtype, int decay_kind);
 
 }  // namespace kda

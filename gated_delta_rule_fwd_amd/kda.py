@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 DECAY_NONE, DECAY_HEAD, DECAY_CHANNEL = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
-          4: "KDA_ERR_VALUE", 5: "KDA_ERR_HIP"}
+          4: "KDA_ERR_VALUE", 5: "KDA_ERR_HIP", 6: "KDA_ERR_WORKSPACE"}
 TF_GATE, TF_LOWER_BOUND, TF_BETA_SIGMOID, TF_NEG_EIGVAL = 1, 2, 4, 8
 
 _lib = None
@@ -41,13 +41,18 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m gated_delta_rule_fwd_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
-        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
-                                      i, i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp]
+                                      i, i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp, sz, vp]
         L.kda_fwd_chunked.restype = i
+        L.kda_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+        L.kda_fwd_chunked_workspace_bytes.restype = sz
         L.kda_fwd_chunked_varlen.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i,
-                                             i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp]
+                                             i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp, sz,
+                                             vp]
         L.kda_fwd_chunked_varlen.restype = i
+        L.kda_fwd_chunked_varlen_workspace_bytes.argtypes = [vp, i, i, i, i, i, i, i, i]
+        L.kda_fwd_chunked_varlen_workspace_bytes.restype = sz
         L.kda_fwd_recurrent.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
                                         i, i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_fwd_recurrent.restype = i
@@ -138,6 +143,34 @@ def _transforms(kind, H, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_boun
     return _ptr(A_log), _ptr(dt_bias), lb, flags
 
 
+def _workspace(workspace, nbytes, dev):
+    """The caller's workspace (a device tensor of at least the bytes the
+    library asks for; any dtype, contiguous), or a fresh torch.empty one."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), device=dev, dtype=torch.uint8)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return workspace
+
+
+def chunked_workspace_bytes(B, T, H, HV, DK, DV, dtype, decay_kind, chunk_size=64):
+    """Bytes of workspace for one launch pair of fwd_chunked over the whole
+    sequence (kda_fwd_chunked_workspace_bytes); ``dtype`` a torch dtype or
+    the library's code.  With T = chunk_size: the least it accepts."""
+    code = dtype if isinstance(dtype, int) else (KDA_F32 if dtype == torch.float32 else KDA_BF16)
+    return int(lib().kda_fwd_chunked_workspace_bytes(B, T, H, HV, DK, DV, code, decay_kind,
+                                                     chunk_size))
+
+
+def chunked_varlen_workspace_bytes(cu_seqlens, H, HV, DK, DV, dtype, decay_kind, chunk_size=64):
+    """Bytes of workspace fwd_chunked_varlen needs for these offsets
+    (kda_fwd_chunked_varlen_workspace_bytes; cu_seqlens N + 1 int offsets)."""
+    cu = torch.as_tensor(cu_seqlens).to("cpu", torch.int32).contiguous()
+    code = dtype if isinstance(dtype, int) else (KDA_F32 if dtype == torch.float32 else KDA_BF16)
+    return int(lib().kda_fwd_chunked_varlen_workspace_bytes(_ptr(cu), cu.numel() - 1, H, HV, DK,
+                                                            DV, code, decay_kind, chunk_size))
+
+
 def _state_shape(N, HV, DK, DV, state_v_first):
     return (N, HV, DV, DK) if state_v_first else (N, HV, DK, DV)
 
@@ -166,7 +199,8 @@ def _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first=False):
 def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
                 use_qk_l2norm=True, chunk_size=64, out=None, final_state=None,
                 state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
-                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                workspace=None):
     """Chunked forward.  q, k [B,T,H,DK]; v [B,T,HV,DV] (HV a multiple of H);
     beta [B,T,HV]; decay None, [B,T,HV] or [B,T,HV,DK].  Returns (o [B,T,HV,DV]
     fp32, final_state fp32), states [B,HV,DK,DV], or [B,HV,DV,DK] with
@@ -177,7 +211,12 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
     -exp(A_log) * softplus(gate + dt_bias), floored at ``lower_bound`` if
     given (A_log [HV] fp32; dt_bias [HV], or [HV, DK] for a per-channel gate,
     fp32 or None); ``use_beta_sigmoid_in_kernel`` reads beta as logits
-    (sigmoid, or 2 * sigmoid with ``allow_neg_eigval``)."""
+    (sigmoid, or 2 * sigmoid with ``allow_neg_eigval``).
+
+    ``workspace``: a device tensor the library may use for the per-chunk
+    records (chunked_workspace_bytes gives the size for one launch pair; a
+    smaller one, down to one chunk of every head, processes the sequence in
+    segments).  None: torch.empty of the full size."""
     B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first)
     tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
@@ -187,10 +226,14 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
     fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
                                                                  dtype=torch.float32)
     _check_state("final_state", fs, sshape, dev)
+    need = lib().kda_fwd_chunked_workspace_bytes(B, T, H, HV, DK, DV, _dtype_code(q), kind,
+                                                 int(chunk_size))
+    ws = _workspace(workspace, need, dev)
     st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, HV, DK, DV,
                                _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
-                               int(bool(state_v_first)), int(chunk_size), *tf, _stream(dev))
+                               int(bool(state_v_first)), int(chunk_size), *tf, _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked", st)
     return o, fs
@@ -198,13 +241,15 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
 
 def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None,
                        softmax_scale=None, use_qk_l2norm=True, chunk_size=64, out=None,
-                       final_state=None, state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
-                lower_bound=None, use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+                       final_state=None, state_v_first=False, use_gate_in_kernel=False,
+                       A_log=None, dt_bias=None, lower_bound=None,
+                       use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False, workspace=None):
     """Chunked forward over N packed sequences (tokens [1, T, ...], sequence n
     is tokens cu_seqlens[n] .. cu_seqlens[n + 1]).  cu_seqlens: int32, N + 1
     offsets, on the CPU or the GPU (the other copy is made here).  Returns
     (o [1,T,HV,DV] fp32, final_state [N,HV,DK,DV] fp32).  Heads, state layout
-    and transforms as fwd_chunked."""
+    and transforms as fwd_chunked; ``workspace`` (None: allocated here) holds
+    every chunk's record, kda_fwd_chunked_varlen_workspace_bytes of them."""
     B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, None)
     tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
                      use_beta_sigmoid_in_kernel, allow_neg_eigval)
@@ -222,12 +267,15 @@ def fwd_chunked_varlen(q, k, v, beta, cu_seqlens, decay=None, initial_state=None
     fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
                                                                  dtype=torch.float32)
     _check_state("final_state", fs, sshape, dev)
+    need = lib().kda_fwd_chunked_varlen_workspace_bytes(_ptr(cu_host), N, H, HV, DK, DV,
+                                                        _dtype_code(q), kind, int(chunk_size))
+    ws = _workspace(workspace, need, dev)
     st = lib().kda_fwd_chunked_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                                       _ptr(initial_state), _ptr(o), _ptr(fs), _ptr(cu_dev),
                                       _ptr(cu_host), N, T, H, HV, DK, DV, _dtype_code(q),
                                       _scale(softmax_scale), int(bool(use_qk_l2norm)),
                                       int(bool(state_v_first)), int(chunk_size), *tf,
-                                      _stream(dev))
+                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked_varlen", st)
     return o, fs

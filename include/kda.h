@@ -21,8 +21,10 @@
  *
  *  - Every tensor pointer is a DEVICE pointer, owned by the caller, dense and
  *    row-major in the shape stated.  The library never allocates, frees or
- *    keeps device memory, and keeps no state between calls: calls are
- *    thread-safe and need no init.
+ *    keeps device memory: the chunked entry points take a caller-owned
+ *    device workspace (size query below).  Calls keep no state between them
+ *    and need no init; they are thread-safe as long as concurrent calls do
+ *    not share a workspace or an output.
  *  - Activations (q, k, v, beta, decay) share one dtype, KDA_F32 or KDA_BF16.
  *    Outputs o are fp32; states are fp32 (TileOPs DeltaNetFwdOp: the
  *    recurrent state is FP32 and belongs to the caller).
@@ -82,7 +84,8 @@ typedef enum {
   KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent         */
   KDA_ERR_UNSUPPORTED = 3, /* DK/DV/chunk/dtype/decay kind not implemented   */
   KDA_ERR_VALUE = 4,       /* invalid transform flags, floor or state layout */
-  KDA_ERR_HIP = 5          /* the HIP runtime reported an error at launch    */
+  KDA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch    */
+  KDA_ERR_WORKSPACE = 6    /* workspace NULL, misaligned or too small        */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -119,22 +122,23 @@ typedef enum {
  * Two kernels run on `stream`: a chunk-parallel one that prepares every
  * chunk (normalisation, gate sums, the WY inverse, decayed operands) and a
  * sequential one that carries the state through the chunks and writes o.
- * The prepared chunks pass through a device workspace that the library
- * allocates on first use and keeps, one per (device, stream), growing it when
- * a larger problem arrives (about 50 KB per chunk and head for DK = 128 fp16
- * operands; the first call of a larger size synchronises `stream`).
- *
- * With KDA_DECAY_CHANNEL the decay of every 16-token block (aligned to the
- * chunk start) must stay above about -87 in every channel: the prepared
- * operands hold products of exp(decay) over a block in fp32 range.  With the
- * raw gate, KDA_TF_LOWER_BOUND at -5 or above guarantees it.
+ * The prepared chunks pass through `workspace`, DEVICE memory owned by the
+ * caller, 16-byte aligned, of `workspace_bytes` bytes; its contents on entry
+ * do not matter and are garbage on return.  kda_fwd_chunked_workspace_bytes
+ * gives the size that lets one launch pair cover the whole sequence.  A
+ * smaller workspace works too, down to the size that query gives for
+ * T = chunk_size (one chunk of every head): the chunks are then processed in
+ * segments, each launch pair handing its final state to the next (the same
+ * result, bitwise).  The workspace must not be used by anything else until
+ * the call's work on `stream` has finished.
  *
  * T == 0 copies initial_state (or zeros) to final_state; then q, k, v, beta,
  * decay and o are not read and may be NULL.
  * Errors: KDA_ERR_NULL if final_state is NULL, or (T > 0) q/k/v/beta/o is
  * NULL or decay is NULL with decay_kind != NONE; KDA_ERR_SHAPE for negative or overflowing sizes;
  * KDA_ERR_UNSUPPORTED for other DK/DV/chunk/dtype/decay_kind values;
- * KDA_ERR_HIP if a launch or the workspace allocation fails.
+ * KDA_ERR_WORKSPACE (T > 0) if workspace is NULL, not 16-byte aligned or
+ * smaller than one chunk of every head; KDA_ERR_HIP if a launch fails.
  */
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                     const void* decay, int decay_kind, const float* initial_state,
@@ -142,7 +146,17 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
                     int B, int T, int H, int HV, int DK, int DV, int dtype,
                     float softmax_scale, int use_qk_l2norm, int state_v_first, int chunk_size,
                     const float* A_log, const float* dt_bias, float lower_bound,
-                    int transforms, void* stream);
+                    int transforms, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes for kda_fwd_chunked with these sizes and types to run the
+ * whole sequence in one launch pair: one record per (batch, value head,
+ * chunk).  A host-only query; 0 when T == 0 (no workspace is read) or when
+ * the arguments are invalid or unsupported (the call itself reports which).
+ * Called with T = chunk_size it gives the least workspace the call accepts.
+ */
+size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int HV, int DK, int DV, int dtype,
+                                       int decay_kind, int chunk_size);
 
 /*
  * Chunked forward over packed variable-length sequences (TileOPs
@@ -163,11 +177,15 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* bet
  *   o              [1, T, HV, DV] fp32, written
  *   final_state    like initial_state, written; may alias initial_state
  *
- * An empty sequence passes its initial state through.  The workspace holds
- * the records of all chunks of all sequences at once (no segmentation).
+ * An empty sequence passes its initial state through.  The caller-owned
+ * workspace (as for kda_fwd_chunked) holds the records of all chunks of all
+ * sequences at once and the sequences' chunk offsets: at least
+ * kda_fwd_chunked_varlen_workspace_bytes for the same offsets (no
+ * segmentation).
  * Errors as kda_fwd_chunked, plus: KDA_ERR_NULL if cu_seqlens or
  * cu_seqlens_host is NULL; KDA_ERR_SHAPE if N < 1, cu_seqlens_host[0] != 0,
- * cu_seqlens_host[N] != T or the offsets decrease.
+ * cu_seqlens_host[N] != T or the offsets decrease; KDA_ERR_WORKSPACE (T > 0)
+ * if workspace is NULL, misaligned or smaller than that size.
  */
 int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* beta,
                            const void* decay, int decay_kind, const float* initial_state,
@@ -177,11 +195,23 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
                            float softmax_scale, int use_qk_l2norm, int state_v_first,
                            int chunk_size,
                            const float* A_log, const float* dt_bias, float lower_bound,
-                           int transforms, void* stream);
+                           int transforms, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Workspace bytes kda_fwd_chunked_varlen needs for the N + 1 HOST offsets
+ * cu_seqlens_host (the records of every chunk of every sequence and head, and
+ * the chunk offsets).  0 when the sequences hold no token, or when the
+ * arguments are invalid or unsupported (the call itself reports which).
+ */
+size_t kda_fwd_chunked_varlen_workspace_bytes(const int* cu_seqlens_host, int N, int H, int HV,
+                                              int DK, int DV, int dtype, int decay_kind,
+                                              int chunk_size);
 /*
  * Recurrent forward: the pure sequential scan (ejkernel kda, section
  * "Algorithm Modes", Recurrent).  Same arguments and errors as
- * kda_fwd_chunked without chunk_size.  Computes in fp32 throughout.
+ * kda_fwd_chunked without chunk_size and the workspace.  Computes in fp32
+ * throughout.
  */
 int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* beta,
                       const void* decay, int decay_kind, const float* initial_state,

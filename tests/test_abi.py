@@ -38,26 +38,27 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 103
+    assert L.kda_abi_version() == 200
     assert L.kda_status_string(0) == b"ok"
-    for code in (1, 2, 3, 4, 5):
+    for code in (1, 2, 3, 4, 5, 6):
         assert len(L.kda_status_string(code)) > 3
     assert L.kda_status_string(99) == b"unknown status"
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+BIG = 1 << 40                    # a workspace size no validation rejects
 
 
 def chunked(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
              B=1, T=8, H=1, HV=None, DK=64, DV=64, dtype=1, scale=0.0, l2=1, vf=0, chunk=64,
-             A=None, dt=None, lb=0.0, tf=0)
+             A=None, dt=None, lb=0.0, tf=0, ws=FAKE, wsb=BIG)
     a.update(kw)
     hv = a["H"] if a["HV"] is None else a["HV"]
     return L.kda_fwd_chunked(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
                              a["o"], a["fs"], a["B"], a["T"], a["H"], hv, a["DK"], a["DV"],
                              a["dtype"], a["scale"], a["l2"], a["vf"], a["chunk"], a["A"], a["dt"],
-                             a["lb"], a["tf"], None)
+                             a["lb"], a["tf"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -77,6 +78,9 @@ def chunked(L, **kw):
     # value heads: a multiple of the q/k heads; state layout flag 0 or 1
     (dict(H=2, HV=3), 2), (dict(H=2, HV=0), 2), (dict(H=4, HV=2), 2), (dict(HV=65536), 2),
     (dict(vf=2), 4), (dict(vf=-1), 4),
+    # caller-owned workspace: present, 16-byte aligned, at least one chunk of every head
+    (dict(ws=None), 6), (dict(ws=ctypes.c_void_p(0x1008)), 6), (dict(wsb=0), 6),
+    (dict(B=2, H=3, wsb=6 * 9000), 6),
 ])
 def test_chunked_rejects_bad_arguments(L, kw, code):
     assert chunked(L, **kw) == code
@@ -104,13 +108,14 @@ def test_recurrent_and_decode_reject_bad_arguments(L):
 def varlen(L, cu, N, T=8, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, o=FAKE, fs=FAKE,
              cud=FAKE, H=1, HV=1, DK=64, DV=64, dtype=1, scale=0.0, l2=1, vf=0, chunk=64,
-             A=None, dt=None, lb=0.0, tf=0)
+             A=None, dt=None, lb=0.0, tf=0, ws=FAKE, wsb=BIG)
     a.update(kw)
     cuh = None if cu is None else (ctypes.c_int * len(cu))(*cu)
     return L.kda_fwd_chunked_varlen(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"],
                                     a["init"], a["o"], a["fs"], a["cud"], cuh, N, T, a["H"],
                                     a["HV"], a["DK"], a["DV"], a["dtype"], a["scale"], a["l2"],
-                                    a["vf"], a["chunk"], a["A"], a["dt"], a["lb"], a["tf"], None)
+                                    a["vf"], a["chunk"], a["A"], a["dt"], a["lb"], a["tf"],
+                                    a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("cu,N,T,kw,code", [
@@ -124,9 +129,45 @@ def varlen(L, cu, N, T=8, **kw):
     ([0, 4, 8], 2, 8, dict(chunk=128), 3),
     ([0, 4, 8], 2, 8, dict(DK=48), 3),
     ([0, 4, 8], 2, 8, dict(tf=12 | 16), 4),
+    ([0, 4, 8], 2, 8, dict(ws=None), 6),
+    ([0, 4, 8], 2, 8, dict(wsb=100), 6),
 ])
 def test_varlen_rejects_bad_arguments(L, cu, N, T, kw, code):
     assert varlen(L, cu, N, T, **kw) == code
+
+
+def _rec(L, DK, C, dtype, kind, heads=1):
+    """record bytes of one chunk (T = chunk_size) for `heads` value heads"""
+    return L.kda_fwd_chunked_workspace_bytes(1, C, heads, heads, DK, DK, dtype, kind, C)
+
+
+def test_workspace_size_query(L):
+    q = L.kda_fwd_chunked_workspace_bytes
+    for dtype in (0, 1):
+        for kind in (0, 1, 2):
+            for C in (16, 32, 64):
+                one = _rec(L, 128, C, dtype, kind)
+                assert one > 0 and one % 256 == 0
+                # one record per (batch, value head, chunk); a ragged tail is a whole chunk
+                assert q(3, 5 * C + 1, 2, 4, 128, 128, dtype, kind, C) == one * 3 * 4 * 6
+                assert q(3, C, 2, 4, 128, 128, dtype, kind, C) == one * 3 * 4
+    # what the request does not support, and no tokens, give 0
+    assert q(1, 0, 1, 1, 128, 128, 1, 1, 64) == 0
+    assert q(1, 64, 1, 1, 96, 128, 1, 1, 64) == 0
+    assert q(1, 64, 1, 1, 128, 128, 1, 1, 128) == 0
+    assert q(1, 64, 2, 3, 128, 128, 1, 1, 64) == 0
+    assert q(1, 64, 1, 1, 128, 128, 5, 1, 64) == 0
+
+
+def test_varlen_workspace_size_query(L):
+    q = L.kda_fwd_chunked_varlen_workspace_bytes
+    one = _rec(L, 64, 32, 1, 2, heads=2)
+    cu = (ctypes.c_int * 5)(0, 0, 33, 97, 100)     # 0, 2, 2 and 1 chunks of 32
+    need = q(cu, 4, 1, 2, 64, 64, 1, 2, 32)
+    assert need >= one * 5 and need - one * 5 >= 5 * 4 and need - one * 5 < 5 * 4 + 16
+    assert q(cu, 4, 1, 2, 64, 64, 1, 2, 128) == 0
+    assert q((ctypes.c_int * 2)(0, 0), 1, 1, 1, 64, 64, 1, 2, 32) == 0
+    assert q((ctypes.c_int * 3)(0, 9, 4), 2, 1, 1, 64, 64, 1, 2, 32) == 0
 
 
 def test_python_binding_refuses_cpu_tensors():

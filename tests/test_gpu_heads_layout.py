@@ -187,10 +187,10 @@ def test_decode_value_major_equals_key_major_bitwise_after_transpose():
     assert rel(vm(s_vm), s_km.double().cpu().numpy()) < 1e-5
 
 
-def test_full_size_grouped_heads_sampled():
+def test_full_size_grouped_heads_every_head():
     # gdn_d128's shape with 4 q/k heads for its 16 value heads, as the
-    # benchmark's grouped-head extra runs it; a sample of (b, value head)
-    from oracle import kda_scan_heads
+    # benchmark's grouped-head extra runs it; every (b, value head)
+    from test_gpu_parity import full_oracle
     w = WORKLOADS["gdn_d128"].scaled(H=4, HV=16)
     print(f"\n[case] grouped heads full size {w}", flush=True)
     inp = make_inputs(w)
@@ -198,16 +198,13 @@ def test_full_size_grouped_heads_sampled():
     o, S = fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"],
                        chunk_size=w.chunk)
     torch.cuda.synchronize()
-    heads = [(0, 0), (7, 15), (4, 9)]
-    o_ref, S_ref = kda_scan_heads(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
-                                  inp["initial_state"], heads)
-    check("grouped sampled", torch.stack([o[b, :, h] for b, h in heads]),
-          torch.stack([S[b, h] for b, h in heads]), o_ref, S_ref, TOL[w.dtype])
+    o_ref, S_ref = full_oracle(inp)
+    check("grouped every head", o, S, o_ref, S_ref, TOL[w.dtype])
 
 
 def test_decode_full_size_value_major():
     # decode_d128 at full size with a value-major state, as the benchmark's
-    # value-major extra runs it; a sample of batch entries
+    # value-major extra runs it; every batch entry
     from oracle import kda_decode
     w = WORKLOADS["decode_d128"]
     print(f"\n[case] decode value-major full size {w}", flush=True)
@@ -216,7 +213,6 @@ def test_decode_full_size_value_major():
     state = vm(d["initial_state"])
     o = decode_step(d["q"], d["k"], d["v"], d["beta"], d["decay"], state, state_v_first=True)
     torch.cuda.synchronize()
-    bs = [0, 77, 255]
-    o_ref, S_ref = kda_decode(inp["q"][bs], inp["k"][bs], inp["v"][bs], inp["beta"][bs],
-                              inp["decay"][bs], inp["initial_state"][bs])
-    check("decode value-major sampled", o[bs], state[bs], o_ref, vm(S_ref), TOL[w.dtype])
+    o_ref, S_ref = kda_decode(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                              inp["initial_state"])
+    check("decode value-major every row", o, state, o_ref, vm(S_ref), TOL[w.dtype])

@@ -13,7 +13,7 @@ import torch
 
 from gated_delta_rule_fwd_amd import decode_step, fwd_chunked, fwd_chunked_varlen, fwd_recurrent
 from gated_delta_rule_fwd_amd.inputs import WORKLOADS, make_inputs
-from oracle import kda_decode, kda_scan, kda_scan_heads
+from oracle import kda_decode, kda_scan
 
 pytestmark = pytest.mark.gpu
 
@@ -157,18 +157,28 @@ def test_decode_matches_oracle(kw):
 
 # ------------------------------------------------------ full-size, sampled --
 
-SAMPLED = {
-    "deltanet_d64": [(0, 0), (3, 15), (2, 7)],
-    "gdn_d128": [(0, 0), (7, 15), (4, 9)],
-    "kda_d128": [(0, 0), (1, 31), (1, 5)],
-}
+FULL_SIZE = ["deltanet_d64", "gdn_d128", "kda_d128"]
 
 
-@pytest.mark.parametrize("name", list(SAMPLED))
-def test_chunked_full_size_sampled_heads(name):
+def full_oracle(inp):
+    """The oracle over every (batch, head) of a full-size workload, one batch
+    entry at a time (every batch entry is independent)."""
+    outs, states = [], []
+    B = inp["q"].shape[0]
+    for b in range(B):
+        sl = lambda x: None if x is None else x[b:b + 1]
+        o, S = kda_scan(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]),
+                        sl(inp["decay"]), sl(inp["initial_state"]))
+        outs.append(o)
+        states.append(S)
+    return np.concatenate(outs), np.concatenate(states)
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_chunked_full_size_every_head(name):
     """The workload at its full size and in the launch configuration the
-    benchmark times; every head is independent, so a sample of (b, h) pairs
-    is checked against the oracle over the whole sequence."""
+    benchmark times, every (b, h) compared with the oracle over the whole
+    sequence."""
     w = WORKLOADS[name]
     announce(f"chunked full size {w}")
     inp = make_inputs(w)
@@ -177,12 +187,6 @@ def test_chunked_full_size_sampled_heads(name):
                        chunk_size=w.chunk)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
-    heads = SAMPLED[name]
-    o_ref, S_ref = kda_scan_heads(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
-                                  inp["initial_state"], heads)
-    o_s = torch.stack([o[b, :, h] for b, h in heads])
-    S_s = torch.stack([S[b, h] for b, h in heads])
-    check("chunked sampled", o_s, S_s, o_ref, S_ref, TOL[w.dtype])
     # every (b, h) at full size, run to run: the waves of a workgroup hand
     # each other operands through LDS, and any missing wait shows up here
     for _ in range(3):
@@ -190,9 +194,14 @@ def test_chunked_full_size_sampled_heads(name):
                              chunk_size=w.chunk)
         torch.cuda.synchronize()
         assert torch.equal(o2, o) and torch.equal(S2, S), "full-size run-to-run difference"
+    o_c, S_c = o.cpu(), S.cpu()
+    del o, S, o2, S2, d
+    torch.cuda.empty_cache()
+    o_ref, S_ref = full_oracle(inp)
+    check("chunked every head", o_c, S_c, o_ref, S_ref, TOL[w.dtype])
 
 
-def test_decode_full_size_sampled_heads():
+def test_decode_full_size_every_row():
     w = WORKLOADS["decode_d128"]
     announce(f"decode full size {w}")
     inp = make_inputs(w)
@@ -200,10 +209,9 @@ def test_decode_full_size_sampled_heads():
     state = d["initial_state"].clone()
     o = decode_step(d["q"], d["k"], d["v"], d["beta"], d["decay"], state)
     torch.cuda.synchronize()
-    bs = [0, 77, 255]
-    o_ref, S_ref = kda_decode(inp["q"][bs], inp["k"][bs], inp["v"][bs], inp["beta"][bs],
-                              inp["decay"][bs], inp["initial_state"][bs])
-    check("decode sampled", o[bs], state[bs], o_ref, S_ref, TOL[w.dtype])
+    o_ref, S_ref = kda_decode(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                              inp["initial_state"])
+    check("decode every row", o, state, o_ref, S_ref, TOL[w.dtype])
 
 
 # ------------------------------------------------- packed variable length --
@@ -352,24 +360,37 @@ def test_nan_stays_in_its_head():
     assert torch.isfinite(o[1, :64, 2]).all()
 
 
-def test_segmented_chunk_walk_matches_single_pass(monkeypatch):
-    """A small workspace budget splits the sequence into segments of chunks
-    (each state pass hands its final state to the next); the result must be
-    bitwise the single-pass result and within tolerance of the oracle."""
+def test_segmented_chunk_walk_matches_single_pass():
+    """A workspace smaller than the whole sequence's records splits it into
+    segments of chunks (each state pass hands its final state to the next);
+    the result must be bitwise the single-pass result and within tolerance of
+    the oracle.  Sizes: the full size, one chunk of every head (the least the
+    call accepts: a segment per chunk), and three chunks' worth."""
+    from gated_delta_rule_fwd_amd import chunked_workspace_bytes
     for name, kw in (("gdn_d128", dict(B=2, T=333, H=4)),
-                     ("kda_d128", dict(B=1, T=300, H=4, init_state=True))):
+                     ("kda_d128", dict(B=1, T=300, H=4, init_state=True)),
+                     ("fp32_small", dict(T=100, chunk=16, init_state=True))):
         w = small(name, **kw)
         announce(f"segmented {w}")
         inp = make_inputs(w)
         d = to_dev(inp)
         args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
-        monkeypatch.delenv("KDA_CHUNKED_SEGMENT_MB", raising=False)
-        o1, S1 = fwd_chunked(*args, chunk_size=w.chunk)
-        monkeypatch.setenv("KDA_CHUNKED_SEGMENT_MB", "1")   # ~1 MiB of records: several segments
-        o2, S2 = fwd_chunked(*args, chunk_size=w.chunk)
-        monkeypatch.delenv("KDA_CHUNKED_SEGMENT_MB")
-        torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(S1, S2), "segmented walk differs from one pass"
+        dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        full = chunked_workspace_bytes(w.B, w.T, w.H, w.hv, w.DK, w.DV, dt, w.decay_kind, w.chunk)
+        least = chunked_workspace_bytes(w.B, w.chunk, w.H, w.hv, w.DK, w.DV, dt, w.decay_kind,
+                                        w.chunk)
+        assert 0 < least < full
+        o1, S1 = fwd_chunked(*args, chunk_size=w.chunk,
+                             workspace=torch.empty(full, dtype=torch.uint8, device=dev()))
+        for nb in (least, 3 * least + 100):
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev())
+            o2, S2 = fwd_chunked(*args, chunk_size=w.chunk, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(S1, S2), "segmented walk differs from one pass"
         o_ref, S_ref = kda_scan(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
                                 inp["initial_state"])
         check("segmented", o2, S2, o_ref, S_ref, TOL[w.dtype])
+        # one byte short of the least is refused before anything runs
+        with pytest.raises(Exception, match="WORKSPACE"):
+            fwd_chunked(*args, chunk_size=w.chunk,
+                        workspace=torch.empty(least - 1, dtype=torch.uint8, device=dev()))

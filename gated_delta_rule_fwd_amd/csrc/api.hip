@@ -182,6 +182,39 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   return kda::to_status(kda::launch_chunked_varlen(a, cu_seqlens, cu_seqlens_host, N, workspace, s));
 }
 
+int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                            const void* decay, int decay_kind, const float* initial_state,
+                            float* o, float* final_state,
+                            int B, int T, int H, int HV, int DK, int DV, int dtype,
+                            float softmax_scale, int use_qk_l2norm, int state_v_first,
+                            int chunk_size, const float* A_log, const float* dt_bias,
+                            float lower_bound, int transforms, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype,
+                             state_v_first);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
+  if (st != KDA_OK) return st;
+  if (!final_state || (T != 0 && !o)) return KDA_ERR_NULL;
+  if (!kda::chunk_ok(chunk_size)) return KDA_ERR_UNSUPPORTED;
+  if (kda::chunked_lds_bytes(DK, DV, chunk_size, dtype, decay_kind) == 0) return KDA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    return kda::to_status(kda::launch_state_copy(initial_state, final_state,
+                                                 static_cast<long>(B) * HV * DK * DV, s));
+  }
+  // the scratch must hold one chunk index of every head (checked before any HIP call)
+  const size_t least = kda::records_bytes(1, static_cast<long>(B) * HV, DK, DV, dtype, decay_kind,
+                                          chunk_size);
+  if (least > KDA_NOALLOC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = kda::noalloc_scratch(&ws);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  const kda::FwdArgs a = kda::make_args(q, k, v, beta, decay, decay_kind, initial_state, o,
+                                        final_state, B, T, H, HV, DK, DV, dtype, softmax_scale,
+                                        use_qk_l2norm, state_v_first, chunk_size,
+                                        kda::make_tf(A_log, dt_bias, lower_bound, transforms));
+  return kda::to_status(kda::launch_chunked(a, ws, KDA_NOALLOC_WORKSPACE_BYTES, s));
+}
+
 size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int HV, int DK, int DV, int dtype,
                                        int decay_kind, int chunk_size) {
   if (B < 1 || T < 1 || H < 1 || HV < 1 || HV % H != 0) return 0;

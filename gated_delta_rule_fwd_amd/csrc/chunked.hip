@@ -2,10 +2,20 @@
 // segments of chunks that the caller's workspace holds the records of (the
 // prep kernel writes one record per chunk, the state kernel reads it), and
 // dispatch to the bf16 / fp32 instantiations (chunked_impl.h).
+#include <mutex>
+
+#include "../../include/kda.h"
 #include "chunked_impl.h"
 
 namespace kda {
 namespace {
+
+// Fixed device scratch of kda_fwd_chunked_noalloc: the per-chunk records of
+// callers that cannot allocate.  Each device the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below) and only that is passed on.
+__device__ __align__(256) unsigned char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
 
 using chunked::PrepParams;
 using chunked::StateParams;
@@ -32,6 +42,27 @@ size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind) {
   // the plan at the smallest grid (B = H = 1) is the widest slice
   const Plan a = plan_for(1, 1, DK, DV, chunk, dtype, decay_kind == DECAY_CHANNEL);
   return a.dvs == 0 ? 0 : a.lds;
+}
+
+// The device address of this device's `scratch`, looked up once per device
+// with that device current (the caller's current device).
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t chunked_record_bytes(int DK, int chunk, int dtype, int decay_kind) {

@@ -41,6 +41,9 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
 // LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.
 size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind);
+// The device address of the current device's fixed scratch of
+// KDA_NOALLOC_WORKSPACE_BYTES (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
 // Workspace bytes of one chunk's record (one head), 0 if unsupported.
 size_t chunked_record_bytes(int DK, int chunk, int dtype, int decay_kind);
 

@@ -22,6 +22,8 @@ DECAY_NONE, DECAY_HEAD, DECAY_CHANNEL = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
           4: "KDA_ERR_VALUE", 5: "KDA_ERR_HIP", 6: "KDA_ERR_WORKSPACE"}
 TF_GATE, TF_LOWER_BOUND, TF_BETA_SIGMOID, TF_NEG_EIGVAL = 1, 2, 4, 8
+# the fixed per-device scratch of kda_fwd_chunked_noalloc (KDA_NOALLOC_WORKSPACE_BYTES)
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 _lib = None
 
@@ -45,6 +47,9 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
                                       i, i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp, sz, vp]
         L.kda_fwd_chunked.restype = i
+        L.kda_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp,
+                                              i, i, i, i, i, i, i, f, i, i, i, vp, vp, f, i, vp]
+        L.kda_fwd_chunked_noalloc.restype = i
         L.kda_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
         L.kda_fwd_chunked_workspace_bytes.restype = sz
         L.kda_fwd_chunked_varlen.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, i,
@@ -236,6 +241,34 @@ def fwd_chunked(q, k, v, beta, decay=None, initial_state=None, softmax_scale=Non
                                ws.numel() * ws.element_size(), _stream(dev))
     if st != 0:
         raise KdaError("kda_fwd_chunked", st)
+    return o, fs
+
+
+def fwd_chunked_noalloc(q, k, v, beta, decay=None, initial_state=None, softmax_scale=None,
+                        use_qk_l2norm=True, chunk_size=64, out=None, final_state=None,
+                        state_v_first=False, use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                        lower_bound=None, use_beta_sigmoid_in_kernel=False,
+                        allow_neg_eigval=False):
+    """fwd_chunked through kda_fwd_chunked_noalloc: the library keeps the
+    per-chunk records in its fixed per-device scratch, so the C call
+    allocates nothing (pass ``out`` and ``final_state`` to allocate nothing
+    here either).  Calls that overlap on one device race on that scratch."""
+    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
+    sshape = _state_shape(B, HV, DK, DV, state_v_first)
+    o = out if out is not None else torch.empty((B, T, HV, DV), device=dev, dtype=torch.float32)
+    _check_state("out", o, (B, T, HV, DV), dev)
+    fs = final_state if final_state is not None else torch.empty(sshape, device=dev,
+                                                                 dtype=torch.float32)
+    _check_state("final_state", fs, sshape, dev)
+    st = lib().kda_fwd_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
+                                       _ptr(initial_state), _ptr(o), _ptr(fs), B, T, H, HV, DK,
+                                       DV, _dtype_code(q), _scale(softmax_scale),
+                                       int(bool(use_qk_l2norm)), int(bool(state_v_first)),
+                                       int(chunk_size), *tf, _stream(dev))
+    if st != 0:
+        raise KdaError("kda_fwd_chunked_noalloc", st)
     return o, fs
 
 

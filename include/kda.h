@@ -242,6 +242,34 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* bet
                     const float* A_log, const float* dt_bias, float lower_bound,
                     int transforms, void* stream);
 
+/*
+ * Allocation-free chunked forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops and harnesses that
+ * forbid allocation): kda_fwd_chunked with the same arguments, minus the
+ * workspace.  The per-chunk records go to a fixed scratch array of
+ * KDA_NOALLOC_WORKSPACE_BYTES that the library holds on each device it runs
+ * on (its own copy per device, kept until the process ends).  Sequences
+ * longer than the scratch holds are processed in segments of chunks, as
+ * kda_fwd_chunked does with a small workspace (bitwise the same result).
+ * The call allocates and frees nothing, and needs nothing zeroed.
+ *
+ * Every call on one device shares that device's scratch: calls that overlap
+ * on one device (different streams or threads, with no ordering between
+ * their work) race and give wrong results.  Calls in one stream are ordered.
+ *
+ * Errors as kda_fwd_chunked; KDA_ERR_WORKSPACE (T > 0) if one chunk of every
+ * head (kda_fwd_chunked_workspace_bytes with T = chunk_size) exceeds
+ * KDA_NOALLOC_WORKSPACE_BYTES.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                            const void* decay, int decay_kind, const float* initial_state,
+                            float* o, float* final_state,
+                            int B, int T, int H, int HV, int DK, int DV, int dtype,
+                            float softmax_scale, int use_qk_l2norm, int state_v_first,
+                            int chunk_size, const float* A_log, const float* dt_bias,
+                            float lower_bound, int transforms, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(int status);
 

@@ -175,3 +175,19 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         K.fwd_chunked(x, x, x, torch.zeros(1, 4, 1))
+
+
+def test_noalloc_constant_and_size_limit(L):
+    text = open(HEADER).read()
+    import re as _re
+    m = _re.search(r"#define\s+KDA_NOALLOC_WORKSPACE_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == K.NOALLOC_WORKSPACE_BYTES
+    # one chunk of 2048 per-channel D128 heads needs more than the scratch: refused on the
+    # host before any HIP call
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, FAKE,
+            1, 64, 2048, 2048, 128, 128, 1, 0.0, 1, 0, 64, None, None, 0.0, 0, None]
+    assert L.kda_fwd_chunked_workspace_bytes(1, 64, 2048, 2048, 128, 128, 1, 2, 64) > \
+        K.NOALLOC_WORKSPACE_BYTES
+    assert L.kda_fwd_chunked_noalloc(*args) == 6
+    args[2] = None
+    assert L.kda_fwd_chunked_noalloc(*args) == 1

@@ -33,13 +33,17 @@
 // rounded once to fp16; derived operands rounded once to fp16) and
 // v_mfma_f32_16x16x4_f32 for fp32 activations.  The inverse is built in fp32.
 //
-// Per-key-channel decay uses products of per-token factors exp(g) <= 1
-// referenced to 16-token block boundaries, so no factor exceeds 1 except the
-// inverse-prefix operand: balanced by sqrt of the block factor it stays
-// within exp(+-8) (fp16) when a block decays by at most exp(-16).  A chunk
-// with a steeper block keeps all its Gram operands as bf16 (fp32 range: the
-// decay over 16 tokens must stay above about -87 in every channel), and the
-// diagonal of P (no decay) is computed directly from the normalised rows.
+// Per-key-channel decay uses products of per-token factors exp(g) <= 1 only,
+// so no operand exceeds the normalised row it scales, whatever the decay
+// (exp(g) may underflow to 0: the products it belongs to are then 0, as
+// they should be to well below fp16 resolution).  A Gram entry of tokens
+// s < r carries the decay of the tokens strictly between them (A) or of
+// s+1 .. r (P).  Between 16-token blocks it is split as (k_s decayed to the
+// end of its block) x (the decay of the blocks in between, an fp32 scale) x
+// (the row decayed from the start of its block).  Within a diagonal block
+// the same split is made at 4-token quarters (one MFMA pass per column
+// quarter), and the pairs inside one quarter are summed over the channels
+// directly in fp32.
 //
 // Accumulator layout of a 16x16 MFMA result: lane l holds rows 4*(l/16)+j,
 // j = 0..3, of column l%16.  The k index of an MFMA is a sum, so A and B may
@@ -60,7 +64,6 @@ namespace chunked {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr float kSteepBlockLogDecay = -16.f;   // a 16-token block decaying faster is "steep"
 
 // Barrier over LDS only: outstanding global loads (the next chunk's prefetch)
 // stay in flight across it.
@@ -100,6 +103,16 @@ template <> struct Mma<_Float16> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (T)(static_cast<float>(f[e]) * v[k0 + 8 * g + e]);
   }
+  // times v1 (if u1) and v2 (if u2) per k, rounded once
+  __device__ static void scale_cont2(frag& f, const float* v1, bool u1, const float* v2, bool u2, int k0,
+                                     int g) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = u1 ? v1[k0 + 8 * g + e] : 1.f, b = u2 ? v2[k0 + 8 * g + e] : 1.f;
+      f[e] = (T)(static_cast<float>(f[e]) * (a * b));
+    }
+  }
+  __device__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
 };
 
 template <> struct Mma<float> {
@@ -128,19 +141,19 @@ template <> struct Mma<float> {
       f.hi[e] *= v[k0 + 16 + 4 * g + e];
     }
   }
+  __device__ static void scale_cont2(frag& f, const float* v1, bool u1, const float* v2, bool u2, int k0,
+                                     int g) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = u1 ? v1[k0 + 4 * g + e] : 1.f, b0 = u2 ? v2[k0 + 4 * g + e] : 1.f;
+      const float a1 = u1 ? v1[k0 + 16 + 4 * g + e] : 1.f, b1 = u2 ? v2[k0 + 16 + 4 * g + e] : 1.f;
+      f.lo[e] *= a0 * b0;
+      f.hi[e] *= a1 * b1;
+    }
+  }
+  __device__ static frag zero() { return frag{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
 };
 
-// bf16 x bf16 products for the Gram blocks of a steep per-channel chunk,
-// whose operands are stored as bf16 bit patterns (fp32 range).  Whole-vector
-// bit casts: building a __bf16 vector element by element from 16-bit patterns
-// is not reliably compiled.
-__device__ __forceinline__ void mma_bf16_raw(f32x4& acc, const uint16_t* a_row, const uint16_t* b_row,
-                                             int k0, int g) {
-  const uint4 araw = *reinterpret_cast<const uint4*>(a_row + k0 + 8 * g);
-  const uint4 braw = *reinterpret_cast<const uint4*>(b_row + k0 + 8 * g);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
-                                               __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
-}
 // bf16 operand of 8 elements from two accumulator tiles (rows 4g..4g+3 of
 // each), rounded to nearest even; and the bf16 product.
 __device__ __forceinline__ bf16x8 bf_from_acc(const f32x4& a, const f32x4& b) {
@@ -167,33 +180,8 @@ __device__ __forceinline__ float sumsq_bf(const bf16x8& x, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(c, c, acc, false);
   return __builtin_amdgcn_fdot2_f32_bf16(d, d, acc, false);
 }
-// The same with the A operand scaled per k (v[k0 + 8g + e]) in fp32 and
-// rounded once more to bf16; kT: the product with the operands' roles
-// swapped (the transposed tile).
-template <bool kT = false>
-__device__ __forceinline__ void mma_bf16_raw_scaled(f32x4& acc, const uint16_t* a_row, const float* v,
-                                                    const uint16_t* b_row, int k0, int g) {
-  const uint4 a0 = *reinterpret_cast<const uint4*>(a_row + k0 + 8 * g);
-  const uint4 braw = *reinterpret_cast<const uint4*>(b_row + k0 + 8 * g);
-  const uint32_t w[4] = {a0.x, a0.y, a0.z, a0.w};
-  uint32_t aw[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = f32_to_bf16(__uint_as_float(w[e] << 16) * v[k0 + 8 * g + 2 * e]);
-    const uint32_t hi = f32_to_bf16(__uint_as_float(w[e] & 0xffff0000u) * v[k0 + 8 * g + 2 * e + 1]);
-    aw[e] = lo | (hi << 16);
-  }
-  const uint4 araw = uint4{aw[0], aw[1], aw[2], aw[3]};
-  if constexpr (kT)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, braw),
-                                                 __builtin_bit_cast(bf16x8, araw), acc, 0, 0, 0);
-  else
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, araw),
-                                                 __builtin_bit_cast(bf16x8, braw), acc, 0, 0, 0);
-}
-
-template <typename In> struct OpOf { using T = _Float16; using KinvT = uint16_t; };
-template <> struct OpOf<float> { using T = float; using KinvT = float; };
+template <typename In> struct OpOf { using T = _Float16; };
+template <> struct OpOf<float> { using T = float; };
 
 // Packed variable-length input (B = 1, N sequences back to back in T): cu
 // holds the N + 1 token offsets of the sequences, cb the N + 1 offsets of
@@ -346,7 +334,6 @@ constexpr int prep_waves() {
 template <int DK, int C, typename In, int DECAY, bool TF>
 __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) void prep_kernel(PrepParams p) {
   using OpT = typename OpOf<In>::T;
-  using KinvT = typename OpOf<In>::KinvT;
   using M = Mma<OpT>;
   constexpr bool chan = DECAY == DECAY_CHANNEL;
   constexpr bool headdecay = DECAY == DECAY_HEAD;
@@ -391,19 +378,17 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   float* sAm = reinterpret_cast<float*>(smem + L::oAM);
   OpT* sGst = reinterpret_cast<OpT*>(smem + L::oAM);     // staged per-channel gate [C][DK]
   float* sTm = reinterpret_cast<float*>(smem + L::oRA(chan));
-  KinvT* sKinv = reinterpret_cast<KinvT*>(smem + L::oKinv(chan));
+  OpT* sKB = reinterpret_cast<OpT*>(smem + L::oKB);       // per-channel: k decayed to its quarter's / block's end
   float* sv = reinterpret_cast<float*>(smem + L::oVec(chan));
   float* s_bt = sv;
   float* s_Gi = sv + C;
   float* s_Ge = sv + 2 * C;
   float* s_qk = sv + 3 * C;                    // per-channel decay: q_hat . k_hat per token;
   float* s_fk = s_qk;                          // raw K: the row factor of k
-  float* s_misc = sv + 4 * C;                  // [1] = steep-gate flag
-  int* s_flag = reinterpret_cast<int*>(s_misc + 1);
-  float* s_tau = s_misc + 16;                  // [NB][DK] whole-block decay factors
-  float* s_Cb = s_tau + NB * DK;               // [NB][DK] decay of all earlier blocks
-  float* s_rsq = s_Cb + NB * DK;               // [NB][DK] rs: exp(block log decay / 2)
-  float* s_D = s_rsq + NB * DK;                // [ND][DK] decay strictly between blocks
+  float* s_misc = sv + 4 * C;
+  float* s_tau4 = s_misc + 16;                 // [NQ][DK] decay factor of each 4-token quarter
+  float* s_wq = s_tau4 + L::NQ * DK;           // [NQ][12] within-quarter Gram sums (A, then P)
+  float* s_D = s_wq;                           // [NDD][DK] decay between blocks i, j (i - j >= 2), later
 
   const In* gq = static_cast<const In*>(p.q);
   const In* gk = static_cast<const In*>(p.k);
@@ -517,10 +502,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           rvec[R::vEF + lane] = __expf(Glast - G);
         }
       }
-      if (lane == 0) {
-        if (headdecay) rvec[R::vMisc] = __expf(Glast);
-        *s_flag = 0;
-      }
+      if (lane == 0 && headdecay) rvec[R::vMisc] = __expf(Glast);
     }
   }
   lds_barrier();
@@ -538,199 +520,27 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     }
   }
 
-  if constexpr (chan) {
-    if constexpr (sizeof(OpT) == 2) {
-      // (1a) a chunk with a block that decays by more than exp(-16) in some
-      // channel is "steep": its Gram operands are kept as bf16 (fp32 range),
-      // since the prefix factors can then underflow fp16
-      for (int task = tid; task < NB * DK; task += kPrepThreads) {
-        const int i = task / DK, c = task % DK;
-        float sum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) sum += static_cast<float>(sGst[(16 * i + t) * DK + c]);
-        if (sum < kSteepBlockLogDecay) *s_flag = 1;
-        s_rsq[i * DK + c] = __expf(0.5f * sum);   // rs of the balanced operands (1b)
-      }
-      lds_barrier();
-    }
-    const bool steep = *s_flag != 0;
-    // (1b) per (16-token block, key channel): normalised q, k times exp(g)
-    // products referenced to the block start (prefix) and end (suffix);
-    // all of them are <= 1.  The decay-to-block-end operand of the
-    // off-diagonal Gram blocks is the inverse-prefix one times the block
-    // factor, folded into their A-operand scale (D below).
-    // fp16 operands (not steep) are balanced: the prefix products are stored
-    // divided by rs = exp(block log decay / 2) and the inverse-prefix ones
-    // multiplied by it, so both lie within exp(+-8) of the normalised rows
-    // and neither underflows fp16 late in a strongly decaying block.
-    constexpr int NT = (NB * DK + kPrepThreads - 1) / kPrepThreads;
-    float kbr[NT][16];       // k decayed to the block end (for the record's F)
-#pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      const int task = tid + it * kPrepThreads;
-      if (task < NB * DK) {
-        const int i = task / DK, c = task % DK;
-        float a[16], kx[16], kin[16];
-        float pre = 1.f;
-        const bool bal = sizeof(OpT) == 2 && !steep;
-        const float rs = bal ? s_rsq[i * DK + c] : 1.f;
-        const float irs = 1.f / rs;
-        // Ka (k times the exclusive prefix) and Qa (q times the inclusive
-        // one) replace k and q in place: fp16, or bf16 bit patterns when steep
-        auto put = [&](OpT* tile, int r, float x) {
-          if (sizeof(OpT) == 2 && steep)
-            reinterpret_cast<uint16_t*>(tile)[r * L::LDK + c] = f32_to_bf16(x);
-          else
-            tile[r * L::LDK + c] = (OpT)x;
-        };
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 16 * i + t;
-          a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
-          kx[t] = static_cast<float>(sK[r * L::LDK + c]);
-          const float qx = static_cast<float>(sQ[r * L::LDK + c]);
-          put(sK, r, kx[t] * pre * irs);
-          pre *= a[t];
-          kin[t] = kx[t] / pre;                             // k / inclusive prefix
-          put(sQ, r, qx * pre * irs);
-        }
-        float suf = 1.f;
-#pragma unroll
-        for (int t = 15; t >= 0; --t) {
-          kbr[it][t] = kx[t] * suf;                         // decay to the block end
-          suf *= a[t];
-        }
-        s_tau[i * DK + c] = pre;   // whole-block factor
-        if constexpr (sizeof(OpT) == 2) {
-          if (!steep) {
-            // diagonal blocks pair a factor <= 1 with its inverse; balanced by
-            // rs both stay within exp(+-8) for a block factor >= exp(-16),
-            // which fp16 holds
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-              *reinterpret_cast<_Float16*>(&sKinv[(16 * i + t) * L::LDK + c]) = (_Float16)(kin[t] * rs);
-          } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = f32_to_bf16(kin[t]);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) sKinv[(16 * i + t) * L::LDK + c] = kin[t];
-        }
-      }
-    }
-    lds_barrier();
-    // (1c) chunk-level factors; k decayed to the chunk end goes to the record
-#pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      const int task = tid + it * kPrepThreads;
-      if (task < NB * DK) {
-        const int i = task / DK, c = task % DK;
-        const float tau = s_tau[i * DK + c];
-        float cb = 1.f, ca = 1.f;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const float tj = s_tau[j * DK + c];
-          if (j < i) cb *= tj;
-          if (j > i) ca *= tj;
-        }
-        // balanced fp16 operands: block i's prefix products carry 1 / rs_i,
-        // block j's inverse-prefix ones rs_j (restored below)
-        const bool bal = sizeof(OpT) == 2 && !steep;
-        const float rsi = bal ? s_rsq[i * DK + c] : 1.f;
-        s_Cb[i * DK + c] = cb * rsi;
-        if (i == 0) rvec[R::vDecC + c] = ca * tau;
-        // D[i][j] = rs_i prod_{j < m < i} tau_m * tau_j / rs_j: the stored
-        // inverse-prefix operand of block j times tau_j / rs_j is k decayed to
-        // the end of block j
-        float dd = 1.f;
-#pragma unroll
-        for (int j = NB - 1; j >= 0; --j) {
-          if (j < i) {
-            const float tj = s_tau[j * DK + c];
-            s_D[L::dslot(i, j) * DK + c] = rsi * dd * (bal ? tj / s_rsq[j * DK + c] : tj);
-            dd *= tj;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 16 * i + t;
-          *reinterpret_cast<OpT*>(rec + R::oF + swz_off<R::PPRK>(r, perm_pos(c) * static_cast<int>(sizeof(OpT)))) =
-              (OpT)(kbr[it][t] * ca);
-        }
-      }
-    }
-    lds_barrier();
-  }
-
-  // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-  // (raw rows: A only; the state kernel forms P)
-  for (int job = wave; job < (R::kRawK ? NPAIR : 2 * NPAIR); job += kPrepWaves) {
-    const bool isP = job >= NPAIR;
-    const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
-    const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
-    f32x4 acc = {0, 0, 0, 0};
-    if (!chan) {
-      const OpT* brow = sK + (16 * j + l16) * L::LDK;
-      typename M::frag fa[NKP], fb[NKP];
-#pragma unroll
-      for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
-#pragma unroll
-      for (int m = 0; m < NKP; ++m) M::mma(acc, fb[m], fa[m]);
-    } else if (i == j) {
-      if constexpr (sizeof(OpT) == 2) {
-        const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
-        if (*s_flag == 0) {
-          const OpT* krh = reinterpret_cast<const OpT*>(krow);
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(krh, 32 * m, g), M::ld_cont(arow, 32 * m, g));
-        } else {
-          const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) mma_bf16_raw(acc, krow, arh, 32 * m, g);
-        }
-      } else {
-        const OpT* krow = sKinv + (16 * j + l16) * L::LDK;
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) M::mma(acc, M::ld_cont(krow, 32 * m, g), M::ld_cont(arow, 32 * m, g));
-      }
-    } else {
-      const KinvT* krow = sKinv + (16 * j + l16) * L::LDK;
-      const float* dv = s_D + L::dslot(i, j) * DK;
-      if constexpr (sizeof(OpT) == 2) {
-        if (*s_flag == 0) {
-          const OpT* krh = reinterpret_cast<const OpT*>(krow);
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) {
-            auto fa = M::ld_cont(arow, 32 * m, g);
-            M::scale_cont(fa, dv, 32 * m, g);
-            M::mma(acc, M::ld_cont(krh, 32 * m, g), fa);
-          }
-        } else {
-          const uint16_t* arh = reinterpret_cast<const uint16_t*>(arow);
-#pragma unroll
-          for (int m = 0; m < NKP; ++m) mma_bf16_raw_scaled<true>(acc, arh, dv, krow, 32 * m, g);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          auto fa = M::ld_cont(arow, 32 * m, g);
-          M::scale_cont(fa, dv, 32 * m, g);
-          M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
-        }
-      }
-    }
-    // The tile comes out transposed (row block j's rows times block i's): a
-    // lane holds row r = 16 i + l16 at the four consecutive columns s0 ..
-    // s0 + 3, written with one store.
+  // The Gram tiles leave the MFMA transposed (row block j's rows times block
+  // i's): a lane holds row r = 16 i + l16 at the four consecutive columns
+  // s0 = 16 j + 4 g .. s0 + 3.  A gets beta_r and goes to LDS (strictly
+  // lower); P (lower, inclusive) goes straight to the record, the state
+  // kernel being its only reader.  wq: per-channel decay, the within-quarter
+  // sums of a diagonal block (s and r in one quarter), added here.
+  auto emit = [&](int i, int j, bool isP, const f32x4& acc) {
     const int r = 16 * i + l16, s0 = 16 * j + 4 * g;
     const f32x4 gs = *reinterpret_cast<const f32x4*>(s_Gi + s0);
+    // same quarter (diagonal blocks of per-channel decay): local rows rl, jj
+    const bool sameq = chan && i == j && (l16 >> 2) == g;
+    const int rl = l16 & 3;
+    const float* wq = s_wq + (4 * i + g) * L::kWQ + (isP ? 6 : 0) + rl * (rl - 1) / 2;
     if (!isP) {
       const float bt = s_bt[r], ge = s_Ge[r];
       f32x4 v;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float val = acc[jj] * bt;
+        float val = acc[jj];
+        if (sameq && jj < rl) val += wq[jj];
+        val *= bt;
         if (headdecay) val *= __expf(ge - gs[jj]);
         v[jj] = (i > j || s0 + jj < r) ? val : 0.f;
       }
@@ -741,11 +551,11 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         float val = acc[jj];
+        if (sameq && jj < rl) val += wq[jj];
         if (headdecay) val *= __expf(gi - gs[jj]);
-        if (chan && s0 + jj == r) val = s_qk[r];
+        if (chan && s0 + jj == r) val = s_qk[r];   // no decay on the diagonal: exact
         v[jj] = (i > j || s0 + jj <= r) ? val : 0.f;
       }
-      // straight to the record (the state kernel is its only reader)
       unsigned char* dst = rec + R::oP + swz_off<R::PPRC>(r, perm_pos(s0) * static_cast<int>(sizeof(OpT)));
       if constexpr (sizeof(OpT) == 2) {
         *reinterpret_cast<f16x4*>(dst) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
@@ -753,8 +563,223 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
       }
     }
+  };
+
+  if constexpr (!chan) {
+    // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
+    // (raw rows: A only; the state kernel forms P)
+    for (int job = wave; job < (R::kRawK ? NPAIR : 2 * NPAIR); job += kPrepWaves) {
+      const bool isP = job >= NPAIR;
+      const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
+      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+      const OpT* brow = sK + (16 * j + l16) * L::LDK;
+      f32x4 acc = {0, 0, 0, 0};
+      typename M::frag fa[NKP], fb[NKP];
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) { fa[m] = M::ld_cont(arow, 32 * m, g); fb[m] = M::ld_cont(brow, 32 * m, g); }
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) M::mma(acc, fb[m], fa[m]);
+      emit(i, j, isP, acc);
+    }
+  } else {
+    // Per-key-channel decay: products of exp(g) <= 1 only (see the top of
+    // this file).  Quarter Q holds tokens 4Q .. 4Q+3; LPQ lanes share a
+    // quarter, CPT consecutive channels each.
+    constexpr int NQ = L::NQ;
+    constexpr int LPQ = (kPrepThreads / NQ < DK ? kPrepThreads / NQ : DK) < 64
+                            ? (kPrepThreads / NQ < DK ? kPrepThreads / NQ : DK) : 64;
+    constexpr int CPT = DK / LPQ;
+    static_assert(LPQ >= 4 && CPT * LPQ == DK && NQ * LPQ <= kPrepThreads, "quarter lanes");
+    const int Q = tid / LPQ, c0 = (tid % LPQ) * CPT;
+    const bool qt = tid < NQ * LPQ;   // this thread has a (quarter, channel group)
+
+    // (1b) per quarter and channel: the quarter's decay products.  k times
+    // the decay from the quarter start to the token before (Ka) and q times
+    // it through the token (Qa) replace k and q; k decayed to the quarter
+    // end goes to KB; tau4 is the whole quarter's factor.  The sums over
+    // channels of the 6 within-quarter pairs of A and of P are formed here.
+    if (qt) {
+      float w[12];
+#pragma unroll
+      for (int x = 0; x < 12; ++x) w[x] = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const int c = c0 + e;
+        float a[4], kx[4], qx[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
+          kx[t] = static_cast<float>(sK[r * L::LDK + c]);
+          qx[t] = static_cast<float>(sQ[r * L::LDK + c]);
+        }
+        float pre = 1.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          sK[r * L::LDK + c] = (OpT)(kx[t] * pre);
+          pre *= a[t];
+          sQ[r * L::LDK + c] = (OpT)(qx[t] * pre);
+        }
+        float suf = 1.f;
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+          sKB[(4 * Q + t) * L::LDK + c] = (OpT)(kx[t] * suf);
+          suf *= a[t];
+        }
+        s_tau4[Q * DK + c] = pre;
+        // A_rs: decay of s+1 .. r-1; P_rs: of s+1 .. r  (pairs 10 20 21 30 31 32)
+        const float a12 = a[1] * a[2], a23 = a[2] * a[3];
+        w[0] += kx[1] * kx[0];
+        w[1] += kx[2] * kx[0] * a[1];
+        w[2] += kx[2] * kx[1];
+        w[3] += kx[3] * kx[0] * a12;
+        w[4] += kx[3] * kx[1] * a[2];
+        w[5] += kx[3] * kx[2];
+        w[6] += qx[1] * kx[0] * a[1];
+        w[7] += qx[2] * kx[0] * a12;
+        w[8] += qx[2] * kx[1] * a[2];
+        w[9] += qx[3] * kx[0] * (a12 * a[3]);
+        w[10] += qx[3] * kx[1] * a23;
+        w[11] += qx[3] * kx[2] * a[3];
+      }
+#pragma unroll
+      for (int x = 0; x < 12; ++x) w[x] = dpp_group_sum<LPQ>(w[x]);
+      if (c0 == 0) {
+#pragma unroll
+        for (int x = 0; x < 12; ++x) s_wq[Q * L::kWQ + x] = w[x];
+      }
+    }
+    lds_barrier();
+
+    // (2a) diagonal blocks: one pass per column quarter S = 0, 1, 2.  Pass S
+    // takes the columns of quarter S (k decayed to its end, KB) against the
+    // rows of the later quarters R (Ka or Qa) times the decay of the
+    // quarters strictly between S and R; the other rows and columns are zero,
+    // so the passes add up in one accumulator.
+    for (int job = wave; job < 2 * NB; job += kPrepWaves) {
+      const bool isP = job >= NB;
+      const int i = isP ? job - NB : job;
+      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+      const OpT* krow = sKB + (16 * i + l16) * L::LDK;
+      const int Rq = l16 >> 2;      // this lane's row quarter and column quarter
+      f32x4 acc = {0, 0, 0, 0};
+      static_for<3>([&](auto S_) {
+        constexpr int S = decltype(S_)::value;
+        const float* t1 = s_tau4 + (4 * i + S + 1) * DK;
+        const float* t2 = s_tau4 + (4 * i + (S + 2 < 4 ? S + 2 : 3)) * DK;
+#pragma unroll
+        for (int m = 0; m < NKP; ++m) {
+          typename M::frag fk = Rq == S ? M::ld_cont(krow, 32 * m, g) : M::zero();
+          typename M::frag fa = Rq > S ? M::ld_cont(arow, 32 * m, g) : M::zero();
+          if constexpr (S < 2) M::scale_cont2(fa, t1, Rq >= S + 2, t2, S < 1 && Rq >= S + 3, 32 * m, g);
+          M::mma(acc, fk, fa);
+        }
+      });
+      emit(i, i, isP, acc);
+    }
+    lds_barrier();
+
+    // (2b) from quarters to blocks: Ka, Qa times the decay of the earlier
+    // quarters of their block, KB times that of the later ones; the record's
+    // chunk-referenced operands K = k exp(Gx), Q = q exp(G) and
+    // F = k exp(G_last - G); exp(G_last) per channel; and D, the decay of the
+    // blocks strictly between two blocks i - j >= 2 apart.
+    if (qt) {
+      const int blk = Q >> 2;
+      float cqp[CPT], cqs[CPT], cb[CPT], ca[CPT];
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const int c = c0 + e;
+        float t16[NB];
+#pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
+        cqp[e] = cqs[e] = 1.f;
+#pragma unroll
+        for (int q2 = 0; q2 < NQ; ++q2) {
+          const float t = s_tau4[q2 * DK + c];
+          t16[q2 >> 2] *= t;
+          if ((q2 >> 2) == blk && q2 < Q) cqp[e] *= t;
+          if ((q2 >> 2) == blk && q2 > Q) cqs[e] *= t;
+        }
+        cb[e] = ca[e] = 1.f;
+        float all = 1.f;
+#pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2) {
+          if (b2 < blk) cb[e] *= t16[b2];
+          if (b2 > blk) ca[e] *= t16[b2];
+          all *= t16[b2];
+        }
+        if (Q == 0) {
+          rvec[R::vDecC + c] = all;
+#pragma unroll
+          for (int i2 = 2; i2 < NB; ++i2) {
+            float dd = 1.f;
+#pragma unroll
+            for (int j2 = i2 - 2; j2 >= 0; --j2) {
+              dd *= t16[j2 + 1];
+              s_D[L::ddslot(i2, j2) * DK + c] = dd;
+            }
+          }
+        }
+      }
+      // (s_D overlays the within-quarter sums, whose last reader was (2a))
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * Q + t;
+        float xk[CPT], xq[CPT], xf[CPT];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          const int c = c0 + e;
+          const float ka = static_cast<float>(sK[r * L::LDK + c]);
+          const float qa = static_cast<float>(sQ[r * L::LDK + c]);
+          const float kb = static_cast<float>(sKB[r * L::LDK + c]);
+          sK[r * L::LDK + c] = (OpT)(ka * cqp[e]);
+          sQ[r * L::LDK + c] = (OpT)(qa * cqp[e]);
+          sKB[r * L::LDK + c] = (OpT)(kb * cqs[e]);
+          xk[e] = ka * (cqp[e] * cb[e]);
+          xq[e] = qa * (cqp[e] * cb[e]);
+          xf[e] = kb * (cqs[e] * ca[e]);
+        }
+        if constexpr (CPT % 4 == 0) {
+          put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
+          put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);
+          put_perm<OpT, R::PPRK>(rec + R::oF, r, c0, xf);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) {
+            const int off = swz_off<R::PPRK>(r, perm_pos(c0 + e) * static_cast<int>(sizeof(OpT)));
+            *reinterpret_cast<OpT*>(rec + R::oK + off) = (OpT)xk[e];
+            *reinterpret_cast<OpT*>(rec + R::oQ + off) = (OpT)xq[e];
+            *reinterpret_cast<OpT*>(rec + R::oF + off) = (OpT)xf[e];
+          }
+        }
+      }
+    }
+    lds_barrier();
+
+    // (2c) off-diagonal blocks i > j: the rows decayed from their block's
+    // start (Ka, Qa) times D, against k decayed to the end of block j (KB)
+    constexpr int NOFF = NB * (NB - 1) / 2;
+    for (int job = wave; job < 2 * NOFF; job += kPrepWaves) {
+      const bool isP = job >= NOFF;
+      const int pr = isP ? job - NOFF : job;
+      const int i = pair_i(pr) + 1, j = pair_j(pr);    // pairs of the strictly lower triangle
+      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+      const OpT* krow = sKB + (16 * j + l16) * L::LDK;
+      const float* dv = s_D + L::ddslot(i > j + 1 ? i : 2, i > j + 1 ? j : 0) * DK;
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < NKP; ++m) {
+        auto fa = M::ld_cont(arow, 32 * m, g);
+        if (i > j + 1) M::scale_cont(fa, dv, 32 * m, g);
+        M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
+      }
+      emit(i, j, isP, acc);
+    }
   }
   lds_barrier();
+
 
   // ============ phase 3: T = (I + A)^-1 (fp32) ============
   if (wave == 0) {
@@ -775,8 +800,8 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       for (int r = 0; r < 16; ++r) sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];
     }
   } else {
-    // meanwhile the other waves write the finished record tiles
-    // P above the block diagonal (never produced by the Gram) is zero
+    // meanwhile the other waves zero P above the block diagonal (never
+    // produced by the Gram)
     constexpr int VE = 16 / sizeof(OpT);
     constexpr int RowV = R::NCOL / VE;       // 16-byte pieces per P row
     for (int idx = tid - 64; !R::kRawK && idx < C * RowV; idx += kPrepThreads - 64) {
@@ -786,28 +811,6 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 #pragma unroll
         for (int e = 0; e < VE; ++e) x[e] = 0.f;
         put_perm<OpT, R::PPRC>(rec + R::oP, r, s0, x);
-      }
-    }
-    if (chan) {
-      // chunk-referenced decays for the state step: K * exp(Gx), Q * exp(G)
-      constexpr int RowK = DK / VE;
-      for (int idx = tid - 64; idx < C * RowK; idx += kPrepThreads - 64) {
-        const int r = idx / RowK, c = (idx % RowK) * VE;
-        const float* cb = s_Cb + (r >> 4) * DK + c;
-        const bool steep = sizeof(OpT) == 2 && *s_flag != 0;   // tiles hold bf16 patterns
-        auto get = [&](const OpT* tile, int e) {
-          if (sizeof(OpT) == 2 && steep)
-            return bf16_to_f32(reinterpret_cast<const uint16_t*>(tile)[r * L::LDK + c + e]);
-          return static_cast<float>(tile[r * L::LDK + c + e]);
-        };
-        float kx[VE], qx[VE];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          kx[e] = get(sK, e) * cb[e];
-          qx[e] = get(sQ, e) * cb[e];
-        }
-        put_perm<OpT, R::PPRK>(rec + R::oK, r, c, kx);
-        put_perm<OpT, R::PPRK>(rec + R::oQ, r, c, qx);
       }
     }
   }

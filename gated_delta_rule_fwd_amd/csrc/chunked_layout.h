@@ -106,12 +106,12 @@ struct RecLayout {
 template <int DK, int C, int OpBytes, bool Raw>
 struct PrepLayout {
   static constexpr int NB = C / 16;                 // 16-token blocks per chunk
+  static constexpr int NQ = C / 4;                  // 4-token quarters per chunk (per-channel decay)
   static constexpr int NCOL = C < 32 ? 32 : C;      // token columns read by 32-wide k steps
   static constexpr int PAD = 16 / OpBytes;          // 16-byte row padding
   static constexpr int LDK = DK + PAD;              // row stride of [C][DK] operand tiles
   static constexpr int LC = NCOL + PAD;             // row stride of the [C][tokens] P tile
   static constexpr int LF = C + 4;                  // row stride of fp32 [C][C] tiles
-  static constexpr int KinvBytes = OpBytes == 2 ? 2 : 4;
 
   static constexpr size_t kRowTile = size_t(C) * LDK * OpBytes;     // [C][DK]
   static constexpr size_t kCC = size_t(C) * LC * OpBytes;            // [C][tokens] operand
@@ -119,39 +119,46 @@ struct PrepLayout {
   static constexpr size_t kGst = size_t(C) * DK * OpBytes;           // staged per-channel gate
 
   // Regions and what they hold:
-  //   Q    q normalised (per-channel: and decayed)                load .. Gram
+  //   Q    q normalised; per-channel decay: times the decay products of its
+  //        quarter (Gram of the diagonal blocks), then of its block (the
+  //        off-diagonal ones)                                       load .. Gram
   //        (none with raw rows)
-  //   K    k normalised (per-channel: and decayed)                load .. Gram
+  //   K    k normalised; per-channel decay: likewise                load .. Gram
   //   AM   fp32 A (Gram .. inverse); per-channel: staged gate first (load)
-  //   RA   per-channel: the inverse-prefix Gram factor Kinv (load .. Gram),
-  //        then fp32 T; otherwise, where it fits, fp32 T over the Q and K
-  //        tiles, dead after the Gram
+  //   KB   per-channel decay: k decayed to the end of its quarter, then of
+  //        its block                                                load .. Gram
+  //   T    fp32 T: over the Q (per-channel) or the Q and K tiles (otherwise)
+  //        where it fits, dead after the Gram; else a region of its own
   // (P goes from the MFMA accumulators straight to the record.)
   static constexpr size_t oQ = 0;
   static constexpr size_t oK = Raw ? 0 : chunked_layout::al(oQ + kRowTile);
   static constexpr size_t oAM = chunked_layout::al(oK + kRowTile);
   static constexpr size_t szAM(bool ch) { return ch ? chunked_layout::mx(kF32CC, kGst) : kF32CC; }
+  static constexpr size_t oKB = chunked_layout::al(oAM + szAM(true));
   static constexpr bool kTinQK = kF32CC <= oAM - oQ;   // T fits over Q and K
+  static constexpr bool kTinQ = kF32CC <= kRowTile;    // T fits over Q
+  // the T region
   static constexpr size_t oRA(bool ch) {
-    return (!ch && kTinQK) ? oQ : chunked_layout::al(oAM + szAM(ch));
+    return ch ? (kTinQ ? oQ : chunked_layout::al(oKB + kRowTile))
+              : (kTinQK ? oQ : chunked_layout::al(oAM + szAM(false)));
   }
-  static constexpr size_t oKinv(bool ch) { return oRA(ch); }
-  static constexpr size_t szRA(bool ch) {
-    return (!ch && kTinQK) ? 0 : chunked_layout::mx(ch ? size_t(C) * LDK * KinvBytes : 0, kF32CC);
+  static constexpr size_t tilesEnd(bool ch) {
+    return ch ? chunked_layout::al(chunked_layout::mx(oKB + kRowTile, oRA(true) + kF32CC))
+              : (kTinQK ? chunked_layout::al(oAM + szAM(false)) : chunked_layout::al(oRA(false) + kF32CC));
   }
-  // D[i][j], j < i: the A-operand factor of the off-diagonal Gram block (i, j)
-  // (decay of the blocks strictly between j and i, times the factor that turns
-  // block j's inverse-prefix operand into its decay-to-block-end one)
-  static constexpr int ND = NB >= 2 ? NB * (NB - 1) / 2 : 1;
-  static constexpr int dslot(int i, int j) { return i * (i - 1) / 2 + j; }
-  // fp32 vectors: bt Gi Ge qk (each C), misc[16]; per-channel: tau[NB] Cb[NB] rsq[NB] D[ND] (each DK)
+  // per-channel decay: off-diagonal block pairs (i, j) with i - j >= 2 take
+  // the decay of the blocks strictly between them as a scale, D[ddslot]
+  static constexpr int NDD = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 1;
+  static constexpr int ddslot(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
+  static constexpr int kWQ = 12;                    // within-quarter sums per quarter
+  static constexpr int kWQD = NQ * kWQ > NDD * DK ? NQ * kWQ : NDD * DK;
+  // fp32 vectors: bt Gi Ge qk (each C), misc[16]; per-channel: tau4[NQ][DK]
+  // (the decay factor of each quarter), then the within-quarter sums [NQ][12],
+  // later (same place) D[NDD][DK]
   static constexpr int kVecRows = 4;
-  static constexpr int kChanVecs = 3 * NB + ND;
-  static constexpr size_t oVec(bool ch) {
-    return (!ch && kTinQK) ? chunked_layout::al(oAM + szAM(ch)) : chunked_layout::al(oRA(ch) + szRA(ch));
-  }
+  static constexpr size_t oVec(bool ch) { return tilesEnd(ch); }
   static constexpr size_t szVec(bool ch) {
-    return size_t(kVecRows) * C * 4 + 64 + (ch ? size_t(kChanVecs) * DK * 4 : 0);
+    return size_t(kVecRows) * C * 4 + 64 + (ch ? (size_t(NQ) * DK + kWQD) * 4 : 0);
   }
   static constexpr size_t bytes(bool ch) { return chunked_layout::al(oVec(ch) + szVec(ch)); }
 };

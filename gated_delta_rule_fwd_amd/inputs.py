@@ -49,7 +49,7 @@ class Workload:
     DV: int
     chunk: int            # 0 for decode
     decay: str            # "none" | "head_small" | "head_logsig" | "channel_softplus"
-                          # | "channel_strong" | "channel_steep"
+                          # | "channel_strong" | "channel_steep" | "channel_extreme"
     init_state: bool
     decode: bool = False
     seed: int = 1000
@@ -62,8 +62,8 @@ class Workload:
     @property
     def decay_kind(self) -> int:
         return {"none": DECAY_NONE, "channel_softplus": DECAY_CHANNEL,
-                "channel_strong": DECAY_CHANNEL,
-                "channel_steep": DECAY_CHANNEL}.get(self.decay, DECAY_HEAD)
+                "channel_strong": DECAY_CHANNEL, "channel_steep": DECAY_CHANNEL,
+                "channel_extreme": DECAY_CHANNEL}.get(self.decay, DECAY_HEAD)
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -127,6 +127,9 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         # strong per-channel decay: a 16-token block decays by about exp(-20)
         # (steeper than exp(-16) in most channels), still far from fp32 underflow
         decay = act(-_softplus(1.0 + normal(lead + (w.DK,))))
+    elif w.decay == "channel_extreme":
+        # about -10 per token: a 16-token block decays by about exp(-160)
+        decay = act(-_softplus(10.0 + 2.0 * normal(lead + (w.DK,))))
     else:
         raise ValueError(w.decay)
     init = None

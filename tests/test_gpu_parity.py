@@ -85,6 +85,12 @@ CHUNK_CASES = [
     ("kda_d128", dict(B=1, T=200, H=2, decay="channel_steep", init_state=True)),
     ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_steep")),
     ("fp32_small", dict(T=70, chunk=32, decay="channel_steep", init_state=True)),
+    # per-channel decay of about -10 per token (16-token blocks near exp(-160),
+    # far past fp32 range for any product referenced to a block start)
+    ("kda_d128", dict(B=1, T=200, H=2, decay="channel_extreme", init_state=True)),
+    ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_extreme")),
+    ("kda_d128", dict(B=1, T=70, H=2, DK=32, DV=32, chunk=16, decay="channel_extreme")),
+    ("fp32_small", dict(T=100, chunk=64, decay="channel_extreme", init_state=True)),
     # fp32 at DK = 128: the state kernel's single-buffer LDS plan
     ("fp32_small", dict(B=1, T=150, H=2, DK=128, DV=128, chunk=64, init_state=True)),
     ("fp32_small", dict(B=1, T=100, H=2, DK=128, DV=64, chunk=64, decay="channel_softplus")),
@@ -104,6 +110,36 @@ def test_chunked_matches_oracle(name, kw):
     o_ref, S_ref = kda_scan(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
                             inp["initial_state"])
     check("chunked", o, S, o_ref, S_ref, TOL[w.dtype])
+
+
+EXTREME = [("kda_d128", dict(B=1, T=200, H=3, init_state=True)),
+           ("kda_d128", dict(B=1, T=77, H=2, chunk=32, DK=64, DV=64)),
+           ("fp32_small", dict(T=90, H=2, chunk=16, decay="channel_softplus", init_state=True))]
+
+
+@pytest.mark.parametrize("name,kw", EXTREME, ids=lambda x: str(x))
+def test_chunked_extreme_channel_decays(name, kw):
+    """Any decay <= 0 is legal (ejkernel kda parameter list): one channel
+    decays by -100 per token, another is -inf at some tokens (exp(-inf) = 0
+    wipes that state row), another -1e4 at one token; the other channels
+    keep the workload's decay.  Chunked and recurrent against the oracle."""
+    w = small(name, **kw)
+    announce(f"extreme decays {w}")
+    inp = make_inputs(w)
+    dec = inp["decay"]
+    dec[..., 7] = -100.0
+    dec[:, 5::17, :, 3] = float("-inf")
+    dec[:, 40, :, 11] = -1e4
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"])
+    o, S = fwd_chunked(*args, chunk_size=w.chunk)
+    o_r, S_r = fwd_recurrent(*args)
+    torch.cuda.synchronize()
+    o_ref, S_ref = kda_scan(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                            inp["initial_state"])
+    assert np.isfinite(o_ref).all() and np.isfinite(S_ref).all()
+    check("chunked extreme", o, S, o_ref, S_ref, TOL[w.dtype])
+    check("recurrent extreme", o_r, S_r, o_ref, S_ref, TOL[w.dtype])
 
 
 # -------------------------------------------------------------- recurrent --

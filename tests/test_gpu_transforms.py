@@ -165,10 +165,6 @@ def test_transforms_off_is_bitwise_the_plain_call():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.xfail(strict=True, reason=(
-    "known precision limit: 88% of these chunks have a 16-token block decaying faster than "
-    "exp(-16) and take the prep kernel's bf16-operand fallback; at full length the output "
-    "error reaches 2.13e-2 rms against the 2e-2 bar (state 4.8e-3)"))
 def test_full_size_raw_gate_kda_every_head():
     # kda_d128 at its full size from the raw gate and raw beta, in the
     # configuration of the benchmark's raw-gate extra (floor -5, sigmoid);

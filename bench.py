@@ -234,12 +234,25 @@ def cpu_baseline(w):
         nb += 1
     dt = time.perf_counter() - t0
     # threads actually used: the process's CPU time over the wall time
-    cores = max(1, round((time.process_time() - c0) / dt))
-    return {"value": nb * w.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
+    used = max(1, round((time.process_time() - c0) / dt))
+    return {"value": nb * w.T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "seconds": round(dt, 2), "host_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(),
             "sample": f"{w.name}: {nb} of {w.B} sequences x {w.H} heads x {w.T} tokens, "
                       f"NumPy fp64 sequential scan (numpy {np.__version__}); "
-                      f"cores = process CPU time / wall time"}
+                      f"cores = threads used (process CPU time / wall time), "
+                      f"host_cores = cores this process may run on"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def stored_traffic(name):
@@ -258,6 +271,7 @@ def stored_traffic(name):
 TRAFFIC_KERNELS = {
     "gdn_d128": ["prep_kernel<128, 64, kda::bf16_t, 1, false>", "state_kernel<128, 64, 64, kda::bf16_t, 1>"],
     "kda_d128": ["prep_kernel<128, 64, kda::bf16_t, 2, false>", "state_kernel<128, 32, 64, kda::bf16_t, 2>"],
+    "deltanet_d64": ["prep_kernel<64, 64, kda::bf16_t, 0, false>", "state_kernel<64, 16, 64, kda::bf16_t, 0>"],
     "decode_d128": ["decode_kernel<128, 128, kda::bf16_t>"],
 }
 # Later workloads of the same run reuse some of these kernels (the grouped-head
@@ -266,6 +280,7 @@ TRAFFIC_KERNELS = {
 TRAFFIC_WINDOW_END = {
     "gdn_d128": "prep_kernel<128, 64, kda::bf16_t, 2,",
     "kda_d128": "prep_kernel<128, 64, kda::bf16_t, 2, true>",
+    "deltanet_d64": None,
     "decode_d128": None,
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -401,7 +416,18 @@ def main():
             _, k4r, _ = time_chunked(w4, max(3, args.steps // 2), args.warmup, dev, raw=True)
             extra[w4.name + "_raw_gate"] = {
                 "tokens_per_s": round(w4.B * w4.T / (k4r * 1e-3), 1), "kernel_ms_mean": round(k4r, 4),
+                "hbm_frac": round(chunked_bytes(w4) / (k4r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "transforms": "gate -exp(A_log) softplus(gate + dt_bias) floored at -5, beta sigmoid"}
+        # the ungated D64 workload (B4 T2048 H16; its 85 MB fit in the 256 MB
+        # last-level cache, so the figure is cache-warm)
+        w2 = WORKLOADS["deltanet_d64"]
+        if w2.name != w.name:
+            _, k2, _ = time_chunked(w2, max(3, args.steps // 2), args.warmup, dev)
+            extra[w2.name] = {"tokens_per_s": round(w2.B * w2.T / (k2 * 1e-3), 1),
+                              "kernel_ms_mean": round(k2, 4),
+                              "algorithmic_bytes": chunked_bytes(w2),
+                              "hbm_frac": round(chunked_bytes(w2) / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac_dense_count": round(chunked_flops(w2) / (k2 * 1e-3) / MFMA_PEAK_F16, 4)}
         # the same shape with grouped value heads: 4 q/k heads, 16 value heads
         wg = w.scaled(H=4, HV=w.H)
         _, kg, _ = time_chunked(wg, max(3, args.steps // 2), args.warmup, dev)

@@ -286,6 +286,46 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* bet
   return kda::to_status(kda::launch_decode(a, s));
 }
 
+size_t kda_bwd_workspace_bytes(int B, int T, int HV, int DK, int DV) {
+  if (B < 1 || T < 1 || HV < 1 || !kda::dim_ok(DK) || !kda::dim_ok(DV)) return 0;
+  return kda::bwd_workspace_bytes(B, T, HV, DK, DV);
+}
+
+int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const void* decay,
+            int decay_kind, const float* initial_state, const float* d_o,
+            const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
+            float* ddecay, float* d_initial_state, int B, int T, int H, int HV, int DK, int DV,
+            int dtype, float softmax_scale, int use_qk_l2norm, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype, 0);
+  if (st != KDA_OK) return st;
+  if (T != 0 && (!d_o || !dq || !dk || !dv || !dbeta)) return KDA_ERR_NULL;
+  if (T != 0 && decay_kind != KDA_DECAY_NONE && !ddecay) return KDA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // no tokens: the initial state's gradient is the final state's
+    if (!d_initial_state) return KDA_OK;
+    return kda::to_status(kda::launch_state_copy(d_final_state, d_initial_state,
+                                                 static_cast<long>(B) * HV * DK * DV, s));
+  }
+  if (!workspace || !kda::ws_aligned(workspace) ||
+      workspace_bytes < kda::bwd_workspace_bytes(B, T, HV, DK, DV))
+    return KDA_ERR_WORKSPACE;
+  kda::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.beta = beta;
+  a.decay = decay_kind == KDA_DECAY_NONE ? nullptr : decay;
+  a.decay_kind = decay_kind;
+  a.init = initial_state; a.dout = d_o; a.dfinal = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta;
+  a.ddecay = decay_kind == KDA_DECAY_NONE ? nullptr : ddecay;
+  a.dinit = d_initial_state;
+  a.ckpt = static_cast<float*>(workspace);
+  a.B = B; a.T = T; a.H = HV; a.Hk = H; a.DK = DK; a.DV = DV; a.dtype = dtype;
+  a.scale = kda::resolve_scale(softmax_scale, DK);
+  a.l2norm = use_qk_l2norm ? 1 : 0;
+  return kda::to_status(kda::launch_bwd(a, s));
+}
+
 const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "ok";
@@ -299,6 +339,6 @@ const char* kda_status_string(int status) {
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 200; }
+int kda_abi_version(void) { return 201; }
 
 }  // extern "C"

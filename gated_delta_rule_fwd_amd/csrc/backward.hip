@@ -1,0 +1,362 @@
+// Backward of the gated delta rule: the gradients of (o, final state) with
+// respect to q, k, v, beta, the decay and the initial state, given do and the
+// final-state gradient (TileOPs "Linear Attention Operators",
+// DeltaNetChunkBwdOp and GLAChunkBwdOp; kda-neuron-kernels README,
+// kda_chunk_step_exact_bwd: dq, dk, dv, dg, dbeta, dstate_in).
+//
+// Reverse-mode differentiation of the recurrence, token by token (the
+// forward: r = S^T k, delta = beta (v - r), S' = diag(a) S + k delta^T,
+// o = S'^T q, a = exp(g), with q and k normalised and q scaled):
+//
+//   dS' += q do^T;  dq = S' do;  ddelta = dS'^T k;  dk = dS' delta - beta S ddelta
+//   da = rowsum(dS' * S);  dbeta = ddelta . (v - r);  dv = beta ddelta
+//   dS = diag(a) dS' - beta k ddelta^T
+//
+// Every value column of the state evolves on its own given q, k, beta and the
+// decay, so one wave takes one column (lanes over key channels): its state
+// column and gradient column sit in registers.  The reverse pass needs the
+// state before every token: a first pass stores each column every 16 tokens
+// in the workspace; the reverse pass recomputes the 16 states of a block into
+// registers from there and steps back through them.  dv and the column's
+// initial-state gradient belong to the wave alone; dq, dk, dbeta and the
+// decay gradient are sums over columns, gathered per block in LDS by the four
+// waves of a workgroup and added to the outputs with one atomic add per
+// element and workgroup (the order of those additions varies from run to
+// run, within fp32 rounding).  A last kernel carries dq and dk through the
+// L2 norm and the scale.  All arithmetic is fp32.
+//
+// This is the plain form of the backward: time grows with T dependent
+// token steps per column, and the work is not shaped for MFMA.
+#include "common.h"
+#include "launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int kBwdThreads = 256;   // four waves: four value columns of one (batch, head)
+constexpr int kTB = 16;            // tokens per block (the checkpoint interval)
+
+template <int DK, typename In>
+struct BwdStage {
+  float q[kTB][DK], k[kTB][DK], a[kTB][DK];   // normalised q (scaled), k; exp(decay) per channel
+  float b[kTB], ah[kTB];                      // beta; exp(decay) per head
+  // per-block sums over the workgroup's columns
+  float dq[kTB][DK], dk[kTB][DK], dg[kTB][DK];
+  float db[kTB], dgh[kTB];
+};
+
+template <int DK, int DV, typename In>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
+    const float* __restrict__ init, const float* __restrict__ dout, const float* __restrict__ dfinal,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
+    float* __restrict__ ddecay, float* __restrict__ dinit, float* __restrict__ ckpt,
+    int T, int H, int Hk, float scale, int l2norm) {
+  constexpr int CPL = (DK + 63) / 64;   // key channels per lane: c = lane + 64 e
+  constexpr int V = act<In>::kVec;
+  constexpr int LPR = DK / V;           // lanes per token row in the staging loads
+  __shared__ BwdStage<DK, In> st;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncg = DV / 4;                                  // workgroups per (b, h)
+  const int bh = blockIdx.x / ncg;
+  const int b = bh / H, h = bh % H;
+  const int j = (blockIdx.x % ncg) * 4 + wave;             // this wave's value column
+  const int hk = h / (H / Hk);
+  const int nsub = (T + kTB - 1) / kTB;
+  const bool chan = decay_kind == DECAY_CHANNEL, headd = decay_kind == DECAY_HEAD;
+  bool live[CPL];
+  int ch[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    ch[e] = lane + 64 * e;
+    live[e] = ch[e] < DK;
+  }
+  auto tok = [&](int t) { return static_cast<long>(b) * T + t; };
+  // checkpoint of block n: [bh][n][column][DK]
+  auto ck = [&](int n) { return ckpt + ((static_cast<long>(bh) * nsub + n) * DV + j) * DK; };
+
+  // Stage the tokens of block n: normalised q (scaled) and k, decay factors, beta.
+  auto stage = [&](int n) {
+    const int t0 = n * kTB, nt = min(kTB, T - t0);
+    for (int idx = tid; idx < kTB * LPR; idx += kBwdThreads) {
+      const int tt = idx / LPR, seg = idx % LPR;
+      float qv[V], kv[V];
+      const bool in = tt < nt;
+      const long kb = (tok(t0 + tt) * Hk + hk) * DK + seg * V;
+      if (in) {
+        act<In>::load_vec(q + kb, qv);
+        act<In>::load_vec(k + kb, kv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) qv[e] = kv[e] = 0.f;
+      }
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
+      sq = group_sum<LPR>(sq);
+      sk = group_sum<LPR>(sk);
+      const float iq = (l2norm ? inv_norm(sq) : 1.f) * scale;
+      const float ik = l2norm ? inv_norm(sk) : 1.f;
+      float gv[V];
+      if (chan && in) {
+        act<In>::load_vec(decay + (tok(t0 + tt) * H + h) * DK + seg * V, gv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) gv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        st.q[tt][seg * V + e] = qv[e] * iq;
+        st.k[tt][seg * V + e] = kv[e] * ik;
+        st.a[tt][seg * V + e] = __expf(gv[e]);
+      }
+    }
+    if (tid < kTB) {
+      const bool in = tid < nt;
+      const long tk = tok(t0 + tid) * H + h;
+      st.b[tid] = in ? act<In>::load1(beta + tk) : 0.f;
+      st.ah[tid] = __expf(headd && in ? act<In>::load1(decay + tk) : 0.f);
+    }
+  };
+
+  // ---- pass 1: the state column at the start of every block ----
+  float s[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e)
+    s[e] = (init && live[e]) ? init[(static_cast<long>(bh) * DK + ch[e]) * DV + j] : 0.f;
+  for (int n = 0; n < nsub; ++n) {
+    stage(n);
+    __syncthreads();
+    float* c = ck(n);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      if (live[e]) c[ch[e]] = s[e];
+    const int t0 = n * kTB, nt = min(kTB, T - t0);
+    for (int i = 0; i < nt; ++i) {
+      float r = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) r += live[e] ? s[e] * st.k[i][ch[e]] : 0.f;
+      r = dpp_group_sum<64>(r);
+      const float delta = st.b[i] * (act<In>::load1(v + (tok(t0 + i) * H + h) * DV + j) - r);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+        if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
+    }
+    __syncthreads();
+  }
+
+  // ---- pass 2: blocks in reverse ----
+  float ds[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e)
+    ds[e] = (dfinal && live[e]) ? dfinal[(static_cast<long>(bh) * DK + ch[e]) * DV + j] : 0.f;
+  for (int n = nsub - 1; n >= 0; --n) {
+    stage(n);
+    for (int idx = tid; idx < kTB * DK; idx += kBwdThreads) {
+      (&st.dq[0][0])[idx] = 0.f;
+      (&st.dk[0][0])[idx] = 0.f;
+      (&st.dg[0][0])[idx] = 0.f;
+    }
+    if (tid < kTB) st.db[tid] = st.dgh[tid] = 0.f;
+    __syncthreads();
+    const int t0 = n * kTB, nt = min(kTB, T - t0);
+    // recompute the block's states: sp[i] enters token t0 + i
+    float sp[kTB][CPL], rr[kTB], vv[kTB];
+    const float* c = ck(n);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s[e] = live[e] ? c[ch[e]] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kTB; ++i) {
+      if (i < nt) {
+        float r = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          sp[i][e] = s[e];
+          r += live[e] ? s[e] * st.k[i][ch[e]] : 0.f;
+        }
+        r = dpp_group_sum<64>(r);
+        rr[i] = r;
+        vv[i] = act<In>::load1(v + (tok(t0 + i) * H + h) * DV + j);
+        const float delta = st.b[i] * (vv[i] - r);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
+      }
+    }
+    // s now holds the state after the block
+#pragma unroll
+    for (int i = kTB - 1; i >= 0; --i) {
+      if (i < nt) {
+        const float bt = st.b[i], delta = bt * (vv[i] - rr[i]);
+        const float dov = dout[(tok(t0 + i) * H + h) * DV + j];
+        float dqv[CPL], ddl = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const float snew = i + 1 < nt ? sp[i + 1 < kTB ? i + 1 : i][e] : s[e];
+          if (live[e]) {
+            ds[e] += st.q[i][ch[e]] * dov;
+            dqv[e] = snew * dov;
+            ddl += ds[e] * st.k[i][ch[e]];
+          }
+        }
+        ddl = dpp_group_sum<64>(ddl);
+        float dgs = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          if (live[e]) {
+            const float a = chan ? st.a[i][ch[e]] : st.ah[i];
+            const float dkv = ds[e] * delta - bt * ddl * sp[i][e];
+            const float dga = ds[e] * sp[i][e] * a;   // d(decay) = a * da
+            atomicAdd(&st.dq[i][ch[e]], dqv[e]);
+            atomicAdd(&st.dk[i][ch[e]], dkv);
+            if (chan) atomicAdd(&st.dg[i][ch[e]], dga);
+            dgs += dga;
+            ds[e] = a * ds[e] - bt * ddl * st.k[i][ch[e]];
+          }
+        }
+        if (headd) dgs = dpp_group_sum<64>(dgs);
+        if (lane == 0) {
+          atomicAdd(&st.db[i], ddl * (vv[i] - rr[i]));
+          if (headd) atomicAdd(&st.dgh[i], dgs);
+          dv[(tok(t0 + i) * H + h) * DV + j] = bt * ddl;
+        }
+      }
+    }
+    __syncthreads();
+    // the block's sums over this workgroup's columns, into the outputs
+    for (int idx = tid; idx < nt * DK; idx += kBwdThreads) {
+      const int tt = idx / DK, cc = idx % DK;
+      const long qo = (tok(t0 + tt) * Hk + hk) * DK + cc;
+      atomicAdd(dq + qo, st.dq[tt][cc]);
+      atomicAdd(dk + qo, st.dk[tt][cc]);
+      if (chan) atomicAdd(ddecay + (tok(t0 + tt) * H + h) * DK + cc, st.dg[tt][cc]);
+    }
+    if (tid < nt) {
+      atomicAdd(dbeta + tok(t0 + tid) * H + h, st.db[tid]);
+      if (headd) atomicAdd(ddecay + tok(t0 + tid) * H + h, st.dgh[tid]);
+    }
+    __syncthreads();
+  }
+  if (dinit) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      if (live[e]) dinit[(static_cast<long>(bh) * DK + ch[e]) * DV + j] = ds[e];
+  }
+}
+
+// dq, dk hold the gradients of the normalised (and scaled) rows; carry them
+// through x -> scale x / max(||x||, 1e-12), in place.  One wave per row of q
+// or k (rows of q first, then of k).
+template <int DK, typename In>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(const In* __restrict__ q, const In* __restrict__ k,
+                                                       float* __restrict__ dq, float* __restrict__ dk,
+                                                       long rows, float scale, int l2norm) {
+  constexpr int CPL = (DK + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const long w = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (w >= 2 * rows) return;
+  const bool isq = w < rows;
+  const long row = isq ? w : w - rows;
+  const In* x = (isq ? q : k) + row * DK;
+  float* g = (isq ? dq : dk) + row * DK;
+  const float sc = isq ? scale : 1.f;
+  float xv[CPL], gv[CPL], sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const int c = lane + 64 * e;
+    xv[e] = c < DK ? act<In>::load1(x + c) : 0.f;
+    gv[e] = c < DK ? g[c] : 0.f;
+    sq += xv[e] * xv[e];
+  }
+  if (!l2norm) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      if (lane + 64 * e < DK) g[lane + 64 * e] = sc * gv[e];
+    return;
+  }
+  sq = dpp_group_sum<64>(sq);
+  const float n = sqrtf(sq);
+  if (n > 1e-12f) {
+    const float in = 1.f / n;
+    float proj = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) proj += xv[e] * in * gv[e];
+    proj = dpp_group_sum<64>(proj);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      if (lane + 64 * e < DK) g[lane + 64 * e] = sc * (gv[e] - xv[e] * in * proj) * in;
+  } else {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      if (lane + 64 * e < DK) g[lane + 64 * e] = sc * gv[e] * 1e12f;
+  }
+}
+
+__global__ void zero_kernel(float* __restrict__ p, long n) {
+  for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<long>(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t zero(float* p, long n, hipStream_t s) {
+  if (!p || n == 0) return hipSuccess;
+  long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  zero_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
+  const long qk = static_cast<long>(a.B) * a.T * a.Hk * a.DK;
+  const long tokh = static_cast<long>(a.B) * a.T * a.H;
+  hipError_t e = zero(a.dq, qk, s);
+  if (e == hipSuccess) e = zero(a.dk, qk, s);
+  if (e == hipSuccess) e = zero(a.dbeta, tokh, s);
+  if (e == hipSuccess && a.decay_kind != DECAY_NONE)
+    e = zero(a.ddecay, a.decay_kind == DECAY_CHANNEL ? tokh * a.DK : tokh, s);
+  if (e != hipSuccess) return e;
+  const In* q = static_cast<const In*>(a.q);
+  const In* k = static_cast<const In*>(a.k);
+  const In* v = static_cast<const In*>(a.v);
+  const In* be = static_cast<const In*>(a.beta);
+  const In* de = static_cast<const In*>(a.decay);
+  const dim3 grid(a.B * a.H * (a.DV / 4)), block(kBwdThreads);
+  bool launched = false;
+#define KDA_BWD_CASE(dk_, dv_)                                                                   \
+  if (a.DK == dk_ && a.DV == dv_) {                                                              \
+    bwd_kernel<dk_, dv_, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.init, a.dout, \
+                                                    a.dfinal, a.dq, a.dk, a.dv, a.dbeta,         \
+                                                    a.ddecay, a.dinit, a.ckpt, a.T, a.H, a.Hk,   \
+                                                    a.scale, a.l2norm);                          \
+    launched = true;                                                                             \
+  }
+  KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
+  KDA_BWD_CASE(64, 32) KDA_BWD_CASE(64, 64) KDA_BWD_CASE(64, 128)
+  KDA_BWD_CASE(128, 32) KDA_BWD_CASE(128, 64) KDA_BWD_CASE(128, 128)
+#undef KDA_BWD_CASE
+  if (!launched) return hipErrorInvalidValue;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = static_cast<long>(a.B) * a.T * a.Hk;
+  const dim3 g2(static_cast<unsigned>((2 * rows + 3) / 4)), b2(256);
+  if (a.DK == 32) norm_bwd_kernel<32, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
+  else if (a.DK == 64) norm_bwd_kernel<64, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
+  else norm_bwd_kernel<128, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
+  const long nsub = (static_cast<long>(T) + kTB - 1) / kTB;
+  return static_cast<size_t>(B) * H * nsub * DV * DK * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
+  return a.dtype == 0 ? dispatch_bwd<float>(a, s) : dispatch_bwd<bf16_t>(a, s);
+}
+
+}  // namespace kda

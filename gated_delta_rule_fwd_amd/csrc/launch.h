@@ -27,6 +27,29 @@ struct FwdArgs {
   Transforms tf;       // raw gate / raw beta handling (all off: inputs as given)
 };
 
+// Backward of the forward above: gradients of (o, final state).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* decay;   // NULL with DECAY_NONE
+  int decay_kind;
+  const float* init;   // NULL = zeros
+  const float* dout;   // [B, T, H, DV]
+  const float* dfinal; // NULL = zeros
+  float* dq;           // [B, T, Hk, DK]
+  float* dk;
+  float* dv;           // [B, T, H, DV]
+  float* dbeta;        // [B, T, H]
+  float* ddecay;       // like decay (unused with DECAY_NONE)
+  float* dinit;        // NULL: not written
+  float* ckpt;         // workspace: bwd_workspace_bytes
+  int B, T, H, Hk, DK, DV, dtype;
+  float scale;
+  int l2norm;
+};
+
 // Each launcher assumes the front end has validated the arguments.
 hipError_t launch_decode(const FwdArgs& a, hipStream_t s);
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t s);
@@ -39,6 +62,8 @@ hipError_t launch_chunked(const FwdArgs& a, void* ws, size_t ws_bytes, hipStream
 hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int* cu_host, int nseq,
                                  void* ws, hipStream_t s);
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
 // LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.
 size_t chunked_lds_bytes(int DK, int DV, int chunk, int dtype, int decay_kind);
 // The device address of the current device's fixed scratch of

@@ -270,6 +270,47 @@ int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const v
                             int chunk_size, const float* A_log, const float* dt_bias,
                             float lower_bound, int transforms, void* stream);
 
+/*
+ * Backward: the gradients of a forward call's (o, final_state) with respect
+ * to q, k, v, beta, decay and initial_state, given the gradient of o and of
+ * the final state (TileOPs "Linear Attention Operators": DeltaNetChunkBwdOp
+ * returns dq, dk, dv, dbeta, GLAChunkBwdOp takes do and the final-state
+ * gradient; kda-neuron-kernels README, kda_chunk_step_exact_bwd: dq, dk, dv,
+ * dg, dbeta, dstate_in).  The forward it differentiates is kda_fwd_chunked /
+ * kda_fwd_recurrent with the same inputs, key-major states, no transforms.
+ *
+ *   q, k, v, beta, decay, initial_state   as the forward (activation dtype;
+ *                  initial_state NULL = zeros)
+ *   d_o            [B, T, HV, DV] fp32, the gradient of o
+ *   d_final_state  NULL (zeros) | [B, HV, DK, DV] fp32
+ *   dq, dk         [B, T, H, DK] fp32, written (the gradients of the raw q,
+ *                  k: through the L2 norm and the scale; value heads of a
+ *                  group add up)
+ *   dv             [B, T, HV, DV] fp32, written
+ *   dbeta          [B, T, HV] fp32, written
+ *   ddecay         like decay, fp32, written (ignored with KDA_DECAY_NONE)
+ *   d_initial_state NULL (not written) | [B, HV, DK, DV] fp32, written
+ *   workspace      DEVICE, 16-byte aligned, at least kda_bwd_workspace_bytes
+ *                  (the state every 16 tokens, for the reverse pass)
+ *
+ * The reverse pass is sequential over tokens, in fp32; sums over value
+ * columns are gathered with atomic adds, so results may differ in the last
+ * bits from run to run.  Errors as kda_fwd_chunked; KDA_ERR_NULL if (T > 0)
+ * d_o, dq, dk, dv, dbeta or (with a decay) ddecay is NULL; KDA_ERR_WORKSPACE
+ * as for the forward.  T == 0 copies d_final_state (or zeros) to
+ * d_initial_state.
+ */
+int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const void* decay,
+            int decay_kind, const float* initial_state, const float* d_o,
+            const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
+            float* ddecay, float* d_initial_state, int B, int T, int H, int HV, int DK, int DV,
+            int dtype, float softmax_scale, int use_qk_l2norm, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_bwd (host-only); 0 when T == 0 or the sizes are
+ * invalid. */
+size_t kda_bwd_workspace_bytes(int B, int T, int HV, int DK, int DV);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(int status);
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 200
+    assert L.kda_abi_version() == 201
     assert L.kda_status_string(0) == b"ok"
     for code in (1, 2, 3, 4, 5, 6):
         assert len(L.kda_status_string(code)) > 3
@@ -191,3 +191,25 @@ def test_noalloc_constant_and_size_limit(L):
     assert L.kda_fwd_chunked_noalloc(*args) == 6
     args[2] = None
     assert L.kda_fwd_chunked_noalloc(*args) == 1
+
+
+def test_backward_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, do=FAKE,
+                 dfin=None, dq=FAKE, dk=FAKE, dv=FAKE, db=FAKE, dg=None, dinit=None, B=1, T=8,
+                 H=1, HV=1, DK=64, DV=64, dtype=1, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return L.kda_bwd(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
+                         a["do"], a["dfin"], a["dq"], a["dk"], a["dv"], a["db"], a["dg"],
+                         a["dinit"], a["B"], a["T"], a["H"], a["HV"], a["DK"], a["DV"],
+                         a["dtype"], 0.0, 1, a["ws"], a["wsb"], None)
+    assert call(do=None) == 1
+    assert call(dq=None) == 1
+    assert call(kind=1, decay=FAKE) == 1          # a decay needs its gradient
+    assert call(DK=48) == 3
+    assert call(H=2, HV=3) == 2
+    assert call(ws=None) == 6
+    assert call(wsb=L.kda_bwd_workspace_bytes(1, 8, 1, 64, 64) - 1) == 6
+    # the state every 16 tokens for every (batch, value head)
+    assert L.kda_bwd_workspace_bytes(2, 33, 3, 64, 32) == 2 * 3 * 3 * 64 * 32 * 4
+    assert L.kda_bwd_workspace_bytes(1, 0, 1, 64, 64) == 0

@@ -340,6 +340,62 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
+
+
+def write_counters(dirs, out=COUNTERS_FILE):
+    """profiles/counters.json from rocprofv3 --pmc runs of this script (any
+    number of passes): per workload and kernel the mean of every counter
+    over that kernel's dispatches in the workload's window (as for the HBM
+    traffic), and the MFMA figures derived from them: utilisation =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and executed MFMA
+    flops = 512 x the MOPS counters."""
+    import csv
+    import glob
+    passes = []   # per pass directory: [(dispatch, kernel, counter, value)]
+    for d in dirs:
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                                 float(r["Counter_Value"])))
+        passes.append(rows)
+    res = {"_comment": "mean per dispatch of each rocprofv3 --pmc counter over the dispatches of "
+                       "each kernel of one call of the workload (dispatches before the first "
+                       "one of the next workload that reuses the kernel); mfma_util = "
+                       "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), "
+                       "mfma_flops = 512 x (MOPS_F16 + MOPS_BF16 + MOPS_F32)",
+           "kernel_hash": kernel_hash()}
+    for name, frags in TRAFFIC_KERNELS.items():
+        end = TRAFFIC_WINDOW_END[name]
+        ent = {}
+        for fr in frags:
+            sums, counts = {}, {}
+            for rows in passes:
+                last = min([i for i, k, _, _ in rows if end and end in k], default=None)
+                for i, k, c, v in rows:
+                    if fr in k and (last is None or i < last):
+                        sums[c] = sums.get(c, 0.0) + v
+                        counts[c] = counts.get(c, 0) + 1
+            if not sums:
+                continue
+            kc = {c: sums[c] / counts[c] for c in sums}
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in kc and "GRBM_GUI_ACTIVE" in kc:
+                kc["mfma_util"] = kc["SQ_VALU_MFMA_BUSY_CYCLES"] / (kc["GRBM_GUI_ACTIVE"] * SIMDS)
+            mops = [kc.get(c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                        "SQ_INSTS_VALU_MFMA_MOPS_F32")]
+            if all(m is not None for m in mops):
+                kc["mfma_flops"] = 512.0 * sum(mops)
+            ent[fr] = {c: round(v, 4) if abs(v) < 1e6 else round(v) for c, v in sorted(kc.items())}
+        res[name] = ent
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,9 +408,15 @@ def main():
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--write-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters.json from rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counters-out", default=COUNTERS_FILE)
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_counters:
+        write_counters(args.write_counters, args.counters_out)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "

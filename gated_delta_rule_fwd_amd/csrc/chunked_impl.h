@@ -598,36 +598,46 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     // it through the token (Qa) replace k and q; k decayed to the quarter
     // end goes to KB; tau4 is the whole quarter's factor.  The sums over
     // channels of the 6 within-quarter pairs of A and of P are formed here.
+    // this thread's CPT channels of one row, as one LDS access
+    typedef OpT opv __attribute__((ext_vector_type(CPT)));
+    typedef float f32v __attribute__((ext_vector_type(CPT)));
     if (qt) {
       float w[12];
 #pragma unroll
       for (int x = 0; x < 12; ++x) w[x] = 0.f;
+      opv gv[4], kv[4], qv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * Q + t;
+        gv[t] = *reinterpret_cast<const opv*>(sGst + r * DK + c0);
+        kv[t] = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
+        qv[t] = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+      }
+      opv ka[4], qa[4], kb[4];
+      f32v tau;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        const int c = c0 + e;
         float a[4], kx[4], qx[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int r = 4 * Q + t;
-          a[t] = __expf(static_cast<float>(sGst[r * DK + c]));
-          kx[t] = static_cast<float>(sK[r * L::LDK + c]);
-          qx[t] = static_cast<float>(sQ[r * L::LDK + c]);
+          a[t] = __expf(static_cast<float>(gv[t][e]));
+          kx[t] = static_cast<float>(kv[t][e]);
+          qx[t] = static_cast<float>(qv[t][e]);
         }
         float pre = 1.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int r = 4 * Q + t;
-          sK[r * L::LDK + c] = (OpT)(kx[t] * pre);
+          ka[t][e] = (OpT)(kx[t] * pre);
           pre *= a[t];
-          sQ[r * L::LDK + c] = (OpT)(qx[t] * pre);
+          qa[t][e] = (OpT)(qx[t] * pre);
         }
         float suf = 1.f;
 #pragma unroll
         for (int t = 3; t >= 0; --t) {
-          sKB[(4 * Q + t) * L::LDK + c] = (OpT)(kx[t] * suf);
+          kb[t][e] = (OpT)(kx[t] * suf);
           suf *= a[t];
         }
-        s_tau4[Q * DK + c] = pre;
+        tau[e] = pre;
         // A_rs: decay of s+1 .. r-1; P_rs: of s+1 .. r  (pairs 10 20 21 30 31 32)
         const float a12 = a[1] * a[2], a23 = a[2] * a[3];
         w[0] += kx[1] * kx[0];
@@ -643,6 +653,14 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         w[10] += qx[3] * kx[1] * a23;
         w[11] += qx[3] * kx[2] * a[3];
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * Q + t;
+        *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka[t];
+        *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa[t];
+        *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb[t];
+      }
+      *reinterpret_cast<f32v*>(s_tau4 + Q * DK + c0) = tau;
 #pragma unroll
       for (int x = 0; x < 12; ++x) w[x] = dpp_group_sum<LPQ>(w[x]);
       if (c0 == 0) {
@@ -687,60 +705,59 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     // blocks strictly between two blocks i - j >= 2 apart.
     if (qt) {
       const int blk = Q >> 2;
-      float cqp[CPT], cqs[CPT], cb[CPT], ca[CPT];
+      f32v t16[NB], cqp = 1.f, cqs = 1.f;
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        const int c = c0 + e;
-        float t16[NB];
+      for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
 #pragma unroll
-        for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
-        cqp[e] = cqs[e] = 1.f;
+      for (int q2 = 0; q2 < NQ; ++q2) {
+        const f32v t = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
+        t16[q2 >> 2] *= t;
+        if ((q2 >> 2) == blk && q2 < Q) cqp *= t;
+        if ((q2 >> 2) == blk && q2 > Q) cqs *= t;
+      }
+      f32v cb = 1.f, ca = 1.f, all = 1.f;
 #pragma unroll
-        for (int q2 = 0; q2 < NQ; ++q2) {
-          const float t = s_tau4[q2 * DK + c];
-          t16[q2 >> 2] *= t;
-          if ((q2 >> 2) == blk && q2 < Q) cqp[e] *= t;
-          if ((q2 >> 2) == blk && q2 > Q) cqs[e] *= t;
-        }
-        cb[e] = ca[e] = 1.f;
-        float all = 1.f;
+      for (int b2 = 0; b2 < NB; ++b2) {
+        if (b2 < blk) cb *= t16[b2];
+        if (b2 > blk) ca *= t16[b2];
+        all *= t16[b2];
+      }
+      if (Q == 0) {
+        *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
 #pragma unroll
-        for (int b2 = 0; b2 < NB; ++b2) {
-          if (b2 < blk) cb[e] *= t16[b2];
-          if (b2 > blk) ca[e] *= t16[b2];
-          all *= t16[b2];
-        }
-        if (Q == 0) {
-          rvec[R::vDecC + c] = all;
+        for (int i2 = 2; i2 < NB; ++i2) {
+          f32v dd = 1.f;
 #pragma unroll
-          for (int i2 = 2; i2 < NB; ++i2) {
-            float dd = 1.f;
-#pragma unroll
-            for (int j2 = i2 - 2; j2 >= 0; --j2) {
-              dd *= t16[j2 + 1];
-              s_D[L::ddslot(i2, j2) * DK + c] = dd;
-            }
+          for (int j2 = i2 - 2; j2 >= 0; --j2) {
+            dd *= t16[j2 + 1];
+            *reinterpret_cast<f32v*>(s_D + L::ddslot(i2, j2) * DK + c0) = dd;
           }
         }
       }
       // (s_D overlays the within-quarter sums, whose last reader was (2a))
+      const f32v fkq = cqp * cb, ff = cqs * ca;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 4 * Q + t;
+        const opv ka = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
+        const opv qa = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+        const opv kb = *reinterpret_cast<const opv*>(sKB + r * L::LDK + c0);
+        opv ka16, qa16, kb16;
         float xk[CPT], xq[CPT], xf[CPT];
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-          const int c = c0 + e;
-          const float ka = static_cast<float>(sK[r * L::LDK + c]);
-          const float qa = static_cast<float>(sQ[r * L::LDK + c]);
-          const float kb = static_cast<float>(sKB[r * L::LDK + c]);
-          sK[r * L::LDK + c] = (OpT)(ka * cqp[e]);
-          sQ[r * L::LDK + c] = (OpT)(qa * cqp[e]);
-          sKB[r * L::LDK + c] = (OpT)(kb * cqs[e]);
-          xk[e] = ka * (cqp[e] * cb[e]);
-          xq[e] = qa * (cqp[e] * cb[e]);
-          xf[e] = kb * (cqs[e] * ca[e]);
+          const float k1 = static_cast<float>(ka[e]), q1 = static_cast<float>(qa[e]);
+          const float b1 = static_cast<float>(kb[e]);
+          ka16[e] = (OpT)(k1 * cqp[e]);
+          qa16[e] = (OpT)(q1 * cqp[e]);
+          kb16[e] = (OpT)(b1 * cqs[e]);
+          xk[e] = k1 * fkq[e];
+          xq[e] = q1 * fkq[e];
+          xf[e] = b1 * ff[e];
         }
+        *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka16;
+        *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa16;
+        *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb16;
         if constexpr (CPT % 4 == 0) {
           put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
           put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);

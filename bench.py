@@ -31,6 +31,8 @@ METRIC = "chunked fwd tokens/s + MFMA util (DK=DV=128); decode state GB/s vs HBM
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_F16 = 2.5e15         # MI355X dense fp16/bf16 MFMA, flop/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SIMDS = 256 * 4                # MI355X: 256 CUs of 4 SIMDs
 KERNEL_SOURCES = ["chunked_impl.h", "chunked_layout.h", "common.h"]
 
 
@@ -267,6 +269,28 @@ def stored_traffic(name):
     return ent.get("bytes_per_call")
 
 
+def stored_counters(name):
+    """The MFMA figures of one call of workload `name` from profiles/counters.json
+    (None if the counters were taken on other kernel sources): the matrix
+    units' busy fraction over the call (busy SIMD-cycles of its kernels over
+    their cycles x 1024 SIMDs; GRBM_GUI_ACTIVE is summed over the 8 XCDs)
+    and the MFMA flops executed."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = c.get(name)
+    if not ent or c.get("kernel_hash") != kernel_hash():
+        return None
+    busy = sum(k.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) for k in ent.values())
+    cycles = sum(k.get("GRBM_GUI_ACTIVE", 0) / 8 for k in ent.values())
+    flops = sum(k.get("mfma_flops", 0) for k in ent.values())
+    if not cycles:
+        return None
+    return {"mfma_busy_frac": round(busy / (cycles * SIMDS), 4), "mfma_flops_executed": flops}
+
+
 # kernel-name fragments of one call of each workload, as rocprofv3 prints them
 TRAFFIC_KERNELS = {
     "gdn_d128": ["prep_kernel<128, 64, kda::bf16_t, 1, false>", "state_kernel<128, 64, 64, kda::bf16_t, 1>"],
@@ -338,10 +362,6 @@ def write_traffic(fetch_dir, write_dir):
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
-
-
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
-SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
 
 
 def write_counters(dirs, out=COUNTERS_FILE):
@@ -445,7 +465,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
             "kernel": "prep_kernel + state_kernel (one chunked call)", "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_min": round(kern_min, 4), "algorithmic_bytes": byts,
-            "mfma_frac_dense_count": round(flops / (kern_ms * 1e-3) / MFMA_PEAK_F16, 4)}
+            "mfma_frac_dense_count": round(flops / (kern_ms * 1e-3) / MFMA_PEAK_F16, 4),
+            "mfma_counters": stored_counters(w.name)}
     line = {
         "metric": METRIC,
         "value": round(tokens / (ms_step * 1e-3), 1),

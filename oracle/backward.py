@@ -145,3 +145,60 @@ def kda_scan_bwd(q, k, v, beta, decay, initial_state, do, d_final_state=None,
     else:
         ddecay = da * a
     return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, ddecay=ddecay, d_initial_state=dS)
+
+
+def _sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def transforms_bwd(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel,
+                   allow_neg_eigval):
+    """The chain rule through the transforms (see kda_scan_bwd_transforms)."""
+    from .transforms import softplus
+    s = _sigmoid(logits)
+    dlogits = dbeta * s * (1.0 - s) * (2.0 if allow_neg_eigval else 1.0)
+    x = gate + (0.0 if dt_bias is None else dt_bias)
+    negA = -np.exp(A_log)
+    if per_channel:
+        negA = negA[:, None]
+    raw = negA * softplus(x)
+    live = np.ones_like(raw, dtype=bool) if lower_bound is None else raw >= float(lower_bound)
+    dgate = np.where(live, ddecay * negA * _sigmoid(x), 0.0)
+    contrib = np.where(live, ddecay * raw, 0.0)
+    dA = contrib.sum(axis=(0, 1, 3)) if per_channel else contrib.sum(axis=(0, 1))
+    return dict(dbeta_logits=dlogits, dgate=dgate, dA_log=dA,
+                ddt_bias=None if dt_bias is None else dgate.sum(axis=(0, 1)))
+
+
+def kda_scan_bwd_transforms(q, k, v, beta_logits, gate, A_log, initial_state, do,
+                            d_final_state=None, dt_bias=None, lower_bound=None, per_channel=False,
+                            allow_neg_eigval=False, softmax_scale=None, use_qk_l2norm=True):
+    """Gradients with respect to the raw inputs of the in-kernel transforms
+    (oracle.transforms: decay = max(-exp(A_log) softplus(gate + dt_bias),
+    lower_bound), beta = sigmoid(logits) or twice it), by the chain rule
+    through kda_scan_bwd's decay and beta gradients:
+
+        dlogits = dbeta * s (1 - s) (times 2 with allow_neg_eigval), s = sigmoid(logits)
+        where the floor is not taken:
+          dgate = ddecay * (-exp(A_log)) * sigmoid(gate + dt_bias)
+          dA_log = sum over tokens (and channels) of ddecay * decay
+          ddt_bias = sum over batch and tokens of dgate
+        where it is taken, the decay is the constant floor: no gradient.
+
+    gate [B, T, HV] or (per_channel) [B, T, HV, DK]; A_log [HV]; dt_bias
+    None | [HV] | [HV, DK].  Returns kda_scan_bwd's dict with dbeta and ddecay
+    replaced by dbeta_logits, dgate, dA_log and ddt_bias (None without a
+    bias)."""
+    from .transforms import beta_transform, kda_decay
+    g = _f64(gate)
+    a_log = _f64(A_log)
+    bias = None if dt_bias is None else _f64(dt_bias)
+    decay = kda_decay(g, a_log, bias, lower_bound, per_channel=per_channel)
+    logits = _f64(beta_logits)
+    beta = beta_transform(logits, allow_neg_eigval)
+    out = kda_scan_bwd(q, k, v, beta, decay, initial_state, do, d_final_state,
+                       softmax_scale=softmax_scale, use_qk_l2norm=use_qk_l2norm)
+    out.update(transforms_bwd(g, a_log, bias, logits, out.pop("ddecay"), out.pop("dbeta"),
+                              lower_bound, per_channel, allow_neg_eigval))
+    return out

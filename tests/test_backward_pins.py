@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle.backward as bwd_mod
-from oracle import kda_scan, kda_scan_bwd
+from oracle import kda_scan, kda_scan_bwd  # noqa: F401
 
 _TRUE_STEP = bwd_mod.reverse_step
 _TRUE_NORM = bwd_mod._norm_bwd
@@ -219,3 +219,95 @@ def test_backward_pins_catch_planted_mistakes(monkeypatch, attr, mutant):
         if not err < TOL[pin.__name__]:
             caught.append(pin.__name__)
     assert caught, f"no pin caught {mutant.__name__}"
+
+
+# ---- the transforms' backward ----
+
+from oracle import beta_transform, kda_decay, kda_scan_bwd_transforms  # noqa: E402
+
+_TRUE_TF = bwd_mod.transforms_bwd
+
+
+def pin_transform_finite_differences():
+    """Central differences of the forward oracle fed the oracle's own
+    transforms (raw gate -> decay, logits -> beta), for the gate, the beta
+    logits, A_log and dt_bias; per-head and per-channel gates, with and
+    without the floor (a floor of -0.6 catches some of these decays), and the
+    factor 2 of allow_neg_eigval."""
+    worst = 0.0
+    cases = [(False, None, False, True), (True, -0.6, True, True), (True, None, False, False),
+             (False, -0.6, True, True)]
+    for n, (per_channel, lb, neg, bias) in enumerate(cases):
+        rng = np.random.default_rng(500 + n)
+        B, T, H, DK, DV = 1, 5, 2, 4, 3
+        q, k = rng.standard_normal((B, T, H, DK)), rng.standard_normal((B, T, H, DK))
+        v = rng.standard_normal((B, T, H, DV))
+        logits = rng.standard_normal((B, T, H))
+        gate = rng.standard_normal((B, T, H, DK) if per_channel else (B, T, H))
+        A_log = 0.3 * rng.standard_normal(H)
+        dt_bias = (rng.uniform(-2, 0, (H, DK) if per_channel else H)) if bias else None
+        S0 = 0.3 * rng.standard_normal((B, H, DK, DV))
+        do, dST = rng.standard_normal((B, T, H, DV)), rng.standard_normal((B, H, DK, DV))
+        x = dict(gate=gate, logits=logits, A_log=A_log, dt_bias=dt_bias)
+
+        def loss(x):
+            dec = kda_decay(x["gate"], x["A_log"], x["dt_bias"], lb, per_channel=per_channel)
+            o, S = kda_scan(q, k, v, beta_transform(x["logits"], neg), dec, S0)
+            return float(np.sum(o * do) + np.sum(S * dST))
+
+        gr = kda_scan_bwd_transforms(q, k, v, logits, gate, A_log, S0, do, dST, dt_bias=dt_bias,
+                                     lower_bound=lb, per_channel=per_channel, allow_neg_eigval=neg)
+        names = {"gate": "dgate", "logits": "dbeta_logits", "A_log": "dA_log", "dt_bias": "ddt_bias"}
+        h = 1e-6
+        for name, gname in names.items():
+            if x[name] is None:
+                continue
+            flat = x[name].reshape(-1)
+            for i in range(flat.size):
+                keep = flat[i]
+                flat[i] = keep + h
+                lp = loss(x)
+                flat[i] = keep - h
+                lm = loss(x)
+                flat[i] = keep
+                fd = (lp - lm) / (2 * h)
+                worst = max(worst, abs(fd - gr[gname].reshape(-1)[i]) / max(1.0, abs(fd)))
+    return worst
+
+
+def _tf_no_floor_mask(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, neg):
+    return _TRUE_TF(gate, A_log, dt_bias, logits, ddecay, dbeta, None, per_channel, neg)
+
+
+def _tf_softplus_for_sigmoid(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel,
+                             neg):
+    out = _TRUE_TF(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, neg)
+    x = gate + (0.0 if dt_bias is None else dt_bias)
+    s = 1 / (1 + np.exp(-x))
+    out["dgate"] = out["dgate"] / np.where(s == 0, 1, s) * np.log1p(np.exp(x))
+    return out
+
+
+def _tf_no_eigval_factor(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, neg):
+    return _TRUE_TF(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, False)
+
+
+def _tf_dA_without_exp(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, neg):
+    out = _TRUE_TF(gate, A_log, dt_bias, logits, ddecay, dbeta, lower_bound, per_channel, neg)
+    out["dA_log"] = out["dA_log"] * np.exp(-A_log)
+    return out
+
+
+TF_MUTANTS = [_tf_no_floor_mask, _tf_softplus_for_sigmoid, _tf_no_eigval_factor, _tf_dA_without_exp]
+
+
+def test_transform_backward_pin():
+    err = pin_transform_finite_differences()
+    print(f"pin_transform_finite_differences: {err:.2e}")
+    assert err < 1e-7
+
+
+@pytest.mark.parametrize("mutant", TF_MUTANTS, ids=lambda m: m.__name__)
+def test_transform_backward_pin_catches_planted_mistakes(monkeypatch, mutant):
+    monkeypatch.setattr(bwd_mod, "transforms_bwd", mutant)
+    assert not pin_transform_finite_differences() < 1e-7

@@ -295,18 +295,29 @@ int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const
             int decay_kind, const float* initial_state, const float* d_o,
             const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
             float* ddecay, float* d_initial_state, int B, int T, int H, int HV, int DK, int DV,
-            int dtype, float softmax_scale, int use_qk_l2norm, void* workspace,
-            size_t workspace_bytes, void* stream) {
-  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype, 0);
+            int dtype, float softmax_scale, int use_qk_l2norm, int state_v_first,
+            const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+            float* dA_log, float* ddt_bias, void* workspace, size_t workspace_bytes,
+            void* stream) {
+  int st = kda::check_common(q, k, v, beta, decay, decay_kind, B, T, H, HV, DK, DV, dtype,
+                             state_v_first);
+  if (st == KDA_OK) st = kda::check_transforms(decay_kind, T, A_log, lower_bound, transforms);
   if (st != KDA_OK) return st;
   if (T != 0 && (!d_o || !dq || !dk || !dv || !dbeta)) return KDA_ERR_NULL;
   if (T != 0 && decay_kind != KDA_DECAY_NONE && !ddecay) return KDA_ERR_NULL;
+  if (T != 0 && (transforms & KDA_TF_GATE) && (!dA_log || (dt_bias && !ddt_bias))) return KDA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
-    // no tokens: the initial state's gradient is the final state's
-    if (!d_initial_state) return KDA_OK;
-    return kda::to_status(kda::launch_state_copy(d_final_state, d_initial_state,
-                                                 static_cast<long>(B) * HV * DK * DV, s));
+    // no tokens: the initial state's gradient is the final state's (the
+    // gradients of A_log and dt_bias are zero)
+    hipError_t e = hipSuccess;
+    if ((transforms & KDA_TF_GATE) && dA_log) e = kda::launch_state_copy(nullptr, dA_log, HV, s);
+    if (e == hipSuccess && (transforms & KDA_TF_GATE) && dt_bias && ddt_bias)
+      e = kda::launch_state_copy(nullptr, ddt_bias,
+                                 decay_kind == KDA_DECAY_CHANNEL ? static_cast<long>(HV) * DK : HV, s);
+    if (e == hipSuccess && d_initial_state)
+      e = kda::launch_state_copy(d_final_state, d_initial_state, static_cast<long>(B) * HV * DK * DV, s);
+    return kda::to_status(e);
   }
   if (!workspace || !kda::ws_aligned(workspace) ||
       workspace_bytes < kda::bwd_workspace_bytes(B, T, HV, DK, DV))
@@ -323,6 +334,10 @@ int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const
   a.B = B; a.T = T; a.H = HV; a.Hk = H; a.DK = DK; a.DV = DV; a.dtype = dtype;
   a.scale = kda::resolve_scale(softmax_scale, DK);
   a.l2norm = use_qk_l2norm ? 1 : 0;
+  a.vfirst = state_v_first;
+  a.tf = kda::make_tf(A_log, dt_bias, lower_bound, transforms);
+  a.dA_log = (transforms & KDA_TF_GATE) ? dA_log : nullptr;
+  a.ddt_bias = (transforms & KDA_TF_GATE) && dt_bias ? ddt_bias : nullptr;
   return kda::to_status(kda::launch_bwd(a, s));
 }
 
@@ -339,6 +354,6 @@ const char* kda_status_string(int status) {
   return "unknown status";
 }
 
-int kda_abi_version(void) { return 201; }
+int kda_abi_version(void) { return 202; }
 
 }  // extern "C"

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     const float* __restrict__ init, const float* __restrict__ dout, const float* __restrict__ dfinal,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta,
     float* __restrict__ ddecay, float* __restrict__ dinit, float* __restrict__ ckpt,
-    int T, int H, int Hk, float scale, int l2norm) {
+    int T, int H, int Hk, float scale, int l2norm, int vfirst, Transforms tf) {
   constexpr int CPL = (DK + 63) / 64;   // key channels per lane: c = lane + 64 e
   constexpr int V = act<In>::kVec;
   constexpr int LPR = DK / V;           // lanes per token row in the staging loads
@@ -74,6 +74,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     live[e] = ch[e] < DK;
   }
   auto tok = [&](int t) { return static_cast<long>(b) * T + t; };
+  // element (key row c, this wave's column) of an initial / final state
+  auto sidx = [&](int c) {
+    return vfirst ? (static_cast<long>(bh) * DV + j) * DK + c : (static_cast<long>(bh) * DK + c) * DV + j;
+  };
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
   // checkpoint of block n: [bh][n][column][DK]
   auto ck = [&](int n) { return ckpt + ((static_cast<long>(bh) * nsub + n) * DV + j) * DK; };
 
@@ -102,6 +107,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       float gv[V];
       if (chan && in) {
         act<In>::load_vec(decay + (tok(t0 + tt) * H + h) * DK + seg * V, gv);
+        if (tf.A_log) {
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            gv[e] = gate_decay(gv[e], negA, tf.dt_bias ? tf.dt_bias[h * DK + seg * V + e] : 0.f, tf.lower);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) gv[e] = 0.f;
@@ -116,8 +126,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     if (tid < kTB) {
       const bool in = tid < nt;
       const long tk = tok(t0 + tid) * H + h;
-      st.b[tid] = in ? act<In>::load1(beta + tk) : 0.f;
-      st.ah[tid] = __expf(headd && in ? act<In>::load1(decay + tk) : 0.f);
+      st.b[tid] = in ? beta_transform(act<In>::load1(beta + tk), tf.beta_mode) : 0.f;
+      float gh = 0.f;
+      if (headd && in) {
+        gh = act<In>::load1(decay + tk);
+        if (tf.A_log) gh = gate_decay(gh, negA, tf.dt_bias ? tf.dt_bias[h] : 0.f, tf.lower);
+      }
+      st.ah[tid] = __expf(gh);
     }
   };
 
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   float s[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e)
-    s[e] = (init && live[e]) ? init[(static_cast<long>(bh) * DK + ch[e]) * DV + j] : 0.f;
+    s[e] = (init && live[e]) ? init[sidx(ch[e])] : 0.f;
   for (int n = 0; n < nsub; ++n) {
     stage(n);
     __syncthreads();
@@ -151,7 +166,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   float ds[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e)
-    ds[e] = (dfinal && live[e]) ? dfinal[(static_cast<long>(bh) * DK + ch[e]) * DV + j] : 0.f;
+    ds[e] = (dfinal && live[e]) ? dfinal[sidx(ch[e])] : 0.f;
   for (int n = nsub - 1; n >= 0; --n) {
     stage(n);
     for (int idx = tid; idx < kTB * DK; idx += kBwdThreads) {
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   if (dinit) {
 #pragma unroll
     for (int e = 0; e < CPL; ++e)
-      if (live[e]) dinit[(static_cast<long>(bh) * DK + ch[e]) * DV + j] = ds[e];
+      if (live[e]) dinit[sidx(ch[e])] = ds[e];
   }
 }
 
@@ -294,6 +309,39 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const In* __restrict__ q,
   }
 }
 
+// The raw-gate / raw-beta chain rule, in place: dbeta and ddecay hold the
+// gradients of the transformed beta and decay; they become those of the raw
+// inputs, and dA_log / ddt_bias collect their sums (atomic adds).  Where the
+// floor is taken the decay is the constant floor and gets no gradient.
+// Elements n of [B, T, H] (or [B, T, H, DK] per channel, W = DK).
+template <typename In>
+__global__ void tf_bwd_kernel(const In* __restrict__ beta, const In* __restrict__ gate,
+                              float* __restrict__ dbeta, float* __restrict__ dgate,
+                              float* __restrict__ dA_log, float* __restrict__ dbias, Transforms tf,
+                              int H, int W, long ntok) {
+  const long tot = ntok * W;
+  for (long n = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; n < tot;
+       n += static_cast<long>(gridDim.x) * blockDim.x) {
+    const long t = n / W;            // token-head index
+    const int h = static_cast<int>(t % H), c = static_cast<int>(n % W);
+    if (c == 0 && tf.beta_mode) {
+      const float sgm = 1.f / (1.f + __expf(-act<In>::load1(beta + t)));
+      dbeta[t] *= sgm * (1.f - sgm) * (tf.beta_mode == 2 ? 2.f : 1.f);
+    }
+    if (tf.A_log && dgate) {
+      const float x = act<In>::load1(gate + n) + (tf.dt_bias ? tf.dt_bias[W == 1 ? h : h * W + c] : 0.f);
+      const float negA = -__expf(tf.A_log[h]);
+      const float raw = negA * softplus_f(x);
+      const float gd = dgate[n];
+      const bool live = raw >= tf.lower;
+      const float dx = live ? gd * negA / (1.f + __expf(-x)) : 0.f;
+      dgate[n] = dx;
+      if (live) atomicAdd(dA_log + h, gd * raw);
+      if (dbias) atomicAdd(dbias + (W == 1 ? h : h * W + c), dx);
+    }
+  }
+}
+
 __global__ void zero_kernel(float* __restrict__ p, long n) {
   for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<long>(gridDim.x) * blockDim.x)
@@ -317,6 +365,9 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   if (e == hipSuccess) e = zero(a.dbeta, tokh, s);
   if (e == hipSuccess && a.decay_kind != DECAY_NONE)
     e = zero(a.ddecay, a.decay_kind == DECAY_CHANNEL ? tokh * a.DK : tokh, s);
+  if (e == hipSuccess && a.tf.A_log) e = zero(a.dA_log, a.H, s);
+  if (e == hipSuccess && a.tf.A_log && a.tf.dt_bias)
+    e = zero(a.ddt_bias, a.decay_kind == DECAY_CHANNEL ? static_cast<long>(a.H) * a.DK : a.H, s);
   if (e != hipSuccess) return e;
   const In* q = static_cast<const In*>(a.q);
   const In* k = static_cast<const In*>(a.k);
@@ -330,7 +381,7 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
     bwd_kernel<dk_, dv_, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.init, a.dout, \
                                                     a.dfinal, a.dq, a.dk, a.dv, a.dbeta,         \
                                                     a.ddecay, a.dinit, a.ckpt, a.T, a.H, a.Hk,   \
-                                                    a.scale, a.l2norm);                          \
+                                                    a.scale, a.l2norm, a.vfirst, a.tf);          \
     launched = true;                                                                             \
   }
   KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
@@ -345,6 +396,14 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   if (a.DK == 32) norm_bwd_kernel<32, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
   else if (a.DK == 64) norm_bwd_kernel<64, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
   else norm_bwd_kernel<128, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
+  e = hipGetLastError();
+  if (e != hipSuccess || (!a.tf.A_log && !a.tf.beta_mode)) return e;
+  const int W = a.decay_kind == DECAY_CHANNEL ? a.DK : 1;
+  long blocks = (tokh * W + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  tf_bwd_kernel<In><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      be, de, a.dbeta, a.tf.A_log ? a.ddecay : nullptr, a.dA_log, a.tf.dt_bias ? a.ddt_bias : nullptr,
+      a.tf, a.H, W, tokh);
   return hipGetLastError();
 }
 

@@ -48,6 +48,10 @@ struct BwdArgs {
   int B, T, H, Hk, DK, DV, dtype;
   float scale;
   int l2norm;
+  int vfirst;          // states value-major
+  Transforms tf;       // raw gate / raw beta (all off: inputs as given)
+  float* dA_log;       // [H] with the raw gate
+  float* ddt_bias;     // like dt_bias (with the raw gate and a bias)
 };
 
 // Each launcher assumes the front end has validated the arguments.

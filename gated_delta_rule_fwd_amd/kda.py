@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
                                       i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp]
         L.kda_decode_step.restype = i
         L.kda_bwd.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                              i, i, i, i, i, i, i, f, i, vp, sz, vp]
+                              i, i, i, i, i, i, i, f, i, i, vp, vp, f, i, vp, vp, vp, sz, vp]
         L.kda_bwd.restype = i
         L.kda_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.kda_bwd_workspace_bytes.restype = sz
@@ -381,32 +381,45 @@ def decode_step(q, k, v, beta, decay, state, softmax_scale=None, use_qk_l2norm=T
 
 
 def bwd(q, k, v, beta, decay, initial_state, d_o, d_final_state=None, softmax_scale=None,
-        use_qk_l2norm=True, workspace=None, with_initial_state_grad=True):
+        use_qk_l2norm=True, workspace=None, with_initial_state_grad=True, state_v_first=False,
+        use_gate_in_kernel=False, A_log=None, dt_bias=None, lower_bound=None,
+        use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """Gradients of fwd_chunked / fwd_recurrent's (o, final_state) with the same
-    inputs (key-major states, no transforms) pulled back from d_o [B,T,HV,DV]
-    and d_final_state [B,HV,DK,DV] (None: zeros), both fp32.  Returns a dict:
-    dq, dk [B,T,H,DK], dv [B,T,HV,DV], dbeta [B,T,HV], ddecay (None or the
-    decay's shape), d_initial_state [B,HV,DK,DV] (None unless asked), all fp32.
+    inputs and arguments, pulled back from d_o [B,T,HV,DV] and d_final_state
+    (the state's shape; None: zeros), both fp32.  Returns a dict: dq, dk
+    [B,T,H,DK], dv [B,T,HV,DV], dbeta [B,T,HV] (of the logits with
+    ``use_beta_sigmoid_in_kernel``), ddecay (None or the decay's shape; of the
+    raw gate with ``use_gate_in_kernel``), d_initial_state (None unless
+    asked), dA_log [HV] and ddt_bias (dt_bias's shape) with
+    ``use_gate_in_kernel`` (else None), all fp32.
     ``workspace``: kda_bwd_workspace_bytes of device memory (None: allocated)."""
-    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state)
+    B, T, H, HV, DK, DV, dev, kind = _prep_fwd(q, k, v, beta, decay, initial_state, state_v_first)
+    tf = _transforms(kind, HV, DK, dev, use_gate_in_kernel, A_log, dt_bias, lower_bound,
+                     use_beta_sigmoid_in_kernel, allow_neg_eigval)
+    sshape = _state_shape(B, HV, DK, DV, state_v_first)
     _check_state("d_o", d_o, (B, T, HV, DV), dev)
     if d_o is None:
         raise ValueError("d_o is required")
-    _check_state("d_final_state", d_final_state, (B, HV, DK, DV), dev)
+    _check_state("d_final_state", d_final_state, sshape, dev)
     f32 = dict(device=dev, dtype=torch.float32)
     dq = torch.empty((B, T, H, DK), **f32)
     dk = torch.empty((B, T, H, DK), **f32)
     dv = torch.empty((B, T, HV, DV), **f32)
     dbeta = torch.empty((B, T, HV), **f32)
     ddecay = None if decay is None else torch.empty(tuple(decay.shape), **f32)
-    dinit = torch.empty((B, HV, DK, DV), **f32) if with_initial_state_grad else None
+    dinit = torch.empty(sshape, **f32) if with_initial_state_grad else None
+    dA = torch.empty((HV,), **f32) if use_gate_in_kernel else None
+    dbias = (torch.empty(tuple(dt_bias.shape), **f32)
+             if use_gate_in_kernel and dt_bias is not None else None)
     need = lib().kda_bwd_workspace_bytes(B, T, HV, DK, DV)
     ws = _workspace(workspace, need, dev)
     st = lib().kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(decay), kind,
                        _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
                        _ptr(dv), _ptr(dbeta), _ptr(ddecay), _ptr(dinit), B, T, H, HV, DK, DV,
                        _dtype_code(q), _scale(softmax_scale), int(bool(use_qk_l2norm)),
+                       int(bool(state_v_first)), *tf, _ptr(dA), _ptr(dbias),
                        _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     if st != 0:
         raise KdaError("kda_bwd", st)
-    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, ddecay=ddecay, d_initial_state=dinit)
+    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, ddecay=ddecay, d_initial_state=dinit,
+                dA_log=dA, ddt_bias=dbias)

@@ -277,35 +277,44 @@ int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const v
  * returns dq, dk, dv, dbeta, GLAChunkBwdOp takes do and the final-state
  * gradient; kda-neuron-kernels README, kda_chunk_step_exact_bwd: dq, dk, dv,
  * dg, dbeta, dstate_in).  The forward it differentiates is kda_fwd_chunked /
- * kda_fwd_recurrent with the same inputs, key-major states, no transforms.
+ * kda_fwd_recurrent with the same inputs and arguments.
  *
- *   q, k, v, beta, decay, initial_state   as the forward (activation dtype;
- *                  initial_state NULL = zeros)
+ *   q, k, v, beta, decay, initial_state, H, HV, state_v_first, the scale, the
+ *                  L2 norm and the transform arguments: as the forward
+ *                  (initial_state NULL = zeros)
  *   d_o            [B, T, HV, DV] fp32, the gradient of o
- *   d_final_state  NULL (zeros) | [B, HV, DK, DV] fp32
+ *   d_final_state  NULL (zeros) | like initial_state, fp32
  *   dq, dk         [B, T, H, DK] fp32, written (the gradients of the raw q,
  *                  k: through the L2 norm and the scale; value heads of a
  *                  group add up)
  *   dv             [B, T, HV, DV] fp32, written
- *   dbeta          [B, T, HV] fp32, written
- *   ddecay         like decay, fp32, written (ignored with KDA_DECAY_NONE)
- *   d_initial_state NULL (not written) | [B, HV, DK, DV] fp32, written
+ *   dbeta          [B, T, HV] fp32, written: the gradient of beta as passed
+ *                  (of the logits with KDA_TF_BETA_SIGMOID)
+ *   ddecay         like decay, fp32, written (ignored with KDA_DECAY_NONE):
+ *                  the gradient of decay as passed (of the raw gate with
+ *                  KDA_TF_GATE; zero where the floor is taken)
+ *   dA_log         with KDA_TF_GATE: [HV] fp32, written
+ *   ddt_bias       with KDA_TF_GATE and a dt_bias: like dt_bias, fp32, written
+ *   d_initial_state NULL (not written) | like initial_state, fp32, written
  *   workspace      DEVICE, 16-byte aligned, at least kda_bwd_workspace_bytes
  *                  (the state every 16 tokens, for the reverse pass)
  *
  * The reverse pass is sequential over tokens, in fp32; sums over value
- * columns are gathered with atomic adds, so results may differ in the last
- * bits from run to run.  Errors as kda_fwd_chunked; KDA_ERR_NULL if (T > 0)
- * d_o, dq, dk, dv, dbeta or (with a decay) ddecay is NULL; KDA_ERR_WORKSPACE
- * as for the forward.  T == 0 copies d_final_state (or zeros) to
- * d_initial_state.
+ * columns (and, for dA_log and ddt_bias, over tokens) are gathered with
+ * atomic adds, so results may differ in the last bits from run to run.
+ * Errors as kda_fwd_chunked; KDA_ERR_NULL if (T > 0) d_o, dq, dk, dv, dbeta,
+ * (with a decay) ddecay, or (with KDA_TF_GATE) dA_log or (with a dt_bias)
+ * ddt_bias is NULL; KDA_ERR_WORKSPACE as for the forward.  T == 0 copies
+ * d_final_state (or zeros) to d_initial_state and zeroes dA_log, ddt_bias.
  */
 int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const void* decay,
             int decay_kind, const float* initial_state, const float* d_o,
             const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
             float* ddecay, float* d_initial_state, int B, int T, int H, int HV, int DK, int DV,
-            int dtype, float softmax_scale, int use_qk_l2norm, void* workspace,
-            size_t workspace_bytes, void* stream);
+            int dtype, float softmax_scale, int use_qk_l2norm, int state_v_first,
+            const float* A_log, const float* dt_bias, float lower_bound, int transforms,
+            float* dA_log, float* ddt_bias, void* workspace, size_t workspace_bytes,
+            void* stream);
 
 /* Workspace bytes of kda_bwd (host-only); 0 when T == 0 or the sizes are
  * invalid. */

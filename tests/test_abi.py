@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.kda_abi_version() == 201
+    assert L.kda_abi_version() == 202
     assert L.kda_status_string(0) == b"ok"
     for code in (1, 2, 3, 4, 5, 6):
         assert len(L.kda_status_string(code)) > 3
@@ -197,12 +197,14 @@ def test_backward_rejects_bad_arguments(L):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, decay=None, kind=0, init=None, do=FAKE,
                  dfin=None, dq=FAKE, dk=FAKE, dv=FAKE, db=FAKE, dg=None, dinit=None, B=1, T=8,
-                 H=1, HV=1, DK=64, DV=64, dtype=1, ws=FAKE, wsb=BIG)
+                 H=1, HV=1, DK=64, DV=64, dtype=1, vfirst=0, A_log=None, bias=None, tf=0,
+                 dA=None, dbias=None, ws=FAKE, wsb=BIG)
         a.update(kw)
         return L.kda_bwd(a["q"], a["k"], a["v"], a["beta"], a["decay"], a["kind"], a["init"],
                          a["do"], a["dfin"], a["dq"], a["dk"], a["dv"], a["db"], a["dg"],
                          a["dinit"], a["B"], a["T"], a["H"], a["HV"], a["DK"], a["DV"],
-                         a["dtype"], 0.0, 1, a["ws"], a["wsb"], None)
+                         a["dtype"], 0.0, 1, a["vfirst"], a["A_log"], a["bias"], 0.0, a["tf"],
+                         a["dA"], a["dbias"], a["ws"], a["wsb"], None)
     assert call(do=None) == 1
     assert call(dq=None) == 1
     assert call(kind=1, decay=FAKE) == 1          # a decay needs its gradient
@@ -210,6 +212,13 @@ def test_backward_rejects_bad_arguments(L):
     assert call(H=2, HV=3) == 2
     assert call(ws=None) == 6
     assert call(wsb=L.kda_bwd_workspace_bytes(1, 8, 1, 64, 64) - 1) == 6
+    # the raw gate: A_log and its gradient are required, and a dt_bias needs its gradient
+    gate = dict(kind=1, decay=FAKE, dg=FAKE, tf=1)
+    assert call(**gate) == 1                      # no A_log
+    assert call(**gate, A_log=FAKE) == 1          # no dA_log
+    assert call(**gate, A_log=FAKE, dA=FAKE, bias=FAKE) == 1
+    assert call(tf=1, A_log=FAKE, dA=FAKE) == 4   # a raw gate needs a decay
+    assert call(tf=64) == 4                       # an unknown flag
     # the state every 16 tokens for every (batch, value head)
     assert L.kda_bwd_workspace_bytes(2, 33, 3, 64, 32) == 2 * 3 * 3 * 64 * 32 * 4
     assert L.kda_bwd_workspace_bytes(1, 0, 1, 64, 64) == 0

@@ -9,8 +9,10 @@ import pytest
 import torch
 
 from gated_delta_rule_fwd_amd import bwd
-from gated_delta_rule_fwd_amd.inputs import WORKLOADS, make_inputs
-from oracle import kda_scan_bwd
+from gated_delta_rule_fwd_amd.inputs import (DECAY_CHANNEL, WORKLOADS, make_inputs,
+                                             make_transform_inputs)
+from oracle import beta_transform, kda_decay, kda_scan_bwd, kda_scan_bwd_transforms
+from oracle.backward import transforms_bwd
 
 from test_gpu_parity import TOL, announce, dev, rel, to_dev
 
@@ -75,3 +77,122 @@ def test_backward_zero_length_and_no_state_gradients():
     torch.cuda.synchronize()
     for n, t in out.items():
         assert t is None or float(t.abs().max()) == 0.0, n
+
+
+# Raw-gate / raw-beta transforms: gradients with respect to the raw inputs
+# (oracle.backward.kda_scan_bwd_transforms, pinned by finite differences
+# through the transformed forward).
+TF_CASES = [
+    ("gdn_d128", dict(B=1, T=45, H=2), dict()),
+    ("gdn_d128", dict(B=2, T=33, H=2, init_state=True), dict(neg=True, lb=-0.3)),
+    ("kda_d128", dict(B=1, T=40, H=2, DV=64), dict(lb=-0.8)),
+    ("kda_d128", dict(B=1, T=21, H=2, DV=32), dict(bias=False, neg=True)),
+    ("fp32_small", dict(T=37, H=2, decay="channel_softplus", init_state=True), dict(lb=-1.0)),
+    ("fp32_small", dict(T=29, H=1, HV=2), dict(sigmoid=False)),
+    ("fp32_small", dict(T=29, H=2), dict(gate=False, neg=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw,opts", TF_CASES, ids=lambda x: str(x))
+def test_backward_transforms_match_oracle(name, kw, opts):
+    w = WORKLOADS[name].scaled(**kw)
+    announce(f"backward transforms {opts} {w}")
+    raw = make_transform_inputs(w)
+    gate_on = opts.get("gate", True)
+    sig = opts.get("sigmoid", True)
+    neg = opts.get("neg", False)
+    lb = opts.get("lb")
+    bias = raw["dt_bias"] if opts.get("bias", True) else None
+    g = torch.Generator().manual_seed(6)
+    do = torch.randn((w.B, w.T, w.hv, w.DV), generator=g)
+    dST = torch.randn((w.B, w.hv, w.DK, w.DV), generator=g)
+    d = {k: (None if v is None else v.to(dev())) for k, v in raw.items()}
+    beta_dev = d["beta_logits"] if sig else d["beta"]
+    decay_dev = d["gate"] if gate_on else d["decay"]
+    out = bwd(d["q"], d["k"], d["v"], beta_dev, decay_dev, d["initial_state"], do.to(dev()),
+              dST.to(dev()), use_gate_in_kernel=gate_on, A_log=d["A_log"] if gate_on else None,
+              dt_bias=None if (bias is None or not gate_on) else bias.to(dev()),
+              lower_bound=lb if gate_on else None, use_beta_sigmoid_in_kernel=sig,
+              allow_neg_eigval=neg)
+    torch.cuda.synchronize()
+    per_channel = w.decay_kind == DECAY_CHANNEL
+    if gate_on and sig:
+        ref = kda_scan_bwd_transforms(raw["q"], raw["k"], raw["v"], raw["beta_logits"],
+                                      raw["gate"], raw["A_log"], raw["initial_state"], do, dST,
+                                      dt_bias=bias, lower_bound=lb, per_channel=per_channel,
+                                      allow_neg_eigval=neg)
+        pairs = dict(dbeta="dbeta_logits", ddecay="dgate", dA_log="dA_log", ddt_bias="ddt_bias")
+    else:
+        # one transform alone: the plain backward on the transformed input,
+        # and the chain rule of the other from the oracle's transforms_bwd
+        logits = raw["beta_logits"].double().numpy()
+        beta = beta_transform(logits, neg) if sig else raw["beta"]
+        gate = raw["gate"].double().numpy() if gate_on else None
+        decay = (kda_decay(gate, raw["A_log"], bias, lb, per_channel=per_channel) if gate_on
+                 else raw["decay"])
+        ref = kda_scan_bwd(raw["q"], raw["k"], raw["v"], beta, decay, raw["initial_state"], do, dST)
+        if gate_on:
+            chain = transforms_bwd(gate, raw["A_log"].double().numpy(),
+                                   None if bias is None else bias.double().numpy(), logits,
+                                   ref["ddecay"], ref["dbeta"], lb, per_channel, neg)
+        else:
+            # the gate's part of the chain rule on a zero gate, unused
+            zero = np.zeros_like(ref["dbeta"])
+            chain = transforms_bwd(zero, raw["A_log"].double().numpy(), None, logits, zero,
+                                   ref["dbeta"], None, False, neg)
+        pairs = {}
+        if sig:
+            ref["dbeta"] = chain["dbeta_logits"]
+        if gate_on:
+            ref["ddecay"] = chain["dgate"]
+            ref["dA_log"], ref["ddt_bias"] = chain["dA_log"], chain["ddt_bias"]
+            pairs = dict(dA_log="dA_log", ddt_bias="ddt_bias")
+    tol = TOL[w.dtype]
+    for name_g in ("dq", "dk", "dv", "dbeta", "ddecay", "d_initial_state", "dA_log", "ddt_bias"):
+        key = pairs.get(name_g, name_g)
+        r = ref.get(key)
+        if r is None:
+            assert out[name_g] is None, name_g
+            continue
+        e = rel(out[name_g], r)
+        print(f"  {name_g}: err/rms={e:.3e} (tol {tol})", flush=True)
+        assert e <= tol, f"{name_g}: {e:.3e} > {tol}"
+    if lb is not None and gate_on:
+        # where the floor is taken the raw gate gets no gradient
+        decay = kda_decay(raw["gate"], raw["A_log"], bias, None, per_channel=per_channel)
+        floored = torch.from_numpy(np.asarray(decay) < lb)
+        assert int(floored.sum()) > 0, "the case takes the floor somewhere"
+        assert float(out["ddecay"].cpu()[floored].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gdn_d128", dict(B=2, T=35, H=2, init_state=True)),
+    ("kda_d128", dict(B=1, T=20, H=2, DV=64, init_state=True)),
+    ("fp32_small", dict(T=18, H=1, HV=2, DK=64, DV=32, init_state=True)),
+], ids=lambda x: str(x))
+def test_backward_value_major_states(name, kw):
+    """state_v_first: the initial state, its gradient and the final-state
+    gradient are [B, HV, DV, DK]; every gradient equals the key-major one's
+    (the same oracle, the states transposed)."""
+    w = WORKLOADS[name].scaled(**kw)
+    announce(f"backward value-major {w}")
+    inp = make_inputs(w)
+    g = torch.Generator().manual_seed(8)
+    do = torch.randn((w.B, w.T, w.hv, w.DV), generator=g)
+    dST = torch.randn((w.B, w.hv, w.DK, w.DV), generator=g)
+    d = to_dev(inp)
+    out = bwd(d["q"], d["k"], d["v"], d["beta"], d["decay"],
+              d["initial_state"].transpose(-1, -2).contiguous(), do.to(dev()),
+              dST.transpose(-1, -2).contiguous().to(dev()), state_v_first=True)
+    torch.cuda.synchronize()
+    ref = kda_scan_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                       inp["initial_state"], do, dST)
+    ref["d_initial_state"] = np.swapaxes(ref["d_initial_state"], -1, -2)
+    tol = TOL[w.dtype]
+    for name_g in ("dq", "dk", "dv", "dbeta", "ddecay", "d_initial_state"):
+        if ref[name_g] is None:
+            assert out[name_g] is None
+            continue
+        e = rel(out[name_g], ref[name_g])
+        print(f"  {name_g}: err/rms={e:.3e} (tol {tol})", flush=True)
+        assert e <= tol, f"{name_g}: {e:.3e} > {tol}"

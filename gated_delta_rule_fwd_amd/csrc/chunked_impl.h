@@ -875,6 +875,13 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 
 // Wait until this wave's global loads (the LDS copies included) have landed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's global loads are outstanding (loads
+// complete in issue order: all but the last N have landed).
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 // Wait until this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -974,6 +981,25 @@ __device__ __forceinline__ void dma16_buf(i32x4 rs, uint32_t m0, int voff, int s
       : "memory");
 }
 
+// L2 prefetch: a 4-byte load per lane (buffer_load_dword ... lds) whose data
+// lands in a dummy LDS slot at m0 (lane i at m0 + 4 i), so no register waits
+// for it; its purpose is the line it brings into the L2.  Offsets outside the
+// buffer's range read nothing.
+__device__ __forceinline__ void touch_buf(i32x4 rs, uint32_t m0, int voff) {
+  const i32x4 r = i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                        __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r)
+      : "memory");
+}
+
 // State-kernel workgroup: DVS/16 owner waves that compute, and as many
 // helper waves that copy the next chunk into LDS, so the owners never wait to
 // issue a copy.
@@ -1010,6 +1036,20 @@ void state_kernel(StateParams p) {
   static_assert(DVS % 16 == 0 && NOWN + NHELP == state_waves<DVS>(), "slice width");
   static_assert(L::PPRV >= 1, "value rows hold whole 16-byte pieces");
   static_assert(nQK % 64 == 0, "k copies fill whole instructions");
+  // L2 prefetch loads per helper and chunk (64-byte lines; sized for one
+  // slice per head, the most a slice prefetches): the record's and (raw rows)
+  // the q and k rows' share of this slice, and its own value rows
+  constexpr int kLinesRec = static_cast<int>((R::gBytes + 63) / 64);
+  constexpr int kLinesQK = rawk ? C * DK * AB / 64 : 0;       // per tensor
+  constexpr int kLPV = (DVS * AB + 63) / 64;                  // lines per value row
+  constexpr int kPfR = (kLinesRec + 64 * NHELP - 1) / (64 * NHELP);
+  constexpr int kPfQ = (kLinesQK + 64 * NHELP - 1) / (64 * NHELP);
+  constexpr int kPfV = (C * kLPV + 64 * NHELP - 1) / (64 * NHELP);
+  // (with raw rows the record is small and the owners bound the step: no prefetch)
+  constexpr bool kPrefetch = !rawk;
+  static_assert(!kPrefetch || L::kTouch == 256, "the prefetch slot");
+  constexpr int kPf = kPrefetch ? kPfR + 2 * kPfQ + kPfV : 0;   // the most a helper issues per chunk
+  int npf = 0;                                  // prefetch loads of the last issue
 
   extern __shared__ __align__(256) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1098,7 +1138,7 @@ void state_kernel(StateParams p) {
   const uint32_t lds0 = lds_addr(smem);
   // part 1: (raw rows) the q and k rows, part 2: the record and the value
   // rows, 0: both
-  auto issue = [&](int c, unsigned char* dstp, auto part_tag) {
+  auto issue = [&](int c, unsigned char* dstp, auto part_tag) __attribute__((always_inline)) {
     constexpr int part = decltype(part_tag)::value;
     const uint32_t dst = lds0 + static_cast<uint32_t>(dstp - smem);
     const int t0 = c * C, Lc = min(C, Trem - t0);
@@ -1137,10 +1177,52 @@ void state_kernel(StateParams p) {
           dma16_buf(rv, dst + L::oV + j * 1024, vr[sv] < Lc ? voff[sv] : 0, 0);
       }
     }
+    // Prefetch chunk c + 1 into the L2, one step before its copy: this
+    // slice's share of the lines every slice of the head copies (the record,
+    // and with raw rows the q and k rows), and its own value rows.  These are
+    // the last loads this helper issues before its wait (finish), which leaves
+    // them in flight; npf counts them.  Lanes past the share repeat a line of
+    // it (no load leaves the buffers).
+    npf = 0;
+    if (kPrefetch && c + 1 < nchunks) {
+      const int cn = c + 1, tn = cn * C, Ln = min(C, Trem - tn);
+      const uint32_t tslot = lds0 + static_cast<uint32_t>(L::oTouch);
+      const int shareR = min((kLinesRec + p.nsl - 1) / p.nsl, kLinesRec - slice * ((kLinesRec + p.nsl - 1) / p.nsl));
+      const int firstR = slice * ((kLinesRec + p.nsl - 1) / p.nsl);
+      const i32x4 rr2 = rsrc(rec0 + static_cast<size_t>(cn) * R::gBytes, static_cast<int>(R::gBytes));
+      const int nR = shareR > 0 ? (shareR + 64 * NHELP - 1) / (64 * NHELP) : 0;
+      for (int i = 0; i < nR; ++i) {
+        const int li = (i * NHELP + hw) * 64 + lane;
+        touch_buf(rr2, tslot, (firstR + (li < shareR ? li : 0)) * 64);
+      }
+      npf += nR;
+      if constexpr (rawk && kPrefetch) {
+        const long e1 = ((seq0 + tn) * p.Hk + hk) * static_cast<long>(DK);
+        const i32x4 rk2 = rsrc(gk + e1, (Ln - 1) * rowK + DK * AB), rq2 = rsrc(gq + e1, (Ln - 1) * rowK + DK * AB);
+        constexpr int LPK = DK * AB / 64;   // lines per q or k row
+        const int lines = Ln * LPK, per = (lines + p.nsl - 1) / p.nsl;
+        const int firstQ = slice * per, shareQ = min(per, lines - firstQ);
+        const int nQ = shareQ > 0 ? (shareQ + 64 * NHELP - 1) / (64 * NHELP) : 0;
+        for (int i = 0; i < nQ; ++i) {
+          const int li = (i * NHELP + hw) * 64 + lane, line = firstQ + (li < shareQ ? li : 0);
+          const int off = (line / LPK) * rowK + (line % LPK) * 64;
+          touch_buf(rk2, tslot, off);
+          touch_buf(rq2, tslot, off);
+        }
+        npf += 2 * nQ;
+      }
+      const i32x4 rv2 = rsrc(gv + ((seq0 + tn) * H + h) * static_cast<long>(DV) + n0, (Ln - 1) * rowV + DVS * AB);
+      const int linesV = Ln * kLPV, nV = (linesV + 64 * NHELP - 1) / (64 * NHELP);
+      for (int i = 0; i < nV; ++i) {
+        const int li = (i * NHELP + hw) * 64 + lane, line = li < linesV ? li : 0;
+        touch_buf(rv2, tslot, (line / kLPV) * rowV + (line % kLPV) * 64);
+      }
+      npf += nV;
+    }
   };
   // After the copy of chunk c into `buf` has landed: value rows past the
   // sequence end read as zero (each helper clears the pieces it copied).
-  auto zero_tail = [&](int c, unsigned char* buf) {
+  auto zero_tail = [&](int c, unsigned char* buf) __attribute__((always_inline)) {
     const int Lc = min(C, Trem - c * C);
     if (!owner && Lc < C) {
       unsigned char* dst = buf + L::oV;
@@ -1152,8 +1234,13 @@ void state_kernel(StateParams p) {
       }
     }
   };
-  auto finish = [&](int c, unsigned char* buf) {
-    wait_vm();
+  auto finish = [&](int c, unsigned char* buf) __attribute__((always_inline)) {
+    // the copies have landed; the npf prefetch loads after them may not have
+    static_for<kPf + 1>([&](auto n_) {
+      constexpr int n = decltype(n_)::value;
+      if (npf == n) wait_vm_keep<n>();
+    });
+    if (npf > kPf) wait_vm();
     zero_tail(c, buf);
   };
 
@@ -1526,6 +1613,8 @@ void state_kernel(StateParams p) {
     }
   }
 
+  // no load may still be landing in LDS when the workgroup ends
+  if (!owner) wait_vm();
   if constexpr (!rawk) {
     if (owner && nchunks > 0) store_out(nchunks - 1);
   }

@@ -182,7 +182,8 @@ struct StateLayout {
   static constexpr size_t kRecLds = (R::gBytes + kRecSlot - 1) / kRecSlot * kRecSlot;
   static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);
-  static constexpr int NBUF = 2 * kBuf <= kMaxLds ? 2 : 1;
+  static constexpr size_t kTouch = R::kRawK ? 0 : 256;   // the prefetch slot (below)
+  static constexpr int NBUF = 2 * kBuf + kTouch <= kMaxLds ? 2 : 1;
   static constexpr int NBT = C / 16;
   static constexpr int kNPF = NBT * (NBT + 2) / 4;   // P fragments: sum over row blocks ib of ib/2 + 1
   static constexpr bool kHelperP = R::kRawK && NBUF == 2;
@@ -190,8 +191,11 @@ struct StateLayout {
   static constexpr size_t oFQ = oPF + size_t(kNPF) * 1024;
   static constexpr size_t oFlags = oFQ + chunked_layout::al(size_t(C) * 4);
   static constexpr size_t kFlags = 256;
+  // the 256-byte landing slot of the L2 prefetch loads (never read; none
+  // with raw rows, which are not prefetched)
+  static constexpr size_t oTouch = kHelperP ? oFlags + kFlags : NBUF * kBuf;
   // raw rows need the helper-formed P: otherwise no plan (more than the LDS)
-  static constexpr size_t bytes = kHelperP ? oFlags + kFlags : R::kRawK ? kMaxLds + 1 : NBUF * kBuf;
+  static constexpr size_t bytes = R::kRawK && !kHelperP ? kMaxLds + 1 : oTouch + kTouch;
 };
 
 }  // namespace kda

@@ -800,18 +800,26 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 
   // ============ phase 3: T = (I + A)^-1 (fp32) ============
   if (wave == 0) {
-    // diagonal 16x16 blocks, lane -> (block, column): right-looking
-    // substitution, so each step leaves only independent updates behind
+    // diagonal 16x16 blocks, lane -> (block, column jc): forward substitution
+    // by rows, x_r = [r == jc] - sum_{s < r} A_rs x_s, A's row read four
+    // entries at a time (one 16-byte read for the 16 lanes of a block), the
+    // sum in four partial sums
     const int i = g, jc = l16;
     if (i < NB) {
       float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
       const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
+      x[0] = jc == 0 ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < 15; ++s) {
+      for (int r = 1; r < 16; ++r) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = s + 1; r < 16; ++r) x[r] -= ablk[r * L::LF + s] * x[s];
+        for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(ablk + r * L::LF + 4 * s4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * s4 + e < r) acc[e] += a4[e] * x[4 * s4 + e];
+        }
+        x[r] = (r == jc ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];

@@ -19,11 +19,14 @@
 // in the workspace; the reverse pass recomputes the 16 states of a block into
 // registers from there and steps back through them.  dv and the column's
 // initial-state gradient belong to the wave alone; dq, dk, dbeta and the
-// decay gradient are sums over columns, gathered per block in LDS by the four
-// waves of a workgroup and added to the outputs with one atomic add per
-// element and workgroup (the order of those additions varies from run to
-// run, within fp32 rounding).  A last kernel carries dq and dk through the
-// L2 norm and the scale.  All arithmetic is fp32.
+// decay gradient are sums over columns.  Each wave stores its column's terms
+// of dq, dk (and the per-channel decay gradient) in an LDS slice of its own;
+// every 8 tokens the workgroup sums its four waves' slices and adds them to
+// the outputs with one atomic add per element and workgroup (the order of
+// those additions varies from run to run, within fp32 rounding).  LDS
+// atomics, four waves adding to one address, cost about two thirds of the
+// time when the sums were formed that way.  A last kernel carries dq and dk
+// through the L2 norm and the scale.  All arithmetic is fp32.
 //
 // This is the plain form of the backward: time grows with T dependent
 // token steps per column, and the work is not shaped for MFMA.
@@ -35,13 +38,18 @@ namespace {
 
 constexpr int kBwdThreads = 256;   // four waves: four value columns of one (batch, head)
 constexpr int kTB = 16;            // tokens per block (the checkpoint interval)
+constexpr int kTH = kTB / 2;       // tokens per flush of the column sums
 
 template <int DK, typename In>
 struct BwdStage {
   float q[kTB][DK], k[kTB][DK], a[kTB][DK];   // normalised q (scaled), k; exp(decay) per channel
   float b[kTB], ah[kTB];                      // beta; exp(decay) per head
-  // per-block sums over the workgroup's columns
-  float dq[kTB][DK], dk[kTB][DK], dg[kTB][DK];
+  float v[kTB][4], dout[kTB][4];              // v and do at the workgroup's four columns
+  // each wave's own column terms of dq, dk and the per-channel decay
+  // gradient for half a block (plain stores), summed over the waves at each
+  // half's end; per token the column sums of dbeta and the per-head decay
+  // gradient
+  float pq[4][kTH][DK], pk[4][kTH][DK], pg[4][kTH][DK];
   float db[kTB], dgh[kTB];
 };
 
@@ -82,8 +90,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   // checkpoint of block n: [bh][n][column][DK]
   auto ck = [&](int n) { return ckpt + ((static_cast<long>(bh) * nsub + n) * DV + j) * DK; };
 
-  // Stage the tokens of block n: normalised q (scaled) and k, decay factors, beta.
-  auto stage = [&](int n) {
+  // Stage the tokens of block n: normalised q (scaled) and k, decay factors,
+  // beta, and v (and with_do, do) at the workgroup's four columns.
+  auto stage = [&](int n, bool with_do) {
     const int t0 = n * kTB, nt = min(kTB, T - t0);
     for (int idx = tid; idx < kTB * LPR; idx += kBwdThreads) {
       const int tt = idx / LPR, seg = idx % LPR;
@@ -123,6 +132,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         st.a[tt][seg * V + e] = __expf(gv[e]);
       }
     }
+    if (tid >= 64 && tid < 64 + 4 * kTB) {
+      const int tt = (tid - 64) >> 2, cw = (tid - 64) & 3;
+      const bool in = tt < nt;
+      const long vo = (tok(t0 + tt) * H + h) * DV + (j - wave) + cw;
+      st.v[tt][cw] = in ? act<In>::load1(v + vo) : 0.f;
+      st.dout[tt][cw] = (in && with_do) ? dout[vo] : 0.f;
+    }
     if (tid < kTB) {
       const bool in = tid < nt;
       const long tk = tok(t0 + tid) * H + h;
@@ -142,7 +158,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   for (int e = 0; e < CPL; ++e)
     s[e] = (init && live[e]) ? init[sidx(ch[e])] : 0.f;
   for (int n = 0; n < nsub; ++n) {
-    stage(n);
+    stage(n, false);
     __syncthreads();
     float* c = ck(n);
 #pragma unroll
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
 #pragma unroll
       for (int e = 0; e < CPL; ++e) r += live[e] ? s[e] * st.k[i][ch[e]] : 0.f;
       r = dpp_group_sum<64>(r);
-      const float delta = st.b[i] * (act<In>::load1(v + (tok(t0 + i) * H + h) * DV + j) - r);
+      const float delta = st.b[i] * (st.v[i][wave] - r);
 #pragma unroll
       for (int e = 0; e < CPL; ++e)
         if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
@@ -168,12 +184,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   for (int e = 0; e < CPL; ++e)
     ds[e] = (dfinal && live[e]) ? dfinal[sidx(ch[e])] : 0.f;
   for (int n = nsub - 1; n >= 0; --n) {
-    stage(n);
-    for (int idx = tid; idx < kTB * DK; idx += kBwdThreads) {
-      (&st.dq[0][0])[idx] = 0.f;
-      (&st.dk[0][0])[idx] = 0.f;
-      (&st.dg[0][0])[idx] = 0.f;
-    }
+    stage(n, true);
     if (tid < kTB) st.db[tid] = st.dgh[tid] = 0.f;
     __syncthreads();
     const int t0 = n * kTB, nt = min(kTB, T - t0);
@@ -193,19 +204,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         }
         r = dpp_group_sum<64>(r);
         rr[i] = r;
-        vv[i] = act<In>::load1(v + (tok(t0 + i) * H + h) * DV + j);
+        vv[i] = st.v[i][wave];
         const float delta = st.b[i] * (vv[i] - r);
 #pragma unroll
         for (int e = 0; e < CPL; ++e)
           if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
       }
     }
+    // The half block's column sums of dq, dk (and the per-channel decay
+    // gradient), tokens t0 + hb .. t0 + hb + kTH - 1, into the outputs.
+    auto flush = [&](int hb) {
+      __syncthreads();
+      for (int idx = tid; idx < kTH * DK; idx += kBwdThreads) {
+        const int tt = idx / DK, cc = idx % DK;
+        if (hb + tt < nt) {
+          const long qo = (tok(t0 + hb + tt) * Hk + hk) * DK + cc;
+          atomicAdd(dq + qo, (st.pq[0][tt][cc] + st.pq[1][tt][cc]) + (st.pq[2][tt][cc] + st.pq[3][tt][cc]));
+          atomicAdd(dk + qo, (st.pk[0][tt][cc] + st.pk[1][tt][cc]) + (st.pk[2][tt][cc] + st.pk[3][tt][cc]));
+          if (chan)
+            atomicAdd(ddecay + (tok(t0 + hb + tt) * H + h) * DK + cc,
+                      (st.pg[0][tt][cc] + st.pg[1][tt][cc]) + (st.pg[2][tt][cc] + st.pg[3][tt][cc]));
+        }
+      }
+      __syncthreads();
+    };
     // s now holds the state after the block
 #pragma unroll
     for (int i = kTB - 1; i >= 0; --i) {
+      if (i == kTH - 1) flush(kTH);
       if (i < nt) {
         const float bt = st.b[i], delta = bt * (vv[i] - rr[i]);
-        const float dov = dout[(tok(t0 + i) * H + h) * DV + j];
+        const float dov = st.dout[i][wave];
         float dqv[CPL], ddl = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
@@ -224,9 +253,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
             const float a = chan ? st.a[i][ch[e]] : st.ah[i];
             const float dkv = ds[e] * delta - bt * ddl * sp[i][e];
             const float dga = ds[e] * sp[i][e] * a;   // d(decay) = a * da
-            atomicAdd(&st.dq[i][ch[e]], dqv[e]);
-            atomicAdd(&st.dk[i][ch[e]], dkv);
-            if (chan) atomicAdd(&st.dg[i][ch[e]], dga);
+            st.pq[wave][i % kTH][ch[e]] = dqv[e];
+            st.pk[wave][i % kTH][ch[e]] = dkv;
+            if (chan) st.pg[wave][i % kTH][ch[e]] = dga;
             dgs += dga;
             ds[e] = a * ds[e] - bt * ddl * st.k[i][ch[e]];
           }
@@ -239,15 +268,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         }
       }
     }
-    __syncthreads();
-    // the block's sums over this workgroup's columns, into the outputs
-    for (int idx = tid; idx < nt * DK; idx += kBwdThreads) {
-      const int tt = idx / DK, cc = idx % DK;
-      const long qo = (tok(t0 + tt) * Hk + hk) * DK + cc;
-      atomicAdd(dq + qo, st.dq[tt][cc]);
-      atomicAdd(dk + qo, st.dk[tt][cc]);
-      if (chan) atomicAdd(ddecay + (tok(t0 + tt) * H + h) * DK + cc, st.dg[tt][cc]);
-    }
+    flush(0);
     if (tid < nt) {
       atomicAdd(dbeta + tok(t0 + tid) * H + h, st.db[tid]);
       if (headd) atomicAdd(ddecay + tok(t0 + tid) * H + h, st.dgh[tid]);

@@ -67,8 +67,19 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Sum over aligned groups of W consecutive lanes with DPP lane moves (no LDS
-// traffic), the result in every lane of the group.  W = 4, 8, 16, 32 or 64.
+// x + x of lane ^ 16, and x + x of lane ^ 32 (gfx950 lane-swap moves)
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned groups of W consecutive lanes with DPP lane moves within
+// rows of 16 and lane-swap moves across them (no LDS traffic), the result in
+// every lane of the group.  W = 4, 8, 16, 32 or 64.
 template <int W>
 __device__ __forceinline__ float dpp_group_sum(float x) {
   auto mov = [](float v, auto ctrl) {
@@ -87,19 +98,9 @@ __device__ __forceinline__ float dpp_group_sum(float x) {
   }
   x += mov(x, xor2{});
   x += mov(x, xor1{});
-  if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (W >= 32) x = xor16_sum(x);
+  if constexpr (W >= 64) x = xor32_sum(x);
   return x;
-}
-
-// x + x of lane ^ 16, and x + x of lane ^ 32 (gfx950 lane-swap moves)
-__device__ __forceinline__ float xor16_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Optional input transforms (TileOPs "Linear Attention Operators", GDNFwdOp

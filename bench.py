@@ -139,6 +139,47 @@ def time_chunked(w, steps, warmup, dev, raw=False):
     return wall / steps * 1e3, sum(kern_ms) / len(kern_ms), min(kern_ms)
 
 
+def backward_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: q, k, v, beta, the decay
+    and do read once, dq, dk, dv, dbeta and the decay gradient written once
+    (fp32), the initial state and the final-state gradient read and the
+    initial-state gradient written (the workspace's checkpoints are not
+    counted)."""
+    a = act_bytes(w)
+    gate = {0: 0, 1: 1, 2: w.DK}[w.decay_kind]
+    qk = w.B * w.T * w.H * 2 * w.DK * (a + 4)                       # q, k read; dq, dk written
+    per_tok = (w.DV + 1 + gate) * a + w.DV * 4 + (w.DV + 1 + gate) * 4   # v beta decay do; dv dbeta ddecay
+    state = w.DK * w.DV * 4 * (3 if w.init_state else 2)
+    return qk + w.B * w.T * w.hv * per_tok + w.B * w.hv * state
+
+
+def time_backward(w, steps, warmup, dev):
+    """Per-call time (HIP events on the launch stream) of kda_bwd on workload
+    w, from do and a final-state gradient; the workspace is allocated once."""
+    import torch
+    from gated_delta_rule_fwd_amd import bwd
+    from gated_delta_rule_fwd_amd.inputs import make_inputs
+    d = to_dev(make_inputs(w), dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    do = torch.randn((w.B, w.T, w.hv, w.DV), device=dev, generator=g)
+    dST = torch.randn((w.B, w.hv, w.DK, w.DV), device=dev, generator=g)
+    import gated_delta_rule_fwd_amd.kda as K
+    ws = torch.empty(max(1, K.lib().kda_bwd_workspace_bytes(w.B, w.T, w.hv, w.DK, w.DV)),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: bwd(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"], do, dST,
+                       workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for s_, e in evs:
+        s_.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    return sum(s_.elapsed_time(e) for s_, e in evs) / steps
+
+
 VARLEN_SEQS = 16
 
 
@@ -522,6 +563,14 @@ def main():
             "sequences": VARLEN_SEQS, "tokens": w.B * w.T, "min_len": min(lens), "max_len": max(lens),
             "tokens_per_s": round(w.B * w.T / (vk * 1e-3), 1), "kernel_ms_mean": round(vk, 4),
             "hbm_frac": round(vb / (vk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # the backward (kda_bwd) at the headline shape: the plain form, a
+        # sequential reverse pass per value column
+        b_ms = time_backward(w, max(3, args.steps // 20), args.warmup, dev)
+        extra[w.name + "_backward"] = {
+            "kernel_ms_mean": round(b_ms, 3), "tokens_per_s": round(w.B * w.T / (b_ms * 1e-3), 1),
+            "algorithmic_bytes": backward_bytes(w),
+            "hbm_frac": round(backward_bytes(w) / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "form": "sequential reverse pass per value column, fp32 VALU (no chunked MFMA form)"}
         w5 = WORKLOADS["decode_d128"]
         d_ms = time_decode(w5, max(5, args.steps), args.warmup, dev)
         gbs = decode_bytes(w5) / (d_ms * 1e-3) / 1e9

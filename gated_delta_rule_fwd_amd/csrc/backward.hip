@@ -13,8 +13,9 @@
 //   dS = diag(a) dS' - beta k ddelta^T
 //
 // Every value column of the state evolves on its own given q, k, beta and the
-// decay, so one wave takes one column (lanes over key channels): its state
-// column and gradient column sit in registers.  The reverse pass needs the
+// decay, so a wave takes two (or, at DK = 32, four) columns, lanes over key
+// channels, and interleaves their independent chains: the state columns and
+// gradient columns sit in registers.  The reverse pass needs the
 // state before every token: a first pass stores each column every 16 tokens
 // in the workspace; the reverse pass recomputes the 16 states of a block into
 // registers from there and steps back through them.  dv and the column's
@@ -39,12 +40,16 @@ namespace {
 constexpr int kBwdThreads = 256;   // four waves: four value columns of one (batch, head)
 constexpr int kTB = 16;            // tokens per block (the checkpoint interval)
 constexpr int kTH = kTB / 2;       // tokens per flush of the column sums
+// value columns per wave: as many as fit two waves per SIMD without
+// spilling much (256 registers; four columns spill 52 bytes a lane at
+// DK = 64 and 648 at DK = 128, and run slower)
+template <int DK> constexpr int ncw() { return DK >= 64 ? 2 : 4; }
 
-template <int DK, typename In>
+template <int DK, int NCW, typename In>
 struct BwdStage {
   float q[kTB][DK], k[kTB][DK], a[kTB][DK];   // normalised q (scaled), k; exp(decay) per channel
   float b[kTB], ah[kTB];                      // beta; exp(decay) per head
-  float v[kTB][4], dout[kTB][4];              // v and do at the workgroup's four columns
+  float v[kTB][4 * NCW], dout[kTB][4 * NCW];  // v and do at the workgroup's columns
   // each wave's own column terms of dq, dk and the per-channel decay
   // gradient for half a block (plain stores), summed over the waves at each
   // half's end; per token the column sums of dbeta and the per-head decay
@@ -53,8 +58,10 @@ struct BwdStage {
   float db[kTB], dgh[kTB];
 };
 
-template <int DK, int DV, typename In>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
+// NCW value columns per wave: their chains are independent, so a wave
+// interleaves them; their terms of the column sums add up in registers.
+template <int DK, int DV, int NCW, typename In>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     const float* __restrict__ init, const float* __restrict__ dout, const float* __restrict__ dfinal,
@@ -64,13 +71,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   constexpr int CPL = (DK + 63) / 64;   // key channels per lane: c = lane + 64 e
   constexpr int V = act<In>::kVec;
   constexpr int LPR = DK / V;           // lanes per token row in the staging loads
-  __shared__ BwdStage<DK, In> st;
+  constexpr int NCG = 4 * NCW;          // columns per workgroup
+  static_assert(DV % NCG == 0, "whole workgroups of columns");
+  __shared__ BwdStage<DK, NCW, In> st;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ncg = DV / 4;                                  // workgroups per (b, h)
+  const int ncg = DV / NCG;                                // workgroups per (b, h)
   const int bh = blockIdx.x / ncg;
   const int b = bh / H, h = bh % H;
-  const int j = (blockIdx.x % ncg) * 4 + wave;             // this wave's value column
+  const int jg = (blockIdx.x % ncg) * NCG;                 // the workgroup's first column
+  const int j0 = jg + wave * NCW;                          // this wave's first column
   const int hk = h / (H / Hk);
   const int nsub = (T + kTB - 1) / kTB;
   const bool chan = decay_kind == DECAY_CHANNEL, headd = decay_kind == DECAY_HEAD;
@@ -82,16 +92,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     live[e] = ch[e] < DK;
   }
   auto tok = [&](int t) { return static_cast<long>(b) * T + t; };
-  // element (key row c, this wave's column) of an initial / final state
-  auto sidx = [&](int c) {
-    return vfirst ? (static_cast<long>(bh) * DV + j) * DK + c : (static_cast<long>(bh) * DK + c) * DV + j;
+  // element (key row c, column jj) of an initial / final state
+  auto sidx = [&](int c, int jj) {
+    return vfirst ? (static_cast<long>(bh) * DV + jj) * DK + c : (static_cast<long>(bh) * DK + c) * DV + jj;
   };
   const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;   // raw gate: -exp(A_log)
-  // checkpoint of block n: [bh][n][column][DK]
-  auto ck = [&](int n) { return ckpt + ((static_cast<long>(bh) * nsub + n) * DV + j) * DK; };
+  // checkpoint of block n, column jj: [bh][n][column][DK]
+  auto ck = [&](int n, int jj) { return ckpt + ((static_cast<long>(bh) * nsub + n) * DV + jj) * DK; };
 
   // Stage the tokens of block n: normalised q (scaled) and k, decay factors,
-  // beta, and v (and with_do, do) at the workgroup's four columns.
+  // beta, and v (and with_do, do) at the workgroup's columns.
   auto stage = [&](int n, bool with_do) {
     const int t0 = n * kTB, nt = min(kTB, T - t0);
     for (int idx = tid; idx < kTB * LPR; idx += kBwdThreads) {
@@ -132,10 +142,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
         st.a[tt][seg * V + e] = __expf(gv[e]);
       }
     }
-    if (tid >= 64 && tid < 64 + 4 * kTB) {
-      const int tt = (tid - 64) >> 2, cw = (tid - 64) & 3;
+    for (int idx = tid; idx < kTB * NCG; idx += kBwdThreads) {
+      const int tt = idx / NCG, cw = idx % NCG;
       const bool in = tt < nt;
-      const long vo = (tok(t0 + tt) * H + h) * DV + (j - wave) + cw;
+      const long vo = (tok(t0 + tt) * H + h) * DV + jg + cw;
       st.v[tt][cw] = in ? act<In>::load1(v + vo) : 0.f;
       st.dout[tt][cw] = (in && with_do) ? dout[vo] : 0.f;
     }
@@ -152,63 +162,86 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
     }
   };
 
-  // ---- pass 1: the state column at the start of every block ----
-  float s[CPL];
+  // ---- pass 1: the state columns at the start of every block ----
+  float s[NCW][CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e)
-    s[e] = (init && live[e]) ? init[sidx(ch[e])] : 0.f;
+  for (int w = 0; w < NCW; ++w) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s[w][e] = (init && live[e]) ? init[sidx(ch[e], j0 + w)] : 0.f;
+  }
   for (int n = 0; n < nsub; ++n) {
     stage(n, false);
     __syncthreads();
-    float* c = ck(n);
 #pragma unroll
-    for (int e = 0; e < CPL; ++e)
-      if (live[e]) c[ch[e]] = s[e];
-    const int t0 = n * kTB, nt = min(kTB, T - t0);
-    for (int i = 0; i < nt; ++i) {
-      float r = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) r += live[e] ? s[e] * st.k[i][ch[e]] : 0.f;
-      r = dpp_group_sum<64>(r);
-      const float delta = st.b[i] * (st.v[i][wave] - r);
+    for (int w = 0; w < NCW; ++w) {
+      float* c = ck(n, j0 + w);
 #pragma unroll
       for (int e = 0; e < CPL; ++e)
-        if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
+        if (live[e]) c[ch[e]] = s[w][e];
+    }
+    const int t0 = n * kTB, nt = min(kTB, T - t0);
+    for (int i = 0; i < nt; ++i) {
+      float r[NCW];
+#pragma unroll
+      for (int w = 0; w < NCW; ++w) {
+        r[w] = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) r[w] += live[e] ? s[w][e] * st.k[i][ch[e]] : 0.f;
+      }
+#pragma unroll
+      for (int w = 0; w < NCW; ++w) r[w] = dpp_group_sum<64>(r[w]);
+#pragma unroll
+      for (int w = 0; w < NCW; ++w) {
+        const float delta = st.b[i] * (st.v[i][wave * NCW + w] - r[w]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          if (live[e]) s[w][e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[w][e] + st.k[i][ch[e]] * delta;
+      }
     }
     __syncthreads();
   }
 
   // ---- pass 2: blocks in reverse ----
-  float ds[CPL];
+  float ds[NCW][CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e)
-    ds[e] = (dfinal && live[e]) ? dfinal[sidx(ch[e])] : 0.f;
+  for (int w = 0; w < NCW; ++w) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) ds[w][e] = (dfinal && live[e]) ? dfinal[sidx(ch[e], j0 + w)] : 0.f;
+  }
   for (int n = nsub - 1; n >= 0; --n) {
     stage(n, true);
     if (tid < kTB) st.db[tid] = st.dgh[tid] = 0.f;
     __syncthreads();
     const int t0 = n * kTB, nt = min(kTB, T - t0);
     // recompute the block's states: sp[i] enters token t0 + i
-    float sp[kTB][CPL], rr[kTB], vv[kTB];
-    const float* c = ck(n);
+    float sp[kTB][NCW][CPL], rr[kTB][NCW];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) s[e] = live[e] ? c[ch[e]] : 0.f;
+    for (int w = 0; w < NCW; ++w) {
+      const float* c = ck(n, j0 + w);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[w][e] = live[e] ? c[ch[e]] : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < kTB; ++i) {
       if (i < nt) {
-        float r = 0.f;
+        float r[NCW];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          sp[i][e] = s[e];
-          r += live[e] ? s[e] * st.k[i][ch[e]] : 0.f;
+        for (int w = 0; w < NCW; ++w) {
+          r[w] = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            sp[i][w][e] = s[w][e];
+            r[w] += live[e] ? s[w][e] * st.k[i][ch[e]] : 0.f;
+          }
         }
-        r = dpp_group_sum<64>(r);
-        rr[i] = r;
-        vv[i] = st.v[i][wave];
-        const float delta = st.b[i] * (vv[i] - r);
 #pragma unroll
-        for (int e = 0; e < CPL; ++e)
-          if (live[e]) s[e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[e] + st.k[i][ch[e]] * delta;
+        for (int w = 0; w < NCW; ++w) {
+          rr[i][w] = dpp_group_sum<64>(r[w]);
+          const float delta = st.b[i] * (st.v[i][wave * NCW + w] - rr[i][w]);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e)
+            if (live[e]) s[w][e] = (chan ? st.a[i][ch[e]] : st.ah[i]) * s[w][e] + st.k[i][ch[e]] * delta;
+        }
       }
     }
     // The half block's column sums of dq, dk (and the per-channel decay
@@ -228,43 +261,69 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
       }
       __syncthreads();
     };
-    // s now holds the state after the block
+    // s now holds the states after the block
 #pragma unroll
     for (int i = kTB - 1; i >= 0; --i) {
       if (i == kTH - 1) flush(kTH);
       if (i < nt) {
-        const float bt = st.b[i], delta = bt * (vv[i] - rr[i]);
-        const float dov = st.dout[i][wave];
-        float dqv[CPL], ddl = 0.f;
+        const float bt = st.b[i];
+        const float a0 = st.ah[i];
+        float ddl[NCW], delta[NCW], dov[NCW];
+        float dqv[CPL], dkv[CPL], dga[CPL];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const float snew = i + 1 < nt ? sp[i + 1 < kTB ? i + 1 : i][e] : s[e];
-          if (live[e]) {
-            ds[e] += st.q[i][ch[e]] * dov;
-            dqv[e] = snew * dov;
-            ddl += ds[e] * st.k[i][ch[e]];
+        for (int e = 0; e < CPL; ++e) dqv[e] = dkv[e] = dga[e] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) {
+          delta[w] = bt * (st.v[i][wave * NCW + w] - rr[i][w]);
+          dov[w] = st.dout[i][wave * NCW + w];
+          ddl[w] = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            const float snew = i + 1 < nt ? sp[i + 1 < kTB ? i + 1 : i][w][e] : s[w][e];
+            if (live[e]) {
+              ds[w][e] += st.q[i][ch[e]] * dov[w];
+              dqv[e] += snew * dov[w];
+              ddl[w] += ds[w][e] * st.k[i][ch[e]];
+            }
           }
         }
-        ddl = dpp_group_sum<64>(ddl);
-        float dgs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) ddl[w] = dpp_group_sum<64>(ddl[w]);
+        float dgs = 0.f, dbs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            if (live[e]) {
+              const float a = chan ? st.a[i][ch[e]] : a0;
+              dkv[e] += ds[w][e] * delta[w] - bt * ddl[w] * sp[i][w][e];
+              const float g1 = ds[w][e] * sp[i][w][e] * a;   // d(decay) = a * da
+              dga[e] += g1;
+              dgs += g1;
+              ds[w][e] = a * ds[w][e] - bt * ddl[w] * st.k[i][ch[e]];
+            }
+          }
+          dbs += ddl[w] * (st.v[i][wave * NCW + w] - rr[i][w]);
+        }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           if (live[e]) {
-            const float a = chan ? st.a[i][ch[e]] : st.ah[i];
-            const float dkv = ds[e] * delta - bt * ddl * sp[i][e];
-            const float dga = ds[e] * sp[i][e] * a;   // d(decay) = a * da
             st.pq[wave][i % kTH][ch[e]] = dqv[e];
-            st.pk[wave][i % kTH][ch[e]] = dkv;
-            if (chan) st.pg[wave][i % kTH][ch[e]] = dga;
-            dgs += dga;
-            ds[e] = a * ds[e] - bt * ddl * st.k[i][ch[e]];
+            st.pk[wave][i % kTH][ch[e]] = dkv[e];
+            if (chan) st.pg[wave][i % kTH][ch[e]] = dga[e];
           }
         }
         if (headd) dgs = dpp_group_sum<64>(dgs);
         if (lane == 0) {
-          atomicAdd(&st.db[i], ddl * (vv[i] - rr[i]));
+          atomicAdd(&st.db[i], dbs);
           if (headd) atomicAdd(&st.dgh[i], dgs);
-          dv[(tok(t0 + i) * H + h) * DV + j] = bt * ddl;
+        }
+        if (lane < NCW) {
+          // lane w stores column j0 + w's dv
+          float dvw = 0.f;
+#pragma unroll
+          for (int w = 0; w < NCW; ++w) dvw = lane == w ? bt * ddl[w] : dvw;
+          dv[(tok(t0 + i) * H + h) * DV + j0 + lane] = dvw;
         }
       }
     }
@@ -277,8 +336,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(
   }
   if (dinit) {
 #pragma unroll
-    for (int e = 0; e < CPL; ++e)
-      if (live[e]) dinit[sidx(ch[e])] = ds[e];
+    for (int w = 0; w < NCW; ++w) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+        if (live[e]) dinit[sidx(ch[e], j0 + w)] = ds[w][e];
+    }
   }
 }
 
@@ -395,11 +457,11 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const In* v = static_cast<const In*>(a.v);
   const In* be = static_cast<const In*>(a.beta);
   const In* de = static_cast<const In*>(a.decay);
-  const dim3 grid(a.B * a.H * (a.DV / 4)), block(kBwdThreads);
+  const dim3 block(kBwdThreads);
   bool launched = false;
 #define KDA_BWD_CASE(dk_, dv_)                                                                   \
   if (a.DK == dk_ && a.DV == dv_) {                                                              \
-    bwd_kernel<dk_, dv_, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.init, a.dout, \
+    bwd_kernel<dk_, dv_, ncw<dk_>(), In><<<dim3(a.B * a.H * (dv_ / (4 * ncw<dk_>()))), block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.init, a.dout, \
                                                     a.dfinal, a.dq, a.dk, a.dv, a.dbeta,         \
                                                     a.ddecay, a.dinit, a.ckpt, a.T, a.H, a.Hk,   \
                                                     a.scale, a.l2norm, a.vfirst, a.tf);          \

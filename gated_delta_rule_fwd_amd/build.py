@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["api.hip", "decode.hip", "recurrent.hip", "chunked.hip", "backward.hip"] + [
+SOURCES = ["api.hip", "decode.hip", "recurrent.hip", "chunked.hip", "backward.hip", "backward_chunked.hip"] + [
     f"chunked_{dt}_d{d}.hip" for dt in ("bf16", "f32") for d in (0, 1, 2)]
 
 ARCH = "gfx950"

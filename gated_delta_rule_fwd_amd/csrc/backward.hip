@@ -31,6 +31,8 @@
 //
 // This is the plain form of the backward: time grows with T dependent
 // token steps per column, and the work is not shaped for MFMA.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -459,8 +461,13 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const In* de = static_cast<const In*>(a.decay);
   const dim3 block(kBwdThreads);
   bool launched = false;
+  if (a.decay_kind != DECAY_CHANNEL) {
+    e = launch_bwd_chunked(a, s);
+    if (e != hipSuccess) return e;
+    launched = true;
+  }
 #define KDA_BWD_CASE(dk_, dv_)                                                                   \
-  if (a.DK == dk_ && a.DV == dv_) {                                                              \
+  if (!launched && a.DK == dk_ && a.DV == dv_) {                                                 \
     bwd_kernel<dk_, dv_, ncw<dk_>(), In><<<dim3(a.B * a.H * (dv_ / (4 * ncw<dk_>()))), block, 0, s>>>(q, k, v, be, de, a.decay_kind, a.init, a.dout, \
                                                     a.dfinal, a.dq, a.dk, a.dv, a.dbeta,         \
                                                     a.ddecay, a.dinit, a.ckpt, a.T, a.H, a.Hk,   \
@@ -494,7 +501,8 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
 
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
   const long nsub = (static_cast<long>(T) + kTB - 1) / kTB;
-  return static_cast<size_t>(B) * H * nsub * DV * DK * sizeof(float);
+  const size_t plain = static_cast<size_t>(B) * H * nsub * DV * DK * sizeof(float);
+  return std::max(plain, bwd_chunked_workspace_bytes(B, T, H, DK, DV));
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {

@@ -297,11 +297,17 @@ int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const v
  *   ddt_bias       with KDA_TF_GATE and a dt_bias: like dt_bias, fp32, written
  *   d_initial_state NULL (not written) | like initial_state, fp32, written
  *   workspace      DEVICE, 16-byte aligned, at least kda_bwd_workspace_bytes
- *                  (the state every 16 tokens, for the reverse pass)
+ *                  (the state at every chunk boundary and the chunks' own
+ *                  matrices, or the state every 16 tokens)
  *
- * The reverse pass is sequential over tokens, in fp32; sums over value
- * columns (and, for dA_log and ddt_bias, over tokens) are gathered with
- * atomic adds, so results may differ in the last bits from run to run.
+ * With a per-head decay or none the backward runs chunk by chunk in the WY
+ * form (chunks of 32 tokens: the states at chunk boundaries forward, their
+ * gradients in reverse, then every chunk's local gradients in parallel);
+ * with a per-channel decay it runs token by token, the state every 16 tokens
+ * checkpointed.  All arithmetic is fp32; sums over value heads of a group
+ * (and, token by token, over value columns; for dA_log and ddt_bias over
+ * tokens) are gathered with atomic adds, so results may differ in the last
+ * bits from run to run.
  * Errors as kda_fwd_chunked; KDA_ERR_NULL if (T > 0) d_o, dq, dk, dv, dbeta,
  * (with a decay) ddecay, or (with KDA_TF_GATE) dA_log or (with a dt_bias)
  * ddt_bias is NULL; KDA_ERR_WORKSPACE as for the forward.  T == 0 copies
@@ -316,8 +322,8 @@ int kda_bwd(const void* q, const void* k, const void* v, const void* beta, const
             float* dA_log, float* ddt_bias, void* workspace, size_t workspace_bytes,
             void* stream);
 
-/* Workspace bytes of kda_bwd (host-only); 0 when T == 0 or the sizes are
- * invalid. */
+/* Workspace bytes of kda_bwd (host-only), enough for either form; 0 when
+ * T == 0 or the sizes are invalid. */
 size_t kda_bwd_workspace_bytes(int B, int T, int HV, int DK, int DV);
 
 /* Static, NUL-terminated description of a status code. */

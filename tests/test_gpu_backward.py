@@ -27,7 +27,9 @@ CASES = [
     ("gdn_d128", dict(B=1, T=16, H=2, DK=64, DV=128), dict(use_qk_l2norm=False)),
     ("kda_d128", dict(B=1, T=53, H=2, DV=64, init_state=True), {}),
     ("kda_d128", dict(B=1, T=40, H=2, decay="channel_steep"), {}),
+    ("gdn_d128", dict(B=1, T=161, H=1, HV=2, init_state=True), {}),
     ("deltanet_d64", dict(B=2, T=33, H=2, HV=4), {}),
+    ("deltanet_d64", dict(B=1, T=130, H=2, init_state=True), {}),
     ("deltanet_d64", dict(B=1, T=1, H=2, DK=128, DV=32, init_state=True), {}),
 ]
 

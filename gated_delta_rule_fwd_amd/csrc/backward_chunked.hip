@@ -194,390 +194,563 @@ __device__ __forceinline__ void load_tokvec(TokVec& tv, const CWs& w, long tok0,
   }
 }
 
-// the normalised rows of k (and with qh, of q) of a chunk into LDS
-template <int DK, typename In>
-__device__ __forceinline__ void load_rows(float (*kh)[DK + 1], float (*qh)[DK + 1], const In* k, const In* q,
-                                          const CWs& w, long tok0, int H, int h, int Hk, int hk, int L,
-                                          int tid, int nthr) {
-  for (int idx = tid; idx < kC * DK; idx += nthr) {
-    const int r = idx / DK, c = idx % DK;
-    const bool in = r < L;
-    const long rb = ((tok0 + r) * Hk + hk) * DK + c;
-    const long t = (tok0 + r) * H + h;
-    kh[r][c] = in ? act<In>::load1(k + rb) * w.sk[t] : 0.f;
-    if (qh) qh[r][c] = in ? act<In>::load1(q + rb) * w.sq[t] : 0.f;
+// The normalised rows of a chunk (raw rows times their norm factor) into
+// LDS rows of pitch KP; rows past the sequence's end are zero.
+template <int DK, int KP, typename In>
+__device__ __forceinline__ void stage_rows(float (*dst)[KP], const In* src, const float* fac, long tok0, int H,
+                                           int h, int Hk, int hk, int L, int tid, int nthr) {
+  constexpr int V = act<In>::kVec, LPR = DK / V;
+  for (int idx = tid; idx < kC * LPR; idx += nthr) {
+    const int r = idx / LPR, seg = idx % LPR;
+    float x[V];
+    if (r < L) {
+      act<In>::load_vec(src + ((tok0 + r) * Hk + hk) * DK + seg * V, x);
+      const float f = fac[(tok0 + r) * H + h];
+#pragma unroll
+      for (int e = 0; e < V; ++e) x[e] *= f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) dst[r][seg * V + e] = x[e];
   }
 }
 
+// T (and with Pd, P) of a chunk into LDS, one 16-byte load per thread and pass
+__device__ __forceinline__ void stage_mats(float (*Td)[kC + 1], float (*Pd)[kC + 1], const CWs& w, size_t cb,
+                                           int tid, int nthr) {
+  for (int idx = tid; idx < kC * kC / 4; idx += nthr) {
+    const int r = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
+    const f32x4 t = *reinterpret_cast<const f32x4*>(w.Tm + cb + r * kC + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Td[r][c4 + e] = t[e];
+    if (Pd) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(w.Pm + cb + r * kC + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Pd[r][c4 + e] = p[e];
+    }
+  }
+}
+
+// acc += A (16 x 4) B (4 x 16), fp32: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16]; it holds rows 4 (l / 16) + j, j = 0..3, of column l % 16.
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
 // (1) per (b, h, slice of kNS value columns): every chunk's S0 into the
-// workspace, chunk after chunk.
+// workspace, chunk after chunk.  The slice of the state (DK x 16) sits in
+// MFMA accumulators, 16 key rows per tile, tile m in wave m % 4.  Per chunk:
+// K S as partial products of each wave's own tiles (the tile is the B
+// operand as it stands), summed through LDS; Y and D = T Y on VALU; then
+// S <- exp(gC) S + K^T (F . D) on MFMA.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const In* __restrict__ v,
                                                  const float* __restrict__ init, CWs w, int T, int H, int Hk,
                                                  int N, int vfirst) {
-  __shared__ float kh[kC][DK + 1];
+  constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
+  __shared__ __align__(16) float kh[kC][KP];
   __shared__ float Tm[kC][kC + 1];
-  __shared__ float S[DK][kNS + 1];
-  __shared__ float Y[kC][kNS + 1], D[kC][kNS + 1];
+  __shared__ float part[NW][kC][kNS + 1];
+  __shared__ float Y[kC][kNS + 1], FD[kC][kNS + 1];
   __shared__ TokVec tv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   constexpr int nsl = DV / kNS;
   const int sl = blockIdx.x % nsl, bh = blockIdx.x / nsl, b = bh / H, h = bh % H, hk = h / (H / Hk);
   const int n0 = sl * kNS;
   const long sb = static_cast<long>(bh) * DK * DV;
   auto sidx = [&](int c, int n) { return sb + (vfirst ? static_cast<long>(n) * DK + c : static_cast<long>(c) * DV + n); };
-  for (int idx = tid; idx < DK * kNS; idx += kThr) {
-    const int c = idx / kNS, n = idx % kNS;
-    S[c][n] = init ? init[sidx(c, n0 + n)] : 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int mt = wave + 4 * j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[j][e] = (mt < MT && init) ? init[sidx(16 * mt + 4 * lg + e, n0 + li)] : 0.f;
   }
   for (int ci = 0; ci < N; ++ci) {
     const int t0 = ci * kC, L = min(kC, T - t0);
     const long tok0 = static_cast<long>(b) * T + t0;
+    float vv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
+      vv[u] = r < L ? act<In>::load1(v + ((tok0 + r) * H + h) * DV + n0 + n) : 0.f;
+    }
     __syncthreads();
     float* s0 = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
-    for (int idx = tid; idx < DK * kNS; idx += kThr) {
-      const int c = idx / kNS, n = idx % kNS;
-      s0[c * DV + n0 + n] = S[c][n];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt = wave + 4 * j;
+      if (mt < MT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s0[(16 * mt + 4 * lg + e) * DV + n0 + li] = acc[j][e];
+      }
     }
-    load_rows<DK, In>(kh, nullptr, k, nullptr, w, tok0, H, h, Hk, hk, L, tid, kThr);
-    const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
-    for (int idx = tid; idx < kC * kC; idx += kThr) Tm[idx / kC][idx % kC] = w.Tm[cb + idx];
+    stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr);
+    stage_mats(Tm, nullptr, w, (static_cast<size_t>(bh) * N + ci) * kC * kC, tid, kThr);
     load_tokvec(tv, w, tok0, H, h, L, tid);
     __syncthreads();
-    // Y = beta . (V - exp(gx) . K S0)
-    for (int idx = tid; idx < kC * kNS; idx += kThr) {
-      const int r = idx / kNS, n = idx % kNS;
-      float ks = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < DK; ++c) ks += kh[r][c] * S[c][n];
-      const float vv = r < L ? act<In>::load1(v + ((tok0 + r) * H + h) * DV + n0 + n) : 0.f;
-      Y[r][n] = tv.bt[r] * (vv - tv.egx[r] * ks);
+    // K S over this wave's key rows: rows 16 rt + l % 16 of K, keys 16 mt + 4 (l / 16) + e
+    if (wave < NW) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int mt = wave + 4 * j;
+          if (mt < MT) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = mma4(a[e], acc[j][e], p);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][li] = p[e];
+      }
     }
     __syncthreads();
-    // D = T Y (T unit lower triangular)
-    for (int idx = tid; idx < kC * kNS; idx += kThr) {
-      const int r = idx / kNS, n = idx % kNS;
+    // Y = beta . (V - exp(gx) . K S)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
+      float ks = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) ks += part[q][r][n];
+      Y[r][n] = tv.bt[r] * (vv[u] - tv.egx[r] * ks);
+    }
+    __syncthreads();
+    // F . D, D = T Y (T unit lower triangular)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
       float d = 0.f;
       for (int s = 0; s <= r; ++s) d += Tm[r][s] * Y[s][n];
-      D[r][n] = d;
+      FD[r][n] = tv.F[r] * d;
     }
     __syncthreads();
     // S <- exp(gC) S + K^T (F . D)
-    for (int idx = tid; idx < DK * kNS; idx += kThr) {
-      const int c = idx / kNS, n = idx % kNS;
-      float u = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < kC; ++r) u += kh[r][c] * tv.F[r] * D[r][n];
-      S[c][n] = tv.egC * S[c][n] + u;
+    const float egC = tv.egC;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt = wave + 4 * j;
+      if (mt < MT) {
+        acc[j] *= egC;
+#pragma unroll
+        for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(kh[4 * ks + lg][16 * mt + li], FD[4 * ks + lg][li], acc[j]);
+      }
     }
   }
 }
 
 // (2) per (b, h, slice): the walk of the state gradient from the last chunk
 // to the first; every chunk's dS1 into the workspace, dv, and the initial
-// state's gradient.
+// state's gradient.  The slice of dS sits in MFMA accumulators as S does in
+// (1); per chunk: K dS (partial products per wave, summed through LDS),
+// dD = P^T dO + F . K dS and dY = T^T dD on VALU, then
+// dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const In* __restrict__ k,
                                                  const float* __restrict__ dout, const float* __restrict__ dfinal,
                                                  float* __restrict__ dv, float* __restrict__ dinit, CWs w, int T,
                                                  int H, int Hk, int N, int vfirst) {
-  __shared__ float kh[kC][DK + 1], qh[kC][DK + 1];
+  constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
+  __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
   __shared__ float Tm[kC][kC + 1], Pm[kC][kC + 1];
-  __shared__ float dS[DK][kNS + 1];
-  __shared__ float dO[kC][kNS + 1], dD[kC][kNS + 1], dX[kC][kNS + 1];
+  __shared__ float part[NW][kC][kNS + 1];
+  __shared__ float dO[kC][kNS + 1], dD[kC][kNS + 1], BB[2 * kC][kNS + 1];
   __shared__ TokVec tv;
-  constexpr int PER = DK * kNS / kThr;
-  static_assert(DK * kNS % kThr == 0, "whole state elements per thread");
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   constexpr int nsl = DV / kNS;
   const int sl = blockIdx.x % nsl, bh = blockIdx.x / nsl, b = bh / H, h = bh % H, hk = h / (H / Hk);
   const int n0 = sl * kNS;
   const long sb = static_cast<long>(bh) * DK * DV;
   auto sidx = [&](int c, int n) { return sb + (vfirst ? static_cast<long>(n) * DK + c : static_cast<long>(c) * DV + n); };
-  for (int idx = tid; idx < DK * kNS; idx += kThr) {
-    const int c = idx / kNS, n = idx % kNS;
-    dS[c][n] = dfinal ? dfinal[sidx(c, n0 + n)] : 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int mt = wave + 4 * j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[j][e] = (mt < MT && dfinal) ? dfinal[sidx(16 * mt + 4 * lg + e, n0 + li)] : 0.f;
   }
   for (int ci = N - 1; ci >= 0; --ci) {
     const int t0 = ci * kC, L = min(kC, T - t0);
     const long tok0 = static_cast<long>(b) * T + t0;
+    float dov[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
+      dov[u] = r < L ? dout[((tok0 + r) * H + h) * DV + n0 + n] : 0.f;
+    }
     __syncthreads();
     float* d1 = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
-    for (int idx = tid; idx < DK * kNS; idx += kThr) {
-      const int c = idx / kNS, n = idx % kNS;
-      d1[c * DV + n0 + n] = dS[c][n];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt = wave + 4 * j;
+      if (mt < MT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d1[(16 * mt + 4 * lg + e) * DV + n0 + li] = acc[j][e];
+      }
     }
-    load_rows<DK, In>(kh, qh, k, q, w, tok0, H, h, Hk, hk, L, tid, kThr);
-    const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
-    for (int idx = tid; idx < kC * kC; idx += kThr) {
-      Tm[idx / kC][idx % kC] = w.Tm[cb + idx];
-      Pm[idx / kC][idx % kC] = w.Pm[cb + idx];
-    }
-    for (int idx = tid; idx < kC * kNS; idx += kThr) {
-      const int r = idx / kNS, n = idx % kNS;
-      dO[r][n] = r < L ? dout[((tok0 + r) * H + h) * DV + n0 + n] : 0.f;
+    stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr);
+    stage_rows<DK, KP, In>(qh, q, w.sq, tok0, H, h, Hk, hk, L, tid, kThr);
+    stage_mats(Tm, Pm, w, (static_cast<size_t>(bh) * N + ci) * kC * kC, tid, kThr);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr;
+      dO[idx / kNS][idx % kNS] = dov[u];
     }
     load_tokvec(tv, w, tok0, H, h, L, tid);
     __syncthreads();
-    // dD = P^T dO + F . K dS1
-    for (int idx = tid; idx < kC * kNS; idx += kThr) {
-      const int r = idx / kNS, n = idx % kNS;
+    // K dS over this wave's key rows
+    if (wave < NW) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int mt = wave + 4 * j;
+          if (mt < MT) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = mma4(a[e], acc[j][e], p);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][li] = p[e];
+      }
+    }
+    __syncthreads();
+    // dD = P^T dO + F . K dS
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
       float kd = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < DK; ++c) kd += kh[r][c] * dS[c][n];
+#pragma unroll
+      for (int qq = 0; qq < NW; ++qq) kd += part[qq][r][n];
       float pd = 0.f;
       for (int s = r; s < kC; ++s) pd += Pm[s][r] * dO[s][n];
       dD[r][n] = pd + tv.F[r] * kd;
     }
     __syncthreads();
-    // dX = beta . T^T dD: the gradient of v
-    for (int idx = tid; idx < kC * kNS; idx += kThr) {
-      const int r = idx / kNS, n = idx % kNS;
+    // dX = beta . T^T dD, the gradient of v; the B operand of the dS update
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
       float y = 0.f;
       for (int s = r; s < kC; ++s) y += Tm[s][r] * dD[s][n];
       const float x = tv.bt[r] * y;
-      dX[r][n] = x;
       if (r < L) dv[((tok0 + r) * H + h) * DV + n0 + n] = x;
+      BB[r][n] = tv.egm[r] * dO[r][n];
+      BB[kC + r][n] = -tv.egx[r] * x;
     }
     __syncthreads();
-    // dS0 = exp(gC) dS1 + Q^T (exp(gam) . dO) - K^T (exp(gx) . dX)
-    float nd[PER];
+    // dS <- exp(gC) dS + Q^T (exp(gam) . dO) - K^T (exp(gx) . dX)
+    const float egC = tv.egC;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + u * kThr, c = idx / kNS, n = idx % kNS;
-      float a = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < kC; ++r) a += qh[r][c] * tv.egm[r] * dO[r][n] - kh[r][c] * tv.egx[r] * dX[r][n];
-      nd[u] = tv.egC * dS[c][n] + a;
-    }
-    __syncthreads();
+    for (int j = 0; j < NT; ++j) {
+      const int mt = wave + 4 * j;
+      if (mt < MT) {
+        acc[j] *= egC;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = tid + u * kThr;
-      dS[idx / kNS][idx % kNS] = nd[u];
+        for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(qh[4 * ks + lg][16 * mt + li], BB[4 * ks + lg][li], acc[j]);
+#pragma unroll
+        for (int ks = 0; ks < kC / 4; ++ks)
+          acc[j] = mma4(kh[4 * ks + lg][16 * mt + li], BB[kC + 4 * ks + lg][li], acc[j]);
+      }
     }
   }
-  __syncthreads();
   if (dinit) {
-    for (int idx = tid; idx < DK * kNS; idx += kThr) {
-      const int c = idx / kNS, n = idx % kNS;
-      dinit[sidx(c, n0 + n)] = dS[c][n];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int mt = wave + 4 * j;
+      if (mt < MT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dinit[sidx(16 * mt + 4 * lg + e, n0 + li)] = acc[j][e];
+      }
     }
   }
 }
 
-// (3) per (b, h, chunk): the remaining gradients over the value columns kNS
+// (3) per (b, h, chunk): the remaining gradients over the value columns, 16
 // at a time: dq and dk of the normalised rows (added: value heads of a group
-// share their q/k head), dbeta and the decay's gradient (written).
+// share their q/k head), dbeta and the decay's gradient (written).  Eight
+// waves.  Per slice: [K S0 | Q S0 | K dS1] on MFMA (each wave a quarter of
+// the keys of one row tile, summed through LDS); X, D, dD, dY and the
+// per-token sums on VALU, one (row, column) element per thread; then on
+// MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
+// dq += dO S0^T, dk += (F . D) dS1^T - (exp(gx) beta . dY) S0^T (tiles per
+// wave, held across the slices).  Then dA, dG and Z on VALU and the last
+// products dq += Z K, dk += (dG + dG^T) K + Z^T Q on MFMA.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, const In* __restrict__ k,
                                                     const In* __restrict__ v, const float* __restrict__ dout,
                                                     float* __restrict__ dq, float* __restrict__ dk,
                                                     float* __restrict__ dbeta, float* __restrict__ ddecay,
                                                     CWs w, int T, int H, int Hk, int N) {
-  __shared__ float kh[kC][DK + 1], qh[kC][DK + 1];
-  __shared__ float aq[kC][DK + 1], ak[kC][DK + 1];   // dq, dk accumulators
-  __shared__ float Tm[kC][kC + 1], Pm[kC][kC + 1], dT[kC][kC + 1], dP[kC][kC + 1];
-  __shared__ float M[kC][kC + 1], EE[kC][kC + 1], PP[kC][kC + 1];
-  __shared__ float S0[DK][kNS + 1], S1[DK][kNS + 1];  // slices of S0 and dS1
-  __shared__ float dO[kC][kNS + 1], X[kC][kNS + 1], D[kC][kNS + 1], dD[kC][kNS + 1], dY[kC][kNS + 1];
-  __shared__ float KS[kC][kNS + 1], QS[kC][kNS + 1], KD[kC][kNS + 1];
-  __shared__ float gb[kC], ggm[kC], ggx[kC], ggc[kC];  // per token: dbeta, dgam, dgx, and parts of dgC
-  __shared__ float sgm[kC], sgx[kC], sdc;
+  constexpr int KP = DK + 4, NT16 = DK / 16, KQ = DK / 16;       // k-steps per quarter of the keys
+  constexpr int NQK = 4 * NT16, TPW = (NQK + 7) / 8;              // dq/dk tiles, per wave
+  constexpr int SPT = DK * kNS / kThr3;                          // state floats per thread per slice
+  constexpr int SL = kNS / SPT;                                   // threads per state row
+  constexpr int nsl = DV / kNS;
+  __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
+  __shared__ float S0s[DK][kNS + 1], S1s[DK][kNS + 1];
+  __shared__ float part[4][3][kC][kNS + 1];
+  __shared__ float Tm[kC][kC + 1], Pm[kC][kC + 1];
+  __shared__ float dO[kC][kNS + 1], Yb[kC][kNS + 1], D[kC][kNS + 1], FD[kC][kNS + 1];
+  __shared__ float dD[kC][kNS + 1], dYs[kC][kNS + 1];
+  __shared__ float dTm[kC][kC + 1], dPm[kC][kC + 1], M[kC][kC + 1], EE[kC][kC + 1], PP[kC][kC + 1];
+  __shared__ float Gp[2][kC][kC + 1], dGs[kC][kC + 1];
+  __shared__ float tb[kC], tm[kC], tx[kC], tc[kC], sgm[kC], sgx[kC], red[8];
   __shared__ TokVec tv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int er = tid / kNS, en = tid % kNS;   // this thread's element of a 32 x 16 slice tile
   const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);
   const int t0 = ci * kC, L = min(kC, T - t0);
   const long tok0 = static_cast<long>(b) * T + t0;
   const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
   const float* s0g = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
   const float* s1g = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
-  load_rows<DK, In>(kh, qh, k, q, w, tok0, H, h, Hk, hk, L, tid, kThr3);
-  for (int idx = tid; idx < kC * DK; idx += kThr3) aq[idx / DK][idx % DK] = ak[idx / DK][idx % DK] = 0.f;
-  for (int idx = tid; idx < kC * kC; idx += kThr3) {
-    const int r = idx / kC, s = idx % kC;
-    Tm[r][s] = w.Tm[cb + idx];
-    Pm[r][s] = w.Pm[cb + idx];
-    dT[r][s] = dP[r][s] = 0.f;
-  }
+  const bool rin = er < L;
+  const long vrow = ((tok0 + er) * H + h) * DV;
+  const int sc = tid / SL, sn = (tid % SL) * SPT;   // this thread's state elements: row sc, columns sn..
+  float ps0[SPT], ps1[SPT], pdo, pv;
+  auto prefetch = [&](int s) {
+    const int nb = s * kNS;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      ps0[e] = s0g[sc * DV + nb + sn + e];
+      ps1[e] = s1g[sc * DV + nb + sn + e];
+    }
+    pdo = rin ? dout[vrow + nb + en] : 0.f;
+    pv = rin ? act<In>::load1(v + vrow + nb + en) : 0.f;
+  };
+  prefetch(0);
+  stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr3);
+  stage_rows<DK, KP, In>(qh, q, w.sq, tok0, H, h, Hk, hk, L, tid, kThr3);
+  stage_mats(Tm, Pm, w, cb, tid, kThr3);
   load_tokvec(tv, w, tok0, H, h, L, tid);
   if (tid < kC) {
-    const int r = tid;
-    gb[r] = ggm[r] = ggx[r] = ggc[r] = 0.f;
-    sgm[r] = r < L ? w.gm[(tok0 + r) * H + h] : 0.f;
-    sgx[r] = r < L ? w.gx[(tok0 + r) * H + h] : 0.f;
-    if (r == 0) sdc = 0.f;
+    sgm[tid] = tid < L ? w.gm[(tok0 + tid) * H + h] : 0.f;
+    sgx[tid] = tid < L ? w.gx[(tok0 + tid) * H + h] : 0.f;
   }
-  for (int n0 = 0; n0 < DV; n0 += kNS) {
-    __syncthreads();
-    for (int idx = tid; idx < DK * kNS; idx += kThr3) {
-      const int c = idx / kNS, n = idx % kNS;
-      S0[c][n] = s0g[c * DV + n0 + n];
-      S1[c][n] = s1g[c * DV + n0 + n];
-    }
-    for (int idx = tid; idx < kC * kNS; idx += kThr3) {
-      const int r = idx / kNS, n = idx % kNS;
-      dO[r][n] = r < L ? dout[((tok0 + r) * H + h) * DV + n0 + n] : 0.f;
-    }
-    __syncthreads();
-    // K S0, Q S0, K dS1, and X = V - exp(gx) . K S0
-    for (int idx = tid; idx < kC * kNS; idx += kThr3) {
-      const int r = idx / kNS, n = idx % kNS;
-      float ks = 0.f, qs = 0.f, kd = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < DK; ++c) {
-        ks += kh[r][c] * S0[c][n];
-        qs += qh[r][c] * S0[c][n];
-        kd += kh[r][c] * S1[c][n];
-      }
-      KS[r][n] = ks;
-      QS[r][n] = qs;
-      KD[r][n] = kd;
-      const float vv = r < L ? act<In>::load1(v + ((tok0 + r) * H + h) * DV + n0 + n) : 0.f;
-      X[r][n] = vv - tv.egx[r] * ks;
-    }
-    __syncthreads();
-    // D = T (beta . X);  dD = P^T dO + F . K dS1
-    for (int idx = tid; idx < kC * kNS; idx += kThr3) {
-      const int r = idx / kNS, n = idx % kNS;
-      float d = 0.f, pd = 0.f;
-      for (int s = 0; s <= r; ++s) d += Tm[r][s] * tv.bt[s] * X[s][n];
-      for (int s = r; s < kC; ++s) pd += Pm[s][r] * dO[s][n];
-      D[r][n] = d;
-      dD[r][n] = pd + tv.F[r] * KD[r][n];
-    }
-    __syncthreads();
-    // dY = T^T dD
-    for (int idx = tid; idx < kC * kNS; idx += kThr3) {
-      const int r = idx / kNS, n = idx % kNS;
-      float y = 0.f;
-      for (int s = r; s < kC; ++s) y += Tm[s][r] * dD[s][n];
-      dY[r][n] = y;
-    }
-    __syncthreads();
-    // Per token: dbeta through Y; the decay through exp(gam) (the output's
-    // Q S0 term), exp(gx) (X's K S0 term) and F (the state's K^T (F . D)),
-    // whose exponent gC - gam feeds dgC and dgam.
-    if (tid < kC) {
-      const int r = tid;
-      float sb = 0.f, so = 0.f, sx = 0.f, sf = 0.f;
+  float sb = 0.f, so = 0.f, sx = 0.f, sf = 0.f, sdc = 0.f;   // per-token sums (this thread's columns)
+  f32x4 atp = {0.f, 0.f, 0.f, 0.f};                          // dT (waves 0-3) or dP (4-7) tile
+  f32x4 aqk[TPW];
 #pragma unroll
-      for (int n = 0; n < kNS; ++n) {
-        sb += dY[r][n] * X[r][n];
-        so += dO[r][n] * QS[r][n];
-        sx += dY[r][n] * KS[r][n];
-        sf += KD[r][n] * D[r][n];
-      }
-      gb[r] += sb;
-      ggm[r] += tv.egm[r] * so - tv.F[r] * sf;
-      ggx[r] -= tv.egx[r] * tv.bt[r] * sx;
-      ggc[r] += tv.F[r] * sf;
-    } else if (tid >= 64 && tid < 128) {
-      // dgC through exp(gC) S0: exp(gC) <dS1, S0> (wave 1)
-      float acc = 0.f;
-      for (int idx = tid - 64; idx < DK * kNS; idx += 64) acc += S1[idx / kNS][idx % kNS] * S0[idx / kNS][idx % kNS];
-      acc = dpp_group_sum<64>(acc);
-      if (tid == 64) sdc += tv.egC * acc;
-    }
-    // dT += dD Y^T (Y = beta . X) on T's lower part; dP += dO D^T on P's support
-    for (int idx = tid; idx < kC * kC; idx += kThr3) {
-      const int r = idx / kC, s = idx % kC;
-      if (s > r) continue;
-      float t = 0.f, pp = 0.f;
+  for (int j = 0; j < TPW; ++j) aqk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tpm = wave >> 2, tpr = (wave >> 1) & 1, tpc = wave & 1;
+  const int pmt = wave & 1, pq = wave >> 1;                  // K-S product: row tile, key quarter
+  for (int s = 0; s < nsl; ++s) {
+    __syncthreads();
 #pragma unroll
-      for (int n = 0; n < kNS; ++n) {
-        t += dD[r][n] * X[s][n];
-        pp += dO[r][n] * D[s][n];
-      }
-      dT[r][s] += t * tv.bt[s];
-      dP[r][s] += pp;
+    for (int e = 0; e < SPT; ++e) {
+      S0s[sc][sn + e] = ps0[e];
+      S1s[sc][sn + e] = ps1[e];
+      sdc += ps0[e] * ps1[e];
     }
-    // dq += exp(gam) . dO S0^T;  dk += -exp(gx) . beta . dY S0^T + F . D dS1^T
-    for (int idx = tid; idx < kC * DK; idx += kThr3) {
-      const int r = idx / DK, c = idx % DK;
-      float a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    dO[er][en] = pdo;
+    const float vcur = pv, docur = pdo;
+    __syncthreads();
+    if (s + 1 < nsl) prefetch(s + 1);
+    // [K S0 | Q S0 | K dS1], this wave's row tile and key quarter
+    {
+      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0;
 #pragma unroll
-      for (int n = 0; n < kNS; ++n) {
-        a1 += dO[r][n] * S0[c][n];
-        a2 += dY[r][n] * S0[c][n];
-        a3 += D[r][n] * S1[c][n];
+      for (int ks = pq * KQ; ks < (pq + 1) * KQ; ++ks) {
+        const float ak = kh[16 * pmt + li][4 * ks + lg], aq = qh[16 * pmt + li][4 * ks + lg];
+        const float b0 = S0s[4 * ks + lg][li], b1 = S1s[4 * ks + lg][li];
+        p0 = mma4(ak, b0, p0);
+        p1 = mma4(aq, b0, p1);
+        p2 = mma4(ak, b1, p2);
       }
-      aq[r][c] += tv.egm[r] * a1;
-      ak[r][c] += tv.F[r] * a3 - tv.egx[r] * tv.bt[r] * a2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part[pq][0][16 * pmt + 4 * lg + e][li] = p0[e];
+        part[pq][1][16 * pmt + 4 * lg + e][li] = p1[e];
+        part[pq][2][16 * pmt + 4 * lg + e][li] = p2[e];
+      }
     }
+    __syncthreads();
+    float ksv = 0.f, qsv = 0.f, kdv = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      ksv += part[qq][0][er][en];
+      qsv += part[qq][1][er][en];
+      kdv += part[qq][2][er][en];
+    }
+    const float x = vcur - tv.egx[er] * ksv;
+    Yb[er][en] = tv.bt[er] * x;
+    __syncthreads();
+    // D = T Y;  dD = P^T dO + F . K dS1
+    float d = 0.f, pd = 0.f;
+    for (int t = 0; t <= er; ++t) d += Tm[er][t] * Yb[t][en];
+    for (int t = er; t < kC; ++t) pd += Pm[t][er] * dO[t][en];
+    const float dd = pd + tv.F[er] * kdv;
+    D[er][en] = d;
+    FD[er][en] = tv.F[er] * d;
+    dD[er][en] = dd;
+    __syncthreads();
+    // dY = T^T dD, and the per-token sums
+    float y = 0.f;
+    for (int t = er; t < kC; ++t) y += Tm[t][er] * dD[t][en];
+    dYs[er][en] = -tv.egx[er] * tv.bt[er] * y;
+    sb += y * x;
+    so += docur * qsv;
+    sx += y * (vcur - x);
+    sf += kdv * d;
+    __syncthreads();
+    // dT += dD Y^T, dP += dO D^T (this wave's tile)
+#pragma unroll
+    for (int ks = 0; ks < kNS / 4; ++ks) {
+      const float a = tpm ? dO[16 * tpr + li][4 * ks + lg] : dD[16 * tpr + li][4 * ks + lg];
+      const float bb = tpm ? D[16 * tpc + li][4 * ks + lg] : Yb[16 * tpc + li][4 * ks + lg];
+      atp = mma4(a, bb, atp);
+    }
+    // dq += dO S0^T;  dk += (F . D) dS1^T + (-exp(gx) beta . dY) S0^T
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + 8 * j;
+      if (t < NQK) {
+        const int mat = t / (2 * NT16), rem = t % (2 * NT16), mt = rem / NT16, nt = rem % NT16;
+#pragma unroll
+        for (int ks = 0; ks < kNS / 4; ++ks) {
+          const int r = 16 * mt + li, n = 4 * ks + lg, c = 16 * nt + li;
+          if (mat == 0) {
+            aqk[j] = mma4(dO[r][n], S0s[c][n], aqk[j]);
+          } else {
+            aqk[j] = mma4(FD[r][n], S1s[c][n], aqk[j]);
+            aqk[j] = mma4(dYs[r][n], S0s[c][n], aqk[j]);
+          }
+        }
+      }
+    }
+  }
+  // per-token sums over the 16 columns of a row (16 consecutive lanes)
+  sb = dpp_group_sum<16>(sb);
+  so = dpp_group_sum<16>(so);
+  sx = dpp_group_sum<16>(sx);
+  sf = dpp_group_sum<16>(sf);
+  sdc = dpp_group_sum<64>(sdc);
+  __syncthreads();
+  if (en == 0) {
+    tb[er] = sb;
+    tm[er] = tv.egm[er] * so - tv.F[er] * sf;
+    tx[er] = -tv.bt[er] * sx;
+    tc[er] = tv.F[er] * sf;
+  }
+  if (lane == 0) red[wave] = sdc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 16 * tpr + 4 * lg + e, c = 16 * tpc + li;
+    if (tpm) dPm[r][c] = atp[e];
+    else dTm[r][c] = c <= r ? atp[e] : 0.f;
   }
   __syncthreads();
-  // M = dT T^T (dT lower, T lower): M_rs = sum_{u <= min(r, s)} dT_ru T_su
-  for (int idx = tid; idx < kC * kC; idx += kThr3) {
-    const int r = idx / kC, s = idx % kC, um = min(r, s);
+  // M = dT T^T (dT, T lower): M_rs = sum_{u <= min(r, s)} dT_ru T_su; K K^T on MFMA
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC, um = min(r, c);
     float m = 0.f;
-    for (int u = 0; u <= um; ++u) m += dT[r][u] * Tm[s][u];
-    M[r][s] = m;
+    for (int t = 0; t <= um; ++t) m += dTm[r][t] * Tm[c][t];
+    M[r][c] = m;
+  }
+  {
+    const int gt = wave & 3, gr = gt >> 1, gc = gt & 1, gh = wave >> 2;
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = gh * (DK / 8); ks < (gh + 1) * (DK / 8); ++ks)
+      p = mma4(kh[16 * gr + li][4 * ks + lg], kh[16 * gc + li][4 * ks + lg], p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Gp[gh][16 * gr + 4 * lg + e][16 * gc + li] = p[e];
   }
   __syncthreads();
-  // dA = -T^T M on s < r; E = dA . (K K^T) . W; dG = diag(beta) dA . W
-  // (into dT); Z = dP . Vw (into dP) and dP . P
-  for (int idx = tid; idx < kC * kC; idx += kThr3) {
-    const int r = idx / kC, s = idx % kC;
+  // dA = -T^T M on s < r; E = dA . (K K^T) . W; dG = diag(beta) dA . W;
+  // Z = dP . Vw (into dPm) and dP . P
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
     float e = 0.f, dg = 0.f;
-    if (s < r) {
+    if (c < r) {
       float da = 0.f;
-      for (int u = r; u < kC; ++u) da -= Tm[u][r] * M[u][s];
-      float g = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < DK; ++c) g += kh[r][c] * kh[s][c];
-      const float wr = __expf(sgx[r] - sgm[s]);
-      e = da * g * wr;
+      for (int t = r; t < kC; ++t) da -= Tm[t][r] * M[t][c];
+      const float wr = __expf(sgx[r] - sgm[c]);
+      e = da * (Gp[0][r][c] + Gp[1][r][c]) * wr;
       dg = da * tv.bt[r] * wr;
     }
-    EE[r][s] = e;
-    dT[r][s] = dg;
-    const float dp = s <= r ? dP[r][s] : 0.f;
-    PP[r][s] = dp * Pm[r][s];
-    dP[r][s] = s <= r ? dp * __expf(sgm[r] - sgm[s]) : 0.f;
+    EE[r][c] = e;
+    Gp[0][r][c] = dg;   // this thread's own element of Gp, read above: dG in its place
+    const float dp = c <= r ? dPm[r][c] : 0.f;
+    PP[r][c] = dp * Pm[r][c];
+    dPm[r][c] = c <= r ? dp * __expf(sgm[r] - sgm[c]) : 0.f;
   }
   __syncthreads();
-  // per token: dbeta, dgx and dgam through A and P
   if (tid < kC) {
     const int r = tid;
     float re = 0.f, rp = 0.f, ce = 0.f, cp = 0.f;
-    for (int s = 0; s < kC; ++s) {
-      re += EE[r][s];
-      rp += PP[r][s];
-      ce += tv.bt[s] * EE[s][r];
-      cp += PP[s][r];
+    for (int t = 0; t < kC; ++t) {
+      re += EE[r][t];
+      rp += PP[r][t];
+      ce += tv.bt[t] * EE[t][r];
+      cp += PP[t][r];
     }
-    gb[r] += re;
-    ggx[r] += tv.bt[r] * re;
-    ggm[r] += rp - ce - cp;
+    tb[r] += re;
+    tx[r] += tv.bt[r] * re;
+    tm[r] += rp - ce - cp;
   }
-  // dq += Z K;  dk += (dG + dG^T) K + Z^T Q; then into the outputs
-  for (int idx = tid; idx < kC * DK; idx += kThr3) {
-    const int r = idx / DK, c = idx % DK;
-    float aqv = aq[r][c], akv = ak[r][c];
-    for (int s = 0; s < kC; ++s) {
-      aqv += dP[r][s] * kh[s][c];
-      akv += (dT[r][s] + dT[s][r]) * kh[s][c] + dP[s][r] * qh[s][c];
-    }
-    if (r < L) {
-      const long o = ((tok0 + r) * Hk + hk) * DK + c;
-      atomicAdd(dq + o, aqv);
-      atomicAdd(dk + o, akv);
-    }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
+    dGs[r][c] = Gp[0][r][c] + Gp[0][c][r];
   }
   __syncthreads();
+  // dq = exp(gam) . (dO S0^T) + Z K;  dk += (dG + dG^T) K + Z^T Q; into the outputs
+  const bool grouped = H != Hk;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + 8 * j;
+    if (t < NQK) {
+      const int mat = t / (2 * NT16), rem = t % (2 * NT16), mt = rem / NT16, nt = rem % NT16;
+      f32x4 a = aqk[j];
+      if (mat == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] *= tv.egm[16 * mt + 4 * lg + e];
+#pragma unroll
+        for (int ks = 0; ks < kC / 4; ++ks) a = mma4(dPm[16 * mt + li][4 * ks + lg], kh[4 * ks + lg][16 * nt + li], a);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kC / 4; ++ks) {
+          a = mma4(dGs[16 * mt + li][4 * ks + lg], kh[4 * ks + lg][16 * nt + li], a);
+          a = mma4(dPm[4 * ks + lg][16 * mt + li], qh[4 * ks + lg][16 * nt + li], a);
+        }
+      }
+      float* out = mat == 0 ? dq : dk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mt + 4 * lg + e;
+        if (r < L) {
+          const long o = ((tok0 + r) * Hk + hk) * DK + 16 * nt + li;
+          if (grouped) atomicAdd(out + o, a[e]);
+          else out[o] = a[e];
+        }
+      }
+    }
+  }
   // dg_t = sum_{r >= t} dgam_r + sum_{r > t} dgx_r + dgC
   if (tid < kC) {
     const int t = tid;
     if (t < L) {
-      float dgc = sdc, sg = 0.f;
+      float dgc = 0.f, sg = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < 8; ++wv) dgc += red[wv];
+      dgc *= tv.egC;
       for (int r = 0; r < kC; ++r) {
-        dgc += ggc[r];
-        if (r >= t) sg += ggm[r];
-        if (r > t) sg += ggx[r];
+        dgc += tc[r];
+        if (r >= t) sg += tm[r];
+        if (r > t) sg += tx[r];
       }
       const long ti = (tok0 + t) * H + h;
-      dbeta[ti] = gb[t];
+      dbeta[ti] = tb[t];
       if (ddecay) ddecay[ti] = sg + dgc;
     }
   }

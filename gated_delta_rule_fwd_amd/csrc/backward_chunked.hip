@@ -75,6 +75,21 @@ size_t ws_floats(int B, int T, int H, int DK, int DV, CWs* w, float* base) {
   return 5 * tok + 2 * mats + 2 * st;
 }
 
+// Workgroup barrier ordering LDS accesses only: global loads in flight (the
+// next chunk's or slice's operands) are not waited for, as __syncthreads
+// would.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// acc += A (16 x 4) B (4 x 16), fp32: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16]; it holds rows 4 (l / 16) + j, j = 0..3, of column l % 16.
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
 // (0) per (b, h, chunk): the norm factors of the rows, beta and the
 // cumulative decays per token; T and P of the chunk.
 template <int DK, typename In>
@@ -82,7 +97,8 @@ __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, cons
                                                   const In* __restrict__ beta, const In* __restrict__ decay,
                                                   int headd, CWs w, int T, int H, int Hk, int N, float scale,
                                                   int l2norm, Transforms tf) {
-  __shared__ float kh[kC][DK + 1], qh[kC][DK + 1];
+  constexpr int KP = DK + 4;
+  __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
   __shared__ float sA[kC][kC + 1];
   __shared__ float sbt[kC], sgm[kC], sgx[kC];
   const int tid = threadIdx.x;
@@ -90,30 +106,38 @@ __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, cons
   const int t0 = ci * kC, L = min(kC, T - t0);
   const long tok0 = static_cast<long>(b) * T + t0;
   {
-    // eight lanes to a row
-    constexpr int SEG = DK / 8;
-    const int r = tid / 8, sg = tid % 8;
-    const bool in = r < L;
-    const long base = ((tok0 + r) * Hk + hk) * DK + sg * SEG;
-    float qv[SEG], kv[SEG], sq = 0.f, sk = 0.f;
+    // LPR lanes to a row, one 16-byte load of q and of k each
+    constexpr int V = act<In>::kVec, LPR = DK / V;
+    static_assert(kC * LPR % 64 == 0, "whole waves per pass");
+    for (int idx = tid; idx < kC * LPR; idx += kThr) {
+      const int r = idx / LPR, seg = idx % LPR;
+      const bool in = r < L;
+      float qv[V], kv[V], sq = 0.f, sk = 0.f;
+      if (in) {
+        const long base = ((tok0 + r) * Hk + hk) * DK + seg * V;
+        act<In>::load_vec(q + base, qv);
+        act<In>::load_vec(k + base, kv);
+      } else {
 #pragma unroll
-    for (int e = 0; e < SEG; ++e) {
-      qv[e] = in ? act<In>::load1(q + base + e) : 0.f;
-      kv[e] = in ? act<In>::load1(k + base + e) : 0.f;
-      sq += qv[e] * qv[e];
-      sk += kv[e] * kv[e];
-    }
-    sq = dpp_group_sum<8>(sq);
-    sk = dpp_group_sum<8>(sk);
-    const float fq = (l2norm ? inv_norm(sq) : 1.f) * scale, fk = l2norm ? inv_norm(sk) : 1.f;
+        for (int e = 0; e < V; ++e) qv[e] = kv[e] = 0.f;
+      }
 #pragma unroll
-    for (int e = 0; e < SEG; ++e) {
-      qh[r][sg * SEG + e] = qv[e] * fq;
-      kh[r][sg * SEG + e] = kv[e] * fk;
-    }
-    if (sg == 0 && in) {
-      w.sq[(tok0 + r) * H + h] = fq;
-      w.sk[(tok0 + r) * H + h] = fk;
+      for (int e = 0; e < V; ++e) {
+        sq += qv[e] * qv[e];
+        sk += kv[e] * kv[e];
+      }
+      sq = dpp_group_sum<LPR>(sq);
+      sk = dpp_group_sum<LPR>(sk);
+      const float fq = (l2norm ? inv_norm(sq) : 1.f) * scale, fk = l2norm ? inv_norm(sk) : 1.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        qh[r][seg * V + e] = qv[e] * fq;
+        kh[r][seg * V + e] = kv[e] * fk;
+      }
+      if (seg == 0 && in) {
+        w.sq[(tok0 + r) * H + h] = fq;
+        w.sk[(tok0 + r) * H + h] = fk;
+      }
     }
   }
   if (tid < kC) {
@@ -144,20 +168,35 @@ __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, cons
       w.gx[ti] = gx;
     }
   }
-  __syncthreads();
+  lds_sync();
   const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
-  for (int idx = tid; idx < kC * kC; idx += kThr) {
-    const int r = idx / kC, s = idx % kC;
-    float gkk = 0.f, gqk = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < DK; ++c) {
-      gkk += kh[r][c] * kh[s][c];
-      gqk += qh[r][c] * kh[s][c];
+  {
+    // K K^T and Q K^T on MFMA, a 16 x 16 tile of each per wave (the upper
+    // tile is zero); a 16-byte row read feeds four products, k = 4 (l / 16) + e
+    const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int rt = wave >> 1, ct = wave & 1;
+    f32x4 g = {0.f, 0.f, 0.f, 0.f}, p = g;
+    if (ct <= rt) {
+#pragma unroll 4
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * kb + 4 * lg]);
+        const f32x4 aq = *reinterpret_cast<const f32x4*>(&qh[16 * rt + li][16 * kb + 4 * lg]);
+        const f32x4 bk = *reinterpret_cast<const f32x4*>(&kh[16 * ct + li][16 * kb + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g = mma4(ak[e], bk[e], g);
+          p = mma4(aq[e], bk[e], p);
+        }
+      }
     }
-    sA[r][s] = s < r ? sbt[r] * gkk * __expf(sgx[r] - sgm[s]) : 0.f;
-    w.Pm[cb + idx] = s <= r ? gqk * __expf(sgm[r] - sgm[s]) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * lg + e, s = 16 * ct + li;
+      sA[r][s] = s < r ? sbt[r] * g[e] * __expf(sgx[r] - sgm[s]) : 0.f;
+      w.Pm[cb + r * kC + s] = s <= r ? p[e] * __expf(sgm[r] - sgm[s]) : 0.f;
+    }
   }
-  __syncthreads();
+  lds_sync();
   if (tid < kC) {
     // column j of T = (I + A)^-1 by forward substitution
     const int j = tid;
@@ -180,63 +219,151 @@ struct TokVec {
   float bt[kC], egx[kC], egm[kC], F[kC];
   float egC;
 };
-__device__ __forceinline__ void load_tokvec(TokVec& tv, const CWs& w, long tok0, int H, int h, int L, int tid) {
-  if (tid < kC) {
-    const int r = tid;
-    const bool in = r < L;
-    const long t = (tok0 + r) * H + h;
-    const float gC = w.gm[(tok0 + L - 1) * H + h];
-    tv.bt[r] = in ? w.bt[t] : 0.f;
-    tv.egx[r] = in ? __expf(w.gx[t]) : 0.f;
-    tv.egm[r] = in ? __expf(w.gm[t]) : 0.f;
-    tv.F[r] = in ? __expf(gC - w.gm[t]) : 0.f;
-    if (r == 0) tv.egC = __expf(gC);
+// One chunk's token values, loaded ahead (lanes 0..31 of wave 0 use them).
+// Loads here and below are unconditional, from clamped in-range addresses,
+// and the values are masked when stored: nothing waits on a load before its
+// values are stored to LDS.
+struct TokPf {
+  float bt, gx, gm, gC;
+  __device__ void load(const CWs& w, long tok0, int H, int h, int L, int tid) {
+    const long t = (tok0 + min(tid & (kC - 1), L - 1)) * H + h;
+    bt = w.bt[t];
+    gx = w.gx[t];
+    gm = w.gm[t];
+    gC = w.gm[(tok0 + L - 1) * H + h];
   }
-}
-
-// The normalised rows of a chunk (raw rows times their norm factor) into
-// LDS rows of pitch KP; rows past the sequence's end are zero.
-template <int DK, int KP, typename In>
-__device__ __forceinline__ void stage_rows(float (*dst)[KP], const In* src, const float* fac, long tok0, int H,
-                                           int h, int Hk, int hk, int L, int tid, int nthr) {
-  constexpr int V = act<In>::kVec, LPR = DK / V;
-  for (int idx = tid; idx < kC * LPR; idx += nthr) {
-    const int r = idx / LPR, seg = idx % LPR;
-    float x[V];
-    if (r < L) {
-      act<In>::load_vec(src + ((tok0 + r) * Hk + hk) * DK + seg * V, x);
-      const float f = fac[(tok0 + r) * H + h];
-#pragma unroll
-      for (int e = 0; e < V; ++e) x[e] *= f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) x[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < V; ++e) dst[r][seg * V + e] = x[e];
-  }
-}
-
-// T (and with Pd, P) of a chunk into LDS, one 16-byte load per thread and pass
-__device__ __forceinline__ void stage_mats(float (*Td)[kC + 1], float (*Pd)[kC + 1], const CWs& w, size_t cb,
-                                           int tid, int nthr) {
-  for (int idx = tid; idx < kC * kC / 4; idx += nthr) {
-    const int r = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
-    const f32x4 t = *reinterpret_cast<const f32x4*>(w.Tm + cb + r * kC + c4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Td[r][c4 + e] = t[e];
-    if (Pd) {
-      const f32x4 p = *reinterpret_cast<const f32x4*>(w.Pm + cb + r * kC + c4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Pd[r][c4 + e] = p[e];
+  __device__ void store(TokVec& tv, int L, int tid) const {
+    if (tid < kC) {
+      const bool in = tid < L;
+      tv.bt[tid] = in ? bt : 0.f;
+      tv.egx[tid] = in ? __expf(gx) : 0.f;
+      tv.egm[tid] = in ? __expf(gm) : 0.f;
+      tv.F[tid] = in ? __expf(gC - gm) : 0.f;
+      if (tid == 0) tv.egC = __expf(gC);
     }
   }
-}
+};
 
-// acc += A (16 x 4) B (4 x 16), fp32: lane l gives A[l % 16][l / 16] and
-// B[l / 16][l % 16]; it holds rows 4 (l / 16) + j, j = 0..3, of column l % 16.
-__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+// Raw 16-byte vectors and single elements of the input type, converted to
+// fp32 only when used
+template <typename In> struct Raw;
+template <> struct Raw<float> {
+  using vec = f32x4;
+  using one = float;
+  static constexpr int V = 4;
+  __device__ static void cvt(const vec& r, float (&o)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = r[e];
+  }
+  __device__ static one ld1(const float* p) { return *p; }
+  __device__ static float cvt1(one x) { return x; }
+};
+template <> struct Raw<bf16_t> {
+  using vec = uint4;
+  using one = uint16_t;
+  static constexpr int V = 8;
+  __device__ static void cvt(const vec& r, float (&o)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static one ld1(const bf16_t* p) { return p->bits; }
+  __device__ static float cvt1(one x) { return bf16_to_f32(x); }
+};
+
+// The raw rows of a chunk and their norm factors, loaded ahead into
+// registers (NTHR threads, one 16-byte load per pass); store() writes the
+// normalised rows into LDS rows of pitch KP (rows past the end: zeros).
+template <int DK, typename In, int NTHR>
+struct RowPf {
+  static constexpr int V = Raw<In>::V, LPR = DK / V, NPT = (kC * LPR + NTHR - 1) / NTHR;
+  typename Raw<In>::vec x[NPT];
+  float f[NPT];
+  __device__ void load(const In* src, const float* fac, long tok0, int H, int h, int Hk, int hk, int L, int tid) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = min(tid + i * NTHR, kC * LPR - 1), r = min(idx / LPR, L - 1), seg = idx % LPR;
+      x[i] = *reinterpret_cast<const typename Raw<In>::vec*>(src + ((tok0 + r) * Hk + hk) * DK + seg * V);
+      f[i] = fac[(tok0 + r) * H + h];
+    }
+  }
+  template <int KP>
+  __device__ void store(float (*dst)[KP], int L, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * NTHR, r = idx / LPR, seg = idx % LPR;
+      if (idx < kC * LPR) {
+        float v[V];
+        Raw<In>::cvt(x[i], v);
+        const float fr = r < L ? f[i] : 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) dst[r][seg * V + e] = r < L ? v[e] * fr : 0.f;
+      }
+    }
+  }
+};
+
+// LDS pitch of 32 x 32 matrices: rows read as 16-byte vectors
+constexpr int kCP = kC + 4;
+
+// T and P of a chunk, loaded ahead (NTHR threads, 16-byte loads); stored
+// into LDS transposed (T^T, P^T) and, if given, as they are
+template <int NTHR, bool withP>
+struct MatPf {
+  static constexpr int NPT = (kC * kC / 4 + NTHR - 1) / NTHR;
+  f32x4 t[NPT], p[NPT];
+  __device__ void load(const CWs& w, size_t cb, int tid) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = min(tid + i * NTHR, kC * kC / 4 - 1);
+      t[i] = *reinterpret_cast<const f32x4*>(w.Tm + cb + 4 * idx);
+      if (withP) p[i] = *reinterpret_cast<const f32x4*>(w.Pm + cb + 4 * idx);
+    }
+  }
+  __device__ void store(float (*Td)[kCP], float (*TdT)[kCP], float (*PdT)[kCP], int tid) const {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * NTHR, r = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
+      if (idx < kC * kC / 4) {
+        if (Td) *reinterpret_cast<f32x4*>(&Td[r][c4]) = t[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (TdT) TdT[c4 + e][r] = t[i][e];
+          if (withP && PdT) PdT[c4 + e][r] = p[i][e];
+        }
+      }
+    }
+  }
+};
+
+// sum_t row[t] col[t][n] over a chunk's 32 tokens (row 16-byte aligned;
+// zeros where a triangular factor vanishes)
+template <int P>
+__device__ __forceinline__ float row_col(const float* row, const float (*col)[P], int n) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 2
+  for (int t = 0; t < kC; t += 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(row + t);
+    a0 += x[0] * col[t][n];
+    a1 += x[1] * col[t + 1][n];
+    a0 += x[2] * col[t + 2][n];
+    a1 += x[3] * col[t + 3][n];
+  }
+  return a0 + a1;
+}
+// sum_t a[t][m] b[t][n] over 32 (two columns)
+template <int PA, int PB>
+__device__ __forceinline__ float col_col(const float (*a)[PA], int m, const float (*b)[PB], int n) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
+  for (int t = 0; t < kC; t += 2) {
+    a0 += a[t][m] * b[t][n];
+    a1 += a[t + 1][m] * b[t + 1][n];
+  }
+  return a0 + a1;
 }
 
 // (1) per (b, h, slice of kNS value columns): every chunk's S0 into the
@@ -244,14 +371,15 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
 // MFMA accumulators, 16 key rows per tile, tile m in wave m % 4.  Per chunk:
 // K S as partial products of each wave's own tiles (the tile is the B
 // operand as it stands), summed through LDS; Y and D = T Y on VALU; then
-// S <- exp(gC) S + K^T (F . D) on MFMA.
+// S <- exp(gC) S + K^T (F . D) on MFMA.  The next chunk's inputs are loaded
+// into registers while this one is computed.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const In* __restrict__ v,
                                                  const float* __restrict__ init, CWs w, int T, int H, int Hk,
                                                  int N, int vfirst) {
   constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
   __shared__ __align__(16) float kh[kC][KP];
-  __shared__ float Tm[kC][kC + 1];
+  __shared__ __align__(16) float Tm[kC][kCP];
   __shared__ float part[NW][kC][kNS + 1];
   __shared__ float Y[kC][kNS + 1], FD[kC][kNS + 1];
   __shared__ TokVec tv;
@@ -268,16 +396,31 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[j][e] = (mt < MT && init) ? init[sidx(16 * mt + 4 * lg + e, n0 + li)] : 0.f;
   }
-  for (int ci = 0; ci < N; ++ci) {
-    const int t0 = ci * kC, L = min(kC, T - t0);
-    const long tok0 = static_cast<long>(b) * T + t0;
-    float vv[2];
+  RowPf<DK, In, kThr> kpf;
+  MatPf<kThr, false> mpf;
+  TokPf tpf;
+  typename Raw<In>::one vv[2];
+  auto prefetch = [&](int c) __attribute__((always_inline)) {
+    const int L = min(kC, T - c * kC);
+    const long tok0 = static_cast<long>(b) * T + c * kC;
+    kpf.load(k, w.sk, tok0, H, h, Hk, hk, L, tid);
+    mpf.load(w, (static_cast<size_t>(bh) * N + c) * kC * kC, tid);
+    tpf.load(w, tok0, H, h, L, tid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
-      vv[u] = r < L ? act<In>::load1(v + ((tok0 + r) * H + h) * DV + n0 + n) : 0.f;
+      const int idx = tid + u * kThr, r = min(idx / kNS, L - 1), n = idx % kNS;
+      vv[u] = Raw<In>::ld1(v + ((tok0 + r) * H + h) * DV + n0 + n);
     }
-    __syncthreads();
+  };
+  prefetch(0);
+  for (int ci = 0; ci < N; ++ci) {
+    const int L = min(kC, T - ci * kC);
+    lds_sync();
+    kpf.store(kh, L, tid);
+    mpf.store(Tm, nullptr, nullptr, tid);
+    tpf.store(tv, L, tid);
+    const float v0 = (tid / kNS) < L ? Raw<In>::cvt1(vv[0]) : 0.f;
+    const float v1 = (tid + kThr) / kNS < L ? Raw<In>::cvt1(vv[1]) : 0.f;
     float* s0 = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -287,10 +430,8 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
         for (int e = 0; e < 4; ++e) s0[(16 * mt + 4 * lg + e) * DV + n0 + li] = acc[j][e];
       }
     }
-    stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr);
-    stage_mats(Tm, nullptr, w, (static_cast<size_t>(bh) * N + ci) * kC * kC, tid, kThr);
-    load_tokvec(tv, w, tok0, H, h, L, tid);
-    __syncthreads();
+    lds_sync();
+    if (ci + 1 < N) prefetch(ci + 1);
     // K S over this wave's key rows: rows 16 rt + l % 16 of K, keys 16 mt + 4 (l / 16) + e
     if (wave < NW) {
 #pragma unroll
@@ -309,7 +450,7 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
         for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][li] = p[e];
       }
     }
-    __syncthreads();
+    lds_sync();
     // Y = beta . (V - exp(gx) . K S)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -317,18 +458,16 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
       float ks = 0.f;
 #pragma unroll
       for (int q = 0; q < NW; ++q) ks += part[q][r][n];
-      Y[r][n] = tv.bt[r] * (vv[u] - tv.egx[r] * ks);
+      Y[r][n] = tv.bt[r] * ((u ? v1 : v0) - tv.egx[r] * ks);
     }
-    __syncthreads();
+    lds_sync();
     // F . D, D = T Y (T unit lower triangular)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
-      float d = 0.f;
-      for (int s = 0; s <= r; ++s) d += Tm[r][s] * Y[s][n];
-      FD[r][n] = tv.F[r] * d;
+      FD[r][n] = tv.F[r] * row_col(Tm[r], Y, n);
     }
-    __syncthreads();
+    lds_sync();
     // S <- exp(gC) S + K^T (F . D)
     const float egC = tv.egC;
 #pragma unroll
@@ -348,7 +487,8 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
 // state's gradient.  The slice of dS sits in MFMA accumulators as S does in
 // (1); per chunk: K dS (partial products per wave, summed through LDS),
 // dD = P^T dO + F . K dS and dY = T^T dD on VALU, then
-// dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.
+// dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.  The
+// next chunk's inputs are loaded into registers while this one is computed.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const In* __restrict__ k,
                                                  const float* __restrict__ dout, const float* __restrict__ dfinal,
@@ -356,7 +496,7 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
                                                  int H, int Hk, int N, int vfirst) {
   constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
   __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
-  __shared__ float Tm[kC][kC + 1], Pm[kC][kC + 1];
+  __shared__ __align__(16) float TmT[kC][kCP], PmT[kC][kCP];
   __shared__ float part[NW][kC][kNS + 1];
   __shared__ float dO[kC][kNS + 1], dD[kC][kNS + 1], BB[2 * kC][kNS + 1];
   __shared__ TokVec tv;
@@ -373,16 +513,37 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[j][e] = (mt < MT && dfinal) ? dfinal[sidx(16 * mt + 4 * lg + e, n0 + li)] : 0.f;
   }
+  RowPf<DK, In, kThr> kpf, qpf;
+  MatPf<kThr, true> mpf;
+  TokPf tpf;
+  float dov[2];
+  auto prefetch = [&](int c) __attribute__((always_inline)) {
+    const int L = min(kC, T - c * kC);
+    const long tok0 = static_cast<long>(b) * T + c * kC;
+    kpf.load(k, w.sk, tok0, H, h, Hk, hk, L, tid);
+    qpf.load(q, w.sq, tok0, H, h, Hk, hk, L, tid);
+    mpf.load(w, (static_cast<size_t>(bh) * N + c) * kC * kC, tid);
+    tpf.load(w, tok0, H, h, L, tid);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThr, r = min(idx / kNS, L - 1), n = idx % kNS;
+      dov[u] = dout[((tok0 + r) * H + h) * DV + n0 + n];
+    }
+  };
+  prefetch(N - 1);
   for (int ci = N - 1; ci >= 0; --ci) {
     const int t0 = ci * kC, L = min(kC, T - t0);
     const long tok0 = static_cast<long>(b) * T + t0;
-    float dov[2];
+    lds_sync();
+    kpf.store(kh, L, tid);
+    qpf.store(qh, L, tid);
+    mpf.store(nullptr, TmT, PmT, tid);
+    tpf.store(tv, L, tid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
-      dov[u] = r < L ? dout[((tok0 + r) * H + h) * DV + n0 + n] : 0.f;
+      const int idx = tid + u * kThr;
+      dO[idx / kNS][idx % kNS] = idx / kNS < L ? dov[u] : 0.f;
     }
-    __syncthreads();
     float* d1 = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -392,16 +553,8 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
         for (int e = 0; e < 4; ++e) d1[(16 * mt + 4 * lg + e) * DV + n0 + li] = acc[j][e];
       }
     }
-    stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr);
-    stage_rows<DK, KP, In>(qh, q, w.sq, tok0, H, h, Hk, hk, L, tid, kThr);
-    stage_mats(Tm, Pm, w, (static_cast<size_t>(bh) * N + ci) * kC * kC, tid, kThr);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr;
-      dO[idx / kNS][idx % kNS] = dov[u];
-    }
-    load_tokvec(tv, w, tok0, H, h, L, tid);
-    __syncthreads();
+    lds_sync();
+    if (ci > 0) prefetch(ci - 1);
     // K dS over this wave's key rows
     if (wave < NW) {
 #pragma unroll
@@ -420,7 +573,7 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
         for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][li] = p[e];
       }
     }
-    __syncthreads();
+    lds_sync();
     // dD = P^T dO + F . K dS
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -428,23 +581,19 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
       float kd = 0.f;
 #pragma unroll
       for (int qq = 0; qq < NW; ++qq) kd += part[qq][r][n];
-      float pd = 0.f;
-      for (int s = r; s < kC; ++s) pd += Pm[s][r] * dO[s][n];
-      dD[r][n] = pd + tv.F[r] * kd;
+      dD[r][n] = row_col(PmT[r], dO, n) + tv.F[r] * kd;
     }
-    __syncthreads();
+    lds_sync();
     // dX = beta . T^T dD, the gradient of v; the B operand of the dS update
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
-      float y = 0.f;
-      for (int s = r; s < kC; ++s) y += Tm[s][r] * dD[s][n];
-      const float x = tv.bt[r] * y;
+      const float x = tv.bt[r] * row_col(TmT[r], dD, n);
       if (r < L) dv[((tok0 + r) * H + h) * DV + n0 + n] = x;
       BB[r][n] = tv.egm[r] * dO[r][n];
       BB[kC + r][n] = -tv.egx[r] * x;
     }
-    __syncthreads();
+    lds_sync();
     // dS <- exp(gC) dS + Q^T (exp(gam) . dO) - K^T (exp(gx) . dX)
     const float egC = tv.egC;
 #pragma unroll
@@ -472,37 +621,53 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
   }
 }
 
+// LDS of the per-chunk gradient kernel: the value-slice arrays and the last
+// phase's matrices share their space.
+template <int DK>
+struct LocalLds {
+  float kh[kC][DK + 4], qh[kC][DK + 4];
+  float TmT[kC][kCP], PmT[kC][kCP];
+  union {
+    struct {
+      float S0s[DK][kNS + 1], S1s[DK][kNS + 1];
+      float KS[kC][kNS + 1], QS[kC][kNS + 1], KD[kC][kNS + 1];
+      float dO[kC][kNS + 1], Yb[kC][kNS + 1], D[kC][kNS + 1], FD[kC][kNS + 1], dD[kC][kNS + 1];
+      float dYs[kC][kNS + 1];
+    } s;
+    struct {
+      float dTm[kC][kCP], M[kC][kCP];
+      float dPm[kC][kC + 1], EE[kC][kC + 1], PP[kC][kC + 1], Gp[2][kC][kC + 1], dGs[kC][kC + 1];
+    } f;
+  } u;
+  float tb[kC], tm[kC], tx[kC], tc[kC], sgm[kC], sgx[kC], red[8];
+  TokVec tv;
+};
+
 // (3) per (b, h, chunk): the remaining gradients over the value columns, 16
 // at a time: dq and dk of the normalised rows (added: value heads of a group
 // share their q/k head), dbeta and the decay's gradient (written).  Eight
-// waves.  Per slice: [K S0 | Q S0 | K dS1] on MFMA (each wave a quarter of
-// the keys of one row tile, summed through LDS); X, D, dD, dY and the
+// waves, two workgroups per CU.  Per slice: K S0, Q S0 and K dS1 on MFMA
+// (one product's row tile per wave, waves 0-5); X, D, dD, dY and the
 // per-token sums on VALU, one (row, column) element per thread; then on
 // MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
 // dq += dO S0^T, dk += (F . D) dS1^T - (exp(gx) beta . dY) S0^T (tiles per
 // wave, held across the slices).  Then dA, dG and Z on VALU and the last
 // products dq += Z K, dk += (dG + dG^T) K + Z^T Q on MFMA.
 template <int DK, int DV, typename In>
-__global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, const In* __restrict__ k,
-                                                    const In* __restrict__ v, const float* __restrict__ dout,
-                                                    float* __restrict__ dq, float* __restrict__ dk,
-                                                    float* __restrict__ dbeta, float* __restrict__ ddecay,
-                                                    CWs w, int T, int H, int Hk, int N) {
-  constexpr int KP = DK + 4, NT16 = DK / 16, KQ = DK / 16;       // k-steps per quarter of the keys
+__global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q, const In* __restrict__ k,
+                                                       const In* __restrict__ v, const float* __restrict__ dout,
+                                                       float* __restrict__ dq, float* __restrict__ dk,
+                                                       float* __restrict__ dbeta, float* __restrict__ ddecay,
+                                                       CWs w, int T, int H, int Hk, int N) {
+  constexpr int NT16 = DK / 16;
   constexpr int NQK = 4 * NT16, TPW = (NQK + 7) / 8;              // dq/dk tiles, per wave
   constexpr int SPT = DK * kNS / kThr3;                          // state floats per thread per slice
   constexpr int SL = kNS / SPT;                                   // threads per state row
   constexpr int nsl = DV / kNS;
-  __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
-  __shared__ float S0s[DK][kNS + 1], S1s[DK][kNS + 1];
-  __shared__ float part[4][3][kC][kNS + 1];
-  __shared__ float Tm[kC][kC + 1], Pm[kC][kC + 1];
-  __shared__ float dO[kC][kNS + 1], Yb[kC][kNS + 1], D[kC][kNS + 1], FD[kC][kNS + 1];
-  __shared__ float dD[kC][kNS + 1], dYs[kC][kNS + 1];
-  __shared__ float dTm[kC][kC + 1], dPm[kC][kC + 1], M[kC][kC + 1], EE[kC][kC + 1], PP[kC][kC + 1];
-  __shared__ float Gp[2][kC][kC + 1], dGs[kC][kC + 1];
-  __shared__ float tb[kC], tm[kC], tx[kC], tc[kC], sgm[kC], sgx[kC], red[8];
-  __shared__ TokVec tv;
+  __shared__ __align__(16) LocalLds<DK> sm;
+  auto& S = sm.u.s;
+  auto& Fm = sm.u.f;
+  TokVec& tv = sm.tv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
   const int er = tid / kNS, en = tid % kNS;   // this thread's element of a 32 x 16 slice tile
   const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);
@@ -512,27 +677,37 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
   const float* s0g = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
   const float* s1g = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
   const bool rin = er < L;
-  const long vrow = ((tok0 + er) * H + h) * DV;
   const int sc = tid / SL, sn = (tid % SL) * SPT;   // this thread's state elements: row sc, columns sn..
-  float ps0[SPT], ps1[SPT], pdo, pv;
-  auto prefetch = [&](int s) {
+  const long vrowc = ((tok0 + min(er, L - 1)) * H + h) * DV;   // clamped: loads stay in range
+  float ps0[SPT], ps1[SPT], pdo;
+  typename Raw<In>::one pv;
+  auto prefetch = [&](int s) __attribute__((always_inline)) {
     const int nb = s * kNS;
 #pragma unroll
     for (int e = 0; e < SPT; ++e) {
       ps0[e] = s0g[sc * DV + nb + sn + e];
       ps1[e] = s1g[sc * DV + nb + sn + e];
     }
-    pdo = rin ? dout[vrow + nb + en] : 0.f;
-    pv = rin ? act<In>::load1(v + vrow + nb + en) : 0.f;
+    pdo = dout[vrowc + nb + en];
+    pv = Raw<In>::ld1(v + vrowc + nb + en);
   };
   prefetch(0);
-  stage_rows<DK, KP, In>(kh, k, w.sk, tok0, H, h, Hk, hk, L, tid, kThr3);
-  stage_rows<DK, KP, In>(qh, q, w.sq, tok0, H, h, Hk, hk, L, tid, kThr3);
-  stage_mats(Tm, Pm, w, cb, tid, kThr3);
-  load_tokvec(tv, w, tok0, H, h, L, tid);
-  if (tid < kC) {
-    sgm[tid] = tid < L ? w.gm[(tok0 + tid) * H + h] : 0.f;
-    sgx[tid] = tid < L ? w.gx[(tok0 + tid) * H + h] : 0.f;
+  {
+    RowPf<DK, In, kThr3> kpf, qpf;
+    MatPf<kThr3, true> mpf;
+    TokPf tpf;
+    kpf.load(k, w.sk, tok0, H, h, Hk, hk, L, tid);
+    qpf.load(q, w.sq, tok0, H, h, Hk, hk, L, tid);
+    mpf.load(w, cb, tid);
+    tpf.load(w, tok0, H, h, L, tid);
+    kpf.store(sm.kh, L, tid);
+    qpf.store(sm.qh, L, tid);
+    mpf.store(nullptr, sm.TmT, sm.PmT, tid);
+    tpf.store(tv, L, tid);
+    if (tid < kC) {
+      sm.sgm[tid] = tid < L ? tpf.gm : 0.f;
+      sm.sgx[tid] = tid < L ? tpf.gx : 0.f;
+    }
   }
   float sb = 0.f, so = 0.f, sx = 0.f, sf = 0.f, sdc = 0.f;   // per-token sums (this thread's columns)
   f32x4 atp = {0.f, 0.f, 0.f, 0.f};                          // dT (waves 0-3) or dP (4-7) tile
@@ -540,71 +715,57 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
 #pragma unroll
   for (int j = 0; j < TPW; ++j) aqk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int tpm = wave >> 2, tpr = (wave >> 1) & 1, tpc = wave & 1;
-  const int pmt = wave & 1, pq = wave >> 1;                  // K-S product: row tile, key quarter
+  const int prod = wave >> 1, prt = wave & 1;                // K-S products: which, row tile
   for (int s = 0; s < nsl; ++s) {
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int e = 0; e < SPT; ++e) {
-      S0s[sc][sn + e] = ps0[e];
-      S1s[sc][sn + e] = ps1[e];
+      S.S0s[sc][sn + e] = ps0[e];
+      S.S1s[sc][sn + e] = ps1[e];
       sdc += ps0[e] * ps1[e];
     }
-    dO[er][en] = pdo;
-    const float vcur = pv, docur = pdo;
-    __syncthreads();
+    const float vcur = rin ? Raw<In>::cvt1(pv) : 0.f, docur = rin ? pdo : 0.f;
+    S.dO[er][en] = docur;
+    lds_sync();
     if (s + 1 < nsl) prefetch(s + 1);
-    // [K S0 | Q S0 | K dS1], this wave's row tile and key quarter
-    {
-      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0;
+    // K S0 (waves 0, 1), Q S0 (2, 3), K dS1 (4, 5): one row tile over all keys
+    if (prod < 3) {
+      const float(*A)[DK + 4] = prod == 1 ? sm.qh : sm.kh;
+      const float(*Bm)[kNS + 1] = prod == 2 ? S.S1s : S.S0s;
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&A[16 * prt + li][16 * kb + 4 * lg]);
 #pragma unroll
-      for (int ks = pq * KQ; ks < (pq + 1) * KQ; ++ks) {
-        const float ak = kh[16 * pmt + li][4 * ks + lg], aq = qh[16 * pmt + li][4 * ks + lg];
-        const float b0 = S0s[4 * ks + lg][li], b1 = S1s[4 * ks + lg][li];
-        p0 = mma4(ak, b0, p0);
-        p1 = mma4(aq, b0, p1);
-        p2 = mma4(ak, b1, p2);
+        for (int e = 0; e < 4; ++e) p = mma4(a[e], Bm[16 * kb + 4 * lg + e][li], p);
       }
+      float(*O)[kNS + 1] = prod == 0 ? S.KS : (prod == 1 ? S.QS : S.KD);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part[pq][0][16 * pmt + 4 * lg + e][li] = p0[e];
-        part[pq][1][16 * pmt + 4 * lg + e][li] = p1[e];
-        part[pq][2][16 * pmt + 4 * lg + e][li] = p2[e];
-      }
+      for (int e = 0; e < 4; ++e) O[16 * prt + 4 * lg + e][li] = p[e];
     }
-    __syncthreads();
-    float ksv = 0.f, qsv = 0.f, kdv = 0.f;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      ksv += part[qq][0][er][en];
-      qsv += part[qq][1][er][en];
-      kdv += part[qq][2][er][en];
-    }
+    lds_sync();
+    // X = V - exp(gx) . K S0, Y = beta . X;  dD = P^T dO + F . K dS1
+    const float ksv = S.KS[er][en], qsv = S.QS[er][en], kdv = S.KD[er][en];
     const float x = vcur - tv.egx[er] * ksv;
-    Yb[er][en] = tv.bt[er] * x;
-    __syncthreads();
-    // D = T Y;  dD = P^T dO + F . K dS1
-    float d = 0.f, pd = 0.f;
-    for (int t = 0; t <= er; ++t) d += Tm[er][t] * Yb[t][en];
-    for (int t = er; t < kC; ++t) pd += Pm[t][er] * dO[t][en];
-    const float dd = pd + tv.F[er] * kdv;
-    D[er][en] = d;
-    FD[er][en] = tv.F[er] * d;
-    dD[er][en] = dd;
-    __syncthreads();
-    // dY = T^T dD, and the per-token sums
-    float y = 0.f;
-    for (int t = er; t < kC; ++t) y += Tm[t][er] * dD[t][en];
-    dYs[er][en] = -tv.egx[er] * tv.bt[er] * y;
+    S.Yb[er][en] = tv.bt[er] * x;
+    S.dD[er][en] = row_col(sm.PmT[er], S.dO, en) + tv.F[er] * kdv;
+    lds_sync();
+    // D = T Y;  dY = T^T dD; the per-token sums
+    const float d = col_col(sm.TmT, er, S.Yb, en);
+    const float y = row_col(sm.TmT[er], S.dD, en);
+    S.D[er][en] = d;
+    S.FD[er][en] = tv.F[er] * d;
+    S.dYs[er][en] = -tv.egx[er] * tv.bt[er] * y;
     sb += y * x;
     so += docur * qsv;
     sx += y * (vcur - x);
     sf += kdv * d;
-    __syncthreads();
+    lds_sync();
     // dT += dD Y^T, dP += dO D^T (this wave's tile)
 #pragma unroll
     for (int ks = 0; ks < kNS / 4; ++ks) {
-      const float a = tpm ? dO[16 * tpr + li][4 * ks + lg] : dD[16 * tpr + li][4 * ks + lg];
-      const float bb = tpm ? D[16 * tpc + li][4 * ks + lg] : Yb[16 * tpc + li][4 * ks + lg];
+      const float a = tpm ? S.dO[16 * tpr + li][4 * ks + lg] : S.dD[16 * tpr + li][4 * ks + lg];
+      const float bb = tpm ? S.D[16 * tpc + li][4 * ks + lg] : S.Yb[16 * tpc + li][4 * ks + lg];
       atp = mma4(a, bb, atp);
     }
     // dq += dO S0^T;  dk += (F . D) dS1^T + (-exp(gx) beta . dY) S0^T
@@ -617,10 +778,10 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
         for (int ks = 0; ks < kNS / 4; ++ks) {
           const int r = 16 * mt + li, n = 4 * ks + lg, c = 16 * nt + li;
           if (mat == 0) {
-            aqk[j] = mma4(dO[r][n], S0s[c][n], aqk[j]);
+            aqk[j] = mma4(S.dO[r][n], S.S0s[c][n], aqk[j]);
           } else {
-            aqk[j] = mma4(FD[r][n], S1s[c][n], aqk[j]);
-            aqk[j] = mma4(dYs[r][n], S0s[c][n], aqk[j]);
+            aqk[j] = mma4(S.FD[r][n], S.S1s[c][n], aqk[j]);
+            aqk[j] = mma4(S.dYs[r][n], S.S0s[c][n], aqk[j]);
           }
         }
       }
@@ -632,39 +793,41 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
   sx = dpp_group_sum<16>(sx);
   sf = dpp_group_sum<16>(sf);
   sdc = dpp_group_sum<64>(sdc);
-  __syncthreads();
+  lds_sync();   // the slice arrays are dead from here: the last phase's matrices take their space
   if (en == 0) {
-    tb[er] = sb;
-    tm[er] = tv.egm[er] * so - tv.F[er] * sf;
-    tx[er] = -tv.bt[er] * sx;
-    tc[er] = tv.F[er] * sf;
+    sm.tb[er] = sb;
+    sm.tm[er] = tv.egm[er] * so - tv.F[er] * sf;
+    sm.tx[er] = -tv.bt[er] * sx;
+    sm.tc[er] = tv.F[er] * sf;
   }
-  if (lane == 0) red[wave] = sdc;
+  if (lane == 0) sm.red[wave] = sdc;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 16 * tpr + 4 * lg + e, c = 16 * tpc + li;
-    if (tpm) dPm[r][c] = atp[e];
-    else dTm[r][c] = c <= r ? atp[e] : 0.f;
+    if (tpm) Fm.dPm[r][c] = atp[e];
+    else Fm.dTm[r][c] = c <= r ? atp[e] : 0.f;
   }
-  __syncthreads();
-  // M = dT T^T (dT, T lower): M_rs = sum_{u <= min(r, s)} dT_ru T_su; K K^T on MFMA
+  lds_sync();
+  // M = dT T^T (dT, T lower: zeros above the diagonal); K K^T on MFMA
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC, um = min(r, c);
-    float m = 0.f;
-    for (int t = 0; t <= um; ++t) m += dTm[r][t] * Tm[c][t];
-    M[r][c] = m;
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
+    Fm.M[r][c] = row_col(Fm.dTm[r], sm.TmT, c);
   }
   {
     const int gt = wave & 3, gr = gt >> 1, gc = gt & 1, gh = wave >> 2;
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kb = gh * (DK / 32); kb < (gh + 1) * (DK / 32); ++kb) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.kh[16 * gr + li][16 * kb + 4 * lg]);
+      const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.kh[16 * gc + li][16 * kb + 4 * lg]);
 #pragma unroll
-    for (int ks = gh * (DK / 8); ks < (gh + 1) * (DK / 8); ++ks)
-      p = mma4(kh[16 * gr + li][4 * ks + lg], kh[16 * gc + li][4 * ks + lg], p);
+      for (int e = 0; e < 4; ++e) p = mma4(a[e], bq[e], p);
+    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Gp[gh][16 * gr + 4 * lg + e][16 * gc + li] = p[e];
+    for (int e = 0; e < 4; ++e) Fm.Gp[gh][16 * gr + 4 * lg + e][16 * gc + li] = p[e];
   }
-  __syncthreads();
+  lds_sync();
   // dA = -T^T M on s < r; E = dA . (K K^T) . W; dG = diag(beta) dA . W;
   // Z = dP . Vw (into dPm) and dP . P
 #pragma unroll
@@ -672,38 +835,38 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
     const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
     float e = 0.f, dg = 0.f;
     if (c < r) {
-      float da = 0.f;
-      for (int t = r; t < kC; ++t) da -= Tm[t][r] * M[t][c];
-      const float wr = __expf(sgx[r] - sgm[c]);
-      e = da * (Gp[0][r][c] + Gp[1][r][c]) * wr;
+      const float da = -row_col(sm.TmT[r], Fm.M, c);
+      const float wr = __expf(sm.sgx[r] - sm.sgm[c]);
+      e = da * (Fm.Gp[0][r][c] + Fm.Gp[1][r][c]) * wr;
       dg = da * tv.bt[r] * wr;
     }
-    EE[r][c] = e;
-    Gp[0][r][c] = dg;   // this thread's own element of Gp, read above: dG in its place
-    const float dp = c <= r ? dPm[r][c] : 0.f;
-    PP[r][c] = dp * Pm[r][c];
-    dPm[r][c] = c <= r ? dp * __expf(sgm[r] - sgm[c]) : 0.f;
+    Fm.EE[r][c] = e;
+    Fm.Gp[0][r][c] = dg;   // this thread's own element of Gp, read above: dG in its place
+    const float dp = c <= r ? Fm.dPm[r][c] : 0.f;
+    Fm.PP[r][c] = dp * sm.PmT[c][r];
+    Fm.dPm[r][c] = c <= r ? dp * __expf(sm.sgm[r] - sm.sgm[c]) : 0.f;
   }
-  __syncthreads();
+  lds_sync();
   if (tid < kC) {
     const int r = tid;
     float re = 0.f, rp = 0.f, ce = 0.f, cp = 0.f;
+#pragma unroll 8
     for (int t = 0; t < kC; ++t) {
-      re += EE[r][t];
-      rp += PP[r][t];
-      ce += tv.bt[t] * EE[t][r];
-      cp += PP[t][r];
+      re += Fm.EE[r][t];
+      rp += Fm.PP[r][t];
+      ce += tv.bt[t] * Fm.EE[t][r];
+      cp += Fm.PP[t][r];
     }
-    tb[r] += re;
-    tx[r] += tv.bt[r] * re;
-    tm[r] += rp - ce - cp;
+    sm.tb[r] += re;
+    sm.tx[r] += tv.bt[r] * re;
+    sm.tm[r] += rp - ce - cp;
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
-    dGs[r][c] = Gp[0][r][c] + Gp[0][c][r];
+    Fm.dGs[r][c] = Fm.Gp[0][r][c] + Fm.Gp[0][c][r];
   }
-  __syncthreads();
+  lds_sync();
   // dq = exp(gam) . (dO S0^T) + Z K;  dk += (dG + dG^T) K + Z^T Q; into the outputs
   const bool grouped = H != Hk;
 #pragma unroll
@@ -716,12 +879,13 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] *= tv.egm[16 * mt + 4 * lg + e];
 #pragma unroll
-        for (int ks = 0; ks < kC / 4; ++ks) a = mma4(dPm[16 * mt + li][4 * ks + lg], kh[4 * ks + lg][16 * nt + li], a);
+        for (int ks = 0; ks < kC / 4; ++ks)
+          a = mma4(Fm.dPm[16 * mt + li][4 * ks + lg], sm.kh[4 * ks + lg][16 * nt + li], a);
       } else {
 #pragma unroll
         for (int ks = 0; ks < kC / 4; ++ks) {
-          a = mma4(dGs[16 * mt + li][4 * ks + lg], kh[4 * ks + lg][16 * nt + li], a);
-          a = mma4(dPm[4 * ks + lg][16 * mt + li], qh[4 * ks + lg][16 * nt + li], a);
+          a = mma4(Fm.dGs[16 * mt + li][4 * ks + lg], sm.kh[4 * ks + lg][16 * nt + li], a);
+          a = mma4(Fm.dPm[4 * ks + lg][16 * mt + li], sm.qh[4 * ks + lg][16 * nt + li], a);
         }
       }
       float* out = mat == 0 ? dq : dk;
@@ -742,15 +906,16 @@ __global__ __launch_bounds__(kThr3) void cbwd_local(const In* __restrict__ q, co
     if (t < L) {
       float dgc = 0.f, sg = 0.f;
 #pragma unroll
-      for (int wv = 0; wv < 8; ++wv) dgc += red[wv];
+      for (int wv = 0; wv < 8; ++wv) dgc += sm.red[wv];
       dgc *= tv.egC;
+#pragma unroll 8
       for (int r = 0; r < kC; ++r) {
-        dgc += tc[r];
-        if (r >= t) sg += tm[r];
-        if (r > t) sg += tx[r];
+        dgc += sm.tc[r];
+        if (r >= t) sg += sm.tm[r];
+        if (r > t) sg += sm.tx[r];
       }
       const long ti = (tok0 + t) * H + h;
-      dbeta[ti] = tb[t];
+      dbeta[ti] = sm.tb[t];
       if (ddecay) ddecay[ti] = sg + dgc;
     }
   }

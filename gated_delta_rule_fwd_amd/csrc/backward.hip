@@ -445,11 +445,17 @@ template <typename In>
 hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const long qk = static_cast<long>(a.B) * a.T * a.Hk * a.DK;
   const long tokh = static_cast<long>(a.B) * a.T * a.H;
-  hipError_t e = zero(a.dq, qk, s);
-  if (e == hipSuccess) e = zero(a.dk, qk, s);
-  if (e == hipSuccess) e = zero(a.dbeta, tokh, s);
-  if (e == hipSuccess && a.decay_kind != DECAY_NONE)
-    e = zero(a.ddecay, a.decay_kind == DECAY_CHANNEL ? tokh * a.DK : tokh, s);
+  // The chunked form writes every element of dbeta and of a per-head
+  // ddecay, and of dq and dk unless value heads share q/k heads (then it
+  // adds); the token-by-token form adds into all of them.
+  const bool chunked = a.decay_kind != DECAY_CHANNEL;
+  hipError_t e = hipSuccess;
+  if (!chunked || a.H != a.Hk) {
+    e = zero(a.dq, qk, s);
+    if (e == hipSuccess) e = zero(a.dk, qk, s);
+  }
+  if (e == hipSuccess && !chunked) e = zero(a.dbeta, tokh, s);
+  if (e == hipSuccess && a.decay_kind == DECAY_CHANNEL) e = zero(a.ddecay, tokh * a.DK, s);
   if (e == hipSuccess && a.tf.A_log) e = zero(a.dA_log, a.H, s);
   if (e == hipSuccess && a.tf.A_log && a.tf.dt_bias)
     e = zero(a.ddt_bias, a.decay_kind == DECAY_CHANNEL ? static_cast<long>(a.H) * a.DK : a.H, s);
@@ -461,7 +467,7 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const In* de = static_cast<const In*>(a.decay);
   const dim3 block(kBwdThreads);
   bool launched = false;
-  if (a.decay_kind != DECAY_CHANNEL) {
+  if (chunked) {
     e = launch_bwd_chunked(a, s);
     if (e != hipSuccess) return e;
     launched = true;

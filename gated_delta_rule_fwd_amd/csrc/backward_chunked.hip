@@ -1,13 +1,14 @@
-// Chunked backward of the gated delta rule for a per-head (scalar) decay or
-// none: the gradients of (o, final state) with respect to q, k, v, beta, the
-// decay and the initial state, the same quantities as the token-by-token
-// backward (backward.hip), computed chunk by chunk in the WY form that the
-// forward uses (TileOPs "Linear Attention Operators": the DeltaNet chunked
-// pipeline and its DeltaNetChunkBwdOp, GLAChunkBwdOp for the decay).
+// Chunked backward of the gated delta rule: the gradients of (o, final state)
+// with respect to q, k, v, beta, the decay and the initial state, computed
+// chunk by chunk in the WY form that the forward uses (TileOPs "Linear
+// Attention Operators": the DeltaNet chunked pipeline and its
+// DeltaNetChunkBwdOp, GLAChunkBwdOp for the decay; kda-neuron-kernels README,
+// kda_chunk_step_exact_bwd).
 //
 // For a chunk of C tokens entering with state S0, with q, k the normalised
 // (q scaled) rows, gam the inclusive and gx the exclusive in-chunk cumulative
-// log decay, gC the chunk's total and F = exp(gC - gam):
+// log decay, gC the chunk's total and F = exp(gC - gam), with a per-head
+// decay (none: all zero):
 //
 //   A = diag(beta) (K K^T . W), W_rs = exp(gx_r - gam_s) on s < r;  T = (I + A)^-1
 //   X = V - exp(gx) . K S0;  Y = diag(beta) X;  D = T Y
@@ -26,14 +27,22 @@
 //   and the decay through gam, gx and gC (each exponential's own factor),
 //   dg_t = sum_{r >= t} dgam_r + sum_{r > t} dgx_r + dgC.
 //
+// With a per-channel decay the same holds with every decay factor taken per
+// key channel c: exp(gx_rc), exp(gam_rc) and exp(gC_c - gam_rc) scale k and q
+// channel by channel, exp(gC_c) scales state row c, and an entry of A or P
+// sums over the channels with its own factor exp(gx_rc - gam_sc) or
+// exp(gam_rc - gam_sc); the gradients of those pair terms, and of the decay,
+// are taken per (token, channel).
+//
 // Four kernels: (0) per chunk, in parallel: the rows' norm factors, beta,
 // the cumulative decays, T and P; (1) per (b, h, kNS value columns): the
 // walk over the chunks storing each chunk's S0; (2) the same slices in
 // reverse: the walk of the state gradient storing each chunk's dS1 and
 // writing dv and the initial state's gradient; (3) per chunk, in parallel:
-// everything else, over the value columns kNS at a time.  The q and k
-// gradients are those of the normalised rows; the norm's backward runs after,
-// as for the token-by-token form.  All arithmetic is fp32.
+// everything else, over the value columns kNS at a time.  (0) and (3) have a
+// per-channel version each; (1) and (2) a per-channel mode.  The q and k
+// gradients are those of the normalised rows; the norm's backward runs after
+// (backward.hip).  All arithmetic is fp32.
 #include "common.h"
 #include "launch.h"
 
@@ -51,6 +60,7 @@ struct CWs {
   float *sq, *sk, *bt, *gm, *gx;   // [B*T*H]: norm factors of q and k, beta, gam, gx
   float *Tm, *Pm;                  // [B*H*N][C][C]
   float *S0, *dS1;                 // [B*H*N][DK][DV]
+  float* gmc;                      // [B*T*H][DK]: gam per key channel (per-channel decay)
 };
 
 size_t align_f(size_t n) { return (n + 63) & ~static_cast<size_t>(63); }
@@ -70,9 +80,10 @@ size_t ws_floats(int B, int T, int H, int DK, int DV, CWs* w, float* base) {
     w->Tm = p; p += mats;
     w->Pm = p; p += mats;
     w->S0 = p; p += st;
-    w->dS1 = p;
+    w->dS1 = p; p += st;
+    w->gmc = p;
   }
-  return 5 * tok + 2 * mats + 2 * st;
+  return 5 * tok + 2 * mats + 2 * st + static_cast<size_t>(B) * T * H * DK;
 }
 
 // Workgroup barrier ordering LDS accesses only: global loads in flight (the
@@ -232,14 +243,42 @@ struct TokPf {
     gm = w.gm[t];
     gC = w.gm[(tok0 + L - 1) * H + h];
   }
+  // CH (per-channel decay): the decay factors are per key channel and
+  // applied elsewhere; the per-token ones are left at one
+  template <bool CH = false>
   __device__ void store(TokVec& tv, int L, int tid) const {
     if (tid < kC) {
       const bool in = tid < L;
       tv.bt[tid] = in ? bt : 0.f;
-      tv.egx[tid] = in ? __expf(gx) : 0.f;
-      tv.egm[tid] = in ? __expf(gm) : 0.f;
-      tv.F[tid] = in ? __expf(gC - gm) : 0.f;
-      if (tid == 0) tv.egC = __expf(gC);
+      tv.egx[tid] = in ? (CH ? 1.f : __expf(gx)) : 0.f;
+      tv.egm[tid] = in ? (CH ? 1.f : __expf(gm)) : 0.f;
+      tv.F[tid] = in ? (CH ? 1.f : __expf(gC - gm)) : 0.f;
+      if (tid == 0) tv.egC = CH ? 1.f : __expf(gC);
+    }
+  }
+};
+
+// One chunk's cumulative decay per key channel (gam, fp32), loaded ahead;
+// stored as rows 1..32 of an LDS array whose row 0 is zero, so that row r
+// holds gx and row r + 1 gam of token r (rows past the end repeat the last
+// token's, which is gC).
+template <int DK, int NTHR>
+struct GamPf {
+  static constexpr int NV = kC * DK / 4, NPT = (NV + NTHR - 1) / NTHR;
+  f32x4 g[NPT];
+  __device__ void load(const float* gmc, long tok0, int H, int h, int L, int tid) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = min(tid + i * NTHR, NV - 1), r = min(idx / (DK / 4), L - 1), c4 = (idx % (DK / 4)) * 4;
+      g[i] = *reinterpret_cast<const f32x4*>(gmc + ((tok0 + r) * H + h) * DK + c4);
+    }
+  }
+  template <int KP>
+  __device__ void store(float (*gs)[KP], int tid) const {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + i * NTHR, r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+      if (idx < NV) *reinterpret_cast<f32x4*>(&gs[r + 1][c4]) = g[i];
     }
   }
 };
@@ -373,12 +412,14 @@ __device__ __forceinline__ float col_col(const float (*a)[PA], int m, const floa
 // operand as it stands), summed through LDS; Y and D = T Y on VALU; then
 // S <- exp(gC) S + K^T (F . D) on MFMA.  The next chunk's inputs are loaded
 // into registers while this one is computed.
-template <int DK, int DV, typename In>
+template <int DK, int DV, typename In, bool CH>
 __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const In* __restrict__ v,
                                                  const float* __restrict__ init, CWs w, int T, int H, int Hk,
                                                  int N, int vfirst) {
   constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
   __shared__ __align__(16) float kh[kC][KP];
+  // per-channel decay: gam per key channel, row r + 1 for token r (row 0: zeros)
+  __shared__ __align__(16) float gs[CH ? kC + 1 : 1][CH ? KP : 4];
   __shared__ __align__(16) float Tm[kC][kCP];
   __shared__ float part[NW][kC][kNS + 1];
   __shared__ float Y[kC][kNS + 1], FD[kC][kNS + 1];
@@ -399,6 +440,9 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
   RowPf<DK, In, kThr> kpf;
   MatPf<kThr, false> mpf;
   TokPf tpf;
+  GamPf<CH ? DK : 4, kThr> gpf;
+  if (CH)
+    for (int c = tid; c < DK; c += kThr) gs[0][c] = 0.f;
   typename Raw<In>::one vv[2];
   auto prefetch = [&](int c) __attribute__((always_inline)) {
     const int L = min(kC, T - c * kC);
@@ -406,6 +450,7 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
     kpf.load(k, w.sk, tok0, H, h, Hk, hk, L, tid);
     mpf.load(w, (static_cast<size_t>(bh) * N + c) * kC * kC, tid);
     tpf.load(w, tok0, H, h, L, tid);
+    if constexpr (CH) gpf.load(w.gmc, tok0, H, h, L, tid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + u * kThr, r = min(idx / kNS, L - 1), n = idx % kNS;
@@ -418,7 +463,8 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
     lds_sync();
     kpf.store(kh, L, tid);
     mpf.store(Tm, nullptr, nullptr, tid);
-    tpf.store(tv, L, tid);
+    tpf.store<CH>(tv, L, tid);
+    if constexpr (CH) gpf.store(gs, tid);
     const float v0 = (tid / kNS) < L ? Raw<In>::cvt1(vv[0]) : 0.f;
     const float v1 = (tid + kThr) / kNS < L ? Raw<In>::cvt1(vv[1]) : 0.f;
     float* s0 = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
@@ -441,7 +487,13 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
         for (int j = 0; j < NT; ++j) {
           const int mt = wave + 4 * j;
           if (mt < MT) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+            f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+            if constexpr (CH) {
+              // k exp(gx) per channel
+              const f32x4 gx = *reinterpret_cast<const f32x4*>(&gs[16 * rt + li][16 * mt + 4 * lg]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[e] *= __expf(gx[e]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) p = mma4(a[e], acc[j][e], p);
           }
@@ -468,15 +520,27 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
       FD[r][n] = tv.F[r] * row_col(Tm[r], Y, n);
     }
     lds_sync();
-    // S <- exp(gC) S + K^T (F . D)
+    // S <- exp(gC) S + K^T (F . D); per channel: exp(gC_c) per state row and
+    // F = exp(gC_c - gam_rc) in the K operand
     const float egC = tv.egC;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int mt = wave + 4 * j;
       if (mt < MT) {
-        acc[j] *= egC;
+        if constexpr (CH) {
 #pragma unroll
-        for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(kh[4 * ks + lg][16 * mt + li], FD[4 * ks + lg][li], acc[j]);
+          for (int e = 0; e < 4; ++e) acc[j][e] *= __expf(gs[L][16 * mt + 4 * lg + e]);
+          const float gC = gs[L][16 * mt + li];
+#pragma unroll
+          for (int ks = 0; ks < kC / 4; ++ks) {
+            const int r = 4 * ks + lg;
+            acc[j] = mma4(kh[r][16 * mt + li] * __expf(gC - gs[r + 1][16 * mt + li]), FD[r][li], acc[j]);
+          }
+        } else {
+          acc[j] *= egC;
+#pragma unroll
+          for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(kh[4 * ks + lg][16 * mt + li], FD[4 * ks + lg][li], acc[j]);
+        }
       }
     }
   }
@@ -489,13 +553,14 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
 // dD = P^T dO + F . K dS and dY = T^T dD on VALU, then
 // dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.  The
 // next chunk's inputs are loaded into registers while this one is computed.
-template <int DK, int DV, typename In>
+template <int DK, int DV, typename In, bool CH>
 __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const In* __restrict__ k,
                                                  const float* __restrict__ dout, const float* __restrict__ dfinal,
                                                  float* __restrict__ dv, float* __restrict__ dinit, CWs w, int T,
                                                  int H, int Hk, int N, int vfirst) {
   constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
   __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
+  __shared__ __align__(16) float gs[CH ? kC + 1 : 1][CH ? KP : 4];
   __shared__ __align__(16) float TmT[kC][kCP], PmT[kC][kCP];
   __shared__ float part[NW][kC][kNS + 1];
   __shared__ float dO[kC][kNS + 1], dD[kC][kNS + 1], BB[2 * kC][kNS + 1];
@@ -516,6 +581,9 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
   RowPf<DK, In, kThr> kpf, qpf;
   MatPf<kThr, true> mpf;
   TokPf tpf;
+  GamPf<CH ? DK : 4, kThr> gpf;
+  if (CH)
+    for (int c = tid; c < DK; c += kThr) gs[0][c] = 0.f;
   float dov[2];
   auto prefetch = [&](int c) __attribute__((always_inline)) {
     const int L = min(kC, T - c * kC);
@@ -524,6 +592,7 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     qpf.load(q, w.sq, tok0, H, h, Hk, hk, L, tid);
     mpf.load(w, (static_cast<size_t>(bh) * N + c) * kC * kC, tid);
     tpf.load(w, tok0, H, h, L, tid);
+    if constexpr (CH) gpf.load(w.gmc, tok0, H, h, L, tid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + u * kThr, r = min(idx / kNS, L - 1), n = idx % kNS;
@@ -538,7 +607,8 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     kpf.store(kh, L, tid);
     qpf.store(qh, L, tid);
     mpf.store(nullptr, TmT, PmT, tid);
-    tpf.store(tv, L, tid);
+    tpf.store<CH>(tv, L, tid);
+    if constexpr (CH) gpf.store(gs, tid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + u * kThr;
@@ -564,7 +634,14 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
         for (int j = 0; j < NT; ++j) {
           const int mt = wave + 4 * j;
           if (mt < MT) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+            f32x4 a = *reinterpret_cast<const f32x4*>(&kh[16 * rt + li][16 * mt + 4 * lg]);
+            if constexpr (CH) {
+              // k exp(gC - gam) per channel
+              const f32x4 gm = *reinterpret_cast<const f32x4*>(&gs[16 * rt + li + 1][16 * mt + 4 * lg]);
+              const f32x4 gC = *reinterpret_cast<const f32x4*>(&gs[L][16 * mt + 4 * lg]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[e] *= __expf(gC[e] - gm[e]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) p = mma4(a[e], acc[j][e], p);
           }
@@ -574,6 +651,14 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
       }
     }
     lds_sync();
+    if constexpr (CH) {
+      // the rows of the dS update: q exp(gam) and k exp(gx), in place
+      for (int idx = tid; idx < kC * DK; idx += kThr) {
+        const int r = idx / DK, c = idx % DK;
+        qh[r][c] *= __expf(gs[r + 1][c]);
+        kh[r][c] *= __expf(gs[r][c]);
+      }
+    }
     // dD = P^T dO + F . K dS
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -600,7 +685,12 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     for (int j = 0; j < NT; ++j) {
       const int mt = wave + 4 * j;
       if (mt < MT) {
-        acc[j] *= egC;
+        if constexpr (CH) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][e] *= __expf(gs[L][16 * mt + 4 * lg + e]);
+        } else {
+          acc[j] *= egC;
+        }
 #pragma unroll
         for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(qh[4 * ks + lg][16 * mt + li], BB[4 * ks + lg][li], acc[j]);
 #pragma unroll
@@ -921,6 +1011,421 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
   }
 }
 
+// (0) per-channel decay: per (b, h, chunk) the norm factors of the rows,
+// beta, gam per key channel (to the workspace), and T and P of the chunk,
+// each Gram entry summed over the channels with its own decay factor
+// exp(gx_rc - gam_sc) (A) or exp(gam_rc - gam_sc) (P), every exponent <= 0.
+template <int DK, typename In>
+__global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, const In* __restrict__ k,
+                                                     const In* __restrict__ beta, const In* __restrict__ decay,
+                                                     CWs w, int T, int H, int Hk, int N, float scale, int l2norm,
+                                                     Transforms tf) {
+  constexpr int KP = DK + 4;
+  __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
+  __shared__ __align__(16) float gs[kC + 1][KP];   // row r + 1: gam of token r; row 0: zeros
+  __shared__ float sA[kC][kC + 1];
+  __shared__ float sbt[kC];
+  const int tid = threadIdx.x;
+  const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);
+  const int t0 = ci * kC, L = min(kC, T - t0);
+  const long tok0 = static_cast<long>(b) * T + t0;
+  const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;
+  {
+    constexpr int V = act<In>::kVec, LPR = DK / V;
+    static_assert(kC * LPR % 64 == 0, "whole waves per pass");
+    for (int idx = tid; idx < kC * LPR; idx += kThr) {
+      const int r = idx / LPR, seg = idx % LPR;
+      const bool in = r < L;
+      float qv[V], kv[V], gv[V], sq = 0.f, sk = 0.f;
+      if (in) {
+        const long base = ((tok0 + r) * Hk + hk) * DK + seg * V;
+        act<In>::load_vec(q + base, qv);
+        act<In>::load_vec(k + base, kv);
+        act<In>::load_vec(decay + ((tok0 + r) * H + h) * DK + seg * V, gv);
+        if (tf.A_log) {
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            gv[e] = gate_decay(gv[e], negA, tf.dt_bias ? tf.dt_bias[h * DK + seg * V + e] : 0.f, tf.lower);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) qv[e] = kv[e] = gv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sq += qv[e] * qv[e];
+        sk += kv[e] * kv[e];
+      }
+      sq = dpp_group_sum<LPR>(sq);
+      sk = dpp_group_sum<LPR>(sk);
+      const float fq = (l2norm ? inv_norm(sq) : 1.f) * scale, fk = l2norm ? inv_norm(sk) : 1.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        qh[r][seg * V + e] = qv[e] * fq;
+        kh[r][seg * V + e] = kv[e] * fk;
+        gs[r + 1][seg * V + e] = gv[e];
+      }
+      if (seg == 0 && in) {
+        w.sq[(tok0 + r) * H + h] = fq;
+        w.sk[(tok0 + r) * H + h] = fk;
+      }
+    }
+  }
+  if (tid < kC) {
+    const bool in = tid < L;
+    const long ti = (tok0 + tid) * H + h;
+    const float bt = in ? beta_transform(act<In>::load1(beta + ti), tf.beta_mode) : 0.f;
+    sbt[tid] = bt;
+    if (in) w.bt[ti] = bt;
+  }
+  lds_sync();
+  // gam per channel: a running sum down the chunk's tokens (past the end the
+  // decay is zero, so the last token's value repeats)
+  for (int c = tid; c < DK; c += kThr) {
+    float acc = 0.f;
+    gs[0][c] = 0.f;
+    for (int r = 0; r < kC; ++r) {
+      acc += gs[r + 1][c];
+      gs[r + 1][c] = acc;
+      if (r < L) w.gmc[((tok0 + r) * H + h) * DK + c] = acc;
+    }
+  }
+  lds_sync();
+  const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
+  // the 528 pairs s <= r of the chunk, one per thread and pass
+  for (int idx = tid; idx < kC * (kC + 1) / 2; idx += kThr) {
+    int r = static_cast<int>((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
+    if ((r + 1) * (r + 2) / 2 <= idx) ++r;
+    if (r * (r + 1) / 2 > idx) --r;
+    const int s = idx - r * (r + 1) / 2;
+    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < DK; c += 4) {
+      const f32x4 kr = *reinterpret_cast<const f32x4*>(&kh[r][c]);
+      const f32x4 ks = *reinterpret_cast<const f32x4*>(&kh[s][c]);
+      const f32x4 qr = *reinterpret_cast<const f32x4*>(&qh[r][c]);
+      const f32x4 gx = *reinterpret_cast<const f32x4*>(&gs[r][c]);
+      const f32x4 gr = *reinterpret_cast<const f32x4*>(&gs[r + 1][c]);
+      const f32x4 gsv = *reinterpret_cast<const f32x4*>(&gs[s + 1][c]);
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        p0 += qr[e] * ks[e] * __expf(gr[e] - gsv[e]);
+        p1 += qr[e + 1] * ks[e + 1] * __expf(gr[e + 1] - gsv[e + 1]);
+        // exp(gx_r - gam_s) <= 1 only for s < r: masked below
+        a0 += kr[e] * ks[e] * __expf(fminf(gx[e] - gsv[e], 0.f));
+        a1 += kr[e + 1] * ks[e + 1] * __expf(fminf(gx[e + 1] - gsv[e + 1], 0.f));
+      }
+    }
+    sA[r][s] = s < r ? sbt[r] * (a0 + a1) : 0.f;
+    w.Pm[cb + r * kC + s] = p0 + p1;
+  }
+  // the upper triangles: zeros
+  for (int idx = tid; idx < kC * kC; idx += kThr) {
+    const int r = idx / kC, s = idx % kC;
+    if (s > r) {
+      sA[r][s] = 0.f;
+      w.Pm[cb + idx] = 0.f;
+    }
+  }
+  lds_sync();
+  if (tid < kC) {
+    // column j of T = (I + A)^-1 by forward substitution
+    const int j = tid;
+    float x[kC];
+#pragma unroll
+    for (int r = 0; r < kC; ++r) {
+      float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= sA[r][s] * x[s];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < kC; ++r) w.Tm[cb + r * kC + j] = x[r];
+  }
+}
+
+// LDS of the per-chunk gradient kernel with a per-channel decay
+template <int DK>
+struct LocalChLds {
+  float kh[kC][DK + 4], qh[kC][DK + 4];   // normalised rows
+  float kx[kC][DK + 4], kf[kC][DK + 4];   // k exp(gx), k exp(gC - gam)
+  float gs[kC + 1][DK + 4];               // row r + 1: gam of token r; row 0: zeros
+  float TmT[kC][kCP], PmT[kC][kCP];
+  union {
+    struct {
+      float S0s[DK][kNS + 1], S1s[DK][kNS + 1];
+      float KX[kC][kNS + 1], KD[kC][kNS + 1];
+      float dO[kC][kNS + 1], Yb[kC][kNS + 1], D[kC][kNS + 1], dX[kC][kNS + 1], dD[kC][kNS + 1];
+    } s;
+    struct {
+      float dTm[kC][kCP], M[kC][kCP], dA[kC][kCP], dPm[kC][kCP];
+      float Wg[kC][DK + 4];               // dgam_r + dgx_{r+1} per channel
+      float dbp[DK / 16][kC];             // dbeta parts per 16 channels
+      float dgcp[2][DK];                  // dgC parts per row tile
+    } f;
+  } u;
+  float tb[kC], dgs[DK];
+  TokVec tv;
+};
+
+// (3) per-channel decay, per (b, h, chunk): dq, dk (normalised rows),
+// dbeta and the per-channel decay's gradient.  Per slice of 16 value
+// columns: X = V - (k exp(gx)) S0 and K dS1 with F folded in, on MFMA (one
+// row tile per wave, waves 0-3); D, dD, dY on VALU; then the running sums
+// dT, dP (a tile per wave) and, per (row, channel) position held by a wave,
+// dO S0^T, dX S0^T and D dS1^T.  Then dA; then, at each position, the
+// in-chunk pair terms with their own exponentials (sums over the partner
+// token u of dA or dP times k or q and exp of a difference of gam, never
+// positive), and the gradients from them and the three sums.  The decay's
+// gradient is a reverse running sum down the tokens per channel.
+template <int DK, int DV, typename In>
+__global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q, const In* __restrict__ k,
+                                                       const In* __restrict__ v, const float* __restrict__ dout,
+                                                       float* __restrict__ dq, float* __restrict__ dk,
+                                                       float* __restrict__ dbeta, float* __restrict__ ddecay,
+                                                       CWs w, int T, int H, int Hk, int N) {
+  constexpr int NT16 = DK / 16, NPOS = 2 * NT16, PPW = (NPOS + 7) / 8;   // (row tile, channel tile) positions
+  constexpr int SPT = DK * kNS / kThr3, SL = kNS / SPT, nsl = DV / kNS;
+  __shared__ __align__(16) LocalChLds<DK> sm;
+  auto& S = sm.u.s;
+  auto& Fm = sm.u.f;
+  TokVec& tv = sm.tv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int er = tid / kNS, en = tid % kNS;
+  const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);
+  const int t0 = ci * kC, L = min(kC, T - t0);
+  const long tok0 = static_cast<long>(b) * T + t0;
+  const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
+  const float* s0g = w.S0 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
+  const float* s1g = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
+  const bool rin = er < L;
+  const long vrowc = ((tok0 + min(er, L - 1)) * H + h) * DV;
+  const int sc = tid / SL, sn = (tid % SL) * SPT;
+  float ps0[SPT], ps1[SPT], pdo;
+  typename Raw<In>::one pv;
+  auto prefetch = [&](int s) __attribute__((always_inline)) {
+    const int nb = s * kNS;
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      ps0[e] = s0g[sc * DV + nb + sn + e];
+      ps1[e] = s1g[sc * DV + nb + sn + e];
+    }
+    pdo = dout[vrowc + nb + en];
+    pv = Raw<In>::ld1(v + vrowc + nb + en);
+  };
+  prefetch(0);
+  {
+    RowPf<DK, In, kThr3> kpf, qpf;
+    MatPf<kThr3, true> mpf;
+    TokPf tpf;
+    GamPf<DK, kThr3> gpf;
+    kpf.load(k, w.sk, tok0, H, h, Hk, hk, L, tid);
+    qpf.load(q, w.sq, tok0, H, h, Hk, hk, L, tid);
+    mpf.load(w, cb, tid);
+    tpf.load(w, tok0, H, h, L, tid);
+    gpf.load(w.gmc, tok0, H, h, L, tid);
+    kpf.store(sm.kh, L, tid);
+    qpf.store(sm.qh, L, tid);
+    mpf.store(nullptr, sm.TmT, sm.PmT, tid);
+    tpf.store<true>(tv, L, tid);
+    gpf.store(sm.gs, tid);
+    for (int c = tid; c < DK; c += kThr3) sm.gs[0][c] = 0.f;
+  }
+  lds_sync();
+  for (int idx = tid; idx < kC * DK; idx += kThr3) {
+    const int r = idx / DK, c = idx % DK;
+    sm.kx[r][c] = sm.kh[r][c] * __expf(sm.gs[r][c]);
+    sm.kf[r][c] = sm.kh[r][c] * __expf(sm.gs[L][c] - sm.gs[r + 1][c]);
+  }
+  float sb = 0.f, sdc = 0.f;
+  f32x4 atp = {0.f, 0.f, 0.f, 0.f};
+  f32x4 aq[PPW], ax[PPW], af[PPW];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) aq[j] = ax[j] = af[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tpm = wave >> 2, tpr = (wave >> 1) & 1, tpc = wave & 1;
+  const int prod = wave >> 1, prt = wave & 1;   // waves 0-3: K S0 (prod 0) or K dS1 (prod 1), row tile prt
+  for (int s = 0; s < nsl; ++s) {
+    lds_sync();
+#pragma unroll
+    for (int e = 0; e < SPT; ++e) {
+      S.S0s[sc][sn + e] = ps0[e];
+      S.S1s[sc][sn + e] = ps1[e];
+      sdc += ps0[e] * ps1[e];
+    }
+    const float vcur = rin ? Raw<In>::cvt1(pv) : 0.f, docur = rin ? pdo : 0.f;
+    S.dO[er][en] = docur;
+    lds_sync();
+    if (s + 1 < nsl) prefetch(s + 1);
+    if (prod < 2) {
+      const float(*A)[DK + 4] = prod == 0 ? sm.kx : sm.kf;
+      const float(*Bm)[kNS + 1] = prod == 0 ? S.S0s : S.S1s;
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&A[16 * prt + li][16 * kb + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = mma4(a[e], Bm[16 * kb + 4 * lg + e][li], p);
+      }
+      float(*O)[kNS + 1] = prod == 0 ? S.KX : S.KD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[16 * prt + 4 * lg + e][li] = p[e];
+    }
+    lds_sync();
+    const float x = vcur - S.KX[er][en];
+    S.Yb[er][en] = tv.bt[er] * x;
+    S.dD[er][en] = row_col(sm.PmT[er], S.dO, en) + S.KD[er][en];
+    lds_sync();
+    const float d = col_col(sm.TmT, er, S.Yb, en);
+    const float y = row_col(sm.TmT[er], S.dD, en);
+    S.D[er][en] = d;
+    S.dX[er][en] = tv.bt[er] * y;
+    sb += y * x;
+    lds_sync();
+#pragma unroll
+    for (int ks = 0; ks < kNS / 4; ++ks) {
+      const float a = tpm ? S.dO[16 * tpr + li][4 * ks + lg] : S.dD[16 * tpr + li][4 * ks + lg];
+      const float bb = tpm ? S.D[16 * tpc + li][4 * ks + lg] : S.Yb[16 * tpc + li][4 * ks + lg];
+      atp = mma4(a, bb, atp);
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int pos = wave + 8 * j;
+      if (pos < NPOS) {
+        const int mt = pos / NT16, nt = pos % NT16;
+#pragma unroll
+        for (int ks = 0; ks < kNS / 4; ++ks) {
+          const int r = 16 * mt + li, n = 4 * ks + lg, c = 16 * nt + li;
+          const float b0 = S.S0s[c][n];
+          aq[j] = mma4(S.dO[r][n], b0, aq[j]);
+          ax[j] = mma4(S.dX[r][n], b0, ax[j]);
+          af[j] = mma4(S.D[r][n], S.S1s[c][n], af[j]);
+        }
+      }
+    }
+  }
+  sb = dpp_group_sum<16>(sb);
+  // <dS1, S0> per key channel: the SL threads of a state row are consecutive lanes
+  if constexpr (SL > 1) sdc = group_sum<SL>(sdc);
+  lds_sync();
+  if (en == 0) sm.tb[er] = sb;
+  if (tid % SL == 0) sm.dgs[sc] = __expf(sm.gs[L][sc]) * sdc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 16 * tpr + 4 * lg + e, c = 16 * tpc + li;
+    if (tpm) Fm.dPm[r][c] = c <= r ? atp[e] : 0.f;
+    else Fm.dTm[r][c] = c <= r ? atp[e] : 0.f;
+  }
+  lds_sync();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
+    Fm.M[r][c] = row_col(Fm.dTm[r], sm.TmT, c);
+  }
+  lds_sync();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
+    Fm.dA[r][c] = c < r ? -row_col(sm.TmT[r], Fm.M, c) : 0.f;
+  }
+  lds_sync();
+  // per position: the pair terms and the gradients
+  const bool grouped = H != Hk;
+  float dgx[PPW][4];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int pos = wave + 8 * j;
+    if (pos < NPOS) {
+      const int mt = pos / NT16, nt = pos % NT16, c = 16 * nt + li;
+      float G1[4] = {0.f, 0.f, 0.f, 0.f}, G2[4] = {0.f, 0.f, 0.f, 0.f};
+      float H1[4] = {0.f, 0.f, 0.f, 0.f}, H2[4] = {0.f, 0.f, 0.f, 0.f};
+      float gx[4], gm[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gx[e] = sm.gs[16 * mt + 4 * lg + e][c];
+        gm[e] = sm.gs[16 * mt + 4 * lg + e + 1][c];
+      }
+#pragma unroll 2
+      for (int uu = 0; uu < kC; ++uu) {
+        const float ku = sm.kh[uu][c], qu = sm.qh[uu][c], gxu = sm.gs[uu][c], gmu = sm.gs[uu + 1][c];
+        const float bu = tv.bt[uu];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * lg + e;
+          // u < r: exp(gx_r - gam_u); u > r: exp(gx_u - gam_r); u == r: unused
+          const float e1 = __expf(uu < r ? gx[e] - gmu : (uu > r ? gxu - gm[e] : 0.f));
+          // u <= r: exp(gam_r - gam_u); u > r: exp(gam_u - gam_r)
+          const float e2 = __expf(uu <= r ? gm[e] - gmu : gmu - gm[e]);
+          G1[e] += Fm.dA[r][uu] * ku * e1;
+          G2[e] += Fm.dA[uu][r] * bu * ku * e1;
+          H1[e] += Fm.dPm[r][uu] * ku * e2;
+          H2[e] += Fm.dPm[uu][r] * qu * e2;
+        }
+      }
+      float dbe[4], dgc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mt + 4 * lg + e;
+        const float kr = sm.kh[r][c], qr = sm.qh[r][c], br = tv.bt[r];
+        const float egm = __expf(gm[e]), egx = __expf(gx[e]), Fx = __expf(sm.gs[L][c] - gm[e]);
+        const float dqv = egm * aq[j][e] + H1[e];
+        const float dkv = -egx * ax[j][e] + Fx * af[j][e] + br * G1[e] + G2[e] + H2[e];
+        const float kfa = kr * Fx * af[j][e];
+        Fm.Wg[r][c] = qr * egm * aq[j][e] - kfa + qr * H1[e] - kr * (G2[e] + H2[e]);
+        dgx[j][e] = -kr * egx * ax[j][e] + br * kr * G1[e];
+        dbe[e] = kr * G1[e];
+        dgc += kfa;
+        if (r < L) {
+          const long o = ((tok0 + r) * Hk + hk) * DK + c;
+          if (grouped) {
+            atomicAdd(dq + o, dqv);
+            atomicAdd(dk + o, dkv);
+          } else {
+            dq[o] = dqv;
+            dk[o] = dkv;
+          }
+        }
+      }
+      // dbeta: k G1 over the 16 channels of the tile; dgC: over the 16 rows
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dbe[e] = dpp_group_sum<16>(dbe[e]);
+        if (li == 0) Fm.dbp[nt][16 * mt + 4 * lg + e] = dbe[e];
+      }
+      dgc = xor32_sum(xor16_sum(dgc));
+      if (lg == 0) Fm.dgcp[mt][c] = dgc;
+    }
+  }
+  lds_sync();
+  // dgx_{r+1} into row r of Wg (its own element: one adder per element)
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int pos = wave + 8 * j;
+    if (pos < NPOS) {
+      const int mt = pos / NT16, nt = pos % NT16, c = 16 * nt + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mt + 4 * lg + e;
+        if (r >= 1) Fm.Wg[r - 1][c] += dgx[j][e];
+      }
+    }
+  }
+  lds_sync();
+  // dg_tc = sum_{r >= t} (dgam_rc + dgx_{r+1,c}) + dgC_c, from the last token up
+  for (int c = tid; c < DK; c += kThr3) {
+    float acc = sm.dgs[c] + Fm.dgcp[0][c] + Fm.dgcp[1][c];
+    for (int t = kC - 1; t >= 0; --t) {
+      acc += Fm.Wg[t][c];
+      if (t < L) ddecay[((tok0 + t) * H + h) * DK + c] = acc;
+    }
+  }
+  if (tid < kC && tid < L) {
+    float db = sm.tb[tid];
+#pragma unroll
+    for (int nt = 0; nt < NT16; ++nt) db += Fm.dbp[nt][tid];
+    dbeta[(tok0 + tid) * H + h] = db;
+  }
+}
+
 template <int DK, int DV, typename In>
 hipError_t run(const BwdArgs& a, hipStream_t s) {
   const In* q = static_cast<const In*>(a.q);
@@ -932,11 +1437,21 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
   CWs w;
   ws_floats(a.B, a.T, a.H, DK, DV, &w, a.ckpt);
   const unsigned chunks = static_cast<unsigned>(a.B * a.H * N), slices = static_cast<unsigned>(a.B * a.H * (DV / kNS));
+  if (a.decay_kind == DECAY_CHANNEL) {
+    cbwd_prep_ch<DK, In><<<dim3(chunks), dim3(kThr), 0, s>>>(q, k, be, de, w, a.T, a.H, a.Hk, N, a.scale,
+                                                              a.l2norm, a.tf);
+    cbwd_fwd<DK, DV, In, true><<<dim3(slices), dim3(kThr), 0, s>>>(k, v, a.init, w, a.T, a.H, a.Hk, N, a.vfirst);
+    cbwd_rev<DK, DV, In, true><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
+                                                                   a.H, a.Hk, N, a.vfirst);
+    cbwd_local_ch<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(q, k, v, a.dout, a.dq, a.dk, a.dbeta,
+                                                                    a.ddecay, w, a.T, a.H, a.Hk, N);
+    return hipGetLastError();
+  }
   cbwd_prep<DK, In><<<dim3(chunks), dim3(kThr), 0, s>>>(q, k, be, de, a.decay_kind == DECAY_HEAD, w, a.T, a.H,
                                                          a.Hk, N, a.scale, a.l2norm, a.tf);
-  cbwd_fwd<DK, DV, In><<<dim3(slices), dim3(kThr), 0, s>>>(k, v, a.init, w, a.T, a.H, a.Hk, N, a.vfirst);
-  cbwd_rev<DK, DV, In><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T, a.H,
-                                                           a.Hk, N, a.vfirst);
+  cbwd_fwd<DK, DV, In, false><<<dim3(slices), dim3(kThr), 0, s>>>(k, v, a.init, w, a.T, a.H, a.Hk, N, a.vfirst);
+  cbwd_rev<DK, DV, In, false><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
+                                                                  a.H, a.Hk, N, a.vfirst);
   cbwd_local<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(
       q, k, v, a.dout, a.dq, a.dk, a.dbeta, a.decay_kind == DECAY_HEAD ? a.ddecay : nullptr, w, a.T, a.H, a.Hk, N);
   return hipGetLastError();

@@ -68,8 +68,8 @@ hipError_t launch_chunked_varlen(const FwdArgs& a, const int* cu_dev, const int*
 hipError_t launch_state_copy(const float* src, float* dst, long n, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
-// The chunked form of the backward (per-head decay or none); the front end's
-// launch_bwd routes those decays here after clearing the outputs.
+// The chunked kernels of the backward, launched by launch_bwd after it has
+// cleared what they add into.
 hipError_t launch_bwd_chunked(const BwdArgs& a, hipStream_t s);
 size_t bwd_chunked_workspace_bytes(int B, int T, int H, int DK, int DV);
 // LDS footprint (bytes) of the larger chunked kernel for this shape, 0 if unsupported.

@@ -297,17 +297,16 @@ int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const v
  *   ddt_bias       with KDA_TF_GATE and a dt_bias: like dt_bias, fp32, written
  *   d_initial_state NULL (not written) | like initial_state, fp32, written
  *   workspace      DEVICE, 16-byte aligned, at least kda_bwd_workspace_bytes
- *                  (the state at every chunk boundary and the chunks' own
- *                  matrices, or the state every 16 tokens)
+ *                  (the state and its gradient at every chunk start, the
+ *                  chunks' T and P, per-token factors and, for any decay, a
+ *                  per-channel cumulative decay)
  *
- * With a per-head decay or none the backward runs chunk by chunk in the WY
- * form (chunks of 32 tokens: the states at chunk boundaries forward, their
- * gradients in reverse, then every chunk's local gradients in parallel);
- * with a per-channel decay it runs token by token, the state every 16 tokens
- * checkpointed.  All arithmetic is fp32; sums over value heads of a group
- * (and, token by token, over value columns; for dA_log and ddt_bias over
- * tokens) are gathered with atomic adds, so results may differ in the last
- * bits from run to run.
+ * The backward runs chunk by chunk in the WY form, for every decay kind
+ * (chunks of 32 tokens: the states at chunk boundaries forward, their
+ * gradients in reverse, then every chunk's local gradients in parallel).
+ * All arithmetic is fp32; sums over the value heads of a group (and, for
+ * dA_log and ddt_bias, over tokens) are gathered with atomic adds, so those
+ * results may differ in the last bits from run to run.
  * Errors as kda_fwd_chunked; KDA_ERR_NULL if (T > 0) d_o, dq, dk, dv, dbeta,
  * (with a decay) ddecay, or (with KDA_TF_GATE) dA_log or (with a dt_bias)
  * ddt_bias is NULL; KDA_ERR_WORKSPACE as for the forward.  T == 0 copies

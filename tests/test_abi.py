@@ -219,15 +219,14 @@ def test_backward_rejects_bad_arguments(L):
     assert call(**gate, A_log=FAKE, dA=FAKE, bias=FAKE) == 1
     assert call(tf=1, A_log=FAKE, dA=FAKE) == 4   # a raw gate needs a decay
     assert call(tf=64) == 4                       # an unknown flag
-    # the larger of: the state every 16 tokens for every (batch, value head);
-    # and the chunked form's records (chunks of 32: five per-token factors,
-    # T and P per chunk, each in whole 64-float blocks, and the state and
-    # its gradient at every chunk start)
+    # the chunked form's records (chunks of 32): five per-token factors, T
+    # and P per chunk, each in whole 64-float blocks, the state and its
+    # gradient at every chunk start, and a cumulative decay per token and
+    # key channel
     def chunked(B, T, HV, DK, DV):
         blk = lambda n: -(-n // 64) * 64
         ch = B * HV * -(-T // 32)
-        return 4 * (5 * blk(B * T * HV) + 2 * blk(ch * 32 * 32) + 2 * ch * DK * DV)
+        return 4 * (5 * blk(B * T * HV) + 2 * blk(ch * 32 * 32) + 2 * ch * DK * DV + B * T * HV * DK)
     for args in ((2, 33, 3, 64, 32), (1, 100, 2, 128, 128), (3, 7, 1, 32, 64)):
-        plain = args[0] * args[2] * -(-args[1] // 16) * args[3] * args[4] * 4
-        assert L.kda_bwd_workspace_bytes(*args) == max(plain, chunked(*args)), args
+        assert L.kda_bwd_workspace_bytes(*args) == chunked(*args), args
     assert L.kda_bwd_workspace_bytes(1, 0, 1, 64, 64) == 0

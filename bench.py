@@ -143,7 +143,7 @@ def backward_bytes(w) -> int:
     """Algorithmic HBM bytes of one backward call: q, k, v, beta, the decay
     and do read once, dq, dk, dv, dbeta and the decay gradient written once
     (fp32), the initial state and the final-state gradient read and the
-    initial-state gradient written (the workspace's checkpoints are not
+    initial-state gradient written (the workspace's records are not
     counted)."""
     a = act_bytes(w)
     gate = {0: 0, 1: 1, 2: w.DK}[w.decay_kind]
@@ -151,6 +151,21 @@ def backward_bytes(w) -> int:
     per_tok = (w.DV + 1 + gate) * a + w.DV * 4 + (w.DV + 1 + gate) * 4   # v beta decay do; dv dbeta ddecay
     state = w.DK * w.DV * 4 * (3 if w.init_state else 2)
     return qk + w.B * w.T * w.hv * per_tok + w.B * w.hv * state
+
+
+BWD_CHUNK = 32                  # tokens per chunk of the chunked backward
+MFMA_PEAK_F32 = 157.3e12        # MI355X dense fp32 MFMA, flop/s
+
+
+def backward_flops(w) -> int:
+    """Algorithmic flops of one chunked backward call, its contractions as
+    dense tiles (chunks of C = 32): per token-head 2 (11 DK DV + 6 C DK +
+    2 C DV).  The state walks: K S and the state update (2 DK DV), K dS and
+    the dS update with q and k (3 DK DV); per chunk: K S0, Q S0, K dS1 and
+    dO S0^T, D dS1^T, dY S0^T (6 DK DV); K K^T and Q K^T in the prep, K K^T
+    again and Z K, dG K, Z^T Q at the end (6 C DK); dT and dP (2 C DV)."""
+    C = BWD_CHUNK
+    return 2 * (11 * w.DK * w.DV + 6 * C * w.DK + 2 * C * w.DV) * w.B * w.T * w.hv
 
 
 def time_backward(w, steps, warmup, dev):
@@ -563,14 +578,17 @@ def main():
             "sequences": VARLEN_SEQS, "tokens": w.B * w.T, "min_len": min(lens), "max_len": max(lens),
             "tokens_per_s": round(w.B * w.T / (vk * 1e-3), 1), "kernel_ms_mean": round(vk, 4),
             "hbm_frac": round(vb / (vk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        # the backward (kda_bwd) at the headline shape: the plain form, a
-        # sequential reverse pass per value column
-        b_ms = time_backward(w, max(3, args.steps // 20), args.warmup, dev)
-        extra[w.name + "_backward"] = {
-            "kernel_ms_mean": round(b_ms, 3), "tokens_per_s": round(w.B * w.T / (b_ms * 1e-3), 1),
-            "algorithmic_bytes": backward_bytes(w),
-            "hbm_frac": round(backward_bytes(w) / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-            "form": "sequential reverse pass per value column, fp32 VALU (no chunked MFMA form)"}
+        # the backward (kda_bwd) at the headline shape and at the per-channel
+        # one: the chunked form, fp32 MFMA contractions
+        for wb in (w, WORKLOADS["kda_d128"]):
+            b_ms = time_backward(wb, max(3, args.steps // 20), args.warmup, dev)
+            extra[wb.name + "_backward"] = {
+                "kernel_ms_mean": round(b_ms, 3), "tokens_per_s": round(wb.B * wb.T / (b_ms * 1e-3), 1),
+                "algorithmic_flops": backward_flops(wb),
+                "mfma_f32_frac": round(backward_flops(wb) / (b_ms * 1e-3) / MFMA_PEAK_F32, 4),
+                "algorithmic_bytes": backward_bytes(wb),
+                "hbm_frac": round(backward_bytes(wb) / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                "form": "chunked WY (C = 32), fp32 MFMA contractions"}
         w5 = WORKLOADS["decode_d128"]
         d_ms = time_decode(w5, max(5, args.steps), args.warmup, dev)
         gbs = decode_bytes(w5) / (d_ms * 1e-3) / 1e9

@@ -1307,6 +1307,11 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
   // <dS1, S0> per key channel: the SL threads of a state row are consecutive lanes
   if constexpr (SL > 1) sdc = group_sum<SL>(sdc);
   lds_sync();
+  // the per-token decay factors a_t = exp(g_t) per channel, in kx's place
+  for (int idx = tid; idx < kC * DK; idx += kThr3) {
+    const int t = idx / DK, c = idx % DK;
+    sm.kx[t][c] = __expf(sm.gs[t + 1][c] - sm.gs[t][c]);
+  }
   if (en == 0) sm.tb[er] = sb;
   if (tid % SL == 0) sm.dgs[sc] = __expf(sm.gs[L][sc]) * sdc;
 #pragma unroll
@@ -1344,21 +1349,41 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
         gx[e] = sm.gs[16 * mt + 4 * lg + e][c];
         gm[e] = sm.gs[16 * mt + 4 * lg + e + 1][c];
       }
-#pragma unroll 2
-      for (int uu = 0; uu < kC; ++uu) {
-        const float ku = sm.kh[uu][c], qu = sm.qh[uu][c], gxu = sm.gs[uu][c], gmu = sm.gs[uu + 1][c];
-        const float bu = tv.bt[uu];
+      // The decay factor between tokens u and r is a product of the per-token
+      // factors a_t = exp(g_t) <= 1 strictly between or up to them, carried
+      // down (u < r) and up (u > r) the partner tokens: no exponential per
+      // pair, no factor above one.
+      {
+        float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
+        // rows 16 mt .. 16 mt + 15: partners u <= r start at the tile's last row
+#pragma unroll 8
+        for (int uu = 16 * mt + 15; uu >= 0; --uu) {
+          const float ku = sm.kh[uu][c], an = sm.kx[min(uu + 1, kC - 1)][c];   // a_{u+1}
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * mt + 4 * lg + e;
-          // u < r: exp(gx_r - gam_u); u > r: exp(gx_u - gam_r); u == r: unused
-          const float e1 = __expf(uu < r ? gx[e] - gmu : (uu > r ? gxu - gm[e] : 0.f));
-          // u <= r: exp(gam_r - gam_u); u > r: exp(gam_u - gam_r)
-          const float e2 = __expf(uu <= r ? gm[e] - gmu : gmu - gm[e]);
-          G1[e] += Fm.dA[r][uu] * ku * e1;
-          G2[e] += Fm.dA[uu][r] * bu * ku * e1;
-          H1[e] += Fm.dPm[r][uu] * ku * e2;
-          H2[e] += Fm.dPm[uu][r] * qu * e2;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * mt + 4 * lg + e;
+            E1[e] = uu >= r - 1 ? 1.f : E1[e] * an;   // exp(gx_r - gam_u), u < r
+            E2[e] = uu >= r ? 1.f : E2[e] * an;       // exp(gam_r - gam_u), u <= r
+            G1[e] += Fm.dA[r][uu] * ku * E1[e];
+            H1[e] += Fm.dPm[r][uu] * ku * E2[e];
+          }
+        }
+      }
+      {
+        float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
+        // partners u >= r start at the tile's first row
+#pragma unroll 8
+        for (int uu = 16 * mt; uu < kC; ++uu) {
+          const float ku = sm.kh[uu][c], qu = sm.qh[uu][c], bu = tv.bt[uu];
+          const float ap = sm.kx[max(uu - 1, 0)][c], au = sm.kx[uu][c];   // a_{u-1}, a_u
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * mt + 4 * lg + e;
+            E1[e] = uu <= r + 1 ? 1.f : E1[e] * ap;   // exp(gx_u - gam_r), u > r
+            E2[e] = uu <= r ? 1.f : E2[e] * au;       // exp(gam_u - gam_r), u >= r
+            G2[e] += Fm.dA[uu][r] * bu * ku * E1[e];
+            H2[e] += Fm.dPm[uu][r] * qu * E2[e];
+          }
         }
       }
       float dbe[4], dgc = 0.f;

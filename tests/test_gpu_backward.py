@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gated_delta_rule_fwd_amd import bwd
+from gated_delta_rule_fwd_amd import bwd, fwd_chunked
 from gated_delta_rule_fwd_amd.inputs import (DECAY_CHANNEL, WORKLOADS, make_inputs,
                                              make_transform_inputs)
 from oracle import beta_transform, kda_decay, kda_scan_bwd, kda_scan_bwd_transforms
@@ -30,6 +30,10 @@ CASES = [
     ("gdn_d128", dict(B=1, T=161, H=1, HV=2, init_state=True), {}),
     ("deltanet_d64", dict(B=2, T=33, H=2, HV=4), {}),
     ("deltanet_d64", dict(B=1, T=130, H=2, init_state=True), {}),
+    # whole chunks of the backward (32 tokens) and no tail; grouped heads with
+    # a per-channel decay
+    ("kda_d128", dict(B=1, T=64, H=2, DV=32, init_state=True), {}),
+    ("fp32_small", dict(T=45, H=1, HV=2, DK=32, DV=32, decay="channel_softplus", init_state=True), {}),
     ("deltanet_d64", dict(B=1, T=1, H=2, DK=128, DV=32, init_state=True), {}),
 ]
 
@@ -198,3 +202,47 @@ def test_backward_value_major_states(name, kw):
         e = rel(out[name_g], ref[name_g])
         print(f"  {name_g}: err/rms={e:.3e} (tol {tol})", flush=True)
         assert e <= tol, f"{name_g}: {e:.3e} > {tol}"
+
+
+# Full size: the backward against central differences of the forward (both on
+# the GPU), along a random direction per input.  With L = <do, o> +
+# <dS_T, S_T>, (L(x + e d) - L(x - e d)) / 2e must equal <grad_x L, d> up to
+# O(e^2) and the forward's rounding divided by e.  The workloads' shapes with
+# fp32 activations: the fp64 oracle cannot run the whole backward at these
+# sizes, and bf16 inputs cannot carry a small step.
+FD_EPS = 1e-3
+FD_TOL = 1e-2
+
+
+@pytest.mark.parametrize("name", ["gdn_d128", "kda_d128", "deltanet_d64"])
+def test_backward_full_size_directional_derivatives(name):
+    w = WORKLOADS[name].scaled(dtype="f32")
+    announce(f"backward directional derivatives at full size {w}")
+    d = to_dev(make_inputs(w))
+    g = torch.Generator(device=dev()).manual_seed(11)
+    do = torch.randn((w.B, w.T, w.hv, w.DV), device=dev(), generator=g)
+    dST = torch.randn((w.B, w.hv, w.DK, w.DV), device=dev(), generator=g)
+    grads = bwd(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"], do, dST)
+
+    def loss(x):
+        o, st = fwd_chunked(x["q"], x["k"], x["v"], x["beta"], x["decay"], x["initial_state"],
+                            chunk_size=w.chunk)
+        return float((o.double() * do.double()).sum() + (st.double() * dST.double()).sum())
+
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta")]
+    if d["decay"] is not None:
+        names.append(("decay", "ddecay"))
+    if d["initial_state"] is not None:
+        names.append(("initial_state", "d_initial_state"))
+    for x_name, g_name in names:
+        delta = torch.randn(d[x_name].shape, device=dev(), generator=g)
+        if x_name in ("beta", "decay"):
+            delta = delta * d[x_name]          # relative steps: beta stays in (0, 1), the decay <= 0
+        plus, minus = dict(d), dict(d)
+        plus[x_name] = d[x_name] + FD_EPS * delta
+        minus[x_name] = d[x_name] - FD_EPS * delta
+        fd = (loss(plus) - loss(minus)) / (2 * FD_EPS)
+        an = float((grads[g_name].double() * delta.double()).sum())
+        err = abs(fd - an) / max(abs(an), 1e-30)
+        print(f"  {g_name}: analytic {an:.6e} difference quotient {fd:.6e} rel {err:.2e}", flush=True)
+        assert err <= FD_TOL, f"{g_name}: {err:.2e} > {FD_TOL}"

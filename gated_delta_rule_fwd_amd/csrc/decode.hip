@@ -10,9 +10,9 @@
 // so the whole step needs one read and one write of S.  The kernel is bound
 // by HBM bandwidth: 2 * DK * DV * 4 bytes of state traffic per (batch, head)
 // against about 6 * DK * DV flops.  Every value column is independent given
-// the token vectors, so a wave takes CS of the DV columns of one (batch, head)
-// with all their key rows in registers (32 KB of state in flight per wave at
-// DK = 128), and both column reductions stay inside the wave.
+// the token vectors; the reductions run over key rows.  A workgroup holds one
+// (batch, head)'s state in registers (64 KB at DK = DV = 128), read and
+// written in contiguous whole rows (key-major) or whole columns (value-major).
 #include "common.h"
 #include "launch.h"
 
@@ -21,43 +21,47 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Columns per workgroup.
-template <int DV> constexpr int decode_cols() { return DV > 64 ? 64 : DV; }
 // Columns per workgroup of the value-major kernel: at least one pass of
 // DK / 4-lane columns, at most 32.
 template <int DK, int DV> constexpr int decode_vm_cols() {
   return DV < 32 ? DV : (32 > 1024 / DK ? 32 : 1024 / DK);
 }
 
-// Key-major state [.., DK, DV]: one wave takes CS value columns of one
-// (batch, head) and all DK key rows.  A lane holds a float4 of columns in
-// rows rg + NRG i, so each row group reads whole CS-column row pieces; the
-// two reductions over rows run inside the wave (DPP and lane-swap moves), with
-// no LDS round trip and no barrier.  The token vectors go through the wave's
-// own LDS slice.
+// Key-major state [.., DK, DV]: a workgroup of NW waves takes one (batch,
+// head), wave w the key rows w DK/NW .. (w + 1) DK/NW - 1 with all DV columns.
+// A lane holds a float4 of columns in rows rg + NRG i of the wave's block, so
+// one wave instruction reads NRG whole rows, contiguous in memory.  The two
+// reductions over rows run inside the wave (lane-swap and DPP moves), then
+// over the waves through LDS behind the workgroup's one barrier.  Every
+// wave forms the token vectors' norms itself from all DK entries.
+// Waves per workgroup of the key-major kernel: eight where the rows allow
+// (at DK = DV = 128: 16 rows, 8 float4 registers of state per lane; four
+// waves with 32 rows each measured 0.709 of HBM against 0.712-0.720, sixteen
+// waves 0.63)
+template <int DK, int DV> constexpr int decode_waves() {
+  return DK / (256 / DV) >= 8 ? 8 : DK / (256 / DV);
+}
 template <int DK, int DV, typename In>
-__global__ __launch_bounds__(kThreads) void decode_kernel(
+__global__ __launch_bounds__(512) void decode_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const In* __restrict__ beta, const In* __restrict__ decay, int decay_kind,
     float* __restrict__ state, float* __restrict__ o, float scale, int l2norm, int H,
-    Transforms tf, int Hk, int nunits) {
-  constexpr int CS = decode_cols<DV>();
-  constexpr int NSPLIT = DV / CS;
-  constexpr int NC4 = CS / 4;             // float4 column groups: lanes per row
-  constexpr int NRG = 64 / NC4;           // row groups in the wave
-  constexpr int RPT = DK / NRG;           // rows per lane
-  static_assert(RPT >= 1 && DK % NRG == 0 && DV % CS == 0 && (NC4 == 8 || NC4 == 16), "shape");
-  constexpr int NW = kThreads / 64;
+    Transforms tf, int Hk) {
+  constexpr int NW = decode_waves<DK, DV>();
+  constexpr int RW = DK / NW;             // key rows per wave
+  constexpr int NC4 = DV / 4;             // float4 column groups: lanes per row
+  constexpr int NRG = 64 / NC4;           // rows per wave instruction
+  constexpr int RPT = RW / NRG;           // rows per lane
+  static_assert(RPT >= 1 && RW % NRG == 0 && (NC4 == 8 || NC4 == 16 || NC4 == 32), "shape");
 
-  __shared__ float s_q[NW][DK], s_k[NW][DK], s_gate[NW][DK];
+  __shared__ float s_q[DK], s_k[DK], s_gate[DK];
+  __shared__ f32x4 s_r[NW][NC4], s_y[NW][NC4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int unit = blockIdx.x * NW + wave;   // (batch, head, column block)
-  if (unit >= nunits) return;                 // whole waves only: no barrier below
-  const long bh = unit / NSPLIT;
-  const int n0 = (unit % NSPLIT) * CS;
+  const long bh = blockIdx.x;
   const int cg = lane % NC4, rg = lane / NC4;
-  float* S = state + bh * DK * DV + n0;
+  const int r0 = wave * RW;
+  float* S = state + bh * DK * DV;
   const int h = static_cast<int>(bh % H);
   const long bhk = (bh / H) * Hk + h / (H / Hk);
   const float negA = tf.A_log ? -__expf(tf.A_log[h]) : 0.f;
@@ -65,25 +69,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   f32x4 st[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (rg + NRG * i) * DV) + cg);
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (r0 + rg + NRG * i) * DV) + cg);
 
-  float* sq_ = s_q[wave];
-  float* sk_ = s_k[wave];
-  float* sg_ = s_gate[wave];
+  // the token vectors, whole, in every wave (the same values to the same LDS
+  // words), and their norms
   float pq = 0.f, pk = 0.f, pqk = 0.f;
 #pragma unroll
   for (int c = lane; c < DK; c += 64) {
     const float qc = act<In>::load1(q + bhk * DK + c);
     const float kc = act<In>::load1(k + bhk * DK + c);
-    sq_[c] = qc;
-    sk_[c] = kc;
+    s_q[c] = qc;
+    s_k[c] = kc;
     float gc = 1.f;
     if (decay_kind == DECAY_CHANNEL) {
       float g = act<In>::load1(decay + bh * DK + c);
       if (tf.A_log) g = gate_decay(g, negA, tf.dt_bias ? tf.dt_bias[h * DK + c] : 0.f, tf.lower);
       gc = __expf(g);
     }
-    sg_[c] = gc;
+    s_gate[c] = gc;
     pq += qc * qc; pk += kc * kc; pqk += qc * kc;
   }
   pq = group_sum<64>(pq); pk = group_sum<64>(pk); pqk = group_sum<64>(pqk);
@@ -104,30 +107,48 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   f32x4 r = {0, 0, 0, 0}, y = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int c = rg + NRG * i;
-    const float kc = sk_[c] * ik;
-    const float qc = sq_[c] * iq * sg_[c] * ghead;
+    const int c = r0 + rg + NRG * i;
+    const float kc = s_k[c] * ik;
+    const float qc = s_q[c] * iq * s_gate[c] * ghead;
     r += st[i] * kc;
     y += st[i] * qc;
   }
-  // sum over the NRG row groups: lanes with equal lane % NC4
+  // over the wave's row groups (lanes with equal lane % NC4: at NC4 = 32 the
+  // two halves of the wave), then the waves
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    r[e] = rowgroup_sum<NC4>(r[e]);
-    y[e] = rowgroup_sum<NC4>(y[e]);
+    if constexpr (NC4 == 32) {
+      r[e] = xor32_sum(r[e]);
+      y[e] = xor32_sum(y[e]);
+    } else {
+      r[e] = rowgroup_sum<NC4>(r[e]);
+      y[e] = rowgroup_sum<NC4>(y[e]);
+    }
+  }
+  if (rg == 0) {
+    s_r[wave][cg] = r;
+    s_y[wave][cg] = y;
+  }
+  __syncthreads();
+  r = s_r[0][cg];
+  y = s_y[0][cg];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    r += s_r[w][cg];
+    y += s_y[w][cg];
   }
   float vc[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) vc[e] = act<In>::load1(v + bh * DV + n0 + 4 * cg + e);
+  for (int e = 0; e < 4; ++e) vc[e] = act<In>::load1(v + bh * DV + 4 * cg + e);
   f32x4 delta;
 #pragma unroll
   for (int e = 0; e < 4; ++e) delta[e] = b * (vc[e] - r[e]);
-  if (rg == 0) *reinterpret_cast<f32x4*>(o + bh * DV + n0 + 4 * cg) = y + qk * delta;
+  if (wave == 0 && rg == 0) *reinterpret_cast<f32x4*>(o + bh * DV + 4 * cg) = y + qk * delta;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int c = rg + NRG * i;
-    const float gc = sg_[c] * ghead;
-    const float kc = sk_[c] * ik;
+    const int c = r0 + rg + NRG * i;
+    const float gc = s_gate[c] * ghead;
+    const float kc = s_k[c] * ik;
     const f32x4 ns = st[i] * gc + kc * delta;
     __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + c * DV) + cg);
   }
@@ -235,15 +256,13 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t s) {
 #define KDA_DECODE_CASE(dk, dv)                                                              \
   if (a.DK == dk && a.DV == dv) {                                                            \
     const dim3 grid(a.B * a.H * (dv / decode_vm_cols<dk, dv>()));                            \
-    const int units = a.B * a.H * (dv / decode_cols<dv>());                                  \
     if (a.vfirst)                                                                            \
       decode_vm_kernel<dk, dv, In><<<grid, block, 0, s>>>(q, k, v, be, de, a.decay_kind,     \
                                                           a.state, a.o, a.scale, a.l2norm,   \
                                                           a.H, a.tf, a.Hk);                  \
     else                                                                                     \
-      decode_kernel<dk, dv, In><<<dim3((units + 3) / 4), block, 0, s>>>(                     \
-          q, k, v, be, de, a.decay_kind, a.state, a.o, a.scale, a.l2norm, a.H, a.tf, a.Hk,   \
-          units);                                                                            \
+      decode_kernel<dk, dv, In><<<dim3(a.B * a.H), dim3(64 * decode_waves<dk, dv>()), 0, s>>>(\
+          q, k, v, be, de, a.decay_kind, a.state, a.o, a.scale, a.l2norm, a.H, a.tf, a.Hk);  \
     return hipGetLastError();                                                                \
   }
   KDA_DECODE_CASE(32, 32) KDA_DECODE_CASE(32, 64) KDA_DECODE_CASE(32, 128)

@@ -5,11 +5,12 @@
 // kda_chunk_step_exact_bwd: dq, dk, dv, dg, dbeta, dstate_in).
 //
 // The chunked kernels (backward_chunked.hip) produce dv, the initial-state
-// gradient, dbeta, the decay's gradient and dq, dk of the normalised (and
-// scaled) rows.  Here: clearing what is added up rather than written, the
-// dispatch, and two last elementwise kernels, one carrying dq and dk through
-// the L2 norm and the scale, one applying the chain rule of the raw-gate and
-// raw-beta transforms.
+// gradient, dbeta, the decay's gradient and dq, dk (through the norm and the
+// scale, unless value heads share q/k heads: then of the normalised rows,
+// added up over the group).  Here: clearing what is added up rather than
+// written, the dispatch, and two last elementwise kernels, one carrying
+// grouped heads' dq and dk through the L2 norm and the scale, one applying
+// the chain rule of the raw-gate and raw-beta transforms.
 #include "common.h"
 #include "launch.h"
 
@@ -111,6 +112,19 @@ hipError_t zero(float* p, long n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the transforms' chain rule, if any transform is on
+template <typename In>
+hipError_t tf_bwd(const BwdArgs& a, const In* be, const In* de, long tokh, hipStream_t s) {
+  if (!a.tf.A_log && !a.tf.beta_mode) return hipSuccess;
+  const int W = a.decay_kind == DECAY_CHANNEL ? a.DK : 1;
+  long blocks = (tokh * W + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  tf_bwd_kernel<In><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      be, de, a.dbeta, a.tf.A_log ? a.ddecay : nullptr, a.dA_log, a.tf.dt_bias ? a.ddt_bias : nullptr,
+      a.tf, a.H, W, tokh);
+  return hipGetLastError();
+}
+
 template <typename In>
 hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const long qk = static_cast<long>(a.B) * a.T * a.Hk * a.DK;
@@ -132,20 +146,16 @@ hipError_t dispatch_bwd(const BwdArgs& a, hipStream_t s) {
   const In* de = static_cast<const In*>(a.decay);
   e = launch_bwd_chunked(a, s);
   if (e != hipSuccess) return e;
+  // without grouped heads the chunked kernels have taken the norm's backward
+  if (a.H == a.Hk) return tf_bwd(a, be, de, tokh, s);
   const long rows = static_cast<long>(a.B) * a.T * a.Hk;
   const dim3 g2(static_cast<unsigned>((2 * rows + 3) / 4)), b2(256);
   if (a.DK == 32) norm_bwd_kernel<32, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
   else if (a.DK == 64) norm_bwd_kernel<64, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
   else norm_bwd_kernel<128, In><<<g2, b2, 0, s>>>(q, k, a.dq, a.dk, rows, a.scale, a.l2norm);
   e = hipGetLastError();
-  if (e != hipSuccess || (!a.tf.A_log && !a.tf.beta_mode)) return e;
-  const int W = a.decay_kind == DECAY_CHANNEL ? a.DK : 1;
-  long blocks = (tokh * W + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  tf_bwd_kernel<In><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-      be, de, a.dbeta, a.tf.A_log ? a.ddecay : nullptr, a.dA_log, a.tf.dt_bias ? a.ddt_bias : nullptr,
-      a.tf, a.H, W, tokh);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return tf_bwd(a, be, de, tokh, s);
 }
 
 }  // namespace

@@ -40,9 +40,11 @@
 // reverse: the walk of the state gradient storing each chunk's dS1 and
 // writing dv and the initial state's gradient; (3) per chunk, in parallel:
 // everything else, over the value columns kNS at a time.  (0) and (3) have a
-// per-channel version each; (1) and (2) a per-channel mode.  The q and k
-// gradients are those of the normalised rows; the norm's backward runs after
-// (backward.hip).  All arithmetic is fp32.
+// per-channel version each; (1) and (2) a per-channel mode.  (3) also
+// carries dq and dk through the L2 norm and the scale when every q/k head has
+// one value head; with grouped heads it adds the normalised rows' gradients
+// over the group and a last kernel (backward.hip) takes the norm.  All
+// arithmetic is fp32.
 #include "common.h"
 #include "launch.h"
 
@@ -727,6 +729,8 @@ struct LocalLds {
     struct {
       float dTm[kC][kCP], M[kC][kCP];
       float dPm[kC][kC + 1], EE[kC][kC + 1], PP[kC][kC + 1], Gp[2][kC][kC + 1], dGs[kC][kC + 1];
+      float nd[2][DK / 16][kC];   // the norm's row dots, per 16 key channels
+      float fq[kC], fk[kC];       // the rows' norm factors
     } f;
   } u;
   float tb[kC], tm[kC], tx[kC], tc[kC], sgm[kC], sgx[kC], red[8];
@@ -748,7 +752,8 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
                                                        const In* __restrict__ v, const float* __restrict__ dout,
                                                        float* __restrict__ dq, float* __restrict__ dk,
                                                        float* __restrict__ dbeta, float* __restrict__ ddecay,
-                                                       CWs w, int T, int H, int Hk, int N) {
+                                                       CWs w, int T, int H, int Hk, int N, float scale,
+                                                       int l2norm) {
   constexpr int NT16 = DK / 16;
   constexpr int NQK = 4 * NT16, TPW = (NQK + 7) / 8;              // dq/dk tiles, per wave
   constexpr int SPT = DK * kNS / kThr3;                          // state floats per thread per slice
@@ -950,6 +955,9 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     sm.tb[r] += re;
     sm.tx[r] += tv.bt[r] * re;
     sm.tm[r] += rp - ce - cp;
+    const long ti = (tok0 + min(r, L - 1)) * H + h;
+    Fm.fq[r] = w.sq[ti];
+    Fm.fk[r] = w.sk[ti];
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -957,14 +965,17 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     Fm.dGs[r][c] = Fm.Gp[0][r][c] + Fm.Gp[0][c][r];
   }
   lds_sync();
-  // dq = exp(gam) . (dO S0^T) + Z K;  dk += (dG + dG^T) K + Z^T Q; into the outputs
+  // dq = exp(gam) . (dO S0^T) + Z K;  dk += (dG + dG^T) K + Z^T Q.  Without
+  // grouped heads a row's gradient is whole here: the norm's backward
+  // follows (the row dot with the unit row through LDS); with them the rows
+  // are added up over the group and a last kernel takes the norm.
   const bool grouped = H != Hk;
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int t = wave + 8 * j;
     if (t < NQK) {
       const int mat = t / (2 * NT16), rem = t % (2 * NT16), mt = rem / NT16, nt = rem % NT16;
-      f32x4 a = aqk[j];
+      f32x4& a = aqk[j];
       if (mat == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] *= tv.egm[16 * mt + 4 * lg + e];
@@ -979,13 +990,46 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
         }
       }
       float* out = mat == 0 ? dq : dk;
+      if (grouped) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * mt + 4 * lg + e;
-        if (r < L) {
-          const long o = ((tok0 + r) * Hk + hk) * DK + 16 * nt + li;
-          if (grouped) atomicAdd(out + o, a[e]);
-          else out[o] = a[e];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * lg + e;
+          if (r < L) atomicAdd(out + ((tok0 + r) * Hk + hk) * DK + 16 * nt + li, a[e]);
+        }
+      } else {
+        // unit row: q's normalised row is qh / scale, k's is kh
+        const float xs = l2norm ? (mat == 0 ? 1.f / scale : 1.f) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * lg + e;
+          const float xr = (mat == 0 ? sm.qh[r][16 * nt + li] : sm.kh[r][16 * nt + li]) * xs;
+          const float pd = dpp_group_sum<16>(xr * a[e]);
+          if (li == 0) Fm.nd[mat][nt][r] = pd;
+        }
+      }
+    }
+  }
+  if (!grouped) {
+    lds_sync();
+    // g_raw = f (g - x (x . g)), f the row's norm factor (scale / |x| for q)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + 8 * j;
+      if (t < NQK) {
+        const int mat = t / (2 * NT16), rem = t % (2 * NT16), mt = rem / NT16, nt = rem % NT16;
+        float* out = mat == 0 ? dq : dk;
+        const float xs = l2norm ? (mat == 0 ? 1.f / scale : 1.f) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * lg + e;
+          if (r < L) {
+            float dot = 0.f;
+#pragma unroll
+            for (int u = 0; u < NT16; ++u) dot += Fm.nd[mat][u][r];
+            const float xr = (mat == 0 ? sm.qh[r][16 * nt + li] : sm.kh[r][16 * nt + li]) * xs;
+            const float f = mat == 0 ? Fm.fq[r] : Fm.fk[r];
+            out[((tok0 + r) * Hk + hk) * DK + 16 * nt + li] = f * (aqk[j][e] - xr * dot);
+          }
         }
       }
     }
@@ -1162,6 +1206,8 @@ struct LocalChLds {
       float Wg[kC][DK + 4];               // dgam_r + dgx_{r+1} per channel
       float dbp[DK / 16][kC];             // dbeta parts per 16 channels
       float dgcp[2][DK];                  // dgC parts per row tile
+      float nd[2][DK / 16][kC];           // the norm's row dots, per 16 channels
+      float fq[kC], fk[kC];               // the rows' norm factors
     } f;
   } u;
   float tb[kC], dgs[DK];
@@ -1183,7 +1229,8 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
                                                        const In* __restrict__ v, const float* __restrict__ dout,
                                                        float* __restrict__ dq, float* __restrict__ dk,
                                                        float* __restrict__ dbeta, float* __restrict__ ddecay,
-                                                       CWs w, int T, int H, int Hk, int N) {
+                                                       CWs w, int T, int H, int Hk, int N, float scale,
+                                                       int l2norm) {
   constexpr int NT16 = DK / 16, NPOS = 2 * NT16, PPW = (NPOS + 7) / 8;   // (row tile, channel tile) positions
   constexpr int SPT = DK * kNS / kThr3, SL = kNS / SPT, nsl = DV / kNS;
   __shared__ __align__(16) LocalChLds<DK> sm;
@@ -1314,6 +1361,11 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
   }
   if (en == 0) sm.tb[er] = sb;
   if (tid % SL == 0) sm.dgs[sc] = __expf(sm.gs[L][sc]) * sdc;
+  if (tid < kC) {
+    const long ti = (tok0 + min(tid, L - 1)) * H + h;
+    Fm.fq[tid] = w.sq[ti];
+    Fm.fk[tid] = w.sk[ti];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 16 * tpr + 4 * lg + e, c = 16 * tpc + li;
@@ -1333,9 +1385,10 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
     Fm.dA[r][c] = c < r ? -row_col(sm.TmT[r], Fm.M, c) : 0.f;
   }
   lds_sync();
-  // per position: the pair terms and the gradients
+  // per position: the pair terms and the gradients; without grouped heads
+  // the rows of dq and dk are whole here and the norm's backward follows
   const bool grouped = H != Hk;
-  float dgx[PPW][4];
+  float dgx[PPW][4], oq[PPW][4], ok[PPW][4];
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
     const int pos = wave + 8 * j;
@@ -1399,14 +1452,21 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
         dgx[j][e] = -kr * egx * ax[j][e] + br * kr * G1[e];
         dbe[e] = kr * G1[e];
         dgc += kfa;
-        if (r < L) {
-          const long o = ((tok0 + r) * Hk + hk) * DK + c;
-          if (grouped) {
+        oq[j][e] = dqv;
+        ok[j][e] = dkv;
+        if (grouped) {
+          if (r < L) {
+            const long o = ((tok0 + r) * Hk + hk) * DK + c;
             atomicAdd(dq + o, dqv);
             atomicAdd(dk + o, dkv);
-          } else {
-            dq[o] = dqv;
-            dk[o] = dkv;
+          }
+        } else {
+          // row dots with the unit rows (qh / scale, kh)
+          const float xq = l2norm ? qr / scale : 0.f, xk = l2norm ? kr : 0.f;
+          const float pq = dpp_group_sum<16>(xq * dqv), pk = dpp_group_sum<16>(xk * dkv);
+          if (li == 0) {
+            Fm.nd[0][nt][r] = pq;
+            Fm.nd[1][nt][r] = pk;
           }
         }
       }
@@ -1421,7 +1481,8 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
     }
   }
   lds_sync();
-  // dgx_{r+1} into row r of Wg (its own element: one adder per element)
+  // dgx_{r+1} into row r of Wg (its own element: one adder per element); the
+  // norm's backward g_raw = f (g - x (x . g)) and the stores
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
     const int pos = wave + 8 * j;
@@ -1431,6 +1492,18 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * mt + 4 * lg + e;
         if (r >= 1) Fm.Wg[r - 1][c] += dgx[j][e];
+        if (!grouped && r < L) {
+          float dq_dot = 0.f, dk_dot = 0.f;
+#pragma unroll
+          for (int u = 0; u < NT16; ++u) {
+            dq_dot += Fm.nd[0][u][r];
+            dk_dot += Fm.nd[1][u][r];
+          }
+          const float xq = l2norm ? sm.qh[r][c] / scale : 0.f, xk = l2norm ? sm.kh[r][c] : 0.f;
+          const long o = ((tok0 + r) * Hk + hk) * DK + c;
+          dq[o] = Fm.fq[r] * (oq[j][e] - xq * dq_dot);
+          dk[o] = Fm.fk[r] * (ok[j][e] - xk * dk_dot);
+        }
       }
     }
   }
@@ -1469,7 +1542,8 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
     cbwd_rev<DK, DV, In, true><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
                                                                    a.H, a.Hk, N, a.vfirst);
     cbwd_local_ch<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(q, k, v, a.dout, a.dq, a.dk, a.dbeta,
-                                                                    a.ddecay, w, a.T, a.H, a.Hk, N);
+                                                                    a.ddecay, w, a.T, a.H, a.Hk, N, a.scale,
+                                                                    a.l2norm);
     return hipGetLastError();
   }
   cbwd_prep<DK, In><<<dim3(chunks), dim3(kThr), 0, s>>>(q, k, be, de, a.decay_kind == DECAY_HEAD, w, a.T, a.H,
@@ -1478,7 +1552,8 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
   cbwd_rev<DK, DV, In, false><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
                                                                   a.H, a.Hk, N, a.vfirst);
   cbwd_local<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(
-      q, k, v, a.dout, a.dq, a.dk, a.dbeta, a.decay_kind == DECAY_HEAD ? a.ddecay : nullptr, w, a.T, a.H, a.Hk, N);
+      q, k, v, a.dout, a.dq, a.dk, a.dbeta, a.decay_kind == DECAY_HEAD ? a.ddecay : nullptr, w, a.T, a.H, a.Hk, N,
+      a.scale, a.l2norm);
   return hipGetLastError();
 }
 

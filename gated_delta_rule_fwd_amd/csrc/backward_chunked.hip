@@ -738,8 +738,9 @@ struct LocalLds {
 };
 
 // (3) per (b, h, chunk): the remaining gradients over the value columns, 16
-// at a time: dq and dk of the normalised rows (added: value heads of a group
-// share their q/k head), dbeta and the decay's gradient (written).  Eight
+// at a time: dq and dk (through the norm and the scale; with grouped value
+// heads those of the normalised rows, added up over the group), dbeta and the
+// decay's gradient (written).  Eight
 // waves, two workgroups per CU.  Per slice: K S0, Q S0 and K dS1 on MFMA
 // (one product's row tile per wave, waves 0-5); X, D, dD, dY and the
 // per-token sums on VALU, one (row, column) element per thread; then on
@@ -1214,16 +1215,17 @@ struct LocalChLds {
   TokVec tv;
 };
 
-// (3) per-channel decay, per (b, h, chunk): dq, dk (normalised rows),
-// dbeta and the per-channel decay's gradient.  Per slice of 16 value
+// (3) per-channel decay, per (b, h, chunk): dq, dk (as in the per-head
+// kernel), dbeta and the per-channel decay's gradient.  Per slice of 16 value
 // columns: X = V - (k exp(gx)) S0 and K dS1 with F folded in, on MFMA (one
 // row tile per wave, waves 0-3); D, dD, dY on VALU; then the running sums
 // dT, dP (a tile per wave) and, per (row, channel) position held by a wave,
 // dO S0^T, dX S0^T and D dS1^T.  Then dA; then, at each position, the
-// in-chunk pair terms with their own exponentials (sums over the partner
-// token u of dA or dP times k or q and exp of a difference of gam, never
-// positive), and the gradients from them and the three sums.  The decay's
-// gradient is a reverse running sum down the tokens per channel.
+// in-chunk pair terms (sums over the partner token u of dA or dP times k or
+// q and the decay factor between u and the row, a product of per-token
+// factors exp(g) <= 1 carried down or up the partners), and the gradients
+// from them and the three sums.  The decay's gradient is a reverse running
+// sum down the tokens per channel.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q, const In* __restrict__ k,
                                                        const In* __restrict__ v, const float* __restrict__ dout,

@@ -1137,32 +1137,59 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
   }
   lds_sync();
   const size_t cb = (static_cast<size_t>(bh) * N + ci) * kC * kC;
-  // the 528 pairs s <= r of the chunk, one per thread and pass
-  for (int idx = tid; idx < kC * (kC + 1) / 2; idx += kThr) {
-    int r = static_cast<int>((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
-    if ((r + 1) * (r + 2) / 2 <= idx) ++r;
-    if (r * (r + 1) / 2 > idx) --r;
-    const int s = idx - r * (r + 1) / 2;
-    float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+  // Entries s <= r.  Token s of the first 16 against token r of the last 16:
+  // exp(gx_r - gam_s) = exp(gx_r - gam_15) exp(gam_15 - gam_s) and
+  // exp(gam_r - gam_s) = exp(gam_r - gam_15) exp(gam_15 - gam_s), each factor
+  // <= 1, so that block is a product of decayed rows on MFMA (wave 0, A and
+  // P together).  The two diagonal blocks' 136 pairs each: one pair per
+  // thread of the other waves, the channel sum with its own factors.
+  if (tid < 64) {
+    const int li = tid & 15, lg = tid >> 4;
+    f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = aa;
 #pragma unroll 4
-    for (int c = 0; c < DK; c += 4) {
-      const f32x4 kr = *reinterpret_cast<const f32x4*>(&kh[r][c]);
-      const f32x4 ks = *reinterpret_cast<const f32x4*>(&kh[s][c]);
-      const f32x4 qr = *reinterpret_cast<const f32x4*>(&qh[r][c]);
-      const f32x4 gx = *reinterpret_cast<const f32x4*>(&gs[r][c]);
-      const f32x4 gr = *reinterpret_cast<const f32x4*>(&gs[r + 1][c]);
-      const f32x4 gsv = *reinterpret_cast<const f32x4*>(&gs[s + 1][c]);
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        p0 += qr[e] * ks[e] * __expf(gr[e] - gsv[e]);
-        p1 += qr[e + 1] * ks[e + 1] * __expf(gr[e + 1] - gsv[e + 1]);
-        // exp(gx_r - gam_s) <= 1 only for s < r: masked below
-        a0 += kr[e] * ks[e] * __expf(fminf(gx[e] - gsv[e], 0.f));
-        a1 += kr[e + 1] * ks[e + 1] * __expf(fminf(gx[e + 1] - gsv[e + 1], 0.f));
-      }
+    for (int ks = 0; ks < DK / 4; ++ks) {
+      const int c = 4 * ks + lg;
+      const float g15 = gs[16][c];
+      const float bk = kh[li][c] * __expf(g15 - gs[li + 1][c]);                 // k_s exp(gam_15 - gam_s)
+      const float ak = kh[16 + li][c] * __expf(gs[16 + li][c] - g15);           // k_r exp(gx_r - gam_15)
+      const float aq = qh[16 + li][c] * __expf(gs[17 + li][c] - g15);           // q_r exp(gam_r - gam_15)
+      aa = mma4(ak, bk, aa);
+      pa = mma4(aq, bk, pa);
     }
-    sA[r][s] = s < r ? sbt[r] * (a0 + a1) : 0.f;
-    w.Pm[cb + r * kC + s] = p0 + p1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 + 4 * lg + e, s2 = li;
+      sA[r][s2] = sbt[r] * aa[e];
+      w.Pm[cb + r * kC + s2] = pa[e];
+    }
+  } else {
+    for (int idx = tid - 64; idx < 2 * 136; idx += kThr - 64) {
+      const int blk = idx / 136, id = idx % 136;
+      int rl = static_cast<int>((sqrtf(8.f * id + 1.f) - 1.f) * 0.5f);
+      if ((rl + 1) * (rl + 2) / 2 <= id) ++rl;
+      if (rl * (rl + 1) / 2 > id) --rl;
+      const int r = 16 * blk + rl, s = 16 * blk + id - rl * (rl + 1) / 2;
+      float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < DK; c += 4) {
+        const f32x4 kr = *reinterpret_cast<const f32x4*>(&kh[r][c]);
+        const f32x4 ks = *reinterpret_cast<const f32x4*>(&kh[s][c]);
+        const f32x4 qr = *reinterpret_cast<const f32x4*>(&qh[r][c]);
+        const f32x4 gx = *reinterpret_cast<const f32x4*>(&gs[r][c]);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&gs[r + 1][c]);
+        const f32x4 gsv = *reinterpret_cast<const f32x4*>(&gs[s + 1][c]);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          p0 += qr[e] * ks[e] * __expf(gr[e] - gsv[e]);
+          p1 += qr[e + 1] * ks[e + 1] * __expf(gr[e + 1] - gsv[e + 1]);
+          // exp(gx_r - gam_s) <= 1 only for s < r: masked below
+          a0 += kr[e] * ks[e] * __expf(fminf(gx[e] - gsv[e], 0.f));
+          a1 += kr[e + 1] * ks[e + 1] * __expf(fminf(gx[e + 1] - gsv[e + 1], 0.f));
+        }
+      }
+      sA[r][s] = s < r ? sbt[r] * (a0 + a1) : 0.f;
+      w.Pm[cb + r * kC + s] = p0 + p1;
+    }
   }
   // the upper triangles: zeros
   for (int idx = tid; idx < kC * kC; idx += kThr) {

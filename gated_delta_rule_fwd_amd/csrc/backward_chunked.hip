@@ -1435,11 +1435,48 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
       // factors a_t = exp(g_t) <= 1 strictly between or up to them, carried
       // down (u < r) and up (u > r) the partner tokens: no exponential per
       // pair, no factor above one.
+      // Partners in the other 16-token block: a product on MFMA, the decay
+      // split at token 15 into two factors <= 1 (exp(gx_r - gam_u) =
+      // exp(gx_r - gam_15) exp(gam_15 - gam_u), and so on), one on the
+      // partner's row, one applied to the result.
+      if (mt == 1) {
+        f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, h1 = g1;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int u = 4 * ks + lg;
+          const float b0 = sm.kh[u][c] * __expf(sm.gs[16][c] - sm.gs[u + 1][c]);   // k_u exp(gam_15 - gam_u)
+          g1 = mma4(Fm.dA[16 + li][u], b0, g1);
+          h1 = mma4(Fm.dPm[16 + li][u], b0, h1);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 + 4 * lg + e;
+          G1[e] += g1[e] * __expf(sm.gs[r][c] - sm.gs[16][c]);
+          H1[e] += h1[e] * __expf(sm.gs[r + 1][c] - sm.gs[16][c]);
+        }
+      } else {
+        f32x4 g2 = {0.f, 0.f, 0.f, 0.f}, h2 = g2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int u = 16 + 4 * ks + lg;
+          const float bk = tv.bt[u] * sm.kh[u][c] * __expf(sm.gs[u][c] - sm.gs[16][c]);   // exp(gx_u - gam_15)
+          const float bq = sm.qh[u][c] * __expf(sm.gs[u + 1][c] - sm.gs[16][c]);          // exp(gam_u - gam_15)
+          g2 = mma4(Fm.dA[u][li], bk, g2);
+          h2 = mma4(Fm.dPm[u][li], bq, h2);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = __expf(sm.gs[16][c] - sm.gs[4 * lg + e + 1][c]);   // exp(gam_15 - gam_r)
+          G2[e] += g2[e] * f;
+          H2[e] += h2[e] * f;
+        }
+      }
+      // partners in the row's own block: running products
       {
         float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
         // rows 16 mt .. 16 mt + 15: partners u <= r start at the tile's last row
 #pragma unroll 8
-        for (int uu = 16 * mt + 15; uu >= 0; --uu) {
+        for (int uu = 16 * mt + 15; uu >= 16 * mt; --uu) {
           const float ku = sm.kh[uu][c], an = sm.kx[min(uu + 1, kC - 1)][c];   // a_{u+1}
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1455,7 +1492,7 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
         float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
         // partners u >= r start at the tile's first row
 #pragma unroll 8
-        for (int uu = 16 * mt; uu < kC; ++uu) {
+        for (int uu = 16 * mt; uu < 16 * mt + 16; ++uu) {
           const float ku = sm.kh[uu][c], qu = sm.qh[uu][c], bu = tv.bt[uu];
           const float ap = sm.kx[max(uu - 1, 0)][c], au = sm.kx[uu][c];   // a_{u-1}, a_u
 #pragma unroll

@@ -33,7 +33,11 @@
 // rounded once to fp16; derived operands rounded once to fp16) and
 // v_mfma_f32_16x16x4_f32 for fp32 activations.  The inverse is built in fp32.
 //
-// Per-key-channel decay uses products of per-token factors exp(g) <= 1 only,
+// Per-key-channel decay.  A chunk whose every 4-token quarter decays by at
+// most e^-3 in every channel (mild decay) takes each 16-token block's
+// operands referenced to its middle token, within e^6 of the row, and one
+// product per block pair.  Any other chunk takes the exact path, which uses
+// products of per-token factors exp(g) <= 1 only,
 // so no operand exceeds the normalised row it scales, whatever the decay
 // (exp(g) may underflow to 0: the products it belongs to are then 0, as
 // they should be to well below fp16 resolution).  A Gram entry of tokens
@@ -112,6 +116,12 @@ template <> struct Mma<_Float16> {
       f[e] = (T)(static_cast<float>(f[e]) * (a * b));
     }
   }
+  // times fn(k) per k, rounded once
+  template <typename Fn>
+  __device__ static void scale_fn(frag& f, int k0, int g, Fn&& fn) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (T)(static_cast<float>(f[e]) * fn(k0 + 8 * g + e));
+  }
   __device__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
 };
 
@@ -149,6 +159,14 @@ template <> struct Mma<float> {
       const float a1 = u1 ? v1[k0 + 16 + 4 * g + e] : 1.f, b1 = u2 ? v2[k0 + 16 + 4 * g + e] : 1.f;
       f.lo[e] *= a0 * b0;
       f.hi[e] *= a1 * b1;
+    }
+  }
+  template <typename Fn>
+  __device__ static void scale_fn(frag& f, int k0, int g, Fn&& fn) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.lo[e] *= fn(k0 + 4 * g + e);
+      f.hi[e] *= fn(k0 + 16 + 4 * g + e);
     }
   }
   __device__ static frag zero() { return frag{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
@@ -319,6 +337,8 @@ __device__ __forceinline__ void put_perm(unsigned char* tile, int r, int e0, con
 // Eight waves per workgroup: the chunk's work is short, so more waves hide
 // the LDS and HBM latencies of its dependent phases.
 constexpr int kPrepThreads = 512;
+// Per-channel decay: the mild path's bound on a 4-token quarter's log decay
+constexpr float kMildQuarterLog = 3.f;
 constexpr int kPrepWaves = kPrepThreads / 64;
 
 // Waves per SIMD of the prep kernel: two 8-wave workgroups share a CU with
@@ -386,9 +406,13 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   float* s_qk = sv + 3 * C;                    // per-channel decay: q_hat . k_hat per token;
   float* s_fk = s_qk;                          // raw K: the row factor of k
   float* s_misc = sv + 4 * C;
+  int* s_steep = reinterpret_cast<int*>(s_misc);   // per-channel decay: a quarter decays by more than e^-3
   float* s_tau4 = s_misc + 16;                 // [NQ][DK] decay factor of each 4-token quarter
+                                               // (first its log, the quarter's gate sum)
   float* s_wq = s_tau4 + L::NQ * DK;           // [NQ][12] within-quarter Gram sums (A, then P)
   float* s_D = s_wq;                           // [NDD][DK] decay between blocks i, j (i - j >= 2), later
+  float* s_mb = s_wq;                          // mild decay: [NB][DK] log decay from the chunk start
+                                               // to the middle of block b
 
   const In* gq = static_cast<const In*>(p.q);
   const In* gk = static_cast<const In*>(p.k);
@@ -482,6 +506,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         }
       }
     }
+    if (chan && tid == 0) *s_steep = 0;
     if (wave == 0) {
       // the scalar gate: lane r holds token r of the chunk (C <= 64)
 #pragma unroll
@@ -526,11 +551,12 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   // lower); P (lower, inclusive) goes straight to the record, the state
   // kernel being its only reader.  wq: per-channel decay, the within-quarter
   // sums of a diagonal block (s and r in one quarter), added here.
+  bool mild = false;   // per-channel decay on the mild path: no within-quarter sums
   auto emit = [&](int i, int j, bool isP, const f32x4& acc) {
     const int r = 16 * i + l16, s0 = 16 * j + 4 * g;
     const f32x4 gs = *reinterpret_cast<const f32x4*>(s_Gi + s0);
     // same quarter (diagonal blocks of per-channel decay): local rows rl, jj
-    const bool sameq = chan && i == j && (l16 >> 2) == g;
+    const bool sameq = chan && !mild && i == j && (l16 >> 2) == g;
     const int rl = l16 & 3;
     const float* wq = s_wq + (4 * i + g) * L::kWQ + (isP ? 6 : 0) + rl * (rl - 1) / 2;
     if (!isP) {
@@ -582,9 +608,8 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       emit(i, j, isP, acc);
     }
   } else {
-    // Per-key-channel decay: products of exp(g) <= 1 only (see the top of
-    // this file).  Quarter Q holds tokens 4Q .. 4Q+3; LPQ lanes share a
-    // quarter, CPT consecutive channels each.
+    // Per-key-channel decay.  Quarter Q holds tokens 4Q .. 4Q+3; LPQ lanes
+    // share a quarter, CPT consecutive channels each.
     constexpr int NQ = L::NQ;
     constexpr int LPQ = (kPrepThreads / NQ < DK ? kPrepThreads / NQ : DK) < 64
                             ? (kPrepThreads / NQ < DK ? kPrepThreads / NQ : DK) : 64;
@@ -592,211 +617,336 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     static_assert(LPQ >= 4 && CPT * LPQ == DK && NQ * LPQ <= kPrepThreads, "quarter lanes");
     const int Q = tid / LPQ, c0 = (tid % LPQ) * CPT;
     const bool qt = tid < NQ * LPQ;   // this thread has a (quarter, channel group)
-
-    // (1b) per quarter and channel: the quarter's decay products.  k times
-    // the decay from the quarter start to the token before (Ka) and q times
-    // it through the token (Qa) replace k and q; k decayed to the quarter
-    // end goes to KB; tau4 is the whole quarter's factor.  The sums over
-    // channels of the 6 within-quarter pairs of A and of P are formed here.
     // this thread's CPT channels of one row, as one LDS access
     typedef OpT opv __attribute__((ext_vector_type(CPT)));
     typedef float f32v __attribute__((ext_vector_type(CPT)));
+
+    // (1a) per quarter and channel: the gate's running sum over the quarter
+    // (kept in registers) and the quarter's sum (to LDS).  A quarter whose
+    // decay exceeds e^-3 in any channel sends the chunk down the exact path.
+    f32v lp[4];
     if (qt) {
-      float w[12];
-#pragma unroll
-      for (int x = 0; x < 12; ++x) w[x] = 0.f;
-      opv gv[4], kv[4], qv[4];
+      f32v run = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int r = 4 * Q + t;
-        gv[t] = *reinterpret_cast<const opv*>(sGst + r * DK + c0);
-        kv[t] = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
-        qv[t] = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+        const opv gv = *reinterpret_cast<const opv*>(sGst + (4 * Q + t) * DK + c0);
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) run[e] += static_cast<float>(gv[e]);
+        lp[t] = run;
       }
-      opv ka[4], qa[4], kb[4];
-      f32v tau;
+      *reinterpret_cast<f32v*>(s_tau4 + Q * DK + c0) = run;
+      bool steep = false;
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        float a[4], kx[4], qx[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          a[t] = __expf(static_cast<float>(gv[t][e]));
-          kx[t] = static_cast<float>(kv[t][e]);
-          qx[t] = static_cast<float>(qv[t][e]);
-        }
-        float pre = 1.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ka[t][e] = (OpT)(kx[t] * pre);
-          pre *= a[t];
-          qa[t][e] = (OpT)(qx[t] * pre);
-        }
-        float suf = 1.f;
-#pragma unroll
-        for (int t = 3; t >= 0; --t) {
-          kb[t][e] = (OpT)(kx[t] * suf);
-          suf *= a[t];
-        }
-        tau[e] = pre;
-        // A_rs: decay of s+1 .. r-1; P_rs: of s+1 .. r  (pairs 10 20 21 30 31 32)
-        const float a12 = a[1] * a[2], a23 = a[2] * a[3];
-        w[0] += kx[1] * kx[0];
-        w[1] += kx[2] * kx[0] * a[1];
-        w[2] += kx[2] * kx[1];
-        w[3] += kx[3] * kx[0] * a12;
-        w[4] += kx[3] * kx[1] * a[2];
-        w[5] += kx[3] * kx[2];
-        w[6] += qx[1] * kx[0] * a[1];
-        w[7] += qx[2] * kx[0] * a12;
-        w[8] += qx[2] * kx[1] * a[2];
-        w[9] += qx[3] * kx[0] * (a12 * a[3]);
-        w[10] += qx[3] * kx[1] * a23;
-        w[11] += qx[3] * kx[2] * a[3];
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * Q + t;
-        *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka[t];
-        *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa[t];
-        *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb[t];
-      }
-      *reinterpret_cast<f32v*>(s_tau4 + Q * DK + c0) = tau;
-#pragma unroll
-      for (int x = 0; x < 12; ++x) w[x] = dpp_group_sum<LPQ>(w[x]);
-      if (c0 == 0) {
-#pragma unroll
-        for (int x = 0; x < 12; ++x) s_wq[Q * L::kWQ + x] = w[x];
-      }
+      for (int e = 0; e < CPT; ++e) steep |= !(run[e] >= -kMildQuarterLog);
+      if (steep) *s_steep = 1;
     }
     lds_barrier();
+    // the mild path's operands reach e^6 times a row: within fp16 for unit
+    // rows and a q factor up to 4
+    mild = *s_steep == 0 && (sizeof(OpT) == 4 || (p.l2norm && p.scale <= 4.f));
 
-    // (2a) diagonal blocks: one pass per column quarter S = 0, 1, 2.  Pass S
-    // takes the columns of quarter S (k decayed to its end, KB) against the
-    // rows of the later quarters R (Ka or Qa) times the decay of the
-    // quarters strictly between S and R; the other rows and columns are zero,
-    // so the passes add up in one accumulator.
-    for (int job = wave; job < 2 * NB; job += kPrepWaves) {
-      const bool isP = job >= NB;
-      const int i = isP ? job - NB : job;
-      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
-      const OpT* krow = sKB + (16 * i + l16) * L::LDK;
-      const int Rq = l16 >> 2;      // this lane's row quarter and column quarter
-      f32x4 acc = {0, 0, 0, 0};
-      static_for<3>([&](auto S_) {
-        constexpr int S = decltype(S_)::value;
-        const float* t1 = s_tau4 + (4 * i + S + 1) * DK;
-        const float* t2 = s_tau4 + (4 * i + (S + 2 < 4 ? S + 2 : 3)) * DK;
+    if (mild) {
+      // Mild decay (every quarter's decay at least e^-3 in every channel, so
+      // every half block's at least e^-6): the operands of a 16-token block b
+      // are referenced to its middle, M_b = G at token 16 b + 7, so that one
+      // product per block pair gives A and P.  Rows k exp(Gx - M_b) and
+      // q exp(G - M_b) replace k and q, columns k exp(M_b - G) go to KB; all
+      // lie within e^6 of the row.  Between blocks i > j the rows take the
+      // fp32 scale exp(M_i - M_j) <= 1.
+      if (qt) {
+        const int blk = Q >> 2;
+        f32v gq = 0.f, mb = 0.f, tot = 0.f;
 #pragma unroll
-        for (int m = 0; m < NKP; ++m) {
-          typename M::frag fk = Rq == S ? M::ld_cont(krow, 32 * m, g) : M::zero();
-          typename M::frag fa = Rq > S ? M::ld_cont(arow, 32 * m, g) : M::zero();
-          if constexpr (S < 2) M::scale_cont2(fa, t1, Rq >= S + 2, t2, S < 1 && Rq >= S + 3, 32 * m, g);
-          M::mma(acc, fk, fa);
+        for (int q2 = 0; q2 < NQ; ++q2) {
+          const f32v sq = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
+          tot += sq;
+          if (q2 < Q) gq += sq;
+          if (q2 < 4 * blk + 2) mb += sq;
         }
-      });
-      emit(i, i, isP, acc);
-    }
-    lds_barrier();
-
-    // (2b) from quarters to blocks: Ka, Qa times the decay of the earlier
-    // quarters of their block, KB times that of the later ones; the record's
-    // chunk-referenced operands K = k exp(Gx), Q = q exp(G) and
-    // F = k exp(G_last - G); exp(G_last) per channel; and D, the decay of the
-    // blocks strictly between two blocks i - j >= 2 apart.
-    if (qt) {
-      const int blk = Q >> 2;
-      f32v t16[NB], cqp = 1.f, cqs = 1.f;
-#pragma unroll
-      for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
-#pragma unroll
-      for (int q2 = 0; q2 < NQ; ++q2) {
-        const f32v t = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
-        t16[q2 >> 2] *= t;
-        if ((q2 >> 2) == blk && q2 < Q) cqp *= t;
-        if ((q2 >> 2) == blk && q2 > Q) cqs *= t;
-      }
-      f32v cb = 1.f, ca = 1.f, all = 1.f;
-#pragma unroll
-      for (int b2 = 0; b2 < NB; ++b2) {
-        if (b2 < blk) cb *= t16[b2];
-        if (b2 > blk) ca *= t16[b2];
-        all *= t16[b2];
-      }
-      if (Q == 0) {
-        *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
-#pragma unroll
-        for (int i2 = 2; i2 < NB; ++i2) {
-          f32v dd = 1.f;
-#pragma unroll
-          for (int j2 = i2 - 2; j2 >= 0; --j2) {
-            dd *= t16[j2 + 1];
-            *reinterpret_cast<f32v*>(s_D + L::ddslot(i2, j2) * DK + c0) = dd;
-          }
-        }
-      }
-      // (s_D overlays the within-quarter sums, whose last reader was (2a))
-      const f32v fkq = cqp * cb, ff = cqs * ca;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * Q + t;
-        const opv ka = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
-        const opv qa = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
-        const opv kb = *reinterpret_cast<const opv*>(sKB + r * L::LDK + c0);
-        opv ka16, qa16, kb16;
-        float xk[CPT], xq[CPT], xf[CPT];
+        f32v emb, ef;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
-          const float k1 = static_cast<float>(ka[e]), q1 = static_cast<float>(qa[e]);
-          const float b1 = static_cast<float>(kb[e]);
-          ka16[e] = (OpT)(k1 * cqp[e]);
-          qa16[e] = (OpT)(q1 * cqp[e]);
-          kb16[e] = (OpT)(b1 * cqs[e]);
-          xk[e] = k1 * fkq[e];
-          xq[e] = q1 * fkq[e];
-          xf[e] = b1 * ff[e];
+          emb[e] = __expf(mb[e]);            // the record's chunk reference: exp(M_b)
+          ef[e] = __expf(tot[e] - mb[e]);    // exp(G_last - M_b)
         }
-        *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka16;
-        *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa16;
-        *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb16;
-        if constexpr (CPT % 4 == 0) {
-          put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
-          put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);
-          put_perm<OpT, R::PPRK>(rec + R::oF, r, c0, xf);
-        } else {
+        if ((Q & 3) == 0) *reinterpret_cast<f32v*>(s_mb + blk * DK + c0) = mb;
+        if (Q == 0) {
+          f32v all;
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) all[e] = __expf(tot[e]);
+          *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          const opv kv = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
+          const opv qv = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+          opv rk, rq, rb;
+          float xk[CPT], xq[CPT], xf[CPT];
 #pragma unroll
           for (int e = 0; e < CPT; ++e) {
-            const int off = swz_off<R::PPRK>(r, perm_pos(c0 + e) * static_cast<int>(sizeof(OpT)));
-            *reinterpret_cast<OpT*>(rec + R::oK + off) = (OpT)xk[e];
-            *reinterpret_cast<OpT*>(rec + R::oQ + off) = (OpT)xq[e];
-            *reinterpret_cast<OpT*>(rec + R::oF + off) = (OpT)xf[e];
+            const float gr = gq[e] + lp[t][e], grx = t > 0 ? gq[e] + lp[t > 0 ? t - 1 : 0][e] : gq[e];
+            const float fk = __expf(grx - mb[e]), fq = __expf(gr - mb[e]), fb = __expf(mb[e] - gr);
+            const float k1 = static_cast<float>(kv[e]), q1 = static_cast<float>(qv[e]);
+            rk[e] = (OpT)(k1 * fk);
+            rq[e] = (OpT)(q1 * fq);
+            rb[e] = (OpT)(k1 * fb);
+            xk[e] = k1 * fk * emb[e];
+            xq[e] = q1 * fq * emb[e];
+            xf[e] = k1 * fb * ef[e];
+          }
+          *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = rk;
+          *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = rq;
+          *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = rb;
+          if constexpr (CPT % 4 == 0) {
+            put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
+            put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);
+            put_perm<OpT, R::PPRK>(rec + R::oF, r, c0, xf);
+          } else {
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+              const int off = swz_off<R::PPRK>(r, perm_pos(c0 + e) * static_cast<int>(sizeof(OpT)));
+              *reinterpret_cast<OpT*>(rec + R::oK + off) = (OpT)xk[e];
+              *reinterpret_cast<OpT*>(rec + R::oQ + off) = (OpT)xq[e];
+              *reinterpret_cast<OpT*>(rec + R::oF + off) = (OpT)xf[e];
+            }
           }
         }
       }
-    }
-    lds_barrier();
-
-    // (2c) off-diagonal blocks i > j: the rows decayed from their block's
-    // start (Ka, Qa) times D, against k decayed to the end of block j (KB)
-    constexpr int NOFF = NB * (NB - 1) / 2;
-    for (int job = wave; job < 2 * NOFF; job += kPrepWaves) {
-      const bool isP = job >= NOFF;
-      const int pr = isP ? job - NOFF : job;
-      const int i = pair_i(pr) + 1, j = pair_j(pr);    // pairs of the strictly lower triangle
-      const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
-      const OpT* krow = sKB + (16 * j + l16) * L::LDK;
-      const float* dv = s_D + L::ddslot(i > j + 1 ? i : 2, i > j + 1 ? j : 0) * DK;
-      f32x4 acc = {0, 0, 0, 0};
+      lds_barrier();
+      // every block pair i >= j, A then P on the diagonal, then below it
+      constexpr int NOFF = NB * (NB - 1) / 2;
+      for (int job = wave; job < 2 * NB + 2 * NOFF; job += kPrepWaves) {
+        bool isP;
+        int i, j;
+        if (job < 2 * NB) {
+          isP = job >= NB;
+          i = j = isP ? job - NB : job;
+        } else {
+          const int o = job - 2 * NB;
+          isP = o >= NOFF;
+          const int pr = isP ? o - NOFF : o;
+          i = pair_i(pr) + 1;
+          j = pair_j(pr);
+        }
+        const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+        const OpT* krow = sKB + (16 * j + l16) * L::LDK;
+        f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int m = 0; m < NKP; ++m) {
-        auto fa = M::ld_cont(arow, 32 * m, g);
-        if (i > j + 1) M::scale_cont(fa, dv, 32 * m, g);
-        M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
+        for (int m = 0; m < NKP; ++m) {
+          auto fa = M::ld_cont(arow, 32 * m, g);
+          if (i > j) {
+            const float* mi = s_mb + i * DK;
+            const float* mj = s_mb + j * DK;
+            M::scale_fn(fa, 32 * m, g, [&](int c) { return __expf(mi[c] - mj[c]); });
+          }
+          M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
+        }
+        emit(i, j, isP, acc);
       }
-      emit(i, j, isP, acc);
+    } else {
+      // Exact path: products of exp(g) <= 1 only (see the top of this file).
+      // (1b) per quarter and channel: the quarter's decay products.  k times
+      // the decay from the quarter start to the token before (Ka) and q times
+      // it through the token (Qa) replace k and q; k decayed to the quarter
+      // end goes to KB; tau4 is the whole quarter's factor.  The sums over
+      // channels of the 6 within-quarter pairs of A and of P are formed here.
+      if (qt) {
+        float w[12];
+  #pragma unroll
+        for (int x = 0; x < 12; ++x) w[x] = 0.f;
+        opv gv[4], kv[4], qv[4];
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          gv[t] = *reinterpret_cast<const opv*>(sGst + r * DK + c0);
+          kv[t] = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
+          qv[t] = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+        }
+        opv ka[4], qa[4], kb[4];
+        f32v tau;
+  #pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          float a[4], kx[4], qx[4];
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            a[t] = __expf(static_cast<float>(gv[t][e]));
+            kx[t] = static_cast<float>(kv[t][e]);
+            qx[t] = static_cast<float>(qv[t][e]);
+          }
+          float pre = 1.f;
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            ka[t][e] = (OpT)(kx[t] * pre);
+            pre *= a[t];
+            qa[t][e] = (OpT)(qx[t] * pre);
+          }
+          float suf = 1.f;
+  #pragma unroll
+          for (int t = 3; t >= 0; --t) {
+            kb[t][e] = (OpT)(kx[t] * suf);
+            suf *= a[t];
+          }
+          tau[e] = pre;
+          // A_rs: decay of s+1 .. r-1; P_rs: of s+1 .. r  (pairs 10 20 21 30 31 32)
+          const float a12 = a[1] * a[2], a23 = a[2] * a[3];
+          w[0] += kx[1] * kx[0];
+          w[1] += kx[2] * kx[0] * a[1];
+          w[2] += kx[2] * kx[1];
+          w[3] += kx[3] * kx[0] * a12;
+          w[4] += kx[3] * kx[1] * a[2];
+          w[5] += kx[3] * kx[2];
+          w[6] += qx[1] * kx[0] * a[1];
+          w[7] += qx[2] * kx[0] * a12;
+          w[8] += qx[2] * kx[1] * a[2];
+          w[9] += qx[3] * kx[0] * (a12 * a[3]);
+          w[10] += qx[3] * kx[1] * a23;
+          w[11] += qx[3] * kx[2] * a[3];
+        }
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka[t];
+          *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa[t];
+          *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb[t];
+        }
+        *reinterpret_cast<f32v*>(s_tau4 + Q * DK + c0) = tau;
+  #pragma unroll
+        for (int x = 0; x < 12; ++x) w[x] = dpp_group_sum<LPQ>(w[x]);
+        if (c0 == 0) {
+  #pragma unroll
+          for (int x = 0; x < 12; ++x) s_wq[Q * L::kWQ + x] = w[x];
+        }
+      }
+      lds_barrier();
+
+      // (2a) diagonal blocks: one pass per column quarter S = 0, 1, 2.  Pass S
+      // takes the columns of quarter S (k decayed to its end, KB) against the
+      // rows of the later quarters R (Ka or Qa) times the decay of the
+      // quarters strictly between S and R; the other rows and columns are zero,
+      // so the passes add up in one accumulator.
+      for (int job = wave; job < 2 * NB; job += kPrepWaves) {
+        const bool isP = job >= NB;
+        const int i = isP ? job - NB : job;
+        const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+        const OpT* krow = sKB + (16 * i + l16) * L::LDK;
+        const int Rq = l16 >> 2;      // this lane's row quarter and column quarter
+        f32x4 acc = {0, 0, 0, 0};
+        static_for<3>([&](auto S_) {
+          constexpr int S = decltype(S_)::value;
+          const float* t1 = s_tau4 + (4 * i + S + 1) * DK;
+          const float* t2 = s_tau4 + (4 * i + (S + 2 < 4 ? S + 2 : 3)) * DK;
+  #pragma unroll
+          for (int m = 0; m < NKP; ++m) {
+            typename M::frag fk = Rq == S ? M::ld_cont(krow, 32 * m, g) : M::zero();
+            typename M::frag fa = Rq > S ? M::ld_cont(arow, 32 * m, g) : M::zero();
+            if constexpr (S < 2) M::scale_cont2(fa, t1, Rq >= S + 2, t2, S < 1 && Rq >= S + 3, 32 * m, g);
+            M::mma(acc, fk, fa);
+          }
+        });
+        emit(i, i, isP, acc);
+      }
+      lds_barrier();
+
+      // (2b) from quarters to blocks: Ka, Qa times the decay of the earlier
+      // quarters of their block, KB times that of the later ones; the record's
+      // chunk-referenced operands K = k exp(Gx), Q = q exp(G) and
+      // F = k exp(G_last - G); exp(G_last) per channel; and D, the decay of the
+      // blocks strictly between two blocks i - j >= 2 apart.
+      if (qt) {
+        const int blk = Q >> 2;
+        f32v t16[NB], cqp = 1.f, cqs = 1.f;
+  #pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
+  #pragma unroll
+        for (int q2 = 0; q2 < NQ; ++q2) {
+          const f32v t = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
+          t16[q2 >> 2] *= t;
+          if ((q2 >> 2) == blk && q2 < Q) cqp *= t;
+          if ((q2 >> 2) == blk && q2 > Q) cqs *= t;
+        }
+        f32v cb = 1.f, ca = 1.f, all = 1.f;
+  #pragma unroll
+        for (int b2 = 0; b2 < NB; ++b2) {
+          if (b2 < blk) cb *= t16[b2];
+          if (b2 > blk) ca *= t16[b2];
+          all *= t16[b2];
+        }
+        if (Q == 0) {
+          *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
+  #pragma unroll
+          for (int i2 = 2; i2 < NB; ++i2) {
+            f32v dd = 1.f;
+  #pragma unroll
+            for (int j2 = i2 - 2; j2 >= 0; --j2) {
+              dd *= t16[j2 + 1];
+              *reinterpret_cast<f32v*>(s_D + L::ddslot(i2, j2) * DK + c0) = dd;
+            }
+          }
+        }
+        // (s_D overlays the within-quarter sums, whose last reader was (2a))
+        const f32v fkq = cqp * cb, ff = cqs * ca;
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * Q + t;
+          const opv ka = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
+          const opv qa = *reinterpret_cast<const opv*>(sQ + r * L::LDK + c0);
+          const opv kb = *reinterpret_cast<const opv*>(sKB + r * L::LDK + c0);
+          opv ka16, qa16, kb16;
+          float xk[CPT], xq[CPT], xf[CPT];
+  #pragma unroll
+          for (int e = 0; e < CPT; ++e) {
+            const float k1 = static_cast<float>(ka[e]), q1 = static_cast<float>(qa[e]);
+            const float b1 = static_cast<float>(kb[e]);
+            ka16[e] = (OpT)(k1 * cqp[e]);
+            qa16[e] = (OpT)(q1 * cqp[e]);
+            kb16[e] = (OpT)(b1 * cqs[e]);
+            xk[e] = k1 * fkq[e];
+            xq[e] = q1 * fkq[e];
+            xf[e] = b1 * ff[e];
+          }
+          *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka16;
+          *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = qa16;
+          *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb16;
+          if constexpr (CPT % 4 == 0) {
+            put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
+            put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);
+            put_perm<OpT, R::PPRK>(rec + R::oF, r, c0, xf);
+          } else {
+  #pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+              const int off = swz_off<R::PPRK>(r, perm_pos(c0 + e) * static_cast<int>(sizeof(OpT)));
+              *reinterpret_cast<OpT*>(rec + R::oK + off) = (OpT)xk[e];
+              *reinterpret_cast<OpT*>(rec + R::oQ + off) = (OpT)xq[e];
+              *reinterpret_cast<OpT*>(rec + R::oF + off) = (OpT)xf[e];
+            }
+          }
+        }
+      }
+      lds_barrier();
+
+      // (2c) off-diagonal blocks i > j: the rows decayed from their block's
+      // start (Ka, Qa) times D, against k decayed to the end of block j (KB)
+      constexpr int NOFF = NB * (NB - 1) / 2;
+      for (int job = wave; job < 2 * NOFF; job += kPrepWaves) {
+        const bool isP = job >= NOFF;
+        const int pr = isP ? job - NOFF : job;
+        const int i = pair_i(pr) + 1, j = pair_j(pr);    // pairs of the strictly lower triangle
+        const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
+        const OpT* krow = sKB + (16 * j + l16) * L::LDK;
+        const float* dv = s_D + L::ddslot(i > j + 1 ? i : 2, i > j + 1 ? j : 0) * DK;
+        f32x4 acc = {0, 0, 0, 0};
+  #pragma unroll
+        for (int m = 0; m < NKP; ++m) {
+          auto fa = M::ld_cont(arow, 32 * m, g);
+          if (i > j + 1) M::scale_cont(fa, dv, 32 * m, g);
+          M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
+        }
+        emit(i, j, isP, acc);
+    }
     }
   }
   lds_barrier();
-
 
   // ============ phase 3: T = (I + A)^-1 (fp32) ============
   if (wave == 0) {

@@ -50,6 +50,7 @@ class Workload:
     chunk: int            # 0 for decode
     decay: str            # "none" | "head_small" | "head_logsig" | "channel_softplus"
                           # | "channel_strong" | "channel_steep" | "channel_extreme"
+                          # | "channel_mild_edge" | "channel_mixed"
     init_state: bool
     decode: bool = False
     seed: int = 1000
@@ -63,7 +64,8 @@ class Workload:
     def decay_kind(self) -> int:
         return {"none": DECAY_NONE, "channel_softplus": DECAY_CHANNEL,
                 "channel_strong": DECAY_CHANNEL, "channel_steep": DECAY_CHANNEL,
-                "channel_extreme": DECAY_CHANNEL}.get(self.decay, DECAY_HEAD)
+                "channel_extreme": DECAY_CHANNEL, "channel_mild_edge": DECAY_CHANNEL,
+                "channel_mixed": DECAY_CHANNEL}.get(self.decay, DECAY_HEAD)
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -130,6 +132,18 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     elif w.decay == "channel_extreme":
         # about -10 per token: a 16-token block decays by about exp(-160)
         decay = act(-_softplus(10.0 + 2.0 * normal(lead + (w.DK,))))
+    elif w.decay == "channel_mild_edge":
+        # -0.66 .. -0.74 per token: every 4 tokens decay by just under exp(-3)
+        # in every channel, half blocks by nearly exp(-6)
+        decay = act(-rng.uniform(0.66, 0.74, lead + (w.DK,)).astype(np.float32))
+    elif w.decay == "channel_mixed":
+        # spans of 96 tokens alternate between the workload's decay and a
+        # steep one, so chunks of either kind, and chunks holding both, follow
+        # one another in one sequence
+        mild = -_softplus(-3.0 + normal(lead + (w.DK,)))
+        steep = -_softplus(1.0 + normal(lead + (w.DK,)))
+        t_idx = np.arange(w.T).reshape((1, w.T) + (1,) * (len(lead) - 2))
+        decay = act(np.where(((t_idx // 96) % 2 == 1)[..., None], steep, mild))
     else:
         raise ValueError(w.decay)
     init = None

@@ -91,6 +91,15 @@ CHUNK_CASES = [
     ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_extreme")),
     ("kda_d128", dict(B=1, T=70, H=2, DK=32, DV=32, chunk=16, decay="channel_extreme")),
     ("fp32_small", dict(T=100, chunk=64, decay="channel_extreme", init_state=True)),
+    # per-channel decay at the mild path's limit (every quarter just under
+    # exp(-3)), and mild and steep chunks in one sequence
+    ("kda_d128", dict(B=1, T=200, H=2, decay="channel_mild_edge", init_state=True)),
+    ("kda_d128", dict(B=1, T=100, H=2, chunk=32, decay="channel_mild_edge")),
+    ("kda_d128", dict(B=1, T=70, H=2, DK=64, DV=64, chunk=16, decay="channel_mild_edge")),
+    ("fp32_small", dict(T=90, chunk=64, decay="channel_mild_edge", init_state=True)),
+    ("kda_d128", dict(B=1, T=400, H=2, decay="channel_mixed", init_state=True)),
+    ("kda_d128", dict(B=2, T=300, H=2, chunk=32, decay="channel_mixed")),
+    ("fp32_small", dict(T=300, chunk=64, decay="channel_mixed")),
     # fp32 at DK = 128: the state kernel's single-buffer LDS plan
     ("fp32_small", dict(B=1, T=150, H=2, DK=128, DV=128, chunk=64, init_state=True)),
     ("fp32_small", dict(B=1, T=100, H=2, DK=128, DV=64, chunk=64, decay="channel_softplus")),

@@ -408,11 +408,12 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   float* s_misc = sv + 4 * C;
   int* s_steep = reinterpret_cast<int*>(s_misc);   // per-channel decay: a quarter decays by more than e^-3
   float* s_tau4 = s_misc + 16;                 // [NQ][DK] decay factor of each 4-token quarter
-                                               // (first its log, the quarter's gate sum)
+                                               // (first its log, the quarter's gate sum; on the
+                                               // mild path then the log decay from the chunk
+                                               // start to the quarter's start)
   float* s_wq = s_tau4 + L::NQ * DK;           // [NQ][12] within-quarter Gram sums (A, then P)
   float* s_D = s_wq;                           // [NDD][DK] decay between blocks i, j (i - j >= 2), later
-  float* s_mb = s_wq;                          // mild decay: [NB][DK] log decay from the chunk start
-                                               // to the middle of block b
+  float* s_tot = s_wq;                         // mild decay: [DK] the chunk's log decay
 
   const In* gq = static_cast<const In*>(p.q);
   const In* gk = static_cast<const In*>(p.k);
@@ -646,6 +647,19 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     mild = *s_steep == 0 && (sizeof(OpT) == 4 || (p.l2norm && p.scale <= 4.f));
 
     if (mild) {
+      // the log decay from the chunk start to every quarter start, in place,
+      // and over the chunk: one thread per channel
+      if (tid < DK) {
+        float acc = 0.f;
+#pragma unroll
+        for (int q2 = 0; q2 < NQ; ++q2) {
+          const float sq = s_tau4[q2 * DK + tid];
+          s_tau4[q2 * DK + tid] = acc;
+          acc += sq;
+        }
+        s_tot[tid] = acc;
+      }
+      lds_barrier();
       // Mild decay (every quarter's decay at least e^-3 in every channel, so
       // every half block's at least e^-6): the operands of a 16-token block b
       // are referenced to its middle, M_b = G at token 16 b + 7, so that one
@@ -655,21 +669,16 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       // fp32 scale exp(M_i - M_j) <= 1.
       if (qt) {
         const int blk = Q >> 2;
-        f32v gq = 0.f, mb = 0.f, tot = 0.f;
-#pragma unroll
-        for (int q2 = 0; q2 < NQ; ++q2) {
-          const f32v sq = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
-          tot += sq;
-          if (q2 < Q) gq += sq;
-          if (q2 < 4 * blk + 2) mb += sq;
-        }
+        // G at the quarter's start, M_b and G_last
+        const f32v gq = *reinterpret_cast<const f32v*>(s_tau4 + Q * DK + c0);
+        const f32v mb = *reinterpret_cast<const f32v*>(s_tau4 + (4 * blk + 2) * DK + c0);
+        const f32v tot = *reinterpret_cast<const f32v*>(s_tot + c0);
         f32v emb, ef;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
           emb[e] = __expf(mb[e]);            // the record's chunk reference: exp(M_b)
           ef[e] = __expf(tot[e] - mb[e]);    // exp(G_last - M_b)
         }
-        if ((Q & 3) == 0) *reinterpret_cast<f32v*>(s_mb + blk * DK + c0) = mb;
         if (Q == 0) {
           f32v all;
 #pragma unroll
@@ -736,8 +745,8 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         for (int m = 0; m < NKP; ++m) {
           auto fa = M::ld_cont(arow, 32 * m, g);
           if (i > j) {
-            const float* mi = s_mb + i * DK;
-            const float* mj = s_mb + j * DK;
+            const float* mi = s_tau4 + (4 * i + 2) * DK;   // M_i
+            const float* mj = s_tau4 + (4 * j + 2) * DK;
             M::scale_fn(fa, 32 * m, g, [&](int c) { return __expf(mi[c] - mj[c]); });
           }
           M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);

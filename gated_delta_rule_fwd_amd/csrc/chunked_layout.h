@@ -151,11 +151,11 @@ struct PrepLayout {
   static constexpr int NDD = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 1;
   static constexpr int ddslot(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
   static constexpr int kWQ = 12;                    // within-quarter sums per quarter
-  static constexpr int kWQD = static_cast<int>(chunked_layout::mx(chunked_layout::mx(NQ * kWQ, NDD * DK), NB * DK));
+  static constexpr int kWQD = NQ * kWQ > NDD * DK ? NQ * kWQ : NDD * DK;
   // fp32 vectors: bt Gi Ge qk (each C), misc[16]; per-channel: tau4[NQ][DK]
   // (the decay factor of each quarter), then the within-quarter sums [NQ][12],
-  // later (same place) D[NDD][DK]; on the mild path the log decay from the
-  // chunk start to each block's middle, [NB][DK]
+  // later (same place) D[NDD][DK]; on the mild path the chunk's log decay
+  // per channel, [DK]
   static constexpr int kVecRows = 4;
   static constexpr size_t oVec(bool ch) { return tilesEnd(ch); }
   static constexpr size_t szVec(bool ch) {

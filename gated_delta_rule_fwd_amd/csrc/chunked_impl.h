@@ -762,10 +762,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       // channels of the 6 within-quarter pairs of A and of P are formed here.
       if (qt) {
         float w[12];
-  #pragma unroll
+#pragma unroll
         for (int x = 0; x < 12; ++x) w[x] = 0.f;
         opv gv[4], kv[4], qv[4];
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * Q + t;
           gv[t] = *reinterpret_cast<const opv*>(sGst + r * DK + c0);
@@ -774,24 +774,24 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         }
         opv ka[4], qa[4], kb[4];
         f32v tau;
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < CPT; ++e) {
           float a[4], kx[4], qx[4];
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < 4; ++t) {
             a[t] = __expf(static_cast<float>(gv[t][e]));
             kx[t] = static_cast<float>(kv[t][e]);
             qx[t] = static_cast<float>(qv[t][e]);
           }
           float pre = 1.f;
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < 4; ++t) {
             ka[t][e] = (OpT)(kx[t] * pre);
             pre *= a[t];
             qa[t][e] = (OpT)(qx[t] * pre);
           }
           float suf = 1.f;
-  #pragma unroll
+#pragma unroll
           for (int t = 3; t >= 0; --t) {
             kb[t][e] = (OpT)(kx[t] * suf);
             suf *= a[t];
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           w[10] += qx[3] * kx[1] * a23;
           w[11] += qx[3] * kx[2] * a[3];
         }
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * Q + t;
           *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = ka[t];
@@ -820,10 +820,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = kb[t];
         }
         *reinterpret_cast<f32v*>(s_tau4 + Q * DK + c0) = tau;
-  #pragma unroll
+#pragma unroll
         for (int x = 0; x < 12; ++x) w[x] = dpp_group_sum<LPQ>(w[x]);
         if (c0 == 0) {
-  #pragma unroll
+#pragma unroll
           for (int x = 0; x < 12; ++x) s_wq[Q * L::kWQ + x] = w[x];
         }
       }
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           constexpr int S = decltype(S_)::value;
           const float* t1 = s_tau4 + (4 * i + S + 1) * DK;
           const float* t2 = s_tau4 + (4 * i + (S + 2 < 4 ? S + 2 : 3)) * DK;
-  #pragma unroll
+#pragma unroll
           for (int m = 0; m < NKP; ++m) {
             typename M::frag fk = Rq == S ? M::ld_cont(krow, 32 * m, g) : M::zero();
             typename M::frag fa = Rq > S ? M::ld_cont(arow, 32 * m, g) : M::zero();
@@ -865,9 +865,9 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       if (qt) {
         const int blk = Q >> 2;
         f32v t16[NB], cqp = 1.f, cqs = 1.f;
-  #pragma unroll
+#pragma unroll
         for (int b2 = 0; b2 < NB; ++b2) t16[b2] = 1.f;
-  #pragma unroll
+#pragma unroll
         for (int q2 = 0; q2 < NQ; ++q2) {
           const f32v t = *reinterpret_cast<const f32v*>(s_tau4 + q2 * DK + c0);
           t16[q2 >> 2] *= t;
@@ -875,7 +875,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           if ((q2 >> 2) == blk && q2 > Q) cqs *= t;
         }
         f32v cb = 1.f, ca = 1.f, all = 1.f;
-  #pragma unroll
+#pragma unroll
         for (int b2 = 0; b2 < NB; ++b2) {
           if (b2 < blk) cb *= t16[b2];
           if (b2 > blk) ca *= t16[b2];
@@ -883,10 +883,10 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         }
         if (Q == 0) {
           *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
-  #pragma unroll
+#pragma unroll
           for (int i2 = 2; i2 < NB; ++i2) {
             f32v dd = 1.f;
-  #pragma unroll
+#pragma unroll
             for (int j2 = i2 - 2; j2 >= 0; --j2) {
               dd *= t16[j2 + 1];
               *reinterpret_cast<f32v*>(s_D + L::ddslot(i2, j2) * DK + c0) = dd;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         }
         // (s_D overlays the within-quarter sums, whose last reader was (2a))
         const f32v fkq = cqp * cb, ff = cqs * ca;
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * Q + t;
           const opv ka = *reinterpret_cast<const opv*>(sK + r * L::LDK + c0);
@@ -903,7 +903,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           const opv kb = *reinterpret_cast<const opv*>(sKB + r * L::LDK + c0);
           opv ka16, qa16, kb16;
           float xk[CPT], xq[CPT], xf[CPT];
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < CPT; ++e) {
             const float k1 = static_cast<float>(ka[e]), q1 = static_cast<float>(qa[e]);
             const float b1 = static_cast<float>(kb[e]);
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
             put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);
             put_perm<OpT, R::PPRK>(rec + R::oF, r, c0, xf);
           } else {
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < CPT; ++e) {
               const int off = swz_off<R::PPRK>(r, perm_pos(c0 + e) * static_cast<int>(sizeof(OpT)));
               *reinterpret_cast<OpT*>(rec + R::oK + off) = (OpT)xk[e];
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         const OpT* krow = sKB + (16 * j + l16) * L::LDK;
         const float* dv = s_D + L::ddslot(i > j + 1 ? i : 2, i > j + 1 ? j : 0) * DK;
         f32x4 acc = {0, 0, 0, 0};
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < NKP; ++m) {
           auto fa = M::ld_cont(arow, 32 * m, g);
           if (i > j + 1) M::scale_cont(fa, dv, 32 * m, g);

@@ -151,6 +151,37 @@ def test_chunked_extreme_channel_decays(name, kw):
     check("recurrent extreme", o_r, S_r, o_ref, S_ref, TOL[w.dtype])
 
 
+VOTE = [("kda_d128", dict(B=1, T=256, H=2, init_state=True)),
+        ("kda_d128", dict(B=1, T=128, H=2, chunk=32, DK=64, DV=64)),
+        ("fp32_small", dict(T=256, H=2, chunk=64, decay="channel_softplus", init_state=True))]
+
+
+@pytest.mark.parametrize("name,kw", VOTE, ids=lambda x: str(x))
+def test_chunked_per_channel_vote_edge(name, kw):
+    """The per-channel prep takes its mild path only when no 4-token quarter
+    decays by more than exp(-3) in any channel.  On the workload's mild decay,
+    one channel's quarter in the second chunk sums to -3.04 (that chunk takes
+    the exact path) and another's in the third chunk to -2.96 (it stays
+    mild); both against the oracle."""
+    w = small(name, **kw)
+    announce(f"vote edge {w}")
+    inp = make_inputs(w)
+    dec = inp["decay"]
+    C = w.chunk
+    dec[:, C + 20:C + 24, :, 5] = -0.76
+    dec[:, 2 * C + 8:2 * C + 12, :, 9] = -0.74
+    dec_np = dec.float().numpy()
+    assert dec_np[:, C + 20:C + 24, :, 5].sum(axis=1).max() < -3.0
+    assert dec_np[:, 2 * C + 8:2 * C + 12, :, 9].sum(axis=1).min() > -3.0
+    d = to_dev(inp)
+    o, S = fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["decay"], d["initial_state"],
+                       chunk_size=C)
+    torch.cuda.synchronize()
+    o_ref, S_ref = kda_scan(inp["q"], inp["k"], inp["v"], inp["beta"], inp["decay"],
+                            inp["initial_state"])
+    check("chunked vote edge", o, S, o_ref, S_ref, TOL[w.dtype])
+
+
 # -------------------------------------------------------------- recurrent --
 
 REC_CASES = [

@@ -1172,7 +1172,7 @@ __device__ __forceinline__ void touch_buf(i32x4 rs, uint32_t m0, int voff) {
 // State-kernel workgroup: DVS/16 owner waves that compute, and as many
 // helper waves that copy the next chunk into LDS, so the owners never wait to
 // issue a copy.
-template <int DVS> constexpr int state_waves() { return 2 * (DVS / 16); }
+template <int DVS> constexpr int state_waves() { return DVS / 16 + state_helpers<DVS>(); }
 
 template <int DK, int DVS, int C, typename In, int DECAY>
 __global__ __launch_bounds__(64 * state_waves<DVS>(), state_waves<DVS>() > 4 ? 2 : 1)
@@ -1195,7 +1195,7 @@ void state_kernel(StateParams p) {
   constexpr int nRecI = static_cast<int>(L::kRecLds / 1024);   // whole slots (image padded)
   constexpr int nVal = C * L::PPRV, nValI = (nVal + 63) / 64;
   constexpr int nQK = rawk ? C * R::PPRK : 0, nQKI = nQK / 64;
-  constexpr int NHELP = NOWN;                 // helper waves (they issue every copy)
+  constexpr int NHELP = state_helpers<DVS>();  // helper waves (they issue every copy)
   constexpr int NPF = L::kNPF;                // P operand fragments (raw rows: formed by the helpers)
   constexpr int NBLK = NB * (NB + 1) / 2;     // P's lower-triangular 16 x 16 blocks
   constexpr int kStThreads = 64 * state_waves<DVS>();

@@ -173,13 +173,18 @@ struct PrepLayout {
 // fragments (PF, one 1 KiB fragment per 16-token row block and 32-token k
 // step), and the row factors of q (FQ, one float per token), then sets its
 // flag (ints after FQ) to the chunk + 1.
+// Helper waves of the state kernel for a slice of DVS value columns: as many
+// as the DVS / 16 owner waves, and at least two (so that a 16-column slice
+// shares P and the copies between two waves).
+template <int DVS> constexpr int state_helpers() { return DVS / 16 > 2 ? DVS / 16 : 2; }
+
 template <int DK, int DVS, int C, int OpBytes, int ActBytes, bool Chan>
 struct StateLayout {
   using R = RecLayout<DK, C, OpBytes, Chan>;
   static constexpr int PPRV = DVS * ActBytes / 16;   // pieces per value row
   // the record's bytes in the image, padded to whole 1 KiB copies for each of
-  // the DVS / 16 waves that issue them
-  static constexpr size_t kRecSlot = size_t(1024) * (DVS / 16);
+  // the helper waves that issue them
+  static constexpr size_t kRecSlot = size_t(1024) * state_helpers<DVS>();
   static constexpr size_t kRecLds = (R::gBytes + kRecSlot - 1) / kRecSlot * kRecSlot;
   static constexpr size_t oV = R::gOff + kRecLds;
   static constexpr size_t kBuf = chunked_layout::al(oV + size_t(C) * DVS * ActBytes);

@@ -555,30 +555,37 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
 // dD = P^T dO + F . K dS and dY = T^T dD on VALU, then
 // dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.  The
 // next chunk's inputs are loaded into registers while this one is computed.
-template <int DK, int DV, typename In, bool CH>
+template <int DK, int DV, typename In, bool CH, int NS>
 __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const In* __restrict__ k,
                                                  const float* __restrict__ dout, const float* __restrict__ dfinal,
                                                  float* __restrict__ dv, float* __restrict__ dinit, CWs w, int T,
                                                  int H, int Hk, int N, int vfirst) {
   constexpr int KP = DK + 4, MT = DK / 16, NT = (MT + 3) / 4, NW = MT < 4 ? MT : 4;
+  constexpr int NCT = NS / 16;           // 16-column tiles of the slice
+  constexpr int NE = kC * NS / kThr;     // (token, column) elements per thread
+  static_assert(NS % 16 == 0 && DV % NS == 0 && (kC * NS) % kThr == 0, "slice width");
   __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
   __shared__ __align__(16) float gs[CH ? kC + 1 : 1][CH ? KP : 4];
   __shared__ __align__(16) float TmT[kC][kCP], PmT[kC][kCP];
-  __shared__ float part[NW][kC][kNS + 1];
-  __shared__ float dO[kC][kNS + 1], dD[kC][kNS + 1], BB[2 * kC][kNS + 1];
+  __shared__ float part[NW][kC][NS + 1];
+  __shared__ float dO[kC][NS + 1], dD[kC][NS + 1], BB[2 * kC][NS + 1];
   __shared__ TokVec tv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
-  constexpr int nsl = DV / kNS;
+  constexpr int nsl = DV / NS;
   const int sl = blockIdx.x % nsl, bh = blockIdx.x / nsl, b = bh / H, h = bh % H, hk = h / (H / Hk);
-  const int n0 = sl * kNS;
+  const int n0 = sl * NS;
   const long sb = static_cast<long>(bh) * DK * DV;
   auto sidx = [&](int c, int n) { return sb + (vfirst ? static_cast<long>(n) * DK + c : static_cast<long>(c) * DV + n); };
-  f32x4 acc[NT];
+  f32x4 acc[NT][NCT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int mt = wave + 4 * j;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[j][e] = (mt < MT && dfinal) ? dfinal[sidx(16 * mt + 4 * lg + e, n0 + li)] : 0.f;
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[j][ct][e] = (mt < MT && dfinal) ? dfinal[sidx(16 * mt + 4 * lg + e, n0 + 16 * ct + li)] : 0.f;
+    }
   }
   RowPf<DK, In, kThr> kpf, qpf;
   MatPf<kThr, true> mpf;
@@ -586,7 +593,7 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
   GamPf<CH ? DK : 4, kThr> gpf;
   if (CH)
     for (int c = tid; c < DK; c += kThr) gs[0][c] = 0.f;
-  float dov[2];
+  float dov[NE];
   auto prefetch = [&](int c) __attribute__((always_inline)) {
     const int L = min(kC, T - c * kC);
     const long tok0 = static_cast<long>(b) * T + c * kC;
@@ -596,8 +603,8 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     tpf.load(w, tok0, H, h, L, tid);
     if constexpr (CH) gpf.load(w.gmc, tok0, H, h, L, tid);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = min(idx / kNS, L - 1), n = idx % kNS;
+    for (int u = 0; u < NE; ++u) {
+      const int idx = tid + u * kThr, r = min(idx / NS, L - 1), n = idx % NS;
       dov[u] = dout[((tok0 + r) * H + h) * DV + n0 + n];
     }
   };
@@ -612,9 +619,9 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     tpf.store<CH>(tv, L, tid);
     if constexpr (CH) gpf.store(gs, tid);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NE; ++u) {
       const int idx = tid + u * kThr;
-      dO[idx / kNS][idx % kNS] = idx / kNS < L ? dov[u] : 0.f;
+      dO[idx / NS][idx % NS] = idx / NS < L ? dov[u] : 0.f;
     }
     float* d1 = w.dS1 + (static_cast<size_t>(bh) * N + ci) * DK * DV;
 #pragma unroll
@@ -622,7 +629,10 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
       const int mt = wave + 4 * j;
       if (mt < MT) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d1[(16 * mt + 4 * lg + e) * DV + n0 + li] = acc[j][e];
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d1[(16 * mt + 4 * lg + e) * DV + n0 + 16 * ct + li] = acc[j][ct][e];
+        }
       }
     }
     lds_sync();
@@ -631,7 +641,9 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     if (wave < NW) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        f32x4 p[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) p[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const int mt = wave + 4 * j;
@@ -645,11 +657,17 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
               for (int e = 0; e < 4; ++e) a[e] *= __expf(gC[e] - gm[e]);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p = mma4(a[e], acc[j][e], p);
+            for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) p[ct] = mma4(a[e], acc[j][ct][e], p[ct]);
+            }
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][li] = p[e];
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[wave][16 * rt + 4 * lg + e][16 * ct + li] = p[ct][e];
+        }
       }
     }
     lds_sync();
@@ -663,8 +681,8 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     }
     // dD = P^T dO + F . K dS
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
+    for (int u = 0; u < NE; ++u) {
+      const int idx = tid + u * kThr, r = idx / NS, n = idx % NS;
       float kd = 0.f;
 #pragma unroll
       for (int qq = 0; qq < NW; ++qq) kd += part[qq][r][n];
@@ -673,8 +691,8 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     lds_sync();
     // dX = beta . T^T dD, the gradient of v; the B operand of the dS update
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
+    for (int u = 0; u < NE; ++u) {
+      const int idx = tid + u * kThr, r = idx / NS, n = idx % NS;
       const float x = tv.bt[r] * row_col(TmT[r], dD, n);
       if (r < L) dv[((tok0 + r) * H + h) * DV + n0 + n] = x;
       BB[r][n] = tv.egm[r] * dO[r][n];
@@ -687,17 +705,27 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     for (int j = 0; j < NT; ++j) {
       const int mt = wave + 4 * j;
       if (mt < MT) {
-        if constexpr (CH) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[j][e] *= __expf(gs[L][16 * mt + 4 * lg + e]);
-        } else {
-          acc[j] *= egC;
+        for (int ct = 0; ct < NCT; ++ct) {
+          if constexpr (CH) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][ct][e] *= __expf(gs[L][16 * mt + 4 * lg + e]);
+          } else {
+            acc[j][ct] *= egC;
+          }
         }
 #pragma unroll
-        for (int ks = 0; ks < kC / 4; ++ks) acc[j] = mma4(qh[4 * ks + lg][16 * mt + li], BB[4 * ks + lg][li], acc[j]);
+        for (int ks = 0; ks < kC / 4; ++ks) {
+          const float qa = qh[4 * ks + lg][16 * mt + li];
 #pragma unroll
-        for (int ks = 0; ks < kC / 4; ++ks)
-          acc[j] = mma4(kh[4 * ks + lg][16 * mt + li], BB[kC + 4 * ks + lg][li], acc[j]);
+          for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = mma4(qa, BB[4 * ks + lg][16 * ct + li], acc[j][ct]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kC / 4; ++ks) {
+          const float ka = kh[4 * ks + lg][16 * mt + li];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc[j][ct] = mma4(ka, BB[kC + 4 * ks + lg][16 * ct + li], acc[j][ct]);
+        }
       }
     }
   }
@@ -707,7 +735,10 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
       const int mt = wave + 4 * j;
       if (mt < MT) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dinit[sidx(16 * mt + 4 * lg + e, n0 + li)] = acc[j][e];
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dinit[sidx(16 * mt + 4 * lg + e, n0 + 16 * ct + li)] = acc[j][ct][e];
+        }
       }
     }
   }
@@ -1601,12 +1632,19 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
   CWs w;
   ws_floats(a.B, a.T, a.H, DK, DV, &w, a.ckpt);
   const unsigned chunks = static_cast<unsigned>(a.B * a.H * N), slices = static_cast<unsigned>(a.B * a.H * (DV / kNS));
+  // The reverse walk without per-channel decay fits two 16-column workgroups
+  // per CU (its LDS): with more slices than that it takes 32 columns per
+  // workgroup, so that every walk runs at once rather than in two rounds.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const bool wide = DV % 32 == 0 && cus > 0 && slices > 2u * static_cast<unsigned>(cus);
   if (a.decay_kind == DECAY_CHANNEL) {
     cbwd_prep_ch<DK, In><<<dim3(chunks), dim3(kThr), 0, s>>>(q, k, be, de, w, a.T, a.H, a.Hk, N, a.scale,
                                                               a.l2norm, a.tf);
     cbwd_fwd<DK, DV, In, true><<<dim3(slices), dim3(kThr), 0, s>>>(k, v, a.init, w, a.T, a.H, a.Hk, N, a.vfirst);
-    cbwd_rev<DK, DV, In, true><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
-                                                                   a.H, a.Hk, N, a.vfirst);
+    cbwd_rev<DK, DV, In, true, kNS><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w,
+                                                                        a.T, a.H, a.Hk, N, a.vfirst);
     cbwd_local_ch<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(q, k, v, a.dout, a.dq, a.dk, a.dbeta,
                                                                     a.ddecay, w, a.T, a.H, a.Hk, N, a.scale,
                                                                     a.l2norm);
@@ -1615,8 +1653,14 @@ hipError_t run(const BwdArgs& a, hipStream_t s) {
   cbwd_prep<DK, In><<<dim3(chunks), dim3(kThr), 0, s>>>(q, k, be, de, a.decay_kind == DECAY_HEAD, w, a.T, a.H,
                                                          a.Hk, N, a.scale, a.l2norm, a.tf);
   cbwd_fwd<DK, DV, In, false><<<dim3(slices), dim3(kThr), 0, s>>>(k, v, a.init, w, a.T, a.H, a.Hk, N, a.vfirst);
-  cbwd_rev<DK, DV, In, false><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w, a.T,
-                                                                  a.H, a.Hk, N, a.vfirst);
+  if (wide) {
+    if constexpr (DV % 32 == 0)
+      cbwd_rev<DK, DV, In, false, 32><<<dim3(slices / 2), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit,
+                                                                              w, a.T, a.H, a.Hk, N, a.vfirst);
+  } else {
+    cbwd_rev<DK, DV, In, false, kNS><<<dim3(slices), dim3(kThr), 0, s>>>(q, k, a.dout, a.dfinal, a.dv, a.dinit, w,
+                                                                         a.T, a.H, a.Hk, N, a.vfirst);
+  }
   cbwd_local<DK, DV, In><<<dim3(chunks), dim3(kThr3), 0, s>>>(
       q, k, v, a.dout, a.dq, a.dk, a.dbeta, a.decay_kind == DECAY_HEAD ? a.ddecay : nullptr, w, a.T, a.H, a.Hk, N,
       a.scale, a.l2norm);

@@ -35,6 +35,11 @@ CASES = [
     ("kda_d128", dict(B=1, T=64, H=2, DV=32, init_state=True), {}),
     ("fp32_small", dict(T=45, H=1, HV=2, DK=32, DV=32, decay="channel_softplus", init_state=True), {}),
     ("deltanet_d64", dict(B=1, T=1, H=2, DK=128, DV=32, init_state=True), {}),
+    # more 16-column slices than two per CU: the reverse walk takes 32 columns
+    # per workgroup (per-head decay and none, bf16 and fp32)
+    ("gdn_d128", dict(B=2, T=45, H=36, init_state=True), {}),
+    ("deltanet_d64", dict(B=1, T=40, H=72, DK=128, DV=128), {}),
+    ("fp32_small", dict(B=1, T=37, H=72, DK=32, DV=128, init_state=True), {}),
 ]
 
 

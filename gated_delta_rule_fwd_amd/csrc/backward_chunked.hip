@@ -1462,10 +1462,10 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
         gx[e] = sm.gs[16 * mt + 4 * lg + e][c];
         gm[e] = sm.gs[16 * mt + 4 * lg + e + 1][c];
       }
-      // The decay factor between tokens u and r is a product of the per-token
-      // factors a_t = exp(g_t) <= 1 strictly between or up to them, carried
-      // down (u < r) and up (u > r) the partner tokens: no exponential per
-      // pair, no factor above one.
+      // The decay factor between tokens u and r.  Partners in the row's own
+      // 16-token block: a product of the per-token factors a_t = exp(g_t) <= 1
+      // strictly between or up to them, carried down (u < r) and up (u > r)
+      // the partner tokens (no exponential per pair, no factor above one).
       // Partners in the other 16-token block: a product on MFMA, the decay
       // split at token 15 into two factors <= 1 (exp(gx_r - gam_u) =
       // exp(gx_r - gam_15) exp(gam_15 - gam_u), and so on), one on the

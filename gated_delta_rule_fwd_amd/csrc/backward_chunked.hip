@@ -38,7 +38,8 @@
 // the cumulative decays, T and P; (1) per (b, h, kNS value columns): the
 // walk over the chunks storing each chunk's S0; (2) the same slices in
 // reverse: the walk of the state gradient storing each chunk's dS1 and
-// writing dv and the initial state's gradient; (3) per chunk, in parallel:
+// writing dv and the initial state's gradient (2 kNS columns per workgroup
+// when slices of kNS would exceed two per CU); (3) per chunk, in parallel:
 // everything else, over the value columns kNS at a time.  (0) and (3) have a
 // per-channel version each; (1) and (2) a per-channel mode.  (3) also
 // carries dq and dk through the L2 norm and the scale when every q/k head has

@@ -495,7 +495,7 @@ def main():
         write_counters(args.write_counters, args.counters_out)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); each (batch, head) is independent, so a "
               f"multi-GPU run would be this single-GPU kernel on each GPU's share.",
               file=sys.stderr)

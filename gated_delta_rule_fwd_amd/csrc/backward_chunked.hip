@@ -1464,13 +1464,14 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
         gm[e] = sm.gs[16 * mt + 4 * lg + e + 1][c];
       }
       // The decay factor between tokens u and r.  Partners in the row's own
-      // 16-token block: a product of the per-token factors a_t = exp(g_t) <= 1
-      // strictly between or up to them, carried down (u < r) and up (u > r)
-      // the partner tokens (no exponential per pair, no factor above one).
-      // Partners in the other 16-token block: a product on MFMA, the decay
-      // split at token 15 into two factors <= 1 (exp(gx_r - gam_u) =
-      // exp(gx_r - gam_15) exp(gam_15 - gam_u), and so on), one on the
-      // partner's row, one applied to the result.
+      // 8-token half block: a product of the per-token factors a_t =
+      // exp(g_t) <= 1 strictly between or up to them, carried down (u < r) and
+      // up (u > r) the partner tokens (no exponential per pair, no factor
+      // above one).  Partners in the other 16-token block, or in the other
+      // half of the row's block: a product on MFMA, the decay split at the
+      // last token of the earlier block or half into two factors <= 1
+      // (exp(gx_r - gam_u) = exp(gx_r - gam_s) exp(gam_s - gam_u), and so on),
+      // one on the partner's row, one applied to the result.
       if (mt == 1) {
         f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, h1 = g1;
 #pragma unroll
@@ -1503,12 +1504,44 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
           H2[e] += h2[e] * f;
         }
       }
-      // partners in the row's own block: running products
+      // partners in the other half of the row's block: split at token s = 16 mt + 7
+      {
+        const float gh = sm.gs[16 * mt + 8][c];   // gam_s
+        const bool hi = li >= 8;                  // the A operand's row in the later half
+        f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, h1 = g1, g2 = g1, h2 = g1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int u1 = 16 * mt + 4 * ks + lg, u2 = u1 + 8, rr = 16 * mt + li;
+          const float b1 = sm.kh[u1][c] * __expf(gh - sm.gs[u1 + 1][c]);                // k_u exp(gam_s - gam_u)
+          const float bk = tv.bt[u2] * sm.kh[u2][c] * __expf(sm.gs[u2][c] - gh);        // exp(gx_u - gam_s)
+          const float bq = sm.qh[u2][c] * __expf(sm.gs[u2 + 1][c] - gh);                // exp(gam_u - gam_s)
+          g1 = mma4(hi ? Fm.dA[rr][u1] : 0.f, b1, g1);
+          h1 = mma4(hi ? Fm.dPm[rr][u1] : 0.f, b1, h1);
+          g2 = mma4(hi ? 0.f : Fm.dA[u2][rr], bk, g2);
+          h2 = mma4(hi ? 0.f : Fm.dPm[u2][rr], bq, h2);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * mt + 4 * lg + e;
+          if (lg >= 2) {
+            G1[e] += g1[e] * __expf(sm.gs[r][c] - gh);       // exp(gx_r - gam_s)
+            H1[e] += h1[e] * __expf(sm.gs[r + 1][c] - gh);   // exp(gam_r - gam_s)
+          } else {
+            const float f = __expf(gh - sm.gs[r + 1][c]);    // exp(gam_s - gam_r)
+            G2[e] += g2[e] * f;
+            H2[e] += h2[e] * f;
+          }
+        }
+      }
+      // partners in the row's own half block: running products (a lane's four
+      // rows lie in one half, which starts at token hb)
+      const int hb = 16 * mt + 8 * (lg >> 1);
       {
         float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
-        // rows 16 mt .. 16 mt + 15: partners u <= r start at the tile's last row
-#pragma unroll 8
-        for (int uu = 16 * mt + 15; uu >= 16 * mt; --uu) {
+        // partners u <= r start at the half's last row
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const int uu = hb + 7 - kk;
           const float ku = sm.kh[uu][c], an = sm.kx[min(uu + 1, kC - 1)][c];   // a_{u+1}
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1522,9 +1555,10 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
       }
       {
         float E1[4] = {1.f, 1.f, 1.f, 1.f}, E2[4] = {1.f, 1.f, 1.f, 1.f};
-        // partners u >= r start at the tile's first row
-#pragma unroll 8
-        for (int uu = 16 * mt; uu < 16 * mt + 16; ++uu) {
+        // partners u >= r start at the half's first row
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const int uu = hb + kk;
           const float ku = sm.kh[uu][c], qu = sm.qh[uu][c], bu = tv.bt[uu];
           const float ap = sm.kx[max(uu - 1, 0)][c], au = sm.kx[uu][c];   // a_{u-1}, a_u
 #pragma unroll

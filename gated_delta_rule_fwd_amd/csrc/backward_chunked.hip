@@ -1173,8 +1173,11 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
   // exp(gx_r - gam_s) = exp(gx_r - gam_15) exp(gam_15 - gam_s) and
   // exp(gam_r - gam_s) = exp(gam_r - gam_15) exp(gam_15 - gam_s), each factor
   // <= 1, so that block is a product of decayed rows on MFMA (wave 0, A and
-  // P together).  The two diagonal blocks' 136 pairs each: one pair per
-  // thread of the other waves, the channel sum with its own factors.
+  // P together).  Within each diagonal block the same split at the last
+  // token of its first half gives the later half's rows against the earlier
+  // half's tokens (wave 1, both blocks in one product).  The four 8-token
+  // halves' 36 pairs each: one pair per thread of waves 2 and 3, the channel
+  // sum with its own factors.
   if (tid < 64) {
     const int li = tid & 15, lg = tid >> 4;
     f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = aa;
@@ -1194,13 +1197,39 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
       sA[r][s2] = sbt[r] * aa[e];
       w.Pm[cb + r * kC + s2] = pa[e];
     }
+  } else if (tid < 128) {
+    // tile row / column i: block i >> 3, token 16 (i >> 3) + 8 + (i & 7) (rows)
+    // or 16 (i >> 3) + (i & 7) (columns); entries across the two blocks are
+    // not kept
+    const int li = tid & 15, lg = (tid >> 4) & 3;
+    const int rr = 16 * (li >> 3) + 8 + (li & 7), sc = 16 * (li >> 3) + (li & 7);
+    f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = aa;
+#pragma unroll 4
+    for (int ks = 0; ks < DK / 4; ++ks) {
+      const int c = 4 * ks + lg;
+      const float gr7 = gs[16 * (li >> 3) + 8][c];   // gam at the block's token 7 (row and column alike)
+      const float bk = kh[sc][c] * __expf(gr7 - gs[sc + 1][c]);    // k_s exp(gam_7 - gam_s)
+      const float ak = kh[rr][c] * __expf(gs[rr][c] - gr7);        // k_r exp(gx_r - gam_7)
+      const float aq = qh[rr][c] * __expf(gs[rr + 1][c] - gr7);    // q_r exp(gam_r - gam_7)
+      aa = mma4(ak, bk, aa);
+      pa = mma4(aq, bk, pa);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ti = 4 * lg + e;
+      if ((ti >> 3) == (li >> 3)) {
+        const int r = 16 * (ti >> 3) + 8 + (ti & 7);
+        sA[r][sc] = sbt[r] * aa[e];
+        w.Pm[cb + r * kC + sc] = pa[e];
+      }
+    }
   } else {
-    for (int idx = tid - 64; idx < 2 * 136; idx += kThr - 64) {
-      const int blk = idx / 136, id = idx % 136;
+    for (int idx = tid - 128; idx < 4 * 36; idx += kThr - 128) {
+      const int hf = idx / 36, id = idx % 36;   // half hf: tokens 8 hf .. 8 hf + 7
       int rl = static_cast<int>((sqrtf(8.f * id + 1.f) - 1.f) * 0.5f);
       if ((rl + 1) * (rl + 2) / 2 <= id) ++rl;
       if (rl * (rl + 1) / 2 > id) --rl;
-      const int r = 16 * blk + rl, s = 16 * blk + id - rl * (rl + 1) / 2;
+      const int r = 8 * hf + rl, s = 8 * hf + id - rl * (rl + 1) / 2;
       float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
 #pragma unroll 4
       for (int c = 0; c < DK; c += 4) {

@@ -106,6 +106,19 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
 
 // (0) per (b, h, chunk): the norm factors of the rows, beta and the
 // cumulative decays per token; T and P of the chunk.
+// Column j of T = (I + A)^-1 (A strictly lower, kC x kC in LDS) by forward
+// substitution, each row's sum in four partial sums (a chain a quarter as
+// long).
+__device__ __forceinline__ void tri_inv_col(const float (*sA)[kC + 1], int j, float (&x)[kC]) {
+#pragma unroll
+  for (int r = 0; r < kC; ++r) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < r; ++s) a[s & 3] += sA[r][s] * x[s];
+    x[r] = (r == j ? 1.f : 0.f) - ((a[0] + a[1]) + (a[2] + a[3]));
+  }
+}
+
 template <int DK, typename In>
 __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, const In* __restrict__ k,
                                                   const In* __restrict__ beta, const In* __restrict__ decay,
@@ -212,16 +225,10 @@ __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, cons
   }
   lds_sync();
   if (tid < kC) {
-    // column j of T = (I + A)^-1 by forward substitution
+    // column j of T = (I + A)^-1
     const int j = tid;
     float x[kC];
-#pragma unroll
-    for (int r = 0; r < kC; ++r) {
-      float acc = r == j ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) acc -= sA[r][s] * x[s];
-      x[r] = acc;
-    }
+    tri_inv_col(sA, j, x);
 #pragma unroll
     for (int r = 0; r < kC; ++r) w.Tm[cb + r * kC + j] = x[r];
   }
@@ -1262,16 +1269,10 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
   }
   lds_sync();
   if (tid < kC) {
-    // column j of T = (I + A)^-1 by forward substitution
+    // column j of T = (I + A)^-1
     const int j = tid;
     float x[kC];
-#pragma unroll
-    for (int r = 0; r < kC; ++r) {
-      float acc = r == j ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) acc -= sA[r][s] * x[s];
-      x[r] = acc;
-    }
+    tri_inv_col(sA, j, x);
 #pragma unroll
     for (int r = 0; r < kC; ++r) w.Tm[cb + r * kC + j] = x[r];
   }

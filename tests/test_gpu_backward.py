@@ -40,6 +40,7 @@ CASES = [
     ("gdn_d128", dict(B=2, T=45, H=36, init_state=True), {}),
     ("deltanet_d64", dict(B=1, T=40, H=72, DK=128, DV=128), {}),
     ("fp32_small", dict(B=1, T=37, H=72, DK=32, DV=128, init_state=True), {}),
+    ("gdn_d128", dict(B=1, T=40, H=18, HV=72, init_state=True), {}),
 ]
 
 

@@ -122,12 +122,11 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     elif w.decay == "channel_softplus":
         decay = act(-_softplus(-3.0 + normal(lead + (w.DK,))))
     elif w.decay == "channel_strong":
-        # a 16-token block decays by exp(-6) to exp(-14) in most channels:
-        # strong, but short of the steep threshold exp(-16)
+        # a 16-token block decays by exp(-6) to exp(-14) in most channels
         decay = act(-_softplus(-1.0 + normal(lead + (w.DK,))))
     elif w.decay == "channel_steep":
         # strong per-channel decay: a 16-token block decays by about exp(-20)
-        # (steeper than exp(-16) in most channels), still far from fp32 underflow
+        # in most channels, still far from fp32 underflow
         decay = act(-_softplus(1.0 + normal(lead + (w.DK,))))
     elif w.decay == "channel_extreme":
         # about -10 per token: a 16-token block decays by about exp(-160)

@@ -76,12 +76,12 @@ CHUNK_CASES = [
     ("gdn_d128", dict(B=1, T=70, H=64, init_state=True)),
     ("gdn_d128", dict(B=1, T=90, H=64, chunk=32)),
     ("deltanet_d64", dict(B=4, T=70, H=64)),
-    # strong per-channel decay short of the fallback: late rows of a block
-    # carry prefix factors near exp(-16) in fp16
+    # strong per-channel decay (16-token blocks at exp(-6) to exp(-14)):
+    # chunks on the exact path, its quarter products far from 1
     ("kda_d128", dict(B=1, T=200, H=2, decay="channel_strong", init_state=True)),
     ("kda_d128", dict(B=1, T=100, H=2, chunk=32, decay="channel_strong")),
     ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=16, decay="channel_strong")),
-    # per-channel decay steep enough for the wide-range operand fallback
+    # steeper per-channel decay (16-token blocks near exp(-20)), exact path
     ("kda_d128", dict(B=1, T=200, H=2, decay="channel_steep", init_state=True)),
     ("kda_d128", dict(B=1, T=90, H=2, DK=64, DV=64, chunk=32, decay="channel_steep")),
     ("fp32_small", dict(T=70, chunk=32, decay="channel_steep", init_state=True)),

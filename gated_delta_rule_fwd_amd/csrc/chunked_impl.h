@@ -509,15 +509,15 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     }
     if (chan && tid == 0) *s_steep = 0;
     if (wave == 0) {
-      // the scalar gate: lane r holds token r of the chunk (C <= 64)
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off, 64);
-        if (lane >= off) G += y;
+      // the scalar gate: lane r holds token r of the chunk (C <= 64); its
+      // cumulative sums (zero without a per-head decay)
+      float Gx = 0.f, Glast = 0.f;
+      if constexpr (headdecay) {
+        const WaveScan ws = wave_scan(G);
+        G = ws.incl;
+        Gx = ws.excl;
+        Glast = ws.total;
       }
-      float Gx = __shfl_up(G, 1, 64);
-      if (lane == 0) Gx = 0.f;
-      const float Glast = __shfl(G, 63, 64);
       if (lane < C) {
         s_bt[lane] = bt;
         s_Gi[lane] = G;
@@ -964,23 +964,34 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     // diagonal 16x16 blocks, lane -> (block, column jc): forward substitution
     // by rows, x_r = [r == jc] - sum_{s < r} A_rs x_s, A's row read four
     // entries at a time (one 16-byte read for the 16 lanes of a block), the
-    // sum in four partial sums
+    // sum in four partial sums.  Row r + 1 is read while row r is summed: the
+    // scheduling fence keeps those reads ahead of the sums, which would
+    // otherwise wait out each row's read latency in turn.
     const int i = g, jc = l16;
     if (i < NB) {
       float x[16];
       const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
       x[0] = jc == 0 ? 1.f : 0.f;
+      f32x4 cur[4], nxt[4];
+      cur[0] = *reinterpret_cast<const f32x4*>(ablk + L::LF);
 #pragma unroll
       for (int r = 1; r < 16; ++r) {
+        if (r < 15) {
+#pragma unroll
+          for (int s4 = 0; s4 < (r + 4) / 4; ++s4)
+            nxt[s4] = *reinterpret_cast<const f32x4*>(ablk + (r + 1) * L::LF + 4 * s4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4*>(ablk + r * L::LF + 4 * s4);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (4 * s4 + e < r) acc[e] += a4[e] * x[4 * s4 + e];
+            if (4 * s4 + e < r) acc[e] += cur[s4][e] * x[4 * s4 + e];
         }
         x[r] = (r == jc ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) cur[s4] = nxt[s4];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];
@@ -1006,16 +1017,23 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     // blocks on diagonal d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, on waves 1..
     const int j = wave - 1, i = j + d;
     if (wave >= 1 && i < NB) {
-      f32x4 X = {0, 0, 0, 0};
-      for (int kb = j; kb < i; ++kb) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(sAm + (16 * i + l16) * L::LF + 16 * kb + 4 * g);
+      // every operand read first (one wait), then the MFMA chain
+      f32x4 a4[NB], t4;
+      float bv[NB][4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float bv = sTm[(16 * kb + 4 * g + jj) * L::LF + 16 * j + l16];
-          X = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[jj], bv, X, 0, 0, 0);
-        }
+      for (int kk = 0; kk < d; ++kk) {
+        a4[kk] = *reinterpret_cast<const f32x4*>(sAm + (16 * i + l16) * L::LF + 16 * (j + kk) + 4 * g);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) bv[kk][jj] = sTm[(16 * (j + kk) + 4 * g + jj) * L::LF + 16 * j + l16];
       }
-      const f32x4 t4 = *reinterpret_cast<const f32x4*>(sTm + (16 * i + l16) * L::LF + 16 * i + 4 * g);
+      t4 = *reinterpret_cast<const f32x4*>(sTm + (16 * i + l16) * L::LF + 16 * i + 4 * g);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 X = {0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < d; ++kk) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) X = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[kk][jj], bv[kk][jj], X, 0, 0, 0);
+      }
       f32x4 Y = {0, 0, 0, 0};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[jj], X[jj], Y, 0, 0, 0);

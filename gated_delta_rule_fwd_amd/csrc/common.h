@@ -142,6 +142,36 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return xor32_sum(xor16_sum(x));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, with its exclusive
+// counterpart (lane i: the inclusive sum of lane i - 1, 0 in lane 0) and the
+// wave's total, all without LDS traffic: DPP right shifts within each row of
+// 16 lanes (a lane with no source adds 0), then the totals of the earlier
+// rows, read from lanes 15, 31 and 47.
+struct WaveScan { float incl, excl, total; };
+__device__ __forceinline__ WaveScan wave_scan(float x) {
+  auto shr = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  auto lane_val = [](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
+  const int lane = __lane_id(), row = lane >> 4;
+  const float r0 = lane_val(x, 15), r1 = lane_val(x, 31), r2 = lane_val(x, 47);
+  const float before = row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  x += before;
+  WaveScan w;
+  w.incl = x;
+  const float prev = shr(x, std::integral_constant<int, 0x111>{});
+  const float e0 = lane_val(x, 15), e1 = lane_val(x, 31), e2 = lane_val(x, 47);
+  const float edge = row == 0 ? 0.f : row == 1 ? e0 : row == 2 ? e1 : e2;
+  w.excl = (lane & 15) == 0 ? edge : prev;
+  w.total = lane_val(x, 63);
+  return w;
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) {
   // 1 / max(||x||_2, 1e-12): the hardware reciprocal square root (about
   // 1 ulp), capped where the norm is below 1e-12 (a NaN sum gives the cap)

@@ -553,6 +553,40 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   // kernel being its only reader.  wq: per-channel decay, the within-quarter
   // sums of a diagonal block (s and r in one quarter), added here.
   bool mild = false;   // per-channel decay on the mild path: no within-quarter sums
+
+  // Diagonal 16x16 block i of T, column jc (this lane's): forward substitution
+  // by rows, x_r = [r == jc] - sum_{s < r} A_rs x_s, A's row read four entries
+  // at a time (one 16-byte read for the 16 lanes of a block), the sum in four
+  // partial sums.  Row r + 1 is read while row r is summed: the scheduling
+  // fence keeps those reads ahead of the sums, which would otherwise wait out
+  // each row's read latency in turn.
+  auto diag_inverse = [&](int i, int jc, float (&x)[16]) {
+    const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
+    x[0] = jc == 0 ? 1.f : 0.f;
+    f32x4 cur[4], nxt[4];
+    cur[0] = *reinterpret_cast<const f32x4*>(ablk + L::LF);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      if (r < 15) {
+#pragma unroll
+        for (int s4 = 0; s4 < (r + 4) / 4; ++s4)
+          nxt[s4] = *reinterpret_cast<const f32x4*>(ablk + (r + 1) * L::LF + 4 * s4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * s4 + e < r) acc[e] += cur[s4][e] * x[4 * s4 + e];
+      }
+      x[r] = (r == jc ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) cur[s4] = nxt[s4];
+    }
+  };
+  float xd[16];   // without per-channel decay: this wave's diagonal block of T (waves < NB)
+
   auto emit = [&](int i, int j, bool isP, const f32x4& acc) {
     const int r = 16 * i + l16, s0 = 16 * j + 4 * g;
     const f32x4 gs = *reinterpret_cast<const f32x4*>(s_Gi + s0);
@@ -594,10 +628,11 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 
   if constexpr (!chan) {
     // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
-    // (raw rows: A only; the state kernel forms P)
-    for (int job = wave; job < (R::kRawK ? NPAIR : 2 * NPAIR); job += kPrepWaves) {
-      const bool isP = job >= NPAIR;
-      const int i = pair_i(isP ? job - NPAIR : job), j = pair_j(isP ? job - NPAIR : job);
+    // (raw rows: A only; the state kernel forms P).  Wave i < NB forms A's
+    // diagonal block i and inverts it at once (its own LDS writes, read back
+    // in order), while the other waves form the remaining blocks: the
+    // inverse overlaps the rest of the Gram.
+    auto gram = [&](int i, int j, bool isP) {
       const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
       const OpT* brow = sK + (16 * j + l16) * L::LDK;
       f32x4 acc = {0, 0, 0, 0};
@@ -607,6 +642,22 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 #pragma unroll
       for (int m = 0; m < NKP; ++m) M::mma(acc, fb[m], fa[m]);
       emit(i, j, isP, acc);
+    };
+    static_assert(NB < kPrepWaves, "a wave per diagonal block, and more for the rest");
+    if (wave < NB) {
+      gram(wave, wave, false);
+      if (g == 0) diag_inverse(wave, l16, xd);
+    }
+    // the rest: A's off-diagonal blocks, then (unless raw rows) every block of
+    // P; with raw rows on the waves past NB only, else on every wave, the
+    // first NB waves after their inverse
+    constexpr int NOFFB = NB * (NB - 1) / 2;
+    constexpr int NREST = NOFFB + (R::kRawK ? 0 : NPAIR);
+    constexpr int NRW = R::kRawK ? kPrepWaves - NB : kPrepWaves;
+    const int rw = R::kRawK ? wave - NB : (wave + kPrepWaves - NB) % kPrepWaves;
+    for (int q = rw; rw >= 0 && q < NREST; q += NRW) {
+      if (q < NOFFB) gram(pair_i(q) + 1, pair_j(q), false);
+      else gram(pair_i(q - NOFFB), pair_j(q - NOFFB), true);
     }
   } else {
     // Per-key-channel decay.  Quarter Q holds tokens 4Q .. 4Q+3; LPQ lanes
@@ -960,43 +1011,23 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   lds_barrier();
 
   // ============ phase 3: T = (I + A)^-1 (fp32) ============
-  if (wave == 0) {
-    // diagonal 16x16 blocks, lane -> (block, column jc): forward substitution
-    // by rows, x_r = [r == jc] - sum_{s < r} A_rs x_s, A's row read four
-    // entries at a time (one 16-byte read for the 16 lanes of a block), the
-    // sum in four partial sums.  Row r + 1 is read while row r is summed: the
-    // scheduling fence keeps those reads ahead of the sums, which would
-    // otherwise wait out each row's read latency in turn.
-    const int i = g, jc = l16;
-    if (i < NB) {
-      float x[16];
-      const float* ablk = sAm + (16 * i) * L::LF + 16 * i;
-      x[0] = jc == 0 ? 1.f : 0.f;
-      f32x4 cur[4], nxt[4];
-      cur[0] = *reinterpret_cast<const f32x4*>(ablk + L::LF);
+  // diagonal blocks of T into their region, over tiles the Gram has now
+  // finished reading
+  if constexpr (!chan) {
+    if (wave < NB && g == 0) {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        if (r < 15) {
-#pragma unroll
-          for (int s4 = 0; s4 < (r + 4) / 4; ++s4)
-            nxt[s4] = *reinterpret_cast<const f32x4*>(ablk + (r + 1) * L::LF + 4 * s4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * s4 + e < r) acc[e] += cur[s4][e] * x[4 * s4 + e];
-        }
-        x[r] = (r == jc ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) cur[s4] = nxt[s4];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sTm[(16 * i + r) * L::LF + 16 * i + jc] = x[r];
+      for (int r = 0; r < 16; ++r) sTm[(16 * wave + r) * L::LF + 16 * wave + l16] = xd[r];
     }
-  } else {
+  } else if (wave == 0) {
+    // per-channel decay: after the Gram, lane -> (block, column)
+    if (g < NB) {
+      float x[16];
+      diag_inverse(g, l16, x);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sTm[(16 * g + r) * L::LF + 16 * g + l16] = x[r];
+    }
+  }
+  if (wave != 0) {
     // meanwhile the other waves zero P above the block diagonal (never
     // produced by the Gram)
     constexpr int VE = 16 / sizeof(OpT);

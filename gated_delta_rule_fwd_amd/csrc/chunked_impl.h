@@ -407,6 +407,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   float* s_fk = s_qk;                          // raw K: the row factor of k
   float* s_misc = sv + 4 * C;
   int* s_steep = reinterpret_cast<int*>(s_misc);   // per-channel decay: a quarter decays by more than e^-3
+  int* s_dflag = reinterpret_cast<int*>(s_misc + 4);   // otherwise: [4] diagonal block i of A written
   float* s_tau4 = s_misc + 16;                 // [NQ][DK] decay factor of each 4-token quarter
                                                // (first its log, the quarter's gate sum; on the
                                                // mild path then the log decay from the chunk
@@ -508,6 +509,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       }
     }
     if (chan && tid == 0) *s_steep = 0;
+    if (!chan && tid < 4) s_dflag[tid] = 0;
     if (wave == 0) {
       // the scalar gate: lane r holds token r of the chunk (C <= 64); its
       // cumulative sums (zero without a per-head decay)
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
       for (int s4 = 0; s4 < 4; ++s4) cur[s4] = nxt[s4];
     }
   };
-  float xd[16];   // without per-channel decay: this wave's diagonal block of T (waves < NB)
+  float xd[16];   // without per-channel decay: wave 0's column of a diagonal block of T
 
   auto emit = [&](int i, int j, bool isP, const f32x4& acc) {
     const int r = 16 * i + l16, s0 = 16 * j + 4 * g;
@@ -629,9 +631,9 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   if constexpr (!chan) {
     // ============ phase 2: Gram A (strictly lower) and P (lower inclusive) ============
     // (raw rows: A only; the state kernel forms P).  Wave i < NB forms A's
-    // diagonal block i and inverts it at once (its own LDS writes, read back
-    // in order), while the other waves form the remaining blocks: the
-    // inverse overlaps the rest of the Gram.
+    // diagonal block i and flags it; wave 0 inverts all of them (lane ->
+    // block, column) as soon as they are flagged, while waves 1 .. 7 form
+    // the remaining blocks: the inverse overlaps the rest of the Gram.
     auto gram = [&](int i, int j, bool isP) {
       const OpT* arow = (isP ? sQ : sK) + (16 * i + l16) * L::LDK;
       const OpT* brow = sK + (16 * j + l16) * L::LDK;
@@ -646,15 +648,22 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
     static_assert(NB < kPrepWaves, "a wave per diagonal block, and more for the rest");
     if (wave < NB) {
       gram(wave, wave, false);
-      if (g == 0) diag_inverse(wave, l16, xd);
+      if (wave > 0) {
+        // (the release orders this wave's writes of the block before the flag)
+        if (lane == 0) __hip_atomic_store(&s_dflag[wave], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        for (int w = 1; w < NB; ++w)
+          while (__hip_atomic_load(&s_dflag[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+            __builtin_amdgcn_s_sleep(1);
+        if (g < NB) diag_inverse(g, l16, xd);
+      }
     }
     // the rest: A's off-diagonal blocks, then (unless raw rows) every block of
-    // P; with raw rows on the waves past NB only, else on every wave, the
-    // first NB waves after their inverse
+    // P, on waves 1 .. 7, those past NB first
     constexpr int NOFFB = NB * (NB - 1) / 2;
     constexpr int NREST = NOFFB + (R::kRawK ? 0 : NPAIR);
-    constexpr int NRW = R::kRawK ? kPrepWaves - NB : kPrepWaves;
-    const int rw = R::kRawK ? wave - NB : (wave + kPrepWaves - NB) % kPrepWaves;
+    constexpr int NRW = kPrepWaves - 1;
+    const int rw = wave == 0 ? -1 : (wave - NB + NRW) % NRW;
     for (int q = rw; rw >= 0 && q < NREST; q += NRW) {
       if (q < NOFFB) gram(pair_i(q) + 1, pair_j(q), false);
       else gram(pair_i(q - NOFFB), pair_j(q - NOFFB), true);
@@ -1014,9 +1023,9 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
   // diagonal blocks of T into their region, over tiles the Gram has now
   // finished reading
   if constexpr (!chan) {
-    if (wave < NB && g == 0) {
+    if (wave == 0 && g < NB) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sTm[(16 * wave + r) * L::LF + 16 * wave + l16] = xd[r];
+      for (int r = 0; r < 16; ++r) sTm[(16 * g + r) * L::LF + 16 * g + l16] = xd[r];
     }
   } else if (wave == 0) {
     // per-channel decay: after the Gram, lane -> (block, column)

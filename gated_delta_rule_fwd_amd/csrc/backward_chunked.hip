@@ -863,7 +863,8 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     S.dO[er][en] = docur;
     lds_sync();
     if (s + 1 < nsl) prefetch(s + 1);
-    // K S0 (waves 0, 1), Q S0 (2, 3), K dS1 (4, 5): one row tile over all keys
+    // K S0 (waves 0, 1), Q S0 (2, 3), K dS1 (4, 5): one row tile over all
+    // keys; P^T dO (6, 7) into dD's place
     if (prod < 3) {
       const float(*A)[DK + 4] = prod == 1 ? sm.qh : sm.kh;
       const float(*Bm)[kNS + 1] = prod == 2 ? S.S1s : S.S0s;
@@ -877,25 +878,70 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
       float(*O)[kNS + 1] = prod == 0 ? S.KS : (prod == 1 ? S.QS : S.KD);
 #pragma unroll
       for (int e = 0; e < 4; ++e) O[16 * prt + 4 * lg + e][li] = p[e];
+    } else {
+      // (P^T)_rt = P_tr vanishes for t < r: row tile 1 takes tokens 16.. only
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= prt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.PmT[16 * prt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], S.dO[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.dD[16 * prt + 4 * lg + e][li] = p[e];
     }
     lds_sync();
     // X = V - exp(gx) . K S0, Y = beta . X;  dD = P^T dO + F . K dS1
-    const float ksv = S.KS[er][en], qsv = S.QS[er][en], kdv = S.KD[er][en];
-    const float x = vcur - tv.egx[er] * ksv;
+    const float ksv = S.KS[er][en], kdv = S.KD[er][en];
+    const float xo = tv.egx[er] * ksv, x = vcur - xo;
     S.Yb[er][en] = tv.bt[er] * x;
-    S.dD[er][en] = row_col(sm.PmT[er], S.dO, en) + tv.F[er] * kdv;
+    S.dD[er][en] += tv.F[er] * kdv;
+    so += docur * S.QS[er][en];
     lds_sync();
-    // D = T Y;  dY = T^T dD; the per-token sums
-    const float d = col_col(sm.TmT, er, S.Yb, en);
-    const float y = row_col(sm.TmT[er], S.dD, en);
-    S.D[er][en] = d;
-    S.FD[er][en] = tv.F[er] * d;
-    S.dYs[er][en] = -tv.egx[er] * tv.bt[er] * y;
+    // D = T Y (waves 0, 1) and dY = T^T dD (2, 3), a row tile each; raw dY
+    // goes over K S0 (read above).  T is lower triangular: T Y's row tile 0
+    // takes tokens 0..15 only, T^T dD's row tile 1 tokens 16.. only.
+    if (wave < 2) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb <= prt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p = mma4(sm.TmT[16 * kb + 4 * lg + e][16 * prt + li], S.Yb[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * prt + 4 * lg + e;
+        S.D[r][li] = p[e];
+        S.FD[r][li] = tv.F[r] * p[e];
+      }
+    } else if (wave < 4) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= prt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.TmT[16 * prt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], S.dD[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * prt + 4 * lg + e;
+        S.KS[r][li] = p[e];
+        S.dYs[r][li] = -tv.egx[r] * tv.bt[r] * p[e];
+      }
+    }
+    lds_sync();
+    // the per-token sums
+    const float d = S.D[er][en], y = S.KS[er][en];
     sb += y * x;
-    so += docur * qsv;
-    sx += y * (vcur - x);
+    sx += y * xo;
     sf += kdv * d;
-    lds_sync();
     // dT += dD Y^T, dP += dO D^T (this wave's tile)
 #pragma unroll
     for (int ks = 0; ks < kNS / 4; ++ks) {

@@ -403,18 +403,6 @@ __device__ __forceinline__ float row_col(const float* row, const float (*col)[P]
   }
   return a0 + a1;
 }
-// sum_t a[t][m] b[t][n] over 32 (two columns)
-template <int PA, int PB>
-__device__ __forceinline__ float col_col(const float (*a)[PA], int m, const float (*b)[PB], int n) {
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll 4
-  for (int t = 0; t < kC; t += 2) {
-    a0 += a[t][m] * b[t][n];
-    a1 += a[t + 1][m] * b[t + 1][n];
-  }
-  return a0 + a1;
-}
-
 // (1) per (b, h, slice of kNS value columns): every chunk's S0 into the
 // workspace, chunk after chunk.  The slice of the state (DK x 16) sits in
 // MFMA accumulators, 16 key rows per tile, tile m in wave m % 4.  Per chunk:
@@ -780,10 +768,10 @@ struct LocalLds {
 // at a time: dq and dk (through the norm and the scale; with grouped value
 // heads those of the normalised rows, added up over the group), dbeta and the
 // decay's gradient (written).  Eight
-// waves, two workgroups per CU.  Per slice: K S0, Q S0 and K dS1 on MFMA
-// (one product's row tile per wave, waves 0-5); X, D, dD, dY and the
-// per-token sums on VALU, one (row, column) element per thread; then on
-// MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
+// waves, two workgroups per CU.  Per slice: K S0, Q S0, K dS1 and P^T dO on
+// MFMA (one product's row tile per wave); X, Y and dD on VALU, one (row,
+// column) element per thread; D = T Y and dY = T^T dD on MFMA (waves 0-3);
+// the per-token sums on VALU; then on MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
 // dq += dO S0^T, dk += (F . D) dS1^T - (exp(gx) beta . dY) S0^T (tiles per
 // wave, held across the slices).  Then dA, dG and Z on VALU and the last
 // products dq += Z K, dk += (dG + dG^T) K + Z^T Q on MFMA.
@@ -1352,8 +1340,9 @@ struct LocalChLds {
 
 // (3) per-channel decay, per (b, h, chunk): dq, dk (as in the per-head
 // kernel), dbeta and the per-channel decay's gradient.  Per slice of 16 value
-// columns: X = V - (k exp(gx)) S0 and K dS1 with F folded in, on MFMA (one
-// row tile per wave, waves 0-3); D, dD, dY on VALU; then the running sums
+// columns: X = V - (k exp(gx)) S0 and K dS1 with F folded in, and P^T dO, on
+// MFMA (one row tile per wave, waves 0-5); then D = T Y and dY = T^T dD on
+// MFMA (waves 0-3); then the running sums
 // dT, dP (a tile per wave) and, per (row, channel) position held by a wave,
 // dO S0^T, dX S0^T and D dS1^T.  Then dA; then, at each position, the
 // in-chunk pair terms (sums over the partner token u of dA or dP times k or
@@ -1453,18 +1442,60 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
       float(*O)[kNS + 1] = prod == 0 ? S.KX : S.KD;
 #pragma unroll
       for (int e = 0; e < 4; ++e) O[16 * prt + 4 * lg + e][li] = p[e];
+    } else if (prod == 2) {
+      // P^T dO (waves 4, 5) into dD's place; (P^T)_rt = P_tr vanishes for
+      // t < r: row tile 1 takes tokens 16.. only
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= prt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.PmT[16 * prt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], S.dO[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.dD[16 * prt + 4 * lg + e][li] = p[e];
     }
     lds_sync();
     const float x = vcur - S.KX[er][en];
     S.Yb[er][en] = tv.bt[er] * x;
-    S.dD[er][en] = row_col(sm.PmT[er], S.dO, en) + S.KD[er][en];
+    S.dD[er][en] += S.KD[er][en];
     lds_sync();
-    const float d = col_col(sm.TmT, er, S.Yb, en);
-    const float y = row_col(sm.TmT[er], S.dD, en);
-    S.D[er][en] = d;
-    S.dX[er][en] = tv.bt[er] * y;
-    sb += y * x;
+    // D = T Y (waves 0, 1) and dY = T^T dD (2, 3), a row tile each; raw dY
+    // goes over K X (read above).  T is lower triangular: T Y's row tile 0
+    // takes tokens 0..15 only, T^T dD's row tile 1 tokens 16.. only.
+    if (wave < 2) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb <= prt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p = mma4(sm.TmT[16 * kb + 4 * lg + e][16 * prt + li], S.Yb[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.D[16 * prt + 4 * lg + e][li] = p[e];
+    } else if (wave < 4) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= prt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.TmT[16 * prt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], S.dD[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * prt + 4 * lg + e;
+        S.KX[r][li] = p[e];
+        S.dX[r][li] = tv.bt[r] * p[e];
+      }
+    }
     lds_sync();
+    sb += S.KX[er][en] * x;
 #pragma unroll
     for (int ks = 0; ks < kNS / 4; ++ks) {
       const float a = tpm ? S.dO[16 * tpr + li][4 * ks + lg] : S.dD[16 * tpr + li][4 * ks + lg];

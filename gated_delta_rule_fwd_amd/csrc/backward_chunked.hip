@@ -407,7 +407,7 @@ __device__ __forceinline__ float row_col(const float* row, const float (*col)[P]
 // workspace, chunk after chunk.  The slice of the state (DK x 16) sits in
 // MFMA accumulators, 16 key rows per tile, tile m in wave m % 4.  Per chunk:
 // K S as partial products of each wave's own tiles (the tile is the B
-// operand as it stands), summed through LDS; Y and D = T Y on VALU; then
+// operand as it stands), summed through LDS; Y on VALU; D = T Y and then
 // S <- exp(gC) S + K^T (F . D) on MFMA.  The next chunk's inputs are loaded
 // into registers while this one is computed.
 template <int DK, int DV, typename In, bool CH>
@@ -511,11 +511,23 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
       Y[r][n] = tv.bt[r] * ((u ? v1 : v0) - tv.egx[r] * ks);
     }
     lds_sync();
-    // F . D, D = T Y (T unit lower triangular)
+    // F . D, D = T Y on MFMA (waves 0, 1, a row tile each; T is unit lower
+    // triangular, so row tile 0 takes tokens 0..15 only)
+    if (wave < 2) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThr, r = idx / kNS, n = idx % kNS;
-      FD[r][n] = tv.F[r] * row_col(Tm[r], Y, n);
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb <= wave) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&Tm[16 * wave + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], Y[16 * kb + 4 * lg + e][li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wave + 4 * lg + e;
+        FD[r][li] = tv.F[r] * p[e];
+      }
     }
     lds_sync();
     // S <- exp(gC) S + K^T (F . D); per channel: exp(gC_c) per state row and
@@ -547,8 +559,8 @@ __global__ __launch_bounds__(kThr) void cbwd_fwd(const In* __restrict__ k, const
 // (2) per (b, h, slice): the walk of the state gradient from the last chunk
 // to the first; every chunk's dS1 into the workspace, dv, and the initial
 // state's gradient.  The slice of dS sits in MFMA accumulators as S does in
-// (1); per chunk: K dS (partial products per wave, summed through LDS),
-// dD = P^T dO + F . K dS and dY = T^T dD on VALU, then
+// (1); per chunk: K dS (partial products per wave, summed through LDS) and
+// P^T dO on MFMA, dD = P^T dO + F . K dS on VALU, dY = T^T dD on MFMA, then
 // dS <- exp(gC) dS + [Q; K]^T [exp(gam) . dO; -exp(gx) . dX] on MFMA.  The
 // next chunk's inputs are loaded into registers while this one is computed.
 template <int DK, int DV, typename In, bool CH, int NS>
@@ -666,6 +678,22 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
         }
       }
     }
+    // P^T dO into dD's place, a (row tile, column tile) per wave; (P^T)_rt =
+    // P_tr vanishes for t < r: row tile 1 takes tokens 16.. only
+    if (wave < 2 * NCT) {
+      const int rt = wave & 1, ct = wave >> 1;
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= rt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&PmT[16 * rt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], dO[16 * kb + 4 * lg + e][16 * ct + li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dD[16 * rt + 4 * lg + e][16 * ct + li] = p[e];
+    }
     lds_sync();
     if constexpr (CH) {
       // the rows of the dS update: q exp(gam) and k exp(gx), in place
@@ -675,24 +703,37 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
         kh[r][c] *= __expf(gs[r][c]);
       }
     }
-    // dD = P^T dO + F . K dS
+    // dD = P^T dO + F . K dS; exp(gam) . dO, the update's first B operand
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
       const int idx = tid + u * kThr, r = idx / NS, n = idx % NS;
       float kd = 0.f;
 #pragma unroll
       for (int qq = 0; qq < NW; ++qq) kd += part[qq][r][n];
-      dD[r][n] = row_col(PmT[r], dO, n) + tv.F[r] * kd;
+      dD[r][n] += tv.F[r] * kd;
+      BB[r][n] = tv.egm[r] * dO[r][n];
     }
     lds_sync();
-    // dX = beta . T^T dD, the gradient of v; the B operand of the dS update
+    // dX = beta . T^T dD on MFMA (a row tile and column tile per wave; T^T is
+    // upper triangular), the gradient of v, and the update's second B operand
+    if (wave < 2 * NCT) {
+      const int rt = wave & 1, ct = wave >> 1;
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int idx = tid + u * kThr, r = idx / NS, n = idx % NS;
-      const float x = tv.bt[r] * row_col(TmT[r], dD, n);
-      if (r < L) dv[((tok0 + r) * H + h) * DV + n0 + n] = x;
-      BB[r][n] = tv.egm[r] * dO[r][n];
-      BB[kC + r][n] = -tv.egx[r] * x;
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        if (kb >= rt) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&TmT[16 * rt + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = mma4(a[e], dD[16 * kb + 4 * lg + e][16 * ct + li], p);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, n = 16 * ct + li;
+        const float x = tv.bt[r] * p[e];
+        if (r < L) dv[((tok0 + r) * H + h) * DV + n0 + n] = x;
+        BB[kC + r][n] = -tv.egx[r] * x;
+      }
     }
     lds_sync();
     // dS <- exp(gC) dS + Q^T (exp(gam) . dO) - K^T (exp(gx) . dX)

@@ -388,21 +388,36 @@ struct MatPf {
   }
 };
 
-// sum_t row[t] col[t][n] over a chunk's 32 tokens (row 16-byte aligned;
-// zeros where a triangular factor vanishes)
-template <int P>
-__device__ __forceinline__ float row_col(const float* row, const float (*col)[P], int n) {
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll 2
-  for (int t = 0; t < kC; t += 4) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(row + t);
-    a0 += x[0] * col[t][n];
-    a1 += x[1] * col[t + 1][n];
-    a0 += x[2] * col[t + 2][n];
-    a1 += x[3] * col[t + 3][n];
+// The 16 x 16 tile (rt, ct) of two 32 x 32 products on fp32 MFMA, with T
+// given transposed (TmT[t][r] = T_rt): M = dT T^T, dT and T both lower
+// triangular (tokens t <= min(r, c) only), and T^T M (tokens t >= r only).
+__device__ __forceinline__ f32x4 tile_dt_tt(const float (*dTm)[kCP], const float (*TmT)[kCP], int rt, int ct,
+                                            int li, int lg) {
+  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < kC / 16; ++kb) {
+    if (kb <= rt && kb <= ct) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&dTm[16 * rt + li][16 * kb + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p = mma4(a[e], TmT[16 * kb + 4 * lg + e][16 * ct + li], p);
+    }
   }
-  return a0 + a1;
+  return p;
 }
+__device__ __forceinline__ f32x4 tile_tt_m(const float (*TmT)[kCP], const float (*Mm)[kCP], int rt, int ct,
+                                           int li, int lg) {
+  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < kC / 16; ++kb) {
+    if (kb >= rt) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&TmT[16 * rt + li][16 * kb + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p = mma4(a[e], Mm[16 * kb + 4 * lg + e][16 * ct + li], p);
+    }
+  }
+  return p;
+}
+
 // (1) per (b, h, slice of kNS value columns): every chunk's S0 into the
 // workspace, chunk after chunk.  The slice of the state (DK x 16) sits in
 // MFMA accumulators, 16 key rows per tile, tile m in wave m % 4.  Per chunk:
@@ -1018,11 +1033,11 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     else Fm.dTm[r][c] = c <= r ? atp[e] : 0.f;
   }
   lds_sync();
-  // M = dT T^T (dT, T lower: zeros above the diagonal); K K^T on MFMA
+  // M = dT T^T (a tile per wave, waves 0-3) and K K^T on MFMA
+  if (wave < 4) {
+    const f32x4 p = tile_dt_tt(Fm.dTm, sm.TmT, wave >> 1, wave & 1, li, lg);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
-    Fm.M[r][c] = row_col(Fm.dTm[r], sm.TmT, c);
+    for (int e = 0; e < 4; ++e) Fm.M[16 * (wave >> 1) + 4 * lg + e][16 * (wave & 1) + li] = p[e];
   }
   {
     const int gt = wave & 3, gr = gt >> 1, gc = gt & 1, gh = wave >> 2;
@@ -1038,6 +1053,13 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     for (int e = 0; e < 4; ++e) Fm.Gp[gh][16 * gr + 4 * lg + e][16 * gc + li] = p[e];
   }
   lds_sync();
+  // -T^T M on MFMA, over dT (dead)
+  if (wave < 4) {
+    const f32x4 p = tile_tt_m(sm.TmT, Fm.M, wave >> 1, wave & 1, li, lg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Fm.dTm[16 * (wave >> 1) + 4 * lg + e][16 * (wave & 1) + li] = -p[e];
+  }
+  lds_sync();
   // dA = -T^T M on s < r; E = dA . (K K^T) . W; dG = diag(beta) dA . W;
   // Z = dP . Vw (into dPm) and dP . P
 #pragma unroll
@@ -1045,7 +1067,7 @@ __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q,
     const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
     float e = 0.f, dg = 0.f;
     if (c < r) {
-      const float da = -row_col(sm.TmT[r], Fm.M, c);
+      const float da = Fm.dTm[r][c];
       const float wr = __expf(sm.sgx[r] - sm.sgm[c]);
       e = da * (Fm.Gp[0][r][c] + Fm.Gp[1][r][c]) * wr;
       dg = da * tv.bt[r] * wr;
@@ -1582,16 +1604,20 @@ __global__ __launch_bounds__(kThr3) void cbwd_local_ch(const In* __restrict__ q,
     else Fm.dTm[r][c] = c <= r ? atp[e] : 0.f;
   }
   lds_sync();
+  // M = dT T^T, then dA = -T^T M on s < r: a tile per wave, waves 0-3
+  if (wave < 4) {
+    const f32x4 p = tile_dt_tt(Fm.dTm, sm.TmT, wave >> 1, wave & 1, li, lg);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
-    Fm.M[r][c] = row_col(Fm.dTm[r], sm.TmT, c);
+    for (int e = 0; e < 4; ++e) Fm.M[16 * (wave >> 1) + 4 * lg + e][16 * (wave & 1) + li] = p[e];
   }
   lds_sync();
+  if (wave < 4) {
+    const f32x4 p = tile_tt_m(sm.TmT, Fm.M, wave >> 1, wave & 1, li, lg);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = tid + u * kThr3, r = idx / kC, c = idx % kC;
-    Fm.dA[r][c] = c < r ? -row_col(sm.TmT[r], Fm.M, c) : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * (wave >> 1) + 4 * lg + e, c = 16 * (wave & 1) + li;
+      Fm.dA[r][c] = c < r ? -p[e] : 0.f;
+    }
   }
   lds_sync();
   // per position: the pair terms and the gradients; without grouped heads

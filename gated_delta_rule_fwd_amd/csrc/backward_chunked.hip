@@ -823,14 +823,15 @@ struct LocalLds {
 // (3) per (b, h, chunk): the remaining gradients over the value columns, 16
 // at a time: dq and dk (through the norm and the scale; with grouped value
 // heads those of the normalised rows, added up over the group), dbeta and the
-// decay's gradient (written).  Eight
-// waves, two workgroups per CU.  Per slice: K S0, Q S0, K dS1 and P^T dO on
-// MFMA (one product's row tile per wave); X, Y and dD on VALU, one (row,
-// column) element per thread; D = T Y and dY = T^T dD on MFMA (waves 0-3);
-// the per-token sums on VALU; then on MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
+// decay's gradient (written).  Eight waves, two workgroups per CU.  Per
+// slice: K S0, Q S0, K dS1 and P^T dO on MFMA (one product's row tile per
+// wave); X, Y and dD on VALU, one (row, column) element per thread; D = T Y
+// and dY = T^T dD on MFMA (waves 0-3); the per-token sums on VALU; then on
+// MFMA the running sums dT += dD Y^T, dP += dO D^T (a tile per wave) and
 // dq += dO S0^T, dk += (F . D) dS1^T - (exp(gx) beta . dY) S0^T (tiles per
-// wave, held across the slices).  Then dA, dG and Z on VALU and the last
-// products dq += Z K, dk += (dG + dG^T) K + Z^T Q on MFMA.
+// wave, held across the slices).  Then M = dT T^T and -T^T M on MFMA; dA,
+// dG and Z on VALU; and the last products dq += Z K, dk += (dG + dG^T) K +
+// Z^T Q on MFMA.
 template <int DK, int DV, typename In>
 __global__ __launch_bounds__(kThr3, 4) void cbwd_local(const In* __restrict__ q, const In* __restrict__ k,
                                                        const In* __restrict__ v, const float* __restrict__ dout,

@@ -116,12 +116,6 @@ template <> struct Mma<_Float16> {
       f[e] = (T)(static_cast<float>(f[e]) * (a * b));
     }
   }
-  // times fn(k) per k, rounded once
-  template <typename Fn>
-  __device__ static void scale_fn(frag& f, int k0, int g, Fn&& fn) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (T)(static_cast<float>(f[e]) * fn(k0 + 8 * g + e));
-  }
   __device__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
 };
 
@@ -159,14 +153,6 @@ template <> struct Mma<float> {
       const float a1 = u1 ? v1[k0 + 16 + 4 * g + e] : 1.f, b1 = u2 ? v2[k0 + 16 + 4 * g + e] : 1.f;
       f.lo[e] *= a0 * b0;
       f.hi[e] *= a1 * b1;
-    }
-  }
-  template <typename Fn>
-  __device__ static void scale_fn(frag& f, int k0, int g, Fn&& fn) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f.lo[e] *= fn(k0 + 4 * g + e);
-      f.hi[e] *= fn(k0 + 16 + 4 * g + e);
     }
   }
   __device__ static frag zero() { return frag{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
@@ -785,18 +771,32 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         }
       }
       lds_barrier();
-      // every block pair i >= j, A then P on the diagonal, then below it
+      // the scale exp(M_i - M_j) <= 1 of each pair i > j, per channel, once
+      // per workgroup: into rows of the quarter table that the operands have
+      // finished with (none of the rows 4 b + 2 that hold M_b)
       constexpr int NOFF = NB * (NB - 1) / 2;
+      auto fac_row = [](int pr) { return 4 * (pr / 3) + (pr % 3 == 2 ? 3 : pr % 3); };
+      static_assert(NOFF <= 6 && NOFF <= L::NQ, "pair scales fit the quarter table");
+      if (NOFF > 0 && tid < DK) {
+        float f[NOFF > 0 ? NOFF : 1];
+#pragma unroll
+        for (int pr = 0; pr < NOFF; ++pr)
+          f[pr] = __expf(s_tau4[(4 * (pair_i(pr) + 1) + 2) * DK + tid] - s_tau4[(4 * pair_j(pr) + 2) * DK + tid]);
+#pragma unroll
+        for (int pr = 0; pr < NOFF; ++pr) s_tau4[fac_row(pr) * DK + tid] = f[pr];
+      }
+      lds_barrier();
+      // every block pair i >= j, A then P on the diagonal, then below it
       for (int job = wave; job < 2 * NB + 2 * NOFF; job += kPrepWaves) {
         bool isP;
-        int i, j;
+        int i, j, pr = 0;
         if (job < 2 * NB) {
           isP = job >= NB;
           i = j = isP ? job - NB : job;
         } else {
           const int o = job - 2 * NB;
           isP = o >= NOFF;
-          const int pr = isP ? o - NOFF : o;
+          pr = isP ? o - NOFF : o;
           i = pair_i(pr) + 1;
           j = pair_j(pr);
         }
@@ -806,11 +806,7 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
 #pragma unroll
         for (int m = 0; m < NKP; ++m) {
           auto fa = M::ld_cont(arow, 32 * m, g);
-          if (i > j) {
-            const float* mi = s_tau4 + (4 * i + 2) * DK;   // M_i
-            const float* mj = s_tau4 + (4 * j + 2) * DK;
-            M::scale_fn(fa, 32 * m, g, [&](int c) { return __expf(mi[c] - mj[c]); });
-          }
+          if (i > j) M::scale_cont(fa, s_tau4 + fac_row(pr) * DK, 32 * m, g);
           M::mma(acc, M::ld_cont(krow, 32 * m, g), fa);
         }
         emit(i, j, isP, acc);

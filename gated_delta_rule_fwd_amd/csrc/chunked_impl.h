@@ -731,7 +731,11 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           for (int e = 0; e < CPT; ++e) all[e] = __expf(tot[e]);
           *reinterpret_cast<f32v*>(rvec + R::vDecC + c0) = all;
         }
-        f32v lprev = 0.f;   // the running sum through the token before
+        // exp(Gx - M_b) of the quarter's first token; each later token's is
+        // the exp(G - M_b) of the token before (the same sum, so the same value)
+        f32v fkn;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) fkn[e] = __expf(gq[e] - mb[e]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * Q + t;
@@ -741,8 +745,9 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           float xk[CPT], xq[CPT], xf[CPT];
 #pragma unroll
           for (int e = 0; e < CPT; ++e) {
-            const float gr = gq[e] + lp[t][e], grx = gq[e] + lprev[e];   // G, Gx of token r
-            const float fk = __expf(grx - mb[e]), fq = __expf(gr - mb[e]), fb = __expf(mb[e] - gr);
+            const float gr = gq[e] + lp[t][e];   // G of token r
+            const float fk = fkn[e], fq = __expf(gr - mb[e]), fb = __expf(mb[e] - gr);
+            fkn[e] = fq;
             const float k1 = static_cast<float>(kv[e]), q1 = static_cast<float>(qv[e]);
             rk[e] = (OpT)(k1 * fk);
             rq[e] = (OpT)(q1 * fq);
@@ -754,7 +759,6 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
           *reinterpret_cast<opv*>(sK + r * L::LDK + c0) = rk;
           *reinterpret_cast<opv*>(sQ + r * L::LDK + c0) = rq;
           *reinterpret_cast<opv*>(sKB + r * L::LDK + c0) = rb;
-          lprev = lp[t];
           if constexpr (CPT % 4 == 0) {
             put_perm<OpT, R::PPRK>(rec + R::oK, r, c0, xk);
             put_perm<OpT, R::PPRK>(rec + R::oQ, r, c0, xq);

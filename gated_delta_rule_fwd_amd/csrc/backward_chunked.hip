@@ -104,18 +104,36 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// LDS pitch of 32 x 32 matrices: rows read as 16-byte vectors
+constexpr int kCP = kC + 4;
+
 // (0) per (b, h, chunk): the norm factors of the rows, beta and the
 // cumulative decays per token; T and P of the chunk.
 // Column j of T = (I + A)^-1 (A strictly lower, kC x kC in LDS) by forward
 // substitution, each row's sum in four partial sums (a chain a quarter as
-// long).
-__device__ __forceinline__ void tri_inv_col(const float (*sA)[kC + 1], int j, float (&x)[kC]) {
+// long).  A's rows are read four entries at a time, row r + 1 while row r
+// is summed (the scheduling fence keeps those reads ahead of the sums).
+__device__ __forceinline__ void tri_inv_col(const float (*sA)[kCP], int j, float (&x)[kC]) {
+  x[0] = j == 0 ? 1.f : 0.f;
+  f32x4 cur[kC / 4], nxt[kC / 4];
+  cur[0] = *reinterpret_cast<const f32x4*>(&sA[1][0]);
 #pragma unroll
-  for (int r = 0; r < kC; ++r) {
+  for (int r = 1; r < kC; ++r) {
+    if (r + 1 < kC) {
+#pragma unroll
+      for (int s4 = 0; s4 < (r + 4) / 4; ++s4) nxt[s4] = *reinterpret_cast<const f32x4*>(&sA[r + 1][4 * s4]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < r; ++s) a[s & 3] += sA[r][s] * x[s];
+    for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * s4 + e < r) a[e] += cur[s4][e] * x[4 * s4 + e];
+    }
     x[r] = (r == j ? 1.f : 0.f) - ((a[0] + a[1]) + (a[2] + a[3]));
+#pragma unroll
+    for (int s4 = 0; s4 < kC / 4; ++s4) cur[s4] = nxt[s4];
   }
 }
 
@@ -126,7 +144,7 @@ __global__ __launch_bounds__(kThr) void cbwd_prep(const In* __restrict__ q, cons
                                                   int l2norm, Transforms tf) {
   constexpr int KP = DK + 4;
   __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
-  __shared__ float sA[kC][kC + 1];
+  __shared__ __align__(16) float sA[kC][kCP];
   __shared__ float sbt[kC], sgm[kC], sgx[kC];
   const int tid = threadIdx.x;
   const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);
@@ -354,9 +372,6 @@ struct RowPf {
     }
   }
 };
-
-// LDS pitch of 32 x 32 matrices: rows read as 16-byte vectors
-constexpr int kCP = kC + 4;
 
 // T and P of a chunk, loaded ahead (NTHR threads, 16-byte loads); stored
 // into LDS transposed (T^T, P^T) and, if given, as they are
@@ -1205,7 +1220,7 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
   constexpr int KP = DK + 4;
   __shared__ __align__(16) float kh[kC][KP], qh[kC][KP];
   __shared__ __align__(16) float gs[kC + 1][KP];   // row r + 1: gam of token r; row 0: zeros
-  __shared__ float sA[kC][kC + 1];
+  __shared__ __align__(16) float sA[kC][kCP];
   __shared__ float sbt[kC];
   const int tid = threadIdx.x;
   const int ci = blockIdx.x % N, bh = blockIdx.x / N, b = bh / H, h = bh % H, hk = h / (H / Hk);

@@ -1343,8 +1343,13 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_ch(const In* __restrict__ q, c
         w.Pm[cb + r * kC + sc] = pa[e];
       }
     }
-  } else {
-    for (int idx = tid - 128; idx < 4 * 36; idx += kThr - 128) {
+  }
+  // The 4 x 36 within-half pairs: one per thread of waves 2 and 3, the 16
+  // left over on wave 1 once its product is done.
+  static_assert(kThr == 256 && 4 * 36 - 128 <= 64, "pair jobs per thread");
+  {
+    const int idx = tid >= 128 ? tid - 128 : (tid >= 64 ? 128 + (tid - 64) : 4 * 36);
+    if (idx < 4 * 36) {
       const int hf = idx / 36, id = idx % 36;   // half hf: tokens 8 hf .. 8 hf + 7
       int rl = static_cast<int>((sqrtf(8.f * id + 1.f) - 1.f) * 0.5f);
       if ((rl + 1) * (rl + 2) / 2 <= id) ++rl;

@@ -726,11 +726,21 @@ __global__ __launch_bounds__(kThr) void cbwd_rev(const In* __restrict__ q, const
     }
     lds_sync();
     if constexpr (CH) {
-      // the rows of the dS update: q exp(gam) and k exp(gx), in place
-      for (int idx = tid; idx < kC * DK; idx += kThr) {
-        const int r = idx / DK, c = idx % DK;
-        qh[r][c] *= __expf(gs[r + 1][c]);
-        kh[r][c] *= __expf(gs[r][c]);
+      // the rows of the dS update: q exp(gam) and k exp(gx), in place.  Row r
+      // of gs is gx of token r and gam of token r - 1, so a thread that takes
+      // one channel over consecutive tokens forms each exponential once.
+      constexpr int TPC = kThr / DK;           // threads per channel
+      static_assert(kThr % DK == 0 && kC % TPC == 0, "token runs per thread");
+      constexpr int RUN = kC / TPC;
+      const int c = tid % DK, r0 = (tid / DK) * RUN;
+      float e0 = __expf(gs[r0][c]);
+#pragma unroll
+      for (int t = 0; t < RUN; ++t) {
+        const int r = r0 + t;
+        const float e1 = __expf(gs[r + 1][c]);
+        kh[r][c] *= e0;
+        qh[r][c] *= e1;
+        e0 = e1;
       }
     }
     // dD = P^T dO + F . K dS; exp(gam) . dO, the update's first B operand

@@ -638,6 +638,8 @@ __global__ __launch_bounds__(kPrepThreads, (prep_waves<DK, C, In, DECAY>())) voi
         // (the release orders this wave's writes of the block before the flag)
         if (lane == 0) __hip_atomic_store(&s_dflag[wave], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       } else {
+        // (waves 1 .. NB-1 are resident in the same workgroup and reach their
+        // flag with no wait of their own, so this wait ends)
         for (int w = 1; w < NB; ++w)
           while (__hip_atomic_load(&s_dflag[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
             __builtin_amdgcn_s_sleep(1);
